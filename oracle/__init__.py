@@ -1,0 +1,6 @@
+"""CPU float64 oracle for the KATA causal forward.
+
+Test infrastructure only: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark may import it; the library path never does.
+"""
+from .kata_oracle import *  # noqa: F401,F403
