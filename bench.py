@@ -1,0 +1,219 @@
+"""Benchmark of the KATA chunked causal forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+
+A step is one pass of the whole hot path over the 131k-token workload (B1 H8
+T131072 d_k16 d_v64 bf16, chunk 64, q/k unit-norm Gaussian rows, v ~ N(0,1)):
+per-chunk or per-segment states, the associative scan over them, the fused
+intra+inter output with normalisation, and the final-state export. Inputs are
+resident in HBM before timing starts. The T=32k workload (B1 H16 d_k32 C128)
+and 1024 decode steps on 512 x 4 rows are measured in the same run and
+reported under "parts". Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KATA chunked fwd tokens/sec + MFMA util at T=32k/131k; decode HBM GB/s"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters_fwd131k.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kernelized_linear_attention_phi_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def alg_flops_per_token_head(dk, dv, C):
+    """QK^T, A.V, phi(K)^T V and phi(Q).P with dense C x C intra tiles."""
+    D = dk * (dk + 1) // 2
+    return 2 * C * dk + 2 * C * dv + 4 * D * dv
+
+
+def alg_bytes_per_token_head(dk, dv, elem=2):
+    """One read of q, k, v and one write of o."""
+    return elem * (2 * dk + 2 * dv)
+
+
+def time_forward(kata, torch, w, q, k, v, steps, warmup):
+    """Times `steps` forwards (state export included) with events on the stream
+    the library launches on; returns (ms per step, per-phase ms)."""
+    B, H, T = w.B, w.H, w.T
+    D = w.dk * (w.dk + 1) // 2
+    o = torch.empty_like(v)
+    S_out = torch.empty((B, H, D, w.dv), dtype=torch.float32, device="cuda")
+    z_out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    nbytes = kata.chunked_fwd_workspace(B, H, T, w.dk, w.dv, w.chunk, 1, True)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        kata.chunked_fwd_into(q, k, v, o, w.chunk, True, ws, S_out=S_out, z_out=z_out)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        kata.chunked_fwd_into(q, k, v, o, w.chunk, True, ws, S_out=S_out, z_out=z_out,
+                              events=evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    total = sum(evs[i][0].elapsed_time(evs[i][3]) for i in range(steps)) / steps
+    phases = {name: sum(evs[i][a].elapsed_time(evs[i][a + 1]) for i in range(steps)) / steps
+              for a, name in enumerate(["states", "scan", "output"])}
+    return total, wall, phases
+
+
+def decode_bench(kata, torch, steps=1024, n_seq=512, heads=4, dk=16, dv=64, reps=3):
+    """1024 decode steps on n_seq x heads rows with fp32 state, replayed from a
+    HIP graph; returns ms per step and algorithmic GB/s."""
+    from kernelized_linear_attention_phi_amd import inputs as gen
+    N = n_seq * heads
+    D = dk * (dk + 1) // 2
+    rng = np.random.Generator(np.random.PCG64(5))
+    q, k, _ = gen.gaussian_qkv(1, steps, N, dk, 1, seed=5000, dtype="bf16")
+    vid = rng.integers(0, dv, (steps, N))
+    v = np.zeros((steps, N, dv), dtype=np.float32)
+    v[np.arange(steps)[:, None], np.arange(N)[None, :], vid] = 1.0
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16)
+    qd, kd, vd = to(q[0]), to(k[0]), to(v)
+    S = torch.rand((N, D, dv), device="cuda") * 0.01
+    z = torch.rand((N, D), device="cuda") + 1.0
+    o = torch.empty((steps, N, dv), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for t in range(4):
+            kata.decode_step(qd[t], kd[t], vd[t], S, z, out=o[t])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for t in range(steps):
+                kata.decode_step(qd[t], kd[t], vd[t], S, z, out=o[t])
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / (reps * steps)
+    bytes_step = N * (2 * 4 * D * (dv + 1) + 2 * (2 * dk + 2 * dv))
+    return ms_step, bytes_step / (ms_step * 1e-3) / 1e9, bytes_step
+
+
+def cpu_baseline(w, q, k, v, budget_s):
+    """The float64 brute-force oracle on a bounded sample of query rows of the
+    same workload (head 0, uniformly drawn positions), scaled to tokens/s."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas")
+    except Exception:  # noqa: BLE001
+        cores = None
+    cores = cores or len(os.sched_getaffinity(0))
+    rng = np.random.Generator(np.random.PCG64(99))
+    qq, kk, vv = q[:1, :1], k[:1, :1], v[:1, :1]
+    rows_done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        rows = np.sort(rng.integers(0, w.T, 64))
+        O.brute_force_rows(qq, kk, vv, rows)
+        rows_done += rows.size
+    el = time.perf_counter() - t0
+    tok_s = rows_done / (w.H * el)     # each token needs H head-rows
+    return {"value": tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 brute force on {rows_done} uniformly drawn query rows of head "
+                      f"(0,0) of the {w.name} workload in {el:.1f} s; tokens/s = rows/(H*s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--quick", action="store_true", help="primary workload only (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(see the sharding paragraph of the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kernelized_linear_attention_phi_amd as kata
+    from kernelized_linear_attention_phi_amd import inputs as gen
+    kata.lib()
+
+    def load(name):
+        w = gen.WORKLOADS[name]
+        q, k, v = gen.gaussian_qkv(w.B, w.H, w.T, w.dk, w.dv, w.seed, w.dtype)
+        to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+        return w, (q, k, v), (to(q), to(k), to(v))
+
+    w, host_in, dev_in = load("fwd131k")
+    ms, wall_ms, phases = time_forward(kata, torch, w, *dev_in, args.steps, args.warmup)
+    tok = w.B * w.T
+    value = tok / (ms * 1e-3)
+    th = w.B * w.H * w.T
+    flops = alg_flops_per_token_head(w.dk, w.dv, w.chunk) * th
+    abytes = alg_bytes_per_token_head(w.dk, w.dv) * th
+    out_ms = phases["output"]
+    achieved = abytes / (out_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS_FILE):
+        c = json.load(open(COUNTERS_FILE))
+        if c.get("kernel_src_sha") == kernel_source_hash():
+            traffic = c.get("traffic_bytes_per_launch")
+    result = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.dk, "d_v": w.dv,
+                   "chunk": w.chunk, "causal": True, "state_export": True},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "output phase (fused intra+inter forward)",
+                     "alg_bytes_per_launch": abytes, "avg_launch_ms": out_ms},
+        "parts": {"fwd131k": {"phase_ms": phases, "wall_ms_per_step": wall_ms,
+                              "mfma_util_alg": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                              "alg_tflops": flops / (ms * 1e-3) / 1e12,
+                              "hbm_frac_alg_whole_step": abytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}},
+    }
+    if not args.quick:
+        del dev_in
+        w3, host3, dev3 = load("fwd32k")
+        ms3, wall3, ph3 = time_forward(kata, torch, w3, *dev3, args.steps, args.warmup)
+        th3 = w3.B * w3.H * w3.T
+        fl3 = alg_flops_per_token_head(w3.dk, w3.dv, w3.chunk) * th3
+        result["parts"]["fwd32k"] = {
+            "tokens_per_s": w3.B * w3.T / (ms3 * 1e-3), "ms_per_step": ms3, "phase_ms": ph3,
+            "alg_tflops": fl3 / (ms3 * 1e-3) / 1e12,
+            "mfma_util_alg": fl3 / (ms3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "mfma_util_alg_output_phase": fl3 / (ph3["output"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        del dev3
+        dms, dgbs, dbytes = decode_bench(kata, torch)
+        result["parts"]["decode"] = {"ms_per_step": dms, "alg_GBps": dgbs,
+                                     "hbm_frac": dgbs / PEAK_HBM_GBS, "bytes_per_step": dbytes,
+                                     "rows": 2048, "steps": 1024, "hip_graph": True}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, *host_in, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

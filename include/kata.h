@@ -1,0 +1,152 @@
+/*
+ * kata.h - C ABI of the MI355X (gfx950) KATA causal-forward library.
+ *
+ * KATA is normalised kernelised linear attention with the rank-one PSD feature
+ * psi(u) = u u^T ("Kernelized Linear Attention: Breaking the Capacity Wall with
+ * Symmetric Cones", arXiv 2607.17419; the gist.science explainers, technical
+ * summary sections 2.1-2.3, and the paper's abstract). For every batch b, head h
+ * and position t:
+ *
+ *     o_t = sum_{j <= t} (q_t . k_j)^2 v_j  /  sum_{j <= t} (q_t . k_j)^2
+ *
+ * (j over all positions when causal = 0; o_t = 0 when the denominator is 0).
+ * The library computes it in the exact O(T) chunked-state form the explainers
+ * describe (section 2.3): a dense masked intra-chunk term, per-chunk states
+ * S = phi(K)^T V and z = phi(K)^T 1, and an associative (prefix) scan over chunk
+ * states; plus the single-token recurrent step the abstract calls constant-time
+ * recurrent inference.
+ *
+ * Packed feature (state layout). phi(x) has D = d(d+1)/2 entries, in row-major
+ * upper-triangle order p(i,j) = i*d - i*(i-1)/2 + (j-i) for i <= j; the entry is
+ * x_i*x_j on the diagonal and sqrt(2)*x_i*x_j off it, so phi(q).phi(k) = (q.k)^2.
+ * Every state argument (S [.., D, d_v], z [.., D]) uses this layout, in fp32.
+ *
+ * Conventions for every entry point
+ *  - Tensors are dense, row-major, last dimension fastest: q, k [B,H,T,d_k],
+ *    v, o [B,H,T,d_v]. Element type is `dtype` (fp32 or bf16) for q, k, v, o;
+ *    states are always fp32.
+ *  - All pointers are device pointers owned by the caller and 16-byte aligned.
+ *    The library never allocates device memory: scratch space is the caller's
+ *    `workspace`, sized by the matching *_workspace query.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *    the call returns without waiting. Results are valid once the stream has
+ *    reached that point.
+ *  - Argument errors are reported synchronously and nothing is launched:
+ *    KATA_EINVAL (null pointer, misalignment, negative size), KATA_EUNSUPPORTED
+ *    (shape outside the supported set), KATA_EWORKSPACE (workspace too small).
+ *    A failed launch returns KATA_EHIP.
+ *  - Supported shapes: d_k in {16, 32}; d_v in {16, 32, 64}; chunk in
+ *    {16, 32, 64, 128}; any T >= 0 (a ragged last chunk covers
+ *    [cC, min(cC+C, T))); B, H >= 0. Empty inputs launch nothing except the
+ *    state export. Inputs must be finite.
+ *  - Inputs and outputs must not overlap, except decode's S and z, which are
+ *    updated in place. The library keeps no global state and is thread-safe;
+ *    calls that share a workspace must be ordered on one stream.
+ */
+#ifndef KATA_H
+#define KATA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KATA_OK = 0,
+    KATA_EINVAL = 1,
+    KATA_EUNSUPPORTED = 2,
+    KATA_EWORKSPACE = 3,
+    KATA_EHIP = 4
+} kata_status_t;
+
+typedef enum { KATA_F32 = 0, KATA_BF16 = 1 } kata_dtype_t;
+
+/* Packed feature dimension D = d(d+1)/2 (the number of unique entries of the
+ * symmetric lift x x^T; explainer section 2.2). Returns -1 for d < 0. */
+int kata_phi_dim(int d);
+
+/* Human-readable name of a status code (static string). */
+const char* kata_status_string(kata_status_t status);
+
+/* Library version string, "major.minor.patch". */
+const char* kata_version(void);
+
+/* Bytes of workspace kata_chunked_fwd needs for this problem (0 if none).
+ * Returns 0 for unsupported or invalid shapes too; kata_chunked_fwd then
+ * reports the precise error. */
+size_t kata_chunked_fwd_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                  kata_dtype_t dtype, int causal);
+
+/* Chunked causal (or full, causal = 0) forward.
+ *   q, k [B,H,T,d_k]; v [B,H,T,d_v] (dtype) - inputs.
+ *   o [B,H,T,d_v] (dtype) - output, overwritten.
+ *   chunk - the chunk length C of the chunked-state form (section 2.3); the
+ *     intra-chunk term covers positions of one chunk, the inter-chunk term the
+ *     prefix state of all earlier chunks.
+ *   S0 [B,H,D,d_v], z0 [B,H,D] (fp32) - optional initial state standing for
+ *     tokens before position 0 (both NULL = zero state; one NULL = KATA_EINVAL).
+ *   S_out [B,H,D,d_v], z_out [B,H,D] (fp32) - optional final state S0 + phi(K)^T V
+ *     and z0 + phi(K)^T 1 (both NULL = not written; one NULL = KATA_EINVAL).
+ *   workspace, ws_bytes - device scratch of at least kata_chunked_fwd_workspace
+ *     bytes (may be NULL when that is 0).
+ * Output dtype equals input dtype. The mask is inclusive (position t sees j <= t):
+ * the explainers' output gate blends the previous readout with the current
+ * value (section 2.1). */
+kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, void* o,
+                               int B, int H, int T, int d_k, int d_v, int chunk, int causal,
+                               kata_dtype_t dtype,
+                               const float* S0, const float* z0,
+                               float* S_out, float* z_out,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/* kata_chunked_fwd with phase timing: identical work and results, and it also
+ * records events[0..3] (hipEvent_t, created by the caller) on `stream` at the
+ * phase boundaries - events[0] before the chunk-state phase, events[1] after it,
+ * events[2] after the inter-chunk scan, events[3] after the output phase - so a
+ * caller can time each phase with hipEventElapsedTime. n_events must be >= 4
+ * (else KATA_EINVAL); events after the fourth are ignored. */
+kata_status_t kata_chunked_fwd_profiled(const void* q, const void* k, const void* v, void* o,
+                                        int B, int H, int T, int d_k, int d_v, int chunk,
+                                        int causal, kata_dtype_t dtype,
+                                        const float* S0, const float* z0,
+                                        float* S_out, float* z_out,
+                                        void* workspace, size_t ws_bytes, void* stream,
+                                        void* const* events, int n_events);
+
+/* Bytes of workspace kata_scan_states needs (currently always 0). */
+size_t kata_scan_states_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                  kata_dtype_t dtype);
+
+/* Per-chunk states and their exclusive prefix (the associative scan over chunk
+ * states, section 2.3; operator +, identity S0 or 0).
+ *   k [B,H,T,d_k], v [B,H,T,d_v] (dtype) - inputs.
+ *   S_prefix [B,H,NC,D,d_v], z_prefix [B,H,NC,D] (fp32, NC = ceil(T/chunk)) -
+ *     output: entry c holds S0 + sum over chunks c' < c of phi(K_c')^T V_c'
+ *     (likewise z). Both required when NC > 0.
+ *   S0, z0 - optional initial state (as kata_chunked_fwd).
+ *   S_out, z_out - optional total state after the last chunk. */
+kata_status_t kata_scan_states(const void* k, const void* v,
+                               int B, int H, int T, int d_k, int d_v, int chunk,
+                               kata_dtype_t dtype,
+                               const float* S0, const float* z0,
+                               float* S_prefix, float* z_prefix,
+                               float* S_out, float* z_out,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/* One recurrent decode step for N independent (sequence, head) rows: the
+ * constant-time recurrent inference of the abstract, with a fixed-size state.
+ *   q, k [N,d_k]; v [N,d_v] (dtype) - the new token.
+ *   S [N,D,d_v], z [N,D] (fp32) - state, updated in place:
+ *     S += phi(k) v^T, z += phi(k).
+ *   o [N,d_v] (dtype) - output phi(q).S / phi(q).z, read after the update
+ *     (the token attends to itself), 0 when the denominator is 0. */
+kata_status_t kata_decode_step(const void* q, const void* k, const void* v,
+                               float* S, float* z, void* o,
+                               int N, int d_k, int d_v, kata_dtype_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KATA_H */

@@ -1,0 +1,13 @@
+"""KATA causal forward on MI355X (gfx950): Python front end of libkata.so.
+
+    import kernelized_linear_attention_phi_amd as kata
+    o = kata.chunked_fwd(q, k, v, chunk=64)                 # [B,H,T,d_v]
+    Sp, zp, S, z = kata.scan_states(k, v, chunk=64)         # per-chunk prefixes
+    o1 = kata.decode_step(q1, k1, v1, S, z)                 # one recurrent step
+
+The shared library is loaded on first use; calls raise if it is missing.
+"""
+from ._binding import (KataError, chunked_fwd, chunked_fwd_into, chunked_fwd_workspace,  # noqa: F401
+                       decode_step, lib, phi_dim, scan_states, LIB_PATH)
+
+__version__ = "0.1.0"

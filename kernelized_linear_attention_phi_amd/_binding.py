@@ -1,0 +1,194 @@
+"""ctypes binding of libkata.so: argument marshalling only.
+
+Torch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's kernels. There is no fallback: if the shared
+library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["KataError", "lib", "chunked_fwd", "chunked_fwd_into", "chunked_fwd_workspace",
+           "scan_states", "decode_step", "phi_dim", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkata.so")
+
+F32, BF16 = 0, 1
+_STATUS = {0: "KATA_OK", 1: "KATA_EINVAL", 2: "KATA_EUNSUPPORTED", 3: "KATA_EWORKSPACE", 4: "KATA_EHIP"}
+
+
+class KataError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_STATUS.get(status, status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loads it on first use; raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m kernelized_linear_attention_phi_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.kata_phi_dim.argtypes = [i]
+        L.kata_phi_dim.restype = i
+        L.kata_status_string.argtypes = [i]
+        L.kata_status_string.restype = ctypes.c_char_p
+        L.kata_version.restype = ctypes.c_char_p
+        L.kata_chunked_fwd_workspace.argtypes = [i, i, i, i, i, i, i, i]
+        L.kata_chunked_fwd_workspace.restype = sz
+        L.kata_chunked_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                       vp, vp, vp, vp, vp, sz, vp]
+        L.kata_chunked_fwd.restype = i
+        L.kata_chunked_fwd_profiled.argtypes = L.kata_chunked_fwd.argtypes + [
+            ctypes.POINTER(ctypes.c_void_p), i]
+        L.kata_chunked_fwd_profiled.restype = i
+        L.kata_scan_states_workspace.argtypes = [i, i, i, i, i, i, i]
+        L.kata_scan_states_workspace.restype = sz
+        L.kata_scan_states.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.kata_scan_states.restype = i
+        L.kata_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+        L.kata_decode_step.restype = i
+        _lib = L
+    return _lib
+
+
+def phi_dim(d: int) -> int:
+    return lib().kata_phi_dim(d)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _raise(st, what):
+    if st != 0:
+        raise KataError(st, what)
+
+
+def chunked_fwd_workspace(B, H, T, dk, dv, chunk, dtype_code, causal=True) -> int:
+    return lib().kata_chunked_fwd_workspace(B, H, T, dk, dv, chunk, dtype_code, int(bool(causal)))
+
+
+def chunked_fwd_into(q, k, v, o, chunk, causal, workspace, S0=None, z0=None, S_out=None,
+                     z_out=None, events=None):
+    """Raw call: every buffer preallocated by the caller (used by the benchmark).
+
+    events: optional sequence of 4 torch.cuda.Event recorded at the phase
+    boundaries (chunk states | scan | output) through kata_chunked_fwd_profiled.
+    """
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, T, dk, dv, chunk, int(bool(causal)),
+            _dtype_code(q), _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(workspace),
+            ws_bytes, _stream())
+    if events is None:
+        st = lib().kata_chunked_fwd(*args)
+    else:
+        arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        st = lib().kata_chunked_fwd_profiled(*args, arr, len(events))
+    _raise(st, "kata_chunked_fwd")
+
+
+def chunked_fwd(q, k, v, chunk=64, causal=True, initial_state=None, return_state=False):
+    """o = KATA forward of q, k [B,H,T,d_k], v [B,H,T,d_v] (fp32 or bf16).
+
+    initial_state: optional (S0 [B,H,D,d_v], z0 [B,H,D]) fp32.
+    return_state: also return the final (S, z).
+    """
+    _check_dev(q, k, v)
+    if q.dim() != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("expected q, k [B,H,T,d_k] and v [B,H,T,d_v]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    D = phi_dim(dk)
+    S0 = z0 = S_out = z_out = None
+    if initial_state is not None:
+        S0, z0 = initial_state
+        _check_dev(S0, z0)
+        if S0.dtype != torch.float32 or z0.dtype != torch.float32:
+            raise TypeError("states are float32")
+        if tuple(S0.shape) != (B, H, D, dv) or tuple(z0.shape) != (B, H, D):
+            raise ValueError("initial state shape mismatch")
+    if return_state:
+        S_out = torch.empty((B, H, D, dv), dtype=torch.float32, device=q.device)
+        z_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    o = torch.empty_like(v)
+    nbytes = chunked_fwd_workspace(B, H, T, dk, dv, chunk, _dtype_code(q), causal)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if nbytes else None
+    chunked_fwd_into(q, k, v, o, chunk, causal, ws, S0, z0, S_out, z_out)
+    return (o, (S_out, z_out)) if return_state else o
+
+
+def scan_states(k, v, chunk=64, initial_state=None):
+    """Per-chunk exclusive prefix states and the final state.
+
+    Returns (S_prefix [B,H,NC,D,d_v], z_prefix [B,H,NC,D], S_T, z_T), fp32.
+    """
+    _check_dev(k, v)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    D = phi_dim(dk)
+    NC = -(-T // chunk)
+    S0 = z0 = None
+    if initial_state is not None:
+        S0, z0 = initial_state
+        _check_dev(S0, z0)
+    dev = k.device
+    Sp = torch.empty((B, H, NC, D, dv), dtype=torch.float32, device=dev)
+    zp = torch.empty((B, H, NC, D), dtype=torch.float32, device=dev)
+    ST = torch.empty((B, H, D, dv), dtype=torch.float32, device=dev)
+    zT = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    nbytes = lib().kata_scan_states_workspace(B, H, T, dk, dv, chunk, _dtype_code(k))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    st = lib().kata_scan_states(_ptr(k), _ptr(v), B, H, T, dk, dv, chunk, _dtype_code(k),
+                                _ptr(S0), _ptr(z0), _ptr(Sp), _ptr(zp), _ptr(ST), _ptr(zT),
+                                _ptr(ws), nbytes, _stream())
+    _raise(st, "kata_scan_states")
+    return Sp, zp, ST, zT
+
+
+def decode_step(q, k, v, S, z, out=None):
+    """One decode step for rows [N, d]: updates S [N,D,d_v], z [N,D] in place,
+    returns o [N, d_v]."""
+    _check_dev(q, k, v, S, z)
+    N, dk = q.shape
+    dv = v.shape[-1]
+    o = torch.empty_like(v) if out is None else out
+    st = lib().kata_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(o), N, dk, dv,
+                                _dtype_code(q), _stream())
+    _raise(st, "kata_decode_step")
+    return o

@@ -1,0 +1,226 @@
+// C ABI of the KATA library: argument checking, workspace planning and launch
+// orchestration. Every kernel runs on the caller's stream; nothing here
+// allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kata.h"
+#include "kata_internal.h"
+
+namespace {
+
+using kata::Shape;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_dk(int d) { return d == 16 || d == 32; }
+bool supported_dv(int d) { return d == 16 || d == 32 || d == 64; }
+bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Checks sizes and the shape set; fills s.
+kata_status_t make_shape(int B, int H, int T, int dk, int dv, int C, kata_dtype_t dt, Shape* s) {
+    if (B < 0 || H < 0 || T < 0 || dk < 0 || dv < 0 || C <= 0) return KATA_EINVAL;
+    if (dt != KATA_F32 && dt != KATA_BF16) return KATA_EINVAL;
+    if (!supported_dk(dk) || !supported_dv(dv) || !supported_chunk(C)) return KATA_EUNSUPPORTED;
+    // indices are 64-bit in the kernels; keep grid dimensions in range
+    if ((int64_t)B * H > 65535 || T > (1 << 28)) return KATA_EUNSUPPORTED;
+    s->B = B; s->H = H; s->T = T; s->dk = dk; s->dv = dv; s->C = C;
+    s->D = dk * (dk + 1) / 2;
+    s->NC = (T + C - 1) / C;
+    s->bf16 = dt == KATA_BF16;
+    return KATA_OK;
+}
+
+// Workspace of the fp32 VALU forward: per-chunk records (causal) or one total
+// record per head (non-causal).
+struct FwdPlan {
+    size_t S_off, z_off, bytes;
+    int NR;
+};
+
+FwdPlan plan_fwd(const Shape& s, int causal) {
+    FwdPlan p{};
+    const size_t BH = (size_t)s.B * s.H;
+    p.NR = causal ? s.NC : 1;
+    // non-causal also needs the per-chunk totals before reducing them
+    const size_t nrec = BH * (size_t)s.NC + (causal ? 0 : BH);
+    p.S_off = 0;
+    p.z_off = align256(nrec * s.D * s.dv * sizeof(float));
+    p.bytes = p.z_off + align256(nrec * s.D * sizeof(float));
+    if (BH == 0 || s.NC == 0) p.bytes = 0;
+    return p;
+}
+
+kata_status_t hip_status(hipError_t e) { return e == hipSuccess ? KATA_OK : KATA_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int kata_phi_dim(int d) { return d < 0 ? -1 : d * (d + 1) / 2; }
+
+const char* kata_status_string(kata_status_t st) {
+    switch (st) {
+        case KATA_OK: return "ok";
+        case KATA_EINVAL: return "invalid argument";
+        case KATA_EUNSUPPORTED: return "unsupported shape";
+        case KATA_EWORKSPACE: return "workspace too small";
+        case KATA_EHIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+const char* kata_version(void) { return "0.1.0"; }
+
+size_t kata_chunked_fwd_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                  kata_dtype_t dtype, int causal) {
+    Shape s;
+    if (make_shape(B, H, T, d_k, d_v, chunk, dtype, &s) != KATA_OK) return 0;
+    return plan_fwd(s, causal).bytes;
+}
+
+static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* v, void* o,
+                                      int B, int H, int T, int d_k, int d_v, int chunk,
+                                      int causal, kata_dtype_t dtype, const float* S0,
+                                      const float* z0, float* S_out, float* z_out,
+                                      void* workspace, size_t ws_bytes, void* stream,
+                                      void* const* events) {
+    Shape s;
+    kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s);
+    if (st != KATA_OK) return st;
+    if ((S0 == nullptr) != (z0 == nullptr)) return KATA_EINVAL;
+    if ((S_out == nullptr) != (z_out == nullptr)) return KATA_EINVAL;
+    const size_t BH = (size_t)B * H;
+    const bool empty = BH == 0 || T == 0;
+    if (!empty && (!q || !k || !v || !o)) return KATA_EINVAL;
+    for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)o,
+                          (const void*)S0, (const void*)z0, (const void*)S_out,
+                          (const void*)z_out, (const void*)workspace})
+        if (p && !aligned16(p)) return KATA_EINVAL;
+    const FwdPlan plan = plan_fwd(s, causal);
+    if (ws_bytes < plan.bytes || (plan.bytes && !workspace)) return KATA_EWORKSPACE;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const size_t nS = (size_t)s.D * s.dv, nz = s.D;
+    auto mark = [&](int i) -> hipError_t {
+        return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) : hipSuccess;
+    };
+
+    if (empty) {
+        hipError_t e = mark(0);
+        if (e == hipSuccess) e = mark(1);
+        if (e == hipSuccess) e = mark(2);
+        if (S_out) {
+            if (e == hipSuccess) e = kata::launch_copy_or_zero(S_out, S0, BH * nS, hs);
+            if (e == hipSuccess) e = kata::launch_copy_or_zero(z_out, z0, BH * nz, hs);
+        }
+        if (e == hipSuccess) e = mark(3);
+        return hip_status(e);
+    }
+
+    char* ws = static_cast<char*>(workspace);
+    float* S_rec = reinterpret_cast<float*>(ws + plan.S_off);
+    float* z_rec = reinterpret_cast<float*>(ws + plan.z_off);
+    hipError_t e = mark(0);
+    if (e == hipSuccess) e = kata::launch_chunk_states_valu(s, k, v, S_rec, z_rec, hs);
+    if (e == hipSuccess) e = mark(1);
+    if (causal) {
+        // exclusive prefix over chunks in place; inclusive total -> final state
+        if (e == hipSuccess)
+            e = kata::launch_scan_records(S_rec, (int)BH, s.NC, (int)nS, S0, S_out, nullptr, hs);
+        if (e == hipSuccess)
+            e = kata::launch_scan_records(z_rec, (int)BH, s.NC, (int)nz, z0, z_out, nullptr, hs);
+        if (e == hipSuccess) e = mark(2);
+        if (e == hipSuccess) e = kata::launch_fwd_valu(s, q, k, v, S_rec, z_rec, o, 1, hs);
+    } else {
+        // total state per head, stored after the per-chunk records
+        float* S_tot = S_rec + BH * s.NC * nS;
+        float* z_tot = z_rec + BH * s.NC * nz;
+        if (e == hipSuccess)
+            e = kata::launch_scan_records(S_rec, (int)BH, s.NC, (int)nS, S0, S_tot, S_out, hs);
+        if (e == hipSuccess)
+            e = kata::launch_scan_records(z_rec, (int)BH, s.NC, (int)nz, z0, z_tot, z_out, hs);
+        if (e == hipSuccess) e = mark(2);
+        if (e == hipSuccess) e = kata::launch_fwd_valu(s, q, k, v, S_tot, z_tot, o, 0, hs);
+    }
+    if (e == hipSuccess) e = mark(3);
+    return hip_status(e);
+}
+
+kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, void* o,
+                               int B, int H, int T, int d_k, int d_v, int chunk, int causal,
+                               kata_dtype_t dtype, const float* S0, const float* z0,
+                               float* S_out, float* z_out, void* workspace, size_t ws_bytes,
+                               void* stream) {
+    return chunked_fwd_impl(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, S0, z0, S_out,
+                            z_out, workspace, ws_bytes, stream, nullptr);
+}
+
+kata_status_t kata_chunked_fwd_profiled(const void* q, const void* k, const void* v, void* o,
+                                        int B, int H, int T, int d_k, int d_v, int chunk,
+                                        int causal, kata_dtype_t dtype, const float* S0,
+                                        const float* z0, float* S_out, float* z_out,
+                                        void* workspace, size_t ws_bytes, void* stream,
+                                        void* const* events, int n_events) {
+    if (!events || n_events < 4) return KATA_EINVAL;
+    for (int i = 0; i < 4; ++i)
+        if (!events[i]) return KATA_EINVAL;
+    return chunked_fwd_impl(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, S0, z0, S_out,
+                            z_out, workspace, ws_bytes, stream, events);
+}
+
+size_t kata_scan_states_workspace(int, int, int, int, int, int, kata_dtype_t) { return 0; }
+
+kata_status_t kata_scan_states(const void* k, const void* v, int B, int H, int T, int d_k,
+                               int d_v, int chunk, kata_dtype_t dtype, const float* S0,
+                               const float* z0, float* S_prefix, float* z_prefix, float* S_out,
+                               float* z_out, void* workspace, size_t ws_bytes, void* stream) {
+    (void)workspace;
+    (void)ws_bytes;
+    Shape s;
+    kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s);
+    if (st != KATA_OK) return st;
+    if ((S0 == nullptr) != (z0 == nullptr)) return KATA_EINVAL;
+    if ((S_out == nullptr) != (z_out == nullptr)) return KATA_EINVAL;
+    const size_t BH = (size_t)B * H;
+    const bool empty = BH == 0 || T == 0;
+    if (!empty && (!k || !v || !S_prefix || !z_prefix)) return KATA_EINVAL;
+    for (const void* p : {(const void*)k, (const void*)v, (const void*)S0, (const void*)z0,
+                          (const void*)S_prefix, (const void*)z_prefix, (const void*)S_out,
+                          (const void*)z_out})
+        if (p && !aligned16(p)) return KATA_EINVAL;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const size_t nS = (size_t)s.D * s.dv, nz = s.D;
+    if (empty) {
+        if (S_out) {
+            hipError_t e = kata::launch_copy_or_zero(S_out, S0, BH * nS, hs);
+            if (e == hipSuccess) e = kata::launch_copy_or_zero(z_out, z0, BH * nz, hs);
+            return hip_status(e);
+        }
+        return KATA_OK;
+    }
+    hipError_t e = kata::launch_chunk_states_valu(s, k, v, S_prefix, z_prefix, hs);
+    if (e == hipSuccess)
+        e = kata::launch_scan_records(S_prefix, (int)BH, s.NC, (int)nS, S0, S_out, nullptr, hs);
+    if (e == hipSuccess)
+        e = kata::launch_scan_records(z_prefix, (int)BH, s.NC, (int)nz, z0, z_out, nullptr, hs);
+    return hip_status(e);
+}
+
+kata_status_t kata_decode_step(const void* q, const void* k, const void* v, float* S, float* z,
+                               void* o, int N, int d_k, int d_v, kata_dtype_t dtype,
+                               void* stream) {
+    if (N < 0 || d_k < 0 || d_v < 0) return KATA_EINVAL;
+    if (dtype != KATA_F32 && dtype != KATA_BF16) return KATA_EINVAL;
+    if (!supported_dk(d_k) || !supported_dv(d_v)) return KATA_EUNSUPPORTED;
+    if (N == 0) return KATA_OK;
+    if (!q || !k || !v || !S || !z || !o) return KATA_EINVAL;
+    for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)S,
+                          (const void*)z, (const void*)o})
+        if (!aligned16(p)) return KATA_EINVAL;
+    return hip_status(kata::launch_decode(q, k, v, S, z, o, N, d_k, d_v, dtype == KATA_BF16,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

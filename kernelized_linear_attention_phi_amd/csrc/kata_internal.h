@@ -1,0 +1,47 @@
+// Host-side launchers of the KATA kernels. Each returns hipSuccess or the
+// launch error; argument checking happens in kata_api.cpp before any call.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace kata {
+
+struct Shape {
+    int B, H, T, dk, dv, C;
+    int D;    // dk * (dk + 1) / 2
+    int NC;   // ceil(T / C)
+    bool bf16;
+};
+
+// ---- fp32 VALU path (any supported shape; fp32 or bf16 inputs, fp32 math) ----
+
+// Per-chunk totals phi(K_c)^T V_c and phi(K_c)^T 1 in packed layout:
+// S_rec [BH, NC, D, dv], z_rec [BH, NC, D].
+hipError_t launch_chunk_states_valu(const Shape& s, const void* k, const void* v,
+                                    float* S_rec, float* z_rec, hipStream_t st);
+
+// Chunked forward reading per-chunk exclusive prefixes (causal) or one total
+// state per head (non-causal: S_rec [BH, D, dv], z_rec [BH, D]).
+hipError_t launch_fwd_valu(const Shape& s, const void* q, const void* k, const void* v,
+                           const float* S_rec, const float* z_rec, void* o, int causal,
+                           hipStream_t st);
+
+// ---- associative scan over records (layout-agnostic, fp32) ----
+
+// For each of `nseq` independent sequences of NR records of E floats (record r
+// of sequence b at rec + (b*NR + r)*E): replaces every record by the exclusive
+// prefix sum init_b + sum_{r' < r} rec_{r'} (init = 0 when NULL; init_b at
+// init + b*E). Writes the inclusive total of every sequence to total_a and/or
+// total_b (each NULL or E floats per sequence).
+hipError_t launch_scan_records(float* rec, int nseq, int NR, int E, const float* init,
+                               float* total_a, float* total_b, hipStream_t st);
+
+// Copies (src != NULL) or zero-fills n floats.
+hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st);
+
+// ---- decode ----
+hipError_t launch_decode(const void* q, const void* k, const void* v, float* S, float* z,
+                         void* o, int N, int dk, int dv, bool bf16, hipStream_t st);
+
+}  // namespace kata

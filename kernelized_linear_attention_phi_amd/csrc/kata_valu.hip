@@ -1,0 +1,154 @@
+// fp32 VALU chunked-state path: every product and sum in fp32 on the vector
+// ALUs. It serves fp32 inputs (whose tolerance a bf16 matrix-core operand would
+// exceed) and stands as the general-shape path.
+//
+// Chunked-state form (KATA explainers, gist.science, technical summary 2.3):
+// chunk c covers positions [cC, min(cC+C, T)); its output is the masked
+// intra-chunk term plus phi(Q_c) times the exclusive prefix of chunk states.
+#include "kata_device.h"
+#include "kata_internal.h"
+
+namespace kata {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxC = 128;
+constexpr int kMaxDk = 32;
+constexpr int kMaxDv = 64;
+constexpr int kMaxD = kMaxDk * (kMaxDk + 1) / 2;
+
+// S_c = phi(K_c)^T V_c, z_c = phi(K_c)^T 1 for one (head, chunk) per block.
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void chunk_states_valu(
+    const TIn* __restrict__ k, const TIn* __restrict__ v, float* __restrict__ S_rec,
+    float* __restrict__ z_rec, int T, int dk, int dv, int C, int NC) {
+    __shared__ float ks[kMaxC * kMaxDk];
+    __shared__ float vs[kMaxC * kMaxDv];
+    __shared__ uint32_t pairs[kMaxD];
+    const int c = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int D = dk * (dk + 1) / 2;
+    const int t0 = c * C;
+    const int n = min(C, T - t0);
+    const TIn* kb = k + (bh * T + t0) * dk;
+    const TIn* vb = v + (bh * T + t0) * dv;
+    for (int e = threadIdx.x; e < n * dk; e += kThreads) ks[e] = io<TIn>::ld(kb, e);
+    for (int e = threadIdx.x; e < n * dv; e += kThreads) vs[e] = io<TIn>::ld(vb, e);
+    fill_pair_table(pairs, dk, D);
+    __syncthreads();
+    const size_t rec = bh * NC + c;
+    float* Sr = S_rec + rec * D * dv;
+    float* zr = z_rec + rec * D;
+    for (int e = threadIdx.x; e < D * dv + D; e += kThreads) {
+        const bool is_z = e >= D * dv;
+        const int p = is_z ? e - D * dv : e / dv;
+        const int col = is_z ? 0 : e % dv;
+        const int i = pairs[p] & 0xff, j = pairs[p] >> 8;
+        const float sc = i == j ? 1.0f : kSqrt2;
+        float acc = 0.0f;
+        for (int t = 0; t < n; ++t) {
+            const float f = sc * (ks[t * dk + i] * ks[t * dk + j]);
+            acc += is_z ? f : f * vs[t * dv + col];
+        }
+        if (is_z) zr[p] = acc; else Sr[e] = acc;
+    }
+}
+
+// o for one (head, chunk): inter term phi(q_t).P_c plus the intra term over the
+// chunk's positions j <= t, normalised. Non-causal: P is the total state of the
+// head and there is no intra term.
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void fwd_valu(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const float* __restrict__ S_rec, const float* __restrict__ z_rec, TIn* __restrict__ o,
+    int T, int dk, int dv, int C, int NC, int causal) {
+    __shared__ float qs[kMaxC * kMaxDk];
+    __shared__ float ks[kMaxC * kMaxDk];
+    __shared__ float vs[kMaxC * kMaxDv];
+    __shared__ uint32_t pairs[kMaxD];
+    const int c = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int D = dk * (dk + 1) / 2;
+    const int t0 = c * C;
+    const int n = min(C, T - t0);
+    const TIn* qb = q + (bh * T + t0) * dk;
+    const TIn* kb = k + (bh * T + t0) * dk;
+    const TIn* vb = v + (bh * T + t0) * dv;
+    for (int e = threadIdx.x; e < n * dk; e += kThreads) {
+        qs[e] = io<TIn>::ld(qb, e);
+        ks[e] = io<TIn>::ld(kb, e);
+    }
+    for (int e = threadIdx.x; e < n * dv; e += kThreads) vs[e] = io<TIn>::ld(vb, e);
+    fill_pair_table(pairs, dk, D);
+    __syncthreads();
+
+    const size_t rec = causal ? bh * NC + c : bh;
+    const float* P = S_rec + rec * D * dv;
+    const float* Z = z_rec + rec * D;
+    const int tpc = kThreads / C;              // threads per position
+    const int t = threadIdx.x / tpc;
+    const int g = threadIdx.x % tpc;
+    if (t >= n) return;
+    constexpr int kMaxCols = kMaxDv;           // dv / tpc <= 32 for C <= 128
+    float num[kMaxCols / 2];
+    const int ncols = (dv + tpc - 1) / tpc;
+#pragma unroll
+    for (int u = 0; u < kMaxCols / 2; ++u) num[u] = 0.0f;
+    float den = 0.0f;
+    const float* qt = qs + t * dk;
+    for (int p = 0; p < D; ++p) {
+        const int i = pairs[p] & 0xff, j = pairs[p] >> 8;
+        const float fq = (i == j ? 1.0f : kSqrt2) * (qt[i] * qt[j]);
+        den += fq * Z[p];
+#pragma unroll
+        for (int u = 0; u < kMaxCols / 2; ++u)
+            if (u < ncols && g + u * tpc < dv) num[u] += fq * P[p * dv + g + u * tpc];
+    }
+    if (causal) {
+        for (int jj = 0; jj <= t; ++jj) {
+            float s = 0.0f;
+            for (int i = 0; i < dk; ++i) s += qt[i] * ks[jj * dk + i];
+            const float w = s * s;
+            den += w;
+#pragma unroll
+            for (int u = 0; u < kMaxCols / 2; ++u)
+                if (u < ncols && g + u * tpc < dv) num[u] += w * vs[jj * dv + g + u * tpc];
+        }
+    }
+    TIn* ob = o + (bh * T + t0 + t) * dv;
+#pragma unroll
+    for (int u = 0; u < kMaxCols / 2; ++u)
+        if (u < ncols && g + u * tpc < dv) io<TIn>::st(ob, g + u * tpc, safe_div(num[u], den));
+}
+
+}  // namespace
+
+hipError_t launch_chunk_states_valu(const Shape& s, const void* k, const void* v,
+                                    float* S_rec, float* z_rec, hipStream_t st) {
+    dim3 grid(s.NC, s.B * s.H);
+    if (s.bf16)
+        chunk_states_valu<bf16_t><<<grid, kThreads, 0, st>>>(
+            (const bf16_t*)k, (const bf16_t*)v, S_rec, z_rec, s.T, s.dk, s.dv, s.C, s.NC);
+    else
+        chunk_states_valu<float><<<grid, kThreads, 0, st>>>(
+            (const float*)k, (const float*)v, S_rec, z_rec, s.T, s.dk, s.dv, s.C, s.NC);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_valu(const Shape& s, const void* q, const void* k, const void* v,
+                           const float* S_rec, const float* z_rec, void* o, int causal,
+                           hipStream_t st) {
+    dim3 grid(s.NC, s.B * s.H);
+    if (s.bf16)
+        fwd_valu<bf16_t><<<grid, kThreads, 0, st>>>(
+            (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, S_rec, z_rec, (bf16_t*)o,
+            s.T, s.dk, s.dv, s.C, s.NC, causal);
+    else
+        fwd_valu<float><<<grid, kThreads, 0, st>>>(
+            (const float*)q, (const float*)k, (const float*)v, S_rec, z_rec, (float*)o,
+            s.T, s.dk, s.dv, s.C, s.NC, causal);
+    return hipGetLastError();
+}
+
+}  // namespace kata

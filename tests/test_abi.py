@@ -1,0 +1,102 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/kata.h, and rejects bad arguments before launching."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "kata.h")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+FAKE = 0x10000            # aligned, never dereferenced: every call below fails first
+MISALIGNED = 0x10008
+
+
+@pytest.fixture(scope="module")
+def L():
+    from kernelized_linear_attention_phi_amd import lib
+    return lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kata_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"kata_chunked_fwd", "kata_scan_states", "kata_decode_step"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in kata.h but not exported"
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_helpers(L):
+    assert L.kata_phi_dim(16) == 136 and L.kata_phi_dim(32) == 528 and L.kata_phi_dim(-1) == -1
+    for s, txt in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported shape"),
+                   (3, b"workspace too small"), (4, b"HIP launch error")]:
+        assert L.kata_status_string(s) == txt
+    assert re.fullmatch(rb"\d+\.\d+\.\d+", L.kata_version())
+
+
+def fwd(L, B=1, H=1, T=64, dk=16, dv=64, C=64, causal=1, dtype=BF16, q=FAKE, S0=None, z0=None,
+        S_out=None, z_out=None, ws=FAKE, ws_bytes=1 << 40, o=FAKE):
+    return L.kata_chunked_fwd(q, FAKE, FAKE, o, B, H, T, dk, dv, C, causal, dtype, S0, z0,
+                              S_out, z_out, ws, ws_bytes, None)
+
+
+def test_fwd_rejects_before_launch(L):
+    assert fwd(L, dk=24) == EUNSUPPORTED
+    assert fwd(L, dv=48) == EUNSUPPORTED
+    assert fwd(L, C=48) == EUNSUPPORTED
+    assert fwd(L, C=0) == EINVAL
+    assert fwd(L, T=-1) == EINVAL
+    assert fwd(L, B=-2) == EINVAL
+    assert fwd(L, dtype=7) == EINVAL
+    assert fwd(L, q=None) == EINVAL
+    assert fwd(L, q=MISALIGNED) == EINVAL
+    assert fwd(L, S0=FAKE) == EINVAL              # S0 without z0
+    assert fwd(L, S_out=FAKE) == EINVAL           # S_out without z_out
+    assert fwd(L, ws_bytes=16) == EWORKSPACE
+    assert fwd(L, ws=None) == EWORKSPACE
+    # empty problems launch nothing
+    assert fwd(L, T=0, q=None, o=None, ws=None, ws_bytes=0) == OK
+    assert fwd(L, B=0, q=None, o=None, ws=None, ws_bytes=0) == OK
+
+
+def test_workspace_query(L):
+    for args in [(1, 8, 131072, 16, 64, 64, BF16, 1), (1, 16, 32768, 32, 64, 128, BF16, 1),
+                 (1, 1, 256, 16, 16, 64, F32, 1), (2, 3, 100, 16, 64, 32, BF16, 0)]:
+        n = L.kata_chunked_fwd_workspace(*args)
+        assert n > 0 and n % 256 == 0
+    assert L.kata_chunked_fwd_workspace(1, 1, 0, 16, 64, 64, BF16, 1) == 0
+    assert L.kata_chunked_fwd_workspace(1, 1, 64, 17, 64, 64, BF16, 1) == 0
+
+
+def test_scan_and_decode_reject(L):
+    sc = L.kata_scan_states
+    assert sc(FAKE, FAKE, 1, 1, 64, 16, 64, 64, BF16, None, None, None, FAKE, None, None,
+              None, 0, None) == EINVAL                       # S_prefix missing
+    assert sc(FAKE, FAKE, 1, 1, 64, 20, 64, 64, BF16, None, None, FAKE, FAKE, None, None,
+              None, 0, None) == EUNSUPPORTED
+    assert sc(None, None, 1, 1, 0, 16, 64, 64, BF16, None, None, None, None, None, None,
+              None, 0, None) == OK
+    dec = L.kata_decode_step
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 12, 64, BF16, None) == EUNSUPPORTED
+    assert dec(FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 16, 64, BF16, None) == EINVAL
+    assert dec(FAKE, FAKE, FAKE, MISALIGNED, FAKE, FAKE, 4, 16, 64, BF16, None) == EINVAL
+    assert dec(None, None, None, None, None, None, 0, 16, 64, BF16, None) == OK
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 16, 64, BF16, None) == EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import kernelized_linear_attention_phi_amd._binding as b
+    monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(b, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        b.lib()

@@ -1,0 +1,90 @@
+"""Parity at the benchmark's full sizes, in the launch configuration the
+benchmark times: sampled rows against the brute-force oracle (computed one row
+at a time), plus properties that hold at any size (convexity, finiteness)."""
+import numpy as np
+import pytest
+
+import oracle as O
+from kernelized_linear_attention_phi_amd import inputs as gen
+from tests.gpu_util import dev, host, row_rel_err, sample_rows, say, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kata():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kernelized_linear_attention_phi_amd as k
+    k.lib()
+    return k
+
+
+def _convex_ok(o, v, tol):
+    lo = np.minimum.accumulate(v, axis=2)
+    hi = np.maximum.accumulate(v, axis=2)
+    scale = np.maximum(np.abs(v).max(axis=(2, 3), keepdims=True), 1e-30)
+    return np.all(o >= lo - tol * scale) and np.all(o <= hi + tol * scale)
+
+
+@pytest.mark.parametrize("name", ["fwd4k", "fwd32k", "fwd131k", "recall16k"])
+def test_fullsize_sampled(kata, name):
+    import torch
+    w, q, k, v, _ = workload_inputs(name)
+    say(f"full size {name}: B{w.B} H{w.H} T{w.T} dk{w.dk} dv{w.dv} C{w.chunk}")
+    o_t = kata.chunked_fwd(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), chunk=w.chunk)
+    torch.cuda.synchronize()
+    o = host(o_t)
+    assert np.all(np.isfinite(o))
+    rows = sample_rows(w.T, w.chunk)
+    ref = O.brute_force_rows(q, k, v, rows)
+    err = row_rel_err(o[:, :, rows], ref)
+    say(f"  {name} sampled rows={rows.size} max row-rel err={err:.3e}")
+    assert err <= w.tol
+    assert _convex_ok(o, v.astype(np.float64), w.tol)
+
+
+def test_fullsize_decode(kata):
+    """Recall stream -> final states -> 1024 decode steps on 512 x 4 rows."""
+    import torch
+    w, q, k, v, g = workload_inputs("recall16k")
+    say("decode: stream forward with state export")
+    _, (S, z) = kata.chunked_fwd(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype),
+                                 chunk=w.chunk, return_state=True)
+    torch.cuda.synchronize()
+    dq, dk, dv, src = gen.decode_continuation(g, w.H, gen.DECODE_SEQS, gen.DECODE_STEPS, seed=5000)
+    N = gen.DECODE_SEQS * w.H
+    S_all = S.reshape(w.B * w.H, *S.shape[2:])[torch.as_tensor(src, device="cuda")].contiguous()
+    z_all = z.reshape(w.B * w.H, -1)[torch.as_tensor(src, device="cuda")].contiguous()
+    S_host0 = host(S_all).astype(np.float32)
+    z_host0 = host(z_all).astype(np.float32)
+    dq_t, dk_t, dv_t = (dev(a.reshape(gen.DECODE_STEPS, N, -1), w.dtype) for a in (dq, dk, dv))
+    outs = []
+    say("decode: 1024 steps")
+    for t in range(gen.DECODE_STEPS):
+        outs.append(kata.decode_step(dq_t[t], dk_t[t], dv_t[t], S_all, z_all))
+        if t == 0:
+            torch.cuda.synchronize()
+            o_ref, _, _ = O.decode_step(dq.reshape(gen.DECODE_STEPS, N, -1)[0],
+                                        dk.reshape(gen.DECODE_STEPS, N, -1)[0],
+                                        dv.reshape(gen.DECODE_STEPS, N, -1)[0], S_host0, z_host0)
+            assert row_rel_err(host(outs[0]), o_ref) <= 2 ** -8
+    torch.cuda.synchronize()
+    o_all = np.stack([host(x) for x in outs])           # [steps, N, dv]
+    assert np.all(np.isfinite(o_all))
+    # sampled rows: brute force over the stream prefix and the decode tokens
+    qf = q.reshape(w.B * w.H, w.T, -1)
+    kf = k.reshape(w.B * w.H, w.T, -1)
+    vf = v.reshape(w.B * w.H, w.T, -1)
+    r = np.random.Generator(np.random.PCG64(1))
+    for row in [0, 1, N - 1] + [int(x) for x in r.integers(0, N, 5)]:
+        b = src[row]
+        s, h = divmod(row, w.H)
+        qq = np.concatenate([qf[b], dq[:, s, h]])[None, None]
+        kk = np.concatenate([kf[b], dk[:, s, h]])[None, None]
+        vv = np.concatenate([vf[b], dv[:, s, h]])[None, None]
+        steps = np.arange(w.T, w.T + gen.DECODE_STEPS)
+        ref = O.brute_force_rows(qq, kk, vv, steps)[0, 0]
+        err = row_rel_err(o_all[:, row], ref)
+        assert err <= w.tol, (row, err)

@@ -1,0 +1,226 @@
+"""GPU parity of the C-ABI path against the float64 oracle.
+
+Tolerances (max row-normwise relative error, see gpu_util.row_rel_err): 1e-4 for
+fp32 inputs, 2e-2 for bf16 inputs with fp32 accumulation. Index logic (chunk
+boundaries, masks, prefixes) is checked bit-exactly: bitwise causality under
+perturbation of a future token, and exact integer probes.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from kernelized_linear_attention_phi_amd import inputs as gen
+from tests.gpu_util import dev, host, row_rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def kata():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kernelized_linear_attention_phi_amd as k
+    k.lib()
+    return k
+
+
+def run_fwd(kata, q, k, v, dtype, C, causal=True, S0=None, z0=None, state=False):
+    import torch
+    init = None if S0 is None else (dev(S0), dev(z0))
+    out = kata.chunked_fwd(dev(q, dtype), dev(k, dtype), dev(v, dtype), chunk=C, causal=causal,
+                           initial_state=init, return_state=state)
+    torch.cuda.synchronize()
+    if state:
+        o, (S, z) = out
+        return host(o), host(S), host(z)
+    return host(out)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (16, 64), (32, 64), (32, 32)])
+@pytest.mark.parametrize("C", [16, 32, 64, 128])
+def test_fwd_small_full(kata, dtype, dk, dv, C):
+    """Several tiles and a ragged tail; every output compared."""
+    B, H, T = 2, 3, 1000
+    q, k, v = gen.gaussian_qkv(B, H, T, dk, dv, seed=100 + dk + dv + C, dtype=dtype)
+    say(f"fwd_small dtype={dtype} dk={dk} dv={dv} C={C} T={T}")
+    o, S, z = run_fwd(kata, q, k, v, dtype, C, state=True)
+    ref = O.brute_force(q, k, v)
+    assert row_rel_err(o, ref) <= TOL[dtype]
+    S_ref, z_ref = O.state_from_tokens(k, v)
+    assert row_rel_err(S, S_ref) <= 1e-5
+    assert row_rel_err(z[..., None], z_ref[..., None]) <= 1e-5
+
+
+def test_tiny_fp32_workload(kata):
+    w, q, k, v, _ = _inputs("tiny")
+    say("tiny workload fp32")
+    o = run_fwd(kata, q, k, v, w.dtype, w.chunk)
+    assert row_rel_err(o, O.brute_force(q, k, v)) <= w.tol
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 7, 63, 64, 65, 129, 200])
+def test_ragged_and_short(kata, dtype, T):
+    q, k, v = gen.gaussian_qkv(1, 2, T, 16, 64, seed=200 + T, dtype=dtype)
+    say(f"ragged dtype={dtype} T={T}")
+    o = run_fwd(kata, q, k, v, dtype, 64)
+    assert row_rel_err(o, O.brute_force(q, k, v)) <= TOL[dtype]
+    if T == 1:
+        assert np.array_equal(o, v.astype(np.float64))     # single token: o = v exactly
+
+
+def test_empty_sequence_returns_initial_state(kata):
+    import torch
+    q = torch.zeros((1, 2, 0, 16), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((1, 2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    S0 = torch.randn((1, 2, 136, 64), device="cuda")
+    z0 = torch.rand((1, 2, 136), device="cuda")
+    say("empty sequence")
+    o, (S, z) = kata.chunked_fwd(q, q, v, chunk=64, initial_state=(S0, z0), return_state=True)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 2, 0, 64)
+    assert torch.equal(S, S0) and torch.equal(z, z0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_noncausal(kata, dtype):
+    q, k, v = gen.gaussian_qkv(2, 2, 333, 16, 64, seed=7, dtype=dtype)
+    say(f"noncausal {dtype}")
+    o = run_fwd(kata, q, k, v, dtype, 64, causal=False)
+    assert row_rel_err(o, O.brute_force(q, k, v, causal=False)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,C", [(16, 64), (32, 128), (16, 16)])
+def test_bitwise_causality(kata, dtype, dk, C):
+    """Perturbing token j leaves every output before j bit-identical."""
+    T = 4 * C + 37
+    q, k, v = gen.gaussian_qkv(1, 2, T, dk, 64, seed=300 + C, dtype=dtype)
+    say(f"causality dtype={dtype} dk={dk} C={C}")
+    base = run_fwd(kata, q, k, v, dtype, C)
+    r = np.random.Generator(np.random.PCG64(5))
+    for j in [C - 1, C, C + 1, 2 * C, 3 * C - 1, int(r.integers(1, T - 1))]:
+        q2, k2, v2 = q.copy(), k.copy(), v.copy()
+        q2[:, :, j] = gen.round_to(-q[:, :, j] + 0.25, dtype)
+        k2[:, :, j] = gen.round_to(k[:, :, j][..., ::-1] + 0.5, dtype)
+        v2[:, :, j] = gen.round_to(v[:, :, j] * 3.0 + 1.0, dtype)
+        got = run_fwd(kata, q2, k2, v2, dtype, C)
+        assert np.array_equal(got[:, :, :j], base[:, :, :j]), f"output before {j} changed"
+        assert not np.array_equal(got[:, :, j], base[:, :, j])
+
+
+def _integer_probe(T, d, dv, seed):
+    r = np.random.Generator(np.random.PCG64(seed))
+    kid = r.integers(0, d, (1, 2, T))
+    qid = r.integers(0, d, (1, 2, T))
+    k = np.eye(d)[kid].astype(np.float32)
+    q = np.eye(d)[qid].astype(np.float32)
+    v = r.integers(-3, 4, (1, 2, T, dv)).astype(np.float32)
+    return q, k, v
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,C", [(16, 64), (32, 128), (16, 32)])
+def test_integer_probe_bit_exact(kata, dtype, dk, C):
+    """Basis keys/queries and small integer values: states are exact integers and
+    every output equals the correctly rounded ratio of exact integers."""
+    import torch
+    T = 600
+    q, k, v = _integer_probe(T, dk, 64, seed=dk + C)
+    say(f"integer probe dtype={dtype} dk={dk} C={C}")
+    o = run_fwd(kata, q, k, v, dtype, C)
+    ref = O.brute_force(q, k, v)
+    want = gen.round_to(ref, dtype).astype(np.float64)      # double rounding is innocuous
+    assert np.array_equal(o, want)
+    Sp, zp, ST, zT = kata.scan_states(dev(k, dtype), dev(v, dtype), chunk=C)
+    torch.cuda.synchronize()
+    P, Z, S, z = O.prefix_states(k, v, C)
+    assert np.array_equal(host(Sp), P) and np.array_equal(host(zp), Z)
+    assert np.array_equal(host(ST), S) and np.array_equal(host(zT), z)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv,C", [(16, 64, 64), (32, 64, 128), (16, 16, 32)])
+def test_scan_states(kata, dtype, dk, dv, C):
+    import torch
+    q, k, v = gen.gaussian_qkv(2, 2, 777, dk, dv, seed=400 + C, dtype=dtype)
+    S0, z0 = O.state_from_tokens(*gen.gaussian_qkv(2, 2, 50, dk, dv, seed=9, dtype="f32")[1:])
+    S0 = S0.astype(np.float32)
+    z0 = z0.astype(np.float32)
+    say(f"scan_states dtype={dtype} dk={dk} dv={dv} C={C}")
+    Sp, zp, ST, zT = kata.scan_states(dev(k, dtype), dev(v, dtype), chunk=C,
+                                      initial_state=(dev(S0), dev(z0)))
+    torch.cuda.synchronize()
+    P, Z, S, z = O.prefix_states(k, v, C, S0, z0)
+    assert row_rel_err(host(Sp), P) <= 1e-5
+    assert row_rel_err(host(zp)[..., None], Z[..., None]) <= 1e-5
+    assert row_rel_err(host(ST), S) <= 1e-5
+    assert row_rel_err(host(zT)[..., None], z[..., None]) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_resume_then_decode(kata, dtype):
+    """fwd(T1) -> state -> fwd(T2 | state) -> decode steps equals the oracle over
+    the whole sequence."""
+    import torch
+    T1, T2, steps = 300, 200, 5
+    q, k, v = gen.gaussian_qkv(1, 3, T1 + T2 + steps, 16, 64, seed=77, dtype=dtype)
+    ref = O.brute_force(q, k, v)
+    say(f"resume dtype={dtype}")
+    o1, S1, z1 = run_fwd(kata, q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], dtype, 64, state=True)
+    o2, S2, z2 = run_fwd(kata, q[:, :, T1:T1 + T2], k[:, :, T1:T1 + T2], v[:, :, T1:T1 + T2],
+                         dtype, 64, S0=S1.astype(np.float32), z0=z1.astype(np.float32), state=True)
+    assert row_rel_err(o1, ref[:, :, :T1]) <= TOL[dtype]
+    assert row_rel_err(o2, ref[:, :, T1:T1 + T2]) <= TOL[dtype]
+    S = dev(S2[0].astype(np.float32))
+    z = dev(z2[0].astype(np.float32))
+    for t in range(T1 + T2, T1 + T2 + steps):
+        o = kata.decode_step(dev(q[0, :, t], dtype), dev(k[0, :, t], dtype), dev(v[0, :, t], dtype), S, z)
+        torch.cuda.synchronize()
+        assert row_rel_err(host(o), ref[0, :, t]) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(16, 64), (32, 64), (16, 16), (32, 32)])
+def test_decode_one_step_from_state(kata, dtype, dk, dv):
+    """One step from a given fp32 state, against float64 on the same state."""
+    import torch
+    N = 96
+    r = np.random.Generator(np.random.PCG64(dk * dv))
+    _, kk, vv = gen.gaussian_qkv(1, N, 40, dk, dv, seed=dk + dv, dtype="f32")
+    S, z = O.state_from_tokens(kk, vv)
+    S = S[0].astype(np.float32)
+    z = z[0].astype(np.float32)
+    q, k, v = gen.gaussian_qkv(1, 1, N, dk, dv, seed=3 * dk + dv, dtype=dtype)
+    q, k, v = q[0, 0], k[0, 0], v[0, 0]
+    q[5] = 0.0                                         # zero query -> zero output
+    o_ref, S_ref, z_ref = O.decode_step(q, k, v, S, z)
+    Sd, zd = dev(S), dev(z)
+    say(f"decode one step dtype={dtype} dk={dk} dv={dv}")
+    o = kata.decode_step(dev(q, dtype), dev(k, dtype), dev(v, dtype), Sd, zd)
+    torch.cuda.synchronize()
+    tol = 1e-5 if dtype == "f32" else 2 ** -8           # bf16 output rounding
+    assert row_rel_err(host(o), o_ref) <= tol
+    assert np.all(host(o)[5] == 0.0)
+    assert row_rel_err(host(Sd), S_ref) <= 1e-6
+    assert row_rel_err(host(zd)[..., None], z_ref[..., None]) <= 1e-6
+    assert r is not None
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_determinism(kata, dtype):
+    q, k, v = gen.gaussian_qkv(2, 4, 3000, 16, 64, seed=11, dtype=dtype)
+    say(f"determinism {dtype}")
+    a = run_fwd(kata, q, k, v, dtype, 64, state=True)
+    b = run_fwd(kata, q, k, v, dtype, 64, state=True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def _inputs(name):
+    from tests.gpu_util import workload_inputs
+    return workload_inputs(name)
