@@ -116,6 +116,9 @@ def chunked_fwd_into(q, k, v, o, chunk, causal, workspace, S0=None, z0=None, S_o
     if events is None:
         st = lib().kata_chunked_fwd(*args)
     else:
+        for e in events:            # torch creates its event lazily, on first record
+            if not e.cuda_event:
+                e.record()
         arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
         st = lib().kata_chunked_fwd_profiled(*args, arr, len(events))
     _raise(st, "kata_chunked_fwd")

@@ -46,6 +46,17 @@ def row_rel_err(got, ref):
     return float(np.max(diff[~zero] / scale[~zero]))
 
 
+def state_rel_err(got, ref, lead=2):
+    """max over the leading `lead` axes (e.g. batch, head) of max|got - ref| /
+    max|ref| over the remaining axes (a whole state at once); an all-zero
+    reference must be matched exactly."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    n = int(np.prod(ref.shape[:lead]))
+    return row_rel_err(got.reshape(n, -1), ref.reshape(n, -1))
+
+
 @functools.lru_cache(maxsize=8)
 def workload_inputs(name):
     w = gen.WORKLOADS[name]

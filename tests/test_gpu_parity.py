@@ -10,7 +10,7 @@ import pytest
 
 import oracle as O
 from kernelized_linear_attention_phi_amd import inputs as gen
-from tests.gpu_util import dev, host, row_rel_err, say
+from tests.gpu_util import dev, host, row_rel_err, say, state_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -51,8 +51,8 @@ def test_fwd_small_full(kata, dtype, dk, dv, C):
     ref = O.brute_force(q, k, v)
     assert row_rel_err(o, ref) <= TOL[dtype]
     S_ref, z_ref = O.state_from_tokens(k, v)
-    assert row_rel_err(S, S_ref) <= 1e-5
-    assert row_rel_err(z[..., None], z_ref[..., None]) <= 1e-5
+    assert state_rel_err(S, S_ref) <= 1e-5
+    assert state_rel_err(z, z_ref) <= 1e-5
 
 
 def test_tiny_fp32_workload(kata):
@@ -69,8 +69,11 @@ def test_ragged_and_short(kata, dtype, T):
     say(f"ragged dtype={dtype} T={T}")
     o = run_fwd(kata, q, k, v, dtype, 64)
     assert row_rel_err(o, O.brute_force(q, k, v)) <= TOL[dtype]
-    if T == 1:
-        assert np.array_equal(o, v.astype(np.float64))     # single token: o = v exactly
+    if T == 1:   # single token: o = (w v) / w, which rounds back to v
+        if dtype == "bf16":
+            assert np.array_equal(o, v.astype(np.float64))
+        else:
+            assert row_rel_err(o, v) <= 2 ** -22
 
 
 def test_empty_sequence_returns_initial_state(kata):
@@ -156,10 +159,10 @@ def test_scan_states(kata, dtype, dk, dv, C):
                                       initial_state=(dev(S0), dev(z0)))
     torch.cuda.synchronize()
     P, Z, S, z = O.prefix_states(k, v, C, S0, z0)
-    assert row_rel_err(host(Sp), P) <= 1e-5
-    assert row_rel_err(host(zp)[..., None], Z[..., None]) <= 1e-5
-    assert row_rel_err(host(ST), S) <= 1e-5
-    assert row_rel_err(host(zT)[..., None], z[..., None]) <= 1e-5
+    assert state_rel_err(host(Sp), P, lead=3) <= 1e-5
+    assert state_rel_err(host(zp), Z, lead=3) <= 1e-5
+    assert state_rel_err(host(ST), S) <= 1e-5
+    assert state_rel_err(host(zT), z) <= 1e-5
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -206,8 +209,8 @@ def test_decode_one_step_from_state(kata, dtype, dk, dv):
     tol = 1e-5 if dtype == "f32" else 2 ** -8           # bf16 output rounding
     assert row_rel_err(host(o), o_ref) <= tol
     assert np.all(host(o)[5] == 0.0)
-    assert row_rel_err(host(Sd), S_ref) <= 1e-6
-    assert row_rel_err(host(zd)[..., None], z_ref[..., None]) <= 1e-6
+    assert state_rel_err(host(Sd), S_ref, lead=1) <= 1e-6
+    assert state_rel_err(host(zd), z_ref, lead=1) <= 1e-6
     assert r is not None
 
 
