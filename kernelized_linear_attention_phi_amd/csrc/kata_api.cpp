@@ -3,6 +3,9 @@
 // allocates device memory or synchronises.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <algorithm>
 
 #include "../../include/kata.h"
 #include "kata_internal.h"
@@ -33,23 +36,47 @@ kata_status_t make_shape(int B, int H, int T, int dk, int dv, int C, kata_dtype_
     return KATA_OK;
 }
 
-// Workspace of the fp32 VALU forward: per-chunk records (causal) or one total
-// record per head (non-causal).
+// Launch plan of kata_chunked_fwd and its workspace layout.
+//  VALU path (fp32 inputs, shapes without a matrix-core kernel): per-chunk
+//    records in packed layout, scanned over chunks.
+//  MFMA path (bf16, d_k = 16): per-segment records of G chunks in accumulator
+//    order, an initial-state record and a total record per head.
 struct FwdPlan {
-    size_t S_off, z_off, bytes;
-    int NR;
+    bool mfma;
+    int G, NSEG, REC;
+    size_t S_off, z_off, init_off, total_off, bytes;
 };
+
+int segment_chunks(const Shape& s) {
+    if (const char* e = getenv("KATA_SEGMENT_CHUNKS")) {
+        const int g = atoi(e);
+        if (g > 0) return g;
+    }
+    // about one wavefront per SIMD (1024 on MI355X), each on a run of chunks
+    const long long chunks = (long long)s.B * s.H * s.NC;
+    return (int)std::max<long long>(1, chunks / 1024);
+}
 
 FwdPlan plan_fwd(const Shape& s, int causal) {
     FwdPlan p{};
     const size_t BH = (size_t)s.B * s.H;
-    p.NR = causal ? s.NC : 1;
+    if (BH == 0 || s.NC == 0) return p;
+    p.mfma = kata::mfma16_supported(s);
+    if (p.mfma) {
+        p.G = std::min(segment_chunks(s), s.NC);
+        p.NSEG = (s.NC + p.G - 1) / p.G;
+        p.REC = kata::mfma16_record_floats(s.dv);
+        p.S_off = 0;
+        p.init_off = align256(BH * p.NSEG * p.REC * sizeof(float));
+        p.total_off = p.init_off + align256(BH * p.REC * sizeof(float));
+        p.bytes = p.total_off + align256(BH * p.REC * sizeof(float));
+        return p;
+    }
     // non-causal also needs the per-chunk totals before reducing them
     const size_t nrec = BH * (size_t)s.NC + (causal ? 0 : BH);
     p.S_off = 0;
     p.z_off = align256(nrec * s.D * s.dv * sizeof(float));
     p.bytes = p.z_off + align256(nrec * s.D * sizeof(float));
-    if (BH == 0 || s.NC == 0) p.bytes = 0;
     return p;
 }
 
@@ -120,9 +147,28 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
     }
 
     char* ws = static_cast<char*>(workspace);
+    hipError_t e = mark(0);
+    if (plan.mfma) {
+        float* rec = reinterpret_cast<float*>(ws + plan.S_off);
+        float* init = reinterpret_cast<float*>(ws + plan.init_off);
+        float* total = reinterpret_cast<float*>(ws + plan.total_off);
+        if (S0 && e == hipSuccess) e = kata::launch_record_from_packed16(init, S0, z0, s.dv, (int)BH, hs);
+        if (e == hipSuccess) e = kata::launch_seg_state16(s, k, v, rec, plan.G, plan.NSEG, hs);
+        if (e == hipSuccess) e = mark(1);
+        // exclusive prefix over segments in place; inclusive total per head
+        if (e == hipSuccess)
+            e = kata::launch_scan_records(rec, (int)BH, plan.NSEG, plan.REC, S0 ? init : nullptr,
+                                          total, nullptr, hs);
+        if (e == hipSuccess) e = mark(2);
+        if (e == hipSuccess)
+            e = kata::launch_fwd16(s, q, k, v, causal ? rec : total, o, causal, plan.G, plan.NSEG, hs);
+        if (S_out && e == hipSuccess)
+            e = kata::launch_record_to_packed16(total, S_out, z_out, s.dv, (int)BH, hs);
+        if (e == hipSuccess) e = mark(3);
+        return hip_status(e);
+    }
     float* S_rec = reinterpret_cast<float*>(ws + plan.S_off);
     float* z_rec = reinterpret_cast<float*>(ws + plan.z_off);
-    hipError_t e = mark(0);
     if (e == hipSuccess) e = kata::launch_chunk_states_valu(s, k, v, S_rec, z_rec, hs);
     if (e == hipSuccess) e = mark(1);
     if (causal) {

@@ -40,6 +40,23 @@ hipError_t launch_scan_records(float* rec, int nseq, int NR, int E, const float*
 // Copies (src != NULL) or zero-fills n floats.
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st);
 
+// ---- bf16 matrix-core path, d_k = 16 (one wavefront per segment of G chunks) ----
+
+bool mfma16_supported(const Shape& s);
+// floats per state record (accumulator order, see kata_fwd16.hip)
+int mfma16_record_floats(int dv);
+// rec [BH, NSEG, REC]: total state of every segment
+hipError_t launch_seg_state16(const Shape& s, const void* k, const void* v, float* rec, int G,
+                              int NSEG, hipStream_t st);
+// causal: prefix [BH, NSEG, REC] exclusive segment prefixes; else prefix [BH, REC] totals
+hipError_t launch_fwd16(const Shape& s, const void* q, const void* k, const void* v,
+                        const float* prefix, void* o, int causal, int G, int NSEG,
+                        hipStream_t st);
+hipError_t launch_record_from_packed16(float* rec, const float* S, const float* z, int dv,
+                                       int nrec, hipStream_t st);
+hipError_t launch_record_to_packed16(const float* rec, float* S, float* z, int dv, int nrec,
+                                     hipStream_t st);
+
 // ---- decode ----
 hipError_t launch_decode(const void* q, const void* k, const void* v, float* S, float* z,
                          void* o, int N, int dk, int dv, bool bf16, hipStream_t st);

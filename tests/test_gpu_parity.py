@@ -15,6 +15,10 @@ from tests.gpu_util import dev, host, row_rel_err, say, state_rel_err
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+# Exported states: fp32 arithmetic throughout on the fp32 path; on the bf16 path
+# the lifted keys phi(k) are matrix-core operands rounded to bf16, so the state
+# carries that rounding (relative ~2^-9 per term) and is held to the bf16 bar.
+STATE_TOL = {"f32": 1e-5, "bf16": 2e-2}
 
 
 @pytest.fixture(scope="module")
@@ -51,8 +55,27 @@ def test_fwd_small_full(kata, dtype, dk, dv, C):
     ref = O.brute_force(q, k, v)
     assert row_rel_err(o, ref) <= TOL[dtype]
     S_ref, z_ref = O.state_from_tokens(k, v)
-    assert state_rel_err(S, S_ref) <= 1e-5
-    assert state_rel_err(z, z_ref) <= 1e-5
+    assert state_rel_err(S, S_ref) <= STATE_TOL[dtype]
+    assert state_rel_err(z, z_ref) <= STATE_TOL[dtype]
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 5, 16, 40])
+@pytest.mark.parametrize("C,T", [(64, 1000), (32, 999)])
+def test_segment_lengths(kata, monkeypatch, G, C, T):
+    """Chunks per segment (running state carried across chunks, ragged last
+    segment, one segment per head) must not change the result beyond rounding."""
+    monkeypatch.setenv("KATA_SEGMENT_CHUNKS", str(G))
+    q, k, v = gen.gaussian_qkv(2, 3, T, 16, 64, seed=500 + G, dtype="bf16")
+    say(f"segments G={G} C={C} T={T}")
+    o, S, z = run_fwd(kata, q, k, v, "bf16", C, state=True)
+    assert row_rel_err(o, O.brute_force(q, k, v)) <= TOL["bf16"]
+    S_ref, z_ref = O.state_from_tokens(k, v)
+    assert state_rel_err(S, S_ref) <= STATE_TOL["bf16"]
+    assert state_rel_err(z, z_ref) <= STATE_TOL["bf16"]
+    S0, z0 = (a.astype(np.float32) for a in O.state_from_tokens(k[:, :, :77], v[:, :, :77]))
+    o2 = run_fwd(kata, q, k, v, "bf16", C, S0=S0, z0=z0)
+    ref2 = O.brute_force(q, k, v, S0=S0.astype(np.float64), z0=z0.astype(np.float64))
+    assert row_rel_err(o2, ref2) <= TOL["bf16"]
 
 
 def test_tiny_fp32_workload(kata):
@@ -98,9 +121,11 @@ def test_noncausal(kata, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("dk,C", [(16, 64), (32, 128), (16, 16)])
-def test_bitwise_causality(kata, dtype, dk, C):
+@pytest.mark.parametrize("dk,C,G", [(16, 64, 0), (32, 128, 0), (16, 16, 0), (16, 64, 2), (16, 32, 3)])
+def test_bitwise_causality(kata, monkeypatch, dtype, dk, C, G):
     """Perturbing token j leaves every output before j bit-identical."""
+    if G:
+        monkeypatch.setenv("KATA_SEGMENT_CHUNKS", str(G))
     T = 4 * C + 37
     q, k, v = gen.gaussian_qkv(1, 2, T, dk, 64, seed=300 + C, dtype=dtype)
     say(f"causality dtype={dtype} dk={dk} C={C}")
