@@ -147,6 +147,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--quick", action="store_true", help="primary workload only (for profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -154,6 +156,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4,
+                          "launches": 3}), flush=True)
+        return
     import kernelized_linear_attention_phi_amd as kata
     from kernelized_linear_attention_phi_amd import inputs as gen
     kata.lib()

@@ -3,15 +3,15 @@
 // Method (KATA explainers, gist.science, technical summary 2.3; the paper's
 // abstract): the sequence is cut into chunks of C positions; each output is the
 // masked intra-chunk term plus phi(Q_c) times the prefix of chunk states; the
-// prefix is propagated by an associative scan. Here one wavefront owns a
-// segment of G consecutive chunks of one (batch, head) and carries the running
-// state S = sum phi(k) v^T (and z = sum phi(k)) in its matrix-core accumulators
-// across the segment, so only one state per segment touches HBM:
-//   kata_seg_state16 : segment totals         (phi(K)^T [V | 1] on MFMA)
+// prefix is propagated by an associative scan. Here one workgroup of two
+// wavefronts owns a segment of G consecutive chunks of one (batch, head) and
+// carries the running state S = sum phi(k) v^T across the segment in matrix-core
+// accumulators, so only one state per segment touches HBM:
+//   kata_seg_state16 : segment totals         (phi(K)^T V on MFMA)
 //   (scan kernel)    : exclusive prefix over segments of each head
-//   kata_fwd16       : per chunk, intra (QK^T -> square -> mask -> A.V) and inter
-//                      (phi(Q).S) on MFMA into one accumulator, normalise,
-//                      store, then S += phi(K)^T [V | 1].
+//   kata_fwd16       : per chunk, inter (phi(Q).S) and intra (QK^T -> square ->
+//                      mask -> A.V) on MFMA, normalise, store, then
+//                      S += phi(K)^T V.
 //
 // Internal feature order ("circulant"). The D = 136 unique products x_a x_b are
 // arranged as 9 tiles of 16 rows: tile delta (0..8), row rho (0..15) holds
@@ -23,9 +23,19 @@
 // tile and phi(Q) is built from a per-lane rotated copy of q: no LDS traffic
 // for either lift.
 //
-// Denominators ride along as a fifth value tile whose first column is 1 (the
-// "ones" tile): z = phi(K)^T 1, phi(Q).z and sum_j A_tj come out of the same
-// MFMAs as the numerators.
+// Work split inside a segment. Wavefront 0 owns feature tiles {0,1,2,3,8},
+// wavefront 1 tiles {4,5,6,7}: each lifts keys and queries for its own tiles
+// only, updates its own rows of S, and computes partial numerators phi(Q).S for
+// all query rows of the chunk over its own tiles. The partials for the other
+// wavefront's query tiles (16-row tiles alternate between the two) go through
+// LDS once per chunk; each wavefront then finishes its own query tiles (intra
+// term, denominators, division, store).
+//
+// Denominators. Inside a chunk, sum_j A_tj comes from the same MFMAs as the
+// numerators through a value tile whose first column is 1 (the "ones" tile).
+// Across chunks, z = sum phi(k) is kept as the 16 x 16 Gram matrix
+// Z = sum k k^T (one accumulator tile; z is its packed upper triangle), and
+// phi(q).z = q^T Z q is one MFMA (Z q) plus a 4-term dot product per lane.
 #include "kata_device.h"
 #include "kata_internal.h"
 #include "kata_mfma.h"
@@ -38,37 +48,51 @@ namespace {
 
 constexpr int DK = 16;
 constexpr int NMT = 9;                  // feature tiles (delta = 0..8)
+constexpr int NW = 2;                   // wavefronts per segment
+constexpr int NSLOT = 5;                // feature tiles per wavefront (at most)
+
+// Feature tile held in slot i of wavefront W.
+template <int W> __host__ __device__ constexpr int tile_of(int slot) {
+    return W == 0 ? (slot < 4 ? slot : 8) : 4 + slot;
+}
+template <int W> __host__ __device__ constexpr int nslots() { return W == 0 ? 5 : 4; }
 
 template <int DV, int C>
 struct Cfg {
     static constexpr int NTV = DV / 16;           // value tiles
-    static constexpr int NT = NTV + 1;            // + ones tile
     static constexpr int TT = C / 16;             // query tiles per chunk
+    static constexpr int TW = TT / NW;            // query tiles per wavefront
     static constexpr int KS = C / 32;             // 32-token K-steps per chunk
     static constexpr int QB = C * DK * 2;         // bytes of a q or k chunk
     static constexpr int VB = C * DV * 2;         // bytes of a v chunk
     static constexpr int BUF = 2 * QB + VB;       // one chunk buffer
-    static constexpr int NLQKV = BUF / 1024;      // 1 KB async loads: q, k, v
-    static constexpr int NLKV = (QB + VB) / 1024; // k, v only
-    static constexpr int NSTORE = TT * NTV;       // 8-byte output stores per chunk
+    static constexpr int NBUF = 2;                // staging depth (prefetch distance 1)
+    static constexpr int XB = NW * TW * NTV * 1024;   // exchange of partial numerators
+    static constexpr int OROW = DV * 2 + 16;      // LDS row stride of a staged output tile
+    static constexpr int OU = 2 * DV;             // 16-byte units per 16-row output tile
+    static constexpr int REC = NMT * NTV * 256 + 256;   // floats per state record
 };
 
-// Register arrays passed by reference (alias templates keep the declarations
-// unambiguous).
-template <int DV, int C> using StateRegs = f32x4_t[NMT][Cfg<DV, C>::NT];
-template <int DV, int C> using KTRegs = f32x4_t[Cfg<DV, C>::TT];
-template <int DV, int C> using KRegs = u32x2_t[Cfg<DV, C>::TT];
-template <int DV, int C> using VRegs = u32x4_t[Cfg<DV, C>::KS][Cfg<DV, C>::NTV];
+// Running state owned by one wavefront: its feature tiles of S (slots, see
+// tile_of) and the Gram matrix Z = sum k k^T (lane = column, rows 4g + r; both
+// wavefronts keep a copy).
+template <int DV, int C>
+struct State {
+    f32x4_t s[NSLOT][Cfg<DV, C>::NTV];
+    f32x4_t zm;
+};
 
 struct Lane {
-    int lane, c16, g;
-    __device__ Lane() : lane(threadIdx.x & 63), c16(threadIdx.x & 15), g((threadIdx.x >> 4) & 3) {}
+    int lane, c16, g, w;
+    __device__ Lane()
+        : lane(threadIdx.x & 63), c16(threadIdx.x & 15), g((threadIdx.x >> 4) & 3),
+          w(threadIdx.x >> 6) {}
 };
 
 // Constant operands. ones: column (or row) 0 of the ones tile = 1 on every slot.
 __device__ __forceinline__ u32x4_t ones_op(const Lane& L) {
-    const uint32_t w = L.c16 == 0 ? 0x3f803f80u : 0u;   // bf16 1.0 twice
-    return u32x4_t{w, w, w, w};
+    const uint32_t x = L.c16 == 0 ? 0x3f803f80u : 0u;   // bf16 1.0 twice
+    return u32x4_t{x, x, x, x};
 }
 // B operand of 16x16x32 selecting value column c16 + 16h of a 32-column block:
 // slot (g, s) stands for column 8g + s.
@@ -93,9 +117,25 @@ __device__ __forceinline__ u32x2_t ident16(const Lane& L) {
     return r;
 }
 
-// ---- chunk staging: q | k | v of one chunk, row-major as in HBM -------------
+// Workgroup barrier that waits only for this wavefront's LDS operations (not for
+// its outstanding global loads, which may be prefetches).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0), other counters free
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
 
-// Full chunk: 1 KB direct-to-LDS loads (lane l moves bytes [16l, 16l+16)).
+// Value of lane (c16 + d) mod 16 of the same row, for a compile-time tile d.
+template <int D>
+__device__ __forceinline__ float partner(float x) {
+    if constexpr (D == 0) return x;
+    else return row_fetch<D>(x);
+}
+
+// ---- chunk staging: q | k | v of one chunk, row-major as in HBM -------------
+// The 1 KB pieces of a full chunk are split round-robin over the wavefronts:
+// piece i goes to wavefront i % NW as a direct-to-LDS load (lane l moves bytes
+// [16l, 16l+16) of the piece).
 template <int DV, int C>
 __device__ __forceinline__ void stage_async(const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                             size_t tok0, char* buf, bool with_q, const Lane& L) {
@@ -103,20 +143,16 @@ __device__ __forceinline__ void stage_async(const bf16_t* q, const bf16_t* k, co
     const char* gq = reinterpret_cast<const char*>(q + tok0 * DK);
     const char* gk = reinterpret_cast<const char*>(k + tok0 * DK);
     const char* gv = reinterpret_cast<const char*>(v + tok0 * DV);
-    if (with_q) {
+    constexpr int PQ = F::QB / 1024, PV = F::VB / 1024;
+    const int first = with_q ? 0 : PQ;
 #pragma unroll
-        for (int i = 0; i < F::QB / 1024; ++i)
-            __builtin_amdgcn_global_load_lds(gq + i * 1024 + L.lane * 16,
-                                             (lds_void_t*)(buf + i * 1024), 16, 0, 0);
+    for (int i = 0; i < 2 * PQ + PV; ++i) {
+        if (i < first || i % NW != L.w) continue;
+        const char* src = i < PQ ? gq + i * 1024
+                        : i < 2 * PQ ? gk + (i - PQ) * 1024
+                                     : gv + (i - 2 * PQ) * 1024;
+        __builtin_amdgcn_global_load_lds(src + L.lane * 16, (lds_void_t*)(buf + i * 1024), 16, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < F::QB / 1024; ++i)
-        __builtin_amdgcn_global_load_lds(gk + i * 1024 + L.lane * 16,
-                                         (lds_void_t*)(buf + F::QB + i * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < F::VB / 1024; ++i)
-        __builtin_amdgcn_global_load_lds(gv + i * 1024 + L.lane * 16,
-                                         (lds_void_t*)(buf + 2 * F::QB + i * 1024), 16, 0, 0);
 }
 
 // Ragged chunk (n < C valid positions): bounded loads, zero fill, then LDS.
@@ -134,387 +170,442 @@ __device__ __forceinline__ void stage_ragged(const bf16_t* q, const bf16_t* k, c
     u32x4_t* lv = reinterpret_cast<u32x4_t*>(buf + 2 * F::QB);
     constexpr int QU = F::QB / 16, VU = F::VB / 16;       // 16-byte units
     constexpr int QPR = DK * 2 / 16, VPR = DV * 2 / 16;   // units per row
-    for (int u = L.lane; u < QU; u += 64) {
+    const int tid = L.w * 64 + L.lane, nthr = NW * 64;
+    for (int u = tid; u < QU; u += nthr) {
         const bool ok = u / QPR < n;
         if (with_q) lq[u] = ok ? gq[u] : zero;
         lk[u] = ok ? gk[u] : zero;
     }
-    for (int u = L.lane; u < VU; u += 64) lv[u] = (u / VPR < n) ? gv[u] : zero;
+    for (int u = tid; u < VU; u += nthr) lv[u] = (u / VPR < n) ? gv[u] : zero;
     compiler_fence();
 }
 
+// Chunk c of a segment [c0, c1) lives in buffer (c - c0) % NBUF and is staged one
+// iteration ahead. Per iteration: wait for every outstanding memory operation of
+// this wavefront (its part of chunk c, and the output stores of chunk c-1,
+// issued before the state update and normally retired by now: on this target
+// loads and stores may retire out of order, so a partial count is not a safe
+// bound), barrier (every part present, both wavefronts done with chunk c-1),
+// then stage chunk c+1 into chunk c-1's buffer.
+template <int DV, int C>
+struct Pipeline {
+    using F = Cfg<DV, C>;
+    char* lds;
+    int c0, c1, T;
+    size_t tok_base;
+    bool with_q;
+
+    __device__ char* buffer(int c) const { return lds + ((c - c0) % F::NBUF) * F::BUF; }
+
+    __device__ void stage(const bf16_t* q, const bf16_t* k, const bf16_t* v, int c, const Lane& L) {
+        if (c >= c1) return;
+        const int n = min(C, T - c * C);
+        const size_t tok0 = tok_base + (size_t)c * C;
+        if (n == C) stage_async<DV, C>(q, k, v, tok0, buffer(c), with_q, L);
+        else stage_ragged<DV, C>(q, k, v, tok0, n, buffer(c), with_q, L);
+    }
+    __device__ void acquire(const bf16_t* q, const bf16_t* k, const bf16_t* v, int c, const Lane& L) {
+        wait_vmcnt<0>();
+        lds_barrier();
+        stage(q, k, v, c + 1, L);
+    }
+};
+
 // ---- per-chunk fragments ----------------------------------------------------
 
-// V^T fragments: vop[m][nt] = 8 values v[token][16nt + c16] for the tokens of
-// K-step m in slot order s -> 32m + 16(s/4) + 4g + s%4. Built by multiplying
-// row-major V blocks with selection matrices (the accumulator layout performs
-// the transpose), so V never needs a transposed copy.
+// V^T fragments of K-step m: vop[nt] = 8 values v[token][16nt + c16] for the
+// tokens 32m + 16(s/4) + 4g + s%4 (slot s). Built by multiplying row-major V
+// blocks with selection matrices (the accumulator layout performs the transpose).
 template <int DV, int C>
-__device__ __forceinline__ void v_fragments(const bf16_t* bv, VRegs<DV, C>& vop, const Lane& L) {
+__device__ __forceinline__ void v_fragment_step(const bf16_t* bv, u32x4_t (&vop)[Cfg<DV, C>::NTV],
+                                                int m, const Lane& L) {
     using F = Cfg<DV, C>;
+    if constexpr (F::NTV % 2 == 0) {
+        const u32x4_t sel0 = select32(L, 0), sel1 = select32(L, 1);
 #pragma unroll
-    for (int m = 0; m < F::KS; ++m) {
-        if constexpr (F::NTV % 2 == 0) {
-            const u32x4_t sel0 = select32(L, 0), sel1 = select32(L, 1);
-#pragma unroll
-            for (int ntp = 0; ntp < F::NTV / 2; ++ntp) {
-                f32x4_t t[2][2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(
-                        bv + (32 * m + 16 * h + L.c16) * DV + 32 * ntp + 8 * L.g);
-                    t[h][0] = mma32(vf, sel0, zero4());
-                    t[h][1] = mma32(vf, sel1, zero4());
-                }
-#pragma unroll
-                for (int e = 0; e < 2; ++e)
-                    vop[m][2 * ntp + e] = u32x4_t{pk2(t[0][e][0], t[0][e][1]), pk2(t[0][e][2], t[0][e][3]),
-                                                  pk2(t[1][e][0], t[1][e][1]), pk2(t[1][e][2], t[1][e][3])};
-            }
-        } else {
-            static_assert(F::NTV == 1, "odd value-tile count is only 1");
-            const u32x2_t id = ident16(L);
-            f32x4_t t[2];
+        for (int ntp = 0; ntp < F::NTV / 2; ++ntp) {
+            f32x4_t t[2][2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const u32x2_t vf = *reinterpret_cast<const u32x2_t*>(
-                    bv + (32 * m + 16 * h + L.c16) * DV + 4 * L.g);
-                t[h] = mma16(vf, id, zero4());
+                const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(
+                    bv + (32 * m + 16 * h + L.c16) * DV + 32 * ntp + 8 * L.g);
+                t[h][0] = mma32(vf, sel0, zero4());
+                t[h][1] = mma32(vf, sel1, zero4());
             }
-            vop[m][0] = u32x4_t{pk2(t[0][0], t[0][1]), pk2(t[0][2], t[0][3]),
-                                pk2(t[1][0], t[1][1]), pk2(t[1][2], t[1][3])};
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                vop[2 * ntp + e] = u32x4_t{pk2(t[0][e][0], t[0][e][1]), pk2(t[0][e][2], t[0][e][3]),
+                                           pk2(t[1][e][0], t[1][e][1]), pk2(t[1][e][2], t[1][e][3])};
         }
+    } else {
+        static_assert(F::NTV == 1, "odd value-tile count is only 1");
+        const u32x2_t id = ident16(L);
+        f32x4_t t[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x2_t vf = *reinterpret_cast<const u32x2_t*>(
+                bv + (32 * m + 16 * h + L.c16) * DV + 4 * L.g);
+            t[h] = mma16(vf, id, zero4());
+        }
+        vop[0] = u32x4_t{pk2(t[0][0], t[0][1]), pk2(t[0][2], t[0][3]),
+                         pk2(t[1][0], t[1][1]), pk2(t[1][2], t[1][3])};
     }
 }
 
-// S += phi(K_c)^T [V_c | 1]. KT[jb][r] = k[16jb + 4g + r][c16] (fp32).
+// KT[jb][r] = k[16jb + 4g + r][c16] (fp32, exact) via an identity product.
 template <int DV, int C>
-__device__ __forceinline__ void state_update(StateRegs<DV, C>& S, const KTRegs<DV, C>& KT,
-                                             const VRegs<DV, C>& vop, const Lane& L) {
+__device__ __forceinline__ void k_transposed(const bf16_t* bk, f32x4_t (&KT)[Cfg<DV, C>::TT],
+                                             const Lane& L) {
     using F = Cfg<DV, C>;
-    const u32x4_t ones = ones_op(L);
-    const bool upper = L.c16 >= 8;
+    const u32x2_t id = ident16(L);
+#pragma unroll
+    for (int jb = 0; jb < F::TT; ++jb) {
+        const u32x2_t kf = *reinterpret_cast<const u32x2_t*>(bk + (16 * jb + L.c16) * DK + 4 * L.g);
+        KT[jb] = mma16(kf, id, zero4());
+    }
+}
+
+// Lifted keys of feature tile D for the tokens of one K-step (slot s): lane c16
+// holds row rho = c16, i.e. k_rho * k_{(rho+D) mod 16}; bf16 A operand.
+template <int D>
+__device__ __forceinline__ u32x4_t lift_keys(const float (&ka)[8], const Lane& L) {
+    float f[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        f[s] = ka[s] * partner<D>(ka[s]);
+        if (D == 8 && L.c16 >= 8) f[s] = 0.0f;       // repeated pairs stay zero
+    }
+    return u32x4_t{pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
+}
+
+// S(own tiles) += phi(K_c)^T V_c, Z += K_c^T K_c. vop[m] are the V^T fragments.
+template <int W, int DV, int C>
+__device__ __forceinline__ void state_update(State<DV, C>& st, const f32x4_t (&KT)[Cfg<DV, C>::TT],
+                                             const u32x4_t (&vop)[Cfg<DV, C>::KS][Cfg<DV, C>::NTV],
+                                             const Lane& L) {
+    using F = Cfg<DV, C>;
 #pragma unroll
     for (int m = 0; m < F::KS; ++m) {
         float ka[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) ka[s] = KT[2 * m + s / 4][s % 4];
+        // Gram matrix: A = K^T (row = coordinate c16), B = K (column = c16)
+        const u32x4_t kt = {pk2(ka[0], ka[1]), pk2(ka[2], ka[3]), pk2(ka[4], ka[5]), pk2(ka[6], ka[7])};
+        st.zm = mma32(kt, kt, st.zm);
 #pragma unroll
-        for (int d = 0; d < NMT; ++d) {
-            float f[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                float b;
-                if (d == 0) b = ka[s];
-                else if (d == 1) b = row_fetch<1>(ka[s]);
-                else if (d == 2) b = row_fetch<2>(ka[s]);
-                else if (d == 3) b = row_fetch<3>(ka[s]);
-                else if (d == 4) b = row_fetch<4>(ka[s]);
-                else if (d == 5) b = row_fetch<5>(ka[s]);
-                else if (d == 6) b = row_fetch<6>(ka[s]);
-                else if (d == 7) b = row_fetch<7>(ka[s]);
-                else b = row_fetch<8>(ka[s]);
-                f[s] = ka[s] * b;
-                if (d == 8 && upper) f[s] = 0.0f;          // repeated pairs stay zero
+        for (int i = 0; i < nslots<W>(); ++i) {
+            u32x4_t fk;
+            switch (tile_of<W>(i)) {
+                case 0: fk = lift_keys<0>(ka, L); break;
+                case 1: fk = lift_keys<1>(ka, L); break;
+                case 2: fk = lift_keys<2>(ka, L); break;
+                case 3: fk = lift_keys<3>(ka, L); break;
+                case 4: fk = lift_keys<4>(ka, L); break;
+                case 5: fk = lift_keys<5>(ka, L); break;
+                case 6: fk = lift_keys<6>(ka, L); break;
+                case 7: fk = lift_keys<7>(ka, L); break;
+                default: fk = lift_keys<8>(ka, L); break;
             }
-            const u32x4_t fk = {pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
 #pragma unroll
-            for (int nt = 0; nt < F::NTV; ++nt) S[d][nt] = mma32(fk, vop[m][nt], S[d][nt]);
-            S[d][F::NTV] = mma32(fk, ones, S[d][F::NTV]);
-            // keep one tile's lift in flight at a time (bounds register pressure;
-            // the matrix core still overlaps the next tile's VALU work)
-            __builtin_amdgcn_sched_barrier(0);
+            for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] = mma32(fk, vop[m][nt], st.s[i][nt]);
         }
     }
 }
 
-template <int DV, int C>
-__device__ __forceinline__ void k_fragments(const bf16_t* bk, KRegs<DV, C>& kf, KTRegs<DV, C>& KT,
-                                            const Lane& L) {
-    using F = Cfg<DV, C>;
-    const u32x2_t id = ident16(L);
+// Lifted queries (x2 off the diagonal) of tiles (d0, d1) as a B operand: slot
+// s = 4h + r is tile d_h, row rho = 4g + r, i.e. q_rho * q_{rho + d_h}; qr is
+// q rotated by 4g (qr[x] = q[(x + 4g) mod 16]).
+__device__ __forceinline__ u32x4_t lift_queries(const float (&qr)[16], int d0, int d1) {
+    float f[8];
 #pragma unroll
-    for (int jb = 0; jb < F::TT; ++jb) {
-        kf[jb] = *reinterpret_cast<const u32x2_t*>(bk + (16 * jb + L.c16) * DK + 4 * L.g);
-        KT[jb] = mma16(kf[jb], id, zero4());
+    for (int h = 0; h < 2; ++h) {
+        const int d = h ? d1 : d0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            f[4 * h + r] = d == 0 ? qr[r] * qr[r] : (2.0f * qr[r]) * qr[(r + d) & 15];
+    }
+    return u32x4_t{pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
+}
+
+// q row t = 16 tt + c16 of the staged chunk, rotated by 4g lanes; qf = q_t[4g..4g+3].
+__device__ __forceinline__ void load_query(const bf16_t* bq, int tt, const Lane& L, float (&qr)[16],
+                                           u32x2_t& qf) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const u32x2_t piece = *reinterpret_cast<const u32x2_t*>(
+            bq + (16 * tt + L.c16) * DK + 4 * ((L.g + a) & 3));
+        if (a == 0) qf = piece;
+        qr[4 * a + 0] = lo_bf16(piece[0]);
+        qr[4 * a + 1] = hi_bf16(piece[0]);
+        qr[4 * a + 2] = lo_bf16(piece[1]);
+        qr[4 * a + 3] = hi_bf16(piece[1]);
     }
 }
 
 // ---- state records -----------------------------------------------------------
-// A record holds one state in accumulator order: S part at
-// ((tile * NTV + nt) * 64 + lane) * 4 + r, then the z column (ones tile, column
-// 0) at NMT*NTV*256 + tile*16 + 4g + r.
+// A record holds one state in accumulator order: S at
+// ((tile * NTV + nt) * 64 + lane) * 4 + r, then Z at NMT*NTV*256 + lane*4 + r.
 
-template <int DV, int C>
-__device__ __forceinline__ void record_store(float* rec, const StateRegs<DV, C>& S, const Lane& L) {
+template <int W, int DV, int C>
+__device__ __forceinline__ void record_store(float* rec, const State<DV, C>& st, const Lane& L) {
     using F = Cfg<DV, C>;
     f32x4_t* r4 = reinterpret_cast<f32x4_t*>(rec);
 #pragma unroll
-    for (int d = 0; d < NMT; ++d)
+    for (int i = 0; i < nslots<W>(); ++i)
 #pragma unroll
-        for (int nt = 0; nt < F::NTV; ++nt) r4[(d * F::NTV + nt) * 64 + L.lane] = S[d][nt];
-    if (L.c16 == 0) {
-#pragma unroll
-        for (int d = 0; d < NMT; ++d) r4[NMT * F::NTV * 64 + d * 4 + L.g] = S[d][F::NTV];
-    }
+        for (int nt = 0; nt < F::NTV; ++nt)
+            r4[(tile_of<W>(i) * F::NTV + nt) * 64 + L.lane] = st.s[i][nt];
+    if (W == 0) r4[NMT * F::NTV * 64 + L.lane] = st.zm;
 }
 
-template <int DV, int C>
-__device__ __forceinline__ void record_load(const float* rec, StateRegs<DV, C>& S, const Lane& L) {
+template <int W, int DV, int C>
+__device__ __forceinline__ void record_load(const float* rec, State<DV, C>& st, const Lane& L) {
     using F = Cfg<DV, C>;
     const f32x4_t* r4 = reinterpret_cast<const f32x4_t*>(rec);
 #pragma unroll
-    for (int d = 0; d < NMT; ++d)
+    for (int i = 0; i < NSLOT; ++i)
 #pragma unroll
-        for (int nt = 0; nt < F::NTV; ++nt) S[d][nt] = r4[(d * F::NTV + nt) * 64 + L.lane];
+        for (int nt = 0; nt < F::NTV; ++nt)
+            st.s[i][nt] = i < nslots<W>() ? r4[(tile_of<W>(i) * F::NTV + nt) * 64 + L.lane] : zero4();
+    st.zm = r4[NMT * F::NTV * 64 + L.lane];
+}
+
+// ---- per-wavefront bodies --------------------------------------------------------
+
+template <int W, int DV, int C>
+__device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v, float* rec,
+                                               char* lds, int T, int NC, int G, int NSEG,
+                                               const Lane& L) {
+    using F = Cfg<DV, C>;
+    const int seg = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    Pipeline<DV, C> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, false};
+    State<DV, C> st;
 #pragma unroll
-    for (int d = 0; d < NMT; ++d)
-        S[d][F::NTV] = L.c16 == 0 ? r4[NMT * F::NTV * 64 + d * 4 + L.g] : zero4();
+    for (int i = 0; i < NSLOT; ++i)
+#pragma unroll
+        for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] = zero4();
+    st.zm = zero4();
+
+    P.stage(nullptr, k, v, P.c0, L);
+    for (int c = P.c0; c < P.c1; ++c) {
+        P.acquire(nullptr, k, v, c, L);
+        const char* buf = P.buffer(c);
+        const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::QB);
+        const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::QB);
+        f32x4_t KT[F::TT];
+        k_transposed<DV, C>(bk, KT, L);
+        u32x4_t vop[F::KS][F::NTV];
+#pragma unroll
+        for (int m = 0; m < F::KS; ++m) v_fragment_step<DV, C>(bv, vop[m], m, L);
+        state_update<W, DV, C>(st, KT, vop, L);
+        compiler_fence();
+    }
+    record_store<W, DV, C>(rec + (bh * NSEG + seg) * (size_t)F::REC, st, L);
+}
+
+template <int W, int DV, int C, bool CAUSAL>
+__device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                                         const float* prefix, bf16_t* o, char* lds, int T,
+                                         int NC, int G, int NSEG, const Lane& L) {
+    using F = Cfg<DV, C>;
+    const int seg = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    Pipeline<DV, C> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true};
+    // exchange buffer: partials for query tile (u of wavefront w) at [w][u][nt][lane]
+    f32x4_t* xbuf = reinterpret_cast<f32x4_t*>(lds + F::NBUF * F::BUF);
+
+    State<DV, C> st;
+    record_load<W, DV, C>(prefix + (CAUSAL ? bh * NSEG + seg : bh) * (size_t)F::REC, st, L);
+
+    P.stage(q, k, v, P.c0, L);
+    for (int c = P.c0; c < P.c1; ++c) {
+        const int n = min(C, T - c * C);
+        P.acquire(q, k, v, c, L);
+        const char* buf = P.buffer(c);
+        const bf16_t* bq = reinterpret_cast<const bf16_t*>(buf);
+        const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::QB);
+        const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::QB);
+
+        // ---- inter-chunk partials over this wavefront's feature tiles, for every
+        // query tile; those of the other wavefront's tiles go to the exchange
+        f32x4_t num[F::TW][F::NTV + 1];            // own query tiles (+ ones tile)
+        {
+            // S^T in bf16 as A operands: slot s of pair p = own slot 2p + s/4, row 4g + s%4
+            u32x4_t sop[2][F::NTV];
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int nt = 0; nt < F::NTV; ++nt)
+                    sop[p][nt] = u32x4_t{pk2(st.s[2 * p][nt][0], st.s[2 * p][nt][1]),
+                                         pk2(st.s[2 * p][nt][2], st.s[2 * p][nt][3]),
+                                         pk2(st.s[2 * p + 1][nt][0], st.s[2 * p + 1][nt][1]),
+                                         pk2(st.s[2 * p + 1][nt][2], st.s[2 * p + 1][nt][3])};
+            u32x2_t sop8[F::NTV];
+            if (W == 0) {
+#pragma unroll
+                for (int nt = 0; nt < F::NTV; ++nt)
+                    sop8[nt] = u32x2_t{pk2(st.s[4][nt][0], st.s[4][nt][1]), pk2(st.s[4][nt][2], st.s[4][nt][3])};
+            }
+#pragma unroll
+            for (int tt = 0; tt < F::TT; ++tt) {
+                float qr[16];
+                u32x2_t qf;
+                load_query(bq, tt, L, qr, qf);
+                f32x4_t part[F::NTV];
+#pragma unroll
+                for (int nt = 0; nt < F::NTV; ++nt) part[nt] = zero4();
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const u32x4_t fq = lift_queries(qr, tile_of<W>(2 * p), tile_of<W>(2 * p + 1));
+#pragma unroll
+                    for (int nt = 0; nt < F::NTV; ++nt) part[nt] = mma32(sop[p][nt], fq, part[nt]);
+                }
+                if (W == 0) {                         // tile 8 (half K-step)
+                    float f[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) f[r] = (2.0f * qr[r]) * qr[(r + 8) & 15];
+                    const u32x2_t fq = {pk2(f[0], f[1]), pk2(f[2], f[3])};
+#pragma unroll
+                    for (int nt = 0; nt < F::NTV; ++nt) part[nt] = mma16(sop8[nt], fq, part[nt]);
+                }
+                const int u = tt / NW;
+                if (tt % NW == W) {
+#pragma unroll
+                    for (int nt = 0; nt < F::NTV; ++nt) num[u][nt] = part[nt];
+                    num[u][F::NTV] = zero4();
+                } else {
+#pragma unroll
+                    for (int nt = 0; nt < F::NTV; ++nt)
+                        xbuf[((1 - W) * F::TW + u) * F::NTV * 64 + nt * 64 + L.lane] = part[nt];
+                }
+            }
+        }
+        lds_barrier();                                // partials exchanged
+#pragma unroll
+        for (int u = 0; u < F::TW; ++u)
+#pragma unroll
+            for (int nt = 0; nt < F::NTV; ++nt)
+                num[u][nt] += xbuf[(W * F::TW + u) * F::NTV * 64 + nt * 64 + L.lane];
+
+        // V^T fragments (intra term and state update)
+        u32x4_t vop[F::KS][F::NTV];
+        if (CAUSAL) {
+#pragma unroll
+            for (int m = 0; m < F::KS; ++m) v_fragment_step<DV, C>(bv, vop[m], m, L);
+        }
+        // Z as an A operand: lane c16 = row i, slots 4g + s = column j; Z is
+        // symmetric, so the accumulator (lane = column) serves directly.
+        const u32x2_t zop = {pk2(st.zm[0], st.zm[1]), pk2(st.zm[2], st.zm[3])};
+        bf16_t* oc = o + (bh * T + (size_t)c * C) * DV;
+        char* otile = reinterpret_cast<char*>(xbuf + W * F::TW * F::NTV * 64);
+#pragma unroll
+        for (int u = 0; u < F::TW; ++u) {
+            const int tt = NW * u + W;
+            const int t = 16 * tt + L.c16;
+            float qr[16];
+            u32x2_t qf;
+            load_query(bq, tt, L, qr, qf);
+            // ---- intra-chunk term: A = (Q K^T)^2 masked to j <= t, num += A [V | 1]
+            if (CAUSAL) {
+                const u32x4_t ones = ones_op(L);
+#pragma unroll
+                for (int m = 0; m <= tt / 2; ++m) {
+                    const bool diag = 32 * m + 31 > 16 * tt;
+                    float w[8];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const u32x2_t kf = *reinterpret_cast<const u32x2_t*>(
+                            bk + (32 * m + 16 * h + L.c16) * DK + 4 * L.g);
+                        // rows j = 32m + 16h + 4g + r, column t
+                        const f32x4_t sc = mma16(kf, qf, zero4());
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = 32 * m + 16 * h + 4 * L.g + r;
+                            const float x = sc[r] * sc[r];
+                            w[4 * h + r] = (!diag || j <= t) ? x : 0.0f;
+                        }
+                    }
+                    const u32x4_t at = {pk2(w[0], w[1]), pk2(w[2], w[3]), pk2(w[4], w[5]), pk2(w[6], w[7])};
+#pragma unroll
+                    for (int nt = 0; nt < F::NTV; ++nt) num[u][nt] = mma32(vop[m][nt], at, num[u][nt]);
+                    num[u][F::NTV] = mma32(ones, at, num[u][F::NTV]);
+                }
+            }
+            // ---- normalise and store: o = num / den
+            // inter-chunk denominator q^T Z q: (Z q)[4g + r] times q[4g + r],
+            // summed over r here and over the four lane groups below
+            const f32x4_t zq = mma16(zop, qf, zero4());
+            float di = qr[0] * zq[0];
+            di = __builtin_fmaf(qr[1], zq[1], di);
+            di = __builtin_fmaf(qr[2], zq[2], di);
+            di = __builtin_fmaf(qr[3], zq[3], di);
+            di += __shfl_xor(di, 16, 64);
+            di += __shfl_xor(di, 32, 64);
+            // intra-chunk denominator: row 0 of the ones tile (lane group 0)
+            const float den = __shfl(num[u][F::NTV][0], L.c16, 64) + di;
+            const float y = den != 0.0f ? 1.0f / den : 0.0f;   // y = 0 gives o = 0
+            // the 16 x DV bf16 tile goes through LDS (this wavefront's half of the
+            // exchange buffer, already consumed) so that HBM sees whole rows
+#pragma unroll
+            for (int nt = 0; nt < F::NTV; ++nt) {
+                float ov[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // Markstein: with y = RN(1/den), q0 + RN(num - q0 den) y = RN(num/den)
+                    const float x = num[u][nt][r];
+                    const float q0 = x * y;
+                    const float er = __builtin_fmaf(-q0, den, x);
+                    ov[r] = __builtin_fmaf(er, y, q0);
+                }
+                *reinterpret_cast<u32x2_t*>(otile + L.c16 * F::OROW + 2 * (16 * nt + 4 * L.g)) =
+                    u32x2_t{pk2(ov[0], ov[1]), pk2(ov[2], ov[3])};
+            }
+#pragma unroll
+            for (int i = 0; i < (F::OU + 63) / 64; ++i) {
+                const int unit = L.lane + 64 * i;
+                const int row = unit / (F::OU / 16), col = unit % (F::OU / 16);
+                if (unit < F::OU) {
+                    const u32x4_t val = *reinterpret_cast<const u32x4_t*>(otile + row * F::OROW + 16 * col);
+                    if (16 * tt + row < n)
+                        *reinterpret_cast<u32x4_t*>(oc + (size_t)(16 * tt + row) * DV + 8 * col) = val;
+                }
+            }
+        }
+
+        // ---- running state: S += phi(K_c)^T V_c, Z += K_c^T K_c
+        if (CAUSAL) {
+            f32x4_t KT[F::TT];
+            k_transposed<DV, C>(bk, KT, L);
+            state_update<W, DV, C>(st, KT, vop, L);
+        }
+        compiler_fence();
+    }
 }
 
 // ---- kernels -------------------------------------------------------------------
 
 template <int DV, int C>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kata_seg_state16(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                       float* __restrict__ rec, int T, int NC, int G, int NSEG) {
     using F = Cfg<DV, C>;
-    __shared__ __attribute__((aligned(16))) char lds[2 * F::BUF];
+    __shared__ __attribute__((aligned(16))) char lds[F::NBUF * F::BUF];
     const Lane L;
-    const int seg = blockIdx.x;
-    const size_t bh = blockIdx.y;
-    const int c0 = seg * G, c1 = min(NC, c0 + G);
-    f32x4_t S[NMT][F::NT];
-#pragma unroll
-    for (int d = 0; d < NMT; ++d)
-#pragma unroll
-        for (int nt = 0; nt < F::NT; ++nt) S[d][nt] = zero4();
-
-    auto stage = [&](int c, char* buf) -> bool {
-        const int n = min(C, T - c * C);
-        const size_t tok0 = bh * T + (size_t)c * C;
-        if (n == C) { stage_async<DV, C>(nullptr, k, v, tok0, buf, false, L); return true; }
-        stage_ragged<DV, C>(nullptr, k, v, tok0, n, buf, false, L);
-        return false;
-    };
-    stage(c0, lds);
-    for (int c = c0; c < c1; ++c) {
-        char* buf = lds + ((c - c0) & 1) * F::BUF;
-        const bool more = c + 1 < c1;
-        const bool async_next = more && stage(c + 1, lds + ((c + 1 - c0) & 1) * F::BUF);
-        if (async_next) wait_vmcnt<F::NLKV>(); else wait_vmcnt<0>();
-        const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::QB);
-        const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::QB);
-        u32x2_t kf[F::TT];
-        f32x4_t KT[F::TT];
-        u32x4_t vop[F::KS][F::NTV];
-        k_fragments<DV, C>(bk, kf, KT, L);
-        v_fragments<DV, C>(bv, vop, L);
-        state_update<DV, C>(S, KT, vop, L);
-        compiler_fence();
-    }
-    record_store<DV, C>(rec + (bh * NSEG + seg) * (size_t)(NMT * F::NTV * 256 + NMT * 16), S, L);
+    if (L.w == 0) seg_state_body<0, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L);
+    else seg_state_body<1, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L);
 }
 
 template <int DV, int C, bool CAUSAL>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kata_fwd16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bf16_t* __restrict__ v, const float* __restrict__ prefix,
                 bf16_t* __restrict__ o, int T, int NC, int G, int NSEG) {
     using F = Cfg<DV, C>;
-    constexpr int REC = NMT * F::NTV * 256 + NMT * 16;
-    __shared__ __attribute__((aligned(16))) char lds[2 * F::BUF];
+    __shared__ __attribute__((aligned(16))) char lds[F::NBUF * F::BUF + F::XB];
     const Lane L;
-    const int seg = blockIdx.x;
-    const size_t bh = blockIdx.y;
-    const int c0 = seg * G, c1 = min(NC, c0 + G);
-
-    f32x4_t S[NMT][F::NT];
-    record_load<DV, C>(prefix + (CAUSAL ? bh * NSEG + seg : bh) * (size_t)REC, S, L);
-
-    auto stage = [&](int c, char* buf) -> bool {
-        const int n = min(C, T - c * C);
-        const size_t tok0 = bh * T + (size_t)c * C;
-        if (n == C) { stage_async<DV, C>(q, k, v, tok0, buf, true, L); return true; }
-        stage_ragged<DV, C>(q, k, v, tok0, n, buf, true, L);
-        return false;
-    };
-    stage(c0, lds);
-    bool stores_pending = false;
-    for (int c = c0; c < c1; ++c) {
-        char* buf = lds + ((c - c0) & 1) * F::BUF;
-        const int n = min(C, T - c * C);
-        const bool more = c + 1 < c1;
-        const bool async_next = more && stage(c + 1, lds + ((c + 1 - c0) & 1) * F::BUF);
-        // wait for this chunk's staging; the newer loads (next chunk) and the
-        // previous chunk's output stores (issued after this chunk's loads) may
-        // stay in flight
-        if (async_next) {
-            if (stores_pending) wait_vmcnt<F::NLQKV + F::NSTORE>(); else wait_vmcnt<F::NLQKV>();
-        } else {
-            if (stores_pending) wait_vmcnt<F::NSTORE>(); else wait_vmcnt<0>();
-        }
-        const bf16_t* bq = reinterpret_cast<const bf16_t*>(buf);
-        const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::QB);
-        const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::QB);
-
-        // K rows and V^T fragments for the intra term; the state update below
-        // rebuilds its own copies from the (still resident) LDS buffer so that
-        // none of them stays live across the output phase.
-        u32x2_t kf[F::TT];
-        u32x4_t vop[F::KS][F::NTV];
-        if (CAUSAL) {
-#pragma unroll
-            for (int jb = 0; jb < F::TT; ++jb)
-                kf[jb] = *reinterpret_cast<const u32x2_t*>(bk + (16 * jb + L.c16) * DK + 4 * L.g);
-            v_fragments<DV, C>(bv, vop, L);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-
-        // Query tiles are processed in groups of TH (two tiles = 32 rows) to
-        // bound the accumulator and rotated-query registers.
-        constexpr int TH = F::TT < 2 ? F::TT : 2;
-        bf16_t* oc = o + (bh * T + (size_t)c * C) * DV;
-#pragma unroll
-        for (int t0 = 0; t0 < F::TT; t0 += TH) {
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4_t num[F::NT][TH];
-#pragma unroll
-            for (int nt = 0; nt < F::NT; ++nt)
-#pragma unroll
-                for (int u = 0; u < TH; ++u) num[nt][u] = zero4();
-
-            // query rows of this lane: t = 16tt + c16; q rotated by 4g lanes
-            float qr[TH][16];
-#pragma unroll
-            for (int u = 0; u < TH; ++u) {
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const u32x2_t piece = *reinterpret_cast<const u32x2_t*>(
-                        bq + (16 * (t0 + u) + L.c16) * DK + 4 * ((L.g + a) & 3));
-                    qr[u][4 * a + 0] = lo_bf16(piece[0]);
-                    qr[u][4 * a + 1] = hi_bf16(piece[0]);
-                    qr[u][4 * a + 2] = lo_bf16(piece[1]);
-                    qr[u][4 * a + 3] = hi_bf16(piece[1]);
-                }
-            }
-
-            // ---- intra-chunk term: A = (Q K^T)^2 masked to j <= t, num += A [V | 1]
-            if (CAUSAL) {
-                const u32x4_t ones = ones_op(L);
-#pragma unroll
-                for (int u = 0; u < TH; ++u) {
-                    const int tt = t0 + u;
-                    const u32x2_t qf = *reinterpret_cast<const u32x2_t*>(
-                        bq + (16 * tt + L.c16) * DK + 4 * L.g);
-                    const int t = 16 * tt + L.c16;
-#pragma unroll
-                    for (int m = 0; m <= tt / 2; ++m) {
-                        const bool diag = 32 * m + 31 > 16 * tt;
-                        float w[8];
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            // rows j = 16(2m+h) + 4g + r, column t
-                            const f32x4_t st = mma16(kf[2 * m + h], qf, zero4());
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int j = 32 * m + 16 * h + 4 * L.g + r;
-                                const float x = st[r] * st[r];
-                                w[4 * h + r] = (!diag || j <= t) ? x : 0.0f;
-                            }
-                        }
-                        const u32x4_t at = {pk2(w[0], w[1]), pk2(w[2], w[3]), pk2(w[4], w[5]),
-                                            pk2(w[6], w[7])};
-#pragma unroll
-                        for (int nt = 0; nt < F::NTV; ++nt) num[nt][u] = mma32(vop[m][nt], at, num[nt][u]);
-                        num[F::NTV][u] = mma32(ones, at, num[F::NTV][u]);
-                    }
-                }
-            }
-
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- inter-chunk term: num += S^T phi(Q)^T over the 9 feature tiles
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {             // tiles (2m, 2m+1)
-                u32x4_t sop[F::NT];
-#pragma unroll
-                for (int nt = 0; nt < F::NT; ++nt)
-                    sop[nt] = u32x4_t{pk2(S[2 * m][nt][0], S[2 * m][nt][1]),
-                                      pk2(S[2 * m][nt][2], S[2 * m][nt][3]),
-                                      pk2(S[2 * m + 1][nt][0], S[2 * m + 1][nt][1]),
-                                      pk2(S[2 * m + 1][nt][2], S[2 * m + 1][nt][3])};
-#pragma unroll
-                for (int u = 0; u < TH; ++u) {
-                    float f[8];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int d = 2 * m + h;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            f[4 * h + r] = d == 0 ? qr[u][r] * qr[u][r]
-                                                  : (2.0f * qr[u][r]) * qr[u][(r + d) & 15];
-                    }
-                    const u32x4_t fq = {pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
-#pragma unroll
-                    for (int nt = 0; nt < F::NT; ++nt) num[nt][u] = mma32(sop[nt], fq, num[nt][u]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            {                                         // tile 8 (half K-step)
-                u32x2_t sop[F::NT];
-#pragma unroll
-                for (int nt = 0; nt < F::NT; ++nt)
-                    sop[nt] = u32x2_t{pk2(S[8][nt][0], S[8][nt][1]), pk2(S[8][nt][2], S[8][nt][3])};
-#pragma unroll
-                for (int u = 0; u < TH; ++u) {
-                    float f[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) f[r] = (2.0f * qr[u][r]) * qr[u][(r + 8) & 15];
-                    const u32x2_t fq = {pk2(f[0], f[1]), pk2(f[2], f[3])};
-#pragma unroll
-                    for (int nt = 0; nt < F::NT; ++nt) num[nt][u] = mma16(sop[nt], fq, num[nt][u]);
-                }
-            }
-
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- normalise and store: o = num / den (den = row 0 of the ones tile)
-#pragma unroll
-            for (int u = 0; u < TH; ++u) {
-                const int t = 16 * (t0 + u) + L.c16;
-                const float den = __shfl(num[F::NTV][u][0], L.c16, 64);
-                const float y = 1.0f / den;           // correctly rounded reciprocal
-#pragma unroll
-                for (int nt = 0; nt < F::NTV; ++nt) {
-                    float ov[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        // Markstein: with y = RN(1/den), q0 + RN(num - q0 den) y = RN(num/den)
-                        const float x = num[nt][u][r];
-                        const float q0 = x * y;
-                        const float e = __builtin_fmaf(-q0, den, x);
-                        const float qq = __builtin_fmaf(e, y, q0);
-                        ov[r] = den != 0.0f ? qq : 0.0f;
-                    }
-                    if (t < n)
-                        *reinterpret_cast<u32x2_t*>(oc + (size_t)t * DV + 16 * nt + 4 * L.g) =
-                            u32x2_t{pk2(ov[0], ov[1]), pk2(ov[2], ov[3])};
-                }
-            }
-        }
-        stores_pending = true;
-
-        // ---- running state: S += phi(K_c)^T [V_c | 1]
-        __builtin_amdgcn_sched_barrier(0);
-        if (CAUSAL) {
-            u32x2_t kf2[F::TT];
-            f32x4_t KT[F::TT];
-            u32x4_t vop2[F::KS][F::NTV];
-            k_fragments<DV, C>(bk, kf2, KT, L);
-            v_fragments<DV, C>(bv, vop2, L);
-            state_update<DV, C>(S, KT, vop2, L);
-        }
-        compiler_fence();
-    }
+    if (L.w == 0) fwd_body<0, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L);
+    else fwd_body<1, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L);
 }
 
 template <int DV, int C>
@@ -523,16 +614,16 @@ hipError_t launch_dv_c(const Shape& s, const void* q, const void* k, const void*
                        bool state_only, hipStream_t st) {
     dim3 grid(NSEG, s.B * s.H);
     if (state_only) {
-        kata_seg_state16<DV, C><<<grid, 64, 0, st>>>((const bf16_t*)k, (const bf16_t*)v, rec,
-                                                      s.T, s.NC, G, NSEG);
+        kata_seg_state16<DV, C><<<grid, 64 * NW, 0, st>>>((const bf16_t*)k, (const bf16_t*)v, rec,
+                                                           s.T, s.NC, G, NSEG);
     } else if (causal) {
-        kata_fwd16<DV, C, true><<<grid, 64, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
-                                                      (const bf16_t*)v, prefix, (bf16_t*)o, s.T,
-                                                      s.NC, G, NSEG);
+        kata_fwd16<DV, C, true><<<grid, 64 * NW, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
+                                                           (const bf16_t*)v, prefix, (bf16_t*)o,
+                                                           s.T, s.NC, G, NSEG);
     } else {
-        kata_fwd16<DV, C, false><<<grid, 64, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
-                                                       (const bf16_t*)v, prefix, (bf16_t*)o, s.T,
-                                                       s.NC, G, NSEG);
+        kata_fwd16<DV, C, false><<<grid, 64 * NW, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
+                                                            (const bf16_t*)v, prefix, (bf16_t*)o,
+                                                            s.T, s.NC, G, NSEG);
     }
     return hipGetLastError();
 }
@@ -566,7 +657,7 @@ bool mfma16_supported(const Shape& s) {
            (s.dv == 16 || s.dv == 32 || s.dv == 64);
 }
 
-int mfma16_record_floats(int dv) { return NMT * (dv / 16) * 256 + NMT * 16; }
+int mfma16_record_floats(int dv) { return NMT * (dv / 16) * 256 + 256; }
 
 hipError_t launch_seg_state16(const Shape& s, const void* k, const void* v, float* rec, int G,
                               int NSEG, hipStream_t st) {
@@ -584,21 +675,27 @@ hipError_t launch_fwd16(const Shape& s, const void* q, const void* k, const void
 namespace {
 
 // Internal record element -> (packed feature index, value column, scale), or -1
-// for the repeated (always zero) rows.
-__device__ __forceinline__ int record_to_packed(int idx, int NTV, int* col, float* scale) {
+// for elements without a packed counterpart: the repeated (always zero) rows of
+// tile 8, and the lower triangle of Z on export (lower = true marks those so the
+// import can still fill them).
+__device__ __forceinline__ int record_to_packed(int idx, int NTV, int* col, float* scale,
+                                                bool* lower) {
     const int sz = NMT * NTV * 256;
-    int d, rho;
-    if (idx < sz) {
-        const int r = idx & 3, lane = (idx >> 2) & 63, nt = (idx >> 8) % NTV;
-        d = (idx >> 8) / NTV;
-        rho = 4 * (lane >> 4) + r;
-        *col = 16 * nt + (lane & 15);
-    } else {
+    *lower = false;
+    if (idx >= sz) {                                 // Gram matrix Z[i][j]
         const int e = idx - sz;
-        d = e / 16;
-        rho = e % 16;
-        *col = -1;                                   // z entry
+        const int lane = (e >> 2) & 63;
+        const int i = 4 * (lane >> 4) + (e & 3), j = lane & 15;
+        const int a = min(i, j), b = max(i, j);
+        *col = -1;
+        *scale = i == j ? 1.0f : kSqrt2;
+        *lower = i > j;
+        return a * DK - a * (a - 1) / 2 + (b - a);
     }
+    const int r = idx & 3, lane = (idx >> 2) & 63, nt = (idx >> 8) % NTV;
+    const int d = (idx >> 8) / NTV;
+    const int rho = 4 * (lane >> 4) + r;
+    *col = 16 * nt + (lane & 15);
     if (d == 8 && rho >= 8) return -1;
     const int i = rho, j = (rho + d) & 15;
     const int a = min(i, j), b = max(i, j);
@@ -615,7 +712,8 @@ __global__ void record_from_packed(float* __restrict__ rec, const float* __restr
         const int idx = (int)(x % REC);
         int col;
         float scale;
-        const int p = record_to_packed(idx, NTV, &col, &scale);
+        bool lower;
+        const int p = record_to_packed(idx, NTV, &col, &scale, &lower);
         float val = 0.0f;
         if (p >= 0) val = (col >= 0 ? S[(b * D + p) * DV + col] : z[b * D + p]) / scale;
         rec[x] = val;
@@ -631,8 +729,9 @@ __global__ void record_to_packed_kernel(const float* __restrict__ rec, float* __
         const int idx = (int)(x % REC);
         int col;
         float scale;
-        const int p = record_to_packed(idx, NTV, &col, &scale);
-        if (p < 0) continue;
+        bool lower;
+        const int p = record_to_packed(idx, NTV, &col, &scale, &lower);
+        if (p < 0 || lower) continue;
         const float val = rec[x] * scale;
         if (col >= 0) S[(b * D + p) * DV + col] = val;
         else z[b * D + p] = val;
