@@ -101,11 +101,12 @@ kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, void
                                void* workspace, size_t ws_bytes, void* stream);
 
 /* kata_chunked_fwd with phase timing: identical work and results, and it also
- * records events[0..3] (hipEvent_t, created by the caller) on `stream` at the
+ * records events[0..4] (hipEvent_t, created by the caller) on `stream` at the
  * phase boundaries - events[0] before the chunk-state phase, events[1] after it,
- * events[2] after the inter-chunk scan, events[3] after the output phase - so a
- * caller can time each phase with hipEventElapsedTime. n_events must be >= 4
- * (else KATA_EINVAL); events after the fourth are ignored. */
+ * events[2] after the inter-chunk scan, events[3] after the output kernel,
+ * events[4] after the final-state export (S_out, z_out; an empty phase when they
+ * are NULL) - so a caller can time each phase with hipEventElapsedTime.
+ * n_events must be >= 5 (else KATA_EINVAL); events after the fifth are ignored. */
 kata_status_t kata_chunked_fwd_profiled(const void* q, const void* k, const void* v, void* o,
                                         int B, int H, int T, int d_k, int d_v, int chunk,
                                         int causal, kata_dtype_t dtype,

@@ -104,8 +104,9 @@ def chunked_fwd_into(q, k, v, o, chunk, causal, workspace, S0=None, z0=None, S_o
                      z_out=None, events=None):
     """Raw call: every buffer preallocated by the caller (used by the benchmark).
 
-    events: optional sequence of 4 torch.cuda.Event recorded at the phase
-    boundaries (chunk states | scan | output) through kata_chunked_fwd_profiled.
+    events: optional sequence of 5 torch.cuda.Event recorded at the phase
+    boundaries (chunk states | scan | output kernel | state export) through
+    kata_chunked_fwd_profiled.
     """
     B, H, T, dk = q.shape
     dv = v.shape[-1]

@@ -138,11 +138,12 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
         hipError_t e = mark(0);
         if (e == hipSuccess) e = mark(1);
         if (e == hipSuccess) e = mark(2);
+        if (e == hipSuccess) e = mark(3);
         if (S_out) {
             if (e == hipSuccess) e = kata::launch_copy_or_zero(S_out, S0, BH * nS, hs);
             if (e == hipSuccess) e = kata::launch_copy_or_zero(z_out, z0, BH * nz, hs);
         }
-        if (e == hipSuccess) e = mark(3);
+        if (e == hipSuccess) e = mark(4);
         return hip_status(e);
     }
 
@@ -162,9 +163,10 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
         if (e == hipSuccess) e = mark(2);
         if (e == hipSuccess)
             e = kata::launch_fwd16(s, q, k, v, causal ? rec : total, o, causal, plan.G, plan.NSEG, hs);
+        if (e == hipSuccess) e = mark(3);
         if (S_out && e == hipSuccess)
             e = kata::launch_record_to_packed16(total, S_out, z_out, s.dv, (int)BH, hs);
-        if (e == hipSuccess) e = mark(3);
+        if (e == hipSuccess) e = mark(4);
         return hip_status(e);
     }
     float* S_rec = reinterpret_cast<float*>(ws + plan.S_off);
@@ -191,6 +193,7 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
         if (e == hipSuccess) e = kata::launch_fwd_valu(s, q, k, v, S_tot, z_tot, o, 0, hs);
     }
     if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess) e = mark(4);
     return hip_status(e);
 }
 
@@ -209,7 +212,7 @@ kata_status_t kata_chunked_fwd_profiled(const void* q, const void* k, const void
                                         const float* z0, float* S_out, float* z_out,
                                         void* workspace, size_t ws_bytes, void* stream,
                                         void* const* events, int n_events) {
-    if (!events || n_events < 4) return KATA_EINVAL;
+    if (!events || n_events < 5) return KATA_EINVAL;
     for (int i = 0; i < 4; ++i)
         if (!events[i]) return KATA_EINVAL;
     return chunked_fwd_impl(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, S0, z0, S_out,

@@ -69,6 +69,16 @@ def test_fwd_rejects_before_launch(L):
     assert fwd(L, B=0, q=None, o=None, ws=None, ws_bytes=0) == OK
 
 
+def test_profiled_needs_five_events(L):
+    prof = L.kata_chunked_fwd_profiled
+    evs = (ctypes.c_void_p * 5)(*([FAKE] * 5))
+    base = (FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 16, 64, 64, 1, BF16, None, None, None, None,
+            FAKE, 1 << 40, None)
+    assert prof(*base, None, 5) == EINVAL
+    assert prof(*base, evs, 4) == EINVAL
+    assert prof(*base[:4], 1, 1, 64, 24, *base[8:], evs, 5) == EUNSUPPORTED
+
+
 def test_workspace_query(L):
     for args in [(1, 8, 131072, 16, 64, 64, BF16, 1), (1, 16, 32768, 32, 64, 128, BF16, 1),
                  (1, 1, 256, 16, 16, 64, F32, 1), (2, 3, 100, 16, 64, 32, BF16, 0)]:
