@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkata.so")
 
-SOURCES = ["kata_api.cpp", "kata_valu.hip", "kata_scan.hip", "kata_decode.hip", "kata_fwd16.hip"]
+SOURCES = ["kata_api.cpp", "kata_valu.hip", "kata_scan.hip", "kata_decode.hip", "kata_fwd16.hip",
+           "kata_fwd32.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

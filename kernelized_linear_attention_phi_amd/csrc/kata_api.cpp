@@ -39,33 +39,36 @@ kata_status_t make_shape(int B, int H, int T, int dk, int dv, int C, kata_dtype_
 // Launch plan of kata_chunked_fwd and its workspace layout.
 //  VALU path (fp32 inputs, shapes without a matrix-core kernel): per-chunk
 //    records in packed layout, scanned over chunks.
-//  MFMA path (bf16, d_k = 16): per-segment records of G chunks in accumulator
-//    order, an initial-state record and a total record per head.
+//  MFMA path (bf16, d_k = 16 or 32): per-segment records of G chunks in
+//    accumulator order, an initial-state record and a total record per head.
 struct FwdPlan {
-    bool mfma;
+    int mfma;   // 0 (VALU path), 16 or 32 (d_k of the matrix-core path)
     int G, NSEG, REC;
     size_t S_off, z_off, init_off, total_off, bytes;
 };
 
-int segment_chunks(const Shape& s) {
+int segment_chunks(const Shape& s, int workgroups) {
     if (const char* e = getenv("KATA_SEGMENT_CHUNKS")) {
         const int g = atoi(e);
         if (g > 0) return g;
     }
-    // about one wavefront per SIMD (1024 on MI355X), each on a run of chunks
+    // about `workgroups` segments in flight (one wave of resident workgroups
+    // over the 256 compute units), each on a run of chunks
     const long long chunks = (long long)s.B * s.H * s.NC;
-    return (int)std::max<long long>(1, chunks / 1024);
+    return (int)std::max<long long>(1, chunks / workgroups);
 }
 
 FwdPlan plan_fwd(const Shape& s, int causal) {
     FwdPlan p{};
     const size_t BH = (size_t)s.B * s.H;
     if (BH == 0 || s.NC == 0) return p;
-    p.mfma = kata::mfma16_supported(s);
+    p.mfma = kata::mfma16_supported(s) ? 16 : kata::mfma32_supported(s) ? 32 : 0;
     if (p.mfma) {
-        p.G = std::min(segment_chunks(s), s.NC);
+        // d_k = 16: four 2-wavefront workgroups per compute unit; d_k = 32: one
+        // 4-wavefront workgroup (its LDS fills the compute unit)
+        p.G = std::min(segment_chunks(s, p.mfma == 16 ? 1024 : 256), s.NC);
         p.NSEG = (s.NC + p.G - 1) / p.G;
-        p.REC = kata::mfma16_record_floats(s.dv);
+        p.REC = p.mfma == 16 ? kata::mfma16_record_floats(s.dv) : kata::mfma32_record_floats(s.dv);
         p.S_off = 0;
         p.init_off = align256(BH * p.NSEG * p.REC * sizeof(float));
         p.total_off = p.init_off + align256(BH * p.REC * sizeof(float));
@@ -153,8 +156,13 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
         float* rec = reinterpret_cast<float*>(ws + plan.S_off);
         float* init = reinterpret_cast<float*>(ws + plan.init_off);
         float* total = reinterpret_cast<float*>(ws + plan.total_off);
-        if (S0 && e == hipSuccess) e = kata::launch_record_from_packed16(init, S0, z0, s.dv, (int)BH, hs);
-        if (e == hipSuccess) e = kata::launch_seg_state16(s, k, v, rec, plan.G, plan.NSEG, hs);
+        const bool d16 = plan.mfma == 16;
+        if (S0 && e == hipSuccess)
+            e = d16 ? kata::launch_record_from_packed16(init, S0, z0, s.dv, (int)BH, hs)
+                    : kata::launch_record_from_packed32(init, S0, z0, s.dv, (int)BH, hs);
+        if (e == hipSuccess)
+            e = d16 ? kata::launch_seg_state16(s, k, v, rec, plan.G, plan.NSEG, hs)
+                    : kata::launch_seg_state32(s, k, v, rec, plan.G, plan.NSEG, hs);
         if (e == hipSuccess) e = mark(1);
         // exclusive prefix over segments in place; inclusive total per head
         if (e == hipSuccess)
@@ -162,10 +170,14 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
                                           total, nullptr, hs);
         if (e == hipSuccess) e = mark(2);
         if (e == hipSuccess)
-            e = kata::launch_fwd16(s, q, k, v, causal ? rec : total, o, causal, plan.G, plan.NSEG, hs);
+            e = d16 ? kata::launch_fwd16(s, q, k, v, causal ? rec : total, o, causal, plan.G,
+                                         plan.NSEG, hs)
+                    : kata::launch_fwd32(s, q, k, v, causal ? rec : total, o, causal, plan.G,
+                                         plan.NSEG, hs);
         if (e == hipSuccess) e = mark(3);
         if (S_out && e == hipSuccess)
-            e = kata::launch_record_to_packed16(total, S_out, z_out, s.dv, (int)BH, hs);
+            e = d16 ? kata::launch_record_to_packed16(total, S_out, z_out, s.dv, (int)BH, hs)
+                    : kata::launch_record_to_packed32(total, S_out, z_out, s.dv, (int)BH, hs);
         if (e == hipSuccess) e = mark(4);
         return hip_status(e);
     }
@@ -213,7 +225,7 @@ kata_status_t kata_chunked_fwd_profiled(const void* q, const void* k, const void
                                         void* workspace, size_t ws_bytes, void* stream,
                                         void* const* events, int n_events) {
     if (!events || n_events < 5) return KATA_EINVAL;
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 5; ++i)
         if (!events[i]) return KATA_EINVAL;
     return chunked_fwd_impl(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, S0, z0, S_out,
                             z_out, workspace, ws_bytes, stream, events);

@@ -1,0 +1,162 @@
+// Pieces shared by the matrix-core chunked-forward kernels (d_k = 16 and 32):
+// lane coordinates, constant MFMA operands, the workgroup barrier, LDS
+// transposed reads, and the direct-to-LDS staging of one chunk of q | k | v.
+//
+// Chunks (KATA explainers, gist.science, technical summary 2.3): chunk c of a
+// sequence covers positions [cC, min(cC + C, T)); a ragged last chunk is staged
+// with zero rows past the end, which add nothing to any sum.
+#pragma once
+
+#include "kata_device.h"
+#include "kata_mfma.h"
+
+namespace kata {
+
+struct Lane {
+    int lane, c16, g, w;
+    __device__ Lane()
+        : lane(threadIdx.x & 63), c16(threadIdx.x & 15), g((threadIdx.x >> 4) & 3),
+          w(threadIdx.x >> 6) {}
+};
+
+// Row (or column) 0 of the "ones" operand = 1 on every K-slot: as the A operand
+// of A.V it turns row 0 of the product into the column sums of the B operand.
+__device__ __forceinline__ u32x4_t ones_op(const Lane& L) {
+    const uint32_t x = L.c16 == 0 ? 0x3f803f80u : 0u;   // bf16 1.0 twice
+    return u32x4_t{x, x, x, x};
+}
+
+// B operand of 16x16x16 = identity: slot (g, s) stands for row 4g + s.
+__device__ __forceinline__ u32x2_t ident16(const Lane& L) {
+    u32x2_t r;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int s0 = 4 * L.g + 2 * p;
+        r[p] = (s0 == L.c16 ? 0x3f80u : 0u) | (s0 + 1 == L.c16 ? 0x3f800000u : 0u);
+    }
+    return r;
+}
+
+// Workgroup barrier that waits only for this wavefront's LDS operations (not for
+// its outstanding global loads, which may be prefetches).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0), other counters free
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
+
+// Value of lane (c16 + d) mod 16 of the same row, for a compile-time d.
+template <int D>
+__device__ __forceinline__ float partner(float x) {
+    if constexpr (D == 0) return x;
+    else return row_fetch<D>(x);
+}
+
+// ds_read_b64_tr_b16: every lane supplies the LDS address of 4 consecutive
+// 16-bit elements; within each group of 16 lanes, lane l receives element l % 4
+// of the block of lane 4i + l / 4 as its element i (i = 0..3).
+__device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
+    typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+    const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+    return __builtin_bit_cast(u32x2_t, r);
+}
+
+// V^T fragment of the 32-token K-step m and value tile nt, read transposed from
+// the row-major [C][DV] chunk in LDS: lane (c16, g), slot s holds
+// v[32m + 16(s/4) + 4g + s%4][16nt + c16]. Lane j of group g points at row
+// 32m + 16h + 4g + j/4, columns 16nt + 4(j%4) .. +3.
+template <int DV>
+__device__ __forceinline__ u32x4_t v_fragment_tr(const bf16_t* bv, int m, int nt, const Lane& L) {
+    u32x2_t h2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        h2[h] = lds_read_tr16(bv + (32 * m + 16 * h + 4 * L.g + (L.c16 >> 2)) * DV + 16 * nt +
+                              4 * (L.c16 & 3));
+    return u32x4_t{h2[0][0], h2[0][1], h2[1][0], h2[1][1]};
+}
+
+// ---- chunk staging: q | k | v of one chunk, row-major as in HBM -------------
+template <int DK, int DV, int C, int NW>
+struct ChunkIO {
+    static constexpr int QB = C * DK * 2;         // bytes of a q or k chunk
+    static constexpr int VB = C * DV * 2;         // bytes of a v chunk
+    static constexpr int BUF = 2 * QB + VB;       // one chunk buffer
+    static_assert(QB % 1024 == 0 && VB % 1024 == 0, "chunks are whole 1 KB pieces");
+
+    // Full chunk: the 1 KB pieces are split round-robin over the wavefronts;
+    // piece i goes to wavefront i % NW as a direct-to-LDS load (lane l moves
+    // bytes [16l, 16l+16) of the piece).
+    static __device__ __forceinline__ void stage_async(const bf16_t* q, const bf16_t* k,
+                                                       const bf16_t* v, size_t tok0, char* buf,
+                                                       bool with_q, const Lane& L) {
+        const char* gq = reinterpret_cast<const char*>(q + tok0 * DK);
+        const char* gk = reinterpret_cast<const char*>(k + tok0 * DK);
+        const char* gv = reinterpret_cast<const char*>(v + tok0 * DV);
+        constexpr int PQ = QB / 1024, PV = VB / 1024;
+        const int first = with_q ? 0 : PQ;
+#pragma unroll
+        for (int i = 0; i < 2 * PQ + PV; ++i) {
+            if (i < first || i % NW != L.w) continue;
+            const char* src = i < PQ ? gq + i * 1024
+                            : i < 2 * PQ ? gk + (i - PQ) * 1024
+                                         : gv + (i - 2 * PQ) * 1024;
+            __builtin_amdgcn_global_load_lds(src + L.lane * 16, (lds_void_t*)(buf + i * 1024), 16,
+                                             0, 0);
+        }
+    }
+
+    // Ragged chunk (n < C valid positions): bounded loads, zero fill, then LDS.
+    static __device__ __forceinline__ void stage_ragged(const bf16_t* q, const bf16_t* k,
+                                                        const bf16_t* v, size_t tok0, int n,
+                                                        char* buf, bool with_q, const Lane& L) {
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
+        const u32x4_t* gq = reinterpret_cast<const u32x4_t*>(q + tok0 * DK);
+        const u32x4_t* gk = reinterpret_cast<const u32x4_t*>(k + tok0 * DK);
+        const u32x4_t* gv = reinterpret_cast<const u32x4_t*>(v + tok0 * DV);
+        u32x4_t* lq = reinterpret_cast<u32x4_t*>(buf);
+        u32x4_t* lk = reinterpret_cast<u32x4_t*>(buf + QB);
+        u32x4_t* lv = reinterpret_cast<u32x4_t*>(buf + 2 * QB);
+        constexpr int QU = QB / 16, VU = VB / 16;       // 16-byte units
+        constexpr int QPR = DK * 2 / 16, VPR = DV * 2 / 16;   // units per row
+        const int tid = L.w * 64 + L.lane, nthr = NW * 64;
+        for (int u = tid; u < QU; u += nthr) {
+            const bool ok = u / QPR < n;
+            if (with_q) lq[u] = ok ? gq[u] : zero;
+            lk[u] = ok ? gk[u] : zero;
+        }
+        for (int u = tid; u < VU; u += nthr) lv[u] = (u / VPR < n) ? gv[u] : zero;
+        compiler_fence();
+    }
+};
+
+// Chunk c of a segment [c0, c1) lives in buffer (c - c0) % 2 and is staged one
+// iteration ahead. Per iteration: wait for every outstanding memory operation of
+// this wavefront (its part of chunk c, and its output stores of chunk c-1: loads
+// and stores may complete out of order, so no partial count is safe), barrier
+// (every wavefront's part has landed and everyone is done with the buffer chunk
+// c+1 will overwrite), then issue chunk c+1.
+template <int DK, int DV, int C, int NW>
+struct Pipeline {
+    using IO = ChunkIO<DK, DV, C, NW>;
+    char* lds;
+    int c0, c1, T;
+    size_t tok_base;
+    bool with_q;
+
+    __device__ char* buffer(int c) const { return lds + ((c - c0) & 1) * IO::BUF; }
+
+    __device__ void stage(const bf16_t* q, const bf16_t* k, const bf16_t* v, int c, const Lane& L) {
+        if (c >= c1) return;
+        const int n = min(C, T - c * C);
+        const size_t tok0 = tok_base + (size_t)c * C;
+        if (n == C) IO::stage_async(q, k, v, tok0, buffer(c), with_q, L);
+        else IO::stage_ragged(q, k, v, tok0, n, buffer(c), with_q, L);
+    }
+    __device__ void acquire(const bf16_t* q, const bf16_t* k, const bf16_t* v, int c, const Lane& L) {
+        wait_vmcnt<0>();
+        lds_barrier();
+        stage(q, k, v, c + 1, L);
+    }
+};
+
+}  // namespace kata

@@ -36,9 +36,8 @@
 // Across chunks, z = sum phi(k) is kept as the 16 x 16 Gram matrix
 // Z = sum k k^T (one accumulator tile; z is its packed upper triangle), and
 // phi(q).z = q^T Z q is one MFMA (Z q) plus a 4-term dot product per lane.
-#include "kata_device.h"
+#include "kata_chunk.h"
 #include "kata_internal.h"
-#include "kata_mfma.h"
 
 #include <algorithm>
 
@@ -82,174 +81,15 @@ struct State {
     f32x4_t zm;
 };
 
-struct Lane {
-    int lane, c16, g, w;
-    __device__ Lane()
-        : lane(threadIdx.x & 63), c16(threadIdx.x & 15), g((threadIdx.x >> 4) & 3),
-          w(threadIdx.x >> 6) {}
-};
-
-// Constant operands. ones: column (or row) 0 of the ones tile = 1 on every slot.
-__device__ __forceinline__ u32x4_t ones_op(const Lane& L) {
-    const uint32_t x = L.c16 == 0 ? 0x3f803f80u : 0u;   // bf16 1.0 twice
-    return u32x4_t{x, x, x, x};
-}
-// B operand of 16x16x32 selecting value column c16 + 16h of a 32-column block:
-// slot (g, s) stands for column 8g + s.
-__device__ __forceinline__ u32x4_t select32(const Lane& L, int h) {
-    u32x4_t r;
-    const int want = L.c16 + 16 * h;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int s0 = 8 * L.g + 2 * p;
-        r[p] = (s0 == want ? 0x3f80u : 0u) | (s0 + 1 == want ? 0x3f800000u : 0u);
-    }
-    return r;
-}
-// B operand of 16x16x16 = identity: slot (g, s) stands for row 4g + s.
-__device__ __forceinline__ u32x2_t ident16(const Lane& L) {
-    u32x2_t r;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int s0 = 4 * L.g + 2 * p;
-        r[p] = (s0 == L.c16 ? 0x3f80u : 0u) | (s0 + 1 == L.c16 ? 0x3f800000u : 0u);
-    }
-    return r;
-}
-
-// Workgroup barrier that waits only for this wavefront's LDS operations (not for
-// its outstanding global loads, which may be prefetches).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0), other counters free
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-}
-
-// Value of lane (c16 + d) mod 16 of the same row, for a compile-time tile d.
-template <int D>
-__device__ __forceinline__ float partner(float x) {
-    if constexpr (D == 0) return x;
-    else return row_fetch<D>(x);
-}
-
-// ---- chunk staging: q | k | v of one chunk, row-major as in HBM -------------
-// The 1 KB pieces of a full chunk are split round-robin over the wavefronts:
-// piece i goes to wavefront i % NW as a direct-to-LDS load (lane l moves bytes
-// [16l, 16l+16) of the piece).
-template <int DV, int C>
-__device__ __forceinline__ void stage_async(const bf16_t* q, const bf16_t* k, const bf16_t* v,
-                                            size_t tok0, char* buf, bool with_q, const Lane& L) {
-    using F = Cfg<DV, C>;
-    const char* gq = reinterpret_cast<const char*>(q + tok0 * DK);
-    const char* gk = reinterpret_cast<const char*>(k + tok0 * DK);
-    const char* gv = reinterpret_cast<const char*>(v + tok0 * DV);
-    constexpr int PQ = F::QB / 1024, PV = F::VB / 1024;
-    const int first = with_q ? 0 : PQ;
-#pragma unroll
-    for (int i = 0; i < 2 * PQ + PV; ++i) {
-        if (i < first || i % NW != L.w) continue;
-        const char* src = i < PQ ? gq + i * 1024
-                        : i < 2 * PQ ? gk + (i - PQ) * 1024
-                                     : gv + (i - 2 * PQ) * 1024;
-        __builtin_amdgcn_global_load_lds(src + L.lane * 16, (lds_void_t*)(buf + i * 1024), 16, 0, 0);
-    }
-}
-
-// Ragged chunk (n < C valid positions): bounded loads, zero fill, then LDS.
-template <int DV, int C>
-__device__ __forceinline__ void stage_ragged(const bf16_t* q, const bf16_t* k, const bf16_t* v,
-                                             size_t tok0, int n, char* buf, bool with_q,
-                                             const Lane& L) {
-    using F = Cfg<DV, C>;
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    const u32x4_t* gq = reinterpret_cast<const u32x4_t*>(q + tok0 * DK);
-    const u32x4_t* gk = reinterpret_cast<const u32x4_t*>(k + tok0 * DK);
-    const u32x4_t* gv = reinterpret_cast<const u32x4_t*>(v + tok0 * DV);
-    u32x4_t* lq = reinterpret_cast<u32x4_t*>(buf);
-    u32x4_t* lk = reinterpret_cast<u32x4_t*>(buf + F::QB);
-    u32x4_t* lv = reinterpret_cast<u32x4_t*>(buf + 2 * F::QB);
-    constexpr int QU = F::QB / 16, VU = F::VB / 16;       // 16-byte units
-    constexpr int QPR = DK * 2 / 16, VPR = DV * 2 / 16;   // units per row
-    const int tid = L.w * 64 + L.lane, nthr = NW * 64;
-    for (int u = tid; u < QU; u += nthr) {
-        const bool ok = u / QPR < n;
-        if (with_q) lq[u] = ok ? gq[u] : zero;
-        lk[u] = ok ? gk[u] : zero;
-    }
-    for (int u = tid; u < VU; u += nthr) lv[u] = (u / VPR < n) ? gv[u] : zero;
-    compiler_fence();
-}
-
-// Chunk c of a segment [c0, c1) lives in buffer (c - c0) % NBUF and is staged one
-// iteration ahead. Per iteration: wait for every outstanding memory operation of
-// this wavefront (its part of chunk c, and the output stores of chunk c-1,
-// issued before the state update and normally retired by now: on this target
-// loads and stores may retire out of order, so a partial count is not a safe
-// bound), barrier (every part present, both wavefronts done with chunk c-1),
-// then stage chunk c+1 into chunk c-1's buffer.
-template <int DV, int C>
-struct Pipeline {
-    using F = Cfg<DV, C>;
-    char* lds;
-    int c0, c1, T;
-    size_t tok_base;
-    bool with_q;
-
-    __device__ char* buffer(int c) const { return lds + ((c - c0) % F::NBUF) * F::BUF; }
-
-    __device__ void stage(const bf16_t* q, const bf16_t* k, const bf16_t* v, int c, const Lane& L) {
-        if (c >= c1) return;
-        const int n = min(C, T - c * C);
-        const size_t tok0 = tok_base + (size_t)c * C;
-        if (n == C) stage_async<DV, C>(q, k, v, tok0, buffer(c), with_q, L);
-        else stage_ragged<DV, C>(q, k, v, tok0, n, buffer(c), with_q, L);
-    }
-    __device__ void acquire(const bf16_t* q, const bf16_t* k, const bf16_t* v, int c, const Lane& L) {
-        wait_vmcnt<0>();
-        lds_barrier();
-        stage(q, k, v, c + 1, L);
-    }
-};
-
 // ---- per-chunk fragments ----------------------------------------------------
 
-// V^T fragments of K-step m: vop[nt] = 8 values v[token][16nt + c16] for the
-// tokens 32m + 16(s/4) + 4g + s%4 (slot s). Built by multiplying row-major V
-// blocks with selection matrices (the accumulator layout performs the transpose).
+// V^T fragments of K-step m (slot s = token 32m + 16(s/4) + 4g + s%4, lane =
+// value column), read transposed from the row-major chunk in LDS.
 template <int DV, int C>
 __device__ __forceinline__ void v_fragment_step(const bf16_t* bv, u32x4_t (&vop)[Cfg<DV, C>::NTV],
                                                 int m, const Lane& L) {
-    using F = Cfg<DV, C>;
-    if constexpr (F::NTV % 2 == 0) {
-        const u32x4_t sel0 = select32(L, 0), sel1 = select32(L, 1);
 #pragma unroll
-        for (int ntp = 0; ntp < F::NTV / 2; ++ntp) {
-            f32x4_t t[2][2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(
-                    bv + (32 * m + 16 * h + L.c16) * DV + 32 * ntp + 8 * L.g);
-                t[h][0] = mma32(vf, sel0, zero4());
-                t[h][1] = mma32(vf, sel1, zero4());
-            }
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-                vop[2 * ntp + e] = u32x4_t{pk2(t[0][e][0], t[0][e][1]), pk2(t[0][e][2], t[0][e][3]),
-                                           pk2(t[1][e][0], t[1][e][1]), pk2(t[1][e][2], t[1][e][3])};
-        }
-    } else {
-        static_assert(F::NTV == 1, "odd value-tile count is only 1");
-        const u32x2_t id = ident16(L);
-        f32x4_t t[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const u32x2_t vf = *reinterpret_cast<const u32x2_t*>(
-                bv + (32 * m + 16 * h + L.c16) * DV + 4 * L.g);
-            t[h] = mma16(vf, id, zero4());
-        }
-        vop[0] = u32x4_t{pk2(t[0][0], t[0][1]), pk2(t[0][2], t[0][3]),
-                         pk2(t[1][0], t[1][1]), pk2(t[1][2], t[1][3])};
-    }
+    for (int nt = 0; nt < Cfg<DV, C>::NTV; ++nt) vop[nt] = v_fragment_tr<DV>(bv, m, nt, L);
 }
 
 // KT[jb][r] = k[16jb + 4g + r][c16] (fp32, exact) via an identity product.
@@ -379,7 +219,7 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
     using F = Cfg<DV, C>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    Pipeline<DV, C> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, false};
+    Pipeline<DK, DV, C, NW> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, false};
     State<DV, C> st;
 #pragma unroll
     for (int i = 0; i < NSLOT; ++i)
@@ -411,7 +251,7 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
     using F = Cfg<DV, C>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    Pipeline<DV, C> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true};
+    Pipeline<DK, DV, C, NW> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true};
     // exchange buffer: partials for query tile (u of wavefront w) at [w][u][nt][lane]
     f32x4_t* xbuf = reinterpret_cast<f32x4_t*>(lds + F::NBUF * F::BUF);
 
@@ -467,7 +307,7 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
                     for (int r = 0; r < 4; ++r) f[r] = (2.0f * qr[r]) * qr[(r + 8) & 15];
                     const u32x2_t fq = {pk2(f[0], f[1]), pk2(f[2], f[3])};
 #pragma unroll
-                    for (int nt = 0; nt < F::NTV; ++nt) part[nt] = mma16(sop8[nt], fq, part[nt]);
+                    for (int nt = 0; nt < F::NTV; ++nt) part[nt] = mma16_acc32(sop8[nt], fq, part[nt]);
                 }
                 const int u = tt / NW;
                 if (tt % NW == W) {

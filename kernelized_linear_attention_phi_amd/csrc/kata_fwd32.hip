@@ -1,0 +1,666 @@
+// Fused bf16 chunked-state forward for d_k = 32 on gfx950 matrix cores.
+//
+// Method (KATA explainers, gist.science, technical summary 2.3; the paper's
+// abstract): the sequence is cut into chunks of C positions; each output is the
+// masked intra-chunk term plus phi(Q_c) times the prefix of chunk states; the
+// prefix is propagated by an associative scan. One workgroup of four wavefronts
+// owns a segment of G consecutive chunks of one (batch, head) and carries the
+// running state S = sum phi(k) v^T in registers across the segment:
+//   kata_seg_state32 : segment totals         (phi(K)^T V on MFMA)
+//   (scan kernel)    : exclusive prefix over segments of each head
+//   kata_fwd32       : per chunk, inter (phi(Q).S) and intra (QK^T -> square ->
+//                      mask -> A.V) on MFMA, normalise, store, then
+//                      S += phi(K)^T V.
+//
+// Feature order. With L = coordinates 0..15 and U = 16..31 of a key, the
+// D = 528 unique products x_a x_b fill exactly 33 tiles of 16 rows rho:
+//   tiles  0..7  : L[rho] * L[(rho + delta) mod 16],  delta = 0..7
+//   tiles  8..15 : U[rho] * U[(rho + delta) mod 16],  delta = 0..7
+//   tiles 16..31 : L[rho] * U[(rho + delta) mod 16],  delta = 0..15
+//   tile  32     : L[rho] * L[rho + 8] (rho < 8), U[rho - 8] * U[rho] (rho >= 8)
+// so every key lift is a product of a lane's own coordinate with a DPP-rotated
+// one, and no row is padding. The state holds plain sums of k_a k_b v; the
+// factor 2 of an off-diagonal pair sits on the query side.
+//
+// Work split. Wavefront w owns feature tiles 8w..8w+7 for every value tile, the
+// value tile nt = w of tile 32, and one Gram tile (below): it lifts keys only
+// for those and updates only those rows of S. Once per chunk each wavefront
+// writes its part of S (as bf16 matrix-core operands) to LDS; each wavefront
+// then finishes its own query tiles {w, TT-1-w} against the whole state, so the
+// causal intra-chunk work is balanced and no partial sums are exchanged.
+//
+// Denominators. Inside a chunk, sum_j A_tj comes from the A.V MFMAs through a
+// "ones" value tile. Across chunks, z = sum phi(k) is kept as the Gram matrix
+// Z = sum k k^T in four 16 x 16 tiles (LL, LU, UL, UU; wavefront w keeps tile
+// w), and phi(q).z = q^T Z q is two MFMAs (Z q) plus an 8-term dot product.
+#include "kata_chunk.h"
+#include "kata_internal.h"
+
+#include <algorithm>
+#include <type_traits>
+
+namespace kata {
+
+namespace {
+
+constexpr int DK = 32;
+constexpr int NFT = 33;                 // feature tiles
+constexpr int NW = 4;                   // wavefronts per segment
+constexpr int NZ = 4;                   // Gram tiles
+
+template <int DV, int C>
+struct Cfg32 {
+    static constexpr int NTV = DV / 16;           // value tiles
+    static constexpr int TT = C / 16;             // query tiles per chunk
+    static constexpr int TW = TT / NW;            // query tiles per wavefront
+    static constexpr int KS = C / 32;             // 32-token K-steps per chunk
+    using IO = ChunkIO<DK, DV, C, NW>;
+    // LDS: two chunk buffers | bf16 state operands | one output tile per wavefront
+    static constexpr int SPAIR = 16 * NTV * 1024;   // S^T operands of tile pairs 0..15
+    static constexpr int S32 = NTV * 512;           // S^T operands of tile 32
+    static constexpr int ZOP = 2 * 1024;            // Gram operands (rows L, rows U)
+    static constexpr int SB = SPAIR + S32 + ZOP;
+    static constexpr int OROW = DV * 2 + 16;        // LDS row stride of a staged output tile
+    static constexpr int OTILE = 16 * OROW;
+    static constexpr int OU = 2 * DV;               // 16-byte units per 16-row output tile
+    static constexpr int LDS_FWD = 2 * IO::BUF + SB + NW * OTILE;
+    static constexpr int LDS_SEG = 2 * IO::BUF;
+    static constexpr int REC = NFT * NTV * 256 + NZ * 256;   // floats per state record
+    static_assert(TW >= 1, "at least one query tile per wavefront");
+};
+
+// Running state of wavefront W: tiles 8W..8W+7 of S (all value tiles), value
+// tile W of tile 32 (when W < NTV), Gram tile W.
+template <int DV, int C>
+struct State32 {
+    f32x4_t s[8][Cfg32<DV, C>::NTV];
+    f32x4_t x;
+    f32x4_t z;
+};
+
+// Query tile of slot u of wavefront W.
+template <int W, int TT>
+__device__ __forceinline__ constexpr int own_query_tile(int u) {
+    return u == 0 ? W : TT - 1 - W;
+}
+
+// ---- lifts -----------------------------------------------------------------------
+
+// phi(K) rows of own tile I of wavefront W for the 8 tokens of one K-step:
+// kl / ku hold coordinate c16 / 16 + c16 of each token (fp32, exact).
+template <int W, int I>
+__device__ __forceinline__ u32x4_t lift_keys32(const float (&kl)[8], const float (&ku)[8]) {
+    float f[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        if constexpr (W == 0) f[s] = kl[s] * partner<I>(kl[s]);
+        else if constexpr (W == 1) f[s] = ku[s] * partner<I>(ku[s]);
+        else if constexpr (W == 2) f[s] = kl[s] * partner<I>(ku[s]);
+        else f[s] = kl[s] * partner<8 + I>(ku[s]);
+    }
+    return u32x4_t{pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
+}
+
+// Tile 32: rows < 8 pair L[rho] with L[rho + 8], rows >= 8 pair U[rho] with
+// U[rho - 8]; b is chosen so that the rotated fetch lands on the right half.
+__device__ __forceinline__ u32x4_t lift_keys_mixed(const float (&kl)[8], const float (&ku)[8],
+                                                   const Lane& L) {
+    const bool lo = L.c16 < 8;
+    float f[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const float a = lo ? kl[s] : ku[s];
+        const float b = lo ? ku[s] : kl[s];
+        f[s] = a * partner<8>(b);
+    }
+    return u32x4_t{pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
+}
+
+template <int W>
+__device__ __forceinline__ u32x4_t lift_keys_own(int i, const float (&kl)[8], const float (&ku)[8]) {
+    switch (i) {
+        case 0: return lift_keys32<W, 0>(kl, ku);
+        case 1: return lift_keys32<W, 1>(kl, ku);
+        case 2: return lift_keys32<W, 2>(kl, ku);
+        case 3: return lift_keys32<W, 3>(kl, ku);
+        case 4: return lift_keys32<W, 4>(kl, ku);
+        case 5: return lift_keys32<W, 5>(kl, ku);
+        case 6: return lift_keys32<W, 6>(kl, ku);
+        default: return lift_keys32<W, 7>(kl, ku);
+    }
+}
+
+// One query row (t = 16 tt + c16) in registers: a[x] = q[(x + 4g) mod 16],
+// b[x] = q[16 + (x + 4g) mod 16], a2 / b2 = 2 a / 2 b for x < 4, and the raw bf16
+// q[4g..4g+3] | q[16+4g..16+4g+3] (the B operand of Z q).
+struct QueryRow {
+    float a[16], b[16], a2[4], b2[4];
+    u32x4_t zf;
+};
+
+__device__ __forceinline__ void load_query32(const bf16_t* bq, int tt, const Lane& L, QueryRow& Q) {
+    const bf16_t* row = bq + (16 * tt + L.c16) * DK;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float* dst = h ? Q.b : Q.a;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const u32x2_t piece =
+                *reinterpret_cast<const u32x2_t*>(row + 16 * h + 4 * ((L.g + p) & 3));
+            if (p == 0) {
+                Q.zf[2 * h] = piece[0];
+                Q.zf[2 * h + 1] = piece[1];
+            }
+            dst[4 * p + 0] = lo_bf16(piece[0]);
+            dst[4 * p + 1] = hi_bf16(piece[0]);
+            dst[4 * p + 2] = lo_bf16(piece[1]);
+            dst[4 * p + 3] = hi_bf16(piece[1]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        Q.a2[r] = 2.0f * Q.a[r];
+        Q.b2[r] = 2.0f * Q.b[r];
+    }
+}
+
+// phi(q) entry of feature tile T, row 4g + r (off-diagonal entries doubled).
+template <int T>
+__device__ __forceinline__ float query_entry(const QueryRow& Q, int r, bool lo_rows) {
+    if constexpr (T == 0) return Q.a[r] * Q.a[r];
+    else if constexpr (T < 8) return Q.a2[r] * Q.a[(r + T) & 15];
+    else if constexpr (T == 8) return Q.b[r] * Q.b[r];
+    else if constexpr (T < 16) return Q.b2[r] * Q.b[(r + T - 8) & 15];
+    else if constexpr (T < 32) return Q.a2[r] * Q.b[(r + T - 16) & 15];
+    else return lo_rows ? Q.a2[r] * Q.a[r + 8] : Q.b2[r] * Q.b[r + 8];
+}
+
+// B operand of the tile pair (T, T + 1): slots 0..3 = tile T rows 4g + s,
+// slots 4..7 = tile T + 1.
+template <int T>
+__device__ __forceinline__ u32x4_t lift_query_pair(const QueryRow& Q, const Lane& L) {
+    const bool lo = L.g < 2;
+    return u32x4_t{pk2(query_entry<T>(Q, 0, lo), query_entry<T>(Q, 1, lo)),
+                   pk2(query_entry<T>(Q, 2, lo), query_entry<T>(Q, 3, lo)),
+                   pk2(query_entry<T + 1>(Q, 0, lo), query_entry<T + 1>(Q, 1, lo)),
+                   pk2(query_entry<T + 1>(Q, 2, lo), query_entry<T + 1>(Q, 3, lo))};
+}
+
+__device__ __forceinline__ u32x2_t lift_query_mixed(const QueryRow& Q, const Lane& L) {
+    const bool lo = L.g < 2;
+    return u32x2_t{pk2(query_entry<32>(Q, 0, lo), query_entry<32>(Q, 1, lo)),
+                   pk2(query_entry<32>(Q, 2, lo), query_entry<32>(Q, 3, lo))};
+}
+
+// Compile-time loop over tile pairs.
+template <int P, int NP, typename F>
+__device__ __forceinline__ void for_pairs(F&& f) {
+    if constexpr (P < NP) {
+        f(std::integral_constant<int, P>{});
+        for_pairs<P + 1, NP>(f);
+    }
+}
+
+// ---- K^T fragments ----------------------------------------------------------------
+
+// kl[s] / ku[s] = k[token(s)][c16] / k[token(s)][16 + c16] for the 8 tokens of
+// K-step m (slot s = token 32m + 16(s/4) + 4g + s%4), via identity products.
+__device__ __forceinline__ void key_columns(const bf16_t* bk, int m, const Lane& L, bool need_l,
+                                            bool need_u, float (&kl)[8], float (&ku)[8]) {
+    const u32x2_t id = ident16(L);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const bf16_t* row = bk + (32 * m + 16 * h + L.c16) * DK + 4 * L.g;
+        f32x4_t tl = zero4(), tu = zero4();
+        if (need_l) tl = mma16(*reinterpret_cast<const u32x2_t*>(row), id, zero4());
+        if (need_u) tu = mma16(*reinterpret_cast<const u32x2_t*>(row + 16), id, zero4());
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            kl[4 * h + r] = tl[r];
+            ku[4 * h + r] = tu[r];
+        }
+    }
+}
+
+__device__ __forceinline__ u32x4_t pack8(const float (&x)[8]) {
+    return u32x4_t{pk2(x[0], x[1]), pk2(x[2], x[3]), pk2(x[4], x[5]), pk2(x[6], x[7])};
+}
+
+// S(own tiles) += phi(K_m)^T V_m, Z(own tile) += K_m^T K_m over one K-step.
+template <int W, int DV, int C>
+__device__ __forceinline__ void state_step(State32<DV, C>& st, const bf16_t* bk, const bf16_t* bv,
+                                           int m, const Lane& L) {
+    using F = Cfg32<DV, C>;
+    constexpr bool has_x = W < F::NTV;
+    float kl[8], ku[8];
+    // every wavefront needs L (own tiles, or the L row of its Gram tile LU / UL);
+    // wavefront 0 needs U only for tile 32
+    key_columns(bk, m, L, true, W != 0 || has_x, kl, ku);
+    // Gram tile W: LL, LU, UL, UU (A rows = first half, B columns = second)
+    {
+        const u32x4_t gl = pack8(kl), gu = pack8(ku);
+        if constexpr (W == 0) st.z = mma32(gl, gl, st.z);
+        else if constexpr (W == 1) st.z = mma32(gl, gu, st.z);
+        else if constexpr (W == 2) st.z = mma32(gu, gl, st.z);
+        else st.z = mma32(gu, gu, st.z);
+    }
+    u32x4_t vop[F::NTV];
+#pragma unroll
+    for (int nt = 0; nt < F::NTV; ++nt) vop[nt] = v_fragment_tr<DV>(bv, m, nt, L);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const u32x4_t fk = lift_keys_own<W>(i, kl, ku);
+#pragma unroll
+        for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] = mma32(fk, vop[nt], st.s[i][nt]);
+    }
+    if constexpr (has_x) st.x = mma32(lift_keys_mixed(kl, ku, L), vop[W], st.x);
+}
+
+// ---- state records: S unit (tile t, value tile nt) at ((t*NTV + nt)*64 + lane)*4 + r,
+// Gram tile zt at NFT*NTV*256 + (zt*64 + lane)*4 + r -----------------------------------
+
+template <int W, int DV, int C>
+__device__ __forceinline__ void record_store32(float* rec, const State32<DV, C>& st, const Lane& L) {
+    using F = Cfg32<DV, C>;
+    f32x4_t* r4 = reinterpret_cast<f32x4_t*>(rec);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int nt = 0; nt < F::NTV; ++nt)
+            r4[((8 * W + i) * F::NTV + nt) * 64 + L.lane] = st.s[i][nt];
+    if constexpr (W < F::NTV) r4[(32 * F::NTV + W) * 64 + L.lane] = st.x;
+    r4[(NFT * F::NTV + W) * 64 + L.lane] = st.z;
+}
+
+template <int W, int DV, int C>
+__device__ __forceinline__ void record_load32(const float* rec, State32<DV, C>& st, const Lane& L) {
+    using F = Cfg32<DV, C>;
+    const f32x4_t* r4 = reinterpret_cast<const f32x4_t*>(rec);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int nt = 0; nt < F::NTV; ++nt)
+            st.s[i][nt] = r4[((8 * W + i) * F::NTV + nt) * 64 + L.lane];
+    st.x = W < F::NTV ? r4[(32 * F::NTV + W) * 64 + L.lane] : zero4();
+    st.z = r4[(NFT * F::NTV + W) * 64 + L.lane];
+}
+
+// bf16 operands of this wavefront's part of the state, for every wavefront:
+// pair p, value tile nt at SPAIR-offset ((p*NTV + nt)*64 + lane)*16 (A = S^T:
+// lane = value column, slots 0..3 = tile 2p rows 4g+s, 4..7 = tile 2p+1);
+// tile 32 at S32-offset (nt*64 + lane)*8; Gram rows L (Z_LL | Z_UL) and rows U
+// (Z_LU | Z_UU) at ZOP-offset (half*64 + lane)*16 (+8 for the second tile).
+template <int W, int DV, int C>
+__device__ __forceinline__ void publish_state(char* sb, const State32<DV, C>& st, const Lane& L) {
+    using F = Cfg32<DV, C>;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int nt = 0; nt < F::NTV; ++nt) {
+            const f32x4_t& x = st.s[2 * j][nt];
+            const f32x4_t& y = st.s[2 * j + 1][nt];
+            *reinterpret_cast<u32x4_t*>(sb + (((4 * W + j) * F::NTV + nt) * 64 + L.lane) * 16) =
+                u32x4_t{pk2(x[0], x[1]), pk2(x[2], x[3]), pk2(y[0], y[1]), pk2(y[2], y[3])};
+        }
+    if constexpr (W < F::NTV)
+        *reinterpret_cast<u32x2_t*>(sb + F::SPAIR + (W * 64 + L.lane) * 8) =
+            u32x2_t{pk2(st.x[0], st.x[1]), pk2(st.x[2], st.x[3])};
+    constexpr int half = (W == 1 || W == 3) ? 1 : 0, part = W >= 2 ? 1 : 0;
+    *reinterpret_cast<u32x2_t*>(sb + F::SPAIR + F::S32 + (half * 64 + L.lane) * 16 + part * 8) =
+        u32x2_t{pk2(st.z[0], st.z[1]), pk2(st.z[2], st.z[3])};
+}
+
+// ---- per-wavefront bodies ----------------------------------------------------------
+
+template <int W, int DV, int C>
+__device__ __forceinline__ void seg_state_body32(const bf16_t* k, const bf16_t* v, float* rec,
+                                                 char* lds, int T, int NC, int G, int NSEG,
+                                                 const Lane& L) {
+    using F = Cfg32<DV, C>;
+    const int seg = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    Pipeline<DK, DV, C, NW> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, false};
+    State32<DV, C> st;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] = zero4();
+    st.x = zero4();
+    st.z = zero4();
+
+    P.stage(nullptr, k, v, P.c0, L);
+    for (int c = P.c0; c < P.c1; ++c) {
+        P.acquire(nullptr, k, v, c, L);
+        const char* buf = P.buffer(c);
+        const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::IO::QB);
+        const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::IO::QB);
+#pragma unroll
+        for (int m = 0; m < F::KS; ++m) state_step<W, DV, C>(st, bk, bv, m, L);
+        compiler_fence();
+    }
+    record_store32<W, DV, C>(rec + (bh * NSEG + seg) * (size_t)F::REC, st, L);
+}
+
+template <int W, int DV, int C, bool CAUSAL>
+__device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                                           const float* prefix, bf16_t* o, char* lds, int T,
+                                           int NC, int G, int NSEG, const Lane& L) {
+    using F = Cfg32<DV, C>;
+    const int seg = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    Pipeline<DK, DV, C, NW> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true};
+    char* sb = lds + 2 * F::IO::BUF;
+    char* otile = sb + F::SB + W * F::OTILE;
+
+    State32<DV, C> st;
+    record_load32<W, DV, C>(prefix + (CAUSAL ? bh * NSEG + seg : bh) * (size_t)F::REC, st, L);
+
+    P.stage(q, k, v, P.c0, L);
+    for (int c = P.c0; c < P.c1; ++c) {
+        const int n = min(C, T - c * C);
+        P.acquire(q, k, v, c, L);
+        const char* buf = P.buffer(c);
+        const bf16_t* bq = reinterpret_cast<const bf16_t*>(buf);
+        const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::IO::QB);
+        const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::IO::QB);
+
+        // the state before this chunk, as bf16 operands for every wavefront (the
+        // acquire barrier guarantees the previous chunk's readers are done)
+        if (CAUSAL || c == P.c0) {
+            publish_state<W, DV, C>(sb, st, L);
+            lds_barrier();
+        }
+
+        f32x4_t num[F::TW][F::NTV + 1];
+        float di[F::TW];
+#pragma unroll
+        for (int u = 0; u < F::TW; ++u) {
+            // ---- inter-chunk term phi(Q).P and q^T Z q for own query tile u
+            const int tt = own_query_tile<W, F::TT>(u);
+            QueryRow Q;
+            load_query32(bq, tt, L, Q);
+#pragma unroll
+            for (int nt = 0; nt <= F::NTV; ++nt) num[u][nt] = zero4();
+            for_pairs<0, 16>([&](auto pc) {
+                constexpr int p = decltype(pc)::value;
+                const u32x4_t fq = lift_query_pair<2 * p>(Q, L);
+#pragma unroll
+                for (int nt = 0; nt < F::NTV; ++nt) {
+                    const u32x4_t a =
+                        *reinterpret_cast<const u32x4_t*>(sb + ((p * F::NTV + nt) * 64 + L.lane) * 16);
+                    num[u][nt] = mma32(a, fq, num[u][nt]);
+                }
+            });
+            {
+                const u32x2_t fq = lift_query_mixed(Q, L);
+#pragma unroll
+                for (int nt = 0; nt < F::NTV; ++nt) {
+                    const u32x2_t a =
+                        *reinterpret_cast<const u32x2_t*>(sb + F::SPAIR + (nt * 64 + L.lane) * 8);
+                    num[u][nt] = mma16_acc32(a, fq, num[u][nt]);
+                }
+            }
+            const char* zb = sb + F::SPAIR + F::S32;
+            const f32x4_t zl = mma32(*reinterpret_cast<const u32x4_t*>(zb + L.lane * 16), Q.zf, zero4());
+            const f32x4_t zu =
+                mma32(*reinterpret_cast<const u32x4_t*>(zb + (64 + L.lane) * 16), Q.zf, zero4());
+            float d = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                d = __builtin_fmaf(Q.a[r], zl[r], d);
+                d = __builtin_fmaf(Q.b[r], zu[r], d);
+            }
+            d += __shfl_xor(d, 16, 64);
+            d += __shfl_xor(d, 32, 64);
+            di[u] = d;
+
+            // ---- intra-chunk term: A = (Q K^T)^2 masked to j <= t, num += A [V | 1]
+            if (CAUSAL) {
+                const int t = 16 * tt + L.c16;
+                const u32x4_t qf = *reinterpret_cast<const u32x4_t*>(bq + t * DK + 8 * L.g);
+                const u32x4_t ones = ones_op(L);
+                for (int m = 0; m <= tt / 2; ++m) {
+                    const bool diag = 32 * m + 31 > 16 * tt;
+                    float w[8];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(
+                            bk + (32 * m + 16 * h + L.c16) * DK + 8 * L.g);
+                        // rows j = 32m + 16h + 4g + r, column t
+                        const f32x4_t sc = mma32(kf, qf, zero4());
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = 32 * m + 16 * h + 4 * L.g + r;
+                            const float x = sc[r] * sc[r];
+                            w[4 * h + r] = (!diag || j <= t) ? x : 0.0f;
+                        }
+                    }
+                    const u32x4_t at = pack8(w);
+#pragma unroll
+                    for (int nt = 0; nt < F::NTV; ++nt)
+                        num[u][nt] = mma32(v_fragment_tr<DV>(bv, m, nt, L), at, num[u][nt]);
+                    num[u][F::NTV] = mma32(ones, at, num[u][F::NTV]);
+                }
+            }
+        }
+
+        // ---- normalise and store: o = num / den
+        bf16_t* oc = o + (bh * T + (size_t)c * C) * DV;
+#pragma unroll
+        for (int u = 0; u < F::TW; ++u) {
+            const int tt = own_query_tile<W, F::TT>(u);
+            // intra-chunk denominator: row 0 of the ones tile (lane group 0)
+            const float den = __shfl(num[u][F::NTV][0], L.c16, 64) + di[u];
+            const float y = den != 0.0f ? 1.0f / den : 0.0f;   // y = 0 gives o = 0
+#pragma unroll
+            for (int nt = 0; nt < F::NTV; ++nt) {
+                float ov[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // Markstein: with y = RN(1/den), q0 + RN(num - q0 den) y = RN(num/den)
+                    const float x = num[u][nt][r];
+                    const float q0 = x * y;
+                    const float er = __builtin_fmaf(-q0, den, x);
+                    ov[r] = __builtin_fmaf(er, y, q0);
+                }
+                *reinterpret_cast<u32x2_t*>(otile + L.c16 * F::OROW + 2 * (16 * nt + 4 * L.g)) =
+                    u32x2_t{pk2(ov[0], ov[1]), pk2(ov[2], ov[3])};
+            }
+#pragma unroll
+            for (int i = 0; i < (F::OU + 63) / 64; ++i) {
+                const int unit = L.lane + 64 * i;
+                const int row = unit / (F::OU / 16), col = unit % (F::OU / 16);
+                if (unit < F::OU) {
+                    const u32x4_t val = *reinterpret_cast<const u32x4_t*>(otile + row * F::OROW + 16 * col);
+                    if (16 * tt + row < n)
+                        *reinterpret_cast<u32x4_t*>(oc + (size_t)(16 * tt + row) * DV + 8 * col) = val;
+                }
+            }
+        }
+
+        // ---- running state: S += phi(K_c)^T V_c, Z += K_c^T K_c
+        if (CAUSAL) {
+#pragma unroll
+            for (int m = 0; m < F::KS; ++m) state_step<W, DV, C>(st, bk, bv, m, L);
+        }
+        compiler_fence();
+    }
+}
+
+// ---- kernels -------------------------------------------------------------------
+
+template <int DV, int C>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void kata_seg_state32(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                      float* __restrict__ rec, int T, int NC, int G, int NSEG) {
+    using F = Cfg32<DV, C>;
+    __shared__ __attribute__((aligned(16))) char lds[F::LDS_SEG];
+    const Lane L;
+    switch (L.w) {
+        case 0: seg_state_body32<0, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L); break;
+        case 1: seg_state_body32<1, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L); break;
+        case 2: seg_state_body32<2, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L); break;
+        default: seg_state_body32<3, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L); break;
+    }
+}
+
+template <int DV, int C, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void kata_fwd32(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                const bf16_t* __restrict__ v, const float* __restrict__ prefix,
+                bf16_t* __restrict__ o, int T, int NC, int G, int NSEG) {
+    using F = Cfg32<DV, C>;
+    __shared__ __attribute__((aligned(16))) char lds[F::LDS_FWD];
+    const Lane L;
+    switch (L.w) {
+        case 0: fwd_body32<0, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L); break;
+        case 1: fwd_body32<1, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L); break;
+        case 2: fwd_body32<2, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L); break;
+        default: fwd_body32<3, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L); break;
+    }
+}
+
+template <int DV, int C>
+hipError_t launch_dv_c32(const Shape& s, const void* q, const void* k, const void* v, float* rec,
+                         const float* prefix, void* o, int causal, int G, int NSEG,
+                         bool state_only, hipStream_t st) {
+    dim3 grid(NSEG, s.B * s.H);
+    if (state_only) {
+        kata_seg_state32<DV, C><<<grid, 64 * NW, 0, st>>>((const bf16_t*)k, (const bf16_t*)v, rec,
+                                                           s.T, s.NC, G, NSEG);
+    } else if (causal) {
+        kata_fwd32<DV, C, true><<<grid, 64 * NW, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
+                                                           (const bf16_t*)v, prefix, (bf16_t*)o,
+                                                           s.T, s.NC, G, NSEG);
+    } else {
+        kata_fwd32<DV, C, false><<<grid, 64 * NW, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
+                                                            (const bf16_t*)v, prefix, (bf16_t*)o,
+                                                            s.T, s.NC, G, NSEG);
+    }
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t launch_c32(const Shape& s, const void* q, const void* k, const void* v, float* rec,
+                      const float* prefix, void* o, int causal, int G, int NSEG, bool state_only,
+                      hipStream_t st) {
+    switch (s.dv) {
+        case 16: return launch_dv_c32<16, C>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+        case 32: return launch_dv_c32<32, C>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+        case 64: return launch_dv_c32<64, C>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t dispatch32(const Shape& s, const void* q, const void* k, const void* v, float* rec,
+                      const float* prefix, void* o, int causal, int G, int NSEG, bool state_only,
+                      hipStream_t st) {
+    switch (s.C) {
+        case 64: return launch_c32<64>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+        case 128: return launch_c32<128>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Record element -> (packed feature index, value column or -1 for z, scale);
+// lower = true for Gram entries below the diagonal (skipped on export, filled on
+// import).
+__device__ __forceinline__ int record_to_packed32(int idx, int NTV, int* col, float* scale,
+                                                  bool* lower) {
+    const int sz = NFT * NTV * 256;
+    int a, b;
+    *lower = false;
+    if (idx >= sz) {                                 // Gram tile zt, Z[i][j]
+        const int e = idx - sz;
+        const int zt = e >> 8, lane = (e >> 2) & 63;
+        const int i = 4 * (lane >> 4) + (e & 3), j = lane & 15;
+        a = i + ((zt >> 1) ? 16 : 0);                // row half: L for LL, LU; U for UL, UU
+        b = j + ((zt & 1) ? 16 : 0);                 // column half: L for LL, UL; U for LU, UU
+        *col = -1;
+        *lower = a > b;
+    } else {
+        const int r = idx & 3, lane = (idx >> 2) & 63, nt = (idx >> 8) % NTV;
+        const int t = (idx >> 8) / NTV;
+        const int rho = 4 * (lane >> 4) + r;
+        *col = 16 * nt + (lane & 15);
+        if (t < 8) { a = rho; b = (rho + t) & 15; }
+        else if (t < 16) { a = 16 + rho; b = 16 + ((rho + t - 8) & 15); }
+        else if (t < 32) { a = rho; b = 16 + ((rho + t - 16) & 15); }
+        else if (rho < 8) { a = rho; b = rho + 8; }
+        else { a = 8 + rho; b = 16 + rho; }
+    }
+    *scale = a == b ? 1.0f : kSqrt2;
+    const int i = min(a, b), j = max(a, b);
+    return i * DK - i * (i - 1) / 2 + (j - i);
+}
+
+__global__ void record_from_packed32(float* __restrict__ rec, const float* __restrict__ S,
+                                     const float* __restrict__ z, int NTV, int REC, int nrec) {
+    const int D = DK * (DK + 1) / 2, DV = 16 * NTV;
+    for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < (size_t)REC * nrec;
+         x += (size_t)gridDim.x * blockDim.x) {
+        const size_t b = x / REC;
+        int col;
+        float scale;
+        bool lower;
+        const int p = record_to_packed32((int)(x % REC), NTV, &col, &scale, &lower);
+        rec[x] = (col >= 0 ? S[(b * D + p) * DV + col] : z[b * D + p]) / scale;
+    }
+}
+
+__global__ void record_to_packed32_kernel(const float* __restrict__ rec, float* __restrict__ S,
+                                          float* __restrict__ z, int NTV, int REC, int nrec) {
+    const int D = DK * (DK + 1) / 2, DV = 16 * NTV;
+    for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < (size_t)REC * nrec;
+         x += (size_t)gridDim.x * blockDim.x) {
+        const size_t b = x / REC;
+        int col;
+        float scale;
+        bool lower;
+        const int p = record_to_packed32((int)(x % REC), NTV, &col, &scale, &lower);
+        if (lower) continue;
+        const float val = rec[x] * scale;
+        if (col >= 0) S[(b * D + p) * DV + col] = val;
+        else z[b * D + p] = val;
+    }
+}
+
+}  // namespace
+
+bool mfma32_supported(const Shape& s) {
+    return s.bf16 && s.dk == 32 && (s.C == 64 || s.C == 128) &&
+           (s.dv == 16 || s.dv == 32 || s.dv == 64);
+}
+
+int mfma32_record_floats(int dv) { return NFT * (dv / 16) * 256 + NZ * 256; }
+
+hipError_t launch_seg_state32(const Shape& s, const void* k, const void* v, float* rec, int G,
+                              int NSEG, hipStream_t st) {
+    return dispatch32(s, nullptr, k, v, rec, nullptr, nullptr, 1, G, NSEG, true, st);
+}
+
+hipError_t launch_fwd32(const Shape& s, const void* q, const void* k, const void* v,
+                        const float* prefix, void* o, int causal, int G, int NSEG,
+                        hipStream_t st) {
+    return dispatch32(s, q, k, v, nullptr, prefix, o, causal, G, NSEG, false, st);
+}
+
+hipError_t launch_record_from_packed32(float* rec, const float* S, const float* z, int dv,
+                                       int nrec, hipStream_t st) {
+    const int REC = mfma32_record_floats(dv);
+    const size_t n = (size_t)REC * nrec;
+    const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+    record_from_packed32<<<blocks, 256, 0, st>>>(rec, S, z, dv / 16, REC, nrec);
+    return hipGetLastError();
+}
+
+hipError_t launch_record_to_packed32(const float* rec, float* S, float* z, int dv, int nrec,
+                                     hipStream_t st) {
+    const int REC = mfma32_record_floats(dv);
+    const size_t n = (size_t)REC * nrec;
+    const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+    record_to_packed32_kernel<<<blocks, 256, 0, st>>>(rec, S, z, dv / 16, REC, nrec);
+    return hipGetLastError();
+}
+
+}  // namespace kata

@@ -40,7 +40,7 @@ hipError_t launch_scan_records(float* rec, int nseq, int NR, int E, const float*
 // Copies (src != NULL) or zero-fills n floats.
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st);
 
-// ---- bf16 matrix-core path, d_k = 16 (one wavefront per segment of G chunks) ----
+// ---- bf16 matrix-core path, d_k = 16 (two wavefronts per segment of G chunks) ----
 
 bool mfma16_supported(const Shape& s);
 // floats per state record (accumulator order, see kata_fwd16.hip)
@@ -55,6 +55,20 @@ hipError_t launch_fwd16(const Shape& s, const void* q, const void* k, const void
 hipError_t launch_record_from_packed16(float* rec, const float* S, const float* z, int dv,
                                        int nrec, hipStream_t st);
 hipError_t launch_record_to_packed16(const float* rec, float* S, float* z, int dv, int nrec,
+                                     hipStream_t st);
+
+// ---- bf16 matrix-core path, d_k = 32 (four wavefronts per segment of G chunks) ----
+
+bool mfma32_supported(const Shape& s);
+int mfma32_record_floats(int dv);
+hipError_t launch_seg_state32(const Shape& s, const void* k, const void* v, float* rec, int G,
+                              int NSEG, hipStream_t st);
+hipError_t launch_fwd32(const Shape& s, const void* q, const void* k, const void* v,
+                        const float* prefix, void* o, int causal, int G, int NSEG,
+                        hipStream_t st);
+hipError_t launch_record_from_packed32(float* rec, const float* S, const float* z, int dv,
+                                       int nrec, hipStream_t st);
+hipError_t launch_record_to_packed32(const float* rec, float* S, float* z, int dv, int nrec,
                                      hipStream_t st);
 
 // ---- decode ----

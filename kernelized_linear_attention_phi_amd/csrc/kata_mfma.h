@@ -47,6 +47,15 @@ __device__ __forceinline__ f32x4_t mma16(u32x2_t a, u32x2_t b, f32x4_t c) {
                                                      __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
 }
 
+// D = A(16x16) * B(16x16) + C issued as a 16x16x32 with the upper K half zero.
+// Use it wherever a K = 16 product accumulates onto a 16x16x32 chain: feeding
+// one matrix-core opcode's result to another opcode's accumulator input has
+// produced stale sums on gfx950 with the wait states the compiler inserts, while
+// chains of one opcode are exact.
+__device__ __forceinline__ f32x4_t mma16_acc32(u32x2_t a, u32x2_t b, f32x4_t c) {
+    return mma32(u32x4_t{a[0], a[1], 0u, 0u}, u32x4_t{b[0], b[1], 0u, 0u}, c);
+}
+
 // Value of lane (c16 + k) mod 16 of the same 16-lane row (DPP row rotate by
 // 16 - k: row_ror:n delivers lane (c16 - n) mod 16).
 template <int K>

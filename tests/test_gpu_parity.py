@@ -32,19 +32,32 @@ def kata():
 
 
 def run_fwd(kata, q, k, v, dtype, C, causal=True, S0=None, z0=None, state=False):
+    """Forward through the raw entry point with every output and the workspace
+    pre-filled with NaN: an element the library fails to write, or scratch it
+    reads before writing, cannot pass for a correct value."""
     import torch
-    init = None if S0 is None else (dev(S0), dev(z0))
-    out = kata.chunked_fwd(dev(q, dtype), dev(k, dtype), dev(v, dtype), chunk=C, causal=causal,
-                           initial_state=init, return_state=state)
+    qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    B, H, T, dk = qd.shape
+    dv = vd.shape[-1]
+    D = dk * (dk + 1) // 2
+    nan = float("nan")
+    o = torch.full_like(vd, nan)
+    S_out = torch.full((B, H, D, dv), nan, device="cuda") if state else None
+    z_out = torch.full((B, H, D), nan, device="cuda") if state else None
+    code = 1 if dtype == "bf16" else 0
+    nbytes = kata.chunked_fwd_workspace(B, H, T, dk, dv, C, code, causal)
+    ws = torch.full((max(nbytes, 4) // 4,), nan, device="cuda")
+    kata.chunked_fwd_into(qd, kd, vd, o, C, causal, ws,
+                          S0=None if S0 is None else dev(S0), z0=None if z0 is None else dev(z0),
+                          S_out=S_out, z_out=z_out)
     torch.cuda.synchronize()
     if state:
-        o, (S, z) = out
-        return host(o), host(S), host(z)
-    return host(out)
+        return host(o), host(S_out), host(z_out)
+    return host(o)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("dk,dv", [(16, 16), (16, 64), (32, 64), (32, 32)])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (16, 64), (32, 64), (32, 32), (32, 16)])
 @pytest.mark.parametrize("C", [16, 32, 64, 128])
 def test_fwd_small_full(kata, dtype, dk, dv, C):
     """Several tiles and a ragged tail; every output compared."""
@@ -60,13 +73,13 @@ def test_fwd_small_full(kata, dtype, dk, dv, C):
 
 
 @pytest.mark.parametrize("G", [1, 2, 3, 5, 16, 40])
-@pytest.mark.parametrize("C,T", [(64, 1000), (32, 999)])
-def test_segment_lengths(kata, monkeypatch, G, C, T):
+@pytest.mark.parametrize("dk,C,T", [(16, 64, 1000), (16, 32, 999), (32, 128, 1000), (32, 64, 999)])
+def test_segment_lengths(kata, monkeypatch, G, dk, C, T):
     """Chunks per segment (running state carried across chunks, ragged last
     segment, one segment per head) must not change the result beyond rounding."""
     monkeypatch.setenv("KATA_SEGMENT_CHUNKS", str(G))
-    q, k, v = gen.gaussian_qkv(2, 3, T, 16, 64, seed=500 + G, dtype="bf16")
-    say(f"segments G={G} C={C} T={T}")
+    q, k, v = gen.gaussian_qkv(2, 3, T, dk, 64, seed=500 + G + dk, dtype="bf16")
+    say(f"segments G={G} dk={dk} C={C} T={T}")
     o, S, z = run_fwd(kata, q, k, v, "bf16", C, state=True)
     assert row_rel_err(o, O.brute_force(q, k, v)) <= TOL["bf16"]
     S_ref, z_ref = O.state_from_tokens(k, v)
@@ -78,6 +91,27 @@ def test_segment_lengths(kata, monkeypatch, G, C, T):
     assert row_rel_err(o2, ref2) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("dk,C", [(16, 32), (16, 64), (32, 64), (32, 128)])
+@pytest.mark.parametrize("dv", [16, 32, 64])
+def test_initial_state_every_query_tile(kata, dk, dv, C):
+    """Inter-chunk and intra-chunk terms combined in every query tile of every
+    wavefront: a nonzero initial state on a short causal sequence (first chunk
+    full, second ragged), for each matrix-core shape."""
+    T = C + C // 2 + 3
+    q, k, v = gen.gaussian_qkv(1, 2, T, dk, dv, seed=600 + dk + dv + C, dtype="bf16")
+    S0, z0 = (a.astype(np.float32) for a in O.state_from_tokens(
+        *gen.gaussian_qkv(1, 2, 50, dk, dv, seed=9, dtype="f32")[1:]))
+    say(f"initial state dk={dk} dv={dv} C={C}")
+    o, S, z = run_fwd(kata, q, k, v, "bf16", C, S0=S0, z0=z0, state=True)
+    ref = O.brute_force(q, k, v, S0=S0.astype(np.float64), z0=z0.astype(np.float64))
+    for t0 in range(0, T, 16):
+        assert row_rel_err(o[:, :, t0:t0 + 16], ref[:, :, t0:t0 + 16]) <= TOL["bf16"], f"rows {t0}.."
+    S_ref, z_ref = O.state_from_tokens(k, v)
+    S_ref, z_ref = S_ref + S0, z_ref + z0
+    assert state_rel_err(S, S_ref) <= STATE_TOL["bf16"]
+    assert state_rel_err(z, z_ref) <= STATE_TOL["bf16"]
+
+
 def test_tiny_fp32_workload(kata):
     w, q, k, v, _ = _inputs("tiny")
     say("tiny workload fp32")
@@ -86,11 +120,12 @@ def test_tiny_fp32_workload(kata):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("T", [1, 7, 63, 64, 65, 129, 200])
-def test_ragged_and_short(kata, dtype, T):
-    q, k, v = gen.gaussian_qkv(1, 2, T, 16, 64, seed=200 + T, dtype=dtype)
-    say(f"ragged dtype={dtype} T={T}")
-    o = run_fwd(kata, q, k, v, dtype, 64)
+@pytest.mark.parametrize("dk,C", [(16, 64), (32, 128)])
+@pytest.mark.parametrize("T", [1, 7, 63, 64, 65, 127, 128, 129, 200])
+def test_ragged_and_short(kata, dtype, dk, C, T):
+    q, k, v = gen.gaussian_qkv(1, 2, T, dk, 64, seed=200 + T, dtype=dtype)
+    say(f"ragged dtype={dtype} dk={dk} C={C} T={T}")
+    o = run_fwd(kata, q, k, v, dtype, C)
     assert row_rel_err(o, O.brute_force(q, k, v)) <= TOL[dtype]
     if T == 1:   # single token: o = (w v) / w, which rounds back to v
         if dtype == "bf16":
@@ -113,15 +148,17 @@ def test_empty_sequence_returns_initial_state(kata):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_noncausal(kata, dtype):
-    q, k, v = gen.gaussian_qkv(2, 2, 333, 16, 64, seed=7, dtype=dtype)
-    say(f"noncausal {dtype}")
-    o = run_fwd(kata, q, k, v, dtype, 64, causal=False)
+@pytest.mark.parametrize("dk,C", [(16, 64), (32, 128), (32, 64)])
+def test_noncausal(kata, dtype, dk, C):
+    q, k, v = gen.gaussian_qkv(2, 2, 333, dk, 64, seed=7, dtype=dtype)
+    say(f"noncausal {dtype} dk={dk} C={C}")
+    o = run_fwd(kata, q, k, v, dtype, C, causal=False)
     assert row_rel_err(o, O.brute_force(q, k, v, causal=False)) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("dk,C,G", [(16, 64, 0), (32, 128, 0), (16, 16, 0), (16, 64, 2), (16, 32, 3)])
+@pytest.mark.parametrize("dk,C,G", [(16, 64, 0), (32, 128, 0), (16, 16, 0), (16, 64, 2), (16, 32, 3),
+                                    (32, 64, 2), (32, 128, 3)])
 def test_bitwise_causality(kata, monkeypatch, dtype, dk, C, G):
     """Perturbing token j leaves every output before j bit-identical."""
     if G:
@@ -191,17 +228,18 @@ def test_scan_states(kata, dtype, dk, dv, C):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_resume_then_decode(kata, dtype):
+@pytest.mark.parametrize("dk,C", [(16, 64), (32, 128)])
+def test_resume_then_decode(kata, dtype, dk, C):
     """fwd(T1) -> state -> fwd(T2 | state) -> decode steps equals the oracle over
     the whole sequence."""
     import torch
     T1, T2, steps = 300, 200, 5
-    q, k, v = gen.gaussian_qkv(1, 3, T1 + T2 + steps, 16, 64, seed=77, dtype=dtype)
+    q, k, v = gen.gaussian_qkv(1, 3, T1 + T2 + steps, dk, 64, seed=77, dtype=dtype)
     ref = O.brute_force(q, k, v)
-    say(f"resume dtype={dtype}")
-    o1, S1, z1 = run_fwd(kata, q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], dtype, 64, state=True)
+    say(f"resume dtype={dtype} dk={dk} C={C}")
+    o1, S1, z1 = run_fwd(kata, q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], dtype, C, state=True)
     o2, S2, z2 = run_fwd(kata, q[:, :, T1:T1 + T2], k[:, :, T1:T1 + T2], v[:, :, T1:T1 + T2],
-                         dtype, 64, S0=S1.astype(np.float32), z0=z1.astype(np.float32), state=True)
+                         dtype, C, S0=S1.astype(np.float32), z0=z1.astype(np.float32), state=True)
     assert row_rel_err(o1, ref[:, :, :T1]) <= TOL[dtype]
     assert row_rel_err(o2, ref[:, :, T1:T1 + T2]) <= TOL[dtype]
     S = dev(S2[0].astype(np.float32))
@@ -240,11 +278,12 @@ def test_decode_one_step_from_state(kata, dtype, dk, dv):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_determinism(kata, dtype):
-    q, k, v = gen.gaussian_qkv(2, 4, 3000, 16, 64, seed=11, dtype=dtype)
-    say(f"determinism {dtype}")
-    a = run_fwd(kata, q, k, v, dtype, 64, state=True)
-    b = run_fwd(kata, q, k, v, dtype, 64, state=True)
+@pytest.mark.parametrize("dk,C", [(16, 64), (32, 128)])
+def test_determinism(kata, dtype, dk, C):
+    q, k, v = gen.gaussian_qkv(2, 4, 3000, dk, 64, seed=11, dtype=dtype)
+    say(f"determinism {dtype} dk={dk}")
+    a = run_fwd(kata, q, k, v, dtype, C, state=True)
+    b = run_fwd(kata, q, k, v, dtype, C, state=True)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
 
