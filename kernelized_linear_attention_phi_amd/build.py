@@ -29,6 +29,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
     "-Wall", "-Wno-unused-function",
+    # LDS buffers are reinterpreted between vector types (partials, staged rows);
+    # type-based alias analysis must not reorder those accesses
+    "-fno-strict-aliasing",
     # keep matrix-core accumulators in the VGPR file: the running state is both
     # an MFMA accumulator and a VALU operand (its bf16 conversion)
     "-mllvm", "-amdgpu-mfma-vgpr-form",

@@ -75,20 +75,40 @@ __device__ __forceinline__ u32x4_t v_fragment_tr(const bf16_t* bv, int m, int nt
     return u32x4_t{h2[0][0], h2[0][1], h2[1][0], h2[1][1]};
 }
 
+// Direct-to-LDS copy of 16 bytes per lane: lane l moves 16 bytes from gsrc (its
+// own address) to LDS lds_dst + 16 l (lds_dst wavefront-uniform, through M0).
+// Issued as inline assembly so that the compiler does not track it: with more
+// than eight such loads in flight it would otherwise make every later LDS read
+// wait for all of them, which serialises the one-chunk-ahead prefetch. Every
+// read of a staged buffer is ordered by the pipeline's own vmcnt wait and
+// barrier instead. The leading s_nop is the wait state between the M0 write the
+// compiler places before the statement and the DMA that reads M0.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_dst) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_dst) : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(p);
+}
+
 // ---- chunk staging: q | k | v of one chunk, row-major as in HBM -------------
-template <int DK, int DV, int C, int NW>
+// Full chunks are loaded by the first NLOAD wavefronts only (a wavefront that
+// issues no loads never waits for its own stores when it waits for data).
+template <int DK, int DV, int C, int NW, int NLOAD = NW>
 struct ChunkIO {
     static constexpr int QB = C * DK * 2;         // bytes of a q or k chunk
     static constexpr int VB = C * DV * 2;         // bytes of a v chunk
     static constexpr int BUF = 2 * QB + VB;       // one chunk buffer
     static_assert(QB % 1024 == 0 && VB % 1024 == 0, "chunks are whole 1 KB pieces");
 
-    // Full chunk: the 1 KB pieces are split round-robin over the wavefronts;
-    // piece i goes to wavefront i % NW as a direct-to-LDS load (lane l moves
-    // bytes [16l, 16l+16) of the piece).
+    // Full chunk: the 1 KB pieces are split round-robin over the loading
+    // wavefronts; piece i goes to wavefront i % NLOAD as a direct-to-LDS load
+    // (lane l moves bytes [16l, 16l+16) of the piece).
     static __device__ __forceinline__ void stage_async(const bf16_t* q, const bf16_t* k,
-                                                       const bf16_t* v, size_t tok0, char* buf,
-                                                       bool with_q, const Lane& L) {
+                                                       const bf16_t* v, size_t tok0,
+                                                       uint32_t buf_lds, bool with_q,
+                                                       const Lane& L) {
         const char* gq = reinterpret_cast<const char*>(q + tok0 * DK);
         const char* gk = reinterpret_cast<const char*>(k + tok0 * DK);
         const char* gv = reinterpret_cast<const char*>(v + tok0 * DV);
@@ -96,12 +116,11 @@ struct ChunkIO {
         const int first = with_q ? 0 : PQ;
 #pragma unroll
         for (int i = 0; i < 2 * PQ + PV; ++i) {
-            if (i < first || i % NW != L.w) continue;
+            if (i < first || i % NLOAD != L.w) continue;
             const char* src = i < PQ ? gq + i * 1024
                             : i < 2 * PQ ? gk + (i - PQ) * 1024
                                          : gv + (i - 2 * PQ) * 1024;
-            __builtin_amdgcn_global_load_lds(src + L.lane * 16, (lds_void_t*)(buf + i * 1024), 16,
-                                             0, 0);
+            dma16(src + L.lane * 16, buf_lds + i * 1024);
         }
     }
 
@@ -130,30 +149,33 @@ struct ChunkIO {
 };
 
 // Chunk c of a segment [c0, c1) lives in buffer (c - c0) % 2 and is staged one
-// iteration ahead. Per iteration: wait for every outstanding memory operation of
-// this wavefront (its part of chunk c, and its output stores of chunk c-1: loads
-// and stores may complete out of order, so no partial count is safe), barrier
-// (every wavefront's part has landed and everyone is done with the buffer chunk
-// c+1 will overwrite), then issue chunk c+1.
-template <int DK, int DV, int C, int NW>
+// iteration ahead. Per iteration: a loading wavefront waits for every
+// outstanding memory operation of its own (its part of chunk c, and any stores:
+// loads and stores may complete out of order, so no partial count is safe),
+// then all meet at a barrier (every part has landed and everyone is done with
+// the buffer chunk c+1 will overwrite), then chunk c+1 is issued.
+template <int DK, int DV, int C, int NW, int NLOAD = NW>
 struct Pipeline {
-    using IO = ChunkIO<DK, DV, C, NW>;
+    using IO = ChunkIO<DK, DV, C, NW, NLOAD>;
     char* lds;
     int c0, c1, T;
     size_t tok_base;
     bool with_q;
 
     __device__ char* buffer(int c) const { return lds + ((c - c0) & 1) * IO::BUF; }
+    __device__ uint32_t buffer_lds(int c) const {
+        return lds_address(lds) + ((c - c0) & 1) * IO::BUF;
+    }
 
     __device__ void stage(const bf16_t* q, const bf16_t* k, const bf16_t* v, int c, const Lane& L) {
         if (c >= c1) return;
         const int n = min(C, T - c * C);
         const size_t tok0 = tok_base + (size_t)c * C;
-        if (n == C) IO::stage_async(q, k, v, tok0, buffer(c), with_q, L);
+        if (n == C) IO::stage_async(q, k, v, tok0, buffer_lds(c), with_q, L);
         else IO::stage_ragged(q, k, v, tok0, n, buffer(c), with_q, L);
     }
     __device__ void acquire(const bf16_t* q, const bf16_t* k, const bf16_t* v, int c, const Lane& L) {
-        wait_vmcnt<0>();
+        if (L.w < NLOAD) wait_vmcnt<0>();
         lds_barrier();
         stage(q, k, v, c + 1, L);
     }

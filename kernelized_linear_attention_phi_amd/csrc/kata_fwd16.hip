@@ -23,13 +23,15 @@
 // tile and phi(Q) is built from a per-lane rotated copy of q: no LDS traffic
 // for either lift.
 //
-// Work split inside a segment. Wavefront 0 owns feature tiles {0,1,2,3,8},
-// wavefront 1 tiles {4,5,6,7}: each lifts keys and queries for its own tiles
-// only, updates its own rows of S, and computes partial numerators phi(Q).S for
-// all query rows of the chunk over its own tiles. The partials for the other
-// wavefront's query tiles (16-row tiles alternate between the two) go through
-// LDS once per chunk; each wavefront then finishes its own query tiles (intra
-// term, denominators, division, store).
+// Work split inside a segment. Wavefront 0 owns feature tiles 0..3, wavefront 1
+// tiles 4..7, and tile 8 is split by value tiles (the first half of them to
+// wavefront 0): each lifts keys and queries for its own tiles only, updates its
+// own rows of S, and computes partial numerators phi(Q).S for all query rows of
+// the chunk over its own tiles. The partials for the other wavefront's query
+// tiles (16-row tiles alternate between the two) go through LDS once per chunk;
+// each wavefront then finishes its own query tiles (intra term, denominators,
+// division). Wavefront 0 issues all chunk loads and no stores, wavefront 1 all
+// output stores, so waiting for chunk data never waits for stores.
 //
 // Denominators. Inside a chunk, sum_j A_tj comes from the same MFMAs as the
 // numerators through a value tile whose first column is 1 (the "ones" tile).
@@ -48,13 +50,6 @@ namespace {
 constexpr int DK = 16;
 constexpr int NMT = 9;                  // feature tiles (delta = 0..8)
 constexpr int NW = 2;                   // wavefronts per segment
-constexpr int NSLOT = 5;                // feature tiles per wavefront (at most)
-
-// Feature tile held in slot i of wavefront W.
-template <int W> __host__ __device__ constexpr int tile_of(int slot) {
-    return W == 0 ? (slot < 4 ? slot : 8) : 4 + slot;
-}
-template <int W> __host__ __device__ constexpr int nslots() { return W == 0 ? 5 : 4; }
 
 template <int DV, int C>
 struct Cfg {
@@ -68,16 +63,22 @@ struct Cfg {
     static constexpr int NBUF = 2;                // staging depth (prefetch distance 1)
     static constexpr int XB = NW * TW * NTV * 1024;   // exchange of partial numerators
     static constexpr int OROW = DV * 2 + 16;      // LDS row stride of a staged output tile
-    static constexpr int OU = 2 * DV;             // 16-byte units per 16-row output tile
     static constexpr int REC = NMT * NTV * 256 + 256;   // floats per state record
+    static constexpr int H8 = (NTV + 1) / 2;      // value tiles of tile 8 held by wavefront 0
+    static_assert(TW * 16 * OROW <= TW * NTV * 1024, "staged output fits its exchange half");
 };
 
-// Running state owned by one wavefront: its feature tiles of S (slots, see
-// tile_of) and the Gram matrix Z = sum k k^T (lane = column, rows 4g + r; both
-// wavefronts keep a copy).
+// Value tiles [lo8, hi8) of feature tile 8 belong to wavefront W.
+template <int W, int NTV> __host__ __device__ constexpr int lo8() { return W == 0 ? 0 : (NTV + 1) / 2; }
+template <int W, int NTV> __host__ __device__ constexpr int hi8() { return W == 0 ? (NTV + 1) / 2 : NTV; }
+
+// Running state of wavefront W: feature tiles 4W..4W+3 of S for every value
+// tile, value tiles [lo8, hi8) of tile 8, and the Gram matrix Z = sum k k^T
+// (lane = column, rows 4g + r).
 template <int DV, int C>
 struct State {
-    f32x4_t s[NSLOT][Cfg<DV, C>::NTV];
+    f32x4_t s[4][Cfg<DV, C>::NTV];
+    f32x4_t x[Cfg<DV, C>::H8];
     f32x4_t zm;
 };
 
@@ -118,36 +119,53 @@ __device__ __forceinline__ u32x4_t lift_keys(const float (&ka)[8], const Lane& L
     return u32x4_t{pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
 }
 
-// S(own tiles) += phi(K_c)^T V_c, Z += K_c^T K_c. vop[m] are the V^T fragments.
-template <int W, int DV, int C>
+template <int W>
+__device__ __forceinline__ u32x4_t lift_keys_own(int i, const float (&ka)[8], const Lane& L) {
+    if constexpr (W == 0) {
+        switch (i) {
+            case 0: return lift_keys<0>(ka, L);
+            case 1: return lift_keys<1>(ka, L);
+            case 2: return lift_keys<2>(ka, L);
+            default: return lift_keys<3>(ka, L);
+        }
+    } else {
+        switch (i) {
+            case 0: return lift_keys<4>(ka, L);
+            case 1: return lift_keys<5>(ka, L);
+            case 2: return lift_keys<6>(ka, L);
+            default: return lift_keys<7>(ka, L);
+        }
+    }
+}
+
+// S(own tiles) += phi(K_c)^T V_c; Z += K_c^T K_c when WITH_Z. vop[m] are the V^T
+// fragments.
+template <int W, bool WITH_Z, int DV, int C>
 __device__ __forceinline__ void state_update(State<DV, C>& st, const f32x4_t (&KT)[Cfg<DV, C>::TT],
                                              const u32x4_t (&vop)[Cfg<DV, C>::KS][Cfg<DV, C>::NTV],
                                              const Lane& L) {
     using F = Cfg<DV, C>;
+    constexpr int l8 = lo8<W, F::NTV>(), h8 = hi8<W, F::NTV>();
 #pragma unroll
     for (int m = 0; m < F::KS; ++m) {
         float ka[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) ka[s] = KT[2 * m + s / 4][s % 4];
-        // Gram matrix: A = K^T (row = coordinate c16), B = K (column = c16)
-        const u32x4_t kt = {pk2(ka[0], ka[1]), pk2(ka[2], ka[3]), pk2(ka[4], ka[5]), pk2(ka[6], ka[7])};
-        st.zm = mma32(kt, kt, st.zm);
+        if constexpr (WITH_Z) {
+            // Gram matrix: A = K^T (row = coordinate c16), B = K (column = c16)
+            const u32x4_t kt = {pk2(ka[0], ka[1]), pk2(ka[2], ka[3]), pk2(ka[4], ka[5]), pk2(ka[6], ka[7])};
+            st.zm = mma32(kt, kt, st.zm);
+        }
 #pragma unroll
-        for (int i = 0; i < nslots<W>(); ++i) {
-            u32x4_t fk;
-            switch (tile_of<W>(i)) {
-                case 0: fk = lift_keys<0>(ka, L); break;
-                case 1: fk = lift_keys<1>(ka, L); break;
-                case 2: fk = lift_keys<2>(ka, L); break;
-                case 3: fk = lift_keys<3>(ka, L); break;
-                case 4: fk = lift_keys<4>(ka, L); break;
-                case 5: fk = lift_keys<5>(ka, L); break;
-                case 6: fk = lift_keys<6>(ka, L); break;
-                case 7: fk = lift_keys<7>(ka, L); break;
-                default: fk = lift_keys<8>(ka, L); break;
-            }
+        for (int i = 0; i < 4; ++i) {
+            const u32x4_t fk = lift_keys_own<W>(i, ka, L);
 #pragma unroll
             for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] = mma32(fk, vop[m][nt], st.s[i][nt]);
+        }
+        if constexpr (h8 > l8) {
+            const u32x4_t fk = lift_keys<8>(ka, L);
+#pragma unroll
+            for (int j = 0; j < h8 - l8; ++j) st.x[j] = mma32(fk, vop[m][l8 + j], st.x[j]);
         }
     }
 }
@@ -186,27 +204,34 @@ __device__ __forceinline__ void load_query(const bf16_t* bq, int tt, const Lane&
 // A record holds one state in accumulator order: S at
 // ((tile * NTV + nt) * 64 + lane) * 4 + r, then Z at NMT*NTV*256 + lane*4 + r.
 
-template <int W, int DV, int C>
+template <int W, bool WITH_Z, int DV, int C>
 __device__ __forceinline__ void record_store(float* rec, const State<DV, C>& st, const Lane& L) {
     using F = Cfg<DV, C>;
+    constexpr int l8 = lo8<W, F::NTV>(), h8 = hi8<W, F::NTV>();
     f32x4_t* r4 = reinterpret_cast<f32x4_t*>(rec);
 #pragma unroll
-    for (int i = 0; i < nslots<W>(); ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int nt = 0; nt < F::NTV; ++nt)
-            r4[(tile_of<W>(i) * F::NTV + nt) * 64 + L.lane] = st.s[i][nt];
-    if (W == 0) r4[NMT * F::NTV * 64 + L.lane] = st.zm;
+            r4[((4 * W + i) * F::NTV + nt) * 64 + L.lane] = st.s[i][nt];
+#pragma unroll
+    for (int j = 0; j < h8 - l8; ++j) r4[(8 * F::NTV + l8 + j) * 64 + L.lane] = st.x[j];
+    if (WITH_Z) r4[NMT * F::NTV * 64 + L.lane] = st.zm;
 }
 
 template <int W, int DV, int C>
 __device__ __forceinline__ void record_load(const float* rec, State<DV, C>& st, const Lane& L) {
     using F = Cfg<DV, C>;
+    constexpr int l8 = lo8<W, F::NTV>(), h8 = hi8<W, F::NTV>();
     const f32x4_t* r4 = reinterpret_cast<const f32x4_t*>(rec);
 #pragma unroll
-    for (int i = 0; i < NSLOT; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int nt = 0; nt < F::NTV; ++nt)
-            st.s[i][nt] = i < nslots<W>() ? r4[(tile_of<W>(i) * F::NTV + nt) * 64 + L.lane] : zero4();
+            st.s[i][nt] = r4[((4 * W + i) * F::NTV + nt) * 64 + L.lane];
+#pragma unroll
+    for (int j = 0; j < F::H8; ++j)
+        st.x[j] = j < h8 - l8 ? r4[(8 * F::NTV + l8 + j) * 64 + L.lane] : zero4();
     st.zm = r4[NMT * F::NTV * 64 + L.lane];
 }
 
@@ -222,9 +247,11 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
     Pipeline<DK, DV, C, NW> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, false};
     State<DV, C> st;
 #pragma unroll
-    for (int i = 0; i < NSLOT; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] = zero4();
+#pragma unroll
+    for (int j = 0; j < F::H8; ++j) st.x[j] = zero4();
     st.zm = zero4();
 
     P.stage(nullptr, k, v, P.c0, L);
@@ -238,22 +265,51 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
         u32x4_t vop[F::KS][F::NTV];
 #pragma unroll
         for (int m = 0; m < F::KS; ++m) v_fragment_step<DV, C>(bv, vop[m], m, L);
-        state_update<W, DV, C>(st, KT, vop, L);
+        // the Gram matrix goes with wavefront 1 (wavefront 0 holds more of tile 8
+        // when the value tiles are odd)
+        state_update<W, W == 1, DV, C>(st, KT, vop, L);
         compiler_fence();
     }
-    record_store<W, DV, C>(rec + (bh * NSEG + seg) * (size_t)F::REC, st, L);
+    record_store<W, W == 1, DV, C>(rec + (bh * NSEG + seg) * (size_t)F::REC, st, L);
 }
 
+// Stores the output rows wavefront 0 staged in LDS (its exchange half, row
+// stride OROW, query tiles NW*u) for a chunk with n valid rows; wavefront 1 only.
+template <int DV, int C>
+__device__ __forceinline__ void store_staged_rows(const char* ostage, bf16_t* oc, int n,
+                                                  const Lane& L) {
+    using F = Cfg<DV, C>;
+    constexpr int UPR = DV * 2 / 16;              // 16-byte units per row
+    constexpr int NU = F::TW * 16 * UPR;
+#pragma unroll
+    for (int i = 0; i < (NU + 63) / 64; ++i) {
+        const int unit = L.lane + 64 * i;
+        if (unit < NU) {
+            const int rl = unit / UPR, col = unit % UPR;
+            const int row = 16 * NW * (rl / 16) + rl % 16;
+            const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ostage + rl * F::OROW + 16 * col);
+            if (row < n) *reinterpret_cast<u32x4_t*>(oc + (size_t)row * DV + 8 * col) = val;
+        }
+    }
+}
+
+// Memory roles: wavefront 0 issues every direct-to-LDS load and no global store,
+// so its wait for chunk data never waits for stores; wavefront 1 issues every
+// output store (its own rows from registers, wavefront 0's rows from LDS one
+// chunk later) and never waits for them.
 template <int W, int DV, int C, bool CAUSAL>
 __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                          const float* prefix, bf16_t* o, char* lds, int T,
                                          int NC, int G, int NSEG, const Lane& L) {
     using F = Cfg<DV, C>;
+    constexpr int l8 = lo8<W, F::NTV>(), h8 = hi8<W, F::NTV>();
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    Pipeline<DK, DV, C, NW> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true};
-    // exchange buffer: partials for query tile (u of wavefront w) at [w][u][nt][lane]
+    Pipeline<DK, DV, C, NW, 1> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true};
+    // exchange buffer: partials for query tile (u of wavefront w) at [w][u][nt][lane];
+    // half 0 then holds wavefront 0's staged output rows until the next chunk
     f32x4_t* xbuf = reinterpret_cast<f32x4_t*>(lds + F::NBUF * F::BUF);
+    char* ostage = reinterpret_cast<char*>(xbuf);
 
     State<DV, C> st;
     record_load<W, DV, C>(prefix + (CAUSAL ? bh * NSEG + seg : bh) * (size_t)F::REC, st, L);
@@ -266,12 +322,17 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         const bf16_t* bq = reinterpret_cast<const bf16_t*>(buf);
         const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::QB);
         const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::QB);
+        bf16_t* oc = o + (bh * T + (size_t)c * C) * DV;
+
+        // wavefront 0's rows of the previous chunk, before its half is reused
+        if (W == 1 && c > P.c0) store_staged_rows<DV, C>(ostage, oc - (size_t)C * DV, C, L);
+        compiler_fence();
 
         // ---- inter-chunk partials over this wavefront's feature tiles, for every
         // query tile; those of the other wavefront's tiles go to the exchange
         f32x4_t num[F::TW][F::NTV + 1];            // own query tiles (+ ones tile)
         {
-            // S^T in bf16 as A operands: slot s of pair p = own slot 2p + s/4, row 4g + s%4
+            // S^T in bf16 as A operands: slot s of pair p = own tile 2p + s/4, row 4g + s%4
             u32x4_t sop[2][F::NTV];
 #pragma unroll
             for (int p = 0; p < 2; ++p)
@@ -281,12 +342,10 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
                                          pk2(st.s[2 * p][nt][2], st.s[2 * p][nt][3]),
                                          pk2(st.s[2 * p + 1][nt][0], st.s[2 * p + 1][nt][1]),
                                          pk2(st.s[2 * p + 1][nt][2], st.s[2 * p + 1][nt][3])};
-            u32x2_t sop8[F::NTV];
-            if (W == 0) {
+            u32x2_t sop8[F::H8];
 #pragma unroll
-                for (int nt = 0; nt < F::NTV; ++nt)
-                    sop8[nt] = u32x2_t{pk2(st.s[4][nt][0], st.s[4][nt][1]), pk2(st.s[4][nt][2], st.s[4][nt][3])};
-            }
+            for (int j = 0; j < h8 - l8; ++j)
+                sop8[j] = u32x2_t{pk2(st.x[j][0], st.x[j][1]), pk2(st.x[j][2], st.x[j][3])};
 #pragma unroll
             for (int tt = 0; tt < F::TT; ++tt) {
                 float qr[16];
@@ -297,17 +356,18 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
                 for (int nt = 0; nt < F::NTV; ++nt) part[nt] = zero4();
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
-                    const u32x4_t fq = lift_queries(qr, tile_of<W>(2 * p), tile_of<W>(2 * p + 1));
+                    const u32x4_t fq = lift_queries(qr, 4 * W + 2 * p, 4 * W + 2 * p + 1);
 #pragma unroll
                     for (int nt = 0; nt < F::NTV; ++nt) part[nt] = mma32(sop[p][nt], fq, part[nt]);
                 }
-                if (W == 0) {                         // tile 8 (half K-step)
+                if constexpr (h8 > l8) {              // own value tiles of tile 8 (half K-step)
                     float f[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) f[r] = (2.0f * qr[r]) * qr[(r + 8) & 15];
                     const u32x2_t fq = {pk2(f[0], f[1]), pk2(f[2], f[3])};
 #pragma unroll
-                    for (int nt = 0; nt < F::NTV; ++nt) part[nt] = mma16_acc32(sop8[nt], fq, part[nt]);
+                    for (int j = 0; j < h8 - l8; ++j)
+                        part[l8 + j] = mma16_acc32(sop8[j], fq, part[l8 + j]);
                 }
                 const int u = tt / NW;
                 if (tt % NW == W) {
@@ -327,6 +387,7 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
 #pragma unroll
             for (int nt = 0; nt < F::NTV; ++nt)
                 num[u][nt] += xbuf[(W * F::TW + u) * F::NTV * 64 + nt * 64 + L.lane];
+        compiler_fence();                             // partials read before rows are staged
 
         // V^T fragments (intra term and state update)
         u32x4_t vop[F::KS][F::NTV];
@@ -337,8 +398,6 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         // Z as an A operand: lane c16 = row i, slots 4g + s = column j; Z is
         // symmetric, so the accumulator (lane = column) serves directly.
         const u32x2_t zop = {pk2(st.zm[0], st.zm[1]), pk2(st.zm[2], st.zm[3])};
-        bf16_t* oc = o + (bh * T + (size_t)c * C) * DV;
-        char* otile = reinterpret_cast<char*>(xbuf + W * F::TW * F::NTV * 64);
 #pragma unroll
         for (int u = 0; u < F::TW; ++u) {
             const int tt = NW * u + W;
@@ -372,7 +431,7 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
                     num[u][F::NTV] = mma32(ones, at, num[u][F::NTV]);
                 }
             }
-            // ---- normalise and store: o = num / den
+            // ---- normalise: o = num / den
             // inter-chunk denominator q^T Z q: (Z q)[4g + r] times q[4g + r],
             // summed over r here and over the four lane groups below
             const f32x4_t zq = mma16(zop, qf, zero4());
@@ -385,8 +444,6 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
             // intra-chunk denominator: row 0 of the ones tile (lane group 0)
             const float den = __shfl(num[u][F::NTV][0], L.c16, 64) + di;
             const float y = den != 0.0f ? 1.0f / den : 0.0f;   // y = 0 gives o = 0
-            // the 16 x DV bf16 tile goes through LDS (this wavefront's half of the
-            // exchange buffer, already consumed) so that HBM sees whole rows
 #pragma unroll
             for (int nt = 0; nt < F::NTV; ++nt) {
                 float ov[4];
@@ -398,17 +455,13 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
                     const float er = __builtin_fmaf(-q0, den, x);
                     ov[r] = __builtin_fmaf(er, y, q0);
                 }
-                *reinterpret_cast<u32x2_t*>(otile + L.c16 * F::OROW + 2 * (16 * nt + 4 * L.g)) =
-                    u32x2_t{pk2(ov[0], ov[1]), pk2(ov[2], ov[3])};
-            }
-#pragma unroll
-            for (int i = 0; i < (F::OU + 63) / 64; ++i) {
-                const int unit = L.lane + 64 * i;
-                const int row = unit / (F::OU / 16), col = unit % (F::OU / 16);
-                if (unit < F::OU) {
-                    const u32x4_t val = *reinterpret_cast<const u32x4_t*>(otile + row * F::OROW + 16 * col);
-                    if (16 * tt + row < n)
-                        *reinterpret_cast<u32x4_t*>(oc + (size_t)(16 * tt + row) * DV + 8 * col) = val;
+                const u32x2_t packed = {pk2(ov[0], ov[1]), pk2(ov[2], ov[3])};
+                if (W == 0) {
+                    // staged in this wavefront's exchange half (its partials are consumed)
+                    *reinterpret_cast<u32x2_t*>(ostage + (16 * u + L.c16) * F::OROW +
+                                                2 * (16 * nt + 4 * L.g)) = packed;
+                } else if (t < n) {
+                    *reinterpret_cast<u32x2_t*>(oc + (size_t)t * DV + 16 * nt + 4 * L.g) = packed;
                 }
             }
         }
@@ -417,9 +470,15 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         if (CAUSAL) {
             f32x4_t KT[F::TT];
             k_transposed<DV, C>(bk, KT, L);
-            state_update<W, DV, C>(st, KT, vop, L);
+            state_update<W, true, DV, C>(st, KT, vop, L);
         }
         compiler_fence();
+    }
+    // wavefront 0's rows of the last chunk
+    lds_barrier();
+    if (W == 1) {
+        const int cl = P.c1 - 1;
+        store_staged_rows<DV, C>(ostage, o + (bh * T + (size_t)cl * C) * DV, min(C, T - cl * C), L);
     }
 }
 

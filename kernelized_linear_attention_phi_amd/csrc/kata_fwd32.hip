@@ -371,49 +371,65 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
             lds_barrier();
         }
 
+        // ---- inter-chunk term phi(Q).P and q^T Z q for every own query tile at
+        // once: each state operand is read from LDS once and feeds TW products
         f32x4_t num[F::TW][F::NTV + 1];
         float di[F::TW];
+        QueryRow Q[F::TW];
 #pragma unroll
         for (int u = 0; u < F::TW; ++u) {
-            // ---- inter-chunk term phi(Q).P and q^T Z q for own query tile u
-            const int tt = own_query_tile<W, F::TT>(u);
-            QueryRow Q;
-            load_query32(bq, tt, L, Q);
+            load_query32(bq, own_query_tile<W, F::TT>(u), L, Q[u]);
 #pragma unroll
             for (int nt = 0; nt <= F::NTV; ++nt) num[u][nt] = zero4();
-            for_pairs<0, 16>([&](auto pc) {
-                constexpr int p = decltype(pc)::value;
-                const u32x4_t fq = lift_query_pair<2 * p>(Q, L);
+        }
+        for_pairs<0, 16>([&](auto pc) {
+            constexpr int p = decltype(pc)::value;
+            u32x4_t fq[F::TW];
 #pragma unroll
-                for (int nt = 0; nt < F::NTV; ++nt) {
-                    const u32x4_t a =
-                        *reinterpret_cast<const u32x4_t*>(sb + ((p * F::NTV + nt) * 64 + L.lane) * 16);
-                    num[u][nt] = mma32(a, fq, num[u][nt]);
-                }
-            });
-            {
-                const u32x2_t fq = lift_query_mixed(Q, L);
+            for (int u = 0; u < F::TW; ++u) fq[u] = lift_query_pair<2 * p>(Q[u], L);
 #pragma unroll
-                for (int nt = 0; nt < F::NTV; ++nt) {
-                    const u32x2_t a =
-                        *reinterpret_cast<const u32x2_t*>(sb + F::SPAIR + (nt * 64 + L.lane) * 8);
-                    num[u][nt] = mma16_acc32(a, fq, num[u][nt]);
-                }
+            for (int nt = 0; nt < F::NTV; ++nt) {
+                const u32x4_t a =
+                    *reinterpret_cast<const u32x4_t*>(sb + ((p * F::NTV + nt) * 64 + L.lane) * 16);
+#pragma unroll
+                for (int u = 0; u < F::TW; ++u) num[u][nt] = mma32(a, fq[u], num[u][nt]);
             }
+        });
+        {
+            u32x2_t fq[F::TW];
+#pragma unroll
+            for (int u = 0; u < F::TW; ++u) fq[u] = lift_query_mixed(Q[u], L);
+#pragma unroll
+            for (int nt = 0; nt < F::NTV; ++nt) {
+                const u32x2_t a =
+                    *reinterpret_cast<const u32x2_t*>(sb + F::SPAIR + (nt * 64 + L.lane) * 8);
+#pragma unroll
+                for (int u = 0; u < F::TW; ++u) num[u][nt] = mma16_acc32(a, fq[u], num[u][nt]);
+            }
+        }
+        {
             const char* zb = sb + F::SPAIR + F::S32;
-            const f32x4_t zl = mma32(*reinterpret_cast<const u32x4_t*>(zb + L.lane * 16), Q.zf, zero4());
-            const f32x4_t zu =
-                mma32(*reinterpret_cast<const u32x4_t*>(zb + (64 + L.lane) * 16), Q.zf, zero4());
-            float d = 0.0f;
+            const u32x4_t zal = *reinterpret_cast<const u32x4_t*>(zb + L.lane * 16);
+            const u32x4_t zau = *reinterpret_cast<const u32x4_t*>(zb + (64 + L.lane) * 16);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                d = __builtin_fmaf(Q.a[r], zl[r], d);
-                d = __builtin_fmaf(Q.b[r], zu[r], d);
+            for (int u = 0; u < F::TW; ++u) {
+                const f32x4_t zl = mma32(zal, Q[u].zf, zero4());
+                const f32x4_t zu = mma32(zau, Q[u].zf, zero4());
+                float d = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    d = __builtin_fmaf(Q[u].a[r], zl[r], d);
+                    d = __builtin_fmaf(Q[u].b[r], zu[r], d);
+                }
+                d += __shfl_xor(d, 16, 64);
+                d += __shfl_xor(d, 32, 64);
+                di[u] = d;
             }
-            d += __shfl_xor(d, 16, 64);
-            d += __shfl_xor(d, 32, 64);
-            di[u] = d;
+        }
 
+#pragma unroll
+        for (int u = 0; u < F::TW; ++u) {
+            const int tt = own_query_tile<W, F::TT>(u);
             // ---- intra-chunk term: A = (Q K^T)^2 masked to j <= t, num += A [V | 1]
             if (CAUSAL) {
                 const int t = 16 * tt + L.c16;
@@ -466,6 +482,7 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
                 *reinterpret_cast<u32x2_t*>(otile + L.c16 * F::OROW + 2 * (16 * nt + 4 * L.g)) =
                     u32x2_t{pk2(ov[0], ov[1]), pk2(ov[2], ov[3])};
             }
+            compiler_fence();                         // staged rows written before read back
 #pragma unroll
             for (int i = 0; i < (F::OU + 63) / 64; ++i) {
                 const int unit = L.lane + 64 * i;

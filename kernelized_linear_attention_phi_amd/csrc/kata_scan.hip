@@ -1,18 +1,17 @@
 // Associative scan over chunk (or segment) states, elementwise fp32 addition.
 //
 // KATA explainers (gist.science, technical summary 2.3): the inter-chunk state
-// is propagated by an associative scan (parallel prefix sum), cutting the
-// recurrence depth over N_C chunks from O(N_C) to O(log N_C).
+// is propagated by an associative scan (parallel prefix sum) over chunk states
+// instead of a sequential recurrence.
 //
 // Layout-agnostic: a "record" is E contiguous floats (one chunk's or segment's
-// state). A block owns 32 consecutive elements of one sequence and walks its
-// records in super-tiles of 128, each loaded at once through LDS (coalesced
-// 128-byte rows, every load in flight together). Every wavefront scans one
-// element across 64 records with a log2(64) = 6-step Hillis-Steele prefix on
-// its 64 lanes (DPP lane shifts); 64-record tiles are chained by a running
-// carry, so the depth is 6 * ceil(NR / 64) adds. The exclusive prefix is the
-// inclusive one shifted by a lane (no subtraction, so a record never depends on
-// its own value).
+// state; E is a multiple of 4). The scan is exclusive: record r becomes
+// init + sum_{r' < r} rec_{r'}, and the inclusive total goes to the totals.
+// Sequences of at most 32 records take a per-element walk; longer ones a
+// blocked two-level scan: groups of 16 consecutive records are summed in
+// parallel, the group sums are prefixed, and each group is walked from its
+// offset. Either way each record is read once and written once, with many
+// 16-byte loads in flight per thread, since the scan is bound by HBM.
 #include "kata_device.h"
 #include "kata_internal.h"
 
@@ -20,91 +19,105 @@ namespace kata {
 
 namespace {
 
-constexpr int kTile = 64;      // records per wavefront scan = lanes per wavefront
-constexpr int kCols = 32;      // elements per block
-constexpr int kRows = 128;     // records per super-tile
-constexpr int kWaves = 4;
-constexpr int kColsPerWave = kCols / kWaves;
-
-// Inclusive prefix sum over the 64 lanes of a wavefront in 6 DPP steps: shifts by
-// 1, 2, 4, 8 inside each 16-lane row, then the last lane of a row is broadcast
-// into the following row(s). Lanes without a source add 0.
-__device__ __forceinline__ float wave_inclusive_scan(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));  // row_shr:1
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));  // row_shr:2
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));  // row_shr:4
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));  // row_shr:8
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false));  // row_bcast:15
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, false));  // row_bcast:31
-    return x;
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-// Lane i receives lane i-1 (lane 0 receives 0): wave_shr:1.
-__device__ __forceinline__ float wave_shift_right(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x138, 0xf, 0xf, false));
-}
+// Few records per sequence (NR <= kSeqMax): one thread per 4 consecutive
+// elements walks the records in order. Loads are issued 8 records ahead of the
+// dependent adds, so every thread keeps 8 coalesced 16-byte reads in flight.
+constexpr int kSeqMax = 32;
+constexpr int kSeqUnroll = 8;
 
-__global__ __launch_bounds__(256) void scan_records_kernel(
+__global__ __launch_bounds__(256) void scan_records_seq_kernel(
     float* __restrict__ rec, int NR, int E, const float* __restrict__ init,
     float* __restrict__ total_a, float* __restrict__ total_b) {
-    // a super-tile of kRows records x kCols elements is loaded with every load in
-    // flight at once, scanned in LDS, and stored back
-    __shared__ float tile[kRows][kCols + 1];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
     const size_t seq = blockIdx.y;
-    const int e0 = blockIdx.x * kCols;
-    // load/store mapping: thread -> (row phase rr = tid / kCols, column tid % kCols)
-    const int lc = threadIdx.x % kCols, lr = threadIdx.x / kCols;
-    constexpr int kRowStep = 256 / kCols;
-    const int e = e0 + lc;
-    float* base = rec + seq * (size_t)NR * E;
-
-    // running carry of the elements this wave scans (uniform across lanes)
-    float carry[kColsPerWave];
+    const int E4 = E / 4;
+    const int e4 = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e4 >= E4) return;
+    float4* base = reinterpret_cast<float4*>(rec + seq * (size_t)NR * E) + e4;
+    float4 carry = init ? reinterpret_cast<const float4*>(init + seq * E)[e4]
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r0 = 0; r0 < NR; r0 += kSeqUnroll) {
+        float4 x[kSeqUnroll];
 #pragma unroll
-    for (int u = 0; u < kColsPerWave; ++u) {
-        const int ee = e0 + wave * kColsPerWave + u;
-        carry[u] = (init != nullptr && ee < E) ? init[seq * E + ee] : 0.0f;
-    }
-
-    for (int r0 = 0; r0 < NR; r0 += kRows) {
+        for (int i = 0; i < kSeqUnroll; ++i)
+            if (r0 + i < NR) x[i] = base[(size_t)(r0 + i) * E4];
 #pragma unroll
-        for (int i = 0; i < kRows / kRowStep; ++i) {
-            const int r = lr + kRowStep * i;
-            const int rr = r0 + r;
-            tile[r][lc] = (rr < NR && e < E) ? base[(size_t)rr * E + e] : 0.0f;
-        }
-        __syncthreads();
-        // scan: lane = record, one element column at a time, 64 records per pass
-#pragma unroll
-        for (int h = 0; h < kRows / kTile; ++h) {
-            if (r0 + h * kTile >= NR) break;
-#pragma unroll
-            for (int u = 0; u < kColsPerWave; ++u) {
-                const int col = wave * kColsPerWave + u;
-                const float inc = wave_inclusive_scan(tile[h * kTile + lane][col]);
-                tile[h * kTile + lane][col] = carry[u] + wave_shift_right(inc);
-                carry[u] += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), 63));
+        for (int i = 0; i < kSeqUnroll; ++i)
+            if (r0 + i < NR) {
+                base[(size_t)(r0 + i) * E4] = carry;
+                carry = add4(carry, x[i]);
             }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < kRows / kRowStep; ++i) {
-            const int r = lr + kRowStep * i;
-            const int rr = r0 + r;
-            if (rr < NR && e < E) base[(size_t)rr * E + e] = tile[r][lc];
-        }
-        __syncthreads();
     }
-    // inclusive totals
+    if (total_a) reinterpret_cast<float4*>(total_a + seq * E)[e4] = carry;
+    if (total_b) reinterpret_cast<float4*>(total_b + seq * E)[e4] = carry;
+}
+
+// Blocked two-level scan. A block owns kCols4 float4 columns of one sequence
+// and walks its records in tiles of kGroups * kPer: thread (group g, column c)
+// holds records g*kPer .. g*kPer + kPer - 1 of the tile in registers, sums them,
+// publishes the sum in LDS, takes the sum of the groups before it (plus the
+// running carry of earlier tiles) as its offset, and writes its records'
+// exclusive prefixes.
+constexpr int kCols4 = 32;
+constexpr int kGroups = 8;
+constexpr int kPer = 16;
+constexpr int kTileRecs = kGroups * kPer;
+
+__global__ __launch_bounds__(kCols4 * kGroups) void scan_records_blocked_kernel(
+    float* __restrict__ rec, int NR, int E, const float* __restrict__ init,
+    float* __restrict__ total_a, float* __restrict__ total_b) {
+    __shared__ float4 gsum[kGroups][kCols4];
+    const size_t seq = blockIdx.y;
+    const int E4 = E / 4;
+    const int c = threadIdx.x % kCols4, g = threadIdx.x / kCols4;
+    const int e4 = blockIdx.x * kCols4 + c;
+    const bool col_ok = e4 < E4;
+    // loads always read a valid address (clamped column and record) and the
+    // value is zeroed afterwards, so no pointer select reaches the load
+    float4* base = reinterpret_cast<float4*>(rec + seq * (size_t)NR * E) + e4;
+    const float4* load_base =
+        reinterpret_cast<const float4*>(rec + seq * (size_t)NR * E) + min(e4, E4 - 1);
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 carry = zero;
+    if (init) {
+        const float4 i4 = reinterpret_cast<const float4*>(init + seq * E)[min(e4, E4 - 1)];
+        if (col_ok) carry = i4;
+    }
+    for (int r0 = 0; r0 < NR; r0 += kTileRecs) {
+        const int rg = r0 + g * kPer;
+        float4 x[kPer];
 #pragma unroll
-    for (int u = 0; u < kColsPerWave; ++u) {
-        const int ee = e0 + wave * kColsPerWave + u;
-        if (lane == 0 && ee < E) {
-            if (total_a) total_a[seq * E + ee] = carry[u];
-            if (total_b) total_b[seq * E + ee] = carry[u];
+        for (int i = 0; i < kPer; ++i) {
+            const float4 t = load_base[(size_t)min(rg + i, NR - 1) * E4];
+            const bool ok = col_ok && rg + i < NR;
+            x[i] = make_float4(ok ? t.x : 0.f, ok ? t.y : 0.f, ok ? t.z : 0.f, ok ? t.w : 0.f);
         }
+        float4 s = zero;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) s = add4(s, x[i]);
+        gsum[g][c] = s;
+        __syncthreads();
+        float4 off = carry, tot = carry;
+#pragma unroll
+        for (int j = 0; j < kGroups; ++j) {
+            const float4 gj = gsum[j][c];
+            if (j < g) off = add4(off, gj);
+            tot = add4(tot, gj);
+        }
+        __syncthreads();                           // gsum is rewritten by the next tile
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            if (col_ok && rg + i < NR) base[(size_t)(rg + i) * E4] = off;
+            off = add4(off, x[i]);
+        }
+        carry = tot;
+    }
+    if (g == 0 && col_ok) {
+        if (total_a) reinterpret_cast<float4*>(total_a + seq * E)[e4] = carry;
+        if (total_b) reinterpret_cast<float4*>(total_b + seq * E)[e4] = carry;
     }
 }
 
@@ -120,8 +133,15 @@ __global__ void copy_or_zero_kernel(float* __restrict__ dst, const float* __rest
 hipError_t launch_scan_records(float* rec, int nseq, int NR, int E, const float* init,
                                float* total_a, float* total_b, hipStream_t st) {
     if (nseq == 0 || E == 0) return hipSuccess;
-    dim3 grid((E + kCols - 1) / kCols, nseq);
-    scan_records_kernel<<<grid, 256, 0, st>>>(rec, NR, E, init, total_a, total_b);
+    if (E % 4 != 0) return hipErrorInvalidValue;      // every record length is a multiple of 4
+    if (NR <= kSeqMax) {
+        dim3 grid((E / 4 + 255) / 256, nseq);
+        scan_records_seq_kernel<<<grid, 256, 0, st>>>(rec, NR, E, init, total_a, total_b);
+    } else {
+        dim3 grid((E / 4 + kCols4 - 1) / kCols4, nseq);
+        scan_records_blocked_kernel<<<grid, kCols4 * kGroups, 0, st>>>(rec, NR, E, init, total_a,
+                                                                       total_b);
+    }
     return hipGetLastError();
 }
 
