@@ -32,7 +32,7 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters_fwd131k.json")
 
 # sources of the dominant (output) kernel: HBM counters taken on another build
 # of it are not reported
-DOMINANT_KERNEL_SOURCES = ("kata_fwd16.hip", "kata_mfma.h", "kata_device.h")
+DOMINANT_KERNEL_SOURCES = ("kata_fwd16.hip", "kata_chunk.h", "kata_mfma.h", "kata_device.h")
 
 
 def kernel_source_hash():
