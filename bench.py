@@ -80,6 +80,41 @@ def time_forward(kata, torch, w, q, k, v, steps, warmup):
     return total, wall, phases
 
 
+def time_calls(torch, fn, steps, warmup):
+    """Mean ms of fn() over `steps` calls, timed with events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def quadratic_vs_chunked(kata, torch, gen, name, steps, warmup):
+    """The same workload through the chunked form and the quadratic form."""
+    w = gen.WORKLOADS[name]
+    q, k, v = gen.gaussian_qkv(w.B, w.H, w.T, w.dk, w.dv, w.seed, w.dtype)
+    to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+    q, k, v = to(q), to(k), to(v)
+    o = torch.empty_like(v)
+    nbytes = kata.chunked_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1, True)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    ms_c = time_calls(torch, lambda: kata.chunked_fwd_into(q, k, v, o, w.chunk, True, ws),
+                      steps, warmup)
+    ms_f = time_calls(torch, lambda: kata.flash_fwd(q, k, v, out=o), steps, warmup)
+    tok = w.B * w.T
+    # quadratic form: 2 (d_k + d_v) flops per (query, key) pair, (T^2 + T) / 2 pairs
+    qflops = w.B * w.H * (w.T * (w.T + 1) / 2) * 2 * (w.dk + w.dv)
+    return {"chunked_ms": ms_c, "flash_ms": ms_f, "chunked_tokens_per_s": tok / (ms_c * 1e-3),
+            "flash_tokens_per_s": tok / (ms_f * 1e-3),
+            "flash_alg_tflops": qflops / (ms_f * 1e-3) / 1e12,
+            "flash_mfma_util_alg": qflops / (ms_f * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def decode_bench(kata, torch, steps=1024, n_seq=512, heads=4, dk=16, dv=64, reps=3):
     """1024 decode steps on n_seq x heads rows with fp32 state, replayed from a
     HIP graph; returns ms per step and algorithmic GB/s."""
@@ -221,6 +256,8 @@ def main():
             "mfma_util_alg": fl3 / (ms3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "mfma_util_alg_output_phase": fl3 / (ph3["output"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         del dev3
+        result["parts"]["fwd4k"] = quadratic_vs_chunked(kata, torch, gen, "fwd4k", args.steps,
+                                                        args.warmup)
         dms, dgbs, dbytes = decode_bench(kata, torch)
         result["parts"]["decode"] = {"ms_per_step": dms, "alg_GBps": dgbs,
                                      "hbm_frac": dgbs / PEAK_HBM_GBS, "bytes_per_step": dbytes,

@@ -135,6 +135,19 @@ kata_status_t kata_scan_states(const void* k, const void* v,
                                float* S_out, float* z_out,
                                void* workspace, size_t ws_bytes, void* stream);
 
+/* Quadratic ("flash-style") forward: the same o as kata_chunked_fwd, evaluated
+ * directly as sum_{j <= t} (q_t.k_j)^2 v_j / sum_{j <= t} (q_t.k_j)^2 by
+ * streaming key blocks past tiles of queries (the quadratic KATA forward
+ * of the explainers, section 4, and the abstract), with no chunk states. It
+ * takes no initial state and keeps no final state.
+ *   q, k [B,H,T,d_k]; v, o [B,H,T,d_v] - bf16 only (fp32 inputs return
+ *     KATA_EUNSUPPORTED); d_k in {16, 32}, d_v in {16, 32, 64}.
+ *   causal - as kata_chunked_fwd (inclusive mask when nonzero).
+ * Work grows as T^2 / 2 per (b, h); no workspace. */
+kata_status_t kata_flash_fwd(const void* q, const void* k, const void* v, void* o,
+                             int B, int H, int T, int d_k, int d_v, int causal,
+                             kata_dtype_t dtype, void* stream);
+
 /* One recurrent decode step for N independent (sequence, head) rows: the
  * constant-time recurrent inference of the abstract, with a fixed-size state.
  *   q, k [N,d_k]; v [N,d_v] (dtype) - the new token.

@@ -12,7 +12,7 @@ import os
 import torch
 
 __all__ = ["KataError", "lib", "chunked_fwd", "chunked_fwd_into", "chunked_fwd_workspace",
-           "scan_states", "decode_step", "phi_dim", "LIB_PATH"]
+           "scan_states", "flash_fwd", "decode_step", "phi_dim", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkata.so")
 
@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.kata_scan_states_workspace.restype = sz
         L.kata_scan_states.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.kata_scan_states.restype = i
+        L.kata_flash_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+        L.kata_flash_fwd.restype = i
         L.kata_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
         L.kata_decode_step.restype = i
         _lib = L
@@ -183,6 +185,21 @@ def scan_states(k, v, chunk=64, initial_state=None):
                                 _ptr(ws), nbytes, _stream())
     _raise(st, "kata_scan_states")
     return Sp, zp, ST, zT
+
+
+def flash_fwd(q, k, v, causal=True, out=None):
+    """Quadratic-form forward (bf16 q, k [B,H,T,d_k], v [B,H,T,d_v]): the same
+    output as chunked_fwd without chunk states."""
+    _check_dev(q, k, v)
+    if q.dim() != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("expected q, k [B,H,T,d_k] and v [B,H,T,d_v]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    o = torch.empty_like(v) if out is None else out
+    st = lib().kata_flash_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, T, dk, dv,
+                              int(bool(causal)), _dtype_code(q), _stream())
+    _raise(st, "kata_flash_fwd")
+    return o
 
 
 def decode_step(q, k, v, S, z, out=None):

@@ -269,6 +269,21 @@ kata_status_t kata_scan_states(const void* k, const void* v, int B, int H, int T
     return hip_status(e);
 }
 
+kata_status_t kata_flash_fwd(const void* q, const void* k, const void* v, void* o, int B, int H,
+                             int T, int d_k, int d_v, int causal, kata_dtype_t dtype,
+                             void* stream) {
+    Shape s;
+    // the chunk size does not enter the quadratic form; any supported value
+    kata_status_t st = make_shape(B, H, T, d_k, d_v, 64, dtype, &s);
+    if (st != KATA_OK) return st;
+    if (!kata::flash_supported(s)) return KATA_EUNSUPPORTED;
+    if ((size_t)B * H == 0 || T == 0) return KATA_OK;
+    if (!q || !k || !v || !o) return KATA_EINVAL;
+    for (const void* p : {q, k, v, (const void*)o})
+        if (!aligned16(p)) return KATA_EINVAL;
+    return hip_status(kata::launch_flash_fwd(s, q, k, v, o, causal, static_cast<hipStream_t>(stream)));
+}
+
 kata_status_t kata_decode_step(const void* q, const void* k, const void* v, float* S, float* z,
                                void* o, int N, int d_k, int d_v, kata_dtype_t dtype,
                                void* stream) {

@@ -181,4 +181,73 @@ struct Pipeline {
     }
 };
 
+// vmcnt(n) for a run-time n in 0..15 (larger n waits for everything).
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+    switch (n) {
+        case 1: wait_vmcnt<1>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 7: wait_vmcnt<7>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 9: wait_vmcnt<9>(); break;
+        case 10: wait_vmcnt<10>(); break;
+        case 11: wait_vmcnt<11>(); break;
+        case 12: wait_vmcnt<12>(); break;
+        case 13: wait_vmcnt<13>(); break;
+        case 14: wait_vmcnt<14>(); break;
+        case 15: wait_vmcnt<15>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
+}
+
+// NBUF-deep staging for kernels whose wavefronts issue loads only (k | v of
+// chunks, no global stores until the end): chunk c lives in buffer
+// (c - c0) % NBUF and is staged NBUF - 1 iterations ahead. Loads of one
+// wavefront complete in order, so at chunk c each wavefront waits only until
+// no more than its copies of the already-staged later chunks are outstanding,
+// then all meet at a barrier and chunk c + NBUF - 1 is issued into the buffer
+// chunk c - 1 used.
+template <int DK, int DV, int C, int NW, int NBUF>
+struct LoadPipeline {
+    using IO = ChunkIO<DK, DV, C, NW, NW>;
+    static constexpr int PQ = IO::QB / 1024, PV = IO::VB / 1024;
+    char* lds;
+    int c0, c1, T;
+    size_t tok_base;
+
+    __device__ char* buffer(int c) const { return lds + ((c - c0) % NBUF) * IO::BUF; }
+    __device__ uint32_t buffer_lds(int c) const {
+        return lds_address(lds) + ((c - c0) % NBUF) * IO::BUF;
+    }
+    __device__ bool full(int c) const { return c < c1 && T - c * C >= C; }
+    // direct-to-LDS copies wavefront w issues for one full chunk (k and v pieces)
+    __device__ static int pieces(int w) {
+        int n = 0;
+        for (int i = PQ; i < 2 * PQ + PV; ++i) n += (i % NW == w);
+        return n;
+    }
+    __device__ void stage(const bf16_t* k, const bf16_t* v, int c, const Lane& L) {
+        if (c >= c1) return;
+        const int n = min(C, T - c * C);
+        const size_t tok0 = tok_base + (size_t)c * C;
+        if (n == C) IO::stage_async(nullptr, k, v, tok0, buffer_lds(c), false, L);
+        else IO::stage_ragged(nullptr, k, v, tok0, n, buffer(c), false, L);
+    }
+    __device__ void prologue(const bf16_t* k, const bf16_t* v, const Lane& L) {
+#pragma unroll
+        for (int i = 0; i < NBUF - 1; ++i) stage(k, v, c0 + i, L);
+    }
+    __device__ void acquire(const bf16_t* k, const bf16_t* v, int c, const Lane& L) {
+        int later = 0;                             // full chunks staged after c
+#pragma unroll
+        for (int j = 1; j < NBUF - 1; ++j) later += full(c + j) ? 1 : 0;
+        wait_vmcnt_upto(later * pieces(L.w));
+        lds_barrier();
+        stage(k, v, c + NBUF - 1, L);
+    }
+};
+
 }  // namespace kata

@@ -244,7 +244,7 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
     using F = Cfg<DV, C>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    Pipeline<DK, DV, C, NW> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, false};
+    LoadPipeline<DK, DV, C, NW, 3> P{lds, seg * G, min(NC, seg * G + G), T, bh * T};
     State<DV, C> st;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -254,9 +254,9 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
     for (int j = 0; j < F::H8; ++j) st.x[j] = zero4();
     st.zm = zero4();
 
-    P.stage(nullptr, k, v, P.c0, L);
+    P.prologue(k, v, L);
     for (int c = P.c0; c < P.c1; ++c) {
-        P.acquire(nullptr, k, v, c, L);
+        P.acquire(k, v, c, L);
         const char* buf = P.buffer(c);
         const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::QB);
         const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::QB);
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kata_seg_state16(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                       float* __restrict__ rec, int T, int NC, int G, int NSEG) {
     using F = Cfg<DV, C>;
-    __shared__ __attribute__((aligned(16))) char lds[F::NBUF * F::BUF];
+    __shared__ __attribute__((aligned(16))) char lds[3 * F::BUF];
     const Lane L;
     if (L.w == 0) seg_state_body<0, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L);
     else seg_state_body<1, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L);

@@ -64,7 +64,7 @@ struct Cfg32 {
     static constexpr int OTILE = 16 * OROW;
     static constexpr int OU = 2 * DV;               // 16-byte units per 16-row output tile
     static constexpr int LDS_FWD = 2 * IO::BUF + SB + NW * OTILE;
-    static constexpr int LDS_SEG = 2 * IO::BUF;
+    static constexpr int LDS_SEG = 4 * IO::BUF;     // 4-deep staging of k | v
     static constexpr int REC = NFT * NTV * 256 + NZ * 256;   // floats per state record
     static_assert(TW >= 1, "at least one query tile per wavefront");
 };
@@ -319,7 +319,7 @@ __device__ __forceinline__ void seg_state_body32(const bf16_t* k, const bf16_t* 
     using F = Cfg32<DV, C>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    Pipeline<DK, DV, C, NW> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, false};
+    LoadPipeline<DK, DV, C, NW, 4> P{lds, seg * G, min(NC, seg * G + G), T, bh * T};
     State32<DV, C> st;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -328,9 +328,9 @@ __device__ __forceinline__ void seg_state_body32(const bf16_t* k, const bf16_t* 
     st.x = zero4();
     st.z = zero4();
 
-    P.stage(nullptr, k, v, P.c0, L);
+    P.prologue(k, v, L);
     for (int c = P.c0; c < P.c1; ++c) {
-        P.acquire(nullptr, k, v, c, L);
+        P.acquire(k, v, c, L);
         const char* buf = P.buffer(c);
         const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::IO::QB);
         const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::IO::QB);

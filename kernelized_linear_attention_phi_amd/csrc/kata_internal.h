@@ -71,6 +71,11 @@ hipError_t launch_record_from_packed32(float* rec, const float* S, const float* 
 hipError_t launch_record_to_packed32(const float* rec, float* S, float* z, int dv, int nrec,
                                      hipStream_t st);
 
+// ---- quadratic (flash-style) forward, bf16 ----
+bool flash_supported(const Shape& s);
+hipError_t launch_flash_fwd(const Shape& s, const void* q, const void* k, const void* v, void* o,
+                            int causal, hipStream_t st);
+
 // ---- decode ----
 hipError_t launch_decode(const void* q, const void* k, const void* v, float* S, float* z,
                          void* o, int N, int dk, int dv, bool bf16, hipStream_t st);

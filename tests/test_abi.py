@@ -104,6 +104,18 @@ def test_scan_and_decode_reject(L):
     assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 16, 64, BF16, None) == EINVAL
 
 
+def test_flash_rejects_before_launch(L):
+    fl = L.kata_flash_fwd
+    assert fl(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 16, 64, 1, F32, None) == EUNSUPPORTED
+    assert fl(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 24, 64, 1, BF16, None) == EUNSUPPORTED
+    assert fl(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 16, 48, 1, BF16, None) == EUNSUPPORTED
+    assert fl(MISALIGNED, FAKE, FAKE, FAKE, 1, 1, 64, 16, 64, 1, BF16, None) == EINVAL
+    assert fl(None, FAKE, FAKE, FAKE, 1, 1, 64, 16, 64, 1, BF16, None) == EINVAL
+    assert fl(FAKE, FAKE, FAKE, FAKE, 1, 1, -3, 16, 64, 1, BF16, None) == EINVAL
+    assert fl(None, None, None, None, 1, 1, 0, 16, 64, 1, BF16, None) == OK     # empty: no launch
+    assert fl(None, None, None, None, 0, 4, 64, 32, 64, 0, BF16, None) == OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import kernelized_linear_attention_phi_amd._binding as b
     monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
