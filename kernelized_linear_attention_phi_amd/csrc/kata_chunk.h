@@ -52,6 +52,35 @@ __device__ __forceinline__ float partner(float x) {
     else return row_fetch<D>(x);
 }
 
+// Staged rows (q, k, v of a chunk in LDS) are stored XOR-swizzled in 16-byte
+// units: unit c of row r sits at unit c ^ swz(r) of that row, with
+// swz(r) = (r / (16 / U)) & (U - 1) for U units per row. The 16 consecutive rows
+// a group of lanes reads at one column then fall on 16 distinct 16-byte slots
+// of the 64 four-byte banks instead of 2 to 8 of them. The swizzle is its own
+// inverse within a row, so the same map gives the slot of a unit and the unit of
+// a slot.
+template <int ROWB>
+struct Swz {
+    static_assert(ROWB == 32 || ROWB == 64 || ROWB == 128, "row of 2, 4 or 8 units");
+    static constexpr int U = ROWB / 16;          // 16-byte units per row
+    static constexpr int RPB = 16 / U;           // rows per 256-byte span of the banks
+    __host__ __device__ static constexpr int swz(int r) { return (r / RPB) & (U - 1); }
+    // LDS byte offset of byte b of row r
+    __host__ __device__ static constexpr int off(int r, int b) {
+        return r * ROWB + (((b >> 4) ^ swz(r)) << 4) + (b & 15);
+    }
+    // unit index <-> slot index (an involution)
+    __host__ __device__ static constexpr int slot(int u) {
+        return (u / U) * U + ((u % U) ^ swz(u / U));
+    }
+};
+
+// Element read of a staged row: byte b of row r of the buffer at base.
+template <int ROWB, typename T>
+__device__ __forceinline__ T lds_row(const bf16_t* base, int r, int b) {
+    return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + Swz<ROWB>::off(r, b));
+}
+
 // ds_read_b64_tr_b16: every lane supplies the LDS address of 4 consecutive
 // 16-bit elements; within each group of 16 lanes, lane l receives element l % 4
 // of the block of lane 4i + l / 4 as its element i (i = 0..3).
@@ -62,7 +91,7 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
 }
 
 // V^T fragment of the 32-token K-step m and value tile nt, read transposed from
-// the row-major [C][DV] chunk in LDS: lane (c16, g), slot s holds
+// the staged [C][DV] chunk in LDS: lane (c16, g), slot s holds
 // v[32m + 16(s/4) + 4g + s%4][16nt + c16]. Lane j of group g points at row
 // 32m + 16h + 4g + j/4, columns 16nt + 4(j%4) .. +3.
 template <int DV>
@@ -70,8 +99,9 @@ __device__ __forceinline__ u32x4_t v_fragment_tr(const bf16_t* bv, int m, int nt
     u32x2_t h2[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-        h2[h] = lds_read_tr16(bv + (32 * m + 16 * h + 4 * L.g + (L.c16 >> 2)) * DV + 16 * nt +
-                              4 * (L.c16 & 3));
+        h2[h] = lds_read_tr16(reinterpret_cast<const char*>(bv) +
+                              Swz<2 * DV>::off(32 * m + 16 * h + 4 * L.g + (L.c16 >> 2),
+                                               32 * nt + 8 * (L.c16 & 3)));
     return u32x4_t{h2[0][0], h2[0][1], h2[1][0], h2[1][1]};
 }
 
@@ -103,8 +133,9 @@ struct ChunkIO {
     static_assert(QB % 1024 == 0 && VB % 1024 == 0, "chunks are whole 1 KB pieces");
 
     // Full chunk: the 1 KB pieces are split round-robin over the loading
-    // wavefronts; piece i goes to wavefront i % NLOAD as a direct-to-LDS load
-    // (lane l moves bytes [16l, 16l+16) of the piece).
+    // wavefronts; piece i goes to wavefront i % NLOAD as a direct-to-LDS load.
+    // Lane l fills 16-byte slot l of the piece with the unit the swizzle puts
+    // there.
     static __device__ __forceinline__ void stage_async(const bf16_t* q, const bf16_t* k,
                                                        const bf16_t* v, size_t tok0,
                                                        uint32_t buf_lds, bool with_q,
@@ -117,10 +148,10 @@ struct ChunkIO {
 #pragma unroll
         for (int i = 0; i < 2 * PQ + PV; ++i) {
             if (i < first || i % NLOAD != L.w) continue;
-            const char* src = i < PQ ? gq + i * 1024
-                            : i < 2 * PQ ? gk + (i - PQ) * 1024
-                                         : gv + (i - 2 * PQ) * 1024;
-            dma16(src + L.lane * 16, buf_lds + i * 1024);
+            const char* src = i < PQ ? gq + 16 * Swz<2 * DK>::slot(64 * i + L.lane)
+                            : i < 2 * PQ ? gk + 16 * Swz<2 * DK>::slot(64 * (i - PQ) + L.lane)
+                                         : gv + 16 * Swz<2 * DV>::slot(64 * (i - 2 * PQ) + L.lane);
+            dma16(src, buf_lds + i * 1024);
         }
     }
 
@@ -140,10 +171,11 @@ struct ChunkIO {
         const int tid = L.w * 64 + L.lane, nthr = NW * 64;
         for (int u = tid; u < QU; u += nthr) {
             const bool ok = u / QPR < n;
-            if (with_q) lq[u] = ok ? gq[u] : zero;
-            lk[u] = ok ? gk[u] : zero;
+            const int sl = Swz<2 * DK>::slot(u);
+            if (with_q) lq[sl] = ok ? gq[u] : zero;
+            lk[sl] = ok ? gk[u] : zero;
         }
-        for (int u = tid; u < VU; u += nthr) lv[u] = (u / VPR < n) ? gv[u] : zero;
+        for (int u = tid; u < VU; u += nthr) lv[Swz<2 * DV>::slot(u)] = (u / VPR < n) ? gv[u] : zero;
         compiler_fence();
     }
 };

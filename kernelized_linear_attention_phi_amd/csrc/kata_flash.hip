@@ -70,15 +70,16 @@ __device__ __forceinline__ QFrag<DK> load_qfrag(const bf16_t* qh, int t, int T, 
     return f;
 }
 
-// Scores of 16 keys (rows, 16 h + c16 of the 32-key step) against the query tile
-// (columns): D[key 4g + r][query c16].
+// Scores of 16 keys (staged rows r .. r + 15 of the block, lane c16 taking row
+// r + c16) against the query tile (columns): D[key 4g + r'][query c16].
 template <int DK>
-__device__ __forceinline__ f32x4_t key_scores(const bf16_t* krow, const QFrag<DK>& qf, const Lane& L) {
+__device__ __forceinline__ f32x4_t key_scores(const bf16_t* bk, int row, const QFrag<DK>& qf,
+                                              const Lane& L) {
     if constexpr (DK == 32) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(krow + 8 * L.g);
+        const u32x4_t kf = lds_row<2 * DK, u32x4_t>(bk, row, 16 * L.g);
         return mma32(kf, qf.x, zero4());
     } else {
-        const u32x2_t kf = *reinterpret_cast<const u32x2_t*>(krow + 4 * L.g);
+        const u32x2_t kf = lds_row<2 * DK, u32x2_t>(bk, row, 8 * L.g);
         return mma16(kf, u32x2_t{qf.x[0], qf.x[1]}, zero4());
     }
 }
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(64 * FNW) void kata_flash_fwd_kernel(
                 float w[8];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const f32x4_t sc = key_scores<DK>(bk + (32 * m + 16 * h + L.c16) * DK, qf[u], L);
+                    const f32x4_t sc = key_scores<DK>(bk, 32 * m + 16 * h + L.c16, qf[u], L);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int j = key0 + 16 * h + 4 * L.g + r;

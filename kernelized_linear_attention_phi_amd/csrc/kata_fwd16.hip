@@ -101,7 +101,7 @@ __device__ __forceinline__ void k_transposed(const bf16_t* bk, f32x4_t (&KT)[Cfg
     const u32x2_t id = ident16(L);
 #pragma unroll
     for (int jb = 0; jb < F::TT; ++jb) {
-        const u32x2_t kf = *reinterpret_cast<const u32x2_t*>(bk + (16 * jb + L.c16) * DK + 4 * L.g);
+        const u32x2_t kf = lds_row<2 * DK, u32x2_t>(bk, 16 * jb + L.c16, 8 * L.g);
         KT[jb] = mma16(kf, id, zero4());
     }
 }
@@ -190,8 +190,7 @@ __device__ __forceinline__ void load_query(const bf16_t* bq, int tt, const Lane&
                                            u32x2_t& qf) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-        const u32x2_t piece = *reinterpret_cast<const u32x2_t*>(
-            bq + (16 * tt + L.c16) * DK + 4 * ((L.g + a) & 3));
+        const u32x2_t piece = lds_row<2 * DK, u32x2_t>(bq, 16 * tt + L.c16, 8 * ((L.g + a) & 3));
         if (a == 0) qf = piece;
         qr[4 * a + 0] = lo_bf16(piece[0]);
         qr[4 * a + 1] = hi_bf16(piece[0]);
@@ -414,8 +413,8 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
                     float w[8];
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const u32x2_t kf = *reinterpret_cast<const u32x2_t*>(
-                            bk + (32 * m + 16 * h + L.c16) * DK + 4 * L.g);
+                        const u32x2_t kf =
+                            lds_row<2 * DK, u32x2_t>(bk, 32 * m + 16 * h + L.c16, 8 * L.g);
                         // rows j = 32m + 16h + 4g + r, column t
                         const f32x4_t sc = mma16(kf, qf, zero4());
 #pragma unroll

@@ -45,11 +45,18 @@ namespace {
 
 constexpr int DK = 32;
 constexpr int NFT = 33;                 // feature tiles
-constexpr int NW = 4;                   // wavefronts per segment
 constexpr int NZ = 4;                   // Gram tiles
+
+// Wavefronts per segment: eight (two per SIMD) when the chunk has eight query
+// tiles, four otherwise.
+template <int C> __host__ __device__ constexpr int nw32() { return C == 128 ? 8 : 4; }
+template <int C> constexpr int kThreads32 = 64 * nw32<C>();
+template <int C> constexpr int kWavesPerSimd32 = nw32<C>() / 4;
 
 template <int DV, int C>
 struct Cfg32 {
+    static constexpr int NW = nw32<C>();
+    static constexpr int TPW = 32 / NW;           // full feature tiles per wavefront
     static constexpr int NTV = DV / 16;           // value tiles
     static constexpr int TT = C / 16;             // query tiles per chunk
     static constexpr int TW = TT / NW;            // query tiles per wavefront
@@ -67,36 +74,55 @@ struct Cfg32 {
     static constexpr int LDS_SEG = 4 * IO::BUF;     // 4-deep staging of k | v
     static constexpr int REC = NFT * NTV * 256 + NZ * 256;   // floats per state record
     static_assert(TW >= 1, "at least one query tile per wavefront");
+    static_assert(NW * TPW == 32 && TPW % 2 == 0, "tile pairs do not straddle wavefronts");
 };
 
-// Running state of wavefront W: tiles 8W..8W+7 of S (all value tiles), value
-// tile W of tile 32 (when W < NTV), Gram tile W.
+// Ownership. Wavefront W holds full tiles TPW*W .. TPW*W + TPW - 1 for every
+// value tile; value tile xnt of tile 32 when has_x (the last four wavefronts
+// with eight, wavefront nt with four); Gram tile W when W < 4.
+template <int DV, int C, int W> __host__ __device__ constexpr bool has_x() {
+    return Cfg32<DV, C>::NW == 8 ? (W >= 4 && W - 4 < Cfg32<DV, C>::NTV) : (W < Cfg32<DV, C>::NTV);
+}
+template <int DV, int C, int W> __host__ __device__ constexpr int xnt() {
+    return Cfg32<DV, C>::NW == 8 ? W - 4 : W;
+}
+// feature class of tile t: 0 = L-circulant, 1 = U-circulant, 2 = cross
+__host__ __device__ constexpr int tile_class(int t) { return t < 8 ? 0 : t < 16 ? 1 : 2; }
+template <int DV, int C, int W> __host__ __device__ constexpr bool needs_l() {
+    constexpr int t0 = Cfg32<DV, C>::TPW * W;
+    return tile_class(t0) != 1 || has_x<DV, C, W>() || (W < 4 && W != 3);
+}
+template <int DV, int C, int W> __host__ __device__ constexpr bool needs_u() {
+    constexpr int t0 = Cfg32<DV, C>::TPW * W;
+    return tile_class(t0) != 0 || has_x<DV, C, W>() || (W >= 1 && W < 4);
+}
+
+// Running state of one wavefront (see the ownership rules above).
 template <int DV, int C>
 struct State32 {
-    f32x4_t s[8][Cfg32<DV, C>::NTV];
+    f32x4_t s[Cfg32<DV, C>::TPW][Cfg32<DV, C>::NTV];
     f32x4_t x;
     f32x4_t z;
 };
 
 // Query tile of slot u of wavefront W.
-template <int W, int TT>
+template <int W, int TT, int NW>
 __device__ __forceinline__ constexpr int own_query_tile(int u) {
     return u == 0 ? W : TT - 1 - W;
 }
 
 // ---- lifts -----------------------------------------------------------------------
 
-// phi(K) rows of own tile I of wavefront W for the 8 tokens of one K-step:
-// kl / ku hold coordinate c16 / 16 + c16 of each token (fp32, exact).
-template <int W, int I>
+// phi(K) rows of feature tile T for the 8 tokens of one K-step: kl / ku hold
+// coordinate c16 / 16 + c16 of each token (fp32, exact).
+template <int T>
 __device__ __forceinline__ u32x4_t lift_keys32(const float (&kl)[8], const float (&ku)[8]) {
     float f[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        if constexpr (W == 0) f[s] = kl[s] * partner<I>(kl[s]);
-        else if constexpr (W == 1) f[s] = ku[s] * partner<I>(ku[s]);
-        else if constexpr (W == 2) f[s] = kl[s] * partner<I>(ku[s]);
-        else f[s] = kl[s] * partner<8 + I>(ku[s]);
+        if constexpr (T < 8) f[s] = kl[s] * partner<T>(kl[s]);
+        else if constexpr (T < 16) f[s] = ku[s] * partner<T - 8>(ku[s]);
+        else f[s] = kl[s] * partner<T - 16>(ku[s]);
     }
     return u32x4_t{pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
 }
@@ -116,17 +142,12 @@ __device__ __forceinline__ u32x4_t lift_keys_mixed(const float (&kl)[8], const f
     return u32x4_t{pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
 }
 
-template <int W>
-__device__ __forceinline__ u32x4_t lift_keys_own(int i, const float (&kl)[8], const float (&ku)[8]) {
-    switch (i) {
-        case 0: return lift_keys32<W, 0>(kl, ku);
-        case 1: return lift_keys32<W, 1>(kl, ku);
-        case 2: return lift_keys32<W, 2>(kl, ku);
-        case 3: return lift_keys32<W, 3>(kl, ku);
-        case 4: return lift_keys32<W, 4>(kl, ku);
-        case 5: return lift_keys32<W, 5>(kl, ku);
-        case 6: return lift_keys32<W, 6>(kl, ku);
-        default: return lift_keys32<W, 7>(kl, ku);
+// Compile-time loop.
+template <int P, int NP, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (P < NP) {
+        f(std::integral_constant<int, P>{});
+        static_for<P + 1, NP>(f);
     }
 }
 
@@ -139,14 +160,13 @@ struct QueryRow {
 };
 
 __device__ __forceinline__ void load_query32(const bf16_t* bq, int tt, const Lane& L, QueryRow& Q) {
-    const bf16_t* row = bq + (16 * tt + L.c16) * DK;
+    const int row = 16 * tt + L.c16;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         float* dst = h ? Q.b : Q.a;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const u32x2_t piece =
-                *reinterpret_cast<const u32x2_t*>(row + 16 * h + 4 * ((L.g + p) & 3));
+            const u32x2_t piece = lds_row<2 * DK, u32x2_t>(bq, row, 32 * h + 8 * ((L.g + p) & 3));
             if (p == 0) {
                 Q.zf[2 * h] = piece[0];
                 Q.zf[2 * h + 1] = piece[1];
@@ -192,28 +212,20 @@ __device__ __forceinline__ u32x2_t lift_query_mixed(const QueryRow& Q, const Lan
                    pk2(query_entry<32>(Q, 2, lo), query_entry<32>(Q, 3, lo))};
 }
 
-// Compile-time loop over tile pairs.
-template <int P, int NP, typename F>
-__device__ __forceinline__ void for_pairs(F&& f) {
-    if constexpr (P < NP) {
-        f(std::integral_constant<int, P>{});
-        for_pairs<P + 1, NP>(f);
-    }
-}
-
 // ---- K^T fragments ----------------------------------------------------------------
 
 // kl[s] / ku[s] = k[token(s)][c16] / k[token(s)][16 + c16] for the 8 tokens of
 // K-step m (slot s = token 32m + 16(s/4) + 4g + s%4), via identity products.
-__device__ __forceinline__ void key_columns(const bf16_t* bk, int m, const Lane& L, bool need_l,
-                                            bool need_u, float (&kl)[8], float (&ku)[8]) {
+template <bool NEED_L, bool NEED_U>
+__device__ __forceinline__ void key_columns(const bf16_t* bk, int m, const Lane& L,
+                                            float (&kl)[8], float (&ku)[8]) {
     const u32x2_t id = ident16(L);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const bf16_t* row = bk + (32 * m + 16 * h + L.c16) * DK + 4 * L.g;
+        const int row = 32 * m + 16 * h + L.c16;
         f32x4_t tl = zero4(), tu = zero4();
-        if (need_l) tl = mma16(*reinterpret_cast<const u32x2_t*>(row), id, zero4());
-        if (need_u) tu = mma16(*reinterpret_cast<const u32x2_t*>(row + 16), id, zero4());
+        if constexpr (NEED_L) tl = mma16(lds_row<2 * DK, u32x2_t>(bk, row, 8 * L.g), id, zero4());
+        if constexpr (NEED_U) tu = mma16(lds_row<2 * DK, u32x2_t>(bk, row, 32 + 8 * L.g), id, zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             kl[4 * h + r] = tl[r];
@@ -231,13 +243,10 @@ template <int W, int DV, int C>
 __device__ __forceinline__ void state_step(State32<DV, C>& st, const bf16_t* bk, const bf16_t* bv,
                                            int m, const Lane& L) {
     using F = Cfg32<DV, C>;
-    constexpr bool has_x = W < F::NTV;
     float kl[8], ku[8];
-    // every wavefront needs L (own tiles, or the L row of its Gram tile LU / UL);
-    // wavefront 0 needs U only for tile 32
-    key_columns(bk, m, L, true, W != 0 || has_x, kl, ku);
-    // Gram tile W: LL, LU, UL, UU (A rows = first half, B columns = second)
-    {
+    key_columns<needs_l<DV, C, W>(), needs_u<DV, C, W>()>(bk, m, L, kl, ku);
+    if constexpr (W < 4) {
+        // Gram tile W: LL, LU, UL, UU (A rows = first half, B columns = second)
         const u32x4_t gl = pack8(kl), gu = pack8(ku);
         if constexpr (W == 0) st.z = mma32(gl, gl, st.z);
         else if constexpr (W == 1) st.z = mma32(gl, gu, st.z);
@@ -247,13 +256,14 @@ __device__ __forceinline__ void state_step(State32<DV, C>& st, const bf16_t* bk,
     u32x4_t vop[F::NTV];
 #pragma unroll
     for (int nt = 0; nt < F::NTV; ++nt) vop[nt] = v_fragment_tr<DV>(bv, m, nt, L);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const u32x4_t fk = lift_keys_own<W>(i, kl, ku);
+    static_for<0, F::TPW>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const u32x4_t fk = lift_keys32<F::TPW * W + i>(kl, ku);
 #pragma unroll
         for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] = mma32(fk, vop[nt], st.s[i][nt]);
-    }
-    if constexpr (has_x) st.x = mma32(lift_keys_mixed(kl, ku, L), vop[W], st.x);
+    });
+    if constexpr (has_x<DV, C, W>())
+        st.x = mma32(lift_keys_mixed(kl, ku, L), vop[xnt<DV, C, W>()], st.x);
 }
 
 // ---- state records: S unit (tile t, value tile nt) at ((t*NTV + nt)*64 + lane)*4 + r,
@@ -264,12 +274,12 @@ __device__ __forceinline__ void record_store32(float* rec, const State32<DV, C>&
     using F = Cfg32<DV, C>;
     f32x4_t* r4 = reinterpret_cast<f32x4_t*>(rec);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < F::TPW; ++i)
 #pragma unroll
         for (int nt = 0; nt < F::NTV; ++nt)
-            r4[((8 * W + i) * F::NTV + nt) * 64 + L.lane] = st.s[i][nt];
-    if constexpr (W < F::NTV) r4[(32 * F::NTV + W) * 64 + L.lane] = st.x;
-    r4[(NFT * F::NTV + W) * 64 + L.lane] = st.z;
+            r4[((F::TPW * W + i) * F::NTV + nt) * 64 + L.lane] = st.s[i][nt];
+    if constexpr (has_x<DV, C, W>()) r4[(32 * F::NTV + xnt<DV, C, W>()) * 64 + L.lane] = st.x;
+    if constexpr (W < 4) r4[(NFT * F::NTV + W) * 64 + L.lane] = st.z;
 }
 
 template <int W, int DV, int C>
@@ -277,12 +287,12 @@ __device__ __forceinline__ void record_load32(const float* rec, State32<DV, C>& 
     using F = Cfg32<DV, C>;
     const f32x4_t* r4 = reinterpret_cast<const f32x4_t*>(rec);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < F::TPW; ++i)
 #pragma unroll
         for (int nt = 0; nt < F::NTV; ++nt)
-            st.s[i][nt] = r4[((8 * W + i) * F::NTV + nt) * 64 + L.lane];
-    st.x = W < F::NTV ? r4[(32 * F::NTV + W) * 64 + L.lane] : zero4();
-    st.z = r4[(NFT * F::NTV + W) * 64 + L.lane];
+            st.s[i][nt] = r4[((F::TPW * W + i) * F::NTV + nt) * 64 + L.lane];
+    st.x = has_x<DV, C, W>() ? r4[(32 * F::NTV + xnt<DV, C, W>()) * 64 + L.lane] : zero4();
+    st.z = W < 4 ? r4[(NFT * F::NTV + W) * 64 + L.lane] : zero4();
 }
 
 // bf16 operands of this wavefront's part of the state, for every wavefront:
@@ -294,20 +304,23 @@ template <int W, int DV, int C>
 __device__ __forceinline__ void publish_state(char* sb, const State32<DV, C>& st, const Lane& L) {
     using F = Cfg32<DV, C>;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < F::TPW / 2; ++j)
 #pragma unroll
         for (int nt = 0; nt < F::NTV; ++nt) {
             const f32x4_t& x = st.s[2 * j][nt];
             const f32x4_t& y = st.s[2 * j + 1][nt];
-            *reinterpret_cast<u32x4_t*>(sb + (((4 * W + j) * F::NTV + nt) * 64 + L.lane) * 16) =
+            const int p = F::TPW / 2 * W + j;
+            *reinterpret_cast<u32x4_t*>(sb + ((p * F::NTV + nt) * 64 + L.lane) * 16) =
                 u32x4_t{pk2(x[0], x[1]), pk2(x[2], x[3]), pk2(y[0], y[1]), pk2(y[2], y[3])};
         }
-    if constexpr (W < F::NTV)
-        *reinterpret_cast<u32x2_t*>(sb + F::SPAIR + (W * 64 + L.lane) * 8) =
+    if constexpr (has_x<DV, C, W>())
+        *reinterpret_cast<u32x2_t*>(sb + F::SPAIR + (xnt<DV, C, W>() * 64 + L.lane) * 8) =
             u32x2_t{pk2(st.x[0], st.x[1]), pk2(st.x[2], st.x[3])};
-    constexpr int half = (W == 1 || W == 3) ? 1 : 0, part = W >= 2 ? 1 : 0;
-    *reinterpret_cast<u32x2_t*>(sb + F::SPAIR + F::S32 + (half * 64 + L.lane) * 16 + part * 8) =
-        u32x2_t{pk2(st.z[0], st.z[1]), pk2(st.z[2], st.z[3])};
+    if constexpr (W < 4) {
+        constexpr int half = (W == 1 || W == 3) ? 1 : 0, part = W >= 2 ? 1 : 0;
+        *reinterpret_cast<u32x2_t*>(sb + F::SPAIR + F::S32 + (half * 64 + L.lane) * 16 + part * 8) =
+            u32x2_t{pk2(st.z[0], st.z[1]), pk2(st.z[2], st.z[3])};
+    }
 }
 
 // ---- per-wavefront bodies ----------------------------------------------------------
@@ -319,10 +332,10 @@ __device__ __forceinline__ void seg_state_body32(const bf16_t* k, const bf16_t* 
     using F = Cfg32<DV, C>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    LoadPipeline<DK, DV, C, NW, 4> P{lds, seg * G, min(NC, seg * G + G), T, bh * T};
+    LoadPipeline<DK, DV, C, F::NW, 4> P{lds, seg * G, min(NC, seg * G + G), T, bh * T};
     State32<DV, C> st;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < F::TPW; ++i)
 #pragma unroll
         for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] = zero4();
     st.x = zero4();
@@ -348,7 +361,7 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
     using F = Cfg32<DV, C>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    Pipeline<DK, DV, C, NW> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true};
+    Pipeline<DK, DV, C, F::NW> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true};
     char* sb = lds + 2 * F::IO::BUF;
     char* otile = sb + F::SB + W * F::OTILE;
 
@@ -378,11 +391,11 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
         QueryRow Q[F::TW];
 #pragma unroll
         for (int u = 0; u < F::TW; ++u) {
-            load_query32(bq, own_query_tile<W, F::TT>(u), L, Q[u]);
+            load_query32(bq, own_query_tile<W, F::TT, F::NW>(u), L, Q[u]);
 #pragma unroll
             for (int nt = 0; nt <= F::NTV; ++nt) num[u][nt] = zero4();
         }
-        for_pairs<0, 16>([&](auto pc) {
+        static_for<0, 16>([&](auto pc) {
             constexpr int p = decltype(pc)::value;
             u32x4_t fq[F::TW];
 #pragma unroll
@@ -429,19 +442,19 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
 
 #pragma unroll
         for (int u = 0; u < F::TW; ++u) {
-            const int tt = own_query_tile<W, F::TT>(u);
+            const int tt = own_query_tile<W, F::TT, F::NW>(u);
             // ---- intra-chunk term: A = (Q K^T)^2 masked to j <= t, num += A [V | 1]
             if (CAUSAL) {
                 const int t = 16 * tt + L.c16;
-                const u32x4_t qf = *reinterpret_cast<const u32x4_t*>(bq + t * DK + 8 * L.g);
+                const u32x4_t qf = lds_row<2 * DK, u32x4_t>(bq, t, 16 * L.g);
                 const u32x4_t ones = ones_op(L);
                 for (int m = 0; m <= tt / 2; ++m) {
                     const bool diag = 32 * m + 31 > 16 * tt;
                     float w[8];
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(
-                            bk + (32 * m + 16 * h + L.c16) * DK + 8 * L.g);
+                        const u32x4_t kf =
+                            lds_row<2 * DK, u32x4_t>(bk, 32 * m + 16 * h + L.c16, 16 * L.g);
                         // rows j = 32m + 16h + 4g + r, column t
                         const f32x4_t sc = mma32(kf, qf, zero4());
 #pragma unroll
@@ -464,7 +477,7 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
         bf16_t* oc = o + (bh * T + (size_t)c * C) * DV;
 #pragma unroll
         for (int u = 0; u < F::TW; ++u) {
-            const int tt = own_query_tile<W, F::TT>(u);
+            const int tt = own_query_tile<W, F::TT, F::NW>(u);
             // intra-chunk denominator: row 0 of the ones tile (lane group 0)
             const float den = __shfl(num[u][F::NTV][0], L.c16, 64) + di[u];
             const float y = den != 0.0f ? 1.0f / den : 0.0f;   // y = 0 gives o = 0
@@ -504,37 +517,39 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
     }
 }
 
+// Body dispatch by wavefront index (compile-time roles).
+template <int DV, int C, typename F>
+__device__ __forceinline__ void by_wave(int w, F&& f) {
+    static_for<0, Cfg32<DV, C>::NW>([&](auto wc) {
+        if (w == decltype(wc)::value) f(wc);
+    });
+}
+
 // ---- kernels -------------------------------------------------------------------
 
 template <int DV, int C>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads32<C>, kWavesPerSimd32<C>)
 void kata_seg_state32(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                       float* __restrict__ rec, int T, int NC, int G, int NSEG) {
     using F = Cfg32<DV, C>;
     __shared__ __attribute__((aligned(16))) char lds[F::LDS_SEG];
     const Lane L;
-    switch (L.w) {
-        case 0: seg_state_body32<0, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L); break;
-        case 1: seg_state_body32<1, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L); break;
-        case 2: seg_state_body32<2, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L); break;
-        default: seg_state_body32<3, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L); break;
-    }
+    by_wave<DV, C>(L.w, [&](auto wc) {
+        seg_state_body32<decltype(wc)::value, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L);
+    });
 }
 
 template <int DV, int C, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads32<C>, kWavesPerSimd32<C>)
 void kata_fwd32(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bf16_t* __restrict__ v, const float* __restrict__ prefix,
                 bf16_t* __restrict__ o, int T, int NC, int G, int NSEG) {
     using F = Cfg32<DV, C>;
     __shared__ __attribute__((aligned(16))) char lds[F::LDS_FWD];
     const Lane L;
-    switch (L.w) {
-        case 0: fwd_body32<0, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L); break;
-        case 1: fwd_body32<1, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L); break;
-        case 2: fwd_body32<2, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L); break;
-        default: fwd_body32<3, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L); break;
-    }
+    by_wave<DV, C>(L.w, [&](auto wc) {
+        fwd_body32<decltype(wc)::value, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L);
+    });
 }
 
 template <int DV, int C>
@@ -542,15 +557,16 @@ hipError_t launch_dv_c32(const Shape& s, const void* q, const void* k, const voi
                          const float* prefix, void* o, int causal, int G, int NSEG,
                          bool state_only, hipStream_t st) {
     dim3 grid(NSEG, s.B * s.H);
+    constexpr int threads = kThreads32<C>;
     if (state_only) {
-        kata_seg_state32<DV, C><<<grid, 64 * NW, 0, st>>>((const bf16_t*)k, (const bf16_t*)v, rec,
+        kata_seg_state32<DV, C><<<grid, threads, 0, st>>>((const bf16_t*)k, (const bf16_t*)v, rec,
                                                            s.T, s.NC, G, NSEG);
     } else if (causal) {
-        kata_fwd32<DV, C, true><<<grid, 64 * NW, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
+        kata_fwd32<DV, C, true><<<grid, threads, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
                                                            (const bf16_t*)v, prefix, (bf16_t*)o,
                                                            s.T, s.NC, G, NSEG);
     } else {
-        kata_fwd32<DV, C, false><<<grid, 64 * NW, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
+        kata_fwd32<DV, C, false><<<grid, threads, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
                                                             (const bf16_t*)v, prefix, (bf16_t*)o,
                                                             s.T, s.NC, G, NSEG);
     }
