@@ -45,6 +45,15 @@ __device__ __forceinline__ void lds_barrier() {
     compiler_fence();
 }
 
+// Reciprocal of a denominator for a bf16 output row: v_rcp_f32 (within 1 ulp),
+// and 0 for den == 0 so that the row's output is 0. o = num * y is then within
+// 2 fp32 ulps of num / den; rounding to bf16 (8 bits of mantissa) takes the same
+// value as for the correctly rounded quotient except within 2 fp32 ulps of a
+// bf16 rounding midpoint.
+__device__ __forceinline__ float inv_den(float den) {
+    return den != 0.0f ? __builtin_amdgcn_rcpf(den) : 0.0f;
+}
+
 // Value of lane (c16 + d) mod 16 of the same row, for a compile-time d.
 template <int D>
 __device__ __forceinline__ float partner(float x) {
@@ -180,6 +189,28 @@ struct ChunkIO {
     }
 };
 
+// vmcnt(n) for a run-time n in 0..15 (larger n waits for everything).
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+    switch (n) {
+        case 1: wait_vmcnt<1>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 7: wait_vmcnt<7>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 9: wait_vmcnt<9>(); break;
+        case 10: wait_vmcnt<10>(); break;
+        case 11: wait_vmcnt<11>(); break;
+        case 12: wait_vmcnt<12>(); break;
+        case 13: wait_vmcnt<13>(); break;
+        case 14: wait_vmcnt<14>(); break;
+        case 15: wait_vmcnt<15>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
+}
+
 // Chunk c of a segment [c0, c1) lives in buffer (c - c0) % 2 and is staged one
 // iteration ahead. Per iteration: a loading wavefront waits for every
 // outstanding memory operation of its own (its part of chunk c, and any stores:
@@ -211,29 +242,29 @@ struct Pipeline {
         lds_barrier();
         stage(q, k, v, c + 1, L);
     }
-};
 
-// vmcnt(n) for a run-time n in 0..15 (larger n waits for everything).
-__device__ __forceinline__ void wait_vmcnt_upto(int n) {
-    switch (n) {
-        case 1: wait_vmcnt<1>(); break;
-        case 2: wait_vmcnt<2>(); break;
-        case 3: wait_vmcnt<3>(); break;
-        case 4: wait_vmcnt<4>(); break;
-        case 5: wait_vmcnt<5>(); break;
-        case 6: wait_vmcnt<6>(); break;
-        case 7: wait_vmcnt<7>(); break;
-        case 8: wait_vmcnt<8>(); break;
-        case 9: wait_vmcnt<9>(); break;
-        case 10: wait_vmcnt<10>(); break;
-        case 11: wait_vmcnt<11>(); break;
-        case 12: wait_vmcnt<12>(); break;
-        case 13: wait_vmcnt<13>(); break;
-        case 14: wait_vmcnt<14>(); break;
-        case 15: wait_vmcnt<15>(); break;
-        default: wait_vmcnt<0>(); break;
+    // Split acquisition for kernels whose loading wavefronts issue no global
+    // stores (their loads then complete in issue order, so partial counts are
+    // exact): acquire_q makes only the q part of chunk c visible (a loading
+    // wavefront lets its k and v copies of chunk c stay in flight), then stages
+    // chunk c+1; wait_kv, placed before a later workgroup barrier, waits for
+    // the rest of chunk c (everything except the copies of chunk c+1).
+    __device__ static int pieces(int w, int first) {
+        int n = 0;
+        for (int i = first; i < 2 * (IO::QB / 1024) + IO::VB / 1024; ++i) n += (i % NLOAD == w);
+        return n;
     }
-}
+    __device__ bool full(int c) const { return c < c1 && T - c * C >= C; }
+    __device__ void acquire_q(const bf16_t* q, const bf16_t* k, const bf16_t* v, int c,
+                              const Lane& L) {
+        if (L.w < NLOAD) wait_vmcnt_upto(full(c) ? pieces(L.w, IO::QB / 1024) : 0);
+        lds_barrier();
+        stage(q, k, v, c + 1, L);
+    }
+    __device__ void wait_kv(int c, const Lane& L) const {
+        if (L.w < NLOAD) wait_vmcnt_upto(full(c + 1) ? pieces(L.w, with_q ? 0 : IO::QB / 1024) : 0);
+    }
+};
 
 // NBUF-deep staging for kernels whose wavefronts issue loads only (k | v of
 // chunks, no global stores until the end): chunk c lives in buffer

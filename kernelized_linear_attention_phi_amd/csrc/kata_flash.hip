@@ -165,17 +165,13 @@ __global__ __launch_bounds__(64 * FNW) void kata_flash_fwd_kernel(
     for (int u = 0; u < FQT; ++u) {
         const int t = q0 + 16 * u + L.c16;
         const float den = __shfl(num[u][F::NTV][0], L.c16, 64);
-        const float y = den != 0.0f ? 1.0f / den : 0.0f;
+        const float y = inv_den(den);   // y = 0 gives o = 0
 #pragma unroll
         for (int nt = 0; nt < F::NTV; ++nt) {
             float ov[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                // Markstein: with y = RN(1/den), q0 + RN(num - q0 den) y = RN(num/den)
-                const float x = num[u][nt][r];
-                const float p = x * y;
-                const float er = __builtin_fmaf(-p, den, x);
-                ov[r] = __builtin_fmaf(er, y, p);
+                ov[r] = num[u][nt][r] * y;
             }
             if (t < T)
                 *reinterpret_cast<u32x2_t*>(o + (head + t) * DV + 16 * nt + 4 * L.g) =

@@ -272,8 +272,10 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
     record_store<W, W == 1, DV, C>(rec + (bh * NSEG + seg) * (size_t)F::REC, st, L);
 }
 
-// Stores the output rows wavefront 0 staged in LDS (its exchange half, row
-// stride OROW, query tiles NW*u) for a chunk with n valid rows; wavefront 1 only.
+// Stores the output rows one wavefront staged in LDS (its exchange half, row
+// stride OROW, query tiles NW*u + w): row r of the staged tiles goes to
+// oc[16*NW*(r/16) + r%16] if that is below n (the caller offsets oc and n by the
+// 16 w rows of the staging wavefront); issued by wavefront 1 only.
 template <int DV, int C>
 __device__ __forceinline__ void store_staged_rows(const char* ostage, bf16_t* oc, int n,
                                                   const Lane& L) {
@@ -294,8 +296,9 @@ __device__ __forceinline__ void store_staged_rows(const char* ostage, bf16_t* oc
 
 // Memory roles: wavefront 0 issues every direct-to-LDS load and no global store,
 // so its wait for chunk data never waits for stores; wavefront 1 issues every
-// output store (its own rows from registers, wavefront 0's rows from LDS one
-// chunk later) and never waits for them.
+// output store and never waits for them. Both stage their output rows in LDS
+// (their own exchange half); wavefront 1 stores its rows in the same chunk and
+// wavefront 0's one chunk later, as whole rows.
 template <int W, int DV, int C, bool CAUSAL>
 __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                          const float* prefix, bf16_t* o, char* lds, int T,
@@ -316,7 +319,7 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
     P.stage(q, k, v, P.c0, L);
     for (int c = P.c0; c < P.c1; ++c) {
         const int n = min(C, T - c * C);
-        P.acquire(q, k, v, c, L);
+        P.acquire_q(q, k, v, c, L);                   // q of chunk c visible
         const char* buf = P.buffer(c);
         const bf16_t* bq = reinterpret_cast<const bf16_t*>(buf);
         const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::QB);
@@ -380,7 +383,8 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
                 }
             }
         }
-        lds_barrier();                                // partials exchanged
+        P.wait_kv(c, L);                              // k, v of chunk c landed
+        lds_barrier();                                // partials exchanged, k and v visible
 #pragma unroll
         for (int u = 0; u < F::TW; ++u)
 #pragma unroll
@@ -442,28 +446,24 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
             di += __shfl_xor(di, 32, 64);
             // intra-chunk denominator: row 0 of the ones tile (lane group 0)
             const float den = __shfl(num[u][F::NTV][0], L.c16, 64) + di;
-            const float y = den != 0.0f ? 1.0f / den : 0.0f;   // y = 0 gives o = 0
+            const float y = inv_den(den);                  // y = 0 gives o = 0
 #pragma unroll
             for (int nt = 0; nt < F::NTV; ++nt) {
                 float ov[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    // Markstein: with y = RN(1/den), q0 + RN(num - q0 den) y = RN(num/den)
-                    const float x = num[u][nt][r];
-                    const float q0 = x * y;
-                    const float er = __builtin_fmaf(-q0, den, x);
-                    ov[r] = __builtin_fmaf(er, y, q0);
+                    ov[r] = num[u][nt][r] * y;
                 }
-                const u32x2_t packed = {pk2(ov[0], ov[1]), pk2(ov[2], ov[3])};
-                if (W == 0) {
-                    // staged in this wavefront's exchange half (its partials are consumed)
-                    *reinterpret_cast<u32x2_t*>(ostage + (16 * u + L.c16) * F::OROW +
-                                                2 * (16 * nt + 4 * L.g)) = packed;
-                } else if (t < n) {
-                    *reinterpret_cast<u32x2_t*>(oc + (size_t)t * DV + 16 * nt + 4 * L.g) = packed;
-                }
+                // staged in this wavefront's exchange half (its partials are consumed)
+                *reinterpret_cast<u32x2_t*>(ostage + W * (F::XB / 2) + (16 * u + L.c16) * F::OROW +
+                                            2 * (16 * nt + 4 * L.g)) = {pk2(ov[0], ov[1]),
+                                                                        pk2(ov[2], ov[3])};
             }
         }
+        // wavefront 1's own rows leave as whole 128-byte rows, read back from its
+        // half before the next chunk's partials overwrite it
+        compiler_fence();
+        if (W == 1) store_staged_rows<DV, C>(ostage + F::XB / 2, oc + 16 * DV, n - 16, L);
 
         // ---- running state: S += phi(K_c)^T V_c, Z += K_c^T K_c
         if (CAUSAL) {

@@ -480,17 +480,13 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
             const int tt = own_query_tile<W, F::TT, F::NW>(u);
             // intra-chunk denominator: row 0 of the ones tile (lane group 0)
             const float den = __shfl(num[u][F::NTV][0], L.c16, 64) + di[u];
-            const float y = den != 0.0f ? 1.0f / den : 0.0f;   // y = 0 gives o = 0
+            const float y = inv_den(den);                  // y = 0 gives o = 0
 #pragma unroll
             for (int nt = 0; nt < F::NTV; ++nt) {
                 float ov[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    // Markstein: with y = RN(1/den), q0 + RN(num - q0 den) y = RN(num/den)
-                    const float x = num[u][nt][r];
-                    const float q0 = x * y;
-                    const float er = __builtin_fmaf(-q0, den, x);
-                    ov[r] = __builtin_fmaf(er, y, q0);
+                    ov[r] = num[u][nt][r] * y;
                 }
                 *reinterpret_cast<u32x2_t*>(otile + L.c16 * F::OROW + 2 * (16 * nt + 4 * L.g)) =
                     u32x2_t{pk2(ov[0], ov[1]), pk2(ov[2], ov[3])};
