@@ -115,6 +115,52 @@ kata_status_t kata_chunked_fwd_profiled(const void* q, const void* k, const void
                                         void* workspace, size_t ws_bytes, void* stream,
                                         void* const* events, int n_events);
 
+/* Feature map of kata_chunked_fwd_ex.
+ *  KATA_FEATURE_PSD: the rank-one PSD lift above (weights (q.k)^2; state
+ *    dimension D = d(d+1)/2, packed) - what kata_chunked_fwd computes.
+ *  KATA_FEATURE_IDENTITY: the first-order feature phi1(x) = x, the baseline the
+ *    paper's abstract sets the PSD lift's scan against (weights q.k; state
+ *    dimension d_k, S [.., d_k, d_v] row-major and z [.., d_k]). The output keeps
+ *    the normalised form o_t = sum_j (q_t.k_j) v_j / sum_j (q_t.k_j), 0 where the
+ *    denominator is 0; it is a convex combination when the weights are
+ *    nonnegative (queries and keys in the nonnegative orthant, the cone of this
+ *    feature in explainer section 2.2). bf16 only. */
+typedef enum { KATA_FEATURE_PSD = 0, KATA_FEATURE_IDENTITY = 1 } kata_feature_t;
+
+/* How the inter-chunk prefix is formed (explainer section 2.3: recurrence depth
+ * O(N_C) sequentially, O(log N_C) with an associative scan).
+ *  KATA_PREFIX_SCAN: chunk states of parallel segments, an associative scan over
+ *    them, then every segment's output in parallel (kata_chunked_fwd).
+ *  KATA_PREFIX_SEQUENTIAL: one workgroup per (batch, head) walks every chunk in
+ *    order, carrying the state from chunk to chunk (depth N_C). Same results up
+ *    to fp32 summation order. bf16 only. */
+typedef enum { KATA_PREFIX_SCAN = 0, KATA_PREFIX_SEQUENTIAL = 1 } kata_prefix_t;
+
+/* State dimension of a feature: d(d+1)/2 for KATA_FEATURE_PSD, d for
+ * KATA_FEATURE_IDENTITY; -1 for d < 0 or an unknown feature. */
+int kata_feature_dim(int d, kata_feature_t feature);
+
+/* Workspace of kata_chunked_fwd_ex (0 if none or if the arguments are invalid). */
+size_t kata_chunked_fwd_ex_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                     kata_dtype_t dtype, int causal, kata_feature_t feature,
+                                     kata_prefix_t prefix);
+
+/* kata_chunked_fwd with a choice of feature map and prefix method; every other
+ * argument as there, with the state dimension of `feature` in S0, z0, S_out,
+ * z_out. KATA_FEATURE_PSD with KATA_PREFIX_SCAN is kata_chunked_fwd.
+ * KATA_FEATURE_IDENTITY and KATA_PREFIX_SEQUENTIAL need dtype KATA_BF16, and
+ * KATA_FEATURE_IDENTITY needs chunk in {32, 64, 128} (else KATA_EUNSUPPORTED);
+ * KATA_PREFIX_SEQUENTIAL with KATA_FEATURE_PSD needs a shape of the bf16
+ * matrix-core path (d_k = 16 with chunk 32 or 64, d_k = 32 with chunk 64 or
+ * 128). */
+kata_status_t kata_chunked_fwd_ex(const void* q, const void* k, const void* v, void* o,
+                                  int B, int H, int T, int d_k, int d_v, int chunk, int causal,
+                                  kata_dtype_t dtype, kata_feature_t feature,
+                                  kata_prefix_t prefix,
+                                  const float* S0, const float* z0,
+                                  float* S_out, float* z_out,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
 /* Bytes of workspace kata_scan_states needs (currently always 0). */
 size_t kata_scan_states_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                   kata_dtype_t dtype);

@@ -5,10 +5,12 @@
     Sp, zp, S, z = kata.scan_states(k, v, chunk=64)         # per-chunk prefixes
     o1 = kata.decode_step(q1, k1, v1, S, z)                 # one recurrent step
     o2 = kata.flash_fwd(q, k, v)                            # quadratic form (bf16)
+    o3 = kata.chunked_fwd(q, k, v, prefix="sequential")     # chunk-by-chunk prefix
+    o4 = kata.chunked_fwd(q, k, v, feature="identity")      # first-order feature
 
 The shared library is loaded on first use; calls raise if it is missing.
 """
 from ._binding import (KataError, chunked_fwd, chunked_fwd_into, chunked_fwd_workspace,  # noqa: F401
-                       decode_step, flash_fwd, lib, phi_dim, scan_states, LIB_PATH)
+                       decode_step, feature_dim, flash_fwd, lib, phi_dim, scan_states, LIB_PATH)
 
 __version__ = "0.1.0"

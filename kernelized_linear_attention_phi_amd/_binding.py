@@ -12,7 +12,7 @@ import os
 import torch
 
 __all__ = ["KataError", "lib", "chunked_fwd", "chunked_fwd_into", "chunked_fwd_workspace",
-           "scan_states", "flash_fwd", "decode_step", "phi_dim", "LIB_PATH"]
+           "scan_states", "flash_fwd", "decode_step", "phi_dim", "feature_dim", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkata.so")
 
@@ -51,6 +51,13 @@ def lib() -> ctypes.CDLL:
         L.kata_chunked_fwd_profiled.argtypes = L.kata_chunked_fwd.argtypes + [
             ctypes.POINTER(ctypes.c_void_p), i]
         L.kata_chunked_fwd_profiled.restype = i
+        L.kata_feature_dim.argtypes = [i, i]
+        L.kata_feature_dim.restype = i
+        L.kata_chunked_fwd_ex_workspace.argtypes = [i, i, i, i, i, i, i, i, i, i]
+        L.kata_chunked_fwd_ex_workspace.restype = sz
+        L.kata_chunked_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i,
+                                          vp, vp, vp, vp, vp, sz, vp]
+        L.kata_chunked_fwd_ex.restype = i
         L.kata_scan_states_workspace.argtypes = [i, i, i, i, i, i, i]
         L.kata_scan_states_workspace.restype = sz
         L.kata_scan_states.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -98,25 +105,54 @@ def _raise(st, what):
         raise KataError(st, what)
 
 
-def chunked_fwd_workspace(B, H, T, dk, dv, chunk, dtype_code, causal=True) -> int:
-    return lib().kata_chunked_fwd_workspace(B, H, T, dk, dv, chunk, dtype_code, int(bool(causal)))
+FEATURES = {"psd": 0, "identity": 1}       # kata_feature_t
+PREFIXES = {"scan": 0, "sequential": 1}    # kata_prefix_t
+
+
+def _modes(feature, prefix):
+    if feature not in FEATURES or prefix not in PREFIXES:
+        raise ValueError(f"feature in {sorted(FEATURES)}, prefix in {sorted(PREFIXES)}")
+    return FEATURES[feature], PREFIXES[prefix]
+
+
+def feature_dim(d: int, feature: str = "psd") -> int:
+    """State dimension: d(d+1)/2 for the PSD lift, d for the identity feature."""
+    return lib().kata_feature_dim(d, _modes(feature, "scan")[0])
+
+
+def chunked_fwd_workspace(B, H, T, dk, dv, chunk, dtype_code, causal=True, feature="psd",
+                          prefix="scan") -> int:
+    f, pf = _modes(feature, prefix)
+    if (f, pf) == (0, 0):
+        return lib().kata_chunked_fwd_workspace(B, H, T, dk, dv, chunk, dtype_code,
+                                                int(bool(causal)))
+    return lib().kata_chunked_fwd_ex_workspace(B, H, T, dk, dv, chunk, dtype_code,
+                                               int(bool(causal)), f, pf)
 
 
 def chunked_fwd_into(q, k, v, o, chunk, causal, workspace, S0=None, z0=None, S_out=None,
-                     z_out=None, events=None):
+                     z_out=None, events=None, feature="psd", prefix="scan"):
     """Raw call: every buffer preallocated by the caller (used by the benchmark).
 
     events: optional sequence of 5 torch.cuda.Event recorded at the phase
     boundaries (chunk states | scan | output kernel | state export) through
-    kata_chunked_fwd_profiled.
+    kata_chunked_fwd_profiled (PSD lift with the scan only).
+    feature / prefix: "psd" or "identity" / "scan" or "sequential"; anything but
+    ("psd", "scan") goes through kata_chunked_fwd_ex.
     """
     B, H, T, dk = q.shape
     dv = v.shape[-1]
+    f, pf = _modes(feature, prefix)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, T, dk, dv, chunk, int(bool(causal)),
-            _dtype_code(q), _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(workspace),
-            ws_bytes, _stream())
-    if events is None:
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, T, dk, dv, chunk, int(bool(causal)),
+            _dtype_code(q))
+    tail = (_ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(workspace), ws_bytes, _stream())
+    args = head + tail
+    if (f, pf) != (0, 0):
+        if events is not None:
+            raise ValueError("phase events are for the PSD lift with the scan")
+        st = lib().kata_chunked_fwd_ex(*head, f, pf, *tail)
+    elif events is None:
         st = lib().kata_chunked_fwd(*args)
     else:
         for e in events:            # torch creates its event lazily, on first record
@@ -127,11 +163,16 @@ def chunked_fwd_into(q, k, v, o, chunk, causal, workspace, S0=None, z0=None, S_o
     _raise(st, "kata_chunked_fwd")
 
 
-def chunked_fwd(q, k, v, chunk=64, causal=True, initial_state=None, return_state=False):
+def chunked_fwd(q, k, v, chunk=64, causal=True, initial_state=None, return_state=False,
+                feature="psd", prefix="scan"):
     """o = KATA forward of q, k [B,H,T,d_k], v [B,H,T,d_v] (fp32 or bf16).
 
     initial_state: optional (S0 [B,H,D,d_v], z0 [B,H,D]) fp32.
     return_state: also return the final (S, z).
+    feature: "psd" (the rank-one PSD lift, D = d(d+1)/2) or "identity" (the
+      first-order feature, D = d; bf16 only).
+    prefix: "scan" (segments + associative scan) or "sequential" (one
+      workgroup per head walks every chunk; bf16 matrix-core shapes only).
     """
     _check_dev(q, k, v)
     if q.dim() != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
@@ -140,7 +181,8 @@ def chunked_fwd(q, k, v, chunk=64, causal=True, initial_state=None, return_state
         raise TypeError("q, k, v must share a dtype")
     B, H, T, dk = q.shape
     dv = v.shape[-1]
-    D = phi_dim(dk)
+    _modes(feature, prefix)
+    D = phi_dim(dk) if feature == "psd" else dk
     S0 = z0 = S_out = z_out = None
     if initial_state is not None:
         S0, z0 = initial_state
@@ -153,9 +195,10 @@ def chunked_fwd(q, k, v, chunk=64, causal=True, initial_state=None, return_state
         S_out = torch.empty((B, H, D, dv), dtype=torch.float32, device=q.device)
         z_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
     o = torch.empty_like(v)
-    nbytes = chunked_fwd_workspace(B, H, T, dk, dv, chunk, _dtype_code(q), causal)
+    nbytes = chunked_fwd_workspace(B, H, T, dk, dv, chunk, _dtype_code(q), causal, feature, prefix)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if nbytes else None
-    chunked_fwd_into(q, k, v, o, chunk, causal, ws, S0, z0, S_out, z_out)
+    chunked_fwd_into(q, k, v, o, chunk, causal, ws, S0, z0, S_out, z_out, feature=feature,
+                     prefix=prefix)
     return (o, (S_out, z_out)) if return_state else o
 
 

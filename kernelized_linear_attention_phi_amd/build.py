@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkata.so")
 
 SOURCES = ["kata_api.cpp", "kata_valu.hip", "kata_scan.hip", "kata_decode.hip", "kata_fwd16.hip",
-           "kata_fwd32.hip", "kata_flash.hip"]
+           "kata_fwd32.hip", "kata_flash.hip", "kata_first.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

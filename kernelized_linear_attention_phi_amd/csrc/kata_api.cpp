@@ -22,27 +22,33 @@ bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64 || c == 128; 
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Checks sizes and the shape set; fills s.
-kata_status_t make_shape(int B, int H, int T, int dk, int dv, int C, kata_dtype_t dt, Shape* s) {
+// Checks sizes and the shape set; fills s (s->D is the state dimension of the
+// feature: d(d+1)/2 for the PSD lift, d for the identity).
+kata_status_t make_shape(int B, int H, int T, int dk, int dv, int C, kata_dtype_t dt, Shape* s,
+                         kata_feature_t f = KATA_FEATURE_PSD) {
     if (B < 0 || H < 0 || T < 0 || dk < 0 || dv < 0 || C <= 0) return KATA_EINVAL;
     if (dt != KATA_F32 && dt != KATA_BF16) return KATA_EINVAL;
     if (!supported_dk(dk) || !supported_dv(dv) || !supported_chunk(C)) return KATA_EUNSUPPORTED;
     // indices are 64-bit in the kernels; keep grid dimensions in range
     if ((int64_t)B * H > 65535 || T > (1 << 28)) return KATA_EUNSUPPORTED;
     s->B = B; s->H = H; s->T = T; s->dk = dk; s->dv = dv; s->C = C;
-    s->D = dk * (dk + 1) / 2;
+    s->D = f == KATA_FEATURE_IDENTITY ? dk : dk * (dk + 1) / 2;
     s->NC = (T + C - 1) / C;
     s->bf16 = dt == KATA_BF16;
     return KATA_OK;
 }
 
-// Launch plan of kata_chunked_fwd and its workspace layout.
-//  VALU path (fp32 inputs, shapes without a matrix-core kernel): per-chunk
-//    records in packed layout, scanned over chunks.
-//  MFMA path (bf16, d_k = 16 or 32): per-segment records of G chunks in
-//    accumulator order, an initial-state record and a total record per head.
+// Launch plan of kata_chunked_fwd(_ex) and its workspace layout.
+//  VALU path (fp32 inputs, shapes without a matrix-core kernel; PSD lift with
+//    the scan only): per-chunk records in packed layout, scanned over chunks.
+//  Matrix-core paths (bf16; PSD lift with d_k = 16 or 32, or the identity
+//    feature): per-segment records of G chunks in accumulator order, an
+//    initial-state record and a total record per head. The sequential prefix
+//    is one segment of every chunk per head.
 struct FwdPlan {
-    int mfma;   // 0 (VALU path), 16 or 32 (d_k of the matrix-core path)
+    bool ok;    // supported combination of shape, feature and prefix method
+    int mfma;   // 0 (VALU path), 16 or 32 (PSD lift, d_k), 1 (identity feature)
+    bool seq;   // sequential prefix
     int G, NSEG, REC;
     size_t S_off, z_off, init_off, total_off, bytes;
 };
@@ -58,17 +64,27 @@ int segment_chunks(const Shape& s, int workgroups) {
     return (int)std::max<long long>(1, chunks / workgroups);
 }
 
-FwdPlan plan_fwd(const Shape& s, int causal) {
+FwdPlan plan_fwd(const Shape& s, int causal, kata_feature_t f = KATA_FEATURE_PSD,
+                 kata_prefix_t pf = KATA_PREFIX_SCAN) {
     FwdPlan p{};
+    if (f == KATA_FEATURE_IDENTITY) {
+        p.ok = kata::first_supported(s);
+        p.mfma = 1;
+    } else {
+        p.mfma = kata::mfma16_supported(s) ? 16 : kata::mfma32_supported(s) ? 32 : 0;
+        p.ok = p.mfma != 0 || pf == KATA_PREFIX_SCAN;
+    }
+    p.seq = pf == KATA_PREFIX_SEQUENTIAL;
     const size_t BH = (size_t)s.B * s.H;
-    if (BH == 0 || s.NC == 0) return p;
-    p.mfma = kata::mfma16_supported(s) ? 16 : kata::mfma32_supported(s) ? 32 : 0;
+    if (!p.ok || BH == 0 || s.NC == 0) return p;
     if (p.mfma) {
-        // d_k = 16: four 2-wavefront workgroups per compute unit; d_k = 32: one
-        // 4-wavefront workgroup (its LDS fills the compute unit)
-        p.G = std::min(segment_chunks(s, p.mfma == 16 ? 1024 : 256), s.NC);
+        // d_k = 16 and the identity feature: four 2-wavefront workgroups per
+        // compute unit; d_k = 32: one workgroup (its LDS fills the compute unit)
+        p.G = p.seq ? s.NC : std::min(segment_chunks(s, p.mfma == 32 ? 256 : 1024), s.NC);
         p.NSEG = (s.NC + p.G - 1) / p.G;
-        p.REC = p.mfma == 16 ? kata::mfma16_record_floats(s.dv) : kata::mfma32_record_floats(s.dv);
+        p.REC = p.mfma == 16   ? kata::mfma16_record_floats(s.dv)
+                : p.mfma == 32 ? kata::mfma32_record_floats(s.dv)
+                               : kata::first_record_floats(s.dk, s.dv);
         p.S_off = 0;
         p.init_off = align256(BH * p.NSEG * p.REC * sizeof(float));
         p.total_off = p.init_off + align256(BH * p.REC * sizeof(float));
@@ -111,14 +127,36 @@ size_t kata_chunked_fwd_workspace(int B, int H, int T, int d_k, int d_v, int chu
     return plan_fwd(s, causal).bytes;
 }
 
+int kata_feature_dim(int d, kata_feature_t feature) {
+    if (d < 0) return -1;
+    if (feature == KATA_FEATURE_PSD) return d * (d + 1) / 2;
+    if (feature == KATA_FEATURE_IDENTITY) return d;
+    return -1;
+}
+
+static bool valid_modes(kata_feature_t f, kata_prefix_t pf) {
+    return (f == KATA_FEATURE_PSD || f == KATA_FEATURE_IDENTITY) &&
+           (pf == KATA_PREFIX_SCAN || pf == KATA_PREFIX_SEQUENTIAL);
+}
+
+size_t kata_chunked_fwd_ex_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                     kata_dtype_t dtype, int causal, kata_feature_t feature,
+                                     kata_prefix_t prefix) {
+    Shape s;
+    if (!valid_modes(feature, prefix)) return 0;
+    if (make_shape(B, H, T, d_k, d_v, chunk, dtype, &s, feature) != KATA_OK) return 0;
+    return plan_fwd(s, causal, feature, prefix).bytes;
+}
+
 static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* v, void* o,
                                       int B, int H, int T, int d_k, int d_v, int chunk,
-                                      int causal, kata_dtype_t dtype, const float* S0,
-                                      const float* z0, float* S_out, float* z_out,
-                                      void* workspace, size_t ws_bytes, void* stream,
-                                      void* const* events) {
+                                      int causal, kata_dtype_t dtype, kata_feature_t feature,
+                                      kata_prefix_t prefix, const float* S0, const float* z0,
+                                      float* S_out, float* z_out, void* workspace,
+                                      size_t ws_bytes, void* stream, void* const* events) {
     Shape s;
-    kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s);
+    if (!valid_modes(feature, prefix)) return KATA_EINVAL;
+    kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s, feature);
     if (st != KATA_OK) return st;
     if ((S0 == nullptr) != (z0 == nullptr)) return KATA_EINVAL;
     if ((S_out == nullptr) != (z_out == nullptr)) return KATA_EINVAL;
@@ -129,7 +167,8 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
                           (const void*)S0, (const void*)z0, (const void*)S_out,
                           (const void*)z_out, (const void*)workspace})
         if (p && !aligned16(p)) return KATA_EINVAL;
-    const FwdPlan plan = plan_fwd(s, causal);
+    const FwdPlan plan = plan_fwd(s, causal, feature, prefix);
+    if (!plan.ok) return KATA_EUNSUPPORTED;
     if (ws_bytes < plan.bytes || (plan.bytes && !workspace)) return KATA_EWORKSPACE;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const size_t nS = (size_t)s.D * s.dv, nz = s.D;
@@ -156,28 +195,48 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
         float* rec = reinterpret_cast<float*>(ws + plan.S_off);
         float* init = reinterpret_cast<float*>(ws + plan.init_off);
         float* total = reinterpret_cast<float*>(ws + plan.total_off);
-        const bool d16 = plan.mfma == 16;
-        if (S0 && e == hipSuccess)
-            e = d16 ? kata::launch_record_from_packed16(init, S0, z0, s.dv, (int)BH, hs)
-                    : kata::launch_record_from_packed32(init, S0, z0, s.dv, (int)BH, hs);
-        if (e == hipSuccess)
-            e = d16 ? kata::launch_seg_state16(s, k, v, rec, plan.G, plan.NSEG, hs)
-                    : kata::launch_seg_state32(s, k, v, rec, plan.G, plan.NSEG, hs);
-        if (e == hipSuccess) e = mark(1);
-        // exclusive prefix over segments in place; inclusive total per head
-        if (e == hipSuccess)
-            e = kata::launch_scan_records(rec, (int)BH, plan.NSEG, plan.REC, S0 ? init : nullptr,
-                                          total, nullptr, hs);
-        if (e == hipSuccess) e = mark(2);
-        if (e == hipSuccess)
-            e = d16 ? kata::launch_fwd16(s, q, k, v, causal ? rec : total, o, causal, plan.G,
-                                         plan.NSEG, hs)
-                    : kata::launch_fwd32(s, q, k, v, causal ? rec : total, o, causal, plan.G,
-                                         plan.NSEG, hs);
+        const int m = plan.mfma, nrec = (int)BH;
+        auto from_packed = [&]() {
+            return m == 16   ? kata::launch_record_from_packed16(init, S0, z0, s.dv, nrec, hs)
+                   : m == 32 ? kata::launch_record_from_packed32(init, S0, z0, s.dv, nrec, hs)
+                             : kata::launch_record_from_packed1(init, S0, z0, s.dk, s.dv, nrec, hs);
+        };
+        auto to_packed = [&]() {
+            return m == 16   ? kata::launch_record_to_packed16(total, S_out, z_out, s.dv, nrec, hs)
+                   : m == 32 ? kata::launch_record_to_packed32(total, S_out, z_out, s.dv, nrec, hs)
+                             : kata::launch_record_to_packed1(total, S_out, z_out, s.dk, s.dv, nrec, hs);
+        };
+        auto seg_state = [&]() {
+            return m == 16   ? kata::launch_seg_state16(s, k, v, rec, plan.G, plan.NSEG, hs)
+                   : m == 32 ? kata::launch_seg_state32(s, k, v, rec, plan.G, plan.NSEG, hs)
+                             : kata::launch_seg_state1(s, k, v, rec, plan.G, plan.NSEG, hs);
+        };
+        auto output = [&](const float* pre, float* fin) {
+            return m == 16   ? kata::launch_fwd16(s, q, k, v, pre, fin, o, causal, plan.G, plan.NSEG, hs)
+                   : m == 32 ? kata::launch_fwd32(s, q, k, v, pre, fin, o, causal, plan.G, plan.NSEG, hs)
+                             : kata::launch_fwd1(s, q, k, v, pre, fin, o, causal, plan.G, plan.NSEG, hs);
+        };
+        if (S0 && e == hipSuccess) e = from_packed();
+        if (plan.seq && causal) {
+            // one segment per head walks every chunk from the initial state; its
+            // running state at the end is the final state
+            if (!S0 && e == hipSuccess)
+                e = kata::launch_copy_or_zero(init, nullptr, BH * plan.REC, hs);
+            if (e == hipSuccess) e = mark(1);
+            if (e == hipSuccess) e = mark(2);
+            if (e == hipSuccess) e = output(init, S_out ? total : nullptr);
+        } else {
+            if (e == hipSuccess) e = seg_state();
+            if (e == hipSuccess) e = mark(1);
+            // exclusive prefix over segments in place; inclusive total per head
+            if (e == hipSuccess)
+                e = kata::launch_scan_records(rec, (int)BH, plan.NSEG, plan.REC,
+                                              S0 ? init : nullptr, total, nullptr, hs);
+            if (e == hipSuccess) e = mark(2);
+            if (e == hipSuccess) e = output(causal ? rec : total, nullptr);
+        }
         if (e == hipSuccess) e = mark(3);
-        if (S_out && e == hipSuccess)
-            e = d16 ? kata::launch_record_to_packed16(total, S_out, z_out, s.dv, (int)BH, hs)
-                    : kata::launch_record_to_packed32(total, S_out, z_out, s.dv, (int)BH, hs);
+        if (S_out && e == hipSuccess) e = to_packed();
         if (e == hipSuccess) e = mark(4);
         return hip_status(e);
     }
@@ -214,8 +273,19 @@ kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, void
                                kata_dtype_t dtype, const float* S0, const float* z0,
                                float* S_out, float* z_out, void* workspace, size_t ws_bytes,
                                void* stream) {
-    return chunked_fwd_impl(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, S0, z0, S_out,
-                            z_out, workspace, ws_bytes, stream, nullptr);
+    return chunked_fwd_impl(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, KATA_FEATURE_PSD,
+                            KATA_PREFIX_SCAN, S0, z0, S_out, z_out, workspace, ws_bytes, stream,
+                            nullptr);
+}
+
+kata_status_t kata_chunked_fwd_ex(const void* q, const void* k, const void* v, void* o, int B,
+                                  int H, int T, int d_k, int d_v, int chunk, int causal,
+                                  kata_dtype_t dtype, kata_feature_t feature,
+                                  kata_prefix_t prefix, const float* S0, const float* z0,
+                                  float* S_out, float* z_out, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+    return chunked_fwd_impl(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, feature, prefix,
+                            S0, z0, S_out, z_out, workspace, ws_bytes, stream, nullptr);
 }
 
 kata_status_t kata_chunked_fwd_profiled(const void* q, const void* k, const void* v, void* o,
@@ -227,8 +297,9 @@ kata_status_t kata_chunked_fwd_profiled(const void* q, const void* k, const void
     if (!events || n_events < 5) return KATA_EINVAL;
     for (int i = 0; i < 5; ++i)
         if (!events[i]) return KATA_EINVAL;
-    return chunked_fwd_impl(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, S0, z0, S_out,
-                            z_out, workspace, ws_bytes, stream, events);
+    return chunked_fwd_impl(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, KATA_FEATURE_PSD,
+                            KATA_PREFIX_SCAN, S0, z0, S_out, z_out, workspace, ws_bytes, stream,
+                            events);
 }
 
 size_t kata_scan_states_workspace(int, int, int, int, int, int, kata_dtype_t) { return 0; }

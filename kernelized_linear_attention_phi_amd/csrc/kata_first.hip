@@ -1,0 +1,438 @@
+// First-order (identity feature) chunked forward on gfx950 matrix cores.
+//
+// The paper's abstract sets an associative scan of the first-order feature's
+// inter-chunk recurrence against a matched sequential linear-attention baseline;
+// the KATA explainers (gist.science, technical summary 2.2 and 2.3) place the
+// first-order feature on the orthant cone and give the recurrence depth as
+// O(N_C) sequentially and O(log N_C) with a scan. With phi1(x) = x the weight of
+// key j for query t is q_t . k_j, the state is S = sum_j k_j v_j^T (d_k x d_v) and
+// z = sum_j k_j, and the output takes the same normalised form as the PSD lift:
+// o_t = (A V + q_t P) / (A 1 + q_t Z), zero where the denominator is zero, with
+// A = Q K^T masked to j <= t inside the chunk and (P, Z) the state of every
+// earlier token.
+//
+// The same segment / scan / output structure as the PSD kernels, on the same
+// staging pipeline. A state record holds accumulator tiles: unit (at, u) of 256
+// floats for feature tile at (16 features) and value tile u; u = d_v/16 is the z
+// tile, accumulated against the ones operand so that only its column 0 is
+// nonzero. Element 4*lane + r of a unit is S[16 at + 4 g + r][16 u + c16].
+//
+// Output kernel: two wavefronts; wavefront w owns query tiles w, w + 2, ...
+// (causally balanced) and holds the whole state (d_k x d_v is small), so no
+// partial sums are exchanged. Wavefront 0 issues every chunk copy and no global
+// store; wavefront 1 issues every store (rows staged in LDS by both).
+#include <algorithm>
+
+#include "kata_chunk.h"
+#include "kata_internal.h"
+
+namespace kata {
+
+namespace {
+
+constexpr int NW1 = 2;   // wavefronts per workgroup
+constexpr int ALL = -1;  // "every unit" in place of a wavefront index
+
+template <int DK, int DV, int C>
+struct Cfg1 {
+    static constexpr int NAT = DK / 16;           // feature tiles
+    static constexpr int NTV = DV / 16;           // value tiles
+    static constexpr int NU = NTV + 1;            // value tiles and the z tile
+    static constexpr int TT = C / 16;             // query tiles per chunk
+    static constexpr int TW = TT / NW1;           // query tiles per wavefront
+    static constexpr int KS = C / 32;             // 32-token K-steps per chunk
+    using IO = ChunkIO<DK, DV, C, NW1, 1>;
+    static constexpr int OROW = DV * 2 + 16;      // LDS row stride of staged output rows
+    static constexpr int OST = TW * 16 * OROW;    // staged rows of one wavefront
+    static constexpr int LDS_FWD = 2 * IO::BUF + NW1 * OST;
+    static constexpr int NBUF_SEG = 3 * IO::BUF <= 65536 ? 3 : 2;
+    static constexpr int LDS_SEG = NBUF_SEG * IO::BUF;
+    static constexpr int REC = NAT * NU * 256;
+    static_assert(TW >= 1 && KS >= 1, "chunk of at least 32 tokens");
+};
+
+// Running state: S and z as accumulator tiles, s[at][u].
+template <int DK, int DV, int C>
+struct State1 {
+    f32x4_t s[Cfg1<DK, DV, C>::NAT][Cfg1<DK, DV, C>::NU];
+};
+
+// Unit j = at * NU + u of the state: every unit (W == ALL) or those of
+// wavefront W (j % NW1 == W).
+template <int W, int NU>
+__host__ __device__ constexpr bool owns(int at, int u) {
+    return W == ALL || (at * NU + u) % NW1 == W;
+}
+
+// S += K_c^T [V_c | 1] over one chunk staged in LDS, for the units wavefront W
+// holds: A = K^T fragments (features x tokens), B = V fragments or the ones
+// operand (column 0), both read transposed from the row-major chunk.
+template <int W, int DK, int DV, int C>
+__device__ __forceinline__ void state_update1(State1<DK, DV, C>& st, const bf16_t* bk,
+                                              const bf16_t* bv, const Lane& L) {
+    using F = Cfg1<DK, DV, C>;
+    const u32x4_t ones = ones_op(L);
+#pragma unroll
+    for (int m = 0; m < F::KS; ++m) {
+        u32x4_t kt[F::NAT];
+#pragma unroll
+        for (int at = 0; at < F::NAT; ++at) kt[at] = v_fragment_tr<DK>(bk, m, at, L);
+#pragma unroll
+        for (int u = 0; u < F::NU; ++u) {
+            bool any = false;
+#pragma unroll
+            for (int at = 0; at < F::NAT; ++at) any = any || owns<W, F::NU>(at, u);
+            if (!any) continue;
+            const u32x4_t b = u < F::NTV ? v_fragment_tr<DV>(bv, m, u, L) : ones;
+#pragma unroll
+            for (int at = 0; at < F::NAT; ++at)
+                if (owns<W, F::NU>(at, u)) st.s[at][u] = mma32(kt[at], b, st.s[at][u]);
+        }
+    }
+}
+
+template <int W, int DK, int DV, int C>
+__device__ __forceinline__ void record_store1(float* rec, const State1<DK, DV, C>& st,
+                                              const Lane& L) {
+    using F = Cfg1<DK, DV, C>;
+    f32x4_t* r4 = reinterpret_cast<f32x4_t*>(rec);
+#pragma unroll
+    for (int at = 0; at < F::NAT; ++at)
+#pragma unroll
+        for (int u = 0; u < F::NU; ++u)
+            if (owns<W, F::NU>(at, u)) r4[(at * F::NU + u) * 64 + L.lane] = st.s[at][u];
+}
+
+template <int DK, int DV, int C>
+__device__ __forceinline__ void record_load1(const float* rec, State1<DK, DV, C>& st,
+                                             const Lane& L) {
+    using F = Cfg1<DK, DV, C>;
+    const f32x4_t* r4 = reinterpret_cast<const f32x4_t*>(rec);
+#pragma unroll
+    for (int at = 0; at < F::NAT; ++at)
+#pragma unroll
+        for (int u = 0; u < F::NU; ++u) st.s[at][u] = r4[(at * F::NU + u) * 64 + L.lane];
+}
+
+// ---- segment states ----------------------------------------------------------
+
+template <int W, int DK, int DV, int C>
+__device__ __forceinline__ void seg_state_body1(const bf16_t* k, const bf16_t* v, float* rec,
+                                                char* lds, int T, int NC, int G, int NSEG,
+                                                const Lane& L) {
+    using F = Cfg1<DK, DV, C>;
+    const int seg = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    LoadPipeline<DK, DV, C, NW1, F::NBUF_SEG> P{lds, seg * G, min(NC, seg * G + G), T, bh * T};
+    State1<DK, DV, C> st;
+#pragma unroll
+    for (int at = 0; at < F::NAT; ++at)
+#pragma unroll
+        for (int u = 0; u < F::NU; ++u) st.s[at][u] = zero4();
+    P.prologue(k, v, L);
+    for (int c = P.c0; c < P.c1; ++c) {
+        P.acquire(k, v, c, L);
+        const char* buf = P.buffer(c);
+        state_update1<W, DK, DV, C>(st, reinterpret_cast<const bf16_t*>(buf + F::IO::QB),
+                                    reinterpret_cast<const bf16_t*>(buf + 2 * F::IO::QB), L);
+        compiler_fence();
+    }
+    record_store1<W, DK, DV, C>(rec + (bh * NSEG + seg) * (size_t)F::REC, st, L);
+}
+
+template <int DK, int DV, int C>
+__global__ __launch_bounds__(64 * NW1) void kata_seg_state1(const bf16_t* __restrict__ k,
+                                                            const bf16_t* __restrict__ v,
+                                                            float* __restrict__ rec, int T, int NC,
+                                                            int G, int NSEG) {
+    __shared__ __attribute__((aligned(16))) char lds[Cfg1<DK, DV, C>::LDS_SEG];
+    const Lane L;
+    if (L.w == 0) seg_state_body1<0, DK, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L);
+    else seg_state_body1<1, DK, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L);
+}
+
+// ---- output ------------------------------------------------------------------
+
+// Rows staged by wavefront w (its query tiles NW1*u + w, row stride OROW): staged
+// row r goes to oc[16*NW1*(r/16) + r%16] when that is below n (the caller offsets
+// oc and n by the wavefront's 16 w rows). Wavefront 1 only.
+template <int DK, int DV, int C>
+__device__ __forceinline__ void store_rows1(const char* ost, bf16_t* oc, int n, const Lane& L) {
+    using F = Cfg1<DK, DV, C>;
+    constexpr int UPR = DV * 2 / 16;              // 16-byte units per row
+    constexpr int NUN = F::TW * 16 * UPR;
+#pragma unroll
+    for (int i = 0; i < (NUN + 63) / 64; ++i) {
+        const int unit = L.lane + 64 * i;
+        if (unit < NUN) {
+            const int rl = unit / UPR, col = unit % UPR;
+            const int row = 16 * NW1 * (rl / 16) + rl % 16;
+            const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ost + rl * F::OROW + 16 * col);
+            if (row < n) *reinterpret_cast<u32x4_t*>(oc + (size_t)row * DV + 8 * col) = val;
+        }
+    }
+}
+
+// Query fragment of feature tile at for the K = 16 products (B operand: lane c16
+// = query row, slots 4g + s = features 16 at + 4g + s).
+template <int DK>
+__device__ __forceinline__ u32x2_t query16(const bf16_t* bq, int row, int at, const Lane& L) {
+    return lds_row<2 * DK, u32x2_t>(bq, row, 32 * at + 8 * L.g);
+}
+
+// Scores of 16 keys (rows r .. r+15 of the staged chunk, lane c16 = key r + c16)
+// against a query tile: D[key 4g + r'][query c16] = q . k.
+template <int DK>
+__device__ __forceinline__ f32x4_t scores1(const bf16_t* bk, const bf16_t* bq, int krow, int qrow,
+                                           const Lane& L) {
+    if constexpr (DK == 16) {
+        return mma16(lds_row<32, u32x2_t>(bk, krow, 8 * L.g), lds_row<32, u32x2_t>(bq, qrow, 8 * L.g),
+                     zero4());
+    } else {
+        return mma32(lds_row<64, u32x4_t>(bk, krow, 16 * L.g), lds_row<64, u32x4_t>(bq, qrow, 16 * L.g),
+                     zero4());
+    }
+}
+
+template <int W, int DK, int DV, int C, bool CAUSAL>
+__device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                                          const float* prefix, float* final_rec, bf16_t* o,
+                                          char* lds, int T, int NC, int G, int NSEG,
+                                          const Lane& L) {
+    using F = Cfg1<DK, DV, C>;
+    const int seg = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    Pipeline<DK, DV, C, NW1, 1> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true};
+    char* ostage = lds + 2 * F::IO::BUF;           // [wavefront][OST]
+
+    State1<DK, DV, C> st;
+    record_load1<DK, DV, C>(prefix + (CAUSAL ? bh * NSEG + seg : bh) * (size_t)F::REC, st, L);
+    const u32x4_t ones = ones_op(L);
+
+    P.stage(q, k, v, P.c0, L);
+    for (int c = P.c0; c < P.c1; ++c) {
+        const int n = min(C, T - c * C);
+        P.acquire(q, k, v, c, L);
+        const char* buf = P.buffer(c);
+        const bf16_t* bq = reinterpret_cast<const bf16_t*>(buf);
+        const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::IO::QB);
+        const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::IO::QB);
+        bf16_t* oc = o + (bh * T + (size_t)c * C) * DV;
+
+        // wavefront 0's rows of the previous chunk (always a full chunk)
+        if (W == 1 && c > P.c0) store_rows1<DK, DV, C>(ostage, oc - (size_t)C * DV, C, L);
+        compiler_fence();
+
+        // the state before this chunk as bf16 A operands of S^T (rows = value
+        // columns, K = features); the z tile gives row 0 = z
+        u32x2_t sop[F::NAT][F::NU];
+#pragma unroll
+        for (int at = 0; at < F::NAT; ++at)
+#pragma unroll
+            for (int u = 0; u < F::NU; ++u)
+                sop[at][u] = u32x2_t{pk2(st.s[at][u][0], st.s[at][u][1]),
+                                     pk2(st.s[at][u][2], st.s[at][u][3])};
+
+#pragma unroll
+        for (int ui = 0; ui < F::TW; ++ui) {
+            const int tt = NW1 * ui + W;
+            const int qrow = 16 * tt + L.c16;
+            // num[u]: D[value 16u + 4g + r][query c16]; num[NTV] row 0 = denominator
+            f32x4_t num[F::NU];
+#pragma unroll
+            for (int u = 0; u < F::NU; ++u) num[u] = zero4();
+            // ---- inter-chunk term q.P and q.Z (K = 16 per feature tile)
+#pragma unroll
+            for (int at = 0; at < F::NAT; ++at) {
+                const u32x2_t qa = query16<DK>(bq, qrow, at, L);
+#pragma unroll
+                for (int u = 0; u < F::NU; ++u) num[u] = mma16_acc32(sop[at][u], qa, num[u]);
+            }
+            // ---- intra-chunk term: A = Q K^T masked to j <= t, num += A [V | 1]
+            if (CAUSAL) {
+#pragma unroll
+                for (int m = 0; m <= tt / 2; ++m) {
+                    const bool diag = 32 * m + 31 > 16 * tt;
+                    float w[8];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const f32x4_t sc = scores1<DK>(bk, bq, 32 * m + 16 * h + L.c16, qrow, L);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = 32 * m + 16 * h + 4 * L.g + r;
+                            w[4 * h + r] = (!diag || j <= qrow) ? sc[r] : 0.0f;
+                        }
+                    }
+                    const u32x4_t a = {pk2(w[0], w[1]), pk2(w[2], w[3]), pk2(w[4], w[5]), pk2(w[6], w[7])};
+#pragma unroll
+                    for (int nt = 0; nt < F::NTV; ++nt)
+                        num[nt] = mma32(v_fragment_tr<DV>(bv, m, nt, L), a, num[nt]);
+                    num[F::NTV] = mma32(ones, a, num[F::NTV]);
+                }
+            }
+            // ---- normalise: o = num / den, den = row 0 of the denominator tile
+            const float y = inv_den(__shfl(num[F::NTV][0], L.c16, 64));   // 0 -> o = 0
+#pragma unroll
+            for (int nt = 0; nt < F::NTV; ++nt)
+                *reinterpret_cast<u32x2_t*>(ostage + W * F::OST + (16 * ui + L.c16) * F::OROW +
+                                            2 * (16 * nt + 4 * L.g)) =
+                    u32x2_t{pk2(num[nt][0] * y, num[nt][1] * y), pk2(num[nt][2] * y, num[nt][3] * y)};
+        }
+        // wavefront 1's own rows leave in this chunk, as whole rows
+        compiler_fence();
+        if (W == 1) store_rows1<DK, DV, C>(ostage + F::OST, oc + 16 * DV, n - 16, L);
+
+        // ---- running state: S += K_c^T V_c, z += K_c^T 1 (both wavefronts)
+        if (CAUSAL) state_update1<ALL, DK, DV, C>(st, bk, bv, L);
+        compiler_fence();
+    }
+    // wavefront 0's rows of the last chunk
+    lds_barrier();
+    if (W == 1) {
+        const int cl = P.c1 - 1;
+        store_rows1<DK, DV, C>(ostage, o + (bh * T + (size_t)cl * C) * DV, min(C, T - cl * C), L);
+    }
+    // running state after the segment (the final state when one segment covers
+    // the sequence); the two wavefronts hold the same state and split the units
+    if (CAUSAL && final_rec) record_store1<W, DK, DV, C>(final_rec + bh * (size_t)F::REC, st, L);
+}
+
+template <int DK, int DV, int C, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW1) void kata_fwd1(const bf16_t* __restrict__ q,
+                                                      const bf16_t* __restrict__ k,
+                                                      const bf16_t* __restrict__ v,
+                                                      const float* __restrict__ prefix,
+                                                      float* __restrict__ final_rec,
+                                                      bf16_t* __restrict__ o, int T, int NC,
+                                                      int G, int NSEG) {
+    __shared__ __attribute__((aligned(16))) char lds[Cfg1<DK, DV, C>::LDS_FWD];
+    const Lane L;
+    if (L.w == 0) fwd_body1<0, DK, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC, G, NSEG, L);
+    else fwd_body1<1, DK, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC, G, NSEG, L);
+}
+
+// ---- record <-> packed (S [d_k, d_v] row-major, z [d_k]) ---------------------
+
+__device__ __forceinline__ void rec_coords(int e, int NTV, int* a, int* col, bool* zt) {
+    const int unit = e / 256, lane = (e % 256) / 4, r = e % 4;
+    const int at = unit / (NTV + 1), u = unit % (NTV + 1);
+    *a = 16 * at + 4 * (lane / 16) + r;
+    *zt = u == NTV;
+    *col = *zt ? lane % 16 : 16 * u + lane % 16;
+}
+
+__global__ void record_to_packed1(const float* __restrict__ rec, float* __restrict__ S,
+                                  float* __restrict__ z, int DK, int DV, int REC, int nrec) {
+    for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < (size_t)REC * nrec;
+         x += (size_t)gridDim.x * blockDim.x) {
+        const size_t b = x / REC;
+        int a, col;
+        bool zt;
+        rec_coords((int)(x % REC), DV / 16, &a, &col, &zt);
+        if (!zt) S[(b * DK + a) * DV + col] = rec[x];
+        else if (col == 0) z[b * DK + a] = rec[x];
+    }
+}
+
+__global__ void record_from_packed1(float* __restrict__ rec, const float* __restrict__ S,
+                                    const float* __restrict__ z, int DK, int DV, int REC,
+                                    int nrec) {
+    for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < (size_t)REC * nrec;
+         x += (size_t)gridDim.x * blockDim.x) {
+        const size_t b = x / REC;
+        int a, col;
+        bool zt;
+        rec_coords((int)(x % REC), DV / 16, &a, &col, &zt);
+        rec[x] = !zt ? S[(b * DK + a) * DV + col] : (col == 0 ? z[b * DK + a] : 0.0f);
+    }
+}
+
+// ---- launchers ---------------------------------------------------------------
+
+template <int DK, int DV, int C>
+hipError_t launch_dk_dv_c1(const Shape& s, const void* q, const void* k, const void* v,
+                           float* rec, const float* prefix, void* o, int causal, int G, int NSEG,
+                           bool state_only, hipStream_t st) {
+    dim3 grid(NSEG, s.B * s.H);
+    if (state_only)
+        kata_seg_state1<DK, DV, C><<<grid, 64 * NW1, 0, st>>>((const bf16_t*)k, (const bf16_t*)v,
+                                                               rec, s.T, s.NC, G, NSEG);
+    else if (causal)
+        kata_fwd1<DK, DV, C, true><<<grid, 64 * NW1, 0, st>>>(
+            (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, prefix, rec, (bf16_t*)o, s.T,
+            s.NC, G, NSEG);
+    else
+        kata_fwd1<DK, DV, C, false><<<grid, 64 * NW1, 0, st>>>(
+            (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, prefix, rec, (bf16_t*)o, s.T,
+            s.NC, G, NSEG);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_dk_dv1(const Shape& s, const void* q, const void* k, const void* v, float* rec,
+                         const float* prefix, void* o, int causal, int G, int NSEG,
+                         bool state_only, hipStream_t st) {
+    switch (s.C) {
+        case 32: return launch_dk_dv_c1<DK, DV, 32>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+        case 64: return launch_dk_dv_c1<DK, DV, 64>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+        case 128: return launch_dk_dv_c1<DK, DV, 128>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int DK>
+hipError_t launch_dk1(const Shape& s, const void* q, const void* k, const void* v, float* rec,
+                      const float* prefix, void* o, int causal, int G, int NSEG, bool state_only,
+                      hipStream_t st) {
+    switch (s.dv) {
+        case 16: return launch_dk_dv1<DK, 16>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+        case 32: return launch_dk_dv1<DK, 32>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+        case 64: return launch_dk_dv1<DK, 64>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t dispatch1(const Shape& s, const void* q, const void* k, const void* v, float* rec,
+                     const float* prefix, void* o, int causal, int G, int NSEG, bool state_only,
+                     hipStream_t st) {
+    return s.dk == 16 ? launch_dk1<16>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st)
+                      : launch_dk1<32>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+}
+
+unsigned conv_blocks(size_t n) { return (unsigned)std::min<size_t>((n + 255) / 256, 4096); }
+
+}  // namespace
+
+bool first_supported(const Shape& s) {
+    return s.bf16 && (s.dk == 16 || s.dk == 32) && (s.dv == 16 || s.dv == 32 || s.dv == 64) &&
+           (s.C == 32 || s.C == 64 || s.C == 128);
+}
+
+int first_record_floats(int dk, int dv) { return (dk / 16) * (dv / 16 + 1) * 256; }
+
+hipError_t launch_seg_state1(const Shape& s, const void* k, const void* v, float* rec, int G,
+                             int NSEG, hipStream_t st) {
+    return dispatch1(s, nullptr, k, v, rec, nullptr, nullptr, 1, G, NSEG, true, st);
+}
+
+hipError_t launch_fwd1(const Shape& s, const void* q, const void* k, const void* v,
+                       const float* prefix, float* final_rec, void* o, int causal, int G,
+                       int NSEG, hipStream_t st) {
+    return dispatch1(s, q, k, v, final_rec, prefix, o, causal, G, NSEG, false, st);
+}
+
+hipError_t launch_record_from_packed1(float* rec, const float* S, const float* z, int dk, int dv,
+                                      int nrec, hipStream_t st) {
+    const int REC = first_record_floats(dk, dv);
+    record_from_packed1<<<conv_blocks((size_t)REC * nrec), 256, 0, st>>>(rec, S, z, dk, dv, REC, nrec);
+    return hipGetLastError();
+}
+
+hipError_t launch_record_to_packed1(const float* rec, float* S, float* z, int dk, int dv, int nrec,
+                                    hipStream_t st) {
+    const int REC = first_record_floats(dk, dv);
+    record_to_packed1<<<conv_blocks((size_t)REC * nrec), 256, 0, st>>>(rec, S, z, dk, dv, REC, nrec);
+    return hipGetLastError();
+}
+
+}  // namespace kata

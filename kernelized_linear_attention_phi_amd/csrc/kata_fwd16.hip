@@ -301,8 +301,9 @@ __device__ __forceinline__ void store_staged_rows(const char* ostage, bf16_t* oc
 // wavefront 0's one chunk later, as whole rows.
 template <int W, int DV, int C, bool CAUSAL>
 __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const bf16_t* v,
-                                         const float* prefix, bf16_t* o, char* lds, int T,
-                                         int NC, int G, int NSEG, const Lane& L) {
+                                         const float* prefix, float* final_rec, bf16_t* o,
+                                         char* lds, int T, int NC, int G, int NSEG,
+                                         const Lane& L) {
     using F = Cfg<DV, C>;
     constexpr int l8 = lo8<W, F::NTV>(), h8 = hi8<W, F::NTV>();
     const int seg = blockIdx.x;
@@ -479,6 +480,9 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         const int cl = P.c1 - 1;
         store_staged_rows<DV, C>(ostage, o + (bh * T + (size_t)cl * C) * DV, min(C, T - cl * C), L);
     }
+    // running state after the segment's last chunk (one segment per head: the
+    // final state), when asked for
+    if (CAUSAL && final_rec) record_store<W, W == 1, DV, C>(final_rec + bh * (size_t)F::REC, st, L);
 }
 
 // ---- kernels -------------------------------------------------------------------
@@ -498,12 +502,13 @@ template <int DV, int C, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kata_fwd16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bf16_t* __restrict__ v, const float* __restrict__ prefix,
-                bf16_t* __restrict__ o, int T, int NC, int G, int NSEG) {
+                float* __restrict__ final_rec, bf16_t* __restrict__ o, int T, int NC, int G,
+                int NSEG) {
     using F = Cfg<DV, C>;
     __shared__ __attribute__((aligned(16))) char lds[F::NBUF * F::BUF + F::XB];
     const Lane L;
-    if (L.w == 0) fwd_body<0, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L);
-    else fwd_body<1, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L);
+    if (L.w == 0) fwd_body<0, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC, G, NSEG, L);
+    else fwd_body<1, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC, G, NSEG, L);
 }
 
 template <int DV, int C>
@@ -516,12 +521,12 @@ hipError_t launch_dv_c(const Shape& s, const void* q, const void* k, const void*
                                                            s.T, s.NC, G, NSEG);
     } else if (causal) {
         kata_fwd16<DV, C, true><<<grid, 64 * NW, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
-                                                           (const bf16_t*)v, prefix, (bf16_t*)o,
-                                                           s.T, s.NC, G, NSEG);
+                                                           (const bf16_t*)v, prefix, rec,
+                                                           (bf16_t*)o, s.T, s.NC, G, NSEG);
     } else {
         kata_fwd16<DV, C, false><<<grid, 64 * NW, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
-                                                            (const bf16_t*)v, prefix, (bf16_t*)o,
-                                                            s.T, s.NC, G, NSEG);
+                                                            (const bf16_t*)v, prefix, rec,
+                                                            (bf16_t*)o, s.T, s.NC, G, NSEG);
     }
     return hipGetLastError();
 }
@@ -563,9 +568,9 @@ hipError_t launch_seg_state16(const Shape& s, const void* k, const void* v, floa
 }
 
 hipError_t launch_fwd16(const Shape& s, const void* q, const void* k, const void* v,
-                        const float* prefix, void* o, int causal, int G, int NSEG,
-                        hipStream_t st) {
-    return dispatch(s, q, k, v, nullptr, prefix, o, causal, G, NSEG, false, st);
+                        const float* prefix, float* final_rec, void* o, int causal, int G,
+                        int NSEG, hipStream_t st) {
+    return dispatch(s, q, k, v, final_rec, prefix, o, causal, G, NSEG, false, st);
 }
 
 // ---- record <-> packed state conversion ------------------------------------

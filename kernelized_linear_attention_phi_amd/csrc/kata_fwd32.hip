@@ -356,8 +356,9 @@ __device__ __forceinline__ void seg_state_body32(const bf16_t* k, const bf16_t* 
 
 template <int W, int DV, int C, bool CAUSAL>
 __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, const bf16_t* v,
-                                           const float* prefix, bf16_t* o, char* lds, int T,
-                                           int NC, int G, int NSEG, const Lane& L) {
+                                           const float* prefix, float* final_rec, bf16_t* o,
+                                           char* lds, int T, int NC, int G, int NSEG,
+                                           const Lane& L) {
     using F = Cfg32<DV, C>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
@@ -511,6 +512,9 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
         }
         compiler_fence();
     }
+    // running state after the segment's last chunk (one segment per head: the
+    // final state), when asked for
+    if (CAUSAL && final_rec) record_store32<W, DV, C>(final_rec + bh * (size_t)F::REC, st, L);
 }
 
 // Body dispatch by wavefront index (compile-time roles).
@@ -539,12 +543,14 @@ template <int DV, int C, bool CAUSAL>
 __global__ __launch_bounds__(kThreads32<C>, kWavesPerSimd32<C>)
 void kata_fwd32(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bf16_t* __restrict__ v, const float* __restrict__ prefix,
-                bf16_t* __restrict__ o, int T, int NC, int G, int NSEG) {
+                float* __restrict__ final_rec, bf16_t* __restrict__ o, int T, int NC, int G,
+                int NSEG) {
     using F = Cfg32<DV, C>;
     __shared__ __attribute__((aligned(16))) char lds[F::LDS_FWD];
     const Lane L;
     by_wave<DV, C>(L.w, [&](auto wc) {
-        fwd_body32<decltype(wc)::value, DV, C, CAUSAL>(q, k, v, prefix, o, lds, T, NC, G, NSEG, L);
+        fwd_body32<decltype(wc)::value, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC,
+                                                       G, NSEG, L);
     });
 }
 
@@ -559,12 +565,12 @@ hipError_t launch_dv_c32(const Shape& s, const void* q, const void* k, const voi
                                                            s.T, s.NC, G, NSEG);
     } else if (causal) {
         kata_fwd32<DV, C, true><<<grid, threads, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
-                                                           (const bf16_t*)v, prefix, (bf16_t*)o,
-                                                           s.T, s.NC, G, NSEG);
+                                                           (const bf16_t*)v, prefix, rec,
+                                                           (bf16_t*)o, s.T, s.NC, G, NSEG);
     } else {
         kata_fwd32<DV, C, false><<<grid, threads, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
-                                                            (const bf16_t*)v, prefix, (bf16_t*)o,
-                                                            s.T, s.NC, G, NSEG);
+                                                            (const bf16_t*)v, prefix, rec,
+                                                            (bf16_t*)o, s.T, s.NC, G, NSEG);
     }
     return hipGetLastError();
 }
@@ -669,9 +675,9 @@ hipError_t launch_seg_state32(const Shape& s, const void* k, const void* v, floa
 }
 
 hipError_t launch_fwd32(const Shape& s, const void* q, const void* k, const void* v,
-                        const float* prefix, void* o, int causal, int G, int NSEG,
-                        hipStream_t st) {
-    return dispatch32(s, q, k, v, nullptr, prefix, o, causal, G, NSEG, false, st);
+                        const float* prefix, float* final_rec, void* o, int causal, int G,
+                        int NSEG, hipStream_t st) {
+    return dispatch32(s, q, k, v, final_rec, prefix, o, causal, G, NSEG, false, st);
 }
 
 hipError_t launch_record_from_packed32(float* rec, const float* S, const float* z, int dv,

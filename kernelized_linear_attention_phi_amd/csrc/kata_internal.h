@@ -49,9 +49,11 @@ int mfma16_record_floats(int dv);
 hipError_t launch_seg_state16(const Shape& s, const void* k, const void* v, float* rec, int G,
                               int NSEG, hipStream_t st);
 // causal: prefix [BH, NSEG, REC] exclusive segment prefixes; else prefix [BH, REC] totals
+// final_rec (NULL or [BH, REC]): causal only, the running state after each
+// head's last segment (the final state when NSEG == 1)
 hipError_t launch_fwd16(const Shape& s, const void* q, const void* k, const void* v,
-                        const float* prefix, void* o, int causal, int G, int NSEG,
-                        hipStream_t st);
+                        const float* prefix, float* final_rec, void* o, int causal, int G,
+                        int NSEG, hipStream_t st);
 hipError_t launch_record_from_packed16(float* rec, const float* S, const float* z, int dv,
                                        int nrec, hipStream_t st);
 hipError_t launch_record_to_packed16(const float* rec, float* S, float* z, int dv, int nrec,
@@ -63,13 +65,28 @@ bool mfma32_supported(const Shape& s);
 int mfma32_record_floats(int dv);
 hipError_t launch_seg_state32(const Shape& s, const void* k, const void* v, float* rec, int G,
                               int NSEG, hipStream_t st);
+// final_rec (NULL or [BH, REC]): causal only, the running state after each
+// head's last segment (the final state when NSEG == 1)
 hipError_t launch_fwd32(const Shape& s, const void* q, const void* k, const void* v,
-                        const float* prefix, void* o, int causal, int G, int NSEG,
-                        hipStream_t st);
+                        const float* prefix, float* final_rec, void* o, int causal, int G,
+                        int NSEG, hipStream_t st);
 hipError_t launch_record_from_packed32(float* rec, const float* S, const float* z, int dv,
                                        int nrec, hipStream_t st);
 hipError_t launch_record_to_packed32(const float* rec, float* S, float* z, int dv, int nrec,
                                      hipStream_t st);
+
+// ---- bf16 matrix-core path, first-order (identity) feature ----
+bool first_supported(const Shape& s);
+int first_record_floats(int dk, int dv);
+hipError_t launch_seg_state1(const Shape& s, const void* k, const void* v, float* rec, int G,
+                             int NSEG, hipStream_t st);
+hipError_t launch_fwd1(const Shape& s, const void* q, const void* k, const void* v,
+                       const float* prefix, float* final_rec, void* o, int causal, int G,
+                       int NSEG, hipStream_t st);
+hipError_t launch_record_from_packed1(float* rec, const float* S, const float* z, int dk, int dv,
+                                      int nrec, hipStream_t st);
+hipError_t launch_record_to_packed1(const float* rec, float* S, float* z, int dk, int dv, int nrec,
+                                    hipStream_t st);
 
 // ---- quadratic (flash-style) forward, bf16 ----
 bool flash_supported(const Shape& s);

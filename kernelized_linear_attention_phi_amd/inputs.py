@@ -14,6 +14,10 @@ Workloads (shapes and value distributions):
   recall16k  B8 H4 T16384  d_k16 d_v64 bf16 C64   recall-shaped stream (below)
   decode     1024 steps on 512 sequences x 4 heads continuing recall16k
 
+For the first-order (identity) feature, orthant_qkv draws the same shapes with
+q, k on the nonnegative orthant (unit rows of |N(0, I)|), the cone on which that
+feature's weights q.k are nonnegative.
+
 The recall-shaped stream stands in for the associative-recall and
 repeated-key-overwrite workloads the pages evaluate on; no item of any public
 suite is used. Per (b, h) stream: a codebook of 2048 unit Gaussian keys; at each
@@ -29,7 +33,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "round_to", "gaussian_qkv", "RecallStream",
+__all__ = ["Workload", "WORKLOADS", "round_to", "gaussian_qkv", "orthant_qkv", "RecallStream",
            "recall_stream", "decode_continuation"]
 
 
@@ -83,6 +87,15 @@ def gaussian_qkv(B, H, T, dk, dv, seed, dtype="bf16"):
     rng = np.random.Generator(np.random.PCG64(seed))
     q = _unit_rows(rng, (B, H, T, dk))
     k = _unit_rows(rng, (B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv))
+    return round_to(q, dtype), round_to(k, dtype), round_to(v, dtype)
+
+
+def orthant_qkv(B, H, T, dk, dv, seed, dtype="bf16"):
+    """q, k: rows of |N(0, I)| normalised to unit L2 norm (nonnegative); v ~ N(0, 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = np.abs(_unit_rows(rng, (B, H, T, dk)))
+    k = np.abs(_unit_rows(rng, (B, H, T, dk)))
     v = rng.standard_normal((B, H, T, dv))
     return round_to(q, dtype), round_to(k, dtype), round_to(v, dtype)
 

@@ -69,6 +69,49 @@ def test_fwd_rejects_before_launch(L):
     assert fwd(L, B=0, q=None, o=None, ws=None, ws_bytes=0) == OK
 
 
+PSD, IDENTITY = 0, 1
+SCAN, SEQUENTIAL = 0, 1
+
+
+def fwd_ex(L, feature=IDENTITY, prefix=SCAN, B=1, H=1, T=64, dk=16, dv=64, C=64, causal=1,
+           dtype=BF16, q=FAKE, ws=FAKE, ws_bytes=1 << 40, o=FAKE, S0=None, z0=None):
+    return L.kata_chunked_fwd_ex(q, FAKE, FAKE, o, B, H, T, dk, dv, C, causal, dtype, feature,
+                                 prefix, S0, z0, None, None, ws, ws_bytes, None)
+
+
+def test_fwd_ex_rejects_before_launch(L):
+    assert fwd_ex(L, feature=2) == EINVAL
+    assert fwd_ex(L, prefix=5) == EINVAL
+    assert fwd_ex(L, dtype=F32) == EUNSUPPORTED                   # identity feature: bf16 only
+    assert fwd_ex(L, C=16) == EUNSUPPORTED                        # identity feature: C >= 32
+    assert fwd_ex(L, dk=24) == EUNSUPPORTED
+    assert fwd_ex(L, feature=PSD, prefix=SEQUENTIAL, dtype=F32) == EUNSUPPORTED
+    assert fwd_ex(L, feature=PSD, prefix=SEQUENTIAL, C=128) == EUNSUPPORTED   # d_k=16: C 32 or 64
+    assert fwd_ex(L, prefix=SEQUENTIAL, ws_bytes=16) == EWORKSPACE
+    assert fwd_ex(L, q=MISALIGNED) == EINVAL
+    assert fwd_ex(L, S0=FAKE) == EINVAL
+    assert fwd_ex(L, T=0, q=None, o=None, ws=None, ws_bytes=0) == OK           # empty: no launch
+    assert fwd_ex(L, feature=PSD, prefix=SEQUENTIAL, B=0, q=None, o=None, ws=None, ws_bytes=0) == OK
+
+
+def test_feature_dim_and_ex_workspace(L):
+    assert L.kata_feature_dim(16, PSD) == 136 and L.kata_feature_dim(32, PSD) == 528
+    assert L.kata_feature_dim(16, IDENTITY) == 16 and L.kata_feature_dim(32, IDENTITY) == 32
+    assert L.kata_feature_dim(16, 7) == -1 and L.kata_feature_dim(-1, PSD) == -1
+    ws = L.kata_chunked_fwd_ex_workspace
+    # PSD with the scan: the same plan as kata_chunked_fwd
+    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, PSD, SCAN) == \
+        L.kata_chunked_fwd_workspace(1, 8, 131072, 16, 64, 64, BF16, 1)
+    # sequential: one record per head for the segment, the initial and the final state
+    rec16 = 9 * 4 * 256 + 256            # d_k = 16, d_v = 64: nine feature tiles + Gram tile
+    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, PSD, SEQUENTIAL) == 3 * 8 * rec16 * 4
+    rec1 = 1 * 5 * 256                   # identity, d_k = 16, d_v = 64: four value tiles + z
+    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, IDENTITY, SEQUENTIAL) == 3 * 8 * rec1 * 4
+    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, IDENTITY, SCAN) > 3 * 8 * rec1 * 4
+    assert ws(1, 1, 64, 16, 64, 64, F32, 1, IDENTITY, SCAN) == 0
+    assert ws(1, 1, 64, 16, 64, 64, BF16, 1, 9, SCAN) == 0
+
+
 def test_profiled_needs_five_events(L):
     prof = L.kata_chunked_fwd_profiled
     evs = (ctypes.c_void_p * 5)(*([FAKE] * 5))
