@@ -153,6 +153,38 @@ def decode_bench(kata, torch, steps=1024, n_seq=512, heads=4, dk=16, dv=64, reps
     return ms_step, bytes_step / (ms_step * 1e-3) / 1e9, bytes_step
 
 
+def scan_vs_sequential(kata, torch, gen, names, steps, warmup):
+    """The inter-chunk prefix by the associative scan (segments in parallel) and
+    by the sequential walk (one workgroup per head, depth N_C), for the PSD lift
+    and for the first-order identity feature (orthant inputs), on the same
+    shapes: ms per forward, tokens/s and the scan's speedup."""
+    out = {}
+    speedups = []
+    to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+    for name in names:
+        w = gen.WORKLOADS[name]
+        for feature, draw in (("psd", gen.gaussian_qkv), ("identity", gen.orthant_qkv)):
+            q, k, v = (to(a) for a in draw(w.B, w.H, w.T, w.dk, w.dv, w.seed, "bf16"))
+            o = torch.empty_like(v)
+            row = {}
+            for prefix in ("scan", "sequential"):
+                nbytes = kata.chunked_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1, True,
+                                                    feature, prefix)
+                ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+                n = steps if prefix == "scan" else max(1, min(steps, 3))
+                ms = time_calls(torch, lambda: kata.chunked_fwd_into(
+                    q, k, v, o, w.chunk, True, ws, feature=feature, prefix=prefix), n,
+                    min(warmup, 1) if prefix == "sequential" else warmup)
+                row[prefix] = {"ms": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3)}
+                del ws
+            row["scan_speedup"] = row["sequential"]["ms"] / row["scan"]["ms"]
+            speedups.append(row["scan_speedup"])
+            out[f"{name}/{feature}"] = row
+            del q, k, v, o
+    out["geomean_scan_speedup"] = float(np.exp(np.mean(np.log(speedups))))
+    return out
+
+
 def cpu_baseline(w, q, k, v, budget_s):
     """The float64 brute-force oracle on a bounded sample of query rows of the
     same workload (head 0, uniformly drawn positions), scaled to tokens/s."""
@@ -258,6 +290,8 @@ def main():
         del dev3
         result["parts"]["fwd4k"] = quadratic_vs_chunked(kata, torch, gen, "fwd4k", args.steps,
                                                         args.warmup)
+        result["parts"]["scan_vs_sequential"] = scan_vs_sequential(
+            kata, torch, gen, ("fwd4k", "fwd32k", "fwd131k"), min(args.steps, 10), args.warmup)
         dms, dgbs, dbytes = decode_bench(kata, torch)
         result["parts"]["decode"] = {"ms_per_step": dms, "alg_GBps": dgbs,
                                      "hbm_frac": dgbs / PEAK_HBM_GBS, "bytes_per_step": dbytes,

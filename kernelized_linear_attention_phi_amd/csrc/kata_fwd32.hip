@@ -3,9 +3,10 @@
 // Method (KATA explainers, gist.science, technical summary 2.3; the paper's
 // abstract): the sequence is cut into chunks of C positions; each output is the
 // masked intra-chunk term plus phi(Q_c) times the prefix of chunk states; the
-// prefix is propagated by an associative scan. One workgroup of four wavefronts
-// owns a segment of G consecutive chunks of one (batch, head) and carries the
-// running state S = sum phi(k) v^T in registers across the segment:
+// prefix is propagated by an associative scan. One workgroup (eight wavefronts
+// at C = 128, four at C = 64) owns a segment of G consecutive chunks of one
+// (batch, head) and carries the running state S = sum phi(k) v^T in registers
+// across the segment:
 //   kata_seg_state32 : segment totals         (phi(K)^T V on MFMA)
 //   (scan kernel)    : exclusive prefix over segments of each head
 //   kata_fwd32       : per chunk, inter (phi(Q).S) and intra (QK^T -> square ->
@@ -22,12 +23,14 @@
 // one, and no row is padding. The state holds plain sums of k_a k_b v; the
 // factor 2 of an off-diagonal pair sits on the query side.
 //
-// Work split. Wavefront w owns feature tiles 8w..8w+7 for every value tile, the
-// value tile nt = w of tile 32, and one Gram tile (below): it lifts keys only
-// for those and updates only those rows of S. Once per chunk each wavefront
-// writes its part of S (as bf16 matrix-core operands) to LDS; each wavefront
-// then finishes its own query tiles {w, TT-1-w} against the whole state, so the
-// causal intra-chunk work is balanced and no partial sums are exchanged.
+// Work split (NW wavefronts, TPW = 32 / NW). Wavefront w owns feature tiles
+// TPW*w .. TPW*w + TPW - 1 for every value tile, one value tile of tile 32 (the
+// last four wavefronts with eight, wavefront nt with four) and, for w < 4, one
+// Gram tile (below): it lifts keys only for those and updates only those rows
+// of S. Once per chunk each wavefront writes its part of S (as bf16
+// matrix-core operands) to LDS; each wavefront then finishes its own query
+// tiles against the whole state (tile w, and tile TT-1-w when it owns two), so
+// the causal intra-chunk work is balanced and no partial sums are exchanged.
 //
 // Denominators. Inside a chunk, sum_j A_tj comes from the A.V MFMAs through a
 // "ones" value tile. Across chunks, z = sum phi(k) is kept as the Gram matrix
