@@ -5,3 +5,4 @@ leg of the benchmark may import it; the library path never does.
 """
 from .kata_oracle import *  # noqa: F401,F403
 from .first_order_oracle import *  # noqa: F401,F403
+from .decay_oracle import *  # noqa: F401,F403
