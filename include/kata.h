@@ -161,6 +161,41 @@ kata_status_t kata_chunked_fwd_ex(const void* q, const void* k, const void* v, v
                                   float* S_out, float* z_out,
                                   void* workspace, size_t ws_bytes, void* stream);
 
+/* Decay-gated chunked forward (causal). The pages name decay gates among the
+ * mechanisms whose interaction with the feature geometry the paper studies (the
+ * abstract) and describe gated linear RNNs with learned forget gates (explainer
+ * section 1), but print no formula; the reading implemented is a scalar forget
+ * gate per token and head that scales the whole state before the token is added:
+ *     S_t = exp(g_t) S_{t-1} + phi(k_t) v_t^T,  z_t = exp(g_t) z_{t-1} + phi(k_t),
+ *     o_t = phi(q_t).S_t / phi(q_t).z_t   (0 where the denominator is 0),
+ * i.e. weights (q_t.k_j)^2 exp(g_{j+1} + ... + g_t), still nonnegative.
+ *   log_decay [B,H,T] (fp32, device) - g, every value <= 0 (finite, or very
+ *     negative for a reset).
+ *   prefix - KATA_PREFIX_SCAN (segment states, then an associative scan under
+ *     the non-commutative operator (a1,S1) o (a2,S2) = (a1 a2, a2 S1 + S2)) or
+ *     KATA_PREFIX_SEQUENTIAL (one workgroup per head walks every chunk).
+ * Every other argument as for kata_chunked_fwd (S0, z0 stand for earlier tokens
+ * and decay with the sequence; S_out, z_out are the decayed final state).
+ * Supported: dtype KATA_BF16, d_k = 16, d_v in {16, 32, 64}, chunk in {32, 64};
+ * T a multiple of 4 when B*H > 1 (the log-decays of a head are copied 16 bytes at
+ * a time); else KATA_EUNSUPPORTED. */
+size_t kata_chunked_fwd_decay_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                        kata_dtype_t dtype, kata_prefix_t prefix);
+kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v,
+                                     const float* log_decay, void* o,
+                                     int B, int H, int T, int d_k, int d_v, int chunk,
+                                     kata_dtype_t dtype, kata_prefix_t prefix,
+                                     const float* S0, const float* z0,
+                                     float* S_out, float* z_out,
+                                     void* workspace, size_t ws_bytes, void* stream);
+
+/* kata_decode_step with the decay gate above: log_decay [N] (fp32, device), and
+ * S = exp(g) S + phi(k) v^T, z = exp(g) z + phi(k) before the read. Same shapes,
+ * dtypes and errors as kata_decode_step (log_decay NULL = KATA_EINVAL). */
+kata_status_t kata_decode_step_decay(const void* q, const void* k, const void* v,
+                                     const float* log_decay, float* S, float* z, void* o,
+                                     int N, int d_k, int d_v, kata_dtype_t dtype, void* stream);
+
 /* Bytes of workspace kata_scan_states needs (currently always 0). */
 size_t kata_scan_states_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                   kata_dtype_t dtype);

@@ -7,10 +7,13 @@
     o2 = kata.flash_fwd(q, k, v)                            # quadratic form (bf16)
     o3 = kata.chunked_fwd(q, k, v, prefix="sequential")     # chunk-by-chunk prefix
     o4 = kata.chunked_fwd(q, k, v, feature="identity")      # first-order feature
+    o5 = kata.chunked_fwd_decay(q, k, v, log_decay)         # decay-gated (bf16, d_k 16)
 
 The shared library is loaded on first use; calls raise if it is missing.
 """
 from ._binding import (KataError, chunked_fwd, chunked_fwd_into, chunked_fwd_workspace,  # noqa: F401
-                       decode_step, feature_dim, flash_fwd, lib, phi_dim, scan_states, LIB_PATH)
+                       chunked_fwd_decay, chunked_fwd_decay_into, chunked_fwd_decay_workspace,
+                       decode_step, decode_step_decay, feature_dim, flash_fwd, lib, phi_dim,
+                       scan_states, LIB_PATH)
 
 __version__ = "0.1.0"

@@ -12,7 +12,9 @@ import os
 import torch
 
 __all__ = ["KataError", "lib", "chunked_fwd", "chunked_fwd_into", "chunked_fwd_workspace",
-           "scan_states", "flash_fwd", "decode_step", "phi_dim", "feature_dim", "LIB_PATH"]
+           "scan_states", "flash_fwd", "decode_step", "phi_dim", "feature_dim",
+           "chunked_fwd_decay", "chunked_fwd_decay_into", "chunked_fwd_decay_workspace",
+           "decode_step_decay", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkata.so")
 
@@ -58,6 +60,13 @@ def lib() -> ctypes.CDLL:
         L.kata_chunked_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i,
                                           vp, vp, vp, vp, vp, sz, vp]
         L.kata_chunked_fwd_ex.restype = i
+        L.kata_chunked_fwd_decay_workspace.argtypes = [i, i, i, i, i, i, i, i]
+        L.kata_chunked_fwd_decay_workspace.restype = sz
+        L.kata_chunked_fwd_decay.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                             vp, vp, vp, vp, vp, sz, vp]
+        L.kata_chunked_fwd_decay.restype = i
+        L.kata_decode_step_decay.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+        L.kata_decode_step_decay.restype = i
         L.kata_scan_states_workspace.argtypes = [i, i, i, i, i, i, i]
         L.kata_scan_states_workspace.restype = sz
         L.kata_scan_states.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -255,4 +264,66 @@ def decode_step(q, k, v, S, z, out=None):
     st = lib().kata_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(o), N, dk, dv,
                                 _dtype_code(q), _stream())
     _raise(st, "kata_decode_step")
+    return o
+
+
+# ---- decay gate ------------------------------------------------------------------
+
+def chunked_fwd_decay_workspace(B, H, T, dk, dv, chunk, dtype_code, prefix="scan") -> int:
+    return lib().kata_chunked_fwd_decay_workspace(B, H, T, dk, dv, chunk, dtype_code,
+                                                  _modes("psd", prefix)[1])
+
+
+def chunked_fwd_decay_into(q, k, v, log_decay, o, chunk, workspace, S0=None, z0=None, S_out=None,
+                           z_out=None, prefix="scan"):
+    """Raw decay-gated call (kata_chunked_fwd_decay); every buffer preallocated."""
+    _check_dev(log_decay)
+    if log_decay.dtype != torch.float32:
+        raise TypeError("log_decay is float32 [B,H,T]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().kata_chunked_fwd_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(o), B, H, T,
+                                      dk, dv, chunk, _dtype_code(q), _modes("psd", prefix)[1],
+                                      _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out),
+                                      _ptr(workspace), ws_bytes, _stream())
+    _raise(st, "kata_chunked_fwd_decay")
+
+
+def chunked_fwd_decay(q, k, v, log_decay, chunk=64, initial_state=None, return_state=False,
+                      prefix="scan"):
+    """Decay-gated causal KATA forward: log_decay [B,H,T] fp32 (<= 0) is the
+    per-token log forget gate (S_t = exp(g_t) S_{t-1} + phi(k_t) v_t^T, z
+    likewise). bf16, d_k = 16; initial_state / return_state as chunked_fwd."""
+    _check_dev(q, k, v)
+    if q.dim() != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("expected q, k [B,H,T,d_k] and v [B,H,T,d_v]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if tuple(log_decay.shape) != (B, H, T):
+        raise ValueError("log_decay must be [B,H,T]")
+    D = phi_dim(dk)
+    S0 = z0 = S_out = z_out = None
+    if initial_state is not None:
+        S0, z0 = initial_state
+    if return_state:
+        S_out = torch.empty((B, H, D, dv), dtype=torch.float32, device=q.device)
+        z_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    o = torch.empty_like(v)
+    nbytes = chunked_fwd_decay_workspace(B, H, T, dk, dv, chunk, _dtype_code(q), prefix)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if nbytes else None
+    chunked_fwd_decay_into(q, k, v, log_decay.contiguous(), o, chunk, ws, S0, z0, S_out, z_out,
+                           prefix=prefix)
+    return (o, (S_out, z_out)) if return_state else o
+
+
+def decode_step_decay(q, k, v, log_decay, S, z, out=None):
+    """decode_step with a per-row log-decay [N] (fp32): S = exp(g) S + phi(k) v^T."""
+    _check_dev(q, k, v, log_decay, S, z)
+    N, dk = q.shape
+    dv = v.shape[-1]
+    o = torch.empty_like(v) if out is None else out
+    st = lib().kata_decode_step_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(S), _ptr(z),
+                                      _ptr(o), N, dk, dv, _dtype_code(q), _stream())
+    _raise(st, "kata_decode_step_decay")
     return o

@@ -355,6 +355,104 @@ kata_status_t kata_flash_fwd(const void* q, const void* k, const void* v, void* 
     return hip_status(kata::launch_flash_fwd(s, q, k, v, o, causal, static_cast<hipStream_t>(stream)));
 }
 
+// ---- decay gate ----------------------------------------------------------------
+
+static bool decay_plan(const Shape& s, kata_prefix_t prefix, FwdPlan* p, size_t* dec_off) {
+    *p = plan_fwd(s, 1, KATA_FEATURE_PSD, prefix);
+    if (!p->ok || (p->mfma != 16 && (size_t)s.B * s.H * s.NC != 0)) return false;
+    *dec_off = p->bytes;
+    if (p->mfma == 16 && !p->seq) p->bytes += align256((size_t)s.B * s.H * p->NSEG * sizeof(float));
+    return true;
+}
+
+size_t kata_chunked_fwd_decay_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                        kata_dtype_t dtype, kata_prefix_t prefix) {
+    Shape s;
+    FwdPlan p;
+    size_t dec_off;
+    if (prefix != KATA_PREFIX_SCAN && prefix != KATA_PREFIX_SEQUENTIAL) return 0;
+    if (make_shape(B, H, T, d_k, d_v, chunk, dtype, &s) != KATA_OK) return 0;
+    if (!decay_plan(s, prefix, &p, &dec_off)) return 0;
+    return p.bytes;
+}
+
+kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v,
+                                     const float* log_decay, void* o, int B, int H, int T,
+                                     int d_k, int d_v, int chunk, kata_dtype_t dtype,
+                                     kata_prefix_t prefix, const float* S0, const float* z0,
+                                     float* S_out, float* z_out, void* workspace, size_t ws_bytes,
+                                     void* stream) {
+    if (prefix != KATA_PREFIX_SCAN && prefix != KATA_PREFIX_SEQUENTIAL) return KATA_EINVAL;
+    Shape s;
+    kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s);
+    if (st != KATA_OK) return st;
+    if ((S0 == nullptr) != (z0 == nullptr)) return KATA_EINVAL;
+    if ((S_out == nullptr) != (z_out == nullptr)) return KATA_EINVAL;
+    const size_t BH = (size_t)B * H;
+    const bool empty = BH == 0 || T == 0;
+    if (!empty && (!q || !k || !v || !o || !log_decay)) return KATA_EINVAL;
+    for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)o,
+                          (const void*)log_decay, (const void*)S0, (const void*)z0,
+                          (const void*)S_out, (const void*)z_out, (const void*)workspace})
+        if (p && !aligned16(p)) return KATA_EINVAL;
+    // the per-head log-decay rows are read 16 bytes at a time from T-aligned offsets
+    if (!empty && T % 4 != 0 && H * B > 1) return KATA_EUNSUPPORTED;
+    FwdPlan plan;
+    size_t dec_off;
+    if (!decay_plan(s, prefix, &plan, &dec_off)) return KATA_EUNSUPPORTED;
+    if (ws_bytes < plan.bytes || (plan.bytes && !workspace)) return KATA_EWORKSPACE;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const size_t nS = (size_t)s.D * s.dv, nz = s.D;
+    if (empty) {
+        hipError_t e = hipSuccess;
+        if (S_out) {
+            e = kata::launch_copy_or_zero(S_out, S0, BH * nS, hs);
+            if (e == hipSuccess) e = kata::launch_copy_or_zero(z_out, z0, BH * nz, hs);
+        }
+        return hip_status(e);
+    }
+    char* ws = static_cast<char*>(workspace);
+    float* rec = reinterpret_cast<float*>(ws + plan.S_off);
+    float* init = reinterpret_cast<float*>(ws + plan.init_off);
+    float* total = reinterpret_cast<float*>(ws + plan.total_off);
+    const int nrec = (int)BH;
+    hipError_t e = hipSuccess;
+    if (S0) e = kata::launch_record_from_packed16(init, S0, z0, s.dv, nrec, hs);
+    if (plan.seq) {
+        if (!S0 && e == hipSuccess) e = kata::launch_copy_or_zero(init, nullptr, BH * plan.REC, hs);
+        if (e == hipSuccess)
+            e = kata::launch_fwd16_decay(s, q, k, v, log_decay, init, S_out ? total : nullptr, o,
+                                         plan.G, plan.NSEG, hs);
+    } else {
+        float* segdec = reinterpret_cast<float*>(ws + dec_off);
+        if (e == hipSuccess)
+            e = kata::launch_seg_state16_decay(s, k, v, log_decay, rec, segdec, plan.G, plan.NSEG, hs);
+        if (e == hipSuccess)
+            e = kata::launch_scan_records_decay(rec, segdec, nrec, plan.NSEG, plan.REC,
+                                                S0 ? init : nullptr, total, nullptr, hs);
+        if (e == hipSuccess)
+            e = kata::launch_fwd16_decay(s, q, k, v, log_decay, rec, nullptr, o, plan.G, plan.NSEG, hs);
+    }
+    if (S_out && e == hipSuccess)
+        e = kata::launch_record_to_packed16(total, S_out, z_out, s.dv, nrec, hs);
+    return hip_status(e);
+}
+
+kata_status_t kata_decode_step_decay(const void* q, const void* k, const void* v,
+                                     const float* log_decay, float* S, float* z, void* o, int N,
+                                     int d_k, int d_v, kata_dtype_t dtype, void* stream) {
+    if (N < 0 || d_k < 0 || d_v < 0) return KATA_EINVAL;
+    if (dtype != KATA_F32 && dtype != KATA_BF16) return KATA_EINVAL;
+    if (!supported_dk(d_k) || !supported_dv(d_v)) return KATA_EUNSUPPORTED;
+    if (N == 0) return KATA_OK;
+    if (!q || !k || !v || !S || !z || !o || !log_decay) return KATA_EINVAL;
+    for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)S,
+                          (const void*)z, (const void*)o, (const void*)log_decay})
+        if (!aligned16(p)) return KATA_EINVAL;
+    return hip_status(kata::launch_decode(q, k, v, log_decay, S, z, o, N, d_k, d_v,
+                                          dtype == KATA_BF16, static_cast<hipStream_t>(stream)));
+}
+
 kata_status_t kata_decode_step(const void* q, const void* k, const void* v, float* S, float* z,
                                void* o, int N, int d_k, int d_v, kata_dtype_t dtype,
                                void* stream) {
@@ -366,8 +464,8 @@ kata_status_t kata_decode_step(const void* q, const void* k, const void* v, floa
     for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)S,
                           (const void*)z, (const void*)o})
         if (!aligned16(p)) return KATA_EINVAL;
-    return hip_status(kata::launch_decode(q, k, v, S, z, o, N, d_k, d_v, dtype == KATA_BF16,
-                                          static_cast<hipStream_t>(stream)));
+    return hip_status(kata::launch_decode(q, k, v, nullptr, S, z, o, N, d_k, d_v,
+                                          dtype == KATA_BF16, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

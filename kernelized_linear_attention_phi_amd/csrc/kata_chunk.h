@@ -131,28 +131,36 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(p);
 }
 
-// ---- chunk staging: q | k | v of one chunk, row-major as in HBM -------------
+// ---- chunk staging: q | k | v (| g) of one chunk, row-major as in HBM --------
 // Full chunks are loaded by the first NLOAD wavefronts only (a wavefront that
 // issues no loads never waits for its own stores when it waits for data).
-template <int DK, int DV, int C, int NW, int NLOAD = NW>
+// GATE adds the chunk's C per-token log-decays (fp32) after v; wavefront 0
+// copies them before any other piece.
+template <int DK, int DV, int C, int NW, int NLOAD = NW, bool GATE = false>
 struct ChunkIO {
     static constexpr int QB = C * DK * 2;         // bytes of a q or k chunk
     static constexpr int VB = C * DV * 2;         // bytes of a v chunk
-    static constexpr int BUF = 2 * QB + VB;       // one chunk buffer
+    static constexpr int GB = GATE ? C * 4 : 0;   // bytes of the log-decays
+    static constexpr int BUF = 2 * QB + VB + GB;  // one chunk buffer
     static_assert(QB % 1024 == 0 && VB % 1024 == 0, "chunks are whole 1 KB pieces");
+    static_assert(GB <= 1024, "the log-decays fit one partial piece");
 
     // Full chunk: the 1 KB pieces are split round-robin over the loading
     // wavefronts; piece i goes to wavefront i % NLOAD as a direct-to-LDS load.
     // Lane l fills 16-byte slot l of the piece with the unit the swizzle puts
     // there.
     static __device__ __forceinline__ void stage_async(const bf16_t* q, const bf16_t* k,
-                                                       const bf16_t* v, size_t tok0,
-                                                       uint32_t buf_lds, bool with_q,
-                                                       const Lane& L) {
+                                                       const bf16_t* v, const float* gate,
+                                                       size_t tok0, uint32_t buf_lds,
+                                                       bool with_q, const Lane& L) {
         const char* gq = reinterpret_cast<const char*>(q + tok0 * DK);
         const char* gk = reinterpret_cast<const char*>(k + tok0 * DK);
         const char* gv = reinterpret_cast<const char*>(v + tok0 * DV);
         constexpr int PQ = QB / 1024, PV = VB / 1024;
+        if constexpr (GATE) {
+            if (L.w == 0 && L.lane < GB / 16)
+                dma16(gate + tok0 + 4 * L.lane, buf_lds + 2 * QB + VB);
+        }
         const int first = with_q ? 0 : PQ;
 #pragma unroll
         for (int i = 0; i < 2 * PQ + PV; ++i) {
@@ -166,8 +174,9 @@ struct ChunkIO {
 
     // Ragged chunk (n < C valid positions): bounded loads, zero fill, then LDS.
     static __device__ __forceinline__ void stage_ragged(const bf16_t* q, const bf16_t* k,
-                                                        const bf16_t* v, size_t tok0, int n,
-                                                        char* buf, bool with_q, const Lane& L) {
+                                                        const bf16_t* v, const float* gate,
+                                                        size_t tok0, int n, char* buf,
+                                                        bool with_q, const Lane& L) {
         const u32x4_t zero = {0u, 0u, 0u, 0u};
         const u32x4_t* gq = reinterpret_cast<const u32x4_t*>(q + tok0 * DK);
         const u32x4_t* gk = reinterpret_cast<const u32x4_t*>(k + tok0 * DK);
@@ -185,7 +194,25 @@ struct ChunkIO {
             lk[sl] = ok ? gk[u] : zero;
         }
         for (int u = tid; u < VU; u += nthr) lv[Swz<2 * DV>::slot(u)] = (u / VPR < n) ? gv[u] : zero;
+        if constexpr (GATE) {
+            float* lg = reinterpret_cast<float*>(buf + 2 * QB + VB);
+            for (int t = tid; t < C; t += nthr) lg[t] = t < n ? gate[tok0 + t] : 0.0f;
+        }
         compiler_fence();
+    }
+
+    // Copies wavefront w issues for one full chunk: every piece from `first` on
+    // (its share), plus the log-decays for wavefront 0.
+    static __host__ __device__ constexpr int issued(int w, int first) {
+        int n = GATE && w == 0 ? 1 : 0;
+        for (int i = first; i < 2 * (QB / 1024) + VB / 1024; ++i) n += (i % NLOAD == w);
+        return n;
+    }
+    // Its k and v pieces only (they follow its log-decay and q copies).
+    static __host__ __device__ constexpr int kv_pieces(int w) {
+        int n = 0;
+        for (int i = QB / 1024; i < 2 * (QB / 1024) + VB / 1024; ++i) n += (i % NLOAD == w);
+        return n;
     }
 };
 
@@ -217,13 +244,14 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 // loads and stores may complete out of order, so no partial count is safe),
 // then all meet at a barrier (every part has landed and everyone is done with
 // the buffer chunk c+1 will overwrite), then chunk c+1 is issued.
-template <int DK, int DV, int C, int NW, int NLOAD = NW>
+template <int DK, int DV, int C, int NW, int NLOAD = NW, bool GATE = false>
 struct Pipeline {
-    using IO = ChunkIO<DK, DV, C, NW, NLOAD>;
+    using IO = ChunkIO<DK, DV, C, NW, NLOAD, GATE>;
     char* lds;
     int c0, c1, T;
     size_t tok_base;
     bool with_q;
+    const float* gate = nullptr;   // log-decays [.., T] when GATE
 
     __device__ char* buffer(int c) const { return lds + ((c - c0) & 1) * IO::BUF; }
     __device__ uint32_t buffer_lds(int c) const {
@@ -234,8 +262,8 @@ struct Pipeline {
         if (c >= c1) return;
         const int n = min(C, T - c * C);
         const size_t tok0 = tok_base + (size_t)c * C;
-        if (n == C) IO::stage_async(q, k, v, tok0, buffer_lds(c), with_q, L);
-        else IO::stage_ragged(q, k, v, tok0, n, buffer(c), with_q, L);
+        if (n == C) IO::stage_async(q, k, v, gate, tok0, buffer_lds(c), with_q, L);
+        else IO::stage_ragged(q, k, v, gate, tok0, n, buffer(c), with_q, L);
     }
     __device__ void acquire(const bf16_t* q, const bf16_t* k, const bf16_t* v, int c, const Lane& L) {
         if (L.w < NLOAD) wait_vmcnt<0>();
@@ -249,20 +277,15 @@ struct Pipeline {
     // wavefront lets its k and v copies of chunk c stay in flight), then stages
     // chunk c+1; wait_kv, placed before a later workgroup barrier, waits for
     // the rest of chunk c (everything except the copies of chunk c+1).
-    __device__ static int pieces(int w, int first) {
-        int n = 0;
-        for (int i = first; i < 2 * (IO::QB / 1024) + IO::VB / 1024; ++i) n += (i % NLOAD == w);
-        return n;
-    }
     __device__ bool full(int c) const { return c < c1 && T - c * C >= C; }
     __device__ void acquire_q(const bf16_t* q, const bf16_t* k, const bf16_t* v, int c,
                               const Lane& L) {
-        if (L.w < NLOAD) wait_vmcnt_upto(full(c) ? pieces(L.w, IO::QB / 1024) : 0);
+        if (L.w < NLOAD) wait_vmcnt_upto(full(c) ? IO::kv_pieces(L.w) : 0);
         lds_barrier();
         stage(q, k, v, c + 1, L);
     }
     __device__ void wait_kv(int c, const Lane& L) const {
-        if (L.w < NLOAD) wait_vmcnt_upto(full(c + 1) ? pieces(L.w, with_q ? 0 : IO::QB / 1024) : 0);
+        if (L.w < NLOAD) wait_vmcnt_upto(full(c + 1) ? IO::issued(L.w, with_q ? 0 : IO::QB / 1024) : 0);
     }
 };
 
@@ -273,31 +296,29 @@ struct Pipeline {
 // no more than its copies of the already-staged later chunks are outstanding,
 // then all meet at a barrier and chunk c + NBUF - 1 is issued into the buffer
 // chunk c - 1 used.
-template <int DK, int DV, int C, int NW, int NBUF>
+template <int DK, int DV, int C, int NW, int NBUF, bool GATE = false>
 struct LoadPipeline {
-    using IO = ChunkIO<DK, DV, C, NW, NW>;
+    using IO = ChunkIO<DK, DV, C, NW, NW, GATE>;
     static constexpr int PQ = IO::QB / 1024, PV = IO::VB / 1024;
     char* lds;
     int c0, c1, T;
     size_t tok_base;
+    const float* gate = nullptr;   // log-decays [.., T] when GATE
 
     __device__ char* buffer(int c) const { return lds + ((c - c0) % NBUF) * IO::BUF; }
     __device__ uint32_t buffer_lds(int c) const {
         return lds_address(lds) + ((c - c0) % NBUF) * IO::BUF;
     }
     __device__ bool full(int c) const { return c < c1 && T - c * C >= C; }
-    // direct-to-LDS copies wavefront w issues for one full chunk (k and v pieces)
-    __device__ static int pieces(int w) {
-        int n = 0;
-        for (int i = PQ; i < 2 * PQ + PV; ++i) n += (i % NW == w);
-        return n;
-    }
+    // direct-to-LDS copies wavefront w issues for one full chunk (k and v
+    // pieces, and the log-decays for wavefront 0 when GATE)
+    __device__ static int pieces(int w) { return IO::issued(w, PQ); }
     __device__ void stage(const bf16_t* k, const bf16_t* v, int c, const Lane& L) {
         if (c >= c1) return;
         const int n = min(C, T - c * C);
         const size_t tok0 = tok_base + (size_t)c * C;
-        if (n == C) IO::stage_async(nullptr, k, v, tok0, buffer_lds(c), false, L);
-        else IO::stage_ragged(nullptr, k, v, tok0, n, buffer(c), false, L);
+        if (n == C) IO::stage_async(nullptr, k, v, gate, tok0, buffer_lds(c), false, L);
+        else IO::stage_ragged(nullptr, k, v, gate, tok0, n, buffer(c), false, L);
     }
     __device__ void prologue(const bf16_t* k, const bf16_t* v, const Lane& L) {
 #pragma unroll

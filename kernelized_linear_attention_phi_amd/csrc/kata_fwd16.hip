@@ -234,16 +234,69 @@ __device__ __forceinline__ void record_load(const float* rec, State<DV, C>& st, 
     st.zm = r4[NMT * F::NTV * 64 + L.lane];
 }
 
+// ---- decay gate --------------------------------------------------------------
+// Per-token log-decays g <= 0 (state S_t = exp(g_t) S_{t-1} + phi(k_t) v_t^T, z
+// likewise). Within a chunk, b_t = g_0 + ... + g_t (log2 units here); the
+// inter-chunk term of query t decays by exp(b_t), key j inside the chunk by
+// exp(b_t - b_j), and the state leaves the chunk scaled by exp(b_last) with key
+// j weighted exp(b_last - b_j) (applied as sqrt to the key before the
+// quadratic lift).
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct ChunkDecay {
+    float b;      // lane t (< C): b_t; lanes past the chunk: b_{C-1}
+    float last;   // b_{C-1} (positions past a ragged end carry g = 0)
+};
+
+// Inclusive scan of the staged log-decays over the wavefront (lane = position).
+template <int C>
+__device__ __forceinline__ ChunkDecay chunk_decay(const char* staged_g, const Lane& L) {
+    float x = L.lane < C ? reinterpret_cast<const float*>(staged_g)[L.lane] * kLog2e : 0.0f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_up(x, d, 64);
+        if (L.lane >= d) x += y;
+    }
+    return ChunkDecay{x, __shfl(x, C - 1, 64)};
+}
+
+// b of chunk position 16 jb + 4g + r (the key slots of K^T fragments).
+__device__ __forceinline__ float key_b(const ChunkDecay& cd, int jb, int r, const Lane& L) {
+    return __shfl(cd.b, 16 * jb + 4 * L.g + r, 64);
+}
+
+// State leaving a chunk: every accumulator scaled by a; keys (KT[jb][r] =
+// k[16 jb + 4g + r][c16]) scaled by exp((b_last - b_j) / 2).
+template <int DV, int C>
+__device__ __forceinline__ void decay_state_and_keys(State<DV, C>& st, f32x4_t (&KT)[Cfg<DV, C>::TT],
+                                                     const ChunkDecay& cd, const Lane& L) {
+    using F = Cfg<DV, C>;
+    const float a = exp2f(cd.last);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] *= a;
+#pragma unroll
+    for (int j = 0; j < F::H8; ++j) st.x[j] *= a;
+    st.zm *= a;
+#pragma unroll
+    for (int jb = 0; jb < F::TT; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) KT[jb][r] *= exp2f(0.5f * (cd.last - key_b(cd, jb, r, L)));
+}
+
 // ---- per-wavefront bodies --------------------------------------------------------
 
-template <int W, int DV, int C>
-__device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v, float* rec,
-                                               char* lds, int T, int NC, int G, int NSEG,
-                                               const Lane& L) {
+template <int W, int DV, int C, bool DECAY>
+__device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v, const float* gdec,
+                                               float* rec, float* segdec, char* lds, int T,
+                                               int NC, int G, int NSEG, const Lane& L) {
     using F = Cfg<DV, C>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    LoadPipeline<DK, DV, C, NW, 3> P{lds, seg * G, min(NC, seg * G + G), T, bh * T};
+    LoadPipeline<DK, DV, C, NW, 3, DECAY> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, gdec};
+    float lsum = 0.0f;                             // log2 of the segment's decay
     State<DV, C> st;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -261,6 +314,11 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
         const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::QB);
         f32x4_t KT[F::TT];
         k_transposed<DV, C>(bk, KT, L);
+        if constexpr (DECAY) {
+            const ChunkDecay cd = chunk_decay<C>(buf + 2 * F::QB + F::VB, L);
+            decay_state_and_keys<DV, C>(st, KT, cd, L);
+            lsum += cd.last;
+        }
         u32x4_t vop[F::KS][F::NTV];
 #pragma unroll
         for (int m = 0; m < F::KS; ++m) v_fragment_step<DV, C>(bv, vop[m], m, L);
@@ -270,6 +328,7 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
         compiler_fence();
     }
     record_store<W, W == 1, DV, C>(rec + (bh * NSEG + seg) * (size_t)F::REC, st, L);
+    if (DECAY && W == 0 && L.lane == 0) segdec[bh * NSEG + seg] = exp2f(lsum);
 }
 
 // Stores the output rows one wavefront staged in LDS (its exchange half, row
@@ -299,19 +358,20 @@ __device__ __forceinline__ void store_staged_rows(const char* ostage, bf16_t* oc
 // output store and never waits for them. Both stage their output rows in LDS
 // (their own exchange half); wavefront 1 stores its rows in the same chunk and
 // wavefront 0's one chunk later, as whole rows.
-template <int W, int DV, int C, bool CAUSAL>
+template <int W, int DV, int C, bool CAUSAL, bool DECAY>
 __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const bf16_t* v,
-                                         const float* prefix, float* final_rec, bf16_t* o,
-                                         char* lds, int T, int NC, int G, int NSEG,
-                                         const Lane& L) {
+                                         const float* gdec, const float* prefix,
+                                         float* final_rec, bf16_t* o, char* lds, int T, int NC,
+                                         int G, int NSEG, const Lane& L) {
     using F = Cfg<DV, C>;
+    using IO = ChunkIO<DK, DV, C, NW, 1, DECAY>;
     constexpr int l8 = lo8<W, F::NTV>(), h8 = hi8<W, F::NTV>();
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    Pipeline<DK, DV, C, NW, 1> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true};
+    Pipeline<DK, DV, C, NW, 1, DECAY> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true, gdec};
     // exchange buffer: partials for query tile (u of wavefront w) at [w][u][nt][lane];
     // half 0 then holds wavefront 0's staged output rows until the next chunk
-    f32x4_t* xbuf = reinterpret_cast<f32x4_t*>(lds + F::NBUF * F::BUF);
+    f32x4_t* xbuf = reinterpret_cast<f32x4_t*>(lds + F::NBUF * IO::BUF);
     char* ostage = reinterpret_cast<char*>(xbuf);
 
     State<DV, C> st;
@@ -326,6 +386,14 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::QB);
         const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::QB);
         bf16_t* oc = o + (bh * T + (size_t)c * C) * DV;
+        // decay gate: the chunk's cumulative log-decays (staged with q)
+        ChunkDecay cd{0.0f, 0.0f};
+        float bq_own[F::TW];                        // b of this lane's query in own tile u
+        if constexpr (DECAY) {
+            cd = chunk_decay<C>(buf + 2 * F::QB + F::VB, L);
+#pragma unroll
+            for (int u = 0; u < F::TW; ++u) bq_own[u] = __shfl(cd.b, 16 * (NW * u + W) + L.c16, 64);
+        }
 
         // wavefront 0's rows of the previous chunk, before its half is reused
         if (W == 1 && c > P.c0) store_staged_rows<DV, C>(ostage, oc - (size_t)C * DV, C, L);
@@ -391,6 +459,14 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
 #pragma unroll
             for (int nt = 0; nt < F::NTV; ++nt)
                 num[u][nt] += xbuf[(W * F::TW + u) * F::NTV * 64 + nt * 64 + L.lane];
+        if constexpr (DECAY) {                        // the prefix state decays to query t
+#pragma unroll
+            for (int u = 0; u < F::TW; ++u) {
+                const float e = exp2f(bq_own[u]);
+#pragma unroll
+                for (int nt = 0; nt < F::NTV; ++nt) num[u][nt] *= e;
+            }
+        }
         compiler_fence();                             // partials read before rows are staged
 
         // V^T fragments (intra term and state update)
@@ -425,7 +501,8 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int j = 32 * m + 16 * h + 4 * L.g + r;
-                            const float x = sc[r] * sc[r];
+                            float x = sc[r] * sc[r];
+                            if constexpr (DECAY) x *= exp2f(bq_own[u] - key_b(cd, 2 * m + h, r, L));
                             w[4 * h + r] = (!diag || j <= t) ? x : 0.0f;
                         }
                     }
@@ -445,6 +522,7 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
             di = __builtin_fmaf(qr[3], zq[3], di);
             di += __shfl_xor(di, 16, 64);
             di += __shfl_xor(di, 32, 64);
+            if constexpr (DECAY) di *= exp2f(bq_own[u]);
             // intra-chunk denominator: row 0 of the ones tile (lane group 0)
             const float den = __shfl(num[u][F::NTV][0], L.c16, 64) + di;
             const float y = inv_den(den);                  // y = 0 gives o = 0
@@ -470,6 +548,7 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         if (CAUSAL) {
             f32x4_t KT[F::TT];
             k_transposed<DV, C>(bk, KT, L);
+            if constexpr (DECAY) decay_state_and_keys<DV, C>(st, KT, cd, L);
             state_update<W, true, DV, C>(st, KT, vop, L);
         }
         compiler_fence();
@@ -487,68 +566,85 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
 
 // ---- kernels -------------------------------------------------------------------
 
-template <int DV, int C>
+template <int DV, int C, bool DECAY>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kata_seg_state16(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-                      float* __restrict__ rec, int T, int NC, int G, int NSEG) {
-    using F = Cfg<DV, C>;
-    __shared__ __attribute__((aligned(16))) char lds[3 * F::BUF];
+                      const float* __restrict__ gdec, float* __restrict__ rec,
+                      float* __restrict__ segdec, int T, int NC, int G, int NSEG) {
+    __shared__ __attribute__((aligned(16))) char lds[3 * ChunkIO<DK, DV, C, NW, NW, DECAY>::BUF];
     const Lane L;
-    if (L.w == 0) seg_state_body<0, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L);
-    else seg_state_body<1, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L);
+    if (L.w == 0) seg_state_body<0, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, L);
+    else seg_state_body<1, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, L);
 }
 
-template <int DV, int C, bool CAUSAL>
+template <int DV, int C, bool CAUSAL, bool DECAY>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kata_fwd16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                const bf16_t* __restrict__ v, const float* __restrict__ prefix,
-                float* __restrict__ final_rec, bf16_t* __restrict__ o, int T, int NC, int G,
-                int NSEG) {
+                const bf16_t* __restrict__ v, const float* __restrict__ gdec,
+                const float* __restrict__ prefix, float* __restrict__ final_rec,
+                bf16_t* __restrict__ o, int T, int NC, int G, int NSEG) {
     using F = Cfg<DV, C>;
-    __shared__ __attribute__((aligned(16))) char lds[F::NBUF * F::BUF + F::XB];
+    __shared__ __attribute__((aligned(16))) char lds[F::NBUF * ChunkIO<DK, DV, C, NW, 1, DECAY>::BUF + F::XB];
     const Lane L;
-    if (L.w == 0) fwd_body<0, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC, G, NSEG, L);
-    else fwd_body<1, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC, G, NSEG, L);
+    if (L.w == 0)
+        fwd_body<0, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G, NSEG, L);
+    else
+        fwd_body<1, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G, NSEG, L);
 }
 
+// Launch arguments shared by every shape: gdec (log-decays, NULL = no gate;
+// the gated forward is causal only), segdec (per-segment decays, state kernel).
+struct Args {
+    const void *q, *k, *v;
+    const float* gdec;
+    float* rec;            // state kernel: segment records; output kernel: final_rec
+    float* segdec;
+    const float* prefix;
+    void* o;
+    int causal, G, NSEG;
+    bool state_only;
+};
+
 template <int DV, int C>
-hipError_t launch_dv_c(const Shape& s, const void* q, const void* k, const void* v,
-                       float* rec, const float* prefix, void* o, int causal, int G, int NSEG,
-                       bool state_only, hipStream_t st) {
-    dim3 grid(NSEG, s.B * s.H);
-    if (state_only) {
-        kata_seg_state16<DV, C><<<grid, 64 * NW, 0, st>>>((const bf16_t*)k, (const bf16_t*)v, rec,
-                                                           s.T, s.NC, G, NSEG);
-    } else if (causal) {
-        kata_fwd16<DV, C, true><<<grid, 64 * NW, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
-                                                           (const bf16_t*)v, prefix, rec,
-                                                           (bf16_t*)o, s.T, s.NC, G, NSEG);
+hipError_t launch_dv_c(const Shape& s, const Args& a, hipStream_t st) {
+    dim3 grid(a.NSEG, s.B * s.H);
+    const bf16_t *q = (const bf16_t*)a.q, *k = (const bf16_t*)a.k, *v = (const bf16_t*)a.v;
+    bf16_t* o = (bf16_t*)a.o;
+    if (a.state_only) {
+        if (a.gdec)
+            kata_seg_state16<DV, C, true><<<grid, 64 * NW, 0, st>>>(k, v, a.gdec, a.rec, a.segdec,
+                                                                     s.T, s.NC, a.G, a.NSEG);
+        else
+            kata_seg_state16<DV, C, false><<<grid, 64 * NW, 0, st>>>(k, v, nullptr, a.rec, nullptr,
+                                                                      s.T, s.NC, a.G, a.NSEG);
+    } else if (a.gdec) {
+        kata_fwd16<DV, C, true, true><<<grid, 64 * NW, 0, st>>>(q, k, v, a.gdec, a.prefix, a.rec, o,
+                                                                 s.T, s.NC, a.G, a.NSEG);
+    } else if (a.causal) {
+        kata_fwd16<DV, C, true, false><<<grid, 64 * NW, 0, st>>>(q, k, v, nullptr, a.prefix, a.rec,
+                                                                  o, s.T, s.NC, a.G, a.NSEG);
     } else {
-        kata_fwd16<DV, C, false><<<grid, 64 * NW, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
-                                                            (const bf16_t*)v, prefix, rec,
-                                                            (bf16_t*)o, s.T, s.NC, G, NSEG);
+        kata_fwd16<DV, C, false, false><<<grid, 64 * NW, 0, st>>>(q, k, v, nullptr, a.prefix, a.rec,
+                                                                   o, s.T, s.NC, a.G, a.NSEG);
     }
     return hipGetLastError();
 }
 
 template <int C>
-hipError_t launch_c(const Shape& s, const void* q, const void* k, const void* v, float* rec,
-                    const float* prefix, void* o, int causal, int G, int NSEG, bool state_only,
-                    hipStream_t st) {
+hipError_t launch_c(const Shape& s, const Args& a, hipStream_t st) {
     switch (s.dv) {
-        case 16: return launch_dv_c<16, C>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
-        case 32: return launch_dv_c<32, C>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
-        case 64: return launch_dv_c<64, C>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+        case 16: return launch_dv_c<16, C>(s, a, st);
+        case 32: return launch_dv_c<32, C>(s, a, st);
+        case 64: return launch_dv_c<64, C>(s, a, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t dispatch(const Shape& s, const void* q, const void* k, const void* v, float* rec,
-                    const float* prefix, void* o, int causal, int G, int NSEG, bool state_only,
-                    hipStream_t st) {
+hipError_t dispatch(const Shape& s, const Args& a, hipStream_t st) {
+    if (a.gdec && !a.state_only && !a.causal) return hipErrorInvalidValue;
     switch (s.C) {
-        case 32: return launch_c<32>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
-        case 64: return launch_c<64>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+        case 32: return launch_c<32>(s, a, st);
+        case 64: return launch_c<64>(s, a, st);
     }
     return hipErrorInvalidValue;
 }
@@ -564,13 +660,25 @@ int mfma16_record_floats(int dv) { return NMT * (dv / 16) * 256 + 256; }
 
 hipError_t launch_seg_state16(const Shape& s, const void* k, const void* v, float* rec, int G,
                               int NSEG, hipStream_t st) {
-    return dispatch(s, nullptr, k, v, rec, nullptr, nullptr, 1, G, NSEG, true, st);
+    return dispatch(s, Args{nullptr, k, v, nullptr, rec, nullptr, nullptr, nullptr, 1, G, NSEG, true}, st);
+}
+
+hipError_t launch_seg_state16_decay(const Shape& s, const void* k, const void* v,
+                                    const float* gdec, float* rec, float* segdec, int G, int NSEG,
+                                    hipStream_t st) {
+    return dispatch(s, Args{nullptr, k, v, gdec, rec, segdec, nullptr, nullptr, 1, G, NSEG, true}, st);
 }
 
 hipError_t launch_fwd16(const Shape& s, const void* q, const void* k, const void* v,
                         const float* prefix, float* final_rec, void* o, int causal, int G,
                         int NSEG, hipStream_t st) {
-    return dispatch(s, q, k, v, final_rec, prefix, o, causal, G, NSEG, false, st);
+    return dispatch(s, Args{q, k, v, nullptr, final_rec, nullptr, prefix, o, causal, G, NSEG, false}, st);
+}
+
+hipError_t launch_fwd16_decay(const Shape& s, const void* q, const void* k, const void* v,
+                              const float* gdec, const float* prefix, float* final_rec, void* o,
+                              int G, int NSEG, hipStream_t st) {
+    return dispatch(s, Args{q, k, v, gdec, final_rec, nullptr, prefix, o, 1, G, NSEG, false}, st);
 }
 
 // ---- record <-> packed state conversion ------------------------------------

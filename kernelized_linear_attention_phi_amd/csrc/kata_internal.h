@@ -37,6 +37,13 @@ hipError_t launch_fwd_valu(const Shape& s, const void* q, const void* k, const v
 hipError_t launch_scan_records(float* rec, int nseq, int NR, int E, const float* init,
                                float* total_a, float* total_b, hipStream_t st);
 
+// The same with the decay gate: record r of sequence b also carries the factor
+// dec[b*NR + r] by which its span decays the state before it; record r becomes
+// the exclusive prefix under (a1, S1) o (a2, S2) = (a1 a2, a2 S1 + S2).
+hipError_t launch_scan_records_decay(float* rec, const float* dec, int nseq, int NR, int E,
+                                     const float* init, float* total_a, float* total_b,
+                                     hipStream_t st);
+
 // Copies (src != NULL) or zero-fills n floats.
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st);
 
@@ -54,6 +61,14 @@ hipError_t launch_seg_state16(const Shape& s, const void* k, const void* v, floa
 hipError_t launch_fwd16(const Shape& s, const void* q, const void* k, const void* v,
                         const float* prefix, float* final_rec, void* o, int causal, int G,
                         int NSEG, hipStream_t st);
+// Decay-gated (causal only): gdec [BH, T] per-token log-decays (<= 0); the state
+// kernel also writes each segment's total decay to segdec [BH, NSEG].
+hipError_t launch_seg_state16_decay(const Shape& s, const void* k, const void* v,
+                                    const float* gdec, float* rec, float* segdec, int G, int NSEG,
+                                    hipStream_t st);
+hipError_t launch_fwd16_decay(const Shape& s, const void* q, const void* k, const void* v,
+                              const float* gdec, const float* prefix, float* final_rec, void* o,
+                              int G, int NSEG, hipStream_t st);
 hipError_t launch_record_from_packed16(float* rec, const float* S, const float* z, int dv,
                                        int nrec, hipStream_t st);
 hipError_t launch_record_to_packed16(const float* rec, float* S, float* z, int dv, int nrec,
@@ -94,7 +109,8 @@ hipError_t launch_flash_fwd(const Shape& s, const void* q, const void* k, const 
                             int causal, hipStream_t st);
 
 // ---- decode ----
-hipError_t launch_decode(const void* q, const void* k, const void* v, float* S, float* z,
-                         void* o, int N, int dk, int dv, bool bf16, hipStream_t st);
+// g: NULL, or [N] per-row log-decays (S = exp(g) S + phi(k) v^T, z likewise)
+hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g, float* S,
+                         float* z, void* o, int N, int dk, int dv, bool bf16, hipStream_t st);
 
 }  // namespace kata

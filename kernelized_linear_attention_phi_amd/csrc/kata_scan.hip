@@ -12,6 +12,12 @@
 // parallel, the group sums are prefixed, and each group is walked from its
 // offset. Either way each record is read once and written once, with many
 // 16-byte loads in flight per thread, since the scan is bound by HBM.
+//
+// Decay-gated variant: record r also carries the factor a_r by which its span
+// decays the state before it, and the operator becomes
+// (a1, S1) o (a2, S2) = (a1 a2, a2 S1 + S2) (1 earlier): associative but not
+// commutative, so the walk is carry <- a_r carry + S_r and group aggregates are
+// combined in order.
 #include "kata_device.h"
 #include "kata_internal.h"
 
@@ -23,15 +29,22 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
     return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
+// a * x + y, elementwise (the decayed combine; a = 1 is plain addition)
+__device__ __forceinline__ float4 axpy4(float a, float4 x, float4 y) {
+    return make_float4(__builtin_fmaf(a, x.x, y.x), __builtin_fmaf(a, x.y, y.y),
+                       __builtin_fmaf(a, x.z, y.z), __builtin_fmaf(a, x.w, y.w));
+}
+
 // Few records per sequence (NR <= kSeqMax): one thread per 4 consecutive
 // elements walks the records in order. Loads are issued 8 records ahead of the
 // dependent adds, so every thread keeps 8 coalesced 16-byte reads in flight.
 constexpr int kSeqMax = 32;
 constexpr int kSeqUnroll = 8;
 
+template <bool DECAY>
 __global__ __launch_bounds__(256) void scan_records_seq_kernel(
-    float* __restrict__ rec, int NR, int E, const float* __restrict__ init,
-    float* __restrict__ total_a, float* __restrict__ total_b) {
+    float* __restrict__ rec, const float* __restrict__ dec, int NR, int E,
+    const float* __restrict__ init, float* __restrict__ total_a, float* __restrict__ total_b) {
     const size_t seq = blockIdx.y;
     const int E4 = E / 4;
     const int e4 = blockIdx.x * blockDim.x + threadIdx.x;
@@ -48,7 +61,7 @@ __global__ __launch_bounds__(256) void scan_records_seq_kernel(
         for (int i = 0; i < kSeqUnroll; ++i)
             if (r0 + i < NR) {
                 base[(size_t)(r0 + i) * E4] = carry;
-                carry = add4(carry, x[i]);
+                carry = DECAY ? axpy4(dec[seq * NR + r0 + i], carry, x[i]) : add4(carry, x[i]);
             }
     }
     if (total_a) reinterpret_cast<float4*>(total_a + seq * E)[e4] = carry;
@@ -66,10 +79,12 @@ constexpr int kGroups = 8;
 constexpr int kPer = 16;
 constexpr int kTileRecs = kGroups * kPer;
 
+template <bool DECAY>
 __global__ __launch_bounds__(kCols4 * kGroups) void scan_records_blocked_kernel(
-    float* __restrict__ rec, int NR, int E, const float* __restrict__ init,
-    float* __restrict__ total_a, float* __restrict__ total_b) {
+    float* __restrict__ rec, const float* __restrict__ dec, int NR, int E,
+    const float* __restrict__ init, float* __restrict__ total_a, float* __restrict__ total_b) {
     __shared__ float4 gsum[kGroups][kCols4];
+    __shared__ float gdec[kGroups];
     const size_t seq = blockIdx.y;
     const int E4 = E / 4;
     const int c = threadIdx.x % kCols4, g = threadIdx.x / kCols4;
@@ -95,23 +110,39 @@ __global__ __launch_bounds__(kCols4 * kGroups) void scan_records_blocked_kernel(
             const bool ok = col_ok && rg + i < NR;
             x[i] = make_float4(ok ? t.x : 0.f, ok ? t.y : 0.f, ok ? t.z : 0.f, ok ? t.w : 0.f);
         }
-        float4 s = zero;
+        // decays of this thread's records; records past the end are the
+        // identity (a = 1, S = 0)
+        float a[kPer];
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) s = add4(s, x[i]);
+        for (int i = 0; i < kPer; ++i) a[i] = DECAY && rg + i < NR ? dec[seq * NR + rg + i] : 1.0f;
+        float4 s = zero;
+        float ag = 1.0f;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            s = DECAY ? axpy4(a[i], s, x[i]) : add4(s, x[i]);
+            ag *= a[i];
+        }
         gsum[g][c] = s;
+        if (DECAY && c == 0) gdec[g] = ag;
         __syncthreads();
         float4 off = carry, tot = carry;
 #pragma unroll
         for (int j = 0; j < kGroups; ++j) {
             const float4 gj = gsum[j][c];
-            if (j < g) off = add4(off, gj);
-            tot = add4(tot, gj);
+            if (DECAY) {
+                const float aj = gdec[j];
+                if (j < g) off = axpy4(aj, off, gj);
+                tot = axpy4(aj, tot, gj);
+            } else {
+                if (j < g) off = add4(off, gj);
+                tot = add4(tot, gj);
+            }
         }
         __syncthreads();                           // gsum is rewritten by the next tile
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             if (col_ok && rg + i < NR) base[(size_t)(rg + i) * E4] = off;
-            off = add4(off, x[i]);
+            off = DECAY ? axpy4(a[i], off, x[i]) : add4(off, x[i]);
         }
         carry = tot;
     }
@@ -128,21 +159,33 @@ __global__ void copy_or_zero_kernel(float* __restrict__ dst, const float* __rest
         dst[i] = src ? src[i] : 0.0f;
 }
 
-}  // namespace
-
-hipError_t launch_scan_records(float* rec, int nseq, int NR, int E, const float* init,
-                               float* total_a, float* total_b, hipStream_t st) {
+template <bool DECAY>
+hipError_t scan_impl(float* rec, const float* dec, int nseq, int NR, int E, const float* init,
+                     float* total_a, float* total_b, hipStream_t st) {
     if (nseq == 0 || E == 0) return hipSuccess;
     if (E % 4 != 0) return hipErrorInvalidValue;      // every record length is a multiple of 4
     if (NR <= kSeqMax) {
         dim3 grid((E / 4 + 255) / 256, nseq);
-        scan_records_seq_kernel<<<grid, 256, 0, st>>>(rec, NR, E, init, total_a, total_b);
+        scan_records_seq_kernel<DECAY><<<grid, 256, 0, st>>>(rec, dec, NR, E, init, total_a, total_b);
     } else {
         dim3 grid((E / 4 + kCols4 - 1) / kCols4, nseq);
-        scan_records_blocked_kernel<<<grid, kCols4 * kGroups, 0, st>>>(rec, NR, E, init, total_a,
-                                                                       total_b);
+        scan_records_blocked_kernel<DECAY><<<grid, kCols4 * kGroups, 0, st>>>(rec, dec, NR, E, init,
+                                                                              total_a, total_b);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan_records(float* rec, int nseq, int NR, int E, const float* init,
+                               float* total_a, float* total_b, hipStream_t st) {
+    return scan_impl<false>(rec, nullptr, nseq, NR, E, init, total_a, total_b, st);
+}
+
+hipError_t launch_scan_records_decay(float* rec, const float* dec, int nseq, int NR, int E,
+                                     const float* init, float* total_a, float* total_b,
+                                     hipStream_t st) {
+    return scan_impl<true>(rec, dec, nseq, NR, E, init, total_a, total_b, st);
 }
 
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st) {

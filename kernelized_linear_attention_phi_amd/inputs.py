@@ -16,7 +16,8 @@ Workloads (shapes and value distributions):
 
 For the first-order (identity) feature, orthant_qkv draws the same shapes with
 q, k on the nonnegative orthant (unit rows of |N(0, I)|), the cone on which that
-feature's weights q.k are nonnegative.
+feature's weights q.k are nonnegative. For the decay gate, log_decays draws
+per-token log forget gates uniformly in [gmin, 0].
 
 The recall-shaped stream stands in for the associative-recall and
 repeated-key-overwrite workloads the pages evaluate on; no item of any public
@@ -33,7 +34,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "round_to", "gaussian_qkv", "orthant_qkv", "RecallStream",
+__all__ = ["Workload", "WORKLOADS", "round_to", "gaussian_qkv", "orthant_qkv", "log_decays",
+           "RecallStream",
            "recall_stream", "decode_continuation"]
 
 
@@ -98,6 +100,13 @@ def orthant_qkv(B, H, T, dk, dv, seed, dtype="bf16"):
     k = np.abs(_unit_rows(rng, (B, H, T, dk)))
     v = rng.standard_normal((B, H, T, dv))
     return round_to(q, dtype), round_to(k, dtype), round_to(v, dtype)
+
+
+def log_decays(B, H, T, seed, gmin=-0.05):
+    """Per-token log forget gates g ~ U(gmin, 0) (float32 [B,H,T]): the decay of
+    the state at each token is exp(g) in (exp(gmin), 1]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.uniform(gmin, 0.0, (B, H, T)).astype(np.float32)
 
 
 class RecallStream:

@@ -40,8 +40,8 @@ import numpy as np
 
 from .kata_oracle import _safe_ratio, phi, phi_dim
 
-__all__ = ["decay_brute_force", "decay_recurrent", "decay_combine", "decay_prefix_states",
-           "decay_chunked", "decay_decode_step"]
+__all__ = ["decay_brute_force", "decay_brute_force_rows", "decay_recurrent", "decay_combine",
+           "decay_prefix_states", "decay_chunked", "decay_decode_step"]
 
 
 def _cum(g):
@@ -74,6 +74,24 @@ def decay_brute_force(q, k, v, g, S0=None, z0=None):
                 num = num + e * (fq @ np.asarray(S0[b, h], np.float64))
                 den = den + e[:, 0] * (fq @ np.asarray(z0[b, h], np.float64))
             o[b, h] = _safe_ratio(num, den)
+    return o
+
+
+def decay_brute_force_rows(q, k, v, g, rows):
+    """The same definition for the query positions `rows` only (every b, h):
+    O(T) per row, for spot checks of long sequences. Returns [B,H,len(rows),dv]."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    G = _cum(g)
+    B, H, T, _ = q.shape
+    o = np.zeros((B, H, len(rows), v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            for i, t in enumerate(rows):
+                w = (k[b, h, :t + 1] @ q[b, h, t]) ** 2 * np.exp(G[b, h, t] - G[b, h, :t + 1])
+                den = w.sum()
+                o[b, h, i] = (w @ v[b, h, :t + 1]) / den if den != 0.0 else 0.0
     return o
 
 

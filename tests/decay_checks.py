@@ -6,6 +6,7 @@ checks against copies with a planted mistake.
 
   no_decay          g = 0 reduces to the ungated brute force and prefix states
   golden_worked     hand-worked rationals, gamma = 1/2 (tests/golden/decay_t3.txt)
+  rows_eq           the rows-only brute force = the full one on those rows
   recurrent_eq      brute force = token recurrence (with an initial state)
   chunk_invariance  chunked form with the log-depth combine scan = brute force
                     for every C; final state = the recurrence's
@@ -88,6 +89,12 @@ def golden_worked(O):
         _close(O.decay_brute_force(q, k, v, lg), want, 1e-14)
         _close(O.decay_recurrent(q, k, v, lg)[0], want, 1e-14)
         _close(O.decay_chunked(q, k, v, lg, 2)[0], want, 1e-14)
+
+
+def rows_eq(O):
+    q, k, v, g = _case(12, T=21)
+    rows = [0, 3, 7, 20]
+    _close(O.decay_brute_force_rows(q, k, v, g, rows), O.decay_brute_force(q, k, v, g)[:, :, rows])
 
 
 def recurrent_eq(O):
@@ -175,7 +182,7 @@ def decode_chain(O):
     _close(z, z_ref[0])
 
 
-ALL = [no_decay, golden_worked, recurrent_eq, chunk_invariance, combine_laws, ema_closed_form,
+ALL = [no_decay, golden_worked, rows_eq, recurrent_eq, chunk_invariance, combine_laws, ema_closed_form,
        reset, convexity, decode_chain]
 
 

@@ -112,6 +112,31 @@ def test_feature_dim_and_ex_workspace(L):
     assert ws(1, 1, 64, 16, 64, 64, BF16, 1, 9, SCAN) == 0
 
 
+def fwd_decay(L, B=1, H=2, T=64, dk=16, dv=64, C=64, dtype=BF16, prefix=SCAN, g=FAKE, q=FAKE,
+              ws=FAKE, ws_bytes=1 << 40, o=FAKE):
+    return L.kata_chunked_fwd_decay(q, FAKE, FAKE, g, o, B, H, T, dk, dv, C, dtype, prefix,
+                                    None, None, None, None, ws, ws_bytes, None)
+
+
+def test_decay_rejects_before_launch(L):
+    assert fwd_decay(L, g=None) == EINVAL
+    assert fwd_decay(L, g=MISALIGNED) == EINVAL
+    assert fwd_decay(L, prefix=4) == EINVAL
+    assert fwd_decay(L, dtype=F32) == EUNSUPPORTED
+    assert fwd_decay(L, dk=32, C=128) == EUNSUPPORTED
+    assert fwd_decay(L, C=128) == EUNSUPPORTED
+    assert fwd_decay(L, T=66) == EUNSUPPORTED                 # B*H > 1 needs T % 4 == 0
+    assert fwd_decay(L, ws_bytes=16) == EWORKSPACE
+    assert fwd_decay(L, T=0, q=None, o=None, g=None, ws=None, ws_bytes=0) == OK   # empty
+    ws = L.kata_chunked_fwd_decay_workspace
+    assert ws(1, 8, 131072, 16, 64, 64, BF16, SCAN) > ws(1, 8, 131072, 16, 64, 64, BF16, SEQUENTIAL) > 0
+    assert ws(1, 8, 4096, 32, 64, 128, BF16, SCAN) == 0
+    dec = L.kata_decode_step_decay
+    assert dec(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 16, 64, BF16, None) == EINVAL
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 12, 64, BF16, None) == EUNSUPPORTED
+    assert dec(None, None, None, None, None, None, None, 0, 16, 64, BF16, None) == OK
+
+
 def test_profiled_needs_five_events(L):
     prof = L.kata_chunked_fwd_profiled
     evs = (ctypes.c_void_p * 5)(*([FAKE] * 5))

@@ -32,6 +32,7 @@ MUTATIONS = {
     "chunk_decay_exclusive": ("    return np.exp(G[..., -1]), S, fk.sum(axis=2)",
                               "    return np.exp(G[..., -1] - np.asarray(g, np.float64)[..., 0]), S, fk.sum(axis=2)"),
     "decode_no_decay": ("    gam = np.exp(np.asarray(g, np.float64))\n", "    gam = np.ones_like(np.asarray(g, np.float64))\n"),
+    "rows_weight_sign": ("np.exp(G[b, h, t] - G[b, h, :t + 1])", "np.exp(G[b, h, :t + 1] - G[b, h, t])"),
     "intra_mask_strict": ("        tri = np.tril(np.ones((n, n), dtype=bool))", "        tri = np.tril(np.ones((n, n), dtype=bool), -1)"),
 }
 
