@@ -115,9 +115,10 @@ def quadratic_vs_chunked(kata, torch, gen, name, steps, warmup):
             "flash_mfma_util_alg": qflops / (ms_f * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def decode_bench(kata, torch, steps=1024, n_seq=512, heads=4, dk=16, dv=64, reps=3):
+def decode_bench(kata, torch, steps=1024, n_seq=512, heads=4, dk=16, dv=64, reps=3, gated=False):
     """1024 decode steps on n_seq x heads rows with fp32 state, replayed from a
-    HIP graph; returns ms per step and algorithmic GB/s."""
+    HIP graph; returns ms per step and algorithmic GB/s. gated: the decay-gated
+    step, with per-row log-decays in [-0.05, 0]."""
     from kernelized_linear_attention_phi_amd import inputs as gen
     N = n_seq * heads
     D = dk * (dk + 1) // 2
@@ -131,15 +132,23 @@ def decode_bench(kata, torch, steps=1024, n_seq=512, heads=4, dk=16, dv=64, reps
     S = torch.rand((N, D, dv), device="cuda") * 0.01
     z = torch.rand((N, D), device="cuda") + 1.0
     o = torch.empty((steps, N, dv), dtype=torch.bfloat16, device="cuda")
+    gd = torch.from_numpy(gen.log_decays(1, steps, N, seed=5001)[0]).cuda()
+
+    def step(t):
+        if gated:
+            kata.decode_step_decay(qd[t], kd[t], vd[t], gd[t], S, z, out=o[t])
+        else:
+            kata.decode_step(qd[t], kd[t], vd[t], S, z, out=o[t])
+
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for t in range(4):
-            kata.decode_step(qd[t], kd[t], vd[t], S, z, out=o[t])
+            step(t)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for t in range(steps):
-                kata.decode_step(qd[t], kd[t], vd[t], S, z, out=o[t])
+                step(t)
         g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -149,8 +158,33 @@ def decode_bench(kata, torch, steps=1024, n_seq=512, heads=4, dk=16, dv=64, reps
         e1.record(stream)
         torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / (reps * steps)
-    bytes_step = N * (2 * 4 * D * (dv + 1) + 2 * (2 * dk + 2 * dv))
+    bytes_step = N * (2 * 4 * D * (dv + 1) + 2 * (2 * dk + 2 * dv) + (4 if gated else 0))
     return ms_step, bytes_step / (ms_step * 1e-3) / 1e9, bytes_step
+
+
+def decay_gate(kata, torch, gen, steps, warmup):
+    """The fwd131k forward with per-token log-decays in [-0.05, 0] against the
+    ungated forward on the same inputs (both without state export), and the
+    gated decode step."""
+    w = gen.WORKLOADS["fwd131k"]
+    to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+    q, k, v = (to(a) for a in gen.gaussian_qkv(w.B, w.H, w.T, w.dk, w.dv, w.seed, w.dtype))
+    g = torch.from_numpy(gen.log_decays(w.B, w.H, w.T, seed=w.seed + 100)).cuda()
+    o = torch.empty_like(v)
+    nb = kata.chunked_fwd_decay_workspace(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1, "scan")
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    ms_g = time_calls(torch, lambda: kata.chunked_fwd_decay_into(q, k, v, g, o, w.chunk, ws),
+                      steps, warmup)
+    nb2 = kata.chunked_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1, True)
+    ws2 = torch.empty(max(nb2, 1), dtype=torch.uint8, device="cuda")
+    ms_u = time_calls(torch, lambda: kata.chunked_fwd_into(q, k, v, o, w.chunk, True, ws2),
+                      steps, warmup)
+    dms, dgbs, _ = decode_bench(kata, torch, gated=True)
+    return {"fwd131k_gated_ms": ms_g, "fwd131k_ungated_ms": ms_u,
+            "fwd131k_gated_tokens_per_s": w.B * w.T / (ms_g * 1e-3),
+            "gate_overhead": ms_g / ms_u - 1.0,
+            "decode_gated_ms_per_step": dms, "decode_gated_GBps": dgbs,
+            "decode_gated_hbm_frac": dgbs / PEAK_HBM_GBS}
 
 
 def scan_vs_sequential(kata, torch, gen, names, steps, warmup):
@@ -292,6 +326,8 @@ def main():
                                                         args.warmup)
         result["parts"]["scan_vs_sequential"] = scan_vs_sequential(
             kata, torch, gen, ("fwd4k", "fwd32k", "fwd131k"), min(args.steps, 10), args.warmup)
+        result["parts"]["decay_gate"] = decay_gate(kata, torch, gen, min(args.steps, 10),
+                                                   args.warmup)
         dms, dgbs, dbytes = decode_bench(kata, torch)
         result["parts"]["decode"] = {"ms_per_step": dms, "alg_GBps": dgbs,
                                      "hbm_frac": dgbs / PEAK_HBM_GBS, "bytes_per_step": dbytes,

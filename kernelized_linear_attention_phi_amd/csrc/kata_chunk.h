@@ -157,17 +157,17 @@ struct ChunkIO {
         const char* gk = reinterpret_cast<const char*>(k + tok0 * DK);
         const char* gv = reinterpret_cast<const char*>(v + tok0 * DV);
         constexpr int PQ = QB / 1024, PV = VB / 1024;
+        const int lane = L.lane;
         if constexpr (GATE) {
-            if (L.w == 0 && L.lane < GB / 16)
-                dma16(gate + tok0 + 4 * L.lane, buf_lds + 2 * QB + VB);
+            if (L.w == 0 && lane < GB / 16) dma16(gate + tok0 + 4 * lane, buf_lds + 2 * QB + VB);
         }
         const int first = with_q ? 0 : PQ;
 #pragma unroll
         for (int i = 0; i < 2 * PQ + PV; ++i) {
             if (i < first || i % NLOAD != L.w) continue;
-            const char* src = i < PQ ? gq + 16 * Swz<2 * DK>::slot(64 * i + L.lane)
-                            : i < 2 * PQ ? gk + 16 * Swz<2 * DK>::slot(64 * (i - PQ) + L.lane)
-                                         : gv + 16 * Swz<2 * DV>::slot(64 * (i - 2 * PQ) + L.lane);
+            const char* src = i < PQ ? gq + 16 * Swz<2 * DK>::slot(64 * i + lane)
+                            : i < 2 * PQ ? gk + 16 * Swz<2 * DK>::slot(64 * (i - PQ) + lane)
+                                         : gv + 16 * Swz<2 * DV>::slot(64 * (i - 2 * PQ) + lane);
             dma16(src, buf_lds + i * 1024);
         }
     }

@@ -138,12 +138,84 @@ __device__ __forceinline__ u32x4_t lift_keys_own(int i, const float (&ka)[8], co
     }
 }
 
+// ---- decay gate --------------------------------------------------------------
+// Per-token log-decays g <= 0 (state S_t = exp(g_t) S_{t-1} + phi(k_t) v_t^T, z
+// likewise). Within a chunk, b_t = g_0 + ... + g_t (log2 units here); the
+// inter-chunk term of query t decays by exp(b_t), key j inside the chunk by
+// exp(b_t - b_j), and the state leaves the chunk scaled by exp(b_last) with key
+// j weighted exp(b_last - b_j) (applied as sqrt to the key before the
+// quadratic lift).
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^x for x <= 0 with v_exp_f32 (results below the fp32 normal range may flush
+// to zero, which only drops weights under 2^-126).
+__device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct ChunkDecay {
+    float b;      // lane t (< C): b_t; lanes past the chunk: b_{C-1}
+    float last;   // b_{C-1} (positions past a ragged end carry g = 0)
+};
+
+// Inclusive scan of the staged log-decays over the wavefront (lane = position).
+template <int C>
+__device__ __forceinline__ ChunkDecay chunk_decay(const char* staged_g, const Lane& L) {
+    float x = L.lane < C ? reinterpret_cast<const float*>(staged_g)[L.lane] * kLog2e : 0.0f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_up(x, d, 64);
+        if (L.lane >= d) x += y;
+    }
+    return ChunkDecay{x, __shfl(x, C - 1, 64)};
+}
+
+// b of chunk position 16 jb + 4g + r (the key slots of K^T fragments).
+__device__ __forceinline__ float key_b(const ChunkDecay& cd, int jb, int r, const Lane& L) {
+    return __shfl(cd.b, 16 * jb + 4 * L.g + r, 64);
+}
+
+// The key positions' b values of one chunk, gathered once: b[jb][r] for position
+// 16 jb + 4g + r; last = b_{C-1}.
+template <int TT>
+struct KeyDecay {
+    float b[TT][4];
+    float last;
+};
+
+template <int TT>
+__device__ __forceinline__ KeyDecay<TT> key_decays(const ChunkDecay& cd, const Lane& L) {
+    KeyDecay<TT> kd;
+#pragma unroll
+    for (int jb = 0; jb < TT; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kd.b[jb][r] = key_b(cd, jb, r, L);
+    kd.last = cd.last;
+    return kd;
+}
+
+// State leaving a chunk: every accumulator scaled by a = exp(b_last) (the keys
+// of the chunk are scaled inside state_update).
+template <int DV, int C>
+__device__ __forceinline__ void decay_state(State<DV, C>& st, const ChunkDecay& cd) {
+    using F = Cfg<DV, C>;
+    const float a = exp2_neg(cd.last);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] *= a;
+#pragma unroll
+    for (int j = 0; j < F::H8; ++j) st.x[j] *= a;
+    st.zm *= a;
+}
+
 // S(own tiles) += phi(K_c)^T V_c; Z += K_c^T K_c when WITH_Z. vop[m] are the V^T
-// fragments.
-template <int W, bool WITH_Z, int DV, int C>
+// fragments. With the decay gate (DECAY), key j is first scaled by
+// exp((b_last - b_j) / 2), i.e. its lift by exp(b_last - b_j).
+template <int W, bool WITH_Z, int DV, int C, bool DECAY = false>
 __device__ __forceinline__ void state_update(State<DV, C>& st, const f32x4_t (&KT)[Cfg<DV, C>::TT],
                                              const u32x4_t (&vop)[Cfg<DV, C>::KS][Cfg<DV, C>::NTV],
-                                             const Lane& L) {
+                                             const Lane& L,
+                                             const KeyDecay<Cfg<DV, C>::TT>& kd = KeyDecay<Cfg<DV, C>::TT>{}) {
     using F = Cfg<DV, C>;
     constexpr int l8 = lo8<W, F::NTV>(), h8 = hi8<W, F::NTV>();
 #pragma unroll
@@ -151,6 +223,11 @@ __device__ __forceinline__ void state_update(State<DV, C>& st, const f32x4_t (&K
         float ka[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) ka[s] = KT[2 * m + s / 4][s % 4];
+        if constexpr (DECAY) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                ka[s] *= exp2_neg(0.5f * (kd.last - kd.b[2 * m + s / 4][s % 4]));
+        }
         if constexpr (WITH_Z) {
             // Gram matrix: A = K^T (row = coordinate c16), B = K (column = c16)
             const u32x4_t kt = {pk2(ka[0], ka[1]), pk2(ka[2], ka[3]), pk2(ka[4], ka[5]), pk2(ka[6], ka[7])};
@@ -234,58 +311,6 @@ __device__ __forceinline__ void record_load(const float* rec, State<DV, C>& st, 
     st.zm = r4[NMT * F::NTV * 64 + L.lane];
 }
 
-// ---- decay gate --------------------------------------------------------------
-// Per-token log-decays g <= 0 (state S_t = exp(g_t) S_{t-1} + phi(k_t) v_t^T, z
-// likewise). Within a chunk, b_t = g_0 + ... + g_t (log2 units here); the
-// inter-chunk term of query t decays by exp(b_t), key j inside the chunk by
-// exp(b_t - b_j), and the state leaves the chunk scaled by exp(b_last) with key
-// j weighted exp(b_last - b_j) (applied as sqrt to the key before the
-// quadratic lift).
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-struct ChunkDecay {
-    float b;      // lane t (< C): b_t; lanes past the chunk: b_{C-1}
-    float last;   // b_{C-1} (positions past a ragged end carry g = 0)
-};
-
-// Inclusive scan of the staged log-decays over the wavefront (lane = position).
-template <int C>
-__device__ __forceinline__ ChunkDecay chunk_decay(const char* staged_g, const Lane& L) {
-    float x = L.lane < C ? reinterpret_cast<const float*>(staged_g)[L.lane] * kLog2e : 0.0f;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const float y = __shfl_up(x, d, 64);
-        if (L.lane >= d) x += y;
-    }
-    return ChunkDecay{x, __shfl(x, C - 1, 64)};
-}
-
-// b of chunk position 16 jb + 4g + r (the key slots of K^T fragments).
-__device__ __forceinline__ float key_b(const ChunkDecay& cd, int jb, int r, const Lane& L) {
-    return __shfl(cd.b, 16 * jb + 4 * L.g + r, 64);
-}
-
-// State leaving a chunk: every accumulator scaled by a; keys (KT[jb][r] =
-// k[16 jb + 4g + r][c16]) scaled by exp((b_last - b_j) / 2).
-template <int DV, int C>
-__device__ __forceinline__ void decay_state_and_keys(State<DV, C>& st, f32x4_t (&KT)[Cfg<DV, C>::TT],
-                                                     const ChunkDecay& cd, const Lane& L) {
-    using F = Cfg<DV, C>;
-    const float a = exp2f(cd.last);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] *= a;
-#pragma unroll
-    for (int j = 0; j < F::H8; ++j) st.x[j] *= a;
-    st.zm *= a;
-#pragma unroll
-    for (int jb = 0; jb < F::TT; ++jb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) KT[jb][r] *= exp2f(0.5f * (cd.last - key_b(cd, jb, r, L)));
-}
-
 // ---- per-wavefront bodies --------------------------------------------------------
 
 template <int W, int DV, int C, bool DECAY>
@@ -314,9 +339,11 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
         const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::QB);
         f32x4_t KT[F::TT];
         k_transposed<DV, C>(bk, KT, L);
+        KeyDecay<F::TT> kd{};
         if constexpr (DECAY) {
             const ChunkDecay cd = chunk_decay<C>(buf + 2 * F::QB + F::VB, L);
-            decay_state_and_keys<DV, C>(st, KT, cd, L);
+            kd = key_decays<F::TT>(cd, L);
+            decay_state<DV, C>(st, cd);
             lsum += cd.last;
         }
         u32x4_t vop[F::KS][F::NTV];
@@ -324,11 +351,11 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
         for (int m = 0; m < F::KS; ++m) v_fragment_step<DV, C>(bv, vop[m], m, L);
         // the Gram matrix goes with wavefront 1 (wavefront 0 holds more of tile 8
         // when the value tiles are odd)
-        state_update<W, W == 1, DV, C>(st, KT, vop, L);
+        state_update<W, W == 1, DV, C, DECAY>(st, KT, vop, L, kd);
         compiler_fence();
     }
     record_store<W, W == 1, DV, C>(rec + (bh * NSEG + seg) * (size_t)F::REC, st, L);
-    if (DECAY && W == 0 && L.lane == 0) segdec[bh * NSEG + seg] = exp2f(lsum);
+    if (DECAY && W == 0 && L.lane == 0) segdec[bh * NSEG + seg] = exp2_neg(lsum);
 }
 
 // Stores the output rows one wavefront staged in LDS (its exchange half, row
@@ -386,14 +413,6 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::QB);
         const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::QB);
         bf16_t* oc = o + (bh * T + (size_t)c * C) * DV;
-        // decay gate: the chunk's cumulative log-decays (staged with q)
-        ChunkDecay cd{0.0f, 0.0f};
-        float bq_own[F::TW];                        // b of this lane's query in own tile u
-        if constexpr (DECAY) {
-            cd = chunk_decay<C>(buf + 2 * F::QB + F::VB, L);
-#pragma unroll
-            for (int u = 0; u < F::TW; ++u) bq_own[u] = __shfl(cd.b, 16 * (NW * u + W) + L.c16, 64);
-        }
 
         // wavefront 0's rows of the previous chunk, before its half is reused
         if (W == 1 && c > P.c0) store_staged_rows<DV, C>(ostage, oc - (size_t)C * DV, C, L);
@@ -459,10 +478,22 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
 #pragma unroll
             for (int nt = 0; nt < F::NTV; ++nt)
                 num[u][nt] += xbuf[(W * F::TW + u) * F::NTV * 64 + nt * 64 + L.lane];
+        // decay gate: the chunk's cumulative log-decays (staged with q, valid for
+        // the whole chunk), computed here so that they are not live during the
+        // inter-chunk products
+        ChunkDecay cd{0.0f, 0.0f};
+        KeyDecay<F::TT> kd{};
+        float bq_own[F::TW];                        // b of this lane's query in own tile u
+        if constexpr (DECAY) {
+            cd = chunk_decay<C>(buf + 2 * F::QB + F::VB, L);
+            kd = key_decays<F::TT>(cd, L);
+#pragma unroll
+            for (int u = 0; u < F::TW; ++u) bq_own[u] = __shfl(cd.b, 16 * (NW * u + W) + L.c16, 64);
+        }
         if constexpr (DECAY) {                        // the prefix state decays to query t
 #pragma unroll
             for (int u = 0; u < F::TW; ++u) {
-                const float e = exp2f(bq_own[u]);
+                const float e = exp2_neg(bq_own[u]);
 #pragma unroll
                 for (int nt = 0; nt < F::NTV; ++nt) num[u][nt] *= e;
             }
@@ -502,7 +533,7 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
                         for (int r = 0; r < 4; ++r) {
                             const int j = 32 * m + 16 * h + 4 * L.g + r;
                             float x = sc[r] * sc[r];
-                            if constexpr (DECAY) x *= exp2f(bq_own[u] - key_b(cd, 2 * m + h, r, L));
+                            if constexpr (DECAY) x *= exp2_neg(bq_own[u] - kd.b[2 * m + h][r]);
                             w[4 * h + r] = (!diag || j <= t) ? x : 0.0f;
                         }
                     }
@@ -522,7 +553,7 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
             di = __builtin_fmaf(qr[3], zq[3], di);
             di += __shfl_xor(di, 16, 64);
             di += __shfl_xor(di, 32, 64);
-            if constexpr (DECAY) di *= exp2f(bq_own[u]);
+            if constexpr (DECAY) di *= exp2_neg(bq_own[u]);
             // intra-chunk denominator: row 0 of the ones tile (lane group 0)
             const float den = __shfl(num[u][F::NTV][0], L.c16, 64) + di;
             const float y = inv_den(den);                  // y = 0 gives o = 0
@@ -548,8 +579,8 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         if (CAUSAL) {
             f32x4_t KT[F::TT];
             k_transposed<DV, C>(bk, KT, L);
-            if constexpr (DECAY) decay_state_and_keys<DV, C>(st, KT, cd, L);
-            state_update<W, true, DV, C>(st, KT, vop, L);
+            if constexpr (DECAY) decay_state<DV, C>(st, cd);
+            state_update<W, true, DV, C, DECAY>(st, KT, vop, L, kd);
         }
         compiler_fence();
     }
@@ -577,8 +608,11 @@ void kata_seg_state16(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v
     else seg_state_body<1, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, L);
 }
 
+// The gated variant's larger chunk buffers allow three workgroups per compute
+// unit, not four, so it may also use more than 256 registers per lane (it would
+// otherwise spill loop-invariant addresses).
 template <int DV, int C, bool CAUSAL, bool DECAY>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(DECAY ? 1 : 2, 2)))
 void kata_fwd16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bf16_t* __restrict__ v, const float* __restrict__ gdec,
                 const float* __restrict__ prefix, float* __restrict__ final_rec,
