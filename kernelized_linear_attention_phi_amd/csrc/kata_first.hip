@@ -20,7 +20,9 @@
 // Output kernel: two wavefronts; wavefront w owns query tiles w, w + 2, ...
 // (causally balanced) and holds the whole state (d_k x d_v is small), so no
 // partial sums are exchanged. Wavefront 0 issues every chunk copy and no global
-// store; wavefront 1 issues every store (rows staged in LDS by both).
+// store; wavefront 1 issues every store (rows staged in LDS by both; wavefront
+// 0's in two alternating buffers, since wavefront 1 reads them one chunk later
+// while wavefront 0 already stages the next chunk's rows).
 #include <algorithm>
 
 #include "kata_chunk.h"
@@ -44,7 +46,7 @@ struct Cfg1 {
     using IO = ChunkIO<DK, DV, C, NW1, 1>;
     static constexpr int OROW = DV * 2 + 16;      // LDS row stride of staged output rows
     static constexpr int OST = TW * 16 * OROW;    // staged rows of one wavefront
-    static constexpr int LDS_FWD = 2 * IO::BUF + NW1 * OST;
+    static constexpr int LDS_FWD = 2 * IO::BUF + 3 * OST;   // staged rows: w0 x 2, w1
     static constexpr int NBUF_SEG = 3 * IO::BUF <= 65536 ? 3 : 2;
     static constexpr int LDS_SEG = NBUF_SEG * IO::BUF;
     static constexpr int REC = NAT * NU * 256;
@@ -203,7 +205,8 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
     Pipeline<DK, DV, C, NW1, 1> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true};
-    char* ostage = lds + 2 * F::IO::BUF;           // [wavefront][OST]
+    // staged rows: wavefront 0 in buffer (c - c0) % 2, wavefront 1 in buffer 2
+    char* ostage = lds + 2 * F::IO::BUF;
 
     State1<DK, DV, C> st;
     record_load1<DK, DV, C>(prefix + (CAUSAL ? bh * NSEG + seg : bh) * (size_t)F::REC, st, L);
@@ -220,8 +223,10 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
         bf16_t* oc = o + (bh * T + (size_t)c * C) * DV;
 
         // wavefront 0's rows of the previous chunk (always a full chunk)
-        if (W == 1 && c > P.c0) store_rows1<DK, DV, C>(ostage, oc - (size_t)C * DV, C, L);
+        if (W == 1 && c > P.c0)
+            store_rows1<DK, DV, C>(ostage + ((c - 1 - P.c0) & 1) * F::OST, oc - (size_t)C * DV, C, L);
         compiler_fence();
+        char* own = ostage + (W == 0 ? ((c - P.c0) & 1) : 2) * F::OST;
 
         // the state before this chunk as bf16 A operands of S^T (rows = value
         // columns, K = features); the z tile gives row 0 = z
@@ -274,13 +279,13 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
             const float y = inv_den(__shfl(num[F::NTV][0], L.c16, 64));   // 0 -> o = 0
 #pragma unroll
             for (int nt = 0; nt < F::NTV; ++nt)
-                *reinterpret_cast<u32x2_t*>(ostage + W * F::OST + (16 * ui + L.c16) * F::OROW +
+                *reinterpret_cast<u32x2_t*>(own + (16 * ui + L.c16) * F::OROW +
                                             2 * (16 * nt + 4 * L.g)) =
                     u32x2_t{pk2(num[nt][0] * y, num[nt][1] * y), pk2(num[nt][2] * y, num[nt][3] * y)};
         }
         // wavefront 1's own rows leave in this chunk, as whole rows
         compiler_fence();
-        if (W == 1) store_rows1<DK, DV, C>(ostage + F::OST, oc + 16 * DV, n - 16, L);
+        if (W == 1) store_rows1<DK, DV, C>(own, oc + 16 * DV, n - 16, L);
 
         // ---- running state: S += K_c^T V_c, z += K_c^T 1 (both wavefronts)
         if (CAUSAL) state_update1<ALL, DK, DV, C>(st, bk, bv, L);
@@ -290,7 +295,8 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
     lds_barrier();
     if (W == 1) {
         const int cl = P.c1 - 1;
-        store_rows1<DK, DV, C>(ostage, o + (bh * T + (size_t)cl * C) * DV, min(C, T - cl * C), L);
+        store_rows1<DK, DV, C>(ostage + ((cl - P.c0) & 1) * F::OST, o + (bh * T + (size_t)cl * C) * DV,
+                               min(C, T - cl * C), L);
     }
     // running state after the segment (the final state when one segment covers
     // the sequence); the two wavefronts hold the same state and split the units

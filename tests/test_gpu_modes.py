@@ -210,9 +210,14 @@ def test_psd_sequential_fullsize_fwd4k(kata):
 
 
 def test_modes_deterministic(kata):
-    q, k, v = gen.orthant_qkv(2, 4, 1500, 32, 64, seed=1100, dtype="bf16")
-    for feature in ("identity", "psd"):
-        for prefix in ("scan", "sequential"):
-            a = run(kata, q, k, v, 128, feature, prefix)
-            b = run(kata, q, k, v, 128, feature, prefix)
-            assert np.array_equal(a, b), (feature, prefix)
+    """Repeated calls agree bit for bit (an output row staged in LDS by one
+    wavefront and stored by another must not be overwritten before it is read)."""
+    for dk in (16, 32):
+        q, k, v = gen.orthant_qkv(2, 4, 1500, dk, 64, seed=1100, dtype="bf16")
+        for feature in ("identity", "psd"):
+            for prefix in ("scan", "sequential"):
+                for C in (64, 128) if dk == 32 or feature == "identity" else (32, 64):
+                    a = run(kata, q, k, v, C, feature, prefix)
+                    for _ in range(3):
+                        assert np.array_equal(a, run(kata, q, k, v, C, feature, prefix)), \
+                            (dk, feature, prefix, C)
