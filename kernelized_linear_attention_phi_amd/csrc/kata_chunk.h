@@ -19,6 +19,18 @@ struct Lane {
           w(threadIdx.x >> 6) {}
 };
 
+// The same lane with its wavefront index as a compile-time constant, for a body
+// specialised to wavefront W: work selected by wavefront (which chunk pieces it
+// copies, which rows it stores) then folds to straight-line code instead of
+// lane-masked branches, and no per-piece address stays live for other
+// wavefronts' pieces.
+template <int W>
+__device__ __forceinline__ Lane as_wave(const Lane& L) {
+    Lane x = L;
+    x.w = W;
+    return x;
+}
+
 // Row (or column) 0 of the "ones" operand = 1 on every K-slot: as the A operand
 // of A.V it turns row 0 of the product into the column sums of the B operand.
 __device__ __forceinline__ u32x4_t ones_op(const Lane& L) {
@@ -52,6 +64,13 @@ __device__ __forceinline__ void lds_barrier() {
 // bf16 rounding midpoint.
 __device__ __forceinline__ float inv_den(float den) {
     return den != 0.0f ? __builtin_amdgcn_rcpf(den) : 0.0f;
+}
+
+// 16-byte global store at base + off (base wavefront-uniform, off the lane's
+// 32-bit byte offset): the address is formed as scalar base plus a 32-bit
+// offset, so no 64-bit per-lane address has to stay live.
+__device__ __forceinline__ void store16(void* base, uint32_t off, const u32x4_t& val) {
+    *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(base) + (size_t)off) = val;
 }
 
 // Value of lane (c16 + d) mod 16 of the same row, for a compile-time d.
@@ -121,7 +140,12 @@ __device__ __forceinline__ u32x4_t v_fragment_tr(const bf16_t* bv, int m, int nt
 // wait for all of them, which serialises the one-chunk-ahead prefetch. Every
 // read of a staged buffer is ordered by the pipeline's own vmcnt wait and
 // barrier instead. The leading s_nop is the wait state between the M0 write the
-// compiler places before the statement and the DMA that reads M0.
+// compiler places before the statement and the DMA that reads M0. The address
+// stays a per-lane 64-bit vector operand: a scalar base would have to be
+// written by v_readfirstlane where the compiler holds it in vector registers,
+// and a vector-ALU write of a scalar register needs more wait states before a
+// memory instruction reads it than the compiler's hazard check gives an
+// inline-assembly operand.
 __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_dst) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_dst) : "memory");
 }

@@ -149,8 +149,8 @@ __global__ __launch_bounds__(64 * NW1) void kata_seg_state1(const bf16_t* __rest
                                                             int G, int NSEG) {
     __shared__ __attribute__((aligned(16))) char lds[Cfg1<DK, DV, C>::LDS_SEG];
     const Lane L;
-    if (L.w == 0) seg_state_body1<0, DK, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L);
-    else seg_state_body1<1, DK, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L);
+    if (L.w == 0) seg_state_body1<0, DK, DV, C>(k, v, rec, lds, T, NC, G, NSEG, as_wave<0>(L));
+    else seg_state_body1<1, DK, DV, C>(k, v, rec, lds, T, NC, G, NSEG, as_wave<1>(L));
 }
 
 // ---- output ------------------------------------------------------------------
@@ -313,8 +313,8 @@ __global__ __launch_bounds__(64 * NW1) void kata_fwd1(const bf16_t* __restrict__
                                                       int G, int NSEG) {
     __shared__ __attribute__((aligned(16))) char lds[Cfg1<DK, DV, C>::LDS_FWD];
     const Lane L;
-    if (L.w == 0) fwd_body1<0, DK, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC, G, NSEG, L);
-    else fwd_body1<1, DK, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC, G, NSEG, L);
+    if (L.w == 0) fwd_body1<0, DK, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC, G, NSEG, as_wave<0>(L));
+    else fwd_body1<1, DK, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC, G, NSEG, as_wave<1>(L));
 }
 
 // ---- record <-> packed (S [d_k, d_v] row-major, z [d_k]) ---------------------

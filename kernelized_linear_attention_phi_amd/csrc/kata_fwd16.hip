@@ -604,8 +604,8 @@ void kata_seg_state16(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v
                       float* __restrict__ segdec, int T, int NC, int G, int NSEG) {
     __shared__ __attribute__((aligned(16))) char lds[3 * ChunkIO<DK, DV, C, NW, NW, DECAY>::BUF];
     const Lane L;
-    if (L.w == 0) seg_state_body<0, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, L);
-    else seg_state_body<1, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, L);
+    if (L.w == 0) seg_state_body<0, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, as_wave<0>(L));
+    else seg_state_body<1, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, as_wave<1>(L));
 }
 
 // The gated variant's larger chunk buffers allow three workgroups per compute
@@ -621,9 +621,9 @@ void kata_fwd16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     __shared__ __attribute__((aligned(16))) char lds[F::NBUF * ChunkIO<DK, DV, C, NW, 1, DECAY>::BUF + F::XB];
     const Lane L;
     if (L.w == 0)
-        fwd_body<0, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G, NSEG, L);
+        fwd_body<0, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G, NSEG, as_wave<0>(L));
     else
-        fwd_body<1, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G, NSEG, L);
+        fwd_body<1, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G, NSEG, as_wave<1>(L));
 }
 
 // Launch arguments shared by every shape: gdec (log-decays, NULL = no gate;

@@ -388,65 +388,55 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
             lds_barrier();
         }
 
-        // ---- inter-chunk term phi(Q).P and q^T Z q for every own query tile at
-        // once: each state operand is read from LDS once and feeds TW products
-        f32x4_t num[F::TW][F::NTV + 1];
-        float di[F::TW];
-        QueryRow Q[F::TW];
-#pragma unroll
-        for (int u = 0; u < F::TW; ++u) {
-            load_query32(bq, own_query_tile<W, F::TT, F::NW>(u), L, Q[u]);
-#pragma unroll
-            for (int nt = 0; nt <= F::NTV; ++nt) num[u][nt] = zero4();
-        }
-        static_for<0, 16>([&](auto pc) {
-            constexpr int p = decltype(pc)::value;
-            u32x4_t fq[F::TW];
-#pragma unroll
-            for (int u = 0; u < F::TW; ++u) fq[u] = lift_query_pair<2 * p>(Q[u], L);
-#pragma unroll
-            for (int nt = 0; nt < F::NTV; ++nt) {
-                const u32x4_t a =
-                    *reinterpret_cast<const u32x4_t*>(sb + ((p * F::NTV + nt) * 64 + L.lane) * 16);
-#pragma unroll
-                for (int u = 0; u < F::TW; ++u) num[u][nt] = mma32(a, fq[u], num[u][nt]);
-            }
-        });
-        {
-            u32x2_t fq[F::TW];
-#pragma unroll
-            for (int u = 0; u < F::TW; ++u) fq[u] = lift_query_mixed(Q[u], L);
-#pragma unroll
-            for (int nt = 0; nt < F::NTV; ++nt) {
-                const u32x2_t a =
-                    *reinterpret_cast<const u32x2_t*>(sb + F::SPAIR + (nt * 64 + L.lane) * 8);
-#pragma unroll
-                for (int u = 0; u < F::TW; ++u) num[u][nt] = mma16_acc32(a, fq[u], num[u][nt]);
-            }
-        }
-        {
-            const char* zb = sb + F::SPAIR + F::S32;
-            const u32x4_t zal = *reinterpret_cast<const u32x4_t*>(zb + L.lane * 16);
-            const u32x4_t zau = *reinterpret_cast<const u32x4_t*>(zb + (64 + L.lane) * 16);
-#pragma unroll
-            for (int u = 0; u < F::TW; ++u) {
-                const f32x4_t zl = mma32(zal, Q[u].zf, zero4());
-                const f32x4_t zu = mma32(zau, Q[u].zf, zero4());
-                float d = 0.0f;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    d = __builtin_fmaf(Q[u].a[r], zl[r], d);
-                    d = __builtin_fmaf(Q[u].b[r], zu[r], d);
-                }
-                d += __shfl_xor(d, 16, 64);
-                d += __shfl_xor(d, 32, 64);
-                di[u] = d;
-            }
-        }
-
+        // ---- per own query tile: inter-chunk term phi(Q).P and q^T Z q over the
+        // published state, intra-chunk term, normalise, store. One tile at a time
+        // keeps one query row and one set of accumulators live (the state
+        // operands are read from LDS once per tile).
+        bf16_t* oc = o + (bh * T + (size_t)c * C) * DV;
 #pragma unroll
         for (int u = 0; u < F::TW; ++u) {
             const int tt = own_query_tile<W, F::TT, F::NW>(u);
+            f32x4_t num[F::NTV + 1];
+#pragma unroll
+            for (int nt = 0; nt <= F::NTV; ++nt) num[nt] = zero4();
+            float di;
+            {
+                QueryRow Q;
+                load_query32(bq, tt, L, Q);
+                static_for<0, 16>([&](auto pc) {
+                    constexpr int p = decltype(pc)::value;
+                    const u32x4_t fq = lift_query_pair<2 * p>(Q, L);
+#pragma unroll
+                    for (int nt = 0; nt < F::NTV; ++nt) {
+                        const u32x4_t a =
+                            *reinterpret_cast<const u32x4_t*>(sb + ((p * F::NTV + nt) * 64 + L.lane) * 16);
+                        num[nt] = mma32(a, fq, num[nt]);
+                    }
+                });
+                {
+                    const u32x2_t fq = lift_query_mixed(Q, L);
+#pragma unroll
+                    for (int nt = 0; nt < F::NTV; ++nt) {
+                        const u32x2_t a =
+                            *reinterpret_cast<const u32x2_t*>(sb + F::SPAIR + (nt * 64 + L.lane) * 8);
+                        num[nt] = mma16_acc32(a, fq, num[nt]);
+                    }
+                }
+                const char* zb = sb + F::SPAIR + F::S32;
+                const u32x4_t zal = *reinterpret_cast<const u32x4_t*>(zb + L.lane * 16);
+                const u32x4_t zau = *reinterpret_cast<const u32x4_t*>(zb + (64 + L.lane) * 16);
+                const f32x4_t zl = mma32(zal, Q.zf, zero4());
+                const f32x4_t zu = mma32(zau, Q.zf, zero4());
+                float d = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    d = __builtin_fmaf(Q.a[r], zl[r], d);
+                    d = __builtin_fmaf(Q.b[r], zu[r], d);
+                }
+                d += __shfl_xor(d, 16, 64);
+                d += __shfl_xor(d, 32, 64);
+                di = d;
+            }
             // ---- intra-chunk term: A = (Q K^T)^2 masked to j <= t, num += A [V | 1]
             if (CAUSAL) {
                 const int t = 16 * tt + L.c16;
@@ -471,40 +461,37 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
                     const u32x4_t at = pack8(w);
 #pragma unroll
                     for (int nt = 0; nt < F::NTV; ++nt)
-                        num[u][nt] = mma32(v_fragment_tr<DV>(bv, m, nt, L), at, num[u][nt]);
-                    num[u][F::NTV] = mma32(ones, at, num[u][F::NTV]);
+                        num[nt] = mma32(v_fragment_tr<DV>(bv, m, nt, L), at, num[nt]);
+                    num[F::NTV] = mma32(ones, at, num[F::NTV]);
                 }
             }
-        }
-
-        // ---- normalise and store: o = num / den
-        bf16_t* oc = o + (bh * T + (size_t)c * C) * DV;
+            // ---- normalise and store: o = num / den
+            {
+                // intra-chunk denominator: row 0 of the ones tile (lane group 0)
+                const float den = __shfl(num[F::NTV][0], L.c16, 64) + di;
+                const float y = inv_den(den);                  // y = 0 gives o = 0
 #pragma unroll
-        for (int u = 0; u < F::TW; ++u) {
-            const int tt = own_query_tile<W, F::TT, F::NW>(u);
-            // intra-chunk denominator: row 0 of the ones tile (lane group 0)
-            const float den = __shfl(num[u][F::NTV][0], L.c16, 64) + di[u];
-            const float y = inv_den(den);                  // y = 0 gives o = 0
+                for (int nt = 0; nt < F::NTV; ++nt) {
+                    float ov[4];
 #pragma unroll
-            for (int nt = 0; nt < F::NTV; ++nt) {
-                float ov[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    ov[r] = num[u][nt][r] * y;
+                    for (int r = 0; r < 4; ++r) {
+                        ov[r] = num[nt][r] * y;
+                    }
+                    *reinterpret_cast<u32x2_t*>(otile + L.c16 * F::OROW + 2 * (16 * nt + 4 * L.g)) =
+                        u32x2_t{pk2(ov[0], ov[1]), pk2(ov[2], ov[3])};
                 }
-                *reinterpret_cast<u32x2_t*>(otile + L.c16 * F::OROW + 2 * (16 * nt + 4 * L.g)) =
-                    u32x2_t{pk2(ov[0], ov[1]), pk2(ov[2], ov[3])};
-            }
-            compiler_fence();                         // staged rows written before read back
+                compiler_fence();                         // staged rows written before read back
 #pragma unroll
-            for (int i = 0; i < (F::OU + 63) / 64; ++i) {
-                const int unit = L.lane + 64 * i;
-                const int row = unit / (F::OU / 16), col = unit % (F::OU / 16);
-                if (unit < F::OU) {
-                    const u32x4_t val = *reinterpret_cast<const u32x4_t*>(otile + row * F::OROW + 16 * col);
-                    if (16 * tt + row < n)
-                        *reinterpret_cast<u32x4_t*>(oc + (size_t)(16 * tt + row) * DV + 8 * col) = val;
+                for (int i = 0; i < (F::OU + 63) / 64; ++i) {
+                    const int unit = L.lane + 64 * i;
+                    const int row = unit / (F::OU / 16), col = unit % (F::OU / 16);
+                    if (unit < F::OU) {
+                        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(otile + row * F::OROW + 16 * col);
+                        if (16 * tt + row < n)
+                            store16(oc, (uint32_t)(((16 * tt + row) * DV + 8 * col) * 2), val);
+                    }
                 }
+                compiler_fence();                         // read back before the next tile's rows
             }
         }
 
@@ -538,7 +525,8 @@ void kata_seg_state32(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v
     __shared__ __attribute__((aligned(16))) char lds[F::LDS_SEG];
     const Lane L;
     by_wave<DV, C>(L.w, [&](auto wc) {
-        seg_state_body32<decltype(wc)::value, DV, C>(k, v, rec, lds, T, NC, G, NSEG, L);
+        seg_state_body32<decltype(wc)::value, DV, C>(k, v, rec, lds, T, NC, G, NSEG,
+                                                     as_wave<decltype(wc)::value>(L));
     });
 }
 
@@ -553,7 +541,7 @@ void kata_fwd32(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const Lane L;
     by_wave<DV, C>(L.w, [&](auto wc) {
         fwd_body32<decltype(wc)::value, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC,
-                                                       G, NSEG, L);
+                                                       G, NSEG, as_wave<decltype(wc)::value>(L));
     });
 }
 
