@@ -219,6 +219,55 @@ def scan_vs_sequential(kata, torch, gen, names, steps, warmup):
     return out
 
 
+def recall_forward(kata, torch, gen, steps, warmup):
+    """The recall-shaped stream workload (B=8, H=4, T=16384, d_k=16, d_v=64,
+    C=64): keys from per-stream codebooks with overwrites, one-hot values."""
+    w = gen.WORKLOADS["recall16k"]
+    to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+    q, k, v = (to(a) for a in gen.recall_stream(w.B, w.H, w.T, w.dk, w.dv, w.seed))
+    ms, wall, phases = time_forward(kata, torch, w, q, k, v, steps, warmup)
+    return {"tokens_per_s": w.B * w.T / (ms * 1e-3), "ms_per_step": ms, "phase_ms": phases,
+            "hbm_frac_alg_whole_step":
+                alg_bytes_per_token_head(w.dk, w.dv) * w.B * w.H * w.T / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+def box_peaks(torch):
+    """Measured yardsticks on this GPU: a large bf16 GEMM through torch and a 1 GiB
+    device-to-device copy (bytes read + written per second)."""
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    ms_mm = time_calls(torch, lambda: torch.mm(a, b), 10, 3)
+    del a, b
+    x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    ms_cp = time_calls(torch, lambda: y.copy_(x), 10, 3)
+    nbytes = 2 * x.numel() * 4
+    del x, y
+    return {"bf16_gemm_tflops": 2 * n ** 3 / (ms_mm * 1e-3) / 1e12,
+            "copy_GBps": nbytes / (ms_cp * 1e-3) / 1e9,
+            "gemm": f"torch.mm bf16 {n}x{n}x{n}", "copy": "1 GiB fp32 device-to-device copy_"}
+
+
+def cpu_chunked(w, q, k, v, budget_s):
+    """The float64 chunked-form oracle (O(T) per head) on head (0, 0) of the
+    workload, on prefixes of 8192 tokens repeated until the budget is spent;
+    tokens/s = token-heads per second / H."""
+    import oracle as O
+    Tp = min(8192, w.T)
+    qq, kk, vv = q[:1, :1, :Tp], k[:1, :1, :Tp], v[:1, :1, :Tp]
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        O.chunked(qq, kk, vv, w.chunk)
+        done += Tp
+    el = time.perf_counter() - t0
+    return {"value": done / (w.H * el), "unit": "tokens/s", "kind": "oracle (chunked form)",
+            "sample": f"float64 chunked form, C={w.chunk}, on the first {Tp} tokens of head (0,0) "
+                      f"of the {w.name} workload, {done // Tp} passes in {el:.1f} s; "
+                      "tokens/s = token-heads/(H*s)"}
+
+
 def cpu_baseline(w, q, k, v, budget_s):
     """The float64 brute-force oracle on a bounded sample of query rows of the
     same workload (head 0, uniformly drawn positions), scaled to tokens/s."""
@@ -328,12 +377,20 @@ def main():
             kata, torch, gen, ("fwd4k", "fwd32k", "fwd131k"), min(args.steps, 10), args.warmup)
         result["parts"]["decay_gate"] = decay_gate(kata, torch, gen, min(args.steps, 10),
                                                    args.warmup)
+        result["parts"]["recall16k"] = recall_forward(kata, torch, gen, min(args.steps, 10),
+                                                      args.warmup)
         dms, dgbs, dbytes = decode_bench(kata, torch)
         result["parts"]["decode"] = {"ms_per_step": dms, "alg_GBps": dgbs,
                                      "hbm_frac": dgbs / PEAK_HBM_GBS, "bytes_per_step": dbytes,
                                      "rows": 2048, "steps": 1024, "hip_graph": True}
+        peaks = box_peaks(torch)
+        result["parts"]["box_peaks"] = peaks
+        result["roofline"]["frac_vs_measured_copy"] = achieved / peaks["copy_GBps"]
+        result["parts"]["fwd32k"]["mfma_util_vs_measured_gemm"] = (
+            result["parts"]["fwd32k"]["alg_tflops"] / peaks["bf16_gemm_tflops"])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, *host_in, args.cpu_budget)
+        result["parts"]["cpu_chunked_oracle"] = cpu_chunked(w, *host_in, args.cpu_budget / 2)
     print(json.dumps(result), flush=True)
 
 
