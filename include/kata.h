@@ -176,9 +176,11 @@ kata_status_t kata_chunked_fwd_ex(const void* q, const void* k, const void* v, v
  *     KATA_PREFIX_SEQUENTIAL (one workgroup per head walks every chunk).
  * Every other argument as for kata_chunked_fwd (S0, z0 stand for earlier tokens
  * and decay with the sequence; S_out, z_out are the decayed final state).
- * Supported: dtype KATA_BF16, d_k = 16, d_v in {16, 32, 64}, chunk in {32, 64};
- * T a multiple of 4 when B*H > 1 (the log-decays of a head are copied 16 bytes at
- * a time); else KATA_EUNSUPPORTED. */
+ * Paths: dtype KATA_BF16 with d_k = 16 and chunk in {32, 64} runs on the matrix
+ * cores (either prefix; T a multiple of 4 when B*H > 1, since the log-decays of
+ * a head are copied 16 bytes at a time); every other supported shape (d_k in
+ * {16, 32}, d_v in {16, 32, 64}, chunk in {16, 32, 64, 128}, fp32 or bf16 inputs)
+ * runs the fp32 VALU path, with KATA_PREFIX_SCAN only. Else KATA_EUNSUPPORTED. */
 size_t kata_chunked_fwd_decay_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                         kata_dtype_t dtype, kata_prefix_t prefix);
 kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v,

@@ -242,7 +242,7 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
     }
     float* S_rec = reinterpret_cast<float*>(ws + plan.S_off);
     float* z_rec = reinterpret_cast<float*>(ws + plan.z_off);
-    if (e == hipSuccess) e = kata::launch_chunk_states_valu(s, k, v, S_rec, z_rec, hs);
+    if (e == hipSuccess) e = kata::launch_chunk_states_valu(s, k, v, nullptr, S_rec, z_rec, nullptr, hs);
     if (e == hipSuccess) e = mark(1);
     if (causal) {
         // exclusive prefix over chunks in place; inclusive total -> final state
@@ -251,7 +251,7 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
         if (e == hipSuccess)
             e = kata::launch_scan_records(z_rec, (int)BH, s.NC, (int)nz, z0, z_out, nullptr, hs);
         if (e == hipSuccess) e = mark(2);
-        if (e == hipSuccess) e = kata::launch_fwd_valu(s, q, k, v, S_rec, z_rec, o, 1, hs);
+        if (e == hipSuccess) e = kata::launch_fwd_valu(s, q, k, v, nullptr, S_rec, z_rec, o, 1, hs);
     } else {
         // total state per head, stored after the per-chunk records
         float* S_tot = S_rec + BH * s.NC * nS;
@@ -261,7 +261,7 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
         if (e == hipSuccess)
             e = kata::launch_scan_records(z_rec, (int)BH, s.NC, (int)nz, z0, z_tot, z_out, hs);
         if (e == hipSuccess) e = mark(2);
-        if (e == hipSuccess) e = kata::launch_fwd_valu(s, q, k, v, S_tot, z_tot, o, 0, hs);
+        if (e == hipSuccess) e = kata::launch_fwd_valu(s, q, k, v, nullptr, S_tot, z_tot, o, 0, hs);
     }
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess) e = mark(4);
@@ -332,7 +332,7 @@ kata_status_t kata_scan_states(const void* k, const void* v, int B, int H, int T
         }
         return KATA_OK;
     }
-    hipError_t e = kata::launch_chunk_states_valu(s, k, v, S_prefix, z_prefix, hs);
+    hipError_t e = kata::launch_chunk_states_valu(s, k, v, nullptr, S_prefix, z_prefix, nullptr, hs);
     if (e == hipSuccess)
         e = kata::launch_scan_records(S_prefix, (int)BH, s.NC, (int)nS, S0, S_out, nullptr, hs);
     if (e == hipSuccess)
@@ -357,22 +357,41 @@ kata_status_t kata_flash_fwd(const void* q, const void* k, const void* v, void* 
 
 // ---- decay gate ----------------------------------------------------------------
 
-static bool decay_plan(const Shape& s, kata_prefix_t prefix, FwdPlan* p, size_t* dec_off) {
-    *p = plan_fwd(s, 1, KATA_FEATURE_PSD, prefix);
-    if (!p->ok || (p->mfma != 16 && (size_t)s.B * s.H * s.NC != 0)) return false;
-    *dec_off = p->bytes;
-    if (p->mfma == 16 && !p->seq) p->bytes += align256((size_t)s.B * s.H * p->NSEG * sizeof(float));
+// Matrix-core path for bf16, d_k = 16, C in {32, 64} (segments, scan or
+// sequential prefix); every other supported shape takes the fp32 VALU path
+// (per-chunk records, scan prefix only).
+struct DecayPlan {
+    FwdPlan fwd;           // matrix-core path
+    bool valu = false;     // VALU path: S_rec | z_rec | cdec, one record per chunk
+    size_t z_off = 0, dec_off = 0, bytes = 0;
+};
+
+static bool decay_plan(const Shape& s, kata_prefix_t prefix, DecayPlan* d) {
+    const size_t BH = (size_t)s.B * s.H;
+    if (kata::mfma16_supported(s)) {
+        d->fwd = plan_fwd(s, 1, KATA_FEATURE_PSD, prefix);
+        if (!d->fwd.ok) return false;
+        d->dec_off = d->fwd.bytes;
+        d->bytes = d->fwd.bytes;
+        if (!d->fwd.seq) d->bytes += align256(BH * d->fwd.NSEG * sizeof(float));
+        return true;
+    }
+    if (prefix != KATA_PREFIX_SCAN) return BH * s.NC == 0;   // nothing to run when empty
+    const size_t nrec = BH * s.NC;
+    d->valu = true;
+    d->z_off = align256(nrec * s.D * s.dv * sizeof(float));
+    d->dec_off = d->z_off + align256(nrec * s.D * sizeof(float));
+    d->bytes = nrec ? d->dec_off + align256(nrec * sizeof(float)) : 0;
     return true;
 }
 
 size_t kata_chunked_fwd_decay_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                         kata_dtype_t dtype, kata_prefix_t prefix) {
     Shape s;
-    FwdPlan p;
-    size_t dec_off;
+    DecayPlan p;
     if (prefix != KATA_PREFIX_SCAN && prefix != KATA_PREFIX_SEQUENTIAL) return 0;
     if (make_shape(B, H, T, d_k, d_v, chunk, dtype, &s) != KATA_OK) return 0;
-    if (!decay_plan(s, prefix, &p, &dec_off)) return 0;
+    if (!decay_plan(s, prefix, &p)) return 0;
     return p.bytes;
 }
 
@@ -395,11 +414,11 @@ kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v
                           (const void*)log_decay, (const void*)S0, (const void*)z0,
                           (const void*)S_out, (const void*)z_out, (const void*)workspace})
         if (p && !aligned16(p)) return KATA_EINVAL;
-    // the per-head log-decay rows are read 16 bytes at a time from T-aligned offsets
-    if (!empty && T % 4 != 0 && H * B > 1) return KATA_EUNSUPPORTED;
-    FwdPlan plan;
-    size_t dec_off;
-    if (!decay_plan(s, prefix, &plan, &dec_off)) return KATA_EUNSUPPORTED;
+    DecayPlan plan;
+    if (!decay_plan(s, prefix, &plan)) return KATA_EUNSUPPORTED;
+    // the matrix-core path reads each head's log-decay row 16 bytes at a time
+    // from T-aligned offsets
+    if (!empty && !plan.valu && T % 4 != 0 && H * B > 1) return KATA_EUNSUPPORTED;
     if (ws_bytes < plan.bytes || (plan.bytes && !workspace)) return KATA_EWORKSPACE;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const size_t nS = (size_t)s.D * s.dv, nz = s.D;
@@ -412,26 +431,44 @@ kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v
         return hip_status(e);
     }
     char* ws = static_cast<char*>(workspace);
-    float* rec = reinterpret_cast<float*>(ws + plan.S_off);
-    float* init = reinterpret_cast<float*>(ws + plan.init_off);
-    float* total = reinterpret_cast<float*>(ws + plan.total_off);
-    const int nrec = (int)BH;
     hipError_t e = hipSuccess;
+    if (plan.valu) {
+        float* S_rec = reinterpret_cast<float*>(ws);
+        float* z_rec = reinterpret_cast<float*>(ws + plan.z_off);
+        float* cdec = reinterpret_cast<float*>(ws + plan.dec_off);
+        e = kata::launch_chunk_states_valu(s, k, v, log_decay, S_rec, z_rec, cdec, hs);
+        // exclusive prefix over chunks under the decayed combine; inclusive
+        // total -> final state
+        if (e == hipSuccess)
+            e = kata::launch_scan_records_decay(S_rec, cdec, (int)BH, s.NC, (int)nS, S0, S_out,
+                                                nullptr, hs);
+        if (e == hipSuccess)
+            e = kata::launch_scan_records_decay(z_rec, cdec, (int)BH, s.NC, (int)nz, z0, z_out,
+                                                nullptr, hs);
+        if (e == hipSuccess)
+            e = kata::launch_fwd_valu(s, q, k, v, log_decay, S_rec, z_rec, o, 1, hs);
+        return hip_status(e);
+    }
+    const FwdPlan& fp = plan.fwd;
+    float* rec = reinterpret_cast<float*>(ws + fp.S_off);
+    float* init = reinterpret_cast<float*>(ws + fp.init_off);
+    float* total = reinterpret_cast<float*>(ws + fp.total_off);
+    const int nrec = (int)BH;
     if (S0) e = kata::launch_record_from_packed16(init, S0, z0, s.dv, nrec, hs);
-    if (plan.seq) {
-        if (!S0 && e == hipSuccess) e = kata::launch_copy_or_zero(init, nullptr, BH * plan.REC, hs);
+    if (fp.seq) {
+        if (!S0 && e == hipSuccess) e = kata::launch_copy_or_zero(init, nullptr, BH * fp.REC, hs);
         if (e == hipSuccess)
             e = kata::launch_fwd16_decay(s, q, k, v, log_decay, init, S_out ? total : nullptr, o,
-                                         plan.G, plan.NSEG, hs);
+                                         fp.G, fp.NSEG, hs);
     } else {
-        float* segdec = reinterpret_cast<float*>(ws + dec_off);
+        float* segdec = reinterpret_cast<float*>(ws + plan.dec_off);
         if (e == hipSuccess)
-            e = kata::launch_seg_state16_decay(s, k, v, log_decay, rec, segdec, plan.G, plan.NSEG, hs);
+            e = kata::launch_seg_state16_decay(s, k, v, log_decay, rec, segdec, fp.G, fp.NSEG, hs);
         if (e == hipSuccess)
-            e = kata::launch_scan_records_decay(rec, segdec, nrec, plan.NSEG, plan.REC,
+            e = kata::launch_scan_records_decay(rec, segdec, nrec, fp.NSEG, fp.REC,
                                                 S0 ? init : nullptr, total, nullptr, hs);
         if (e == hipSuccess)
-            e = kata::launch_fwd16_decay(s, q, k, v, log_decay, rec, nullptr, o, plan.G, plan.NSEG, hs);
+            e = kata::launch_fwd16_decay(s, q, k, v, log_decay, rec, nullptr, o, fp.G, fp.NSEG, hs);
     }
     if (S_out && e == hipSuccess)
         e = kata::launch_record_to_packed16(total, S_out, z_out, s.dv, nrec, hs);

@@ -5,6 +5,14 @@
 // Chunked-state form (KATA explainers, gist.science, technical summary 2.3):
 // chunk c covers positions [cC, min(cC+C, T)); its output is the masked
 // intra-chunk term plus phi(Q_c) times the exclusive prefix of chunk states.
+//
+// Decay gate (gdec != NULL): per-token log-decays g <= 0 scale the state
+// before each token is added (gated linear recurrences, KATA explainers,
+// technical summary 1). With b_t = g_0 + ... + g_t inside the chunk (summed in
+// float64, so that differences stay accurate after a very negative gate), the
+// chunk state weights token j by exp(b_last - b_j) and leaves with the factor
+// exp(b_last) for the scan; query t sees the prefix state scaled by exp(b_t)
+// and key j <= t of its own chunk by exp(b_t - b_j).
 #include "kata_device.h"
 #include "kata_internal.h"
 
@@ -18,14 +26,31 @@ constexpr int kMaxDk = 32;
 constexpr int kMaxDv = 64;
 constexpr int kMaxD = kMaxDk * (kMaxDk + 1) / 2;
 
+// Inclusive sum of the chunk's log-decays in float64: bs[t] = g_0 + ... + g_t
+// for t < n (one thread; at most 128 terms).
+__device__ __forceinline__ void chunk_log_decay(const float* g, int n, double* bs) {
+    if (threadIdx.x == 0) {
+        double acc = 0.0;
+        for (int t = 0; t < n; ++t) {
+            acc += (double)g[t];
+            bs[t] = acc;
+        }
+    }
+}
+
 // S_c = phi(K_c)^T V_c, z_c = phi(K_c)^T 1 for one (head, chunk) per block.
+// With the gate, token j is weighted exp(b_last - b_j) and cdec receives the
+// chunk's factor exp(b_last).
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void chunk_states_valu(
-    const TIn* __restrict__ k, const TIn* __restrict__ v, float* __restrict__ S_rec,
-    float* __restrict__ z_rec, int T, int dk, int dv, int C, int NC) {
+    const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ gdec,
+    float* __restrict__ S_rec, float* __restrict__ z_rec, float* __restrict__ cdec, int T, int dk,
+    int dv, int C, int NC) {
     __shared__ float ks[kMaxC * kMaxDk];
     __shared__ float vs[kMaxC * kMaxDv];
     __shared__ uint32_t pairs[kMaxD];
+    __shared__ double bs[kMaxC];
+    __shared__ float wt[kMaxC];
     const int c = blockIdx.x;
     const size_t bh = blockIdx.y;
     const int D = dk * (dk + 1) / 2;
@@ -36,8 +61,14 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
     for (int e = threadIdx.x; e < n * dk; e += kThreads) ks[e] = io<TIn>::ld(kb, e);
     for (int e = threadIdx.x; e < n * dv; e += kThreads) vs[e] = io<TIn>::ld(vb, e);
     fill_pair_table(pairs, dk, D);
+    if (gdec) chunk_log_decay(gdec + bh * T + t0, n, bs);
     __syncthreads();
     const size_t rec = bh * NC + c;
+    if (gdec) {
+        for (int t = threadIdx.x; t < n; t += kThreads) wt[t] = expf((float)(bs[n - 1] - bs[t]));
+        if (threadIdx.x == 0) cdec[rec] = expf((float)bs[n - 1]);
+        __syncthreads();
+    }
     float* Sr = S_rec + rec * D * dv;
     float* zr = z_rec + rec * D;
     for (int e = threadIdx.x; e < D * dv + D; e += kThreads) {
@@ -48,7 +79,8 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
         const float sc = i == j ? 1.0f : kSqrt2;
         float acc = 0.0f;
         for (int t = 0; t < n; ++t) {
-            const float f = sc * (ks[t * dk + i] * ks[t * dk + j]);
+            float f = sc * (ks[t * dk + i] * ks[t * dk + j]);
+            if (gdec) f *= wt[t];
             acc += is_z ? f : f * vs[t * dv + col];
         }
         if (is_z) zr[p] = acc; else Sr[e] = acc;
@@ -61,12 +93,14 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void fwd_valu(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const float* __restrict__ S_rec, const float* __restrict__ z_rec, TIn* __restrict__ o,
-    int T, int dk, int dv, int C, int NC, int causal) {
+    const float* __restrict__ gdec, const float* __restrict__ S_rec,
+    const float* __restrict__ z_rec, TIn* __restrict__ o, int T, int dk, int dv, int C, int NC,
+    int causal) {
     __shared__ float qs[kMaxC * kMaxDk];
     __shared__ float ks[kMaxC * kMaxDk];
     __shared__ float vs[kMaxC * kMaxDv];
     __shared__ uint32_t pairs[kMaxD];
+    __shared__ double bs[kMaxC];
     const int c = blockIdx.x;
     const size_t bh = blockIdx.y;
     const int D = dk * (dk + 1) / 2;
@@ -81,6 +115,7 @@ __global__ __launch_bounds__(kThreads) void fwd_valu(
     }
     for (int e = threadIdx.x; e < n * dv; e += kThreads) vs[e] = io<TIn>::ld(vb, e);
     fill_pair_table(pairs, dk, D);
+    if (gdec) chunk_log_decay(gdec + bh * T + t0, n, bs);
     __syncthreads();
 
     const size_t rec = causal ? bh * NC + c : bh;
@@ -105,11 +140,18 @@ __global__ __launch_bounds__(kThreads) void fwd_valu(
         for (int u = 0; u < kMaxCols / 2; ++u)
             if (u < ncols && g + u * tpc < dv) num[u] += fq * P[p * dv + g + u * tpc];
     }
+    if (gdec) {                                // the prefix state decays to query t
+        const float e = expf((float)bs[t]);
+        den *= e;
+#pragma unroll
+        for (int u = 0; u < kMaxCols / 2; ++u) num[u] *= e;
+    }
     if (causal) {
         for (int jj = 0; jj <= t; ++jj) {
             float s = 0.0f;
             for (int i = 0; i < dk; ++i) s += qt[i] * ks[jj * dk + i];
-            const float w = s * s;
+            float w = s * s;
+            if (gdec) w *= expf((float)(bs[t] - bs[jj]));
             den += w;
 #pragma unroll
             for (int u = 0; u < kMaxCols / 2; ++u)
@@ -125,28 +167,31 @@ __global__ __launch_bounds__(kThreads) void fwd_valu(
 }  // namespace
 
 hipError_t launch_chunk_states_valu(const Shape& s, const void* k, const void* v,
-                                    float* S_rec, float* z_rec, hipStream_t st) {
+                                    const float* gdec, float* S_rec, float* z_rec, float* cdec,
+                                    hipStream_t st) {
     dim3 grid(s.NC, s.B * s.H);
     if (s.bf16)
         chunk_states_valu<bf16_t><<<grid, kThreads, 0, st>>>(
-            (const bf16_t*)k, (const bf16_t*)v, S_rec, z_rec, s.T, s.dk, s.dv, s.C, s.NC);
+            (const bf16_t*)k, (const bf16_t*)v, gdec, S_rec, z_rec, cdec, s.T, s.dk, s.dv, s.C,
+            s.NC);
     else
         chunk_states_valu<float><<<grid, kThreads, 0, st>>>(
-            (const float*)k, (const float*)v, S_rec, z_rec, s.T, s.dk, s.dv, s.C, s.NC);
+            (const float*)k, (const float*)v, gdec, S_rec, z_rec, cdec, s.T, s.dk, s.dv, s.C,
+            s.NC);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd_valu(const Shape& s, const void* q, const void* k, const void* v,
-                           const float* S_rec, const float* z_rec, void* o, int causal,
-                           hipStream_t st) {
+                           const float* gdec, const float* S_rec, const float* z_rec, void* o,
+                           int causal, hipStream_t st) {
     dim3 grid(s.NC, s.B * s.H);
     if (s.bf16)
         fwd_valu<bf16_t><<<grid, kThreads, 0, st>>>(
-            (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, S_rec, z_rec, (bf16_t*)o,
-            s.T, s.dk, s.dv, s.C, s.NC, causal);
+            (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, gdec, S_rec, z_rec,
+            (bf16_t*)o, s.T, s.dk, s.dv, s.C, s.NC, causal);
     else
         fwd_valu<float><<<grid, kThreads, 0, st>>>(
-            (const float*)q, (const float*)k, (const float*)v, S_rec, z_rec, (float*)o,
+            (const float*)q, (const float*)k, (const float*)v, gdec, S_rec, z_rec, (float*)o,
             s.T, s.dk, s.dv, s.C, s.NC, causal);
     return hipGetLastError();
 }

@@ -122,15 +122,22 @@ def test_decay_rejects_before_launch(L):
     assert fwd_decay(L, g=None) == EINVAL
     assert fwd_decay(L, g=MISALIGNED) == EINVAL
     assert fwd_decay(L, prefix=4) == EINVAL
-    assert fwd_decay(L, dtype=F32) == EUNSUPPORTED
-    assert fwd_decay(L, dk=32, C=128) == EUNSUPPORTED
-    assert fwd_decay(L, C=128) == EUNSUPPORTED
-    assert fwd_decay(L, T=66) == EUNSUPPORTED                 # B*H > 1 needs T % 4 == 0
+    # shapes without a matrix-core path take the VALU path, scan prefix only
+    assert fwd_decay(L, dtype=F32, prefix=SEQUENTIAL) == EUNSUPPORTED
+    assert fwd_decay(L, dk=32, C=128, prefix=SEQUENTIAL) == EUNSUPPORTED
+    assert fwd_decay(L, C=128, prefix=SEQUENTIAL) == EUNSUPPORTED
+    assert fwd_decay(L, dtype=F32, ws_bytes=16) == EWORKSPACE
+    assert fwd_decay(L, dk=12) == EUNSUPPORTED
+    assert fwd_decay(L, T=66) == EUNSUPPORTED                 # matrix-core path: T % 4 == 0
     assert fwd_decay(L, ws_bytes=16) == EWORKSPACE
     assert fwd_decay(L, T=0, q=None, o=None, g=None, ws=None, ws_bytes=0) == OK   # empty
     ws = L.kata_chunked_fwd_decay_workspace
     assert ws(1, 8, 131072, 16, 64, 64, BF16, SCAN) > ws(1, 8, 131072, 16, 64, 64, BF16, SEQUENTIAL) > 0
-    assert ws(1, 8, 4096, 32, 64, 128, BF16, SCAN) == 0
+    # VALU path: per-chunk S and z records and one decay factor per chunk
+    nrec = 8 * 32
+    assert ws(1, 8, 4096, 32, 64, 128, BF16, SCAN) == nrec * 528 * 64 * 4 + nrec * 528 * 4 + nrec * 4
+    assert ws(1, 8, 4096, 32, 64, 128, BF16, SEQUENTIAL) == 0
+    assert ws(1, 8, 4096, 16, 64, 64, F32, SCAN) == 8 * 64 * (136 * 64 * 4 + 136 * 4 + 4)
     dec = L.kata_decode_step_decay
     assert dec(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 16, 64, BF16, None) == EINVAL
     assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 12, 64, BF16, None) == EUNSUPPORTED

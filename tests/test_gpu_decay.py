@@ -2,9 +2,12 @@
 (kata_decode_step_decay) against the float64 decay oracle
 (oracle/decay_oracle.py).
 
-bf16 inputs with fp32 accumulation: outputs within 2e-2 (row-normwise), final
-states within 2e-2 of the state norm (the lifted keys are rounded to bf16 before
-the matrix cores, as in the ungated parity tests); the decode step is fp32
+Matrix-core path (bf16, d_k = 16, C in {32, 64}): fp32 accumulation of bf16
+operands, outputs within 2e-2 (row-normwise), final states within 2e-2 of the
+state norm (the lifted keys are rounded to bf16 before the matrix cores, as in
+the ungated parity tests). VALU path (every other shape): fp32 arithmetic
+throughout, outputs within 1e-4 for fp32 inputs and 2e-2 for bf16 (the bf16
+rounding of the output), states within 1e-4. The decode step is fp32
 arithmetic on the state (1e-5 for fp32 inputs)."""
 import numpy as np
 import pytest
@@ -29,10 +32,10 @@ def kata():
     return k
 
 
-def run(kata, q, k, v, g, C, prefix, S0=None, z0=None, state=False):
+def run(kata, q, k, v, g, C, prefix, S0=None, z0=None, state=False, dtype="bf16"):
     """kata_chunked_fwd_decay with outputs and workspace pre-filled with NaN."""
     import torch
-    qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
     gd = dev(g)
     B, H, T, dk = qd.shape
     dv = vd.shape[-1]
@@ -41,7 +44,8 @@ def run(kata, q, k, v, g, C, prefix, S0=None, z0=None, state=False):
     o = torch.full_like(vd, nan)
     S_out = torch.full((B, H, D, dv), nan, device="cuda") if state else None
     z_out = torch.full((B, H, D), nan, device="cuda") if state else None
-    nbytes = kata.chunked_fwd_decay_workspace(B, H, T, dk, dv, C, 1, prefix)
+    nbytes = kata.chunked_fwd_decay_workspace(B, H, T, dk, dv, C, 1 if dtype == "bf16" else 0,
+                                              prefix)
     ws = torch.full((max(nbytes, 4) // 4,), nan, device="cuda")
     kata.chunked_fwd_decay_into(qd, kd, vd, gd, o, C, ws,
                                 S0=None if S0 is None else dev(S0), z0=None if z0 is None else dev(z0),
@@ -166,6 +170,61 @@ def test_decay_fullsize_fwd131k(kata):
     assert np.all(np.isfinite(o))
     rows = sample_rows(w.T, w.chunk, n_random=12)
     assert row_rel_err(o[:, :, rows], O.decay_brute_force_rows(q, k, v, g, rows)) <= TOL
+
+
+VALU_TOL = {"f32": 1e-4, "bf16": TOL}
+VALU_STATE_TOL = 1e-4
+
+
+@pytest.mark.parametrize("dtype,dk,dv,C", [("f32", 16, 64, 64), ("f32", 32, 16, 32),
+                                           ("bf16", 32, 64, 128), ("bf16", 32, 32, 64),
+                                           ("bf16", 16, 64, 128), ("bf16", 16, 16, 16),
+                                           ("f32", 16, 32, 128)])
+@pytest.mark.parametrize("gmin", [-0.05, -0.5])
+def test_decay_valu_path(kata, dtype, dk, dv, C, gmin):
+    """Shapes without a matrix-core path: several chunks, a ragged tail (T not a
+    multiple of 4 across heads), every output and the final state."""
+    B, H, T = 2, 2, 333
+    q, k, v = gen.gaussian_qkv(B, H, T, dk, dv, seed=1500 + dk + dv + C, dtype=dtype)
+    g = gen.log_decays(B, H, T, seed=1501 + C, gmin=gmin)
+    say(f"decay valu dtype={dtype} dk={dk} dv={dv} C={C} gmin={gmin}")
+    o, S, z = run(kata, q, k, v, g, C, "scan", state=True, dtype=dtype)
+    assert row_rel_err(o, O.decay_brute_force(q, k, v, g)) <= VALU_TOL[dtype]
+    _, S_ref, z_ref = O.decay_recurrent(q, k, v, g)
+    assert state_rel_err(S, S_ref) <= VALU_STATE_TOL and state_rel_err(z, z_ref) <= VALU_STATE_TOL
+
+
+def test_decay_valu_resume_and_reset(kata):
+    """fp32, d_k = 32: an initial state that decays with the sequence, and a
+    reset gate (exp(-1e4) = 0) inside a chunk after which the outputs equal the
+    ungated oracle on the suffix."""
+    T1, T2 = 100, 200
+    q, k, v = gen.gaussian_qkv(1, 2, T1 + T2, 32, 64, seed=1510, dtype="f32")
+    g = gen.log_decays(1, 2, T1 + T2, seed=1511, gmin=-0.1)
+    r = T1 + 70
+    g[:, :, r] = -1e4
+    g[:, :, r + 1:] = 0.0
+    _, S0, z0 = O.decay_recurrent(q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], g[:, :, :T1])
+    say("decay valu resume and reset")
+    o, S, z = run(kata, q[:, :, T1:], k[:, :, T1:], v[:, :, T1:], g[:, :, T1:], 64, "scan",
+                  S0=S0.astype(np.float32), z0=z0.astype(np.float32), state=True, dtype="f32")
+    full = O.decay_brute_force(q, k, v, g)
+    assert row_rel_err(o, full[:, :, T1:]) <= 1e-4
+    assert row_rel_err(o[:, :, r - T1:], O.brute_force(q[:, :, r:], k[:, :, r:], v[:, :, r:])) <= 1e-4
+    _, S_ref, z_ref = O.decay_recurrent(q, k, v, g)
+    assert state_rel_err(S, S_ref) <= VALU_STATE_TOL and state_rel_err(z, z_ref) <= VALU_STATE_TOL
+
+
+def test_decay_valu_zero_gate_matches_ungated(kata):
+    """g = 0 on the VALU path gives the ungated VALU forward within rounding."""
+    import torch
+    q, k, v = gen.gaussian_qkv(1, 2, 300, 32, 64, seed=1520, dtype="f32")
+    g = np.zeros((1, 2, 300), np.float32)
+    say("decay valu zero gate")
+    o = run(kata, q, k, v, g, 128, "scan", dtype="f32")
+    ref = host(kata.chunked_fwd(dev(q, "f32"), dev(k, "f32"), dev(v, "f32"), chunk=128))
+    torch.cuda.synchronize()
+    assert row_rel_err(o, ref) <= 1e-6
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
