@@ -1,6 +1,6 @@
 """Benchmark of the KATA chunked causal forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick [--workload W]]
 
 A step is one pass of the whole hot path over the 131k-token workload (B1 H8
 T131072 d_k16 d_v64 bf16, chunk 64, q/k unit-norm Gaussian rows, v ~ N(0,1)):
@@ -313,6 +313,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--quick", action="store_true", help="primary workload only (for profiling)")
+    ap.add_argument("--workload", default="fwd131k",
+                    help="with --quick: the forward workload to time (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scales HBM counters)")
     args = ap.parse_args()
@@ -341,7 +343,10 @@ def main():
         to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
         return w, (q, k, v), (to(q), to(k), to(v))
 
-    w, host_in, dev_in = load("fwd131k")
+    if args.workload != "fwd131k" and not args.quick:
+        print("--workload only applies with --quick", file=sys.stderr)
+        sys.exit(2)
+    w, host_in, dev_in = load(args.workload)
     ms, wall_ms, phases = time_forward(kata, torch, w, *dev_in, args.steps, args.warmup)
     tok = w.B * w.T
     value = tok / (ms * 1e-3)
@@ -351,7 +356,7 @@ def main():
     out_ms = phases["output"]
     achieved = abytes / (out_ms * 1e-3) / 1e9
     traffic = None
-    if os.path.exists(COUNTERS_FILE):
+    if w.name == "fwd131k" and os.path.exists(COUNTERS_FILE):
         c = json.load(open(COUNTERS_FILE))
         if c.get("kernel_src_sha") == kernel_source_hash():
             traffic = c.get("traffic_bytes_per_launch")
@@ -366,7 +371,7 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "output phase (fused intra+inter forward)",
                      "alg_bytes_per_launch": abytes, "avg_launch_ms": out_ms},
-        "parts": {"fwd131k": {"phase_ms": phases, "wall_ms_per_step": wall_ms,
+        "parts": {w.name: {"phase_ms": phases, "wall_ms_per_step": wall_ms,
                               "mfma_util_alg": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                               "alg_tflops": flops / (ms * 1e-3) / 1e12,
                               "hbm_frac_alg_whole_step": abytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}},
