@@ -294,7 +294,9 @@ def chunked_fwd_decay(q, k, v, log_decay, chunk=64, initial_state=None, return_s
                       prefix="scan"):
     """Decay-gated causal KATA forward: log_decay [B,H,T] fp32 (<= 0) is the
     per-token log forget gate (S_t = exp(g_t) S_{t-1} + phi(k_t) v_t^T, z
-    likewise). bf16, d_k = 16; initial_state / return_state as chunked_fwd."""
+    likewise). Matrix cores for bf16 d_k = 16 with chunk 32 or 64 (either
+    prefix); the fp32 VALU path for every other supported shape (scan prefix).
+    initial_state / return_state as chunked_fwd."""
     _check_dev(q, k, v)
     if q.dim() != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
         raise ValueError("expected q, k [B,H,T,d_k] and v [B,H,T,d_v]")
