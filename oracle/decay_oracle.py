@@ -31,6 +31,11 @@ associative, non-commutative operator
 
     (a1, S1) o (a2, S2) = (a1 a2, a2 S1 + S2)      (1 earlier, 2 later).
 
+Every function also takes feature="identity" for the first-order feature
+phi1(x) = x of the first-order oracle (oracle/first_order_oracle.py): the
+weight of key j for query t is then (q_t . k_j) exp(G_t - G_j) and the state
+is d x d_v; the gate acts the same way.
+
 Parity pins: tests/decay_checks.py. None of these functions is "parity
 unpinned".
 """
@@ -48,11 +53,29 @@ def _cum(g):
     return np.cumsum(np.asarray(g, np.float64), axis=-1)
 
 
+def _lift(x, feature):
+    """The feature map: the PSD lift phi, or the identity."""
+    if feature == "psd":
+        return phi(x)
+    if feature == "identity":
+        return np.asarray(x, np.float64)
+    raise ValueError(feature)
+
+
+def _weight(s, feature):
+    """phi(q).phi(k) from s = q.k: s^2 for the PSD lift, s for the identity."""
+    return s ** 2 if feature == "psd" else s
+
+
+def _dim(d, feature):
+    return phi_dim(d) if feature == "psd" else d
+
+
 # ---------------------------------------------------------------------------
 # Plain definition: weights (q_t . k_j)^2 exp(G_t - G_j), j <= t
 # ---------------------------------------------------------------------------
 
-def decay_brute_force(q, k, v, g, S0=None, z0=None):
+def decay_brute_force(q, k, v, g, S0=None, z0=None, feature="psd"):
     """O(T^2) float64 reference. g [B,H,T] log-decays (<= 0)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -65,19 +88,19 @@ def decay_brute_force(q, k, v, g, S0=None, z0=None):
     for b in range(B):
         for h in range(H):
             diff = np.where(mask, G[b, h][:, None] - G[b, h][None, :], -np.inf)
-            w = (q[b, h] @ k[b, h].T) ** 2 * np.exp(diff)
+            w = _weight(q[b, h] @ k[b, h].T, feature) * np.exp(diff)
             num = w @ v[b, h]
             den = w.sum(axis=1)
             if S0 is not None:
                 e = np.exp(G[b, h])[:, None]
-                fq = phi(q[b, h])
+                fq = _lift(q[b, h], feature)
                 num = num + e * (fq @ np.asarray(S0[b, h], np.float64))
                 den = den + e[:, 0] * (fq @ np.asarray(z0[b, h], np.float64))
             o[b, h] = _safe_ratio(num, den)
     return o
 
 
-def decay_brute_force_rows(q, k, v, g, rows):
+def decay_brute_force_rows(q, k, v, g, rows, feature="psd"):
     """The same definition for the query positions `rows` only (every b, h):
     O(T) per row, for spot checks of long sequences. Returns [B,H,len(rows),dv]."""
     q = np.asarray(q, np.float64)
@@ -89,7 +112,7 @@ def decay_brute_force_rows(q, k, v, g, rows):
     for b in range(B):
         for h in range(H):
             for i, t in enumerate(rows):
-                w = (k[b, h, :t + 1] @ q[b, h, t]) ** 2 * np.exp(G[b, h, t] - G[b, h, :t + 1])
+                w = _weight(k[b, h, :t + 1] @ q[b, h, t], feature) * np.exp(G[b, h, t] - G[b, h, :t + 1])
                 den = w.sum()
                 o[b, h, i] = (w @ v[b, h, :t + 1]) / den if den != 0.0 else 0.0
     return o
@@ -99,7 +122,7 @@ def decay_brute_force_rows(q, k, v, g, rows):
 # Recurrent form: decay the state, add the token, read
 # ---------------------------------------------------------------------------
 
-def decay_recurrent(q, k, v, g, S0=None, z0=None):
+def decay_recurrent(q, k, v, g, S0=None, z0=None, feature="psd"):
     """Returns (o [B,H,T,dv], S_T [B,H,D,dv], z_T [B,H,D])."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -107,11 +130,11 @@ def decay_recurrent(q, k, v, g, S0=None, z0=None):
     g = np.asarray(g, np.float64)
     B, H, T, d = q.shape
     dv = v.shape[-1]
-    D = phi_dim(d)
+    D = _dim(d, feature)
     S = np.zeros((B, H, D, dv)) if S0 is None else np.array(S0, np.float64)
     z = np.zeros((B, H, D)) if z0 is None else np.array(z0, np.float64)
     o = np.zeros((B, H, T, dv))
-    fq, fk = phi(q), phi(k)
+    fq, fk = _lift(q, feature), _lift(k, feature)
     for t in range(T):
         gam = np.exp(g[:, :, t])
         S = gam[:, :, None, None] * S + fk[:, :, t, :, None] * v[:, :, t, None, :]
@@ -122,12 +145,12 @@ def decay_recurrent(q, k, v, g, S0=None, z0=None):
     return o, S, z
 
 
-def decay_decode_step(q, k, v, g, S, z):
+def decay_decode_step(q, k, v, g, S, z, feature="psd"):
     """One decode step for N rows: q, k [N,d], v [N,dv], g [N], S [N,D,dv],
     z [N,D]. Returns (o, S', z') with S' = exp(g) S + phi(k) v^T."""
     gam = np.exp(np.asarray(g, np.float64))
-    fk = phi(np.asarray(k, np.float64))
-    fq = phi(np.asarray(q, np.float64))
+    fk = _lift(k, feature)
+    fq = _lift(q, feature)
     S2 = gam[:, None, None] * np.asarray(S, np.float64) + fk[:, :, None] * np.asarray(v, np.float64)[:, None, :]
     z2 = gam[:, None] * np.asarray(z, np.float64) + fk
     num = np.einsum("np,npv->nv", fq, S2)
@@ -147,16 +170,16 @@ def decay_combine(x, y):
     return a1 * a2, a2[..., None, None] * S1 + S2, a2[..., None] * z1 + z2
 
 
-def _chunk_state(k, v, g):
+def _chunk_state(k, v, g, feature):
     """(a, S, z) of one span: a = exp(sum g), S = sum_j exp(G_last - G_j) phi(k_j) v_j^T."""
     G = _cum(g)
     wgt = np.exp(G[..., -1:] - G)                              # [B,H,n]
-    fk = phi(k) * wgt[..., None]
+    fk = _lift(k, feature) * wgt[..., None]
     S = np.einsum("bhtp,bhtn->bhpn", fk, np.asarray(v, np.float64))
     return np.exp(G[..., -1]), S, fk.sum(axis=2)
 
 
-def decay_prefix_states(k, v, g, C: int, S0=None, z0=None):
+def decay_prefix_states(k, v, g, C: int, S0=None, z0=None, feature="psd"):
     """Exclusive prefixes (P_c, Z_c) of the chunk states under decay_combine,
     computed by a Hillis-Steele (log-depth) inclusive scan over chunks, shifted
     by one and started from (S0, z0). Returns (P [B,H,NC,D,dv], Z [B,H,NC,D],
@@ -166,10 +189,10 @@ def decay_prefix_states(k, v, g, C: int, S0=None, z0=None):
     g = np.asarray(g, np.float64)
     B, H, T, d = k.shape
     dv = v.shape[-1]
-    D = phi_dim(d)
+    D = _dim(d, feature)
     NC = -(-T // C)
     items = [_chunk_state(k[:, :, c * C:(c + 1) * C], v[:, :, c * C:(c + 1) * C],
-                          g[:, :, c * C:(c + 1) * C]) for c in range(NC)]
+                          g[:, :, c * C:(c + 1) * C], feature) for c in range(NC)]
     init = (np.ones((B, H)), np.zeros((B, H, D, dv)) if S0 is None else np.array(S0, np.float64),
             np.zeros((B, H, D)) if z0 is None else np.array(z0, np.float64))
     seq = [init] + items                                      # exclusive: identity-like start
@@ -182,17 +205,17 @@ def decay_prefix_states(k, v, g, C: int, S0=None, z0=None):
     return P, Z, seq[NC][1], seq[NC][2]
 
 
-def decay_chunked(q, k, v, g, C: int, S0=None, z0=None):
+def decay_chunked(q, k, v, g, C: int, S0=None, z0=None, feature="psd"):
     """Chunk c: num = A V_c + exp(b_t) phi(Q_c) P_c, den = A 1 + exp(b_t) phi(Q_c) Z_c,
-    A_tj = (q_t . k_j)^2 exp(b_t - b_j) masked to j <= t, b the cumulative log-decay
-    inside the chunk. Returns (o, S_T, z_T)."""
+    A_tj = (q_t . k_j)^2 exp(b_t - b_j) masked to j <= t (q_t . k_j for the
+    identity), b the cumulative log-decay inside the chunk. Returns (o, S_T, z_T)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     g = np.asarray(g, np.float64)
     B, H, T, d = q.shape
     o = np.zeros((B, H, T, v.shape[-1]))
-    P, Z, S_T, z_T = decay_prefix_states(k, v, g, C, S0, z0)
+    P, Z, S_T, z_T = decay_prefix_states(k, v, g, C, S0, z0, feature)
     for c in range(P.shape[2]):
         sl = slice(c * C, min(T, (c + 1) * C))
         Qc, Kc, Vc = q[:, :, sl], k[:, :, sl], v[:, :, sl]
@@ -200,9 +223,9 @@ def decay_chunked(q, k, v, g, C: int, S0=None, z0=None):
         n = Qc.shape[2]
         tri = np.tril(np.ones((n, n), dtype=bool))
         diff = np.where(tri, b[..., :, None] - b[..., None, :], -np.inf)
-        A = np.einsum("bhtd,bhjd->bhtj", Qc, Kc) ** 2 * np.exp(diff)
+        A = _weight(np.einsum("bhtd,bhjd->bhtj", Qc, Kc), feature) * np.exp(diff)
         e = np.exp(b)
-        fq = phi(Qc)
+        fq = _lift(Qc, feature)
         num = np.einsum("bhtj,bhjn->bhtn", A, Vc) + e[..., None] * np.einsum("bhtp,bhpn->bhtn", fq, P[:, :, c])
         den = A.sum(axis=-1) + e * np.einsum("bhtp,bhp->bht", fq, Z[:, :, c])
         o[:, :, sl] = _safe_ratio(num, den)

@@ -18,6 +18,10 @@ checks against copies with a planted mistake.
                     equal the ungated brute force on the suffix from s
   convexity         outputs lie in the hull of the visible values
   decode_chain      repeated decode steps = recurrence
+  identity_*        the same laws with the first-order feature phi1(x) = x:
+                    g = 0 gives the first-order oracle (brute force and state
+                    totals), recurrence = brute force, chunk invariance, the
+                    EMA closed form, the reset, the decode chain
 """
 from __future__ import annotations
 
@@ -182,8 +186,100 @@ def decode_chain(O):
     _close(z, z_ref[0])
 
 
+ID = "identity"
+
+
+def _ocase(seed, **kw):
+    """_case with queries and keys in the nonnegative orthant (the first-order
+    feature's cone: weights q.k >= 0, denominators away from 0)."""
+    q, k, v, g = _case(seed, **kw)
+    return np.abs(q), np.abs(k), v, g
+
+
+def _fo_state0(O, seed, B=2, H=2, d=3, dv=4):
+    r = _rng(seed)
+    kp, vp = np.abs(r.standard_normal((B, H, 6, d))), r.standard_normal((B, H, 6, dv))
+    return O.fo_state_from_tokens(kp, vp)
+
+
+def identity_no_decay(O):
+    q, k, v, g = _ocase(21)
+    g[:] = 0.0
+    S0, z0 = _fo_state0(O, 22)
+    _close(O.decay_brute_force(q, k, v, g, feature=ID), O.fo_brute_force(q, k, v))
+    _close(O.decay_brute_force(q, k, v, g, S0=S0, z0=z0, feature=ID),
+           O.fo_brute_force(q, k, v, S0=S0, z0=z0))
+    _, _, S, z = O.decay_prefix_states(k, v, g, 4, feature=ID)
+    S2, z2 = O.fo_state_from_tokens(k, v)
+    _close(S, S2)
+    _close(z, z2)
+
+
+def identity_recurrent_eq(O):
+    q, k, v, g = _ocase(23)
+    S0, z0 = _fo_state0(O, 24)
+    o, S, z = O.decay_recurrent(q, k, v, g, S0=S0, z0=z0, feature=ID)
+    _close(o, O.decay_brute_force(q, k, v, g, S0=S0, z0=z0, feature=ID), 1e-9)
+    rows = [0, 5, 16]
+    _close(O.decay_brute_force_rows(q, k, v, g, rows, feature=ID),
+           O.decay_brute_force(q, k, v, g, feature=ID)[:, :, rows])
+
+
+def identity_chunk_invariance(O):
+    q, k, v, g = _ocase(25, T=23)
+    S0, z0 = _fo_state0(O, 26)
+    ref = O.decay_brute_force(q, k, v, g, S0=S0, z0=z0, feature=ID)
+    _, S_ref, z_ref = O.decay_recurrent(q, k, v, g, S0=S0, z0=z0, feature=ID)
+    for C in (1, 3, 8, 23):
+        o, S, z = O.decay_chunked(q, k, v, g, C, S0=S0, z0=z0, feature=ID)
+        _close(o, ref, 1e-9)
+        _close(S, S_ref, 1e-10)
+        _close(z, z_ref, 1e-10)
+
+
+def identity_ema(O):
+    T, dv, gam = 12, 3, 0.7
+    v = _rng(27).standard_normal((1, 1, T, dv))
+    q = np.zeros((1, 1, T, 2))
+    k = np.zeros((1, 1, T, 2))
+    q[..., 1] = 1.0
+    k[..., 1] = 1.0
+    g = np.full((1, 1, T), np.log(gam))
+    want = np.zeros((1, 1, T, dv))
+    for t in range(T):
+        wts = np.array([gam ** (t - j) for j in range(t + 1)])
+        want[0, 0, t] = (wts[:, None] * v[0, 0, :t + 1]).sum(axis=0) / wts.sum()
+    for o in (O.decay_brute_force(q, k, v, g, feature=ID), O.decay_recurrent(q, k, v, g, feature=ID)[0],
+              O.decay_chunked(q, k, v, g, 5, feature=ID)[0]):
+        _close(o, want, 1e-12)
+
+
+def identity_reset(O):
+    q, k, v, g = _ocase(28, T=20)
+    s = 9
+    g[:, :, s] = -1e4
+    g[:, :, s + 1:] = 0.0
+    want = O.fo_brute_force(q[:, :, s:], k[:, :, s:], v[:, :, s:])
+    for o in (O.decay_brute_force(q, k, v, g, feature=ID), O.decay_recurrent(q, k, v, g, feature=ID)[0],
+              O.decay_chunked(q, k, v, g, 4, feature=ID)[0]):
+        _close(o[:, :, s:], want, 1e-10)
+
+
+def identity_decode_chain(O):
+    q, k, v, g = _ocase(29, B=1, H=3, T=10)
+    o_ref, S_ref, z_ref = O.decay_recurrent(q, k, v, g, feature=ID)
+    S = np.zeros((3, q.shape[-1], v.shape[-1]))
+    z = np.zeros((3, q.shape[-1]))
+    for t in range(q.shape[2]):
+        o, S, z = O.decay_decode_step(q[0, :, t], k[0, :, t], v[0, :, t], g[0, :, t], S, z, feature=ID)
+        _close(o, o_ref[0, :, t], 1e-10)
+    _close(S, S_ref[0])
+    _close(z, z_ref[0])
+
+
 ALL = [no_decay, golden_worked, rows_eq, recurrent_eq, chunk_invariance, combine_laws, ema_closed_form,
-       reset, convexity, decode_chain]
+       reset, convexity, decode_chain, identity_no_decay, identity_recurrent_eq,
+       identity_chunk_invariance, identity_ema, identity_reset, identity_decode_chain]
 
 
 def failures(O):

@@ -14,6 +14,8 @@ SRC = inspect.getsource(real)
 
 def _ns(mod):
     return types.SimpleNamespace(brute_force=oracle.brute_force, prefix_states=oracle.prefix_states,
+                                 fo_brute_force=oracle.fo_brute_force,
+                                 fo_state_from_tokens=oracle.fo_state_from_tokens,
                                  **{n: getattr(mod, n) for n in real.__all__})
 
 
@@ -34,6 +36,9 @@ MUTATIONS = {
     "decode_no_decay": ("    gam = np.exp(np.asarray(g, np.float64))\n", "    gam = np.ones_like(np.asarray(g, np.float64))\n"),
     "rows_weight_sign": ("np.exp(G[b, h, t] - G[b, h, :t + 1])", "np.exp(G[b, h, :t + 1] - G[b, h, t])"),
     "intra_mask_strict": ("        tri = np.tril(np.ones((n, n), dtype=bool))", "        tri = np.tril(np.ones((n, n), dtype=bool), -1)"),
+    "identity_weight_squared": ('    return s ** 2 if feature == "psd" else s', "    return s ** 2"),
+    "identity_lift_scaled": ('    if feature == "identity":\n        return np.asarray(x, np.float64)',
+                             '    if feature == "identity":\n        return 2.0 * np.asarray(x, np.float64)'),
 }
 
 
