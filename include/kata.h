@@ -148,11 +148,11 @@ size_t kata_chunked_fwd_ex_workspace(int B, int H, int T, int d_k, int d_v, int 
 /* kata_chunked_fwd with a choice of feature map and prefix method; every other
  * argument as there, with the state dimension of `feature` in S0, z0, S_out,
  * z_out. KATA_FEATURE_PSD with KATA_PREFIX_SCAN is kata_chunked_fwd.
- * KATA_FEATURE_IDENTITY and KATA_PREFIX_SEQUENTIAL need dtype KATA_BF16, and
- * KATA_FEATURE_IDENTITY needs chunk in {32, 64, 128} (else KATA_EUNSUPPORTED);
- * KATA_PREFIX_SEQUENTIAL with KATA_FEATURE_PSD needs a shape of the bf16
- * matrix-core path (d_k = 16 with chunk 32 or 64, d_k = 32 with chunk 64 or
- * 128). */
+ * KATA_PREFIX_SEQUENTIAL needs a shape of a bf16 matrix-core path (else
+ * KATA_EUNSUPPORTED): for KATA_FEATURE_PSD d_k = 16 with chunk 32 or 64, d_k = 32
+ * with chunk 64 or 128; for KATA_FEATURE_IDENTITY chunk 32, 64 or 128. Every
+ * other supported shape (fp32 inputs, or chunk 16 with the identity feature)
+ * runs the fp32 VALU path with KATA_PREFIX_SCAN. */
 kata_status_t kata_chunked_fwd_ex(const void* q, const void* k, const void* v, void* o,
                                   int B, int H, int T, int d_k, int d_v, int chunk, int causal,
                                   kata_dtype_t dtype, kata_feature_t feature,
@@ -190,6 +190,22 @@ kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v
                                      const float* S0, const float* z0,
                                      float* S_out, float* z_out,
                                      void* workspace, size_t ws_bytes, void* stream);
+
+/* kata_chunked_fwd_decay with a choice of feature map: KATA_FEATURE_PSD is
+ * kata_chunked_fwd_decay; KATA_FEATURE_IDENTITY gates the first-order feature
+ * phi1(x) = x (weights (q_t.k_j) exp(g_{j+1} + ... + g_t), state d_k x d_v in
+ * S0, z0, S_out, z_out), on the fp32 VALU path with KATA_PREFIX_SCAN only.
+ * Every other argument, error and layout as there. */
+size_t kata_chunked_fwd_decay_ex_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                           kata_dtype_t dtype, kata_feature_t feature,
+                                           kata_prefix_t prefix);
+kata_status_t kata_chunked_fwd_decay_ex(const void* q, const void* k, const void* v,
+                                        const float* log_decay, void* o, int B, int H, int T,
+                                        int d_k, int d_v, int chunk, kata_dtype_t dtype,
+                                        kata_feature_t feature, kata_prefix_t prefix,
+                                        const float* S0, const float* z0, float* S_out,
+                                        float* z_out, void* workspace, size_t ws_bytes,
+                                        void* stream);
 
 /* kata_decode_step with the decay gate above: log_decay [N] (fp32, device), and
  * S = exp(g) S + phi(k) v^T, z = exp(g) z + phi(k) before the read. Same shapes,

@@ -65,6 +65,11 @@ def lib() -> ctypes.CDLL:
         L.kata_chunked_fwd_decay.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                              vp, vp, vp, vp, vp, sz, vp]
         L.kata_chunked_fwd_decay.restype = i
+        L.kata_chunked_fwd_decay_ex_workspace.argtypes = [i, i, i, i, i, i, i, i, i]
+        L.kata_chunked_fwd_decay_ex_workspace.restype = sz
+        L.kata_chunked_fwd_decay_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i,
+                                                vp, vp, vp, vp, vp, sz, vp]
+        L.kata_chunked_fwd_decay_ex.restype = i
         L.kata_decode_step_decay.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
         L.kata_decode_step_decay.restype = i
         L.kata_scan_states_workspace.argtypes = [i, i, i, i, i, i, i]
@@ -269,33 +274,43 @@ def decode_step(q, k, v, S, z, out=None):
 
 # ---- decay gate ------------------------------------------------------------------
 
-def chunked_fwd_decay_workspace(B, H, T, dk, dv, chunk, dtype_code, prefix="scan") -> int:
-    return lib().kata_chunked_fwd_decay_workspace(B, H, T, dk, dv, chunk, dtype_code,
-                                                  _modes("psd", prefix)[1])
+def chunked_fwd_decay_workspace(B, H, T, dk, dv, chunk, dtype_code, prefix="scan",
+                                feature="psd") -> int:
+    f, pf = _modes(feature, prefix)
+    if f == 0:
+        return lib().kata_chunked_fwd_decay_workspace(B, H, T, dk, dv, chunk, dtype_code, pf)
+    return lib().kata_chunked_fwd_decay_ex_workspace(B, H, T, dk, dv, chunk, dtype_code, f, pf)
 
 
 def chunked_fwd_decay_into(q, k, v, log_decay, o, chunk, workspace, S0=None, z0=None, S_out=None,
-                           z_out=None, prefix="scan"):
-    """Raw decay-gated call (kata_chunked_fwd_decay); every buffer preallocated."""
+                           z_out=None, prefix="scan", feature="psd"):
+    """Raw decay-gated call (kata_chunked_fwd_decay, or kata_chunked_fwd_decay_ex
+    for the identity feature); every buffer preallocated."""
     _check_dev(log_decay)
     if log_decay.dtype != torch.float32:
         raise TypeError("log_decay is float32 [B,H,T]")
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().kata_chunked_fwd_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(o), B, H, T,
-                                      dk, dv, chunk, _dtype_code(q), _modes("psd", prefix)[1],
-                                      _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out),
-                                      _ptr(workspace), ws_bytes, _stream())
-    _raise(st, "kata_chunked_fwd_decay")
+    f, pf = _modes(feature, prefix)
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(o), B, H, T, dk, dv, chunk,
+            _dtype_code(q))
+    tail = (_ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(workspace), ws_bytes, _stream())
+    if f == 0:
+        st = lib().kata_chunked_fwd_decay(*head, pf, *tail)
+        _raise(st, "kata_chunked_fwd_decay")
+    else:
+        st = lib().kata_chunked_fwd_decay_ex(*head, f, pf, *tail)
+        _raise(st, "kata_chunked_fwd_decay_ex")
 
 
 def chunked_fwd_decay(q, k, v, log_decay, chunk=64, initial_state=None, return_state=False,
-                      prefix="scan"):
+                      prefix="scan", feature="psd"):
     """Decay-gated causal KATA forward: log_decay [B,H,T] fp32 (<= 0) is the
     per-token log forget gate (S_t = exp(g_t) S_{t-1} + phi(k_t) v_t^T, z
     likewise). Matrix cores for bf16 d_k = 16 with chunk 32 or 64 (either
     prefix); the fp32 VALU path for every other supported shape (scan prefix).
+    feature="identity" gates the first-order feature (VALU path).
     initial_state / return_state as chunked_fwd."""
     _check_dev(q, k, v)
     if q.dim() != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
@@ -304,7 +319,7 @@ def chunked_fwd_decay(q, k, v, log_decay, chunk=64, initial_state=None, return_s
     dv = v.shape[-1]
     if tuple(log_decay.shape) != (B, H, T):
         raise ValueError("log_decay must be [B,H,T]")
-    D = phi_dim(dk)
+    D = feature_dim(dk, feature)
     S0 = z0 = S_out = z_out = None
     if initial_state is not None:
         S0, z0 = initial_state
@@ -312,10 +327,10 @@ def chunked_fwd_decay(q, k, v, log_decay, chunk=64, initial_state=None, return_s
         S_out = torch.empty((B, H, D, dv), dtype=torch.float32, device=q.device)
         z_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
     o = torch.empty_like(v)
-    nbytes = chunked_fwd_decay_workspace(B, H, T, dk, dv, chunk, _dtype_code(q), prefix)
+    nbytes = chunked_fwd_decay_workspace(B, H, T, dk, dv, chunk, _dtype_code(q), prefix, feature)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if nbytes else None
     chunked_fwd_decay_into(q, k, v, log_decay.contiguous(), o, chunk, ws, S0, z0, S_out, z_out,
-                           prefix=prefix)
+                           prefix=prefix, feature=feature)
     return (o, (S_out, z_out)) if return_state else o
 
 

@@ -68,8 +68,9 @@ FwdPlan plan_fwd(const Shape& s, int causal, kata_feature_t f = KATA_FEATURE_PSD
                  kata_prefix_t pf = KATA_PREFIX_SCAN) {
     FwdPlan p{};
     if (f == KATA_FEATURE_IDENTITY) {
-        p.ok = kata::first_supported(s);
-        p.mfma = 1;
+        // matrix cores for the bf16 shapes, else the fp32 VALU path (scan prefix)
+        p.mfma = kata::first_supported(s) ? 1 : 0;
+        p.ok = p.mfma != 0 || pf == KATA_PREFIX_SCAN;
     } else {
         p.mfma = kata::mfma16_supported(s) ? 16 : kata::mfma32_supported(s) ? 32 : 0;
         p.ok = p.mfma != 0 || pf == KATA_PREFIX_SCAN;
@@ -242,7 +243,9 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
     }
     float* S_rec = reinterpret_cast<float*>(ws + plan.S_off);
     float* z_rec = reinterpret_cast<float*>(ws + plan.z_off);
-    if (e == hipSuccess) e = kata::launch_chunk_states_valu(s, k, v, nullptr, S_rec, z_rec, nullptr, hs);
+    const int ident = feature == KATA_FEATURE_IDENTITY;
+    if (e == hipSuccess)
+        e = kata::launch_chunk_states_valu(s, k, v, nullptr, S_rec, z_rec, nullptr, ident, hs);
     if (e == hipSuccess) e = mark(1);
     if (causal) {
         // exclusive prefix over chunks in place; inclusive total -> final state
@@ -251,7 +254,7 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
         if (e == hipSuccess)
             e = kata::launch_scan_records(z_rec, (int)BH, s.NC, (int)nz, z0, z_out, nullptr, hs);
         if (e == hipSuccess) e = mark(2);
-        if (e == hipSuccess) e = kata::launch_fwd_valu(s, q, k, v, nullptr, S_rec, z_rec, o, 1, hs);
+        if (e == hipSuccess) e = kata::launch_fwd_valu(s, q, k, v, nullptr, S_rec, z_rec, o, 1, ident, hs);
     } else {
         // total state per head, stored after the per-chunk records
         float* S_tot = S_rec + BH * s.NC * nS;
@@ -261,7 +264,7 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
         if (e == hipSuccess)
             e = kata::launch_scan_records(z_rec, (int)BH, s.NC, (int)nz, z0, z_tot, z_out, hs);
         if (e == hipSuccess) e = mark(2);
-        if (e == hipSuccess) e = kata::launch_fwd_valu(s, q, k, v, nullptr, S_tot, z_tot, o, 0, hs);
+        if (e == hipSuccess) e = kata::launch_fwd_valu(s, q, k, v, nullptr, S_tot, z_tot, o, 0, ident, hs);
     }
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess) e = mark(4);
@@ -332,7 +335,7 @@ kata_status_t kata_scan_states(const void* k, const void* v, int B, int H, int T
         }
         return KATA_OK;
     }
-    hipError_t e = kata::launch_chunk_states_valu(s, k, v, nullptr, S_prefix, z_prefix, nullptr, hs);
+    hipError_t e = kata::launch_chunk_states_valu(s, k, v, nullptr, S_prefix, z_prefix, nullptr, 0, hs);
     if (e == hipSuccess)
         e = kata::launch_scan_records(S_prefix, (int)BH, s.NC, (int)nS, S0, S_out, nullptr, hs);
     if (e == hipSuccess)
@@ -357,18 +360,19 @@ kata_status_t kata_flash_fwd(const void* q, const void* k, const void* v, void* 
 
 // ---- decay gate ----------------------------------------------------------------
 
-// Matrix-core path for bf16, d_k = 16, C in {32, 64} (segments, scan or
-// sequential prefix); every other supported shape takes the fp32 VALU path
-// (per-chunk records, scan prefix only).
+// Matrix-core path for the PSD lift with bf16, d_k = 16, C in {32, 64}
+// (segments, scan or sequential prefix); every other supported shape, and the
+// identity feature, takes the fp32 VALU path (per-chunk records, scan prefix
+// only).
 struct DecayPlan {
     FwdPlan fwd;           // matrix-core path
     bool valu = false;     // VALU path: S_rec | z_rec | cdec, one record per chunk
     size_t z_off = 0, dec_off = 0, bytes = 0;
 };
 
-static bool decay_plan(const Shape& s, kata_prefix_t prefix, DecayPlan* d) {
+static bool decay_plan(const Shape& s, kata_feature_t f, kata_prefix_t prefix, DecayPlan* d) {
     const size_t BH = (size_t)s.B * s.H;
-    if (kata::mfma16_supported(s)) {
+    if (f == KATA_FEATURE_PSD && kata::mfma16_supported(s)) {
         d->fwd = plan_fwd(s, 1, KATA_FEATURE_PSD, prefix);
         if (!d->fwd.ok) return false;
         d->dec_off = d->fwd.bytes;
@@ -385,25 +389,33 @@ static bool decay_plan(const Shape& s, kata_prefix_t prefix, DecayPlan* d) {
     return true;
 }
 
-size_t kata_chunked_fwd_decay_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
-                                        kata_dtype_t dtype, kata_prefix_t prefix) {
+size_t kata_chunked_fwd_decay_ex_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                           kata_dtype_t dtype, kata_feature_t feature,
+                                           kata_prefix_t prefix) {
     Shape s;
     DecayPlan p;
-    if (prefix != KATA_PREFIX_SCAN && prefix != KATA_PREFIX_SEQUENTIAL) return 0;
-    if (make_shape(B, H, T, d_k, d_v, chunk, dtype, &s) != KATA_OK) return 0;
-    if (!decay_plan(s, prefix, &p)) return 0;
+    if (!valid_modes(feature, prefix)) return 0;
+    if (make_shape(B, H, T, d_k, d_v, chunk, dtype, &s, feature) != KATA_OK) return 0;
+    if (!decay_plan(s, feature, prefix, &p)) return 0;
     return p.bytes;
 }
 
-kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v,
-                                     const float* log_decay, void* o, int B, int H, int T,
-                                     int d_k, int d_v, int chunk, kata_dtype_t dtype,
-                                     kata_prefix_t prefix, const float* S0, const float* z0,
-                                     float* S_out, float* z_out, void* workspace, size_t ws_bytes,
-                                     void* stream) {
-    if (prefix != KATA_PREFIX_SCAN && prefix != KATA_PREFIX_SEQUENTIAL) return KATA_EINVAL;
+size_t kata_chunked_fwd_decay_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                        kata_dtype_t dtype, kata_prefix_t prefix) {
+    return kata_chunked_fwd_decay_ex_workspace(B, H, T, d_k, d_v, chunk, dtype, KATA_FEATURE_PSD,
+                                               prefix);
+}
+
+kata_status_t kata_chunked_fwd_decay_ex(const void* q, const void* k, const void* v,
+                                        const float* log_decay, void* o, int B, int H, int T,
+                                        int d_k, int d_v, int chunk, kata_dtype_t dtype,
+                                        kata_feature_t feature, kata_prefix_t prefix,
+                                        const float* S0, const float* z0, float* S_out,
+                                        float* z_out, void* workspace, size_t ws_bytes,
+                                        void* stream) {
+    if (!valid_modes(feature, prefix)) return KATA_EINVAL;
     Shape s;
-    kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s);
+    kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s, feature);
     if (st != KATA_OK) return st;
     if ((S0 == nullptr) != (z0 == nullptr)) return KATA_EINVAL;
     if ((S_out == nullptr) != (z_out == nullptr)) return KATA_EINVAL;
@@ -415,7 +427,7 @@ kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v
                           (const void*)S_out, (const void*)z_out, (const void*)workspace})
         if (p && !aligned16(p)) return KATA_EINVAL;
     DecayPlan plan;
-    if (!decay_plan(s, prefix, &plan)) return KATA_EUNSUPPORTED;
+    if (!decay_plan(s, feature, prefix, &plan)) return KATA_EUNSUPPORTED;
     // the matrix-core path reads each head's log-decay row 16 bytes at a time
     // from T-aligned offsets
     if (!empty && !plan.valu && T % 4 != 0 && H * B > 1) return KATA_EUNSUPPORTED;
@@ -433,10 +445,11 @@ kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v
     char* ws = static_cast<char*>(workspace);
     hipError_t e = hipSuccess;
     if (plan.valu) {
+        const int ident = feature == KATA_FEATURE_IDENTITY;
         float* S_rec = reinterpret_cast<float*>(ws);
         float* z_rec = reinterpret_cast<float*>(ws + plan.z_off);
         float* cdec = reinterpret_cast<float*>(ws + plan.dec_off);
-        e = kata::launch_chunk_states_valu(s, k, v, log_decay, S_rec, z_rec, cdec, hs);
+        e = kata::launch_chunk_states_valu(s, k, v, log_decay, S_rec, z_rec, cdec, ident, hs);
         // exclusive prefix over chunks under the decayed combine; inclusive
         // total -> final state
         if (e == hipSuccess)
@@ -446,7 +459,7 @@ kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v
             e = kata::launch_scan_records_decay(z_rec, cdec, (int)BH, s.NC, (int)nz, z0, z_out,
                                                 nullptr, hs);
         if (e == hipSuccess)
-            e = kata::launch_fwd_valu(s, q, k, v, log_decay, S_rec, z_rec, o, 1, hs);
+            e = kata::launch_fwd_valu(s, q, k, v, log_decay, S_rec, z_rec, o, 1, ident, hs);
         return hip_status(e);
     }
     const FwdPlan& fp = plan.fwd;
@@ -473,6 +486,17 @@ kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v
     if (S_out && e == hipSuccess)
         e = kata::launch_record_to_packed16(total, S_out, z_out, s.dv, nrec, hs);
     return hip_status(e);
+}
+
+kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v,
+                                     const float* log_decay, void* o, int B, int H, int T,
+                                     int d_k, int d_v, int chunk, kata_dtype_t dtype,
+                                     kata_prefix_t prefix, const float* S0, const float* z0,
+                                     float* S_out, float* z_out, void* workspace, size_t ws_bytes,
+                                     void* stream) {
+    return kata_chunked_fwd_decay_ex(q, k, v, log_decay, o, B, H, T, d_k, d_v, chunk, dtype,
+                                     KATA_FEATURE_PSD, prefix, S0, z0, S_out, z_out, workspace,
+                                     ws_bytes, stream);
 }
 
 kata_status_t kata_decode_step_decay(const void* q, const void* k, const void* v,

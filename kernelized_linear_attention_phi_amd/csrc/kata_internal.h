@@ -19,17 +19,18 @@ struct Shape {
 // Per-chunk totals phi(K_c)^T V_c and phi(K_c)^T 1 in packed layout:
 // S_rec [BH, NC, D, dv], z_rec [BH, NC, D]. gdec: per-token log-decays
 // [BH, T] or NULL; with them each token is weighted by its decay to the chunk
-// end and cdec [BH, NC] receives each chunk's total decay factor.
+// end and cdec [BH, NC] receives each chunk's total decay factor. ident: the
+// identity feature (D = d_k, s.D must say so) instead of the PSD lift.
 hipError_t launch_chunk_states_valu(const Shape& s, const void* k, const void* v,
                                     const float* gdec, float* S_rec, float* z_rec, float* cdec,
-                                    hipStream_t st);
+                                    int ident, hipStream_t st);
 
 // Chunked forward reading per-chunk exclusive prefixes (causal) or one total
 // state per head (non-causal: S_rec [BH, D, dv], z_rec [BH, D]). gdec as above
-// (causal only).
+// (causal only); ident as above.
 hipError_t launch_fwd_valu(const Shape& s, const void* q, const void* k, const void* v,
                            const float* gdec, const float* S_rec, const float* z_rec, void* o,
-                           int causal, hipStream_t st);
+                           int causal, int ident, hipStream_t st);
 
 // ---- associative scan over records (layout-agnostic, fp32) ----
 

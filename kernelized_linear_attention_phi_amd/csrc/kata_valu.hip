@@ -6,6 +6,10 @@
 // chunk c covers positions [cC, min(cC+C, T)); its output is the masked
 // intra-chunk term plus phi(Q_c) times the exclusive prefix of chunk states.
 //
+// Feature (ident): the PSD lift phi(x) (packed pairs, sqrt(2) off the
+// diagonal, weight (q.k)^2) or the first-order identity phi1(x) = x (state
+// d_k x d_v, weight q.k).
+//
 // Decay gate (gdec != NULL): per-token log-decays g <= 0 scale the state
 // before each token is added (gated linear recurrences, KATA explainers,
 // technical summary 1). With b_t = g_0 + ... + g_t inside the chunk (summed in
@@ -45,7 +49,7 @@ template <typename TIn>
 __global__ __launch_bounds__(kThreads) void chunk_states_valu(
     const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ gdec,
     float* __restrict__ S_rec, float* __restrict__ z_rec, float* __restrict__ cdec, int T, int dk,
-    int dv, int C, int NC) {
+    int dv, int C, int NC, int ident) {
     __shared__ float ks[kMaxC * kMaxDk];
     __shared__ float vs[kMaxC * kMaxDv];
     __shared__ uint32_t pairs[kMaxD];
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
     __shared__ float wt[kMaxC];
     const int c = blockIdx.x;
     const size_t bh = blockIdx.y;
-    const int D = dk * (dk + 1) / 2;
+    const int D = ident ? dk : dk * (dk + 1) / 2;
     const int t0 = c * C;
     const int n = min(C, T - t0);
     const TIn* kb = k + (bh * T + t0) * dk;
@@ -75,11 +79,11 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
         const bool is_z = e >= D * dv;
         const int p = is_z ? e - D * dv : e / dv;
         const int col = is_z ? 0 : e % dv;
-        const int i = pairs[p] & 0xff, j = pairs[p] >> 8;
+        const int i = ident ? p : pairs[p] & 0xff, j = ident ? p : pairs[p] >> 8;
         const float sc = i == j ? 1.0f : kSqrt2;
         float acc = 0.0f;
         for (int t = 0; t < n; ++t) {
-            float f = sc * (ks[t * dk + i] * ks[t * dk + j]);
+            float f = ident ? ks[t * dk + i] : sc * (ks[t * dk + i] * ks[t * dk + j]);
             if (gdec) f *= wt[t];
             acc += is_z ? f : f * vs[t * dv + col];
         }
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void fwd_valu(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ gdec, const float* __restrict__ S_rec,
     const float* __restrict__ z_rec, TIn* __restrict__ o, int T, int dk, int dv, int C, int NC,
-    int causal) {
+    int causal, int ident) {
     __shared__ float qs[kMaxC * kMaxDk];
     __shared__ float ks[kMaxC * kMaxDk];
     __shared__ float vs[kMaxC * kMaxDv];
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void fwd_valu(
     __shared__ double bs[kMaxC];
     const int c = blockIdx.x;
     const size_t bh = blockIdx.y;
-    const int D = dk * (dk + 1) / 2;
+    const int D = ident ? dk : dk * (dk + 1) / 2;
     const int t0 = c * C;
     const int n = min(C, T - t0);
     const TIn* qb = q + (bh * T + t0) * dk;
@@ -133,8 +137,8 @@ __global__ __launch_bounds__(kThreads) void fwd_valu(
     float den = 0.0f;
     const float* qt = qs + t * dk;
     for (int p = 0; p < D; ++p) {
-        const int i = pairs[p] & 0xff, j = pairs[p] >> 8;
-        const float fq = (i == j ? 1.0f : kSqrt2) * (qt[i] * qt[j]);
+        const int i = ident ? p : pairs[p] & 0xff, j = ident ? p : pairs[p] >> 8;
+        const float fq = ident ? qt[i] : (i == j ? 1.0f : kSqrt2) * (qt[i] * qt[j]);
         den += fq * Z[p];
 #pragma unroll
         for (int u = 0; u < kMaxCols / 2; ++u)
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void fwd_valu(
         for (int jj = 0; jj <= t; ++jj) {
             float s = 0.0f;
             for (int i = 0; i < dk; ++i) s += qt[i] * ks[jj * dk + i];
-            float w = s * s;
+            float w = ident ? s : s * s;
             if (gdec) w *= expf((float)(bs[t] - bs[jj]));
             den += w;
 #pragma unroll
@@ -168,31 +172,31 @@ __global__ __launch_bounds__(kThreads) void fwd_valu(
 
 hipError_t launch_chunk_states_valu(const Shape& s, const void* k, const void* v,
                                     const float* gdec, float* S_rec, float* z_rec, float* cdec,
-                                    hipStream_t st) {
+                                    int ident, hipStream_t st) {
     dim3 grid(s.NC, s.B * s.H);
     if (s.bf16)
         chunk_states_valu<bf16_t><<<grid, kThreads, 0, st>>>(
             (const bf16_t*)k, (const bf16_t*)v, gdec, S_rec, z_rec, cdec, s.T, s.dk, s.dv, s.C,
-            s.NC);
+            s.NC, ident);
     else
         chunk_states_valu<float><<<grid, kThreads, 0, st>>>(
             (const float*)k, (const float*)v, gdec, S_rec, z_rec, cdec, s.T, s.dk, s.dv, s.C,
-            s.NC);
+            s.NC, ident);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd_valu(const Shape& s, const void* q, const void* k, const void* v,
                            const float* gdec, const float* S_rec, const float* z_rec, void* o,
-                           int causal, hipStream_t st) {
+                           int causal, int ident, hipStream_t st) {
     dim3 grid(s.NC, s.B * s.H);
     if (s.bf16)
         fwd_valu<bf16_t><<<grid, kThreads, 0, st>>>(
             (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, gdec, S_rec, z_rec,
-            (bf16_t*)o, s.T, s.dk, s.dv, s.C, s.NC, causal);
+            (bf16_t*)o, s.T, s.dk, s.dv, s.C, s.NC, causal, ident);
     else
         fwd_valu<float><<<grid, kThreads, 0, st>>>(
             (const float*)q, (const float*)k, (const float*)v, gdec, S_rec, z_rec, (float*)o,
-            s.T, s.dk, s.dv, s.C, s.NC, causal);
+            s.T, s.dk, s.dv, s.C, s.NC, causal, ident);
     return hipGetLastError();
 }
 

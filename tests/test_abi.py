@@ -82,8 +82,10 @@ def fwd_ex(L, feature=IDENTITY, prefix=SCAN, B=1, H=1, T=64, dk=16, dv=64, C=64,
 def test_fwd_ex_rejects_before_launch(L):
     assert fwd_ex(L, feature=2) == EINVAL
     assert fwd_ex(L, prefix=5) == EINVAL
-    assert fwd_ex(L, dtype=F32) == EUNSUPPORTED                   # identity feature: bf16 only
-    assert fwd_ex(L, C=16) == EUNSUPPORTED                        # identity feature: C >= 32
+    # identity feature: fp32 inputs and chunk 16 take the VALU path, scan prefix only
+    assert fwd_ex(L, dtype=F32, prefix=SEQUENTIAL) == EUNSUPPORTED
+    assert fwd_ex(L, C=16, prefix=SEQUENTIAL) == EUNSUPPORTED
+    assert fwd_ex(L, dtype=F32, ws_bytes=16) == EWORKSPACE
     assert fwd_ex(L, dk=24) == EUNSUPPORTED
     assert fwd_ex(L, feature=PSD, prefix=SEQUENTIAL, dtype=F32) == EUNSUPPORTED
     assert fwd_ex(L, feature=PSD, prefix=SEQUENTIAL, C=128) == EUNSUPPORTED   # d_k=16: C 32 or 64
@@ -108,7 +110,9 @@ def test_feature_dim_and_ex_workspace(L):
     rec1 = 1 * 5 * 256                   # identity, d_k = 16, d_v = 64: four value tiles + z
     assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, IDENTITY, SEQUENTIAL) == 3 * 8 * rec1 * 4
     assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, IDENTITY, SCAN) > 3 * 8 * rec1 * 4
-    assert ws(1, 1, 64, 16, 64, 64, F32, 1, IDENTITY, SCAN) == 0
+    # identity on the VALU path: one S record (d_k x d_v) and one z record per chunk
+    assert ws(1, 1, 64, 16, 64, 64, F32, 1, IDENTITY, SCAN) == 16 * 64 * 4 + 256
+    assert ws(1, 1, 64, 16, 64, 64, F32, 1, IDENTITY, SEQUENTIAL) == 0
     assert ws(1, 1, 64, 16, 64, 64, BF16, 1, 9, SCAN) == 0
 
 
@@ -138,6 +142,15 @@ def test_decay_rejects_before_launch(L):
     assert ws(1, 8, 4096, 32, 64, 128, BF16, SCAN) == nrec * 528 * 64 * 4 + nrec * 528 * 4 + nrec * 4
     assert ws(1, 8, 4096, 32, 64, 128, BF16, SEQUENTIAL) == 0
     assert ws(1, 8, 4096, 16, 64, 64, F32, SCAN) == 8 * 64 * (136 * 64 * 4 + 136 * 4 + 4)
+    dex = L.kata_chunked_fwd_decay_ex
+    dex_args = lambda f, pf, wsb: (FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 16, 64, 64, BF16, f, pf,
+                                   None, None, None, None, FAKE, wsb, None)
+    assert dex(*dex_args(IDENTITY, SEQUENTIAL, 1 << 40)) == EUNSUPPORTED   # identity: VALU, scan only
+    assert dex(*dex_args(IDENTITY, SCAN, 16)) == EWORKSPACE
+    assert dex(*dex_args(5, SCAN, 1 << 40)) == EINVAL
+    wsx = L.kata_chunked_fwd_decay_ex_workspace
+    assert wsx(1, 8, 131072, 16, 64, 64, BF16, PSD, SCAN) == ws(1, 8, 131072, 16, 64, 64, BF16, SCAN)
+    assert wsx(1, 2, 64, 16, 64, 64, BF16, IDENTITY, SCAN) == 2 * 16 * 64 * 4 + 256 + 256
     dec = L.kata_decode_step_decay
     assert dec(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 16, 64, BF16, None) == EINVAL
     assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 12, 64, BF16, None) == EUNSUPPORTED

@@ -32,24 +32,24 @@ def kata():
     return k
 
 
-def run(kata, q, k, v, g, C, prefix, S0=None, z0=None, state=False, dtype="bf16"):
+def run(kata, q, k, v, g, C, prefix, S0=None, z0=None, state=False, dtype="bf16", feature="psd"):
     """kata_chunked_fwd_decay with outputs and workspace pre-filled with NaN."""
     import torch
     qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
     gd = dev(g)
     B, H, T, dk = qd.shape
     dv = vd.shape[-1]
-    D = dk * (dk + 1) // 2
+    D = kata.feature_dim(dk, feature)
     nan = float("nan")
     o = torch.full_like(vd, nan)
     S_out = torch.full((B, H, D, dv), nan, device="cuda") if state else None
     z_out = torch.full((B, H, D), nan, device="cuda") if state else None
     nbytes = kata.chunked_fwd_decay_workspace(B, H, T, dk, dv, C, 1 if dtype == "bf16" else 0,
-                                              prefix)
+                                              prefix, feature)
     ws = torch.full((max(nbytes, 4) // 4,), nan, device="cuda")
     kata.chunked_fwd_decay_into(qd, kd, vd, gd, o, C, ws,
                                 S0=None if S0 is None else dev(S0), z0=None if z0 is None else dev(z0),
-                                S_out=S_out, z_out=z_out, prefix=prefix)
+                                S_out=S_out, z_out=z_out, prefix=prefix, feature=feature)
     torch.cuda.synchronize()
     if state:
         return host(o), host(S_out), host(z_out)
@@ -225,6 +225,40 @@ def test_decay_valu_zero_gate_matches_ungated(kata):
     ref = host(kata.chunked_fwd(dev(q, "f32"), dev(k, "f32"), dev(v, "f32"), chunk=128))
     torch.cuda.synchronize()
     assert row_rel_err(o, ref) <= 1e-6
+
+
+@pytest.mark.parametrize("dtype,dk,dv,C", [("f32", 16, 64, 64), ("bf16", 32, 32, 128),
+                                           ("bf16", 16, 64, 32), ("f32", 32, 16, 16)])
+@pytest.mark.parametrize("gmin", [-0.05, -0.5])
+def test_decay_identity(kata, dtype, dk, dv, C, gmin):
+    """The gate on the first-order feature (VALU path), orthant inputs: every
+    output and the final state against the identity-feature decay oracle."""
+    B, H, T = 2, 2, 333
+    q, k, v = gen.orthant_qkv(B, H, T, dk, dv, seed=1800 + dk + dv + C, dtype=dtype)
+    g = gen.log_decays(B, H, T, seed=1801 + C, gmin=gmin)
+    say(f"decay identity dtype={dtype} dk={dk} dv={dv} C={C} gmin={gmin}")
+    o, S, z = run(kata, q, k, v, g, C, "scan", state=True, dtype=dtype, feature="identity")
+    assert row_rel_err(o, O.decay_brute_force(q, k, v, g, feature="identity")) <= VALU_TOL[dtype]
+    _, S_ref, z_ref = O.decay_recurrent(q, k, v, g, feature="identity")
+    assert state_rel_err(S, S_ref) <= VALU_STATE_TOL and state_rel_err(z, z_ref) <= VALU_STATE_TOL
+
+
+def test_decay_identity_reset_and_resume(kata):
+    """fp32 first-order feature: an initial state that decays with the sequence
+    and a reset gate after which outputs equal the ungated first-order oracle."""
+    T1, T2 = 90, 210
+    q, k, v = gen.orthant_qkv(1, 2, T1 + T2, 16, 64, seed=1810, dtype="f32")
+    g = gen.log_decays(1, 2, T1 + T2, seed=1811, gmin=-0.1)
+    r = T1 + 100
+    g[:, :, r] = -1e4
+    g[:, :, r + 1:] = 0.0
+    _, S0, z0 = O.decay_recurrent(q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], g[:, :, :T1],
+                                  feature="identity")
+    say("decay identity resume and reset")
+    o = run(kata, q[:, :, T1:], k[:, :, T1:], v[:, :, T1:], g[:, :, T1:], 64, "scan",
+            S0=S0.astype(np.float32), z0=z0.astype(np.float32), dtype="f32", feature="identity")
+    assert row_rel_err(o, O.decay_brute_force(q, k, v, g, feature="identity")[:, :, T1:]) <= 1e-4
+    assert row_rel_err(o[:, :, r - T1:], O.fo_brute_force(q[:, :, r:], k[:, :, r:], v[:, :, r:])) <= 1e-4
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

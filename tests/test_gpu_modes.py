@@ -34,12 +34,13 @@ def kata():
     return k
 
 
-def run(kata, q, k, v, C, feature, prefix, causal=True, S0=None, z0=None, state=False):
+def run(kata, q, k, v, C, feature, prefix, causal=True, S0=None, z0=None, state=False,
+        dtype="bf16"):
     """kata_chunked_fwd_ex with every output and the workspace pre-filled with
     NaN (an element the library fails to write, or scratch it reads before
     writing, cannot pass for a correct value)."""
     import torch
-    qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
     B, H, T, dk = qd.shape
     dv = vd.shape[-1]
     D = kata.feature_dim(dk, feature)
@@ -47,7 +48,8 @@ def run(kata, q, k, v, C, feature, prefix, causal=True, S0=None, z0=None, state=
     o = torch.full_like(vd, nan)
     S_out = torch.full((B, H, D, dv), nan, device="cuda") if state else None
     z_out = torch.full((B, H, D), nan, device="cuda") if state else None
-    nbytes = kata.chunked_fwd_workspace(B, H, T, dk, dv, C, 1, causal, feature, prefix)
+    nbytes = kata.chunked_fwd_workspace(B, H, T, dk, dv, C, 1 if dtype == "bf16" else 0, causal,
+                                        feature, prefix)
     ws = torch.full((max(nbytes, 4) // 4,), nan, device="cuda")
     kata.chunked_fwd_into(qd, kd, vd, o, C, causal, ws,
                           S0=None if S0 is None else dev(S0), z0=None if z0 is None else dev(z0),
@@ -165,6 +167,29 @@ def test_identity_fullsize_fwd4k(kata):
 
 
 # ---- sequential prefix, PSD lift ---------------------------------------------------
+
+@pytest.mark.parametrize("dtype,dk,dv,C", [("f32", 16, 64, 64), ("f32", 32, 16, 128),
+                                           ("bf16", 16, 64, 16), ("f32", 16, 32, 16)])
+def test_identity_valu_path(kata, dtype, dk, dv, C):
+    """The first-order feature on the fp32 VALU path (fp32 inputs, or chunk 16):
+    causal with a ragged tail and the final state, non-causal, and resume from an
+    initial state."""
+    B, H, T = 2, 2, 333
+    q, k, v = gen.orthant_qkv(B, H, T, dk, dv, seed=1700 + dk + dv + C, dtype=dtype)
+    tol = 1e-4 if dtype == "f32" else TOL
+    say(f"identity valu dtype={dtype} dk={dk} dv={dv} C={C}")
+    o, S, z = run(kata, q, k, v, C, "identity", "scan", state=True, dtype=dtype)
+    assert row_rel_err(o, O.fo_brute_force(q, k, v)) <= tol
+    St, zt = O.fo_state_from_tokens(k, v)
+    assert state_rel_err(S, St) <= 1e-5 and state_rel_err(z, zt) <= 1e-5
+    o = run(kata, q, k, v, C, "identity", "scan", causal=False, dtype=dtype)
+    assert row_rel_err(o, O.fo_brute_force(q, k, v, causal=False)) <= tol
+    T1 = 120
+    S0, z0 = O.fo_state_from_tokens(k[:, :, :T1], v[:, :, :T1])
+    o = run(kata, q[:, :, T1:], k[:, :, T1:], v[:, :, T1:], C, "identity", "scan",
+            S0=S0.astype(np.float32), z0=z0.astype(np.float32), dtype=dtype)
+    assert row_rel_err(o, O.fo_brute_force(q, k, v)[:, :, T1:]) <= tol
+
 
 @pytest.mark.parametrize("dk,dv,C", [(16, 64, 64), (16, 16, 32), (16, 32, 64), (32, 64, 128),
                                      (32, 32, 64), (32, 16, 64)])
