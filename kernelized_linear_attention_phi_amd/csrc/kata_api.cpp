@@ -226,18 +226,25 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
             if (e == hipSuccess) e = mark(1);
             if (e == hipSuccess) e = mark(2);
             if (e == hipSuccess) e = output(init, S_out ? total : nullptr);
+            if (e == hipSuccess) e = mark(3);
+            if (S_out && e == hipSuccess) e = to_packed();
         } else {
             if (e == hipSuccess) e = seg_state();
             if (e == hipSuccess) e = mark(1);
-            // exclusive prefix over segments in place; inclusive total per head
+            // exclusive prefix over segments in place; the inclusive total per
+            // head goes to the packed final state (when asked for) and, for the
+            // non-causal output, to the total record
+            const kata::RecordExport ex{m == 16 ? kata::kRecPsd16 : m == 32 ? kata::kRecPsd32
+                                                                            : kata::kRecIdent,
+                                        s.dk, s.dv, S_out, z_out};
             if (e == hipSuccess)
                 e = kata::launch_scan_records(rec, (int)BH, plan.NSEG, plan.REC,
-                                              S0 ? init : nullptr, total, nullptr, hs);
+                                              S0 ? init : nullptr, causal ? nullptr : total,
+                                              nullptr, hs, S_out ? &ex : nullptr);
             if (e == hipSuccess) e = mark(2);
             if (e == hipSuccess) e = output(causal ? rec : total, nullptr);
+            if (e == hipSuccess) e = mark(3);
         }
-        if (e == hipSuccess) e = mark(3);
-        if (S_out && e == hipSuccess) e = to_packed();
         if (e == hipSuccess) e = mark(4);
         return hip_status(e);
     }
@@ -473,18 +480,20 @@ kata_status_t kata_chunked_fwd_decay_ex(const void* q, const void* k, const void
         if (e == hipSuccess)
             e = kata::launch_fwd16_decay(s, q, k, v, log_decay, init, S_out ? total : nullptr, o,
                                          fp.G, fp.NSEG, hs);
+        if (S_out && e == hipSuccess)
+            e = kata::launch_record_to_packed16(total, S_out, z_out, s.dv, nrec, hs);
     } else {
         float* segdec = reinterpret_cast<float*>(ws + plan.dec_off);
+        const kata::RecordExport ex{kata::kRecPsd16, s.dk, s.dv, S_out, z_out};
         if (e == hipSuccess)
             e = kata::launch_seg_state16_decay(s, k, v, log_decay, rec, segdec, fp.G, fp.NSEG, hs);
         if (e == hipSuccess)
             e = kata::launch_scan_records_decay(rec, segdec, nrec, fp.NSEG, fp.REC,
-                                                S0 ? init : nullptr, total, nullptr, hs);
+                                                S0 ? init : nullptr, nullptr, nullptr, hs,
+                                                S_out ? &ex : nullptr);
         if (e == hipSuccess)
             e = kata::launch_fwd16_decay(s, q, k, v, log_decay, rec, nullptr, o, fp.G, fp.NSEG, hs);
     }
-    if (S_out && e == hipSuccess)
-        e = kata::launch_record_to_packed16(total, S_out, z_out, s.dv, nrec, hs);
     return hip_status(e);
 }
 

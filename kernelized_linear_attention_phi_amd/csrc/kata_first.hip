@@ -27,6 +27,7 @@
 
 #include "kata_chunk.h"
 #include "kata_internal.h"
+#include "kata_records.h"
 
 namespace kata {
 
@@ -319,14 +320,6 @@ __global__ __launch_bounds__(64 * NW1) void kata_fwd1(const bf16_t* __restrict__
 
 // ---- record <-> packed (S [d_k, d_v] row-major, z [d_k]) ---------------------
 
-__device__ __forceinline__ void rec_coords(int e, int NTV, int* a, int* col, bool* zt) {
-    const int unit = e / 256, lane = (e % 256) / 4, r = e % 4;
-    const int at = unit / (NTV + 1), u = unit % (NTV + 1);
-    *a = 16 * at + 4 * (lane / 16) + r;
-    *zt = u == NTV;
-    *col = *zt ? lane % 16 : 16 * u + lane % 16;
-}
-
 __global__ void record_to_packed1(const float* __restrict__ rec, float* __restrict__ S,
                                   float* __restrict__ z, int DK, int DV, int REC, int nrec) {
     for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < (size_t)REC * nrec;
@@ -334,7 +327,7 @@ __global__ void record_to_packed1(const float* __restrict__ rec, float* __restri
         const size_t b = x / REC;
         int a, col;
         bool zt;
-        rec_coords((int)(x % REC), DV / 16, &a, &col, &zt);
+        rec1_coords((int)(x % REC), DV / 16, &a, &col, &zt);
         if (!zt) S[(b * DK + a) * DV + col] = rec[x];
         else if (col == 0) z[b * DK + a] = rec[x];
     }
@@ -348,7 +341,7 @@ __global__ void record_from_packed1(float* __restrict__ rec, const float* __rest
         const size_t b = x / REC;
         int a, col;
         bool zt;
-        rec_coords((int)(x % REC), DV / 16, &a, &col, &zt);
+        rec1_coords((int)(x % REC), DV / 16, &a, &col, &zt);
         rec[x] = !zt ? S[(b * DK + a) * DV + col] : (col == 0 ? z[b * DK + a] : 0.0f);
     }
 }

@@ -40,6 +40,7 @@
 // phi(q).z = q^T Z q is one MFMA (Z q) plus a 4-term dot product per lane.
 #include "kata_chunk.h"
 #include "kata_internal.h"
+#include "kata_records.h"
 
 #include <algorithm>
 
@@ -719,35 +720,6 @@ hipError_t launch_fwd16_decay(const Shape& s, const void* q, const void* k, cons
 
 namespace {
 
-// Internal record element -> (packed feature index, value column, scale), or -1
-// for elements without a packed counterpart: the repeated (always zero) rows of
-// tile 8, and the lower triangle of Z on export (lower = true marks those so the
-// import can still fill them).
-__device__ __forceinline__ int record_to_packed(int idx, int NTV, int* col, float* scale,
-                                                bool* lower) {
-    const int sz = NMT * NTV * 256;
-    *lower = false;
-    if (idx >= sz) {                                 // Gram matrix Z[i][j]
-        const int e = idx - sz;
-        const int lane = (e >> 2) & 63;
-        const int i = 4 * (lane >> 4) + (e & 3), j = lane & 15;
-        const int a = min(i, j), b = max(i, j);
-        *col = -1;
-        *scale = i == j ? 1.0f : kSqrt2;
-        *lower = i > j;
-        return a * DK - a * (a - 1) / 2 + (b - a);
-    }
-    const int r = idx & 3, lane = (idx >> 2) & 63, nt = (idx >> 8) % NTV;
-    const int d = (idx >> 8) / NTV;
-    const int rho = 4 * (lane >> 4) + r;
-    *col = 16 * nt + (lane & 15);
-    if (d == 8 && rho >= 8) return -1;
-    const int i = rho, j = (rho + d) & 15;
-    const int a = min(i, j), b = max(i, j);
-    *scale = d == 0 ? 1.0f : kSqrt2;
-    return a * DK - a * (a - 1) / 2 + (b - a);
-}
-
 __global__ void record_from_packed(float* __restrict__ rec, const float* __restrict__ S,
                                    const float* __restrict__ z, int NTV, int REC, int nrec) {
     const int D = DK * (DK + 1) / 2, DV = 16 * NTV;
@@ -758,7 +730,7 @@ __global__ void record_from_packed(float* __restrict__ rec, const float* __restr
         int col;
         float scale;
         bool lower;
-        const int p = record_to_packed(idx, NTV, &col, &scale, &lower);
+        const int p = rec16_to_packed(idx, NTV, &col, &scale, &lower);
         float val = 0.0f;
         if (p >= 0) val = (col >= 0 ? S[(b * D + p) * DV + col] : z[b * D + p]) / scale;
         rec[x] = val;
@@ -775,7 +747,7 @@ __global__ void record_to_packed_kernel(const float* __restrict__ rec, float* __
         int col;
         float scale;
         bool lower;
-        const int p = record_to_packed(idx, NTV, &col, &scale, &lower);
+        const int p = rec16_to_packed(idx, NTV, &col, &scale, &lower);
         if (p < 0 || lower) continue;
         const float val = rec[x] * scale;
         if (col >= 0) S[(b * D + p) * DV + col] = val;

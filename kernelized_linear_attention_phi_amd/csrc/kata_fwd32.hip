@@ -38,6 +38,7 @@
 // w), and phi(q).z = q^T Z q is two MFMAs (Z q) plus an 8-term dot product.
 #include "kata_chunk.h"
 #include "kata_internal.h"
+#include "kata_records.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -588,38 +589,6 @@ hipError_t dispatch32(const Shape& s, const void* q, const void* k, const void* 
     return hipErrorInvalidValue;
 }
 
-// Record element -> (packed feature index, value column or -1 for z, scale);
-// lower = true for Gram entries below the diagonal (skipped on export, filled on
-// import).
-__device__ __forceinline__ int record_to_packed32(int idx, int NTV, int* col, float* scale,
-                                                  bool* lower) {
-    const int sz = NFT * NTV * 256;
-    int a, b;
-    *lower = false;
-    if (idx >= sz) {                                 // Gram tile zt, Z[i][j]
-        const int e = idx - sz;
-        const int zt = e >> 8, lane = (e >> 2) & 63;
-        const int i = 4 * (lane >> 4) + (e & 3), j = lane & 15;
-        a = i + ((zt >> 1) ? 16 : 0);                // row half: L for LL, LU; U for UL, UU
-        b = j + ((zt & 1) ? 16 : 0);                 // column half: L for LL, UL; U for LU, UU
-        *col = -1;
-        *lower = a > b;
-    } else {
-        const int r = idx & 3, lane = (idx >> 2) & 63, nt = (idx >> 8) % NTV;
-        const int t = (idx >> 8) / NTV;
-        const int rho = 4 * (lane >> 4) + r;
-        *col = 16 * nt + (lane & 15);
-        if (t < 8) { a = rho; b = (rho + t) & 15; }
-        else if (t < 16) { a = 16 + rho; b = 16 + ((rho + t - 8) & 15); }
-        else if (t < 32) { a = rho; b = 16 + ((rho + t - 16) & 15); }
-        else if (rho < 8) { a = rho; b = rho + 8; }
-        else { a = 8 + rho; b = 16 + rho; }
-    }
-    *scale = a == b ? 1.0f : kSqrt2;
-    const int i = min(a, b), j = max(a, b);
-    return i * DK - i * (i - 1) / 2 + (j - i);
-}
-
 __global__ void record_from_packed32(float* __restrict__ rec, const float* __restrict__ S,
                                      const float* __restrict__ z, int NTV, int REC, int nrec) {
     const int D = DK * (DK + 1) / 2, DV = 16 * NTV;
@@ -629,7 +598,7 @@ __global__ void record_from_packed32(float* __restrict__ rec, const float* __res
         int col;
         float scale;
         bool lower;
-        const int p = record_to_packed32((int)(x % REC), NTV, &col, &scale, &lower);
+        const int p = rec32_to_packed((int)(x % REC), NTV, &col, &scale, &lower);
         rec[x] = (col >= 0 ? S[(b * D + p) * DV + col] : z[b * D + p]) / scale;
     }
 }
@@ -643,7 +612,7 @@ __global__ void record_to_packed32_kernel(const float* __restrict__ rec, float* 
         int col;
         float scale;
         bool lower;
-        const int p = record_to_packed32((int)(x % REC), NTV, &col, &scale, &lower);
+        const int p = rec32_to_packed((int)(x % REC), NTV, &col, &scale, &lower);
         if (lower) continue;
         const float val = rec[x] * scale;
         if (col >= 0) S[(b * D + p) * DV + col] = val;

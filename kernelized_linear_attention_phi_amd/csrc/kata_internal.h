@@ -39,15 +39,29 @@ hipError_t launch_fwd_valu(const Shape& s, const void* q, const void* k, const v
 // prefix sum init_b + sum_{r' < r} rec_{r'} (init = 0 when NULL; init_b at
 // init + b*E). Writes the inclusive total of every sequence to total_a and/or
 // total_b (each NULL or E floats per sequence).
+// ex (optional): also writes each sequence's total, converted from the record
+// layout `ex->layout` to the packed state ex->S [nseq, D, dv], ex->z [nseq, D].
+struct RecordExport;
 hipError_t launch_scan_records(float* rec, int nseq, int NR, int E, const float* init,
-                               float* total_a, float* total_b, hipStream_t st);
+                               float* total_a, float* total_b, hipStream_t st,
+                               const RecordExport* ex = nullptr);
 
 // The same with the decay gate: record r of sequence b also carries the factor
 // dec[b*NR + r] by which its span decays the state before it; record r becomes
 // the exclusive prefix under (a1, S1) o (a2, S2) = (a1 a2, a2 S1 + S2).
 hipError_t launch_scan_records_decay(float* rec, const float* dec, int nseq, int NR, int E,
                                      const float* init, float* total_a, float* total_b,
-                                     hipStream_t st);
+                                     hipStream_t st, const RecordExport* ex = nullptr);
+
+// Record layouts of the matrix-core kernels (kata_records.h) and a packed
+// state to export a record to.
+constexpr int kRecNone = 0, kRecPsd16 = 1, kRecPsd32 = 2, kRecIdent = 3;
+struct RecordExport {
+    int layout;      // kRecPsd16, kRecPsd32 or kRecIdent
+    int dk, dv;
+    float* S;        // [nseq, D, dv]
+    float* z;        // [nseq, D]
+};
 
 // Copies (src != NULL) or zero-fills n floats.
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st);

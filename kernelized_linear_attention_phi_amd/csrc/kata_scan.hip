@@ -5,7 +5,9 @@
 // instead of a sequential recurrence.
 //
 // Layout-agnostic: a "record" is E contiguous floats (one chunk's or segment's
-// state; E is a multiple of 4). The scan is exclusive: record r becomes
+// state; E is a multiple of 4). Optionally the inclusive total is also written
+// straight to the packed state of the boundary (the record layout named by the
+// caller, kata_records.h), which saves a conversion pass after the scan. The scan is exclusive: record r becomes
 // init + sum_{r' < r} rec_{r'}, and the inclusive total goes to the totals.
 // Sequences of at most 32 records take a per-element walk; longer ones a
 // blocked two-level scan: groups of 16 consecutive records are summed in
@@ -20,6 +22,7 @@
 // combined in order.
 #include "kata_device.h"
 #include "kata_internal.h"
+#include "kata_records.h"
 
 namespace kata {
 
@@ -35,6 +38,15 @@ __device__ __forceinline__ float4 axpy4(float a, float4 x, float4 y) {
                        __builtin_fmaf(a, x.z, y.z), __builtin_fmaf(a, x.w, y.w));
 }
 
+// The four total elements 4 e4 .. 4 e4 + 3 of sequence seq, written to the
+// packed state in place of a separate conversion pass.
+__device__ __forceinline__ void export_total(const RecordExport& ex, size_t seq, int e4, float4 t) {
+    export_element(ex, seq, 4 * e4 + 0, t.x);
+    export_element(ex, seq, 4 * e4 + 1, t.y);
+    export_element(ex, seq, 4 * e4 + 2, t.z);
+    export_element(ex, seq, 4 * e4 + 3, t.w);
+}
+
 // Few records per sequence (NR <= kSeqMax): one thread per 4 consecutive
 // elements walks the records in order. Loads are issued 8 records ahead of the
 // dependent adds, so every thread keeps 8 coalesced 16-byte reads in flight.
@@ -44,7 +56,8 @@ constexpr int kSeqUnroll = 8;
 template <bool DECAY>
 __global__ __launch_bounds__(256) void scan_records_seq_kernel(
     float* __restrict__ rec, const float* __restrict__ dec, int NR, int E,
-    const float* __restrict__ init, float* __restrict__ total_a, float* __restrict__ total_b) {
+    const float* __restrict__ init, float* __restrict__ total_a, float* __restrict__ total_b,
+    RecordExport ex) {
     const size_t seq = blockIdx.y;
     const int E4 = E / 4;
     const int e4 = blockIdx.x * blockDim.x + threadIdx.x;
@@ -66,6 +79,7 @@ __global__ __launch_bounds__(256) void scan_records_seq_kernel(
     }
     if (total_a) reinterpret_cast<float4*>(total_a + seq * E)[e4] = carry;
     if (total_b) reinterpret_cast<float4*>(total_b + seq * E)[e4] = carry;
+    if (ex.layout != kRecNone) export_total(ex, seq, e4, carry);
 }
 
 // Blocked two-level scan. A block owns kCols4 float4 columns of one sequence
@@ -82,7 +96,8 @@ constexpr int kTileRecs = kGroups * kPer;
 template <bool DECAY>
 __global__ __launch_bounds__(kCols4 * kGroups) void scan_records_blocked_kernel(
     float* __restrict__ rec, const float* __restrict__ dec, int NR, int E,
-    const float* __restrict__ init, float* __restrict__ total_a, float* __restrict__ total_b) {
+    const float* __restrict__ init, float* __restrict__ total_a, float* __restrict__ total_b,
+    RecordExport ex) {
     __shared__ float4 gsum[kGroups][kCols4];
     __shared__ float gdec[kGroups];
     const size_t seq = blockIdx.y;
@@ -149,6 +164,7 @@ __global__ __launch_bounds__(kCols4 * kGroups) void scan_records_blocked_kernel(
     if (g == 0 && col_ok) {
         if (total_a) reinterpret_cast<float4*>(total_a + seq * E)[e4] = carry;
         if (total_b) reinterpret_cast<float4*>(total_b + seq * E)[e4] = carry;
+        if (ex.layout != kRecNone) export_total(ex, seq, e4, carry);
     }
 }
 
@@ -161,16 +177,18 @@ __global__ void copy_or_zero_kernel(float* __restrict__ dst, const float* __rest
 
 template <bool DECAY>
 hipError_t scan_impl(float* rec, const float* dec, int nseq, int NR, int E, const float* init,
-                     float* total_a, float* total_b, hipStream_t st) {
+                     float* total_a, float* total_b, hipStream_t st, const RecordExport* ex) {
     if (nseq == 0 || E == 0) return hipSuccess;
     if (E % 4 != 0) return hipErrorInvalidValue;      // every record length is a multiple of 4
+    const RecordExport x = ex ? *ex : RecordExport{kRecNone, 0, 0, nullptr, nullptr};
     if (NR <= kSeqMax) {
         dim3 grid((E / 4 + 255) / 256, nseq);
-        scan_records_seq_kernel<DECAY><<<grid, 256, 0, st>>>(rec, dec, NR, E, init, total_a, total_b);
+        scan_records_seq_kernel<DECAY><<<grid, 256, 0, st>>>(rec, dec, NR, E, init, total_a, total_b,
+                                                             x);
     } else {
         dim3 grid((E / 4 + kCols4 - 1) / kCols4, nseq);
         scan_records_blocked_kernel<DECAY><<<grid, kCols4 * kGroups, 0, st>>>(rec, dec, NR, E, init,
-                                                                              total_a, total_b);
+                                                                              total_a, total_b, x);
     }
     return hipGetLastError();
 }
@@ -178,14 +196,15 @@ hipError_t scan_impl(float* rec, const float* dec, int nseq, int NR, int E, cons
 }  // namespace
 
 hipError_t launch_scan_records(float* rec, int nseq, int NR, int E, const float* init,
-                               float* total_a, float* total_b, hipStream_t st) {
-    return scan_impl<false>(rec, nullptr, nseq, NR, E, init, total_a, total_b, st);
+                               float* total_a, float* total_b, hipStream_t st,
+                               const RecordExport* ex) {
+    return scan_impl<false>(rec, nullptr, nseq, NR, E, init, total_a, total_b, st, ex);
 }
 
 hipError_t launch_scan_records_decay(float* rec, const float* dec, int nseq, int NR, int E,
                                      const float* init, float* total_a, float* total_b,
-                                     hipStream_t st) {
-    return scan_impl<true>(rec, dec, nseq, NR, E, init, total_a, total_b, st);
+                                     hipStream_t st, const RecordExport* ex) {
+    return scan_impl<true>(rec, dec, nseq, NR, E, init, total_a, total_b, st, ex);
 }
 
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st) {
