@@ -170,29 +170,24 @@ __device__ __forceinline__ ChunkDecay chunk_decay(const char* staged_g, const La
     return ChunkDecay{x, __shfl(x, C - 1, 64)};
 }
 
-// b of chunk position 16 jb + 4g + r (the key slots of K^T fragments).
-__device__ __forceinline__ float key_b(const ChunkDecay& cd, int jb, int r, const Lane& L) {
-    return __shfl(cd.b, 16 * jb + 4 * L.g + r, 64);
-}
-
-// The key positions' b values of one chunk, gathered once: b[jb][r] for position
-// 16 jb + 4g + r; last = b_{C-1}.
-template <int TT>
+// The key positions' b values of one chunk, kept in LDS rather than registers
+// (one 64-float row per wavefront, rewritten each chunk by the same
+// wavefront): b(jb, r) is position 16 jb + 4g + r; last = b_{C-1}.
 struct KeyDecay {
-    float b[TT][4];
-    float last;
+    const float* row = nullptr;   // this lane's view of the row: + 4g
+    float last = 0.0f;
+    __device__ float b(int jb, int r) const { return row[16 * jb + r]; }
 };
 
-template <int TT>
-__device__ __forceinline__ KeyDecay<TT> key_decays(const ChunkDecay& cd, const Lane& L) {
-    KeyDecay<TT> kd;
-#pragma unroll
-    for (int jb = 0; jb < TT; ++jb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) kd.b[jb][r] = key_b(cd, jb, r, L);
-    kd.last = cd.last;
-    return kd;
+// Writes the chunk's b (lane = position; lanes past the chunk hold b_{C-1}) to
+// this wavefront's row.
+__device__ __forceinline__ KeyDecay key_decays(const ChunkDecay& cd, float* wrow, const Lane& L) {
+    wrow[L.lane] = cd.b;
+    return KeyDecay{wrow + 4 * L.g, cd.last};
 }
+
+// Bytes of LDS for the rows of NW wavefronts (gated kernels only).
+constexpr int kKeyDecayRowBytes = 64 * 4;
 
 // State leaving a chunk: every accumulator scaled by a = exp(b_last) (the keys
 // of the chunk are scaled inside state_update).
@@ -216,7 +211,7 @@ template <int W, bool WITH_Z, int DV, int C, bool DECAY = false>
 __device__ __forceinline__ void state_update(State<DV, C>& st, const f32x4_t (&KT)[Cfg<DV, C>::TT],
                                              const u32x4_t (&vop)[Cfg<DV, C>::KS][Cfg<DV, C>::NTV],
                                              const Lane& L,
-                                             const KeyDecay<Cfg<DV, C>::TT>& kd = KeyDecay<Cfg<DV, C>::TT>{}) {
+                                             const KeyDecay& kd = KeyDecay{}) {
     using F = Cfg<DV, C>;
     constexpr int l8 = lo8<W, F::NTV>(), h8 = hi8<W, F::NTV>();
 #pragma unroll
@@ -227,7 +222,7 @@ __device__ __forceinline__ void state_update(State<DV, C>& st, const f32x4_t (&K
         if constexpr (DECAY) {
 #pragma unroll
             for (int s = 0; s < 8; ++s)
-                ka[s] *= exp2_neg(0.5f * (kd.last - kd.b[2 * m + s / 4][s % 4]));
+                ka[s] *= exp2_neg(0.5f * (kd.last - kd.b(2 * m + s / 4, s % 4)));
         }
         if constexpr (WITH_Z) {
             // Gram matrix: A = K^T (row = coordinate c16), B = K (column = c16)
@@ -340,10 +335,11 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
         const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::QB);
         f32x4_t KT[F::TT];
         k_transposed<DV, C>(bk, KT, L);
-        KeyDecay<F::TT> kd{};
+        KeyDecay kd{};
         if constexpr (DECAY) {
             const ChunkDecay cd = chunk_decay<C>(buf + 2 * F::QB + F::VB, L);
-            kd = key_decays<F::TT>(cd, L);
+            kd = key_decays(cd, reinterpret_cast<float*>(lds + 3 * ChunkIO<DK, DV, C, NW, NW, DECAY>::BUF +
+                                                          W * kKeyDecayRowBytes), L);
             decay_state<DV, C>(st, cd);
             lsum += cd.last;
         }
@@ -483,11 +479,12 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         // the whole chunk), computed here so that they are not live during the
         // inter-chunk products
         ChunkDecay cd{0.0f, 0.0f};
-        KeyDecay<F::TT> kd{};
+        KeyDecay kd{};
         float bq_own[F::TW];                        // b of this lane's query in own tile u
         if constexpr (DECAY) {
             cd = chunk_decay<C>(buf + 2 * F::QB + F::VB, L);
-            kd = key_decays<F::TT>(cd, L);
+            kd = key_decays(cd, reinterpret_cast<float*>(lds + F::NBUF * IO::BUF + F::XB +
+                                                          W * kKeyDecayRowBytes), L);
 #pragma unroll
             for (int u = 0; u < F::TW; ++u) bq_own[u] = __shfl(cd.b, 16 * (NW * u + W) + L.c16, 64);
         }
@@ -534,7 +531,7 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
                         for (int r = 0; r < 4; ++r) {
                             const int j = 32 * m + 16 * h + 4 * L.g + r;
                             float x = sc[r] * sc[r];
-                            if constexpr (DECAY) x *= exp2_neg(bq_own[u] - kd.b[2 * m + h][r]);
+                            if constexpr (DECAY) x *= exp2_neg(bq_own[u] - kd.b(2 * m + h, r));
                             w[4 * h + r] = (!diag || j <= t) ? x : 0.0f;
                         }
                     }
@@ -603,7 +600,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kata_seg_state16(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                       const float* __restrict__ gdec, float* __restrict__ rec,
                       float* __restrict__ segdec, int T, int NC, int G, int NSEG) {
-    __shared__ __attribute__((aligned(16))) char lds[3 * ChunkIO<DK, DV, C, NW, NW, DECAY>::BUF];
+    __shared__ __attribute__((aligned(16)))
+    char lds[3 * ChunkIO<DK, DV, C, NW, NW, DECAY>::BUF + (DECAY ? NW * kKeyDecayRowBytes : 0)];
     const Lane L;
     if (L.w == 0) seg_state_body<0, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, as_wave<0>(L));
     else seg_state_body<1, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, as_wave<1>(L));
@@ -619,7 +617,8 @@ void kata_fwd16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const float* __restrict__ prefix, float* __restrict__ final_rec,
                 bf16_t* __restrict__ o, int T, int NC, int G, int NSEG) {
     using F = Cfg<DV, C>;
-    __shared__ __attribute__((aligned(16))) char lds[F::NBUF * ChunkIO<DK, DV, C, NW, 1, DECAY>::BUF + F::XB];
+    __shared__ __attribute__((aligned(16)))
+    char lds[F::NBUF * ChunkIO<DK, DV, C, NW, 1, DECAY>::BUF + F::XB + (DECAY ? NW * kKeyDecayRowBytes : 0)];
     const Lane L;
     if (L.w == 0)
         fwd_body<0, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G, NSEG, as_wave<0>(L));
