@@ -74,7 +74,11 @@ const char* kata_version(void);
 
 /* Bytes of workspace kata_chunked_fwd needs for this problem (0 if none).
  * Returns 0 for unsupported or invalid shapes too; kata_chunked_fwd then
- * reports the precise error. */
+ * reports the precise error. The matrix-core paths cut each (batch, head) into
+ * segments of G chunks (about 1024 segments over the whole problem, 256 at
+ * d_k = 32); the environment variable KATA_SEGMENT_CHUNKS = G (> 0) overrides
+ * G, for tests and tuning. It changes the workspace size, so set it before
+ * both calls. */
 size_t kata_chunked_fwd_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                   kata_dtype_t dtype, int causal);
 
