@@ -198,8 +198,9 @@ kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v
 /* kata_chunked_fwd_decay with a choice of feature map: KATA_FEATURE_PSD is
  * kata_chunked_fwd_decay; KATA_FEATURE_IDENTITY gates the first-order feature
  * phi1(x) = x (weights (q_t.k_j) exp(g_{j+1} + ... + g_t), state d_k x d_v in
- * S0, z0, S_out, z_out), on the fp32 VALU path with KATA_PREFIX_SCAN only.
- * Every other argument, error and layout as there. */
+ * S0, z0, S_out, z_out): on the matrix cores for dtype KATA_BF16 with chunk 32
+ * or 64 (either prefix; T a multiple of 4 when B*H > 1), else on the fp32 VALU
+ * path with KATA_PREFIX_SCAN. Every other argument, error and layout as there. */
 size_t kata_chunked_fwd_decay_ex_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                            kata_dtype_t dtype, kata_feature_t feature,
                                            kata_prefix_t prefix);

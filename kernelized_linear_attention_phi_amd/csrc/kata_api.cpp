@@ -367,10 +367,10 @@ kata_status_t kata_flash_fwd(const void* q, const void* k, const void* v, void* 
 
 // ---- decay gate ----------------------------------------------------------------
 
-// Matrix-core path for the PSD lift with bf16, d_k = 16, C in {32, 64}
-// (segments, scan or sequential prefix); every other supported shape, and the
-// identity feature, takes the fp32 VALU path (per-chunk records, scan prefix
-// only).
+// Matrix-core paths for bf16 with C in {32, 64}: the PSD lift at d_k = 16 and
+// the identity feature at d_k = 16 or 32 (segments, scan or sequential prefix);
+// every other supported shape takes the fp32 VALU path (per-chunk records, scan
+// prefix only).
 struct DecayPlan {
     FwdPlan fwd;           // matrix-core path
     bool valu = false;     // VALU path: S_rec | z_rec | cdec, one record per chunk
@@ -379,8 +379,9 @@ struct DecayPlan {
 
 static bool decay_plan(const Shape& s, kata_feature_t f, kata_prefix_t prefix, DecayPlan* d) {
     const size_t BH = (size_t)s.B * s.H;
-    if (f == KATA_FEATURE_PSD && kata::mfma16_supported(s)) {
-        d->fwd = plan_fwd(s, 1, KATA_FEATURE_PSD, prefix);
+    if ((f == KATA_FEATURE_PSD && kata::mfma16_supported(s)) ||
+        (f == KATA_FEATURE_IDENTITY && kata::first_decay_supported(s))) {
+        d->fwd = plan_fwd(s, 1, f, prefix);
         if (!d->fwd.ok) return false;
         d->dec_off = d->fwd.bytes;
         d->bytes = d->fwd.bytes;
@@ -470,29 +471,36 @@ kata_status_t kata_chunked_fwd_decay_ex(const void* q, const void* k, const void
         return hip_status(e);
     }
     const FwdPlan& fp = plan.fwd;
+    const bool first = fp.mfma == 1;              // identity feature (else PSD, d_k = 16)
     float* rec = reinterpret_cast<float*>(ws + fp.S_off);
     float* init = reinterpret_cast<float*>(ws + fp.init_off);
     float* total = reinterpret_cast<float*>(ws + fp.total_off);
     const int nrec = (int)BH;
-    if (S0) e = kata::launch_record_from_packed16(init, S0, z0, s.dv, nrec, hs);
+    auto output = [&](const float* pre, float* fin) {
+        return first ? kata::launch_fwd1_decay(s, q, k, v, log_decay, pre, fin, o, fp.G, fp.NSEG, hs)
+                     : kata::launch_fwd16_decay(s, q, k, v, log_decay, pre, fin, o, fp.G, fp.NSEG, hs);
+    };
+    if (S0)
+        e = first ? kata::launch_record_from_packed1(init, S0, z0, s.dk, s.dv, nrec, hs)
+                  : kata::launch_record_from_packed16(init, S0, z0, s.dv, nrec, hs);
     if (fp.seq) {
         if (!S0 && e == hipSuccess) e = kata::launch_copy_or_zero(init, nullptr, BH * fp.REC, hs);
-        if (e == hipSuccess)
-            e = kata::launch_fwd16_decay(s, q, k, v, log_decay, init, S_out ? total : nullptr, o,
-                                         fp.G, fp.NSEG, hs);
+        if (e == hipSuccess) e = output(init, S_out ? total : nullptr);
         if (S_out && e == hipSuccess)
-            e = kata::launch_record_to_packed16(total, S_out, z_out, s.dv, nrec, hs);
+            e = first ? kata::launch_record_to_packed1(total, S_out, z_out, s.dk, s.dv, nrec, hs)
+                      : kata::launch_record_to_packed16(total, S_out, z_out, s.dv, nrec, hs);
     } else {
         float* segdec = reinterpret_cast<float*>(ws + plan.dec_off);
-        const kata::RecordExport ex{kata::kRecPsd16, s.dk, s.dv, S_out, z_out};
+        const kata::RecordExport ex{first ? kata::kRecIdent : kata::kRecPsd16, s.dk, s.dv, S_out,
+                                    z_out};
         if (e == hipSuccess)
-            e = kata::launch_seg_state16_decay(s, k, v, log_decay, rec, segdec, fp.G, fp.NSEG, hs);
+            e = first ? kata::launch_seg_state1_decay(s, k, v, log_decay, rec, segdec, fp.G, fp.NSEG, hs)
+                      : kata::launch_seg_state16_decay(s, k, v, log_decay, rec, segdec, fp.G, fp.NSEG, hs);
         if (e == hipSuccess)
             e = kata::launch_scan_records_decay(rec, segdec, nrec, fp.NSEG, fp.REC,
                                                 S0 ? init : nullptr, nullptr, nullptr, hs,
                                                 S_out ? &ex : nullptr);
-        if (e == hipSuccess)
-            e = kata::launch_fwd16_decay(s, q, k, v, log_decay, rec, nullptr, o, fp.G, fp.NSEG, hs);
+        if (e == hipSuccess) e = output(rec, nullptr);
     }
     return hip_status(e);
 }

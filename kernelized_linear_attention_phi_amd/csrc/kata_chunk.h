@@ -262,6 +262,55 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
     }
 }
 
+// ---- decay gate: per-chunk cumulative log-decays ----------------------------
+// Per-token log-decays g <= 0 scale the state before each token is added. With
+// b_t = g_0 + ... + g_t inside a chunk (log2 units here), the prefix state
+// reaches query t scaled by 2^{b_t}, key j <= t of the chunk by 2^{b_t - b_j},
+// and the state leaves the chunk scaled by 2^{b_last} with key j weighted
+// 2^{b_last - b_j}.
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^x for x <= 0 with v_exp_f32 (results below the fp32 normal range may flush
+// to zero, which only drops weights under 2^-126).
+__device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct ChunkDecay {
+    float b;      // lane t (< C): b_t; lanes past the chunk: b_{C-1}
+    float last;   // b_{C-1} (positions past a ragged end carry g = 0)
+};
+
+// Inclusive scan of the staged log-decays over the wavefront (lane = position).
+template <int C>
+__device__ __forceinline__ ChunkDecay chunk_decay(const char* staged_g, const Lane& L) {
+    float x = L.lane < C ? reinterpret_cast<const float*>(staged_g)[L.lane] * kLog2e : 0.0f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_up(x, d, 64);
+        if (L.lane >= d) x += y;
+    }
+    return ChunkDecay{x, __shfl(x, C - 1, 64)};
+}
+
+// The key positions' b values of one chunk, kept in LDS rather than registers
+// (one 64-float row per wavefront, rewritten each chunk by the same
+// wavefront): b(jb, r) is position 16 jb + 4g + r; last = b_{C-1}.
+struct KeyDecay {
+    const float* row = nullptr;   // this lane's view of the row: + 4g
+    float last = 0.0f;
+    __device__ float b(int jb, int r) const { return row[16 * jb + r]; }
+};
+
+// Writes the chunk's b (lane = position; lanes past the chunk hold b_{C-1}) to
+// this wavefront's row.
+__device__ __forceinline__ KeyDecay key_decays(const ChunkDecay& cd, float* wrow, const Lane& L) {
+    wrow[L.lane] = cd.b;
+    return KeyDecay{wrow + 4 * L.g, cd.last};
+}
+
+// Bytes of LDS for the rows of NW wavefronts (gated kernels only).
+constexpr int kKeyDecayRowBytes = 64 * 4;
+
 // Chunk c of a segment [c0, c1) lives in buffer (c - c0) % 2 and is staged one
 // iteration ahead. Per iteration: a loading wavefront waits for every
 // outstanding memory operation of its own (its part of chunk c, and any stores:

@@ -17,6 +17,12 @@
 // tile, accumulated against the ones operand so that only its column 0 is
 // nonzero. Element 4*lane + r of a unit is S[16 at + 4 g + r][16 u + c16].
 //
+// Decay gate (DECAY, chunk 32 or 64; the same reading as for the PSD lift):
+// per chunk the staged log-decays are scanned (lane = position, log2 units);
+// key j's K^T fragment entries are scaled by 2^{b_last - b_j} before the state
+// update, the state by 2^{b_last}; query t's inter-chunk term by 2^{b_t} and its
+// intra weights q_t . k_j by 2^{b_t - b_j}.
+//
 // Output kernel: two wavefronts; wavefront w owns query tiles w, w + 2, ...
 // (causally balanced) and holds the whole state (d_k x d_v is small), so no
 // partial sums are exchanged. Wavefront 0 issues every chunk copy and no global
@@ -36,7 +42,7 @@ namespace {
 constexpr int NW1 = 2;   // wavefronts per workgroup
 constexpr int ALL = -1;  // "every unit" in place of a wavefront index
 
-template <int DK, int DV, int C>
+template <int DK, int DV, int C, bool GATE = false>
 struct Cfg1 {
     static constexpr int NAT = DK / 16;           // feature tiles
     static constexpr int NTV = DV / 16;           // value tiles
@@ -44,12 +50,14 @@ struct Cfg1 {
     static constexpr int TT = C / 16;             // query tiles per chunk
     static constexpr int TW = TT / NW1;           // query tiles per wavefront
     static constexpr int KS = C / 32;             // 32-token K-steps per chunk
-    using IO = ChunkIO<DK, DV, C, NW1, 1>;
+    using IO = ChunkIO<DK, DV, C, NW1, 1, GATE>;
     static constexpr int OROW = DV * 2 + 16;      // LDS row stride of staged output rows
     static constexpr int OST = TW * 16 * OROW;    // staged rows of one wavefront
-    static constexpr int LDS_FWD = 2 * IO::BUF + 3 * OST;   // staged rows: w0 x 2, w1
+    // gated: one row of cumulative log-decays per wavefront after the rest
+    static constexpr int ROWS = GATE ? NW1 * kKeyDecayRowBytes : 0;
+    static constexpr int LDS_FWD = 2 * IO::BUF + 3 * OST + ROWS;   // staged rows: w0 x 2, w1
     static constexpr int NBUF_SEG = 3 * IO::BUF <= 65536 ? 3 : 2;
-    static constexpr int LDS_SEG = NBUF_SEG * IO::BUF;
+    static constexpr int LDS_SEG = NBUF_SEG * IO::BUF + ROWS;
     static constexpr int REC = NAT * NU * 256;
     static_assert(TW >= 1 && KS >= 1, "chunk of at least 32 tokens");
 };
@@ -67,12 +75,31 @@ __host__ __device__ constexpr bool owns(int at, int u) {
     return W == ALL || (at * NU + u) % NW1 == W;
 }
 
+// The 8 bf16 of an operand fragment, each times its own factor, rounded back.
+__device__ __forceinline__ u32x4_t scale_bf16x8(const u32x4_t& x, const float (&f)[8]) {
+    u32x4_t y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = pk2(lo_bf16(x[i]) * f[2 * i], hi_bf16(x[i]) * f[2 * i + 1]);
+    return y;
+}
+
+// The state leaving a chunk: every accumulator times 2^{b_last}.
+template <int DK, int DV, int C>
+__device__ __forceinline__ void decay_state1(State1<DK, DV, C>& st, const ChunkDecay& cd) {
+    const float a = exp2_neg(cd.last);
+#pragma unroll
+    for (int at = 0; at < Cfg1<DK, DV, C>::NAT; ++at)
+#pragma unroll
+        for (int u = 0; u < Cfg1<DK, DV, C>::NU; ++u) st.s[at][u] *= a;
+}
+
 // S += K_c^T [V_c | 1] over one chunk staged in LDS, for the units wavefront W
 // holds: A = K^T fragments (features x tokens), B = V fragments or the ones
 // operand (column 0), both read transposed from the row-major chunk.
-template <int W, int DK, int DV, int C>
+template <int W, int DK, int DV, int C, bool DECAY = false>
 __device__ __forceinline__ void state_update1(State1<DK, DV, C>& st, const bf16_t* bk,
-                                              const bf16_t* bv, const Lane& L) {
+                                              const bf16_t* bv, const Lane& L,
+                                              const KeyDecay& kd = KeyDecay{}) {
     using F = Cfg1<DK, DV, C>;
     const u32x4_t ones = ones_op(L);
 #pragma unroll
@@ -80,6 +107,14 @@ __device__ __forceinline__ void state_update1(State1<DK, DV, C>& st, const bf16_
         u32x4_t kt[F::NAT];
 #pragma unroll
         for (int at = 0; at < F::NAT; ++at) kt[at] = v_fragment_tr<DK>(bk, m, at, L);
+        if constexpr (DECAY) {
+            // slot s is token 32m + 16(s/4) + 4g + s%4: weight 2^{b_last - b_j}
+            float f[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) f[s] = exp2_neg(kd.last - kd.b(2 * m + s / 4, s % 4));
+#pragma unroll
+            for (int at = 0; at < F::NAT; ++at) kt[at] = scale_bf16x8(kt[at], f);
+        }
 #pragma unroll
         for (int u = 0; u < F::NU; ++u) {
             bool any = false;
@@ -119,14 +154,19 @@ __device__ __forceinline__ void record_load1(const float* rec, State1<DK, DV, C>
 
 // ---- segment states ----------------------------------------------------------
 
-template <int W, int DK, int DV, int C>
-__device__ __forceinline__ void seg_state_body1(const bf16_t* k, const bf16_t* v, float* rec,
+template <int W, int DK, int DV, int C, bool DECAY>
+__device__ __forceinline__ void seg_state_body1(const bf16_t* k, const bf16_t* v,
+                                                const float* gdec, float* rec, float* segdec,
                                                 char* lds, int T, int NC, int G, int NSEG,
                                                 const Lane& L) {
     using F = Cfg1<DK, DV, C>;
+    using FG = Cfg1<DK, DV, C, DECAY>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    LoadPipeline<DK, DV, C, NW1, F::NBUF_SEG> P{lds, seg * G, min(NC, seg * G + G), T, bh * T};
+    LoadPipeline<DK, DV, C, NW1, FG::NBUF_SEG, DECAY> P{lds, seg * G, min(NC, seg * G + G), T,
+                                                        bh * T, gdec};
+    float* krow = reinterpret_cast<float*>(lds + FG::NBUF_SEG * FG::IO::BUF + W * kKeyDecayRowBytes);
+    float lsum = 0.0f;                             // log2 of the segment's decay
     State1<DK, DV, C> st;
 #pragma unroll
     for (int at = 0; at < F::NAT; ++at)
@@ -136,22 +176,35 @@ __device__ __forceinline__ void seg_state_body1(const bf16_t* k, const bf16_t* v
     for (int c = P.c0; c < P.c1; ++c) {
         P.acquire(k, v, c, L);
         const char* buf = P.buffer(c);
-        state_update1<W, DK, DV, C>(st, reinterpret_cast<const bf16_t*>(buf + F::IO::QB),
-                                    reinterpret_cast<const bf16_t*>(buf + 2 * F::IO::QB), L);
+        KeyDecay kd{};
+        if constexpr (DECAY) {
+            const ChunkDecay cd = chunk_decay<C>(buf + 2 * F::IO::QB + F::IO::VB, L);
+            kd = key_decays(cd, krow, L);
+            decay_state1<DK, DV, C>(st, cd);
+            lsum += cd.last;
+        }
+        state_update1<W, DK, DV, C, DECAY>(st, reinterpret_cast<const bf16_t*>(buf + F::IO::QB),
+                                           reinterpret_cast<const bf16_t*>(buf + 2 * F::IO::QB), L,
+                                           kd);
         compiler_fence();
     }
     record_store1<W, DK, DV, C>(rec + (bh * NSEG + seg) * (size_t)F::REC, st, L);
+    if (DECAY && W == 0 && L.lane == 0) segdec[bh * NSEG + seg] = exp2_neg(lsum);
 }
 
-template <int DK, int DV, int C>
+template <int DK, int DV, int C, bool DECAY>
 __global__ __launch_bounds__(64 * NW1) void kata_seg_state1(const bf16_t* __restrict__ k,
                                                             const bf16_t* __restrict__ v,
-                                                            float* __restrict__ rec, int T, int NC,
-                                                            int G, int NSEG) {
-    __shared__ __attribute__((aligned(16))) char lds[Cfg1<DK, DV, C>::LDS_SEG];
+                                                            const float* __restrict__ gdec,
+                                                            float* __restrict__ rec,
+                                                            float* __restrict__ segdec, int T,
+                                                            int NC, int G, int NSEG) {
+    __shared__ __attribute__((aligned(16))) char lds[Cfg1<DK, DV, C, DECAY>::LDS_SEG];
     const Lane L;
-    if (L.w == 0) seg_state_body1<0, DK, DV, C>(k, v, rec, lds, T, NC, G, NSEG, as_wave<0>(L));
-    else seg_state_body1<1, DK, DV, C>(k, v, rec, lds, T, NC, G, NSEG, as_wave<1>(L));
+    if (L.w == 0)
+        seg_state_body1<0, DK, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, as_wave<0>(L));
+    else
+        seg_state_body1<1, DK, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, as_wave<1>(L));
 }
 
 // ---- output ------------------------------------------------------------------
@@ -197,17 +250,19 @@ __device__ __forceinline__ f32x4_t scores1(const bf16_t* bk, const bf16_t* bq, i
     }
 }
 
-template <int W, int DK, int DV, int C, bool CAUSAL>
+template <int W, int DK, int DV, int C, bool CAUSAL, bool DECAY>
 __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, const bf16_t* v,
-                                          const float* prefix, float* final_rec, bf16_t* o,
-                                          char* lds, int T, int NC, int G, int NSEG,
-                                          const Lane& L) {
+                                          const float* gdec, const float* prefix,
+                                          float* final_rec, bf16_t* o, char* lds, int T, int NC,
+                                          int G, int NSEG, const Lane& L) {
     using F = Cfg1<DK, DV, C>;
+    using FG = Cfg1<DK, DV, C, DECAY>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    Pipeline<DK, DV, C, NW1, 1> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true};
+    Pipeline<DK, DV, C, NW1, 1, DECAY> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true, gdec};
     // staged rows: wavefront 0 in buffer (c - c0) % 2, wavefront 1 in buffer 2
-    char* ostage = lds + 2 * F::IO::BUF;
+    char* ostage = lds + 2 * FG::IO::BUF;
+    float* krow = reinterpret_cast<float*>(lds + 2 * FG::IO::BUF + 3 * F::OST + W * kKeyDecayRowBytes);
 
     State1<DK, DV, C> st;
     record_load1<DK, DV, C>(prefix + (CAUSAL ? bh * NSEG + seg : bh) * (size_t)F::REC, st, L);
@@ -222,6 +277,13 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
         const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::IO::QB);
         const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::IO::QB);
         bf16_t* oc = o + (bh * T + (size_t)c * C) * DV;
+        // decay gate: the chunk's cumulative log-decays (staged after v)
+        ChunkDecay cd{0.0f, 0.0f};
+        KeyDecay kd{};
+        if constexpr (DECAY) {
+            cd = chunk_decay<C>(buf + 2 * F::IO::QB + F::IO::VB, L);
+            kd = key_decays(cd, krow, L);
+        }
 
         // wavefront 0's rows of the previous chunk (always a full chunk)
         if (W == 1 && c > P.c0)
@@ -254,6 +316,13 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
 #pragma unroll
                 for (int u = 0; u < F::NU; ++u) num[u] = mma16_acc32(sop[at][u], qa, num[u]);
             }
+            float bt = 0.0f;                          // b of this lane's query
+            if constexpr (DECAY) {                    // the prefix state decays to query t
+                bt = krow[qrow];
+                const float e = exp2_neg(bt);
+#pragma unroll
+                for (int u = 0; u < F::NU; ++u) num[u] *= e;
+            }
             // ---- intra-chunk term: A = Q K^T masked to j <= t, num += A [V | 1]
             if (CAUSAL) {
 #pragma unroll
@@ -266,7 +335,9 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int j = 32 * m + 16 * h + 4 * L.g + r;
-                            w[4 * h + r] = (!diag || j <= qrow) ? sc[r] : 0.0f;
+                            float x = sc[r];
+                            if constexpr (DECAY) x *= exp2_neg(bt - kd.b(2 * m + h, r));
+                            w[4 * h + r] = (!diag || j <= qrow) ? x : 0.0f;
                         }
                     }
                     const u32x4_t a = {pk2(w[0], w[1]), pk2(w[2], w[3]), pk2(w[4], w[5]), pk2(w[6], w[7])};
@@ -289,7 +360,10 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
         if (W == 1) store_rows1<DK, DV, C>(own, oc + 16 * DV, n - 16, L);
 
         // ---- running state: S += K_c^T V_c, z += K_c^T 1 (both wavefronts)
-        if (CAUSAL) state_update1<ALL, DK, DV, C>(st, bk, bv, L);
+        if (CAUSAL) {
+            if constexpr (DECAY) decay_state1<DK, DV, C>(st, cd);
+            state_update1<ALL, DK, DV, C, DECAY>(st, bk, bv, L, kd);
+        }
         compiler_fence();
     }
     // wavefront 0's rows of the last chunk
@@ -304,18 +378,23 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
     if (CAUSAL && final_rec) record_store1<W, DK, DV, C>(final_rec + bh * (size_t)F::REC, st, L);
 }
 
-template <int DK, int DV, int C, bool CAUSAL>
+template <int DK, int DV, int C, bool CAUSAL, bool DECAY>
 __global__ __launch_bounds__(64 * NW1) void kata_fwd1(const bf16_t* __restrict__ q,
                                                       const bf16_t* __restrict__ k,
                                                       const bf16_t* __restrict__ v,
+                                                      const float* __restrict__ gdec,
                                                       const float* __restrict__ prefix,
                                                       float* __restrict__ final_rec,
                                                       bf16_t* __restrict__ o, int T, int NC,
                                                       int G, int NSEG) {
-    __shared__ __attribute__((aligned(16))) char lds[Cfg1<DK, DV, C>::LDS_FWD];
+    __shared__ __attribute__((aligned(16))) char lds[Cfg1<DK, DV, C, DECAY>::LDS_FWD];
     const Lane L;
-    if (L.w == 0) fwd_body1<0, DK, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC, G, NSEG, as_wave<0>(L));
-    else fwd_body1<1, DK, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC, G, NSEG, as_wave<1>(L));
+    if (L.w == 0)
+        fwd_body1<0, DK, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G,
+                                               NSEG, as_wave<0>(L));
+    else
+        fwd_body1<1, DK, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G,
+                                               NSEG, as_wave<1>(L));
 }
 
 // ---- record <-> packed (S [d_k, d_v] row-major, z [d_k]) ---------------------
@@ -348,54 +427,76 @@ __global__ void record_from_packed1(float* __restrict__ rec, const float* __rest
 
 // ---- launchers ---------------------------------------------------------------
 
+// Launch arguments shared by every shape: gdec (log-decays, NULL = no gate;
+// causal only, chunk 32 or 64), segdec (per-segment decays, state kernel).
+struct Args1 {
+    const void *q, *k, *v;
+    const float* gdec;
+    float* rec;            // state kernel: segment records; output kernel: final_rec
+    float* segdec;
+    const float* prefix;
+    void* o;
+    int causal, G, NSEG;
+    bool state_only;
+};
+
 template <int DK, int DV, int C>
-hipError_t launch_dk_dv_c1(const Shape& s, const void* q, const void* k, const void* v,
-                           float* rec, const float* prefix, void* o, int causal, int G, int NSEG,
-                           bool state_only, hipStream_t st) {
-    dim3 grid(NSEG, s.B * s.H);
-    if (state_only)
-        kata_seg_state1<DK, DV, C><<<grid, 64 * NW1, 0, st>>>((const bf16_t*)k, (const bf16_t*)v,
-                                                               rec, s.T, s.NC, G, NSEG);
-    else if (causal)
-        kata_fwd1<DK, DV, C, true><<<grid, 64 * NW1, 0, st>>>(
-            (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, prefix, rec, (bf16_t*)o, s.T,
-            s.NC, G, NSEG);
-    else
-        kata_fwd1<DK, DV, C, false><<<grid, 64 * NW1, 0, st>>>(
-            (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, prefix, rec, (bf16_t*)o, s.T,
-            s.NC, G, NSEG);
+hipError_t launch_dk_dv_c1(const Shape& s, const Args1& a, hipStream_t st) {
+    dim3 grid(a.NSEG, s.B * s.H);
+    const bf16_t *q = (const bf16_t*)a.q, *k = (const bf16_t*)a.k, *v = (const bf16_t*)a.v;
+    bf16_t* o = (bf16_t*)a.o;
+    constexpr bool kGate = C == 32 || C == 64;     // gated instantiations
+    if (a.gdec && !kGate) return hipErrorInvalidValue;
+    if (a.state_only) {
+        if constexpr (kGate) {
+            if (a.gdec) {
+                kata_seg_state1<DK, DV, C, true><<<grid, 64 * NW1, 0, st>>>(k, v, a.gdec, a.rec, a.segdec,
+                                                                           s.T, s.NC, a.G, a.NSEG);
+                return hipGetLastError();
+            }
+        }
+        kata_seg_state1<DK, DV, C, false><<<grid, 64 * NW1, 0, st>>>(k, v, nullptr, a.rec, nullptr,
+                                                                    s.T, s.NC, a.G, a.NSEG);
+    } else if (a.causal) {
+        if constexpr (kGate) {
+            if (a.gdec) {
+                kata_fwd1<DK, DV, C, true, true><<<grid, 64 * NW1, 0, st>>>(
+                    q, k, v, a.gdec, a.prefix, a.rec, o, s.T, s.NC, a.G, a.NSEG);
+                return hipGetLastError();
+            }
+        }
+        kata_fwd1<DK, DV, C, true, false><<<grid, 64 * NW1, 0, st>>>(q, k, v, nullptr, a.prefix, a.rec,
+                                                                    o, s.T, s.NC, a.G, a.NSEG);
+    } else {
+        if (a.gdec) return hipErrorInvalidValue;
+        kata_fwd1<DK, DV, C, false, false><<<grid, 64 * NW1, 0, st>>>(q, k, v, nullptr, a.prefix, a.rec,
+                                                                     o, s.T, s.NC, a.G, a.NSEG);
+    }
     return hipGetLastError();
 }
 
 template <int DK, int DV>
-hipError_t launch_dk_dv1(const Shape& s, const void* q, const void* k, const void* v, float* rec,
-                         const float* prefix, void* o, int causal, int G, int NSEG,
-                         bool state_only, hipStream_t st) {
+hipError_t launch_dk_dv1(const Shape& s, const Args1& a, hipStream_t st) {
     switch (s.C) {
-        case 32: return launch_dk_dv_c1<DK, DV, 32>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
-        case 64: return launch_dk_dv_c1<DK, DV, 64>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
-        case 128: return launch_dk_dv_c1<DK, DV, 128>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+        case 32: return launch_dk_dv_c1<DK, DV, 32>(s, a, st);
+        case 64: return launch_dk_dv_c1<DK, DV, 64>(s, a, st);
+        case 128: return launch_dk_dv_c1<DK, DV, 128>(s, a, st);
     }
     return hipErrorInvalidValue;
 }
 
 template <int DK>
-hipError_t launch_dk1(const Shape& s, const void* q, const void* k, const void* v, float* rec,
-                      const float* prefix, void* o, int causal, int G, int NSEG, bool state_only,
-                      hipStream_t st) {
+hipError_t launch_dk1(const Shape& s, const Args1& a, hipStream_t st) {
     switch (s.dv) {
-        case 16: return launch_dk_dv1<DK, 16>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
-        case 32: return launch_dk_dv1<DK, 32>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
-        case 64: return launch_dk_dv1<DK, 64>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+        case 16: return launch_dk_dv1<DK, 16>(s, a, st);
+        case 32: return launch_dk_dv1<DK, 32>(s, a, st);
+        case 64: return launch_dk_dv1<DK, 64>(s, a, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t dispatch1(const Shape& s, const void* q, const void* k, const void* v, float* rec,
-                     const float* prefix, void* o, int causal, int G, int NSEG, bool state_only,
-                     hipStream_t st) {
-    return s.dk == 16 ? launch_dk1<16>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st)
-                      : launch_dk1<32>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+hipError_t dispatch1(const Shape& s, const Args1& a, hipStream_t st) {
+    return s.dk == 16 ? launch_dk1<16>(s, a, st) : launch_dk1<32>(s, a, st);
 }
 
 unsigned conv_blocks(size_t n) { return (unsigned)std::min<size_t>((n + 255) / 256, 4096); }
@@ -411,13 +512,26 @@ int first_record_floats(int dk, int dv) { return (dk / 16) * (dv / 16 + 1) * 256
 
 hipError_t launch_seg_state1(const Shape& s, const void* k, const void* v, float* rec, int G,
                              int NSEG, hipStream_t st) {
-    return dispatch1(s, nullptr, k, v, rec, nullptr, nullptr, 1, G, NSEG, true, st);
+    return dispatch1(s, Args1{nullptr, k, v, nullptr, rec, nullptr, nullptr, nullptr, 1, G, NSEG, true}, st);
 }
 
 hipError_t launch_fwd1(const Shape& s, const void* q, const void* k, const void* v,
                        const float* prefix, float* final_rec, void* o, int causal, int G,
                        int NSEG, hipStream_t st) {
-    return dispatch1(s, q, k, v, final_rec, prefix, o, causal, G, NSEG, false, st);
+    return dispatch1(s, Args1{q, k, v, nullptr, final_rec, nullptr, prefix, o, causal, G, NSEG, false}, st);
+}
+
+bool first_decay_supported(const Shape& s) { return first_supported(s) && (s.C == 32 || s.C == 64); }
+
+hipError_t launch_seg_state1_decay(const Shape& s, const void* k, const void* v, const float* gdec,
+                                   float* rec, float* segdec, int G, int NSEG, hipStream_t st) {
+    return dispatch1(s, Args1{nullptr, k, v, gdec, rec, segdec, nullptr, nullptr, 1, G, NSEG, true}, st);
+}
+
+hipError_t launch_fwd1_decay(const Shape& s, const void* q, const void* k, const void* v,
+                             const float* gdec, const float* prefix, float* final_rec, void* o,
+                             int G, int NSEG, hipStream_t st) {
+    return dispatch1(s, Args1{q, k, v, gdec, final_rec, nullptr, prefix, o, 1, G, NSEG, false}, st);
 }
 
 hipError_t launch_record_from_packed1(float* rec, const float* S, const float* z, int dk, int dv,

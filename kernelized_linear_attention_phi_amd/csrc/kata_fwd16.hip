@@ -147,48 +147,6 @@ __device__ __forceinline__ u32x4_t lift_keys_own(int i, const float (&ka)[8], co
 // j weighted exp(b_last - b_j) (applied as sqrt to the key before the
 // quadratic lift).
 
-constexpr float kLog2e = 1.4426950408889634f;
-
-// 2^x for x <= 0 with v_exp_f32 (results below the fp32 normal range may flush
-// to zero, which only drops weights under 2^-126).
-__device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
-
-struct ChunkDecay {
-    float b;      // lane t (< C): b_t; lanes past the chunk: b_{C-1}
-    float last;   // b_{C-1} (positions past a ragged end carry g = 0)
-};
-
-// Inclusive scan of the staged log-decays over the wavefront (lane = position).
-template <int C>
-__device__ __forceinline__ ChunkDecay chunk_decay(const char* staged_g, const Lane& L) {
-    float x = L.lane < C ? reinterpret_cast<const float*>(staged_g)[L.lane] * kLog2e : 0.0f;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const float y = __shfl_up(x, d, 64);
-        if (L.lane >= d) x += y;
-    }
-    return ChunkDecay{x, __shfl(x, C - 1, 64)};
-}
-
-// The key positions' b values of one chunk, kept in LDS rather than registers
-// (one 64-float row per wavefront, rewritten each chunk by the same
-// wavefront): b(jb, r) is position 16 jb + 4g + r; last = b_{C-1}.
-struct KeyDecay {
-    const float* row = nullptr;   // this lane's view of the row: + 4g
-    float last = 0.0f;
-    __device__ float b(int jb, int r) const { return row[16 * jb + r]; }
-};
-
-// Writes the chunk's b (lane = position; lanes past the chunk hold b_{C-1}) to
-// this wavefront's row.
-__device__ __forceinline__ KeyDecay key_decays(const ChunkDecay& cd, float* wrow, const Lane& L) {
-    wrow[L.lane] = cd.b;
-    return KeyDecay{wrow + 4 * L.g, cd.last};
-}
-
-// Bytes of LDS for the rows of NW wavefronts (gated kernels only).
-constexpr int kKeyDecayRowBytes = 64 * 4;
-
 // State leaving a chunk: every accumulator scaled by a = exp(b_last) (the keys
 // of the chunk are scaled inside state_update).
 template <int DV, int C>

@@ -117,6 +117,14 @@ hipError_t launch_seg_state1(const Shape& s, const void* k, const void* v, float
 hipError_t launch_fwd1(const Shape& s, const void* q, const void* k, const void* v,
                        const float* prefix, float* final_rec, void* o, int causal, int G,
                        int NSEG, hipStream_t st);
+// Decay-gated variants (causal, chunk 32 or 64): gdec [BH, T] log-decays;
+// the state kernel also writes each segment's decay factor to segdec [BH, NSEG].
+bool first_decay_supported(const Shape& s);
+hipError_t launch_seg_state1_decay(const Shape& s, const void* k, const void* v, const float* gdec,
+                                   float* rec, float* segdec, int G, int NSEG, hipStream_t st);
+hipError_t launch_fwd1_decay(const Shape& s, const void* q, const void* k, const void* v,
+                             const float* gdec, const float* prefix, float* final_rec, void* o,
+                             int G, int NSEG, hipStream_t st);
 hipError_t launch_record_from_packed1(float* rec, const float* S, const float* z, int dk, int dv,
                                       int nrec, hipStream_t st);
 hipError_t launch_record_to_packed1(const float* rec, float* S, float* z, int dk, int dv, int nrec,

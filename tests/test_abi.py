@@ -143,14 +143,22 @@ def test_decay_rejects_before_launch(L):
     assert ws(1, 8, 4096, 32, 64, 128, BF16, SEQUENTIAL) == 0
     assert ws(1, 8, 4096, 16, 64, 64, F32, SCAN) == 8 * 64 * (136 * 64 * 4 + 136 * 4 + 4)
     dex = L.kata_chunked_fwd_decay_ex
-    dex_args = lambda f, pf, wsb: (FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 16, 64, 64, BF16, f, pf,
-                                   None, None, None, None, FAKE, wsb, None)
-    assert dex(*dex_args(IDENTITY, SEQUENTIAL, 1 << 40)) == EUNSUPPORTED   # identity: VALU, scan only
+    dex_args = lambda f, pf, wsb, dt=BF16, T=64, C=64: (FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, T, 16, 64, C,
+                                                         dt, f, pf, None, None, None, None, FAKE, wsb,
+                                                         None)
+    # identity: matrix cores for bf16 with chunk 32 or 64, else VALU with the scan only
+    assert dex(*dex_args(IDENTITY, SEQUENTIAL, 1 << 40, dt=F32)) == EUNSUPPORTED
+    assert dex(*dex_args(IDENTITY, SEQUENTIAL, 1 << 40, C=128)) == EUNSUPPORTED
+    assert dex(*dex_args(IDENTITY, SCAN, 1 << 40, T=66)) == EUNSUPPORTED   # matrix cores: T % 4
     assert dex(*dex_args(IDENTITY, SCAN, 16)) == EWORKSPACE
+    assert dex(*dex_args(IDENTITY, SCAN, 16, dt=F32)) == EWORKSPACE
     assert dex(*dex_args(5, SCAN, 1 << 40)) == EINVAL
     wsx = L.kata_chunked_fwd_decay_ex_workspace
     assert wsx(1, 8, 131072, 16, 64, 64, BF16, PSD, SCAN) == ws(1, 8, 131072, 16, 64, 64, BF16, SCAN)
-    assert wsx(1, 2, 64, 16, 64, 64, BF16, IDENTITY, SCAN) == 2 * 16 * 64 * 4 + 256 + 256
+    assert wsx(1, 2, 64, 16, 64, 64, F32, IDENTITY, SCAN) == 2 * 16 * 64 * 4 + 256 + 256
+    rec1 = 1 * 5 * 256                   # identity, d_k = 16, d_v = 64: four value tiles + z
+    assert wsx(1, 8, 131072, 16, 64, 64, BF16, IDENTITY, SEQUENTIAL) == 3 * 8 * rec1 * 4
+    assert wsx(1, 8, 131072, 16, 64, 64, BF16, IDENTITY, SCAN) > 3 * 8 * rec1 * 4
     dec = L.kata_decode_step_decay
     assert dec(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 16, 64, BF16, None) == EINVAL
     assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 12, 64, BF16, None) == EUNSUPPORTED
