@@ -176,8 +176,9 @@ def decode_bench(kata, torch, steps=1024, n_seq=512, heads=4, dk=16, dv=64, reps
 
 def decay_gate(kata, torch, gen, steps, warmup):
     """The fwd131k forward with per-token log-decays in [-0.05, 0] against the
-    ungated forward on the same inputs (both without state export), and the
-    gated decode step."""
+    ungated forward on the same inputs (both without state export), for the
+    PSD lift and for the first-order feature (orthant inputs), and the gated
+    decode step."""
     w = gen.WORKLOADS["fwd131k"]
     to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
     q, k, v = (to(a) for a in gen.gaussian_qkv(w.B, w.H, w.T, w.dk, w.dv, w.seed, w.dtype))
@@ -191,10 +192,23 @@ def decay_gate(kata, torch, gen, steps, warmup):
     ws2 = torch.empty(max(nb2, 1), dtype=torch.uint8, device="cuda")
     ms_u = time_calls(torch, lambda: kata.chunked_fwd_into(q, k, v, o, w.chunk, True, ws2),
                       steps, warmup)
+    del q, k, v
+    q, k, v = (to(a) for a in gen.orthant_qkv(w.B, w.H, w.T, w.dk, w.dv, w.seed, w.dtype))
+    nb3 = kata.chunked_fwd_decay_workspace(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1, "scan",
+                                           "identity")
+    ws3 = torch.empty(max(nb3, 1), dtype=torch.uint8, device="cuda")
+    ms_gi = time_calls(torch, lambda: kata.chunked_fwd_decay_into(
+        q, k, v, g, o, w.chunk, ws3, feature="identity"), steps, warmup)
+    nb4 = kata.chunked_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1, True, "identity")
+    ws4 = torch.empty(max(nb4, 1), dtype=torch.uint8, device="cuda")
+    ms_ui = time_calls(torch, lambda: kata.chunked_fwd_into(
+        q, k, v, o, w.chunk, True, ws4, feature="identity"), steps, warmup)
     dms, dgbs, _ = decode_bench(kata, torch, gated=True)
     return {"fwd131k_gated_ms": ms_g, "fwd131k_ungated_ms": ms_u,
             "fwd131k_gated_tokens_per_s": w.B * w.T / (ms_g * 1e-3),
             "gate_overhead": ms_g / ms_u - 1.0,
+            "fwd131k_identity_gated_ms": ms_gi, "fwd131k_identity_ungated_ms": ms_ui,
+            "identity_gate_overhead": ms_gi / ms_ui - 1.0,
             "decode_gated_ms_per_step": dms, "decode_gated_GBps": dgbs,
             "decode_gated_hbm_frac": dgbs / PEAK_HBM_GBS}
 
