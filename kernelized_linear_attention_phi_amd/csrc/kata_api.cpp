@@ -367,9 +367,11 @@ kata_status_t kata_flash_fwd(const void* q, const void* k, const void* v, void* 
 
 // ---- decay gate ----------------------------------------------------------------
 
-// Matrix-core paths for bf16 with C in {32, 64}: the PSD lift at d_k = 16 and
-// the identity feature at d_k = 16 or 32 (segments, scan or sequential prefix);
-// every other supported shape takes the fp32 VALU path (per-chunk records, scan
+// Matrix-core paths (segments, scan or sequential prefix): the PSD lift for
+// bf16 at d_k = 16 (C 32 or 64) and d_k = 32 (C 64 or 128), the identity
+// feature for bf16 with C 32 or 64. They stage each chunk's log-decays 16 bytes
+// at a time from T-aligned offsets, so with several heads T must be a multiple
+// of 4. Every other case takes the fp32 VALU path (per-chunk records, scan
 // prefix only).
 struct DecayPlan {
     FwdPlan fwd;           // matrix-core path
@@ -379,8 +381,10 @@ struct DecayPlan {
 
 static bool decay_plan(const Shape& s, kata_feature_t f, kata_prefix_t prefix, DecayPlan* d) {
     const size_t BH = (size_t)s.B * s.H;
-    if ((f == KATA_FEATURE_PSD && kata::mfma16_supported(s)) ||
-        (f == KATA_FEATURE_IDENTITY && kata::first_decay_supported(s))) {
+    const bool aligned_rows = s.T % 4 == 0 || BH <= 1;
+    if (aligned_rows &&
+        ((f == KATA_FEATURE_PSD && (kata::mfma16_supported(s) || kata::mfma32_supported(s))) ||
+         (f == KATA_FEATURE_IDENTITY && kata::first_decay_supported(s)))) {
         d->fwd = plan_fwd(s, 1, f, prefix);
         if (!d->fwd.ok) return false;
         d->dec_off = d->fwd.bytes;
@@ -436,9 +440,6 @@ kata_status_t kata_chunked_fwd_decay_ex(const void* q, const void* k, const void
         if (p && !aligned16(p)) return KATA_EINVAL;
     DecayPlan plan;
     if (!decay_plan(s, feature, prefix, &plan)) return KATA_EUNSUPPORTED;
-    // the matrix-core path reads each head's log-decay row 16 bytes at a time
-    // from T-aligned offsets
-    if (!empty && !plan.valu && T % 4 != 0 && H * B > 1) return KATA_EUNSUPPORTED;
     if (ws_bytes < plan.bytes || (plan.bytes && !workspace)) return KATA_EWORKSPACE;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const size_t nS = (size_t)s.D * s.dv, nz = s.D;
@@ -471,31 +472,35 @@ kata_status_t kata_chunked_fwd_decay_ex(const void* q, const void* k, const void
         return hip_status(e);
     }
     const FwdPlan& fp = plan.fwd;
-    const bool first = fp.mfma == 1;              // identity feature (else PSD, d_k = 16)
+    const int m = fp.mfma;                        // 1: identity feature; 16, 32: PSD lift at d_k
     float* rec = reinterpret_cast<float*>(ws + fp.S_off);
     float* init = reinterpret_cast<float*>(ws + fp.init_off);
     float* total = reinterpret_cast<float*>(ws + fp.total_off);
     const int nrec = (int)BH;
     auto output = [&](const float* pre, float* fin) {
-        return first ? kata::launch_fwd1_decay(s, q, k, v, log_decay, pre, fin, o, fp.G, fp.NSEG, hs)
-                     : kata::launch_fwd16_decay(s, q, k, v, log_decay, pre, fin, o, fp.G, fp.NSEG, hs);
+        return m == 1    ? kata::launch_fwd1_decay(s, q, k, v, log_decay, pre, fin, o, fp.G, fp.NSEG, hs)
+               : m == 16 ? kata::launch_fwd16_decay(s, q, k, v, log_decay, pre, fin, o, fp.G, fp.NSEG, hs)
+                         : kata::launch_fwd32_decay(s, q, k, v, log_decay, pre, fin, o, fp.G, fp.NSEG, hs);
     };
     if (S0)
-        e = first ? kata::launch_record_from_packed1(init, S0, z0, s.dk, s.dv, nrec, hs)
-                  : kata::launch_record_from_packed16(init, S0, z0, s.dv, nrec, hs);
+        e = m == 1    ? kata::launch_record_from_packed1(init, S0, z0, s.dk, s.dv, nrec, hs)
+            : m == 16 ? kata::launch_record_from_packed16(init, S0, z0, s.dv, nrec, hs)
+                      : kata::launch_record_from_packed32(init, S0, z0, s.dv, nrec, hs);
     if (fp.seq) {
         if (!S0 && e == hipSuccess) e = kata::launch_copy_or_zero(init, nullptr, BH * fp.REC, hs);
         if (e == hipSuccess) e = output(init, S_out ? total : nullptr);
         if (S_out && e == hipSuccess)
-            e = first ? kata::launch_record_to_packed1(total, S_out, z_out, s.dk, s.dv, nrec, hs)
-                      : kata::launch_record_to_packed16(total, S_out, z_out, s.dv, nrec, hs);
+            e = m == 1    ? kata::launch_record_to_packed1(total, S_out, z_out, s.dk, s.dv, nrec, hs)
+                : m == 16 ? kata::launch_record_to_packed16(total, S_out, z_out, s.dv, nrec, hs)
+                          : kata::launch_record_to_packed32(total, S_out, z_out, s.dv, nrec, hs);
     } else {
         float* segdec = reinterpret_cast<float*>(ws + plan.dec_off);
-        const kata::RecordExport ex{first ? kata::kRecIdent : kata::kRecPsd16, s.dk, s.dv, S_out,
-                                    z_out};
+        const kata::RecordExport ex{m == 1 ? kata::kRecIdent : m == 16 ? kata::kRecPsd16 : kata::kRecPsd32,
+                                    s.dk, s.dv, S_out, z_out};
         if (e == hipSuccess)
-            e = first ? kata::launch_seg_state1_decay(s, k, v, log_decay, rec, segdec, fp.G, fp.NSEG, hs)
-                      : kata::launch_seg_state16_decay(s, k, v, log_decay, rec, segdec, fp.G, fp.NSEG, hs);
+            e = m == 1    ? kata::launch_seg_state1_decay(s, k, v, log_decay, rec, segdec, fp.G, fp.NSEG, hs)
+                : m == 16 ? kata::launch_seg_state16_decay(s, k, v, log_decay, rec, segdec, fp.G, fp.NSEG, hs)
+                          : kata::launch_seg_state32_decay(s, k, v, log_decay, rec, segdec, fp.G, fp.NSEG, hs);
         if (e == hipSuccess)
             e = kata::launch_scan_records_decay(rec, segdec, nrec, fp.NSEG, fp.REC,
                                                 S0 ? init : nullptr, nullptr, nullptr, hs,

@@ -36,6 +36,13 @@
 // "ones" value tile. Across chunks, z = sum phi(k) is kept as the Gram matrix
 // Z = sum k k^T in four 16 x 16 tiles (LL, LU, UL, UU; wavefront w keeps tile
 // w), and phi(q).z = q^T Z q is two MFMAs (Z q) plus an 8-term dot product.
+//
+// Decay gate (DECAY, causal): the chunk's log-decays are staged after v; each
+// wavefront keeps the cumulative values b of the chunk's positions in an LDS
+// row of its own. Key coordinates are scaled by 2^{(b_last - b_j)/2} before the
+// quadratic lift and the Gram product (so S and Z receive 2^{b_last - b_j}), the
+// state by 2^{b_last} per chunk, the prefix term and q^T Z q of query t by
+// 2^{b_t}, and the intra weights by 2^{b_t - b_j}.
 #include "kata_chunk.h"
 #include "kata_internal.h"
 #include "kata_records.h"
@@ -57,7 +64,7 @@ template <int C> __host__ __device__ constexpr int nw32() { return C == 128 ? 8 
 template <int C> constexpr int kThreads32 = 64 * nw32<C>();
 template <int C> constexpr int kWavesPerSimd32 = nw32<C>() / 4;
 
-template <int DV, int C>
+template <int DV, int C, bool GATE = false>
 struct Cfg32 {
     static constexpr int NW = nw32<C>();
     static constexpr int TPW = 32 / NW;           // full feature tiles per wavefront
@@ -65,7 +72,7 @@ struct Cfg32 {
     static constexpr int TT = C / 16;             // query tiles per chunk
     static constexpr int TW = TT / NW;            // query tiles per wavefront
     static constexpr int KS = C / 32;             // 32-token K-steps per chunk
-    using IO = ChunkIO<DK, DV, C, NW>;
+    using IO = ChunkIO<DK, DV, C, NW, NW, GATE>;
     // LDS: two chunk buffers | bf16 state operands | one output tile per wavefront
     static constexpr int SPAIR = 16 * NTV * 1024;   // S^T operands of tile pairs 0..15
     static constexpr int S32 = NTV * 512;           // S^T operands of tile 32
@@ -74,8 +81,9 @@ struct Cfg32 {
     static constexpr int OROW = DV * 2 + 16;        // LDS row stride of a staged output tile
     static constexpr int OTILE = 16 * OROW;
     static constexpr int OU = 2 * DV;               // 16-byte units per 16-row output tile
-    static constexpr int LDS_FWD = 2 * IO::BUF + SB + NW * OTILE;
-    static constexpr int LDS_SEG = 4 * IO::BUF;     // 4-deep staging of k | v
+    static constexpr int KROW = GATE ? 4 * C : 0;   // key-decay row of one wavefront
+    static constexpr int LDS_FWD = 2 * IO::BUF + SB + NW * OTILE + NW * KROW;
+    static constexpr int LDS_SEG = 4 * IO::BUF + NW * KROW;   // 4-deep staging of k | v (| g)
     static constexpr int REC = NFT * NTV * 256 + NZ * 256;   // floats per state record
     static_assert(TW >= 1, "at least one query tile per wavefront");
     static_assert(NW * TPW == 32 && TPW % 2 == 0, "tile pairs do not straddle wavefronts");
@@ -242,13 +250,24 @@ __device__ __forceinline__ u32x4_t pack8(const float (&x)[8]) {
     return u32x4_t{pk2(x[0], x[1]), pk2(x[2], x[3]), pk2(x[4], x[5]), pk2(x[6], x[7])};
 }
 
-// S(own tiles) += phi(K_m)^T V_m, Z(own tile) += K_m^T K_m over one K-step.
-template <int W, int DV, int C>
+// S(own tiles) += phi(K_m)^T V_m, Z(own tile) += K_m^T K_m over one K-step;
+// with DECAY each key weighted 2^{b_last - b_j}.
+template <int W, int DV, int C, bool DECAY = false>
 __device__ __forceinline__ void state_step(State32<DV, C>& st, const bf16_t* bk, const bf16_t* bv,
-                                           int m, const Lane& L) {
+                                           int m, const Lane& L, const KeyDecay& kd = KeyDecay{}) {
     using F = Cfg32<DV, C>;
     float kl[8], ku[8];
     key_columns<needs_l<DV, C, W>(), needs_u<DV, C, W>()>(bk, m, L, kl, ku);
+    if constexpr (DECAY) {
+        // slot s is token 32m + 16(s/4) + 4g + s%4; both factors of every lifted
+        // product and of the Gram product carry the square root of its weight
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const float f = exp2_neg(0.5f * (kd.last - kd.b(2 * m + s / 4, s % 4)));
+            kl[s] *= f;
+            ku[s] *= f;
+        }
+    }
     if constexpr (W < 4) {
         // Gram tile W: LL, LU, UL, UU (A rows = first half, B columns = second)
         const u32x4_t gl = pack8(kl), gu = pack8(ku);
@@ -268,6 +287,50 @@ __device__ __forceinline__ void state_step(State32<DV, C>& st, const bf16_t* bk,
     });
     if constexpr (has_x<DV, C, W>())
         st.x = mma32(lift_keys_mixed(kl, ku, L), vop[xnt<DV, C, W>()], st.x);
+}
+
+// ---- decay gate ---------------------------------------------------------------------
+
+// Cumulative log2-decays of the staged chunk written to this wavefront's row
+// (position p at row[p], C = 128 takes positions lane and 64 + lane); returns
+// the view of KeyDecay with last = b_{C-1}.
+template <int C>
+__device__ __forceinline__ KeyDecay chunk_key_decays(const char* staged_g, float* wrow,
+                                                     const Lane& L) {
+    if constexpr (C <= 64) {
+        return key_decays(chunk_decay<C>(staged_g, L), wrow, L);
+    } else {
+        static_assert(C == 128, "chunk of 64 or 128 positions");
+        const float* g = reinterpret_cast<const float*>(staged_g);
+        float lo = g[L.lane] * kLog2e, hi = g[64 + L.lane] * kLog2e;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const float ylo = __shfl_up(lo, d, 64);
+            const float yhi = __shfl_up(hi, d, 64);
+            if (L.lane >= d) {
+                lo += ylo;
+                hi += yhi;
+            }
+        }
+        hi += __shfl(lo, 63, 64);
+        wrow[L.lane] = lo;
+        wrow[64 + L.lane] = hi;
+        return KeyDecay{wrow + 4 * L.g, __shfl(hi, 63, 64)};
+    }
+}
+
+// The running state leaving a chunk: every accumulator this wavefront holds
+// times 2^{b_last}.
+template <int W, int DV, int C>
+__device__ __forceinline__ void decay_state32(State32<DV, C>& st, float last) {
+    using F = Cfg32<DV, C>;
+    const float a = exp2_neg(last);
+#pragma unroll
+    for (int i = 0; i < F::TPW; ++i)
+#pragma unroll
+        for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] *= a;
+    if constexpr (has_x<DV, C, W>()) st.x *= a;
+    if constexpr (W < 4) st.z *= a;
 }
 
 // ---- state records: S unit (tile t, value tile nt) at ((t*NTV + nt)*64 + lane)*4 + r,
@@ -329,14 +392,16 @@ __device__ __forceinline__ void publish_state(char* sb, const State32<DV, C>& st
 
 // ---- per-wavefront bodies ----------------------------------------------------------
 
-template <int W, int DV, int C>
-__device__ __forceinline__ void seg_state_body32(const bf16_t* k, const bf16_t* v, float* rec,
-                                                 char* lds, int T, int NC, int G, int NSEG,
-                                                 const Lane& L) {
-    using F = Cfg32<DV, C>;
+template <int W, int DV, int C, bool DECAY>
+__device__ __forceinline__ void seg_state_body32(const bf16_t* k, const bf16_t* v, const float* gdec,
+                                                 float* rec, float* segdec, char* lds, int T,
+                                                 int NC, int G, int NSEG, const Lane& L) {
+    using F = Cfg32<DV, C, DECAY>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    LoadPipeline<DK, DV, C, F::NW, 4> P{lds, seg * G, min(NC, seg * G + G), T, bh * T};
+    LoadPipeline<DK, DV, C, F::NW, 4, DECAY> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, gdec};
+    float* krow = reinterpret_cast<float*>(lds + 4 * F::IO::BUF + W * F::KROW);
+    float lsum = 0.0f;                             // log2 of the segment's decay
     State32<DV, C> st;
 #pragma unroll
     for (int i = 0; i < F::TPW; ++i)
@@ -351,24 +416,33 @@ __device__ __forceinline__ void seg_state_body32(const bf16_t* k, const bf16_t* 
         const char* buf = P.buffer(c);
         const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::IO::QB);
         const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::IO::QB);
+        KeyDecay kd{};
+        if constexpr (DECAY) {
+            kd = chunk_key_decays<C>(buf + 2 * F::IO::QB + F::IO::VB, krow, L);
+            decay_state32<W, DV, C>(st, kd.last);
+            lsum += kd.last;
+        }
 #pragma unroll
-        for (int m = 0; m < F::KS; ++m) state_step<W, DV, C>(st, bk, bv, m, L);
+        for (int m = 0; m < F::KS; ++m) state_step<W, DV, C, DECAY>(st, bk, bv, m, L, kd);
         compiler_fence();
     }
     record_store32<W, DV, C>(rec + (bh * NSEG + seg) * (size_t)F::REC, st, L);
+    if (DECAY && W == 0 && L.lane == 0) segdec[bh * NSEG + seg] = exp2_neg(lsum);
 }
 
-template <int W, int DV, int C, bool CAUSAL>
+template <int W, int DV, int C, bool CAUSAL, bool DECAY>
 __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, const bf16_t* v,
-                                           const float* prefix, float* final_rec, bf16_t* o,
-                                           char* lds, int T, int NC, int G, int NSEG,
-                                           const Lane& L) {
-    using F = Cfg32<DV, C>;
+                                           const float* gdec, const float* prefix,
+                                           float* final_rec, bf16_t* o, char* lds, int T, int NC,
+                                           int G, int NSEG, const Lane& L) {
+    using F = Cfg32<DV, C, DECAY>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    Pipeline<DK, DV, C, F::NW> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true};
+    Pipeline<DK, DV, C, F::NW, F::NW, DECAY> P{lds, seg * G, min(NC, seg * G + G), T, bh * T,
+                                               true, gdec};
     char* sb = lds + 2 * F::IO::BUF;
     char* otile = sb + F::SB + W * F::OTILE;
+    float* krow = reinterpret_cast<float*>(sb + F::SB + F::NW * F::OTILE + W * F::KROW);
 
     State32<DV, C> st;
     record_load32<W, DV, C>(prefix + (CAUSAL ? bh * NSEG + seg : bh) * (size_t)F::REC, st, L);
@@ -381,6 +455,8 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
         const bf16_t* bq = reinterpret_cast<const bf16_t*>(buf);
         const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::IO::QB);
         const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::IO::QB);
+        KeyDecay kd{};
+        if constexpr (DECAY) kd = chunk_key_decays<C>(buf + 2 * F::IO::QB + F::IO::VB, krow, L);
 
         // the state before this chunk, as bf16 operands for every wavefront (the
         // acquire barrier guarantees the previous chunk's readers are done)
@@ -438,6 +514,14 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
                 d += __shfl_xor(d, 32, 64);
                 di = d;
             }
+            float bt = 0.0f;                              // b of this lane's query
+            if constexpr (DECAY) {                        // the prefix state decays to query t
+                bt = krow[16 * tt + L.c16];
+                const float e = exp2_neg(bt);
+#pragma unroll
+                for (int nt = 0; nt < F::NTV; ++nt) num[nt] *= e;
+                di *= e;
+            }
             // ---- intra-chunk term: A = (Q K^T)^2 masked to j <= t, num += A [V | 1]
             if (CAUSAL) {
                 const int t = 16 * tt + L.c16;
@@ -455,7 +539,8 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int j = 32 * m + 16 * h + 4 * L.g + r;
-                            const float x = sc[r] * sc[r];
+                            float x = sc[r] * sc[r];
+                            if constexpr (DECAY) x *= exp2_neg(bt - kd.b(2 * m + h, r));
                             w[4 * h + r] = (!diag || j <= t) ? x : 0.0f;
                         }
                     }
@@ -498,8 +583,9 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
 
         // ---- running state: S += phi(K_c)^T V_c, Z += K_c^T K_c
         if (CAUSAL) {
+            if constexpr (DECAY) decay_state32<W, DV, C>(st, kd.last);
 #pragma unroll
-            for (int m = 0; m < F::KS; ++m) state_step<W, DV, C>(st, bk, bv, m, L);
+            for (int m = 0; m < F::KS; ++m) state_step<W, DV, C, DECAY>(st, bk, bv, m, L, kd);
         }
         compiler_fence();
     }
@@ -518,73 +604,92 @@ __device__ __forceinline__ void by_wave(int w, F&& f) {
 
 // ---- kernels -------------------------------------------------------------------
 
-template <int DV, int C>
+template <int DV, int C, bool DECAY>
 __global__ __launch_bounds__(kThreads32<C>, kWavesPerSimd32<C>)
 void kata_seg_state32(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-                      float* __restrict__ rec, int T, int NC, int G, int NSEG) {
-    using F = Cfg32<DV, C>;
+                      const float* __restrict__ gdec, float* __restrict__ rec,
+                      float* __restrict__ segdec, int T, int NC, int G, int NSEG) {
+    using F = Cfg32<DV, C, DECAY>;
     __shared__ __attribute__((aligned(16))) char lds[F::LDS_SEG];
     const Lane L;
     by_wave<DV, C>(L.w, [&](auto wc) {
-        seg_state_body32<decltype(wc)::value, DV, C>(k, v, rec, lds, T, NC, G, NSEG,
-                                                     as_wave<decltype(wc)::value>(L));
+        seg_state_body32<decltype(wc)::value, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC,
+                                                            G, NSEG, as_wave<decltype(wc)::value>(L));
     });
 }
 
-template <int DV, int C, bool CAUSAL>
+template <int DV, int C, bool CAUSAL, bool DECAY>
 __global__ __launch_bounds__(kThreads32<C>, kWavesPerSimd32<C>)
 void kata_fwd32(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                const bf16_t* __restrict__ v, const float* __restrict__ prefix,
-                float* __restrict__ final_rec, bf16_t* __restrict__ o, int T, int NC, int G,
-                int NSEG) {
-    using F = Cfg32<DV, C>;
+                const bf16_t* __restrict__ v, const float* __restrict__ gdec,
+                const float* __restrict__ prefix, float* __restrict__ final_rec,
+                bf16_t* __restrict__ o, int T, int NC, int G, int NSEG) {
+    using F = Cfg32<DV, C, DECAY>;
     __shared__ __attribute__((aligned(16))) char lds[F::LDS_FWD];
     const Lane L;
     by_wave<DV, C>(L.w, [&](auto wc) {
-        fwd_body32<decltype(wc)::value, DV, C, CAUSAL>(q, k, v, prefix, final_rec, o, lds, T, NC,
-                                                       G, NSEG, as_wave<decltype(wc)::value>(L));
+        fwd_body32<decltype(wc)::value, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o,
+                                                              lds, T, NC, G, NSEG,
+                                                              as_wave<decltype(wc)::value>(L));
     });
 }
 
+// Launch arguments shared by every shape: gdec (log-decays, NULL = no gate;
+// causal only), segdec (per-segment decays, state kernel), rec (segment
+// records for the state kernel, the final-state records for the output
+// kernel).
+struct Args32 {
+    const void *q, *k, *v;
+    const float* gdec;
+    float* rec;
+    float* segdec;
+    const float* prefix;
+    void* o;
+    int causal, G, NSEG;
+    bool state_only;
+};
+
 template <int DV, int C>
-hipError_t launch_dv_c32(const Shape& s, const void* q, const void* k, const void* v, float* rec,
-                         const float* prefix, void* o, int causal, int G, int NSEG,
-                         bool state_only, hipStream_t st) {
-    dim3 grid(NSEG, s.B * s.H);
+hipError_t launch_dv_c32(const Shape& s, const Args32& a, hipStream_t st) {
+    dim3 grid(a.NSEG, s.B * s.H);
     constexpr int threads = kThreads32<C>;
-    if (state_only) {
-        kata_seg_state32<DV, C><<<grid, threads, 0, st>>>((const bf16_t*)k, (const bf16_t*)v, rec,
-                                                           s.T, s.NC, G, NSEG);
-    } else if (causal) {
-        kata_fwd32<DV, C, true><<<grid, threads, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
-                                                           (const bf16_t*)v, prefix, rec,
-                                                           (bf16_t*)o, s.T, s.NC, G, NSEG);
+    const bf16_t *q = (const bf16_t*)a.q, *k = (const bf16_t*)a.k, *v = (const bf16_t*)a.v;
+    bf16_t* o = (bf16_t*)a.o;
+    if (a.gdec && !a.causal) return hipErrorInvalidValue;
+    if (a.state_only) {
+        if (a.gdec)
+            kata_seg_state32<DV, C, true><<<grid, threads, 0, st>>>(k, v, a.gdec, a.rec, a.segdec,
+                                                                     s.T, s.NC, a.G, a.NSEG);
+        else
+            kata_seg_state32<DV, C, false><<<grid, threads, 0, st>>>(k, v, nullptr, a.rec, nullptr,
+                                                                      s.T, s.NC, a.G, a.NSEG);
+    } else if (a.gdec) {
+        kata_fwd32<DV, C, true, true><<<grid, threads, 0, st>>>(q, k, v, a.gdec, a.prefix, a.rec, o,
+                                                                 s.T, s.NC, a.G, a.NSEG);
+    } else if (a.causal) {
+        kata_fwd32<DV, C, true, false><<<grid, threads, 0, st>>>(q, k, v, nullptr, a.prefix, a.rec,
+                                                                  o, s.T, s.NC, a.G, a.NSEG);
     } else {
-        kata_fwd32<DV, C, false><<<grid, threads, 0, st>>>((const bf16_t*)q, (const bf16_t*)k,
-                                                            (const bf16_t*)v, prefix, rec,
-                                                            (bf16_t*)o, s.T, s.NC, G, NSEG);
+        kata_fwd32<DV, C, false, false><<<grid, threads, 0, st>>>(q, k, v, nullptr, a.prefix, a.rec,
+                                                                   o, s.T, s.NC, a.G, a.NSEG);
     }
     return hipGetLastError();
 }
 
 template <int C>
-hipError_t launch_c32(const Shape& s, const void* q, const void* k, const void* v, float* rec,
-                      const float* prefix, void* o, int causal, int G, int NSEG, bool state_only,
-                      hipStream_t st) {
+hipError_t launch_c32(const Shape& s, const Args32& a, hipStream_t st) {
     switch (s.dv) {
-        case 16: return launch_dv_c32<16, C>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
-        case 32: return launch_dv_c32<32, C>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
-        case 64: return launch_dv_c32<64, C>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+        case 16: return launch_dv_c32<16, C>(s, a, st);
+        case 32: return launch_dv_c32<32, C>(s, a, st);
+        case 64: return launch_dv_c32<64, C>(s, a, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t dispatch32(const Shape& s, const void* q, const void* k, const void* v, float* rec,
-                      const float* prefix, void* o, int causal, int G, int NSEG, bool state_only,
-                      hipStream_t st) {
+hipError_t dispatch32(const Shape& s, const Args32& a, hipStream_t st) {
     switch (s.C) {
-        case 64: return launch_c32<64>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
-        case 128: return launch_c32<128>(s, q, k, v, rec, prefix, o, causal, G, NSEG, state_only, st);
+        case 64: return launch_c32<64>(s, a, st);
+        case 128: return launch_c32<128>(s, a, st);
     }
     return hipErrorInvalidValue;
 }
@@ -631,13 +736,27 @@ int mfma32_record_floats(int dv) { return NFT * (dv / 16) * 256 + NZ * 256; }
 
 hipError_t launch_seg_state32(const Shape& s, const void* k, const void* v, float* rec, int G,
                               int NSEG, hipStream_t st) {
-    return dispatch32(s, nullptr, k, v, rec, nullptr, nullptr, 1, G, NSEG, true, st);
+    return dispatch32(s, Args32{nullptr, k, v, nullptr, rec, nullptr, nullptr, nullptr, 1, G, NSEG, true},
+                      st);
 }
 
 hipError_t launch_fwd32(const Shape& s, const void* q, const void* k, const void* v,
                         const float* prefix, float* final_rec, void* o, int causal, int G,
                         int NSEG, hipStream_t st) {
-    return dispatch32(s, q, k, v, final_rec, prefix, o, causal, G, NSEG, false, st);
+    return dispatch32(s, Args32{q, k, v, nullptr, final_rec, nullptr, prefix, o, causal, G, NSEG, false},
+                      st);
+}
+
+hipError_t launch_seg_state32_decay(const Shape& s, const void* k, const void* v, const float* gdec,
+                                    float* rec, float* segdec, int G, int NSEG, hipStream_t st) {
+    return dispatch32(s, Args32{nullptr, k, v, gdec, rec, segdec, nullptr, nullptr, 1, G, NSEG, true},
+                      st);
+}
+
+hipError_t launch_fwd32_decay(const Shape& s, const void* q, const void* k, const void* v,
+                              const float* gdec, const float* prefix, float* final_rec, void* o,
+                              int G, int NSEG, hipStream_t st) {
+    return dispatch32(s, Args32{q, k, v, gdec, final_rec, nullptr, prefix, o, 1, G, NSEG, false}, st);
 }
 
 hipError_t launch_record_from_packed32(float* rec, const float* S, const float* z, int dv,

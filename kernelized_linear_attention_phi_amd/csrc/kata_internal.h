@@ -104,6 +104,15 @@ hipError_t launch_seg_state32(const Shape& s, const void* k, const void* v, floa
 hipError_t launch_fwd32(const Shape& s, const void* q, const void* k, const void* v,
                         const float* prefix, float* final_rec, void* o, int causal, int G,
                         int NSEG, hipStream_t st);
+// Decay-gated (causal only, as for d_k = 16): gdec [BH, T] per-token log-decays
+// (<= 0); the state kernel also writes each segment's total decay to segdec
+// [BH, NSEG].
+hipError_t launch_seg_state32_decay(const Shape& s, const void* k, const void* v,
+                                    const float* gdec, float* rec, float* segdec, int G, int NSEG,
+                                    hipStream_t st);
+hipError_t launch_fwd32_decay(const Shape& s, const void* q, const void* k, const void* v,
+                              const float* gdec, const float* prefix, float* final_rec, void* o,
+                              int G, int NSEG, hipStream_t st);
 hipError_t launch_record_from_packed32(float* rec, const float* S, const float* z, int dv,
                                        int nrec, hipStream_t st);
 hipError_t launch_record_to_packed32(const float* rec, float* S, float* z, int dv, int nrec,

@@ -128,19 +128,26 @@ def test_decay_rejects_before_launch(L):
     assert fwd_decay(L, prefix=4) == EINVAL
     # shapes without a matrix-core path take the VALU path, scan prefix only
     assert fwd_decay(L, dtype=F32, prefix=SEQUENTIAL) == EUNSUPPORTED
-    assert fwd_decay(L, dk=32, C=128, prefix=SEQUENTIAL) == EUNSUPPORTED
+    assert fwd_decay(L, dk=32, C=32, prefix=SEQUENTIAL) == EUNSUPPORTED
     assert fwd_decay(L, C=128, prefix=SEQUENTIAL) == EUNSUPPORTED
     assert fwd_decay(L, dtype=F32, ws_bytes=16) == EWORKSPACE
     assert fwd_decay(L, dk=12) == EUNSUPPORTED
-    assert fwd_decay(L, T=66) == EUNSUPPORTED                 # matrix-core path: T % 4 == 0
+    # several heads with T % 4 != 0: the VALU path, scan prefix only
+    assert fwd_decay(L, T=66, prefix=SEQUENTIAL) == EUNSUPPORTED
+    assert fwd_decay(L, dk=32, C=128, T=66, prefix=SEQUENTIAL) == EUNSUPPORTED
     assert fwd_decay(L, ws_bytes=16) == EWORKSPACE
     assert fwd_decay(L, T=0, q=None, o=None, g=None, ws=None, ws_bytes=0) == OK   # empty
     ws = L.kata_chunked_fwd_decay_workspace
     assert ws(1, 8, 131072, 16, 64, 64, BF16, SCAN) > ws(1, 8, 131072, 16, 64, 64, BF16, SEQUENTIAL) > 0
     # VALU path: per-chunk S and z records and one decay factor per chunk
-    nrec = 8 * 32
-    assert ws(1, 8, 4096, 32, 64, 128, BF16, SCAN) == nrec * 528 * 64 * 4 + nrec * 528 * 4 + nrec * 4
-    assert ws(1, 8, 4096, 32, 64, 128, BF16, SEQUENTIAL) == 0
+    nrec = 8 * 128
+    assert ws(1, 8, 4096, 32, 64, 32, BF16, SCAN) == nrec * 528 * 64 * 4 + nrec * 528 * 4 + nrec * 4
+    assert ws(1, 8, 4096, 32, 64, 32, BF16, SEQUENTIAL) == 0
+    # d_k = 32 on the matrix cores: segment records, initial and final state
+    rec32 = 33 * 4 * 256 + 4 * 256
+    assert ws(1, 8, 4096, 32, 64, 128, BF16, SEQUENTIAL) == 3 * 8 * rec32 * 4
+    assert ws(1, 8, 4096, 32, 64, 128, BF16, SCAN) > 3 * 8 * rec32 * 4
+    assert ws(2, 4, 4098, 32, 64, 128, BF16, SEQUENTIAL) == 0      # T % 4 != 0, several heads
     assert ws(1, 8, 4096, 16, 64, 64, F32, SCAN) == 8 * 64 * (136 * 64 * 4 + 136 * 4 + 4)
     dex = L.kata_chunked_fwd_decay_ex
     dex_args = lambda f, pf, wsb, dt=BF16, T=64, C=64: (FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, T, 16, 64, C,
@@ -149,7 +156,7 @@ def test_decay_rejects_before_launch(L):
     # identity: matrix cores for bf16 with chunk 32 or 64, else VALU with the scan only
     assert dex(*dex_args(IDENTITY, SEQUENTIAL, 1 << 40, dt=F32)) == EUNSUPPORTED
     assert dex(*dex_args(IDENTITY, SEQUENTIAL, 1 << 40, C=128)) == EUNSUPPORTED
-    assert dex(*dex_args(IDENTITY, SCAN, 1 << 40, T=66)) == EUNSUPPORTED   # matrix cores: T % 4
+    assert dex(*dex_args(IDENTITY, SEQUENTIAL, 1 << 40, T=66)) == EUNSUPPORTED   # VALU: scan only
     assert dex(*dex_args(IDENTITY, SCAN, 16)) == EWORKSPACE
     assert dex(*dex_args(IDENTITY, SCAN, 16, dt=F32)) == EWORKSPACE
     assert dex(*dex_args(5, SCAN, 1 << 40)) == EINVAL

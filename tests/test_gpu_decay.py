@@ -172,6 +172,127 @@ def test_decay_fullsize_fwd131k(kata):
     assert row_rel_err(o[:, :, rows], O.decay_brute_force_rows(q, k, v, g, rows)) <= TOL
 
 
+# ---- d_k = 32 on the matrix cores (bf16, chunk 64 or 128) ----------------------------
+
+@pytest.mark.parametrize("prefix", ["scan", "sequential"])
+@pytest.mark.parametrize("dv,C", [(64, 128), (16, 128), (32, 64), (64, 64)])
+@pytest.mark.parametrize("gmin", [-0.05, -0.2])
+def test_decay_fwd32(kata, prefix, dv, C, gmin):
+    """d_k = 32: several chunks and segments, a ragged tail; every output and
+    the final state."""
+    B, H, T = 2, 2, 1000
+    q, k, v = gen.gaussian_qkv(B, H, T, 32, dv, seed=1900 + dv + C, dtype="bf16")
+    g = gen.log_decays(B, H, T, seed=1901 + C, gmin=gmin)
+    say(f"decay d32 {prefix} dv={dv} C={C} gmin={gmin}")
+    o, S, z = run(kata, q, k, v, g, C, prefix, state=True)
+    assert row_rel_err(o, O.decay_brute_force(q, k, v, g)) <= TOL
+    _, S_ref, z_ref = O.decay_recurrent(q, k, v, g)
+    assert state_rel_err(S, S_ref) <= STATE_TOL and state_rel_err(z, z_ref) <= STATE_TOL
+
+
+@pytest.mark.parametrize("G", [2, 3])
+@pytest.mark.parametrize("C", [64, 128])
+def test_decay_fwd32_segments(kata, monkeypatch, G, C):
+    """Segments of several chunks: the output kernel carries the decaying state
+    across chunks and the scan combines segment totals with their decays."""
+    B, H, T = 1, 3, 1100
+    q, k, v = gen.gaussian_qkv(B, H, T, 32, 64, seed=1910 + G + C, dtype="bf16")
+    g = gen.log_decays(B, H, T, seed=1911 + G, gmin=-0.05)
+    monkeypatch.setenv("KATA_SEGMENT_CHUNKS", str(G))
+    say(f"decay d32 segments G={G} C={C}")
+    o, S, z = run(kata, q, k, v, g, C, "scan", state=True)
+    assert row_rel_err(o, O.decay_brute_force(q, k, v, g)) <= TOL
+    _, S_ref, z_ref = O.decay_recurrent(q, k, v, g)
+    assert state_rel_err(S, S_ref) <= STATE_TOL and state_rel_err(z, z_ref) <= STATE_TOL
+
+
+@pytest.mark.parametrize("prefix", ["scan", "sequential"])
+def test_decay_fwd32_strong_gate(kata, prefix):
+    """Decays down to exp(-0.5) per token at d_k = 32, with the bar of the
+    d_k = 16 strong-gate test (few effective keys, so bf16 feature rounding
+    does not average out): mean row error within 5e-3, max within 5e-2."""
+    q, k, v = gen.gaussian_qkv(2, 2, 1000, 32, 64, seed=1920, dtype="bf16")
+    g = gen.log_decays(2, 2, 1000, seed=1921, gmin=-0.5)
+    say(f"decay d32 strong gate {prefix}")
+    o = run(kata, q, k, v, g, 64, prefix)
+    ref = O.decay_brute_force(q, k, v, g)
+    err = np.abs(o - ref).max(-1) / np.abs(ref).max(-1)
+    assert err.mean() <= 5e-3 and err.max() <= 5e-2
+
+
+@pytest.mark.parametrize("prefix", ["scan", "sequential"])
+@pytest.mark.parametrize("C", [64, 128])
+def test_decay_fwd32_zero_gate_is_ungated(kata, prefix, C):
+    """g = 0: the gated d_k = 32 kernels reproduce the ungated ones bit for bit."""
+    import torch
+    q, k, v = gen.gaussian_qkv(2, 2, 700, 32, 64, seed=1930, dtype="bf16")
+    g = np.zeros((2, 2, 700), np.float32)
+    say(f"decay d32 zero gate {prefix} C={C}")
+    o = run(kata, q, k, v, g, C, prefix)
+    ref = host(kata.chunked_fwd(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), chunk=C,
+                                prefix=prefix))
+    torch.cuda.synchronize()
+    assert np.array_equal(o, ref)
+
+
+def test_decay_fwd32_reset(kata):
+    """A reset gate inside a chunk at d_k = 32: later outputs equal the ungated
+    oracle on the suffix."""
+    q, k, v = gen.gaussian_qkv(1, 2, 640, 32, 64, seed=1940, dtype="bf16")
+    g = gen.log_decays(1, 2, 640, seed=1941, gmin=-0.2)
+    s = 330
+    g[:, :, s] = -1e4
+    g[:, :, s + 1:] = 0.0
+    say("decay d32 reset")
+    for prefix in ("scan", "sequential"):
+        o = run(kata, q, k, v, g, 128, prefix)
+        assert row_rel_err(o[:, :, s:], O.brute_force(q[:, :, s:], k[:, :, s:], v[:, :, s:])) <= TOL
+        assert row_rel_err(o, O.decay_brute_force(q, k, v, g)) <= TOL
+
+
+@pytest.mark.parametrize("prefix", ["scan", "sequential"])
+def test_decay_fwd32_resume(kata, prefix):
+    """d_k = 32: an initial state standing for earlier tokens decays with the
+    sequence; outputs and the final state."""
+    T1, T2 = 300, 452
+    q, k, v = gen.gaussian_qkv(1, 3, T1 + T2, 32, 32, seed=1950, dtype="bf16")
+    g = gen.log_decays(1, 3, T1 + T2, seed=1951, gmin=-0.05)
+    _, S0, z0 = O.decay_recurrent(q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], g[:, :, :T1])
+    say(f"decay d32 resume {prefix}")
+    o, S, z = run(kata, q[:, :, T1:], k[:, :, T1:], v[:, :, T1:], g[:, :, T1:], 128, prefix,
+                  S0=S0.astype(np.float32), z0=z0.astype(np.float32), state=True)
+    assert row_rel_err(o, O.decay_brute_force(q, k, v, g)[:, :, T1:]) <= TOL
+    _, S_ref, z_ref = O.decay_recurrent(q, k, v, g)
+    assert state_rel_err(S, S_ref) <= STATE_TOL and state_rel_err(z, z_ref) <= STATE_TOL
+
+
+def test_decay_fwd32_bitwise_causality(kata):
+    q, k, v = gen.gaussian_qkv(1, 2, 400, 32, 64, seed=1960, dtype="bf16")
+    g = gen.log_decays(1, 2, 400, seed=1961, gmin=-0.1)
+    say("decay d32 causality")
+    base = run(kata, q, k, v, g, 128, "scan")
+    for j in [63, 127, 128, 255, 300]:
+        k2, v2, g2 = k.copy(), v.copy(), g.copy()
+        k2[:, :, j] = gen.round_to(k[:, :, j][..., ::-1] + 0.5, "bf16")
+        v2[:, :, j] = gen.round_to(v[:, :, j] * 3.0 + 1.0, "bf16")
+        g2[:, :, j] = -0.7
+        got = run(kata, q, k2, v2, g2, 128, "scan")
+        assert np.array_equal(got[:, :, :j], base[:, :, :j]), f"output before {j} changed"
+        assert not np.array_equal(got[:, :, j], base[:, :, j])
+
+
+def test_decay_fullsize_fwd32k(kata):
+    """The 32k d_k = 32 workload with mild gates: sampled rows against the oracle."""
+    from tests.gpu_util import workload_inputs
+    w, q, k, v, _ = workload_inputs("fwd32k")
+    g = gen.log_decays(w.B, w.H, w.T, seed=1970, gmin=-0.01)
+    say("decay full size fwd32k")
+    o = run(kata, q, k, v, g, w.chunk, "scan")
+    assert np.all(np.isfinite(o))
+    rows = sample_rows(w.T, w.chunk, n_random=12)
+    assert row_rel_err(o[:, :, rows], O.decay_brute_force_rows(q, k, v, g, rows)) <= TOL
+
+
 VALU_TOL = {"f32": 1e-4, "bf16": TOL}
 VALU_STATE_TOL = 1e-4
 
@@ -182,8 +303,9 @@ VALU_STATE_TOL = 1e-4
                                            ("f32", 16, 32, 128)])
 @pytest.mark.parametrize("gmin", [-0.05, -0.5])
 def test_decay_valu_path(kata, dtype, dk, dv, C, gmin):
-    """Shapes without a matrix-core path: several chunks, a ragged tail (T not a
-    multiple of 4 across heads), every output and the final state."""
+    """The fp32 VALU path: shapes without a matrix-core path, and matrix-core
+    shapes whose T is not a multiple of 4 across heads (T = 333 here); several
+    chunks, a ragged tail, every output and the final state."""
     B, H, T = 2, 2, 333
     q, k, v = gen.gaussian_qkv(B, H, T, dk, dv, seed=1500 + dk + dv + C, dtype=dtype)
     g = gen.log_decays(B, H, T, seed=1501 + C, gmin=gmin)
