@@ -177,8 +177,8 @@ def decode_bench(kata, torch, steps=1024, n_seq=512, heads=4, dk=16, dv=64, reps
 def decay_gate(kata, torch, gen, steps, warmup):
     """The fwd131k forward with per-token log-decays in [-0.05, 0] against the
     ungated forward on the same inputs (both without state export), for the
-    PSD lift and for the first-order feature (orthant inputs), and the gated
-    decode step."""
+    PSD lift and for the first-order feature (orthant inputs); the same for the
+    fwd32k (d_k = 32) forward; and the gated decode step."""
     w = gen.WORKLOADS["fwd131k"]
     to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
     q, k, v = (to(a) for a in gen.gaussian_qkv(w.B, w.H, w.T, w.dk, w.dv, w.seed, w.dtype))
@@ -203,12 +203,29 @@ def decay_gate(kata, torch, gen, steps, warmup):
     ws4 = torch.empty(max(nb4, 1), dtype=torch.uint8, device="cuda")
     ms_ui = time_calls(torch, lambda: kata.chunked_fwd_into(
         q, k, v, o, w.chunk, True, ws4, feature="identity"), steps, warmup)
+    del q, k, v, o, ws, ws2, ws3, ws4
+    w32 = gen.WORKLOADS["fwd32k"]
+    q, k, v = (to(a) for a in gen.gaussian_qkv(w32.B, w32.H, w32.T, w32.dk, w32.dv, w32.seed,
+                                               w32.dtype))
+    g = torch.from_numpy(gen.log_decays(w32.B, w32.H, w32.T, seed=w32.seed + 100)).cuda()
+    o = torch.empty_like(v)
+    nb5 = kata.chunked_fwd_decay_workspace(w32.B, w32.H, w32.T, w32.dk, w32.dv, w32.chunk, 1, "scan")
+    ws5 = torch.empty(max(nb5, 1), dtype=torch.uint8, device="cuda")
+    ms_g32 = time_calls(torch, lambda: kata.chunked_fwd_decay_into(q, k, v, g, o, w32.chunk, ws5),
+                        steps, warmup)
+    nb6 = kata.chunked_fwd_workspace(w32.B, w32.H, w32.T, w32.dk, w32.dv, w32.chunk, 1, True)
+    ws6 = torch.empty(max(nb6, 1), dtype=torch.uint8, device="cuda")
+    ms_u32 = time_calls(torch, lambda: kata.chunked_fwd_into(q, k, v, o, w32.chunk, True, ws6),
+                        steps, warmup)
+    del q, k, v, o, ws5, ws6
     dms, dgbs, _ = decode_bench(kata, torch, gated=True)
     return {"fwd131k_gated_ms": ms_g, "fwd131k_ungated_ms": ms_u,
             "fwd131k_gated_tokens_per_s": w.B * w.T / (ms_g * 1e-3),
             "gate_overhead": ms_g / ms_u - 1.0,
             "fwd131k_identity_gated_ms": ms_gi, "fwd131k_identity_ungated_ms": ms_ui,
             "identity_gate_overhead": ms_gi / ms_ui - 1.0,
+            "fwd32k_gated_ms": ms_g32, "fwd32k_ungated_ms": ms_u32,
+            "fwd32k_gate_overhead": ms_g32 / ms_u32 - 1.0,
             "decode_gated_ms_per_step": dms, "decode_gated_GBps": dgbs,
             "decode_gated_hbm_frac": dgbs / PEAK_HBM_GBS}
 

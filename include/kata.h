@@ -180,11 +180,12 @@ kata_status_t kata_chunked_fwd_ex(const void* q, const void* k, const void* v, v
  *     KATA_PREFIX_SEQUENTIAL (one workgroup per head walks every chunk).
  * Every other argument as for kata_chunked_fwd (S0, z0 stand for earlier tokens
  * and decay with the sequence; S_out, z_out are the decayed final state).
- * Paths: dtype KATA_BF16 with d_k = 16 and chunk in {32, 64} runs on the matrix
- * cores (either prefix; T a multiple of 4 when B*H > 1, since the log-decays of
- * a head are copied 16 bytes at a time); every other supported shape (d_k in
- * {16, 32}, d_v in {16, 32, 64}, chunk in {16, 32, 64, 128}, fp32 or bf16 inputs)
- * runs the fp32 VALU path, with KATA_PREFIX_SCAN only. Else KATA_EUNSUPPORTED. */
+ * Paths: dtype KATA_BF16 with d_k = 16 and chunk in {32, 64}, or d_k = 32 and
+ * chunk in {64, 128}, runs on the matrix cores with either prefix, provided T
+ * is a multiple of 4 or B*H == 1 (the log-decays of a head are copied 16 bytes
+ * at a time). Every other supported shape (d_k in {16, 32}, d_v in {16, 32, 64},
+ * chunk in {16, 32, 64, 128}, fp32 or bf16 inputs, any T) runs the fp32 VALU
+ * path, with KATA_PREFIX_SCAN only. Else KATA_EUNSUPPORTED. */
 size_t kata_chunked_fwd_decay_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                         kata_dtype_t dtype, kata_prefix_t prefix);
 kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v,
@@ -199,7 +200,7 @@ kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v
  * kata_chunked_fwd_decay; KATA_FEATURE_IDENTITY gates the first-order feature
  * phi1(x) = x (weights (q_t.k_j) exp(g_{j+1} + ... + g_t), state d_k x d_v in
  * S0, z0, S_out, z_out): on the matrix cores for dtype KATA_BF16 with chunk 32
- * or 64 (either prefix; T a multiple of 4 when B*H > 1), else on the fp32 VALU
+ * or 64 (either prefix; T a multiple of 4 or B*H == 1), else on the fp32 VALU
  * path with KATA_PREFIX_SCAN. Every other argument, error and layout as there. */
 size_t kata_chunked_fwd_decay_ex_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                            kata_dtype_t dtype, kata_feature_t feature,
