@@ -2,10 +2,12 @@
 (kata_decode_step_decay) against the float64 decay oracle
 (oracle/decay_oracle.py).
 
-Matrix-core path (bf16, d_k = 16, C in {32, 64}): fp32 accumulation of bf16
-operands, outputs within 2e-2 (row-normwise), final states within 2e-2 of the
-state norm (the lifted keys are rounded to bf16 before the matrix cores, as in
-the ungated parity tests). VALU path (every other shape): fp32 arithmetic
+Matrix-core paths (bf16; PSD lift at d_k = 16 with C in {32, 64} and at
+d_k = 32 with C in {64, 128}; first-order feature with C in {32, 64}; T a
+multiple of 4 across heads): fp32 accumulation of bf16 operands, outputs within
+2e-2 (row-normwise), final states within 2e-2 of the state norm (the lifted
+keys are rounded to bf16 before the matrix cores, as in the ungated parity
+tests). VALU path (every other shape): fp32 arithmetic
 throughout, outputs within 1e-4 for fp32 inputs and 2e-2 for bf16 (the bf16
 rounding of the output), states within 1e-4. The decode step is fp32
 arithmetic on the state (1e-5 for fp32 inputs)."""
