@@ -128,7 +128,7 @@ kata_status_t kata_chunked_fwd_profiled(const void* q, const void* k, const void
  *    the normalised form o_t = sum_j (q_t.k_j) v_j / sum_j (q_t.k_j), 0 where the
  *    denominator is 0; it is a convex combination when the weights are
  *    nonnegative (queries and keys in the nonnegative orthant, the cone of this
- *    feature in explainer section 2.2). bf16 only. */
+ *    feature in explainer section 2.2). */
 typedef enum { KATA_FEATURE_PSD = 0, KATA_FEATURE_IDENTITY = 1 } kata_feature_t;
 
 /* How the inter-chunk prefix is formed (explainer section 2.3: recurrence depth

@@ -184,7 +184,7 @@ def chunked_fwd(q, k, v, chunk=64, causal=True, initial_state=None, return_state
     initial_state: optional (S0 [B,H,D,d_v], z0 [B,H,D]) fp32.
     return_state: also return the final (S, z).
     feature: "psd" (the rank-one PSD lift, D = d(d+1)/2) or "identity" (the
-      first-order feature, D = d; bf16 only).
+      first-order feature, D = d).
     prefix: "scan" (segments + associative scan) or "sequential" (one
       workgroup per head walks every chunk; bf16 matrix-core shapes only).
     """
@@ -308,9 +308,10 @@ def chunked_fwd_decay(q, k, v, log_decay, chunk=64, initial_state=None, return_s
                       prefix="scan", feature="psd"):
     """Decay-gated causal KATA forward: log_decay [B,H,T] fp32 (<= 0) is the
     per-token log forget gate (S_t = exp(g_t) S_{t-1} + phi(k_t) v_t^T, z
-    likewise). Matrix cores for bf16 d_k = 16 with chunk 32 or 64 (either
-    prefix); the fp32 VALU path for every other supported shape (scan prefix).
-    feature="identity" gates the first-order feature (VALU path).
+    likewise). Matrix cores (either prefix) for bf16 with d_k = 16 and chunk 32
+    or 64, d_k = 32 and chunk 64 or 128, or feature="identity" (the gated
+    first-order feature) and chunk 32 or 64, when T is a multiple of 4 or
+    B*H == 1; the fp32 VALU path for every other supported shape (scan prefix).
     initial_state / return_state as chunked_fwd."""
     _check_dev(q, k, v)
     if q.dim() != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:

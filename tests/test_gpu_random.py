@@ -1,0 +1,117 @@
+"""Seeded random configurations across every option of the chunked forwards:
+batch, heads, any length T (ragged tails, T not a multiple of 4 across heads),
+d_k, d_v, chunk, dtype, feature map, prefix method, causal or not, decay gate,
+initial state. Each runs through the C ABI and is compared with the float64
+oracles (oracle/kata_oracle.py, oracle/first_order_oracle.py,
+oracle/decay_oracle.py): outputs row-relative within 1e-4 (fp32 inputs) or
+2e-2 (bf16), final states within 1e-4 (fp32) or 2e-2 (bf16, where the matrix
+cores round lifted keys to bf16). Configurations are drawn only from the
+supported set: the sequential prefix needs a bf16 matrix-core shape, and the
+gated matrix-core shapes also T % 4 == 0 or a single head."""
+import numpy as np
+import pytest
+
+import oracle as O
+from kernelized_linear_attention_phi_amd import inputs as gen
+from tests.gpu_util import dev, host, row_rel_err, say, state_rel_err
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 48
+
+
+def _matrix_core_shape(dtype, feature, dk, C, gated):
+    if dtype != "bf16":
+        return False
+    if feature == "identity":
+        return C in ((32, 64) if gated else (32, 64, 128))
+    return (dk == 16 and C in (32, 64)) or (dk == 32 and C in (64, 128))
+
+
+def _draw(i):
+    r = np.random.Generator(np.random.PCG64(7000 + i))
+    cfg = {
+        "B": int(r.integers(1, 3)), "H": int(r.integers(1, 4)),
+        "T": int(r.choice([int(r.integers(1, 9)), int(r.integers(9, 260)), int(r.integers(260, 700))])),
+        "dk": int(r.choice([16, 32])), "dv": int(r.choice([16, 32, 64])),
+        "C": int(r.choice([16, 32, 64, 128])), "dtype": str(r.choice(["bf16", "bf16", "f32"])),
+        "feature": str(r.choice(["psd", "psd", "identity"])), "gated": bool(r.random() < 0.4),
+    }
+    cfg["causal"] = cfg["gated"] or bool(r.random() < 0.85)
+    cfg["S0"] = cfg["causal"] and bool(r.random() < 0.5)
+    cfg["T0"] = int(r.integers(1, 200))
+    mc = _matrix_core_shape(cfg["dtype"], cfg["feature"], cfg["dk"], cfg["C"], cfg["gated"])
+    if cfg["gated"] and cfg["T"] % 4 and cfg["B"] * cfg["H"] > 1:
+        mc = False                              # gated matrix cores stage T-aligned rows
+    cfg["prefix"] = "sequential" if mc and r.random() < 0.4 else "scan"
+    cfg["gmin"] = float(r.choice([-0.02, -0.2]))
+    return cfg
+
+
+CASES = [_draw(i) for i in range(N_CASES)]
+
+
+def _ids(c):
+    return (f"B{c['B']}H{c['H']}T{c['T']}d{c['dk']}v{c['dv']}C{c['C']}{c['dtype']}-{c['feature']}-"
+            f"{c['prefix']}{'' if c['causal'] else '-full'}{'-gated' if c['gated'] else ''}"
+            f"{'-S0' if c['S0'] else ''}")
+
+
+@pytest.fixture(scope="module")
+def kata():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kernelized_linear_attention_phi_amd as k
+    k.lib()
+    return k
+
+
+@pytest.mark.parametrize("c", CASES, ids=[_ids(c) for c in CASES])
+def test_random_config(kata, c):
+    import torch
+    B, H, T, dk, dv, dtype, feature = c["B"], c["H"], c["T"], c["dk"], c["dv"], c["dtype"], c["feature"]
+    draw = gen.orthant_qkv if feature == "identity" else gen.gaussian_qkv
+    T0 = c["T0"] if c["S0"] else 0
+    seed = 7100 + CASES.index(c)
+    q, k, v = draw(B, H, T0 + T, dk, dv, seed=seed, dtype=dtype)
+    g = gen.log_decays(B, H, T0 + T, seed=seed + 1, gmin=c["gmin"]) if c["gated"] else None
+    S0 = z0 = None
+    if c["S0"]:
+        if c["gated"]:
+            _, S0, z0 = O.decay_recurrent(q[:, :, :T0], k[:, :, :T0], v[:, :, :T0], g[:, :, :T0],
+                                          feature=feature)
+        elif feature == "identity":
+            S0, z0 = O.fo_state_from_tokens(k[:, :, :T0], v[:, :, :T0])
+        else:
+            S0, z0 = O.state_from_tokens(k[:, :, :T0], v[:, :, :T0])
+    qs, ks, vs = q[:, :, T0:], k[:, :, T0:], v[:, :, T0:]
+    say(f"random {_ids(c)}")
+    init = None if S0 is None else (dev(S0.astype(np.float32)), dev(z0.astype(np.float32)))
+    want_state = c["causal"]
+    if c["gated"]:
+        out = kata.chunked_fwd_decay(dev(qs, dtype), dev(ks, dtype), dev(vs, dtype), dev(g[:, :, T0:]),
+                                     chunk=c["C"], initial_state=init, return_state=True,
+                                     prefix=c["prefix"], feature=feature)
+    else:
+        out = kata.chunked_fwd(dev(qs, dtype), dev(ks, dtype), dev(vs, dtype), chunk=c["C"],
+                               causal=c["causal"], initial_state=init, return_state=want_state,
+                               feature=feature, prefix=c["prefix"])
+    torch.cuda.synchronize()
+    o, (S, z) = out if want_state else (out, (None, None))
+    o = host(o)
+
+    if c["gated"]:
+        o_ref = O.decay_brute_force(q, k, v, g, feature=feature)[:, :, T0:]
+        _, S_ref, z_ref = O.decay_recurrent(q, k, v, g, feature=feature)
+    elif feature == "identity":
+        o_ref = O.fo_brute_force(qs, ks, vs, causal=c["causal"], S0=S0, z0=z0)
+        S_ref, z_ref = O.fo_state_from_tokens(k, v)
+    else:
+        o_ref = O.brute_force(qs, ks, vs, causal=c["causal"], S0=S0, z0=z0)
+        S_ref, z_ref = O.state_from_tokens(k, v)
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    assert np.all(np.isfinite(o))
+    assert row_rel_err(o, o_ref) <= tol
+    if want_state:
+        assert state_rel_err(host(S), S_ref) <= tol and state_rel_err(host(z), z_ref) <= tol
