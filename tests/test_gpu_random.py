@@ -17,7 +17,7 @@ from tests.gpu_util import dev, host, row_rel_err, say, state_rel_err
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 96
 
 
 def _matrix_core_shape(dtype, feature, dk, C, gated):
@@ -115,3 +115,71 @@ def test_random_config(kata, c):
     assert row_rel_err(o, o_ref) <= tol
     if want_state:
         assert state_rel_err(host(S), S_ref) <= tol and state_rel_err(host(z), z_ref) <= tol
+
+
+def _draw_flash(i):
+    r = np.random.Generator(np.random.PCG64(7500 + i))
+    return {"B": int(r.integers(1, 3)), "H": int(r.integers(1, 4)),
+            "T": int(r.choice([int(r.integers(1, 40)), int(r.integers(40, 700))])),
+            "dk": int(r.choice([16, 32])), "dv": int(r.choice([16, 32, 64])),
+            "causal": bool(r.random() < 0.75)}
+
+
+FLASH_CASES = [_draw_flash(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("c", FLASH_CASES,
+                         ids=[f"B{c['B']}H{c['H']}T{c['T']}d{c['dk']}v{c['dv']}{'' if c['causal'] else '-full'}"
+                              for c in FLASH_CASES])
+def test_random_flash(kata, c):
+    """The quadratic-form forward (bf16) on random shapes against the brute force."""
+    import torch
+    q, k, v = gen.gaussian_qkv(c["B"], c["H"], c["T"], c["dk"], c["dv"],
+                               seed=7600 + FLASH_CASES.index(c), dtype="bf16")
+    say(f"random flash {c}")
+    o = kata.flash_fwd(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), causal=c["causal"])
+    torch.cuda.synchronize()
+    assert row_rel_err(host(o), O.brute_force(q, k, v, causal=c["causal"])) <= 2e-2
+
+
+def _draw_decode(i):
+    r = np.random.Generator(np.random.PCG64(7700 + i))
+    return {"N": int(r.choice([1, int(r.integers(2, 64)), int(r.integers(64, 700))])),
+            "dk": int(r.choice([16, 32])), "dv": int(r.choice([16, 32, 64])),
+            "dtype": str(r.choice(["bf16", "f32"])), "gated": bool(r.random() < 0.5)}
+
+
+DECODE_CASES = [_draw_decode(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("c", DECODE_CASES,
+                         ids=[f"N{c['N']}d{c['dk']}v{c['dv']}{c['dtype']}{'-gated' if c['gated'] else ''}"
+                              for c in DECODE_CASES])
+def test_random_decode(kata, c):
+    """Three decode steps from a state built from 30 earlier tokens, on random
+    row counts and shapes: outputs and the updated state against the oracle's
+    step (1e-5 for fp32 inputs, whose step is fp32 arithmetic; 2e-2 for bf16
+    outputs, 1e-5 for the fp32 state)."""
+    import torch
+    N, dk, dv, dtype, steps = c["N"], c["dk"], c["dv"], c["dtype"], 3
+    seed = 7800 + DECODE_CASES.index(c)
+    q, k, v = gen.gaussian_qkv(1, N, steps, dk, dv, seed=seed, dtype=dtype)
+    g = gen.log_decays(1, N, steps, seed=seed + 1, gmin=-0.3)
+    kp, vp = gen.gaussian_qkv(1, N, 30, dk, dv, seed=seed + 2, dtype="f32")[1:]
+    S_ref, z_ref = O.state_from_tokens(kp, vp)
+    S_ref, z_ref = S_ref[0], z_ref[0]
+    S, z = dev(S_ref), dev(z_ref)
+    say(f"random decode {c}")
+    for t in range(steps):
+        args = (dev(q[0, :, t], dtype), dev(k[0, :, t], dtype), dev(v[0, :, t], dtype))
+        if c["gated"]:
+            o = kata.decode_step_decay(*args, dev(g[0, :, t]), S, z)
+            o_ref, S_ref, z_ref = O.decay_decode_step(q[0, :, t], k[0, :, t], v[0, :, t], g[0, :, t],
+                                                      S_ref, z_ref)
+        else:
+            o = kata.decode_step(*args, S, z)
+            o_ref, S_ref, z_ref = O.decode_step(q[0, :, t], k[0, :, t], v[0, :, t], S_ref, z_ref)
+        torch.cuda.synchronize()
+        assert row_rel_err(host(o), o_ref) <= (1e-5 if dtype == "f32" else 2e-2)
+    assert state_rel_err(host(S), S_ref, lead=1) <= 1e-5
+    assert state_rel_err(host(z), z_ref, lead=1) <= 1e-5
