@@ -359,8 +359,9 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
         compiler_fence();
         if (W == 1) store_rows1<DK, DV, C>(own, oc + 16 * DV, n - 16, L);
 
-        // ---- running state: S += K_c^T V_c, z += K_c^T 1 (both wavefronts)
-        if (CAUSAL) {
+        // ---- running state: S += K_c^T V_c, z += K_c^T 1 (both wavefronts; not
+        // needed after the segment's last chunk unless the final state is asked for)
+        if (CAUSAL && (c + 1 < P.c1 || final_rec)) {
             if constexpr (DECAY) decay_state1<DK, DV, C>(st, cd);
             state_update1<ALL, DK, DV, C, DECAY>(st, bk, bv, L, kd);
         }

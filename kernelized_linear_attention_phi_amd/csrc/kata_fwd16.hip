@@ -531,8 +531,9 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         compiler_fence();
         if (W == 1) store_staged_rows<DV, C>(ostage + F::XB / 2, oc + 16 * DV, n - 16, L);
 
-        // ---- running state: S += phi(K_c)^T V_c, Z += K_c^T K_c
-        if (CAUSAL) {
+        // ---- running state: S += phi(K_c)^T V_c, Z += K_c^T K_c (not needed
+        // after the segment's last chunk unless the final state is asked for)
+        if (CAUSAL && (c + 1 < P.c1 || final_rec)) {
             f32x4_t KT[F::TT];
             k_transposed<DV, C>(bk, KT, L);
             if constexpr (DECAY) decay_state<DV, C>(st, cd);

@@ -581,8 +581,9 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
             }
         }
 
-        // ---- running state: S += phi(K_c)^T V_c, Z += K_c^T K_c
-        if (CAUSAL) {
+        // ---- running state: S += phi(K_c)^T V_c, Z += K_c^T K_c (not needed
+        // after the segment's last chunk unless the final state is asked for)
+        if (CAUSAL && (c + 1 < P.c1 || final_rec)) {
             if constexpr (DECAY) decay_state32<W, DV, C>(st, kd.last);
 #pragma unroll
             for (int m = 0; m < F::KS; ++m) state_step<W, DV, C, DECAY>(st, bk, bv, m, L, kd);
