@@ -262,6 +262,35 @@ def scan_vs_sequential(kata, torch, gen, names, steps, warmup):
     return out
 
 
+def scan_states_bench(kata, torch, gen, names, steps, warmup):
+    """kata_scan_states (per-chunk exclusive prefix states, fp32 chunk states
+    then an in-place scan over one record per chunk) on the fwd131k and fwd32k
+    shapes: ms per call and GB/s over its minimal traffic (k, v read once; every
+    prefix S, z and the final state written once). The scan alone at one record
+    per chunk moves 2 x 4 D (d_v + 1) bytes per chunk and head (read and write)."""
+    out = {}
+    to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+    for name in names:
+        w = gen.WORKLOADS[name]
+        _, k, v = (to(a) for a in gen.gaussian_qkv(w.B, w.H, w.T, w.dk, w.dv, w.seed, "bf16"))
+        D = w.dk * (w.dk + 1) // 2
+        NC = -(-w.T // w.chunk)
+        BH = w.B * w.H
+        Sp = torch.empty((w.B, w.H, NC, D, w.dv), device="cuda")
+        zp = torch.empty((w.B, w.H, NC, D), device="cuda")
+        ST = torch.empty((w.B, w.H, D, w.dv), device="cuda")
+        zT = torch.empty((w.B, w.H, D), device="cuda")
+        ms = time_calls(torch, lambda: kata.scan_states_into(k, v, w.chunk, Sp, zp, ST, zT),
+                        steps, warmup)
+        nbytes = BH * (w.T * 2 * (w.dk + w.dv) + (NC + 1) * 4 * D * (w.dv + 1))
+        scan_bytes = BH * NC * 2 * 4 * D * (w.dv + 1)
+        out[name] = {"ms": ms, "alg_bytes": nbytes, "alg_GBps": nbytes / (ms * 1e-3) / 1e9,
+                     "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "scan_alone_bytes": scan_bytes}
+        del k, v, Sp, zp, ST, zT
+    return out
+
+
 def recall_forward(kata, torch, gen, steps, warmup):
     """The recall-shaped stream workload (B=8, H=4, T=16384, d_k=16, d_v=64,
     C=64): keys from per-stream codebooks with overwrites, one-hot values."""
@@ -423,6 +452,8 @@ def main():
                                                         args.warmup)
         result["parts"]["scan_vs_sequential"] = scan_vs_sequential(
             kata, torch, gen, ("fwd4k", "fwd32k", "fwd131k"), min(args.steps, 10), args.warmup)
+        result["parts"]["scan_states"] = scan_states_bench(kata, torch, gen, ["fwd131k", "fwd32k"],
+                                                           min(args.steps, 10), min(args.warmup, 3))
         result["parts"]["decay_gate"] = decay_gate(kata, torch, gen, min(args.steps, 10),
                                                    args.warmup)
         result["parts"]["recall16k"] = recall_forward(kata, torch, gen, min(args.steps, 10),

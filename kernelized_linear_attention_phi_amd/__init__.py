@@ -14,6 +14,6 @@ The shared library is loaded on first use; calls raise if it is missing.
 from ._binding import (KataError, chunked_fwd, chunked_fwd_into, chunked_fwd_workspace,  # noqa: F401
                        chunked_fwd_decay, chunked_fwd_decay_into, chunked_fwd_decay_workspace,
                        decode_step, decode_step_decay, feature_dim, flash_fwd, lib, phi_dim,
-                       scan_states, LIB_PATH)
+                       scan_states, scan_states_into, LIB_PATH)
 
 __version__ = "0.1.0"

@@ -244,6 +244,17 @@ def scan_states(k, v, chunk=64, initial_state=None):
     return Sp, zp, ST, zT
 
 
+def scan_states_into(k, v, chunk, S_prefix, z_prefix, S_out=None, z_out=None, S0=None, z0=None):
+    """Raw kata_scan_states into preallocated outputs (used by the benchmark)."""
+    _check_dev(k, v)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    st = lib().kata_scan_states(_ptr(k), _ptr(v), B, H, T, dk, dv, chunk, _dtype_code(k),
+                                _ptr(S0), _ptr(z0), _ptr(S_prefix), _ptr(z_prefix), _ptr(S_out),
+                                _ptr(z_out), None, 0, _stream())
+    _raise(st, "kata_scan_states")
+
+
 def flash_fwd(q, k, v, causal=True, out=None):
     """Quadratic-form forward (bf16 q, k [B,H,T,d_k], v [B,H,T,d_v]): the same
     output as chunked_fwd without chunk states."""

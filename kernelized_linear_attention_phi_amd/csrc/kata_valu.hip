@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
     float* __restrict__ S_rec, float* __restrict__ z_rec, float* __restrict__ cdec, int T, int dk,
     int dv, int C, int NC, int ident) {
     __shared__ float ks[kMaxC * kMaxDk];
-    __shared__ float vs[kMaxC * kMaxDv];
+    __shared__ __attribute__((aligned(16))) float vs[kMaxC * kMaxDv];
     __shared__ uint32_t pairs[kMaxD];
     __shared__ double bs[kMaxC];
     __shared__ float wt[kMaxC];
@@ -75,19 +75,47 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
     }
     float* Sr = S_rec + rec * D * dv;
     float* zr = z_rec + rec * D;
-    for (int e = threadIdx.x; e < D * dv + D; e += kThreads) {
-        const bool is_z = e >= D * dv;
-        const int p = is_z ? e - D * dv : e / dv;
-        const int col = is_z ? 0 : e % dv;
+    // S: one thread per (feature p, group of kCols value columns) forms the
+    // feature entry of each token once and adds it into kCols sums (each sum
+    // over t in order, as one entry per thread would)
+    constexpr int kCols = 16;
+    const int ngrp = dv / kCols;
+    for (int it = threadIdx.x; it < D * ngrp; it += kThreads) {
+        const int p = it / ngrp, c0 = (it % ngrp) * kCols;
+        const int i = ident ? p : pairs[p] & 0xff, j = ident ? p : pairs[p] >> 8;
+        const float sc = i == j ? 1.0f : kSqrt2;
+        float acc[kCols];
+#pragma unroll
+        for (int u = 0; u < kCols; ++u) acc[u] = 0.0f;
+        for (int t = 0; t < n; ++t) {
+            float f = ident ? ks[t * dk + i] : sc * (ks[t * dk + i] * ks[t * dk + j]);
+            if (gdec) f *= wt[t];
+            const float4* vr = reinterpret_cast<const float4*>(vs + t * dv + c0);
+#pragma unroll
+            for (int u = 0; u < kCols / 4; ++u) {
+                const float4 x = vr[u];
+                acc[4 * u + 0] += f * x.x;
+                acc[4 * u + 1] += f * x.y;
+                acc[4 * u + 2] += f * x.z;
+                acc[4 * u + 3] += f * x.w;
+            }
+        }
+        float4* dst = reinterpret_cast<float4*>(Sr + (size_t)p * dv + c0);
+#pragma unroll
+        for (int u = 0; u < kCols / 4; ++u)
+            dst[u] = make_float4(acc[4 * u], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]);
+    }
+    // z: one thread per feature
+    for (int p = threadIdx.x; p < D; p += kThreads) {
         const int i = ident ? p : pairs[p] & 0xff, j = ident ? p : pairs[p] >> 8;
         const float sc = i == j ? 1.0f : kSqrt2;
         float acc = 0.0f;
         for (int t = 0; t < n; ++t) {
             float f = ident ? ks[t * dk + i] : sc * (ks[t * dk + i] * ks[t * dk + j]);
             if (gdec) f *= wt[t];
-            acc += is_z ? f : f * vs[t * dv + col];
+            acc += f;
         }
-        if (is_z) zr[p] = acc; else Sr[e] = acc;
+        zr[p] = acc;
     }
 }
 
