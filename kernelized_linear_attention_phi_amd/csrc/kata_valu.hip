@@ -1,6 +1,8 @@
-// fp32 VALU chunked-state path: every product and sum in fp32 on the vector
-// ALUs. It serves fp32 inputs (whose tolerance a bf16 matrix-core operand would
-// exceed) and stands as the general-shape path.
+// fp32 chunked-state path: every product and sum in fp32. Chunk states
+// phi(K)^T V run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32: fp32
+// operands, fp32 accumulation), everything else on the vector ALUs. It serves
+// fp32 inputs (whose tolerance a bf16 matrix-core operand would exceed) and
+// stands as the general-shape path.
 //
 // Chunked-state form (KATA explainers, gist.science, technical summary 2.3):
 // chunk c covers positions [cC, min(cC+C, T)); its output is the masked
@@ -19,6 +21,7 @@
 // and key j <= t of its own chunk by exp(b_t - b_j).
 #include "kata_device.h"
 #include "kata_internal.h"
+#include "kata_mfma.h"
 
 namespace kata {
 
@@ -42,28 +45,68 @@ __device__ __forceinline__ void chunk_log_decay(const float* g, int n, double* b
     }
 }
 
+// Copies `count` contiguous inputs (a multiple of 16 bytes' worth, from a
+// 16-byte aligned address) to fp32 in LDS: every thread issues all of its
+// 16-byte loads before it converts and stores any of them, so the block waits
+// about one memory latency rather than one per element.
+template <typename TIn, int MAXCOUNT>
+__device__ __forceinline__ void stage_f32(const TIn* __restrict__ src, int count, float* dst) {
+    constexpr int EPU = 16 / (int)sizeof(TIn);              // elements per 16-byte unit
+    constexpr int MAXU = (MAXCOUNT / EPU + kThreads - 1) / kThreads;
+    const int units = count / EPU;
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+    uint4 buf[MAXU];
+#pragma unroll
+    for (int u = 0; u < MAXU; ++u) {
+        const int idx = threadIdx.x + u * kThreads;
+        if (idx < units) buf[u] = s4[idx];
+    }
+#pragma unroll
+    for (int u = 0; u < MAXU; ++u) {
+        const int idx = threadIdx.x + u * kThreads;
+        if (idx >= units) continue;
+        const uint32_t wv[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
+        if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dst[idx * 8 + 2 * e] = __uint_as_float(wv[e] << 16);
+                dst[idx * 8 + 2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[idx * 4 + e] = __uint_as_float(wv[e]);
+        }
+    }
+}
+
 // S_c = phi(K_c)^T V_c, z_c = phi(K_c)^T 1 for one (head, chunk) per block.
 // With the gate, token j is weighted exp(b_last - b_j) and cdec receives the
-// chunk's factor exp(b_last).
+// chunk's factor exp(b_last). S on the fp32 matrix cores: wavefront w takes
+// feature tiles w, w + 4, ... (16 features each, the last one partial); per
+// 4-token K-step lane l lifts phi(K)^T[16 ft + l % 16][4 s + l / 16] in fp32 (A)
+// and loads V[4 s + l / 16][16 nt + l % 16] (B) for each 16-column value tile;
+// the result holds S[16 ft + 4 (l / 16) + r][16 nt + l % 16] in slot r.
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void chunk_states_valu(
     const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ gdec,
     float* __restrict__ S_rec, float* __restrict__ z_rec, float* __restrict__ cdec, int T, int dk,
     int dv, int C, int NC, int ident) {
-    __shared__ float ks[kMaxC * kMaxDk];
-    __shared__ __attribute__((aligned(16))) float vs[kMaxC * kMaxDv];
-    __shared__ uint32_t pairs[kMaxD];
-    __shared__ double bs[kMaxC];
-    __shared__ float wt[kMaxC];
+    // LDS sized for this shape (chunk_states_lds): bs | ks | vs | wt | pairs
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int D = ident ? dk : dk * (dk + 1) / 2;
+    double* bs = reinterpret_cast<double*>(smem);
+    float* ks = reinterpret_cast<float*>(smem + C * 8);
+    float* vs = ks + C * dk;
+    float* wt = vs + C * dv;
+    uint32_t* pairs = reinterpret_cast<uint32_t*>(wt + C);
     const int c = blockIdx.x;
     const size_t bh = blockIdx.y;
-    const int D = ident ? dk : dk * (dk + 1) / 2;
     const int t0 = c * C;
     const int n = min(C, T - t0);
     const TIn* kb = k + (bh * T + t0) * dk;
     const TIn* vb = v + (bh * T + t0) * dv;
-    for (int e = threadIdx.x; e < n * dk; e += kThreads) ks[e] = io<TIn>::ld(kb, e);
-    for (int e = threadIdx.x; e < n * dv; e += kThreads) vs[e] = io<TIn>::ld(vb, e);
+    stage_f32<TIn, kMaxC * kMaxDk>(kb, n * dk, ks);
+    stage_f32<TIn, kMaxC * kMaxDv>(vb, n * dv, vs);
     fill_pair_table(pairs, dk, D);
     if (gdec) chunk_log_decay(gdec + bh * T + t0, n, bs);
     __syncthreads();
@@ -75,35 +118,43 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
     }
     float* Sr = S_rec + rec * D * dv;
     float* zr = z_rec + rec * D;
-    // S: one thread per (feature p, group of kCols value columns) forms the
-    // feature entry of each token once and adds it into kCols sums (each sum
-    // over t in order, as one entry per thread would)
-    constexpr int kCols = 16;
-    const int ngrp = dv / kCols;
-    for (int it = threadIdx.x; it < D * ngrp; it += kThreads) {
-        const int p = it / ngrp, c0 = (it % ngrp) * kCols;
-        const int i = ident ? p : pairs[p] & 0xff, j = ident ? p : pairs[p] >> 8;
+    // S on the matrix cores (see above); 4 wavefronts of 64 lanes
+    static_assert(kThreads == 256, "four wavefronts");
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r16 = lane & 15, kq = lane >> 4;
+    const int nft = (D + 15) / 16, ntv = dv / 16, nks = (n + 3) / 4;
+    for (int ft = w; ft < nft; ft += 4) {
+        const int p = 16 * ft + r16;                 // this lane's feature (A row)
+        const bool live = p < D;
+        const int i = !live ? 0 : ident ? p : pairs[p] & 0xff;
+        const int j = !live ? 0 : ident ? p : pairs[p] >> 8;
         const float sc = i == j ? 1.0f : kSqrt2;
-        float acc[kCols];
+        f32x4_t acc[kMaxDv / 16];
 #pragma unroll
-        for (int u = 0; u < kCols; ++u) acc[u] = 0.0f;
-        for (int t = 0; t < n; ++t) {
-            float f = ident ? ks[t * dk + i] : sc * (ks[t * dk + i] * ks[t * dk + j]);
-            if (gdec) f *= wt[t];
-            const float4* vr = reinterpret_cast<const float4*>(vs + t * dv + c0);
+        for (int nt = 0; nt < kMaxDv / 16; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int st = 0; st < nks; ++st) {
+            const int t = 4 * st + kq;               // this lane's token (A column, B row)
+            float a = 0.0f;
+            if (live && t < n) {
+                a = ident ? ks[t * dk + i] : sc * (ks[t * dk + i] * ks[t * dk + j]);
+                if (gdec) a *= wt[t];
+            }
 #pragma unroll
-            for (int u = 0; u < kCols / 4; ++u) {
-                const float4 x = vr[u];
-                acc[4 * u + 0] += f * x.x;
-                acc[4 * u + 1] += f * x.y;
-                acc[4 * u + 2] += f * x.z;
-                acc[4 * u + 3] += f * x.w;
+            for (int nt = 0; nt < kMaxDv / 16; ++nt) {
+                if (nt >= ntv) break;
+                const float b = t < n ? vs[t * dv + 16 * nt + r16] : 0.0f;
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[nt], 0, 0, 0);
             }
         }
-        float4* dst = reinterpret_cast<float4*>(Sr + (size_t)p * dv + c0);
 #pragma unroll
-        for (int u = 0; u < kCols / 4; ++u)
-            dst[u] = make_float4(acc[4 * u], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]);
+        for (int nt = 0; nt < kMaxDv / 16; ++nt) {
+            if (nt >= ntv) break;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int pf = 16 * ft + 4 * kq + r;
+                if (pf < D) Sr[(size_t)pf * dv + 16 * nt + r16] = acc[nt][r];
+            }
+        }
     }
     // z: one thread per feature
     for (int p = threadIdx.x; p < D; p += kThreads) {
@@ -117,6 +168,11 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
         }
         zr[p] = acc;
     }
+}
+
+// Bytes of LDS chunk_states_valu uses for a shape (its layout above).
+size_t chunk_states_lds(int dk, int dv, int C, int D) {
+    return (size_t)C * 8 + (size_t)C * dk * 4 + (size_t)C * dv * 4 + (size_t)C * 4 + (size_t)D * 4;
 }
 
 // o for one (head, chunk): inter term phi(q_t).P_c plus the intra term over the
@@ -141,11 +197,9 @@ __global__ __launch_bounds__(kThreads) void fwd_valu(
     const TIn* qb = q + (bh * T + t0) * dk;
     const TIn* kb = k + (bh * T + t0) * dk;
     const TIn* vb = v + (bh * T + t0) * dv;
-    for (int e = threadIdx.x; e < n * dk; e += kThreads) {
-        qs[e] = io<TIn>::ld(qb, e);
-        ks[e] = io<TIn>::ld(kb, e);
-    }
-    for (int e = threadIdx.x; e < n * dv; e += kThreads) vs[e] = io<TIn>::ld(vb, e);
+    stage_f32<TIn, kMaxC * kMaxDk>(qb, n * dk, qs);
+    stage_f32<TIn, kMaxC * kMaxDk>(kb, n * dk, ks);
+    stage_f32<TIn, kMaxC * kMaxDv>(vb, n * dv, vs);
     fill_pair_table(pairs, dk, D);
     if (gdec) chunk_log_decay(gdec + bh * T + t0, n, bs);
     __syncthreads();
@@ -202,12 +256,13 @@ hipError_t launch_chunk_states_valu(const Shape& s, const void* k, const void* v
                                     const float* gdec, float* S_rec, float* z_rec, float* cdec,
                                     int ident, hipStream_t st) {
     dim3 grid(s.NC, s.B * s.H);
+    const size_t lds = chunk_states_lds(s.dk, s.dv, s.C, ident ? s.dk : s.dk * (s.dk + 1) / 2);
     if (s.bf16)
-        chunk_states_valu<bf16_t><<<grid, kThreads, 0, st>>>(
+        chunk_states_valu<bf16_t><<<grid, kThreads, lds, st>>>(
             (const bf16_t*)k, (const bf16_t*)v, gdec, S_rec, z_rec, cdec, s.T, s.dk, s.dv, s.C,
             s.NC, ident);
     else
-        chunk_states_valu<float><<<grid, kThreads, 0, st>>>(
+        chunk_states_valu<float><<<grid, kThreads, lds, st>>>(
             (const float*)k, (const float*)v, gdec, S_rec, z_rec, cdec, s.T, s.dk, s.dv, s.C,
             s.NC, ident);
     return hipGetLastError();
