@@ -132,6 +132,7 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
         f32x4_t acc[kMaxDv / 16];
 #pragma unroll
         for (int nt = 0; nt < kMaxDv / 16; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        float zacc = 0.0f;                           // z[p] over this lane's tokens
         for (int st = 0; st < nks; ++st) {
             const int t = 4 * st + kq;               // this lane's token (A column, B row)
             float a = 0.0f;
@@ -139,6 +140,7 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
                 a = ident ? ks[t * dk + i] : sc * (ks[t * dk + i] * ks[t * dk + j]);
                 if (gdec) a *= wt[t];
             }
+            zacc += a;
 #pragma unroll
             for (int nt = 0; nt < kMaxDv / 16; ++nt) {
                 if (nt >= ntv) break;
@@ -155,18 +157,10 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
                 if (pf < D) Sr[(size_t)pf * dv + 16 * nt + r16] = acc[nt][r];
             }
         }
-    }
-    // z: one thread per feature
-    for (int p = threadIdx.x; p < D; p += kThreads) {
-        const int i = ident ? p : pairs[p] & 0xff, j = ident ? p : pairs[p] >> 8;
-        const float sc = i == j ? 1.0f : kSqrt2;
-        float acc = 0.0f;
-        for (int t = 0; t < n; ++t) {
-            float f = ident ? ks[t * dk + i] : sc * (ks[t * dk + i] * ks[t * dk + j]);
-            if (gdec) f *= wt[t];
-            acc += f;
-        }
-        zr[p] = acc;
+        // z[p]: the four lane groups hold the tokens of each residue mod 4
+        zacc += __shfl_xor(zacc, 16, 64);
+        zacc += __shfl_xor(zacc, 32, 64);
+        if (kq == 0 && live) zr[p] = zacc;
     }
 }
 
