@@ -156,7 +156,7 @@ size_t kata_chunked_fwd_ex_workspace(int B, int H, int T, int d_k, int d_v, int 
  * KATA_EUNSUPPORTED): for KATA_FEATURE_PSD d_k = 16 with chunk 32 or 64, d_k = 32
  * with chunk 64 or 128; for KATA_FEATURE_IDENTITY chunk 32, 64 or 128. Every
  * other supported shape (fp32 inputs, or chunk 16 with the identity feature)
- * runs the fp32 VALU path with KATA_PREFIX_SCAN. */
+ * runs the fp32 path with KATA_PREFIX_SCAN. */
 kata_status_t kata_chunked_fwd_ex(const void* q, const void* k, const void* v, void* o,
                                   int B, int H, int T, int d_k, int d_v, int chunk, int causal,
                                   kata_dtype_t dtype, kata_feature_t feature,
@@ -184,8 +184,8 @@ kata_status_t kata_chunked_fwd_ex(const void* q, const void* k, const void* v, v
  * chunk in {64, 128}, runs on the matrix cores with either prefix, provided T
  * is a multiple of 4 or B*H == 1 (the log-decays of a head are copied 16 bytes
  * at a time). Every other supported shape (d_k in {16, 32}, d_v in {16, 32, 64},
- * chunk in {16, 32, 64, 128}, fp32 or bf16 inputs, any T) runs the fp32 VALU
- * path, with KATA_PREFIX_SCAN only. Else KATA_EUNSUPPORTED. */
+ * chunk in {16, 32, 64, 128}, fp32 or bf16 inputs, any T) runs the fp32 path
+ * (fp32 arithmetic throughout), with KATA_PREFIX_SCAN only. Else KATA_EUNSUPPORTED. */
 size_t kata_chunked_fwd_decay_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                         kata_dtype_t dtype, kata_prefix_t prefix);
 kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v,
@@ -200,8 +200,8 @@ kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v
  * kata_chunked_fwd_decay; KATA_FEATURE_IDENTITY gates the first-order feature
  * phi1(x) = x (weights (q_t.k_j) exp(g_{j+1} + ... + g_t), state d_k x d_v in
  * S0, z0, S_out, z_out): on the matrix cores for dtype KATA_BF16 with chunk 32
- * or 64 (either prefix; T a multiple of 4 or B*H == 1), else on the fp32 VALU
- * path with KATA_PREFIX_SCAN. Every other argument, error and layout as there. */
+ * or 64 (either prefix; T a multiple of 4 or B*H == 1), else on the fp32 path
+ * with KATA_PREFIX_SCAN. Every other argument, error and layout as there. */
 size_t kata_chunked_fwd_decay_ex_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                            kata_dtype_t dtype, kata_feature_t feature,
                                            kata_prefix_t prefix);

@@ -322,7 +322,7 @@ def chunked_fwd_decay(q, k, v, log_decay, chunk=64, initial_state=None, return_s
     likewise). Matrix cores (either prefix) for bf16 with d_k = 16 and chunk 32
     or 64, d_k = 32 and chunk 64 or 128, or feature="identity" (the gated
     first-order feature) and chunk 32 or 64, when T is a multiple of 4 or
-    B*H == 1; the fp32 VALU path for every other supported shape (scan prefix).
+    B*H == 1; the fp32 path for every other supported shape (scan prefix).
     initial_state / return_state as chunked_fwd."""
     _check_dev(q, k, v)
     if q.dim() != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:

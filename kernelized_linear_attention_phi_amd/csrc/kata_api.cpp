@@ -68,7 +68,7 @@ FwdPlan plan_fwd(const Shape& s, int causal, kata_feature_t f = KATA_FEATURE_PSD
                  kata_prefix_t pf = KATA_PREFIX_SCAN) {
     FwdPlan p{};
     if (f == KATA_FEATURE_IDENTITY) {
-        // matrix cores for the bf16 shapes, else the fp32 VALU path (scan prefix)
+        // matrix cores for the bf16 shapes, else the fp32 path (scan prefix)
         p.mfma = kata::first_supported(s) ? 1 : 0;
         p.ok = p.mfma != 0 || pf == KATA_PREFIX_SCAN;
     } else {
@@ -371,7 +371,7 @@ kata_status_t kata_flash_fwd(const void* q, const void* k, const void* v, void* 
 // bf16 at d_k = 16 (C 32 or 64) and d_k = 32 (C 64 or 128), the identity
 // feature for bf16 with C 32 or 64. They stage each chunk's log-decays 16 bytes
 // at a time from T-aligned offsets, so with several heads T must be a multiple
-// of 4. Every other case takes the fp32 VALU path (per-chunk records, scan
+// of 4. Every other case takes the fp32 path (per-chunk records, scan
 // prefix only).
 struct DecayPlan {
     FwdPlan fwd;           // matrix-core path

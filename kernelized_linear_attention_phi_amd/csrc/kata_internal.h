@@ -14,7 +14,7 @@ struct Shape {
     bool bf16;
 };
 
-// ---- fp32 VALU path (any supported shape; fp32 or bf16 inputs, fp32 math) ----
+// ---- fp32 path (any supported shape; fp32 or bf16 inputs, fp32 math) ----
 
 // Per-chunk totals phi(K_c)^T V_c and phi(K_c)^T 1 in packed layout:
 // S_rec [BH, NC, D, dv], z_rec [BH, NC, D]. gdec: per-token log-decays

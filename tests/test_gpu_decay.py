@@ -305,7 +305,7 @@ VALU_STATE_TOL = 1e-4
                                            ("f32", 16, 32, 128)])
 @pytest.mark.parametrize("gmin", [-0.05, -0.5])
 def test_decay_valu_path(kata, dtype, dk, dv, C, gmin):
-    """The fp32 VALU path: shapes without a matrix-core path, and matrix-core
+    """The fp32 path: shapes without a matrix-core path, and matrix-core
     shapes whose T is not a multiple of 4 across heads (T = 333 here); several
     chunks, a ragged tail, every output and the final state."""
     B, H, T = 2, 2, 333

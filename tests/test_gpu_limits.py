@@ -1,7 +1,7 @@
 """Parity at the largest shapes the boundary accepts along the axes that set
 launch grids: B*H = 65535 heads (the largest second grid dimension; every
 chunked kernel runs one grid row per head) for the matrix-core forward with
-state export, the decay-gated forward, the fp32 VALU forward and the quadratic
+state export, the decay-gated forward, the fp32 forward and the quadratic
 form. Ragged last chunks throughout. Sampled heads (first, last and random)
 are checked against the float64 oracle; every output is checked for
 finiteness."""

@@ -171,7 +171,7 @@ def test_identity_fullsize_fwd4k(kata):
 @pytest.mark.parametrize("dtype,dk,dv,C", [("f32", 16, 64, 64), ("f32", 32, 16, 128),
                                            ("bf16", 16, 64, 16), ("f32", 16, 32, 16)])
 def test_identity_valu_path(kata, dtype, dk, dv, C):
-    """The first-order feature on the fp32 VALU path (fp32 inputs, or chunk 16):
+    """The first-order feature on the fp32 path (fp32 inputs, or chunk 16):
     causal with a ragged tail and the final state, non-causal, and resume from an
     initial state."""
     B, H, T = 2, 2, 333
