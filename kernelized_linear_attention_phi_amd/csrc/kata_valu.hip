@@ -79,6 +79,28 @@ __device__ __forceinline__ void stage_f32(const TIn* __restrict__ src, int count
     }
 }
 
+// Copies `count` contiguous inputs (16-byte units from a 16-byte aligned
+// address) to LDS unchanged, all loads in flight before the first store.
+template <typename TIn, int MAXCOUNT>
+__device__ __forceinline__ void stage_raw(const TIn* __restrict__ src, int count, TIn* dst) {
+    constexpr int EPU = 16 / (int)sizeof(TIn);
+    constexpr int MAXU = (MAXCOUNT / EPU + kThreads - 1) / kThreads;
+    const int units = count / EPU;
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+    uint4* d4 = reinterpret_cast<uint4*>(dst);
+    uint4 buf[MAXU];
+#pragma unroll
+    for (int u = 0; u < MAXU; ++u) {
+        const int idx = threadIdx.x + u * kThreads;
+        if (idx < units) buf[u] = s4[idx];
+    }
+#pragma unroll
+    for (int u = 0; u < MAXU; ++u) {
+        const int idx = threadIdx.x + u * kThreads;
+        if (idx < units) d4[idx] = buf[u];
+    }
+}
+
 // S_c = phi(K_c)^T V_c, z_c = phi(K_c)^T 1 for one (head, chunk) per block.
 // With the gate, token j is weighted exp(b_last - b_j) and cdec receives the
 // chunk's factor exp(b_last). S on the fp32 matrix cores: wavefront w takes
@@ -91,13 +113,14 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
     const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ gdec,
     float* __restrict__ S_rec, float* __restrict__ z_rec, float* __restrict__ cdec, int T, int dk,
     int dv, int C, int NC, int ident) {
-    // LDS sized for this shape (chunk_states_lds): bs | ks | vs | wt | pairs
+    // LDS sized for this shape (chunk_states_lds): bs | ks | vs | wt | pairs,
+    // k and v kept in the input type and widened to fp32 (exactly) when read
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int D = ident ? dk : dk * (dk + 1) / 2;
     double* bs = reinterpret_cast<double*>(smem);
-    float* ks = reinterpret_cast<float*>(smem + C * 8);
-    float* vs = ks + C * dk;
-    float* wt = vs + C * dv;
+    TIn* ks = reinterpret_cast<TIn*>(smem + C * 8);
+    TIn* vs = ks + C * dk;
+    float* wt = reinterpret_cast<float*>(vs + C * dv);
     uint32_t* pairs = reinterpret_cast<uint32_t*>(wt + C);
     const int c = blockIdx.x;
     const size_t bh = blockIdx.y;
@@ -105,8 +128,8 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
     const int n = min(C, T - t0);
     const TIn* kb = k + (bh * T + t0) * dk;
     const TIn* vb = v + (bh * T + t0) * dv;
-    stage_f32<TIn, kMaxC * kMaxDk>(kb, n * dk, ks);
-    stage_f32<TIn, kMaxC * kMaxDv>(vb, n * dv, vs);
+    stage_raw<TIn, kMaxC * kMaxDk>(kb, n * dk, ks);
+    stage_raw<TIn, kMaxC * kMaxDv>(vb, n * dv, vs);
     fill_pair_table(pairs, dk, D);
     if (gdec) chunk_log_decay(gdec + bh * T + t0, n, bs);
     __syncthreads();
@@ -137,14 +160,15 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
             const int t = 4 * st + kq;               // this lane's token (A column, B row)
             float a = 0.0f;
             if (live && t < n) {
-                a = ident ? ks[t * dk + i] : sc * (ks[t * dk + i] * ks[t * dk + j]);
+                const float ki = io<TIn>::ld(ks, t * dk + i);
+                a = ident ? ki : sc * (ki * io<TIn>::ld(ks, t * dk + j));
                 if (gdec) a *= wt[t];
             }
             zacc += a;
 #pragma unroll
             for (int nt = 0; nt < kMaxDv / 16; ++nt) {
                 if (nt >= ntv) break;
-                const float b = t < n ? vs[t * dv + 16 * nt + r16] : 0.0f;
+                const float b = t < n ? io<TIn>::ld(vs, t * dv + 16 * nt + r16) : 0.0f;
                 acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[nt], 0, 0, 0);
             }
         }
@@ -164,9 +188,11 @@ __global__ __launch_bounds__(kThreads) void chunk_states_valu(
     }
 }
 
-// Bytes of LDS chunk_states_valu uses for a shape (its layout above).
-size_t chunk_states_lds(int dk, int dv, int C, int D) {
-    return (size_t)C * 8 + (size_t)C * dk * 4 + (size_t)C * dv * 4 + (size_t)C * 4 + (size_t)D * 4;
+// Bytes of LDS chunk_states_valu uses for a shape (its layout above); esize
+// is the input element size.
+size_t chunk_states_lds(int dk, int dv, int C, int D, int esize) {
+    return (size_t)C * 8 + (size_t)C * dk * esize + (size_t)C * dv * esize + (size_t)C * 4 +
+           (size_t)D * 4;
 }
 
 // o for one (head, chunk): inter term phi(q_t).P_c plus the intra term over the
@@ -250,7 +276,8 @@ hipError_t launch_chunk_states_valu(const Shape& s, const void* k, const void* v
                                     const float* gdec, float* S_rec, float* z_rec, float* cdec,
                                     int ident, hipStream_t st) {
     dim3 grid(s.NC, s.B * s.H);
-    const size_t lds = chunk_states_lds(s.dk, s.dv, s.C, ident ? s.dk : s.dk * (s.dk + 1) / 2);
+    const size_t lds = chunk_states_lds(s.dk, s.dv, s.C, ident ? s.dk : s.dk * (s.dk + 1) / 2,
+                                        s.bf16 ? 2 : 4);
     if (s.bf16)
         chunk_states_valu<bf16_t><<<grid, kThreads, lds, st>>>(
             (const bf16_t*)k, (const bf16_t*)v, gdec, S_rec, z_rec, cdec, s.T, s.dk, s.dv, s.C,
