@@ -96,7 +96,10 @@ size_t kata_chunked_fwd_workspace(int B, int H, int T, int d_k, int d_v, int chu
  *     bytes (may be NULL when that is 0).
  * Output dtype equals input dtype. The mask is inclusive (position t sees j <= t):
  * the explainers' output gate blends the previous readout with the current
- * value (section 2.1). */
+ * value (section 2.1). With causal = 0, bf16 inputs, no initial state and T <=
+ * chunk, o is evaluated in the quadratic form (as kata_flash_fwd), so that a
+ * few keys do not meet the bf16 rounding of lifted features; the final state is
+ * formed as otherwise. */
 kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, void* o,
                                int B, int H, int T, int d_k, int d_v, int chunk, int causal,
                                kata_dtype_t dtype,
