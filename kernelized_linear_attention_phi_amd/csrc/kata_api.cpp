@@ -207,15 +207,32 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
                    : m == 32 ? kata::launch_record_to_packed32(total, S_out, z_out, s.dv, nrec, hs)
                              : kata::launch_record_to_packed1(total, S_out, z_out, s.dk, s.dv, nrec, hs);
         };
+        // An initial state may stand for only a few tokens. Where it is the
+        // whole inter-chunk prefix - the first chunk of every head - or, with
+        // the keys of one chunk, the whole non-causal state, the output would
+        // carry the bf16 rounding of lifted queries, keys, state entries and
+        // the Gram matrix (terms of size |q|^2 |k|^2 summing to (q.k)^2)
+        // un-averaged. Those chunks are evaluated with split (hi + lo)
+        // operands; every later chunk's prefix also holds at least one whole
+        // chunk of keys.
+        const bool prec_all = S0 && !causal && s.NC == 1;
         auto seg_state = [&]() {
-            return m == 16   ? kata::launch_seg_state16(s, k, v, rec, plan.G, plan.NSEG, hs)
-                   : m == 32 ? kata::launch_seg_state32(s, k, v, rec, plan.G, plan.NSEG, hs)
+            return m == 16   ? kata::launch_seg_state16(s, k, v, rec, plan.G, plan.NSEG, prec_all, hs)
+                   : m == 32 ? kata::launch_seg_state32(s, k, v, rec, plan.G, plan.NSEG, prec_all, hs)
                              : kata::launch_seg_state1(s, k, v, rec, plan.G, plan.NSEG, hs);
         };
         auto output = [&](const float* pre, float* fin) {
-            return m == 16   ? kata::launch_fwd16(s, q, k, v, pre, fin, o, causal, plan.G, plan.NSEG, hs)
-                   : m == 32 ? kata::launch_fwd32(s, q, k, v, pre, fin, o, causal, plan.G, plan.NSEG, hs)
+            return m == 16   ? kata::launch_fwd16(s, q, k, v, pre, fin, o, causal, plan.G, plan.NSEG, prec_all, hs)
+                   : m == 32 ? kata::launch_fwd32(s, q, k, v, pre, fin, o, causal, plan.G, plan.NSEG, prec_all, hs)
                              : kata::launch_fwd1(s, q, k, v, pre, fin, o, causal, plan.G, plan.NSEG, hs);
+        };
+        // the first chunk of every head again, from the initial-state record
+        // (one segment of one chunk per head; the output launch above wrote it
+        // with plain operands first)
+        auto first_chunk_split = [&]() {
+            if (m == 1 || !S0 || !causal) return hipSuccess;
+            return m == 16 ? kata::launch_fwd16(s, q, k, v, init, nullptr, o, 1, 1, 1, true, hs)
+                           : kata::launch_fwd32(s, q, k, v, init, nullptr, o, 1, 1, 1, true, hs);
         };
         if (S0 && e == hipSuccess) e = from_packed();
         if (plan.seq && causal) {
@@ -226,6 +243,7 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
             if (e == hipSuccess) e = mark(1);
             if (e == hipSuccess) e = mark(2);
             if (e == hipSuccess) e = output(init, S_out ? total : nullptr);
+            if (e == hipSuccess) e = first_chunk_split();
             if (e == hipSuccess) e = mark(3);
             if (S_out && e == hipSuccess) e = to_packed();
         } else {
@@ -255,6 +273,7 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
             if (e == hipSuccess) e = mark(2);
             if (e == hipSuccess)
                 e = quad ? kata::launch_flash_fwd(s, q, k, v, o, 0, hs) : output(causal ? rec : total, nullptr);
+            if (e == hipSuccess) e = first_chunk_split();
             if (e == hipSuccess) e = mark(3);
         }
         if (e == hipSuccess) e = mark(4);

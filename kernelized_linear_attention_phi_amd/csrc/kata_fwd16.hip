@@ -110,32 +110,30 @@ __device__ __forceinline__ void k_transposed(const bf16_t* bk, f32x4_t (&KT)[Cfg
 // Lifted keys of feature tile D for the tokens of one K-step (slot s): lane c16
 // holds row rho = c16, i.e. k_rho * k_{(rho+D) mod 16}; bf16 A operand.
 template <int D>
-__device__ __forceinline__ u32x4_t lift_keys(const float (&ka)[8], const Lane& L) {
-    float f[8];
+__device__ __forceinline__ void lift_key_values(const float (&ka)[8], const Lane& L, float (&f)[8]) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         f[s] = ka[s] * partner<D>(ka[s]);
         if (D == 8 && L.c16 >= 8) f[s] = 0.0f;       // repeated pairs stay zero
     }
+}
+
+template <int D>
+__device__ __forceinline__ u32x4_t lift_keys(const float (&ka)[8], const Lane& L) {
+    float f[8];
+    lift_key_values<D>(ka, L, f);
     return u32x4_t{pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
 }
 
+// Lifted keys of own tile i of wavefront W (tiles 4W + i), in fp32.
 template <int W>
-__device__ __forceinline__ u32x4_t lift_keys_own(int i, const float (&ka)[8], const Lane& L) {
-    if constexpr (W == 0) {
-        switch (i) {
-            case 0: return lift_keys<0>(ka, L);
-            case 1: return lift_keys<1>(ka, L);
-            case 2: return lift_keys<2>(ka, L);
-            default: return lift_keys<3>(ka, L);
-        }
-    } else {
-        switch (i) {
-            case 0: return lift_keys<4>(ka, L);
-            case 1: return lift_keys<5>(ka, L);
-            case 2: return lift_keys<6>(ka, L);
-            default: return lift_keys<7>(ka, L);
-        }
+__device__ __forceinline__ void lift_key_values_own(int i, const float (&ka)[8], const Lane& L,
+                                                    float (&f)[8]) {
+    switch (i) {
+        case 0: return lift_key_values<4 * W + 0>(ka, L, f);
+        case 1: return lift_key_values<4 * W + 1>(ka, L, f);
+        case 2: return lift_key_values<4 * W + 2>(ka, L, f);
+        default: return lift_key_values<4 * W + 3>(ka, L, f);
     }
 }
 
@@ -164,8 +162,11 @@ __device__ __forceinline__ void decay_state(State<DV, C>& st, const ChunkDecay& 
 
 // S(own tiles) += phi(K_c)^T V_c; Z += K_c^T K_c when WITH_Z. vop[m] are the V^T
 // fragments. With the decay gate (DECAY), key j is first scaled by
-// exp((b_last - b_j) / 2), i.e. its lift by exp(b_last - b_j).
-template <int W, bool WITH_Z, int DV, int C, bool DECAY = false>
+// exp((b_last - b_j) / 2), i.e. its lift by exp(b_last - b_j). PREC takes the
+// lifted keys as split operands (hi + lo, exact for unscaled bf16 keys), and the
+// Gram product of scaled keys as hi*hi + hi*lo + lo*hi, so the state carries
+// fp32-accurate sums.
+template <int W, bool WITH_Z, int DV, int C, bool DECAY = false, bool PREC = false>
 __device__ __forceinline__ void state_update(State<DV, C>& st, const f32x4_t (&KT)[Cfg<DV, C>::TT],
                                              const u32x4_t (&vop)[Cfg<DV, C>::KS][Cfg<DV, C>::NTV],
                                              const Lane& L,
@@ -183,20 +184,53 @@ __device__ __forceinline__ void state_update(State<DV, C>& st, const f32x4_t (&K
                 ka[s] *= exp2_neg(0.5f * (kd.last - kd.b(2 * m + s / 4, s % 4)));
         }
         if constexpr (WITH_Z) {
-            // Gram matrix: A = K^T (row = coordinate c16), B = K (column = c16)
-            const u32x4_t kt = {pk2(ka[0], ka[1]), pk2(ka[2], ka[3]), pk2(ka[4], ka[5]), pk2(ka[6], ka[7])};
-            st.zm = mma32(kt, kt, st.zm);
+            // Gram matrix: A = K^T (row = coordinate c16), B = K (column = c16);
+            // unscaled bf16 keys are exact operands
+            if constexpr (PREC && DECAY) {
+                u32x4_t kh, kl;
+                split8(ka, kh, kl);
+                st.zm = mma32(kh, kh, st.zm);
+                st.zm = mma32(kh, kl, st.zm);
+                st.zm = mma32(kl, kh, st.zm);
+            } else {
+                const u32x4_t kt = {pk2(ka[0], ka[1]), pk2(ka[2], ka[3]), pk2(ka[4], ka[5]), pk2(ka[6], ka[7])};
+                st.zm = mma32(kt, kt, st.zm);
+            }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const u32x4_t fk = lift_keys_own<W>(i, ka, L);
+            float f[8];
+            lift_key_values_own<W>(i, ka, L, f);
+            if constexpr (PREC) {
+                u32x4_t fh, fl;
+                split8(f, fh, fl);
 #pragma unroll
-            for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] = mma32(fk, vop[m][nt], st.s[i][nt]);
+                for (int nt = 0; nt < F::NTV; ++nt) {
+                    st.s[i][nt] = mma32(fh, vop[m][nt], st.s[i][nt]);
+                    st.s[i][nt] = mma32(fl, vop[m][nt], st.s[i][nt]);
+                }
+            } else {
+                const u32x4_t fk = {pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
+#pragma unroll
+                for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] = mma32(fk, vop[m][nt], st.s[i][nt]);
+            }
         }
         if constexpr (h8 > l8) {
-            const u32x4_t fk = lift_keys<8>(ka, L);
+            float f[8];
+            lift_key_values<8>(ka, L, f);
+            if constexpr (PREC) {
+                u32x4_t fh, fl;
+                split8(f, fh, fl);
 #pragma unroll
-            for (int j = 0; j < h8 - l8; ++j) st.x[j] = mma32(fk, vop[m][l8 + j], st.x[j]);
+                for (int j = 0; j < h8 - l8; ++j) {
+                    st.x[j] = mma32(fh, vop[m][l8 + j], st.x[j]);
+                    st.x[j] = mma32(fl, vop[m][l8 + j], st.x[j]);
+                }
+            } else {
+                const u32x4_t fk = {pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
+#pragma unroll
+                for (int j = 0; j < h8 - l8; ++j) st.x[j] = mma32(fk, vop[m][l8 + j], st.x[j]);
+            }
         }
     }
 }
@@ -204,8 +238,8 @@ __device__ __forceinline__ void state_update(State<DV, C>& st, const f32x4_t (&K
 // Lifted queries (x2 off the diagonal) of tiles (d0, d1) as a B operand: slot
 // s = 4h + r is tile d_h, row rho = 4g + r, i.e. q_rho * q_{rho + d_h}; qr is
 // q rotated by 4g (qr[x] = q[(x + 4g) mod 16]).
-__device__ __forceinline__ u32x4_t lift_queries(const float (&qr)[16], int d0, int d1) {
-    float f[8];
+__device__ __forceinline__ void lift_query_values(const float (&qr)[16], int d0, int d1,
+                                                  float (&f)[8]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int d = h ? d1 : d0;
@@ -213,6 +247,11 @@ __device__ __forceinline__ u32x4_t lift_queries(const float (&qr)[16], int d0, i
         for (int r = 0; r < 4; ++r)
             f[4 * h + r] = d == 0 ? qr[r] * qr[r] : (2.0f * qr[r]) * qr[(r + d) & 15];
     }
+}
+
+__device__ __forceinline__ u32x4_t lift_queries(const float (&qr)[16], int d0, int d1) {
+    float f[8];
+    lift_query_values(qr, d0, d1, f);
     return u32x4_t{pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
 }
 
@@ -267,7 +306,7 @@ __device__ __forceinline__ void record_load(const float* rec, State<DV, C>& st, 
 
 // ---- per-wavefront bodies --------------------------------------------------------
 
-template <int W, int DV, int C, bool DECAY>
+template <int W, int DV, int C, bool DECAY, bool PREC>
 __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v, const float* gdec,
                                                float* rec, float* segdec, char* lds, int T,
                                                int NC, int G, int NSEG, const Lane& L) {
@@ -306,7 +345,7 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
         for (int m = 0; m < F::KS; ++m) v_fragment_step<DV, C>(bv, vop[m], m, L);
         // the Gram matrix goes with wavefront 1 (wavefront 0 holds more of tile 8
         // when the value tiles are odd)
-        state_update<W, W == 1, DV, C, DECAY>(st, KT, vop, L, kd);
+        state_update<W, W == 1, DV, C, DECAY, PREC>(st, KT, vop, L, kd);
         compiler_fence();
     }
     record_store<W, W == 1, DV, C>(rec + (bh * NSEG + seg) * (size_t)F::REC, st, L);
@@ -340,7 +379,7 @@ __device__ __forceinline__ void store_staged_rows(const char* ostage, bf16_t* oc
 // output store and never waits for them. Both stage their output rows in LDS
 // (their own exchange half); wavefront 1 stores its rows in the same chunk and
 // wavefront 0's one chunk later, as whole rows.
-template <int W, int DV, int C, bool CAUSAL, bool DECAY>
+template <int W, int DV, int C, bool CAUSAL, bool DECAY, bool PREC>
 __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                          const float* gdec, const float* prefix,
                                          float* final_rec, bf16_t* o, char* lds, int T, int NC,
@@ -376,7 +415,87 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         // ---- inter-chunk partials over this wavefront's feature tiles, for every
         // query tile; those of the other wavefront's tiles go to the exchange
         f32x4_t num[F::TW][F::NTV + 1];            // own query tiles (+ ones tile)
-        {
+        if constexpr (PREC) {
+            // Split operands: hi*hi + lo*hi + hi*lo per pair (the lifted query is
+            // exact as hi + lo). Query tiles go in groups of two with the pair
+            // loop inside, so one pair's split state operands and two tiles'
+            // accumulators are live at a time.
+            constexpr int TG = F::TT < 2 ? F::TT : 2;
+#pragma unroll
+            for (int t0 = 0; t0 < F::TT; t0 += TG) {
+                f32x4_t acc[TG][F::NTV];
+#pragma unroll
+                for (int j = 0; j < TG; ++j)
+#pragma unroll
+                    for (int nt = 0; nt < F::NTV; ++nt) acc[j][nt] = zero4();
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    u32x4_t sh[F::NTV], sl[F::NTV];
+#pragma unroll
+                    for (int nt = 0; nt < F::NTV; ++nt) {
+                        const f32x4_t& x = st.s[2 * p][nt];
+                        const f32x4_t& y = st.s[2 * p + 1][nt];
+                        sh[nt] = u32x4_t{pk2(x[0], x[1]), pk2(x[2], x[3]), pk2(y[0], y[1]), pk2(y[2], y[3])};
+                        const u32x2_t a = lo_of(x, sh[nt][0], sh[nt][1]), b = lo_of(y, sh[nt][2], sh[nt][3]);
+                        sl[nt] = u32x4_t{a[0], a[1], b[0], b[1]};
+                    }
+#pragma unroll
+                    for (int j = 0; j < TG; ++j) {
+                        float qr[16];
+                        u32x2_t qf;
+                        load_query(bq, t0 + j, L, qr, qf);
+                        float f[8];
+                        lift_query_values(qr, 4 * W + 2 * p, 4 * W + 2 * p + 1, f);
+                        u32x4_t fh, fl;
+                        split8(f, fh, fl);
+#pragma unroll
+                        for (int nt = 0; nt < F::NTV; ++nt) {
+                            acc[j][nt] = mma32(sh[nt], fh, acc[j][nt]);
+                            acc[j][nt] = mma32(sl[nt], fh, acc[j][nt]);
+                            acc[j][nt] = mma32(sh[nt], fl, acc[j][nt]);
+                        }
+                    }
+                }
+                if constexpr (h8 > l8) {              // own value tiles of tile 8 (half K-step)
+                    u32x2_t sh8[F::H8], sl8[F::H8];
+#pragma unroll
+                    for (int i = 0; i < h8 - l8; ++i) {
+                        sh8[i] = u32x2_t{pk2(st.x[i][0], st.x[i][1]), pk2(st.x[i][2], st.x[i][3])};
+                        sl8[i] = lo_of(st.x[i], sh8[i][0], sh8[i][1]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < TG; ++j) {
+                        float qr[16];
+                        u32x2_t qf;
+                        load_query(bq, t0 + j, L, qr, qf);
+                        float f[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) f[r] = (2.0f * qr[r]) * qr[(r + 8) & 15];
+                        u32x2_t fh, fl;
+                        split4(f, fh, fl);
+#pragma unroll
+                        for (int i = 0; i < h8 - l8; ++i) {
+                            acc[j][l8 + i] = mma16_acc32(sh8[i], fh, acc[j][l8 + i]);
+                            acc[j][l8 + i] = mma16_acc32(sl8[i], fh, acc[j][l8 + i]);
+                            acc[j][l8 + i] = mma16_acc32(sh8[i], fl, acc[j][l8 + i]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < TG; ++j) {
+                    const int tt = t0 + j, u = tt / NW;
+                    if (tt % NW == W) {
+#pragma unroll
+                        for (int nt = 0; nt < F::NTV; ++nt) num[u][nt] = acc[j][nt];
+                        num[u][F::NTV] = zero4();
+                    } else {
+#pragma unroll
+                        for (int nt = 0; nt < F::NTV; ++nt)
+                            xbuf[((1 - W) * F::TW + u) * F::NTV * 64 + nt * 64 + L.lane] = acc[j][nt];
+                    }
+                }
+            }
+        } else {
             // S^T in bf16 as A operands: slot s of pair p = own tile 2p + s/4, row 4g + s%4
             u32x4_t sop[2][F::NTV];
 #pragma unroll
@@ -456,15 +575,17 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         }
         compiler_fence();                             // partials read before rows are staged
 
-        // V^T fragments (intra term and state update)
+        // V^T fragments (intra term and state update; the split-operand variant
+        // reads them where they are used rather than keep them live)
         u32x4_t vop[F::KS][F::NTV];
-        if (CAUSAL) {
+        if (CAUSAL && !PREC) {
 #pragma unroll
             for (int m = 0; m < F::KS; ++m) v_fragment_step<DV, C>(bv, vop[m], m, L);
         }
         // Z as an A operand: lane c16 = row i, slots 4g + s = column j; Z is
         // symmetric, so the accumulator (lane = column) serves directly.
         const u32x2_t zop = {pk2(st.zm[0], st.zm[1]), pk2(st.zm[2], st.zm[3])};
+        const u32x2_t zol = PREC ? lo_of(st.zm, zop[0], zop[1]) : u32x2_t{0u, 0u};
 #pragma unroll
         for (int u = 0; u < F::TW; ++u) {
             const int tt = NW * u + W;
@@ -494,15 +615,22 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
                         }
                     }
                     const u32x4_t at = {pk2(w[0], w[1]), pk2(w[2], w[3]), pk2(w[4], w[5]), pk2(w[6], w[7])};
+                    if constexpr (PREC) {
 #pragma unroll
-                    for (int nt = 0; nt < F::NTV; ++nt) num[u][nt] = mma32(vop[m][nt], at, num[u][nt]);
+                        for (int nt = 0; nt < F::NTV; ++nt)
+                            num[u][nt] = mma32(v_fragment_tr<DV>(bv, m, nt, L), at, num[u][nt]);
+                    } else {
+#pragma unroll
+                        for (int nt = 0; nt < F::NTV; ++nt) num[u][nt] = mma32(vop[m][nt], at, num[u][nt]);
+                    }
                     num[u][F::NTV] = mma32(ones, at, num[u][F::NTV]);
                 }
             }
             // ---- normalise: o = num / den
             // inter-chunk denominator q^T Z q: (Z q)[4g + r] times q[4g + r],
             // summed over r here and over the four lane groups below
-            const f32x4_t zq = mma16(zop, qf, zero4());
+            f32x4_t zq = mma16(zop, qf, zero4());
+            if constexpr (PREC) zq = mma16(zol, qf, zq);   // q is exact in bf16
             float di = qr[0] * zq[0];
             di = __builtin_fmaf(qr[1], zq[1], di);
             di = __builtin_fmaf(qr[2], zq[2], di);
@@ -537,7 +665,14 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
             f32x4_t KT[F::TT];
             k_transposed<DV, C>(bk, KT, L);
             if constexpr (DECAY) decay_state<DV, C>(st, cd);
-            state_update<W, true, DV, C, DECAY>(st, KT, vop, L, kd);
+            if constexpr (PREC) {
+                u32x4_t vup[F::KS][F::NTV];
+#pragma unroll
+                for (int m = 0; m < F::KS; ++m) v_fragment_step<DV, C>(bv, vup[m], m, L);
+                state_update<W, true, DV, C, DECAY, PREC>(st, KT, vup, L, kd);
+            } else {
+                state_update<W, true, DV, C, DECAY, PREC>(st, KT, vop, L, kd);
+            }
         }
         compiler_fence();
     }
@@ -554,7 +689,7 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
 
 // ---- kernels -------------------------------------------------------------------
 
-template <int DV, int C, bool DECAY>
+template <int DV, int C, bool DECAY, bool PREC>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kata_seg_state16(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                       const float* __restrict__ gdec, float* __restrict__ rec,
@@ -562,14 +697,14 @@ void kata_seg_state16(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v
     __shared__ __attribute__((aligned(16)))
     char lds[3 * ChunkIO<DK, DV, C, NW, NW, DECAY>::BUF + (DECAY ? NW * kKeyDecayRowBytes : 0)];
     const Lane L;
-    if (L.w == 0) seg_state_body<0, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, as_wave<0>(L));
-    else seg_state_body<1, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, as_wave<1>(L));
+    if (L.w == 0) seg_state_body<0, DV, C, DECAY, PREC>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, as_wave<0>(L));
+    else seg_state_body<1, DV, C, DECAY, PREC>(k, v, gdec, rec, segdec, lds, T, NC, G, NSEG, as_wave<1>(L));
 }
 
 // The gated variant's larger chunk buffers allow three workgroups per compute
 // unit, not four, so it may also use more than 256 registers per lane (it would
 // otherwise spill loop-invariant addresses).
-template <int DV, int C, bool CAUSAL, bool DECAY>
+template <int DV, int C, bool CAUSAL, bool DECAY, bool PREC>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(DECAY ? 1 : 2, 2)))
 void kata_fwd16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bf16_t* __restrict__ v, const float* __restrict__ gdec,
@@ -580,9 +715,9 @@ void kata_fwd16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     char lds[F::NBUF * ChunkIO<DK, DV, C, NW, 1, DECAY>::BUF + F::XB + (DECAY ? NW * kKeyDecayRowBytes : 0)];
     const Lane L;
     if (L.w == 0)
-        fwd_body<0, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G, NSEG, as_wave<0>(L));
+        fwd_body<0, DV, C, CAUSAL, DECAY, PREC>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G, NSEG, as_wave<0>(L));
     else
-        fwd_body<1, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G, NSEG, as_wave<1>(L));
+        fwd_body<1, DV, C, CAUSAL, DECAY, PREC>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G, NSEG, as_wave<1>(L));
 }
 
 // Launch arguments shared by every shape: gdec (log-decays, NULL = no gate;
@@ -596,6 +731,7 @@ struct Args {
     void* o;
     int causal, G, NSEG;
     bool state_only;
+    bool prec;             // split operands (the gated kernels always take them)
 };
 
 template <int DV, int C>
@@ -605,20 +741,31 @@ hipError_t launch_dv_c(const Shape& s, const Args& a, hipStream_t st) {
     bf16_t* o = (bf16_t*)a.o;
     if (a.state_only) {
         if (a.gdec)
-            kata_seg_state16<DV, C, true><<<grid, 64 * NW, 0, st>>>(k, v, a.gdec, a.rec, a.segdec,
-                                                                     s.T, s.NC, a.G, a.NSEG);
+            kata_seg_state16<DV, C, true, true><<<grid, 64 * NW, 0, st>>>(k, v, a.gdec, a.rec, a.segdec,
+                                                                           s.T, s.NC, a.G, a.NSEG);
+        else if (a.prec)
+            kata_seg_state16<DV, C, false, true><<<grid, 64 * NW, 0, st>>>(k, v, nullptr, a.rec, nullptr,
+                                                                            s.T, s.NC, a.G, a.NSEG);
         else
-            kata_seg_state16<DV, C, false><<<grid, 64 * NW, 0, st>>>(k, v, nullptr, a.rec, nullptr,
-                                                                      s.T, s.NC, a.G, a.NSEG);
+            kata_seg_state16<DV, C, false, false><<<grid, 64 * NW, 0, st>>>(k, v, nullptr, a.rec, nullptr,
+                                                                             s.T, s.NC, a.G, a.NSEG);
     } else if (a.gdec) {
-        kata_fwd16<DV, C, true, true><<<grid, 64 * NW, 0, st>>>(q, k, v, a.gdec, a.prefix, a.rec, o,
-                                                                 s.T, s.NC, a.G, a.NSEG);
+        kata_fwd16<DV, C, true, true, true><<<grid, 64 * NW, 0, st>>>(q, k, v, a.gdec, a.prefix, a.rec, o,
+                                                                       s.T, s.NC, a.G, a.NSEG);
     } else if (a.causal) {
-        kata_fwd16<DV, C, true, false><<<grid, 64 * NW, 0, st>>>(q, k, v, nullptr, a.prefix, a.rec,
-                                                                  o, s.T, s.NC, a.G, a.NSEG);
+        if (a.prec)
+            kata_fwd16<DV, C, true, false, true><<<grid, 64 * NW, 0, st>>>(q, k, v, nullptr, a.prefix,
+                                                                            a.rec, o, s.T, s.NC, a.G, a.NSEG);
+        else
+            kata_fwd16<DV, C, true, false, false><<<grid, 64 * NW, 0, st>>>(q, k, v, nullptr, a.prefix,
+                                                                             a.rec, o, s.T, s.NC, a.G, a.NSEG);
     } else {
-        kata_fwd16<DV, C, false, false><<<grid, 64 * NW, 0, st>>>(q, k, v, nullptr, a.prefix, a.rec,
-                                                                   o, s.T, s.NC, a.G, a.NSEG);
+        if (a.prec)
+            kata_fwd16<DV, C, false, false, true><<<grid, 64 * NW, 0, st>>>(q, k, v, nullptr, a.prefix,
+                                                                             a.rec, o, s.T, s.NC, a.G, a.NSEG);
+        else
+            kata_fwd16<DV, C, false, false, false><<<grid, 64 * NW, 0, st>>>(q, k, v, nullptr, a.prefix,
+                                                                              a.rec, o, s.T, s.NC, a.G, a.NSEG);
     }
     return hipGetLastError();
 }
@@ -652,26 +799,26 @@ bool mfma16_supported(const Shape& s) {
 int mfma16_record_floats(int dv) { return NMT * (dv / 16) * 256 + 256; }
 
 hipError_t launch_seg_state16(const Shape& s, const void* k, const void* v, float* rec, int G,
-                              int NSEG, hipStream_t st) {
-    return dispatch(s, Args{nullptr, k, v, nullptr, rec, nullptr, nullptr, nullptr, 1, G, NSEG, true}, st);
+                              int NSEG, bool prec, hipStream_t st) {
+    return dispatch(s, Args{nullptr, k, v, nullptr, rec, nullptr, nullptr, nullptr, 1, G, NSEG, true, prec}, st);
 }
 
 hipError_t launch_seg_state16_decay(const Shape& s, const void* k, const void* v,
                                     const float* gdec, float* rec, float* segdec, int G, int NSEG,
                                     hipStream_t st) {
-    return dispatch(s, Args{nullptr, k, v, gdec, rec, segdec, nullptr, nullptr, 1, G, NSEG, true}, st);
+    return dispatch(s, Args{nullptr, k, v, gdec, rec, segdec, nullptr, nullptr, 1, G, NSEG, true, true}, st);
 }
 
 hipError_t launch_fwd16(const Shape& s, const void* q, const void* k, const void* v,
                         const float* prefix, float* final_rec, void* o, int causal, int G,
-                        int NSEG, hipStream_t st) {
-    return dispatch(s, Args{q, k, v, nullptr, final_rec, nullptr, prefix, o, causal, G, NSEG, false}, st);
+                        int NSEG, bool prec, hipStream_t st) {
+    return dispatch(s, Args{q, k, v, nullptr, final_rec, nullptr, prefix, o, causal, G, NSEG, false, prec}, st);
 }
 
 hipError_t launch_fwd16_decay(const Shape& s, const void* q, const void* k, const void* v,
                               const float* gdec, const float* prefix, float* final_rec, void* o,
                               int G, int NSEG, hipStream_t st) {
-    return dispatch(s, Args{q, k, v, gdec, final_rec, nullptr, prefix, o, 1, G, NSEG, false}, st);
+    return dispatch(s, Args{q, k, v, gdec, final_rec, nullptr, prefix, o, 1, G, NSEG, false, true}, st);
 }
 
 // ---- record <-> packed state conversion ------------------------------------

@@ -128,30 +128,27 @@ __device__ __forceinline__ constexpr int own_query_tile(int u) {
 // phi(K) rows of feature tile T for the 8 tokens of one K-step: kl / ku hold
 // coordinate c16 / 16 + c16 of each token (fp32, exact).
 template <int T>
-__device__ __forceinline__ u32x4_t lift_keys32(const float (&kl)[8], const float (&ku)[8]) {
-    float f[8];
+__device__ __forceinline__ void lift_key_values32(const float (&kl)[8], const float (&ku)[8],
+                                                  float (&f)[8]) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         if constexpr (T < 8) f[s] = kl[s] * partner<T>(kl[s]);
         else if constexpr (T < 16) f[s] = ku[s] * partner<T - 8>(ku[s]);
         else f[s] = kl[s] * partner<T - 16>(ku[s]);
     }
-    return u32x4_t{pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
 }
 
 // Tile 32: rows < 8 pair L[rho] with L[rho + 8], rows >= 8 pair U[rho] with
 // U[rho - 8]; b is chosen so that the rotated fetch lands on the right half.
-__device__ __forceinline__ u32x4_t lift_keys_mixed(const float (&kl)[8], const float (&ku)[8],
-                                                   const Lane& L) {
+__device__ __forceinline__ void lift_key_values_mixed(const float (&kl)[8], const float (&ku)[8],
+                                                      const Lane& L, float (&f)[8]) {
     const bool lo = L.c16 < 8;
-    float f[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         const float a = lo ? kl[s] : ku[s];
         const float b = lo ? ku[s] : kl[s];
         f[s] = a * partner<8>(b);
     }
-    return u32x4_t{pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7])};
 }
 
 // Compile-time loop.
@@ -207,6 +204,17 @@ __device__ __forceinline__ float query_entry(const QueryRow& Q, int r, bool lo_r
     else return lo_rows ? Q.a2[r] * Q.a[r + 8] : Q.b2[r] * Q.b[r + 8];
 }
 
+// The entries of the tile pair (T, T + 1) in B-operand slot order, in fp32.
+template <int T>
+__device__ __forceinline__ void query_pair_values(const QueryRow& Q, const Lane& L, float (&f)[8]) {
+    const bool lo = L.g < 2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        f[r] = query_entry<T>(Q, r, lo);
+        f[4 + r] = query_entry<T + 1>(Q, r, lo);
+    }
+}
+
 // B operand of the tile pair (T, T + 1): slots 0..3 = tile T rows 4g + s,
 // slots 4..7 = tile T + 1.
 template <int T>
@@ -251,8 +259,10 @@ __device__ __forceinline__ u32x4_t pack8(const float (&x)[8]) {
 }
 
 // S(own tiles) += phi(K_m)^T V_m, Z(own tile) += K_m^T K_m over one K-step;
-// with DECAY each key weighted 2^{b_last - b_j}.
-template <int W, int DV, int C, bool DECAY = false>
+// with DECAY each key weighted 2^{b_last - b_j}. PREC takes the lifted keys as
+// split operands (hi + lo; exact for unscaled bf16 keys) and the Gram product of
+// scaled keys as hi*hi + hi*lo + lo*hi, so the state carries fp32-accurate sums.
+template <int W, int DV, int C, bool DECAY = false, bool PREC = false>
 __device__ __forceinline__ void state_step(State32<DV, C>& st, const bf16_t* bk, const bf16_t* bv,
                                            int m, const Lane& L, const KeyDecay& kd = KeyDecay{}) {
     using F = Cfg32<DV, C>;
@@ -270,23 +280,54 @@ __device__ __forceinline__ void state_step(State32<DV, C>& st, const bf16_t* bk,
     }
     if constexpr (W < 4) {
         // Gram tile W: LL, LU, UL, UU (A rows = first half, B columns = second)
-        const u32x4_t gl = pack8(kl), gu = pack8(ku);
-        if constexpr (W == 0) st.z = mma32(gl, gl, st.z);
-        else if constexpr (W == 1) st.z = mma32(gl, gu, st.z);
-        else if constexpr (W == 2) st.z = mma32(gu, gl, st.z);
-        else st.z = mma32(gu, gu, st.z);
+        if constexpr (PREC && DECAY) {
+            u32x4_t a, al, b, bl;
+            split8(W < 2 ? kl : ku, a, al);
+            split8(W == 0 || W == 2 ? kl : ku, b, bl);
+            st.z = mma32(a, b, st.z);
+            st.z = mma32(a, bl, st.z);
+            st.z = mma32(al, b, st.z);
+        } else {
+            const u32x4_t gl = pack8(kl), gu = pack8(ku);
+            if constexpr (W == 0) st.z = mma32(gl, gl, st.z);
+            else if constexpr (W == 1) st.z = mma32(gl, gu, st.z);
+            else if constexpr (W == 2) st.z = mma32(gu, gl, st.z);
+            else st.z = mma32(gu, gu, st.z);
+        }
     }
     u32x4_t vop[F::NTV];
 #pragma unroll
     for (int nt = 0; nt < F::NTV; ++nt) vop[nt] = v_fragment_tr<DV>(bv, m, nt, L);
     static_for<0, F::TPW>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        const u32x4_t fk = lift_keys32<F::TPW * W + i>(kl, ku);
+        float f[8];
+        lift_key_values32<F::TPW * W + i>(kl, ku, f);
+        if constexpr (PREC) {
+            u32x4_t fh, fl;
+            split8(f, fh, fl);
 #pragma unroll
-        for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] = mma32(fk, vop[nt], st.s[i][nt]);
+            for (int nt = 0; nt < F::NTV; ++nt) {
+                st.s[i][nt] = mma32(fh, vop[nt], st.s[i][nt]);
+                st.s[i][nt] = mma32(fl, vop[nt], st.s[i][nt]);
+            }
+        } else {
+            const u32x4_t fk = pack8(f);
+#pragma unroll
+            for (int nt = 0; nt < F::NTV; ++nt) st.s[i][nt] = mma32(fk, vop[nt], st.s[i][nt]);
+        }
     });
-    if constexpr (has_x<DV, C, W>())
-        st.x = mma32(lift_keys_mixed(kl, ku, L), vop[xnt<DV, C, W>()], st.x);
+    if constexpr (has_x<DV, C, W>()) {
+        float f[8];
+        lift_key_values_mixed(kl, ku, L, f);
+        if constexpr (PREC) {
+            u32x4_t fh, fl;
+            split8(f, fh, fl);
+            st.x = mma32(fh, vop[xnt<DV, C, W>()], st.x);
+            st.x = mma32(fl, vop[xnt<DV, C, W>()], st.x);
+        } else {
+            st.x = mma32(pack8(f), vop[xnt<DV, C, W>()], st.x);
+        }
+    }
 }
 
 // ---- decay gate ---------------------------------------------------------------------
@@ -390,9 +431,125 @@ __device__ __forceinline__ void publish_state(char* sb, const State32<DV, C>& st
     }
 }
 
+// ---- split-operand publication (PREC) ---------------------------------------------
+// Split operands (hi + lo) double the published state, more than the LDS holds
+// beside two chunk buffers, so it is published and consumed in two passes over
+// half of the tile pairs each: pass 0 holds pairs 0..7 (wavefronts 0..NW/2-1),
+// tile 32 and the Gram rows; pass 1 pairs 8..15 (the other wavefronts). Layout:
+// hi of local pair pl, value tile nt at ((pl*NTV + nt)*64 + lane)*16, lo SPH
+// bytes later; tile 32 hi / lo and Gram hi / lo after them, as in publish_state.
+template <int DV, int C>
+struct Prec32 {
+    using F = Cfg32<DV, C>;
+    static constexpr int SPH = 8 * F::NTV * 1024;
+    static constexpr int X_HI = 2 * SPH, X_LO = X_HI + F::S32;
+    static constexpr int Z_HI = X_LO + F::S32, Z_LO = Z_HI + F::ZOP;
+    static constexpr int SB = Z_LO + F::ZOP;
+};
+
+template <int DV, int C, bool PREC, bool GATE>
+constexpr int lds_fwd32() {
+    using F = Cfg32<DV, C, GATE>;
+    return PREC ? 2 * F::IO::BUF + Prec32<DV, C>::SB + F::NW * F::OTILE + F::NW * F::KROW
+                : F::LDS_FWD;
+}
+
+template <int W, int PASS, int DV, int C>
+__device__ __forceinline__ void publish_pass(char* sb, const State32<DV, C>& st, const Lane& L) {
+    using F = Cfg32<DV, C>;
+    using P = Prec32<DV, C>;
+    if constexpr ((W < F::NW / 2) == (PASS == 0)) {
+#pragma unroll
+        for (int j = 0; j < F::TPW / 2; ++j)
+#pragma unroll
+            for (int nt = 0; nt < F::NTV; ++nt) {
+                const f32x4_t& x = st.s[2 * j][nt];
+                const f32x4_t& y = st.s[2 * j + 1][nt];
+                const int pl = F::TPW / 2 * W + j - 8 * PASS;
+                const u32x4_t hi = {pk2(x[0], x[1]), pk2(x[2], x[3]), pk2(y[0], y[1]), pk2(y[2], y[3])};
+                const u32x2_t lx = lo_of(x, hi[0], hi[1]), ly = lo_of(y, hi[2], hi[3]);
+                char* dst = sb + ((pl * F::NTV + nt) * 64 + L.lane) * 16;
+                *reinterpret_cast<u32x4_t*>(dst) = hi;
+                *reinterpret_cast<u32x4_t*>(dst + P::SPH) = u32x4_t{lx[0], lx[1], ly[0], ly[1]};
+            }
+    }
+    if constexpr (PASS == 0) {
+        if constexpr (has_x<DV, C, W>()) {
+            const u32x2_t hi = {pk2(st.x[0], st.x[1]), pk2(st.x[2], st.x[3])};
+            const int off = (xnt<DV, C, W>() * 64 + L.lane) * 8;
+            *reinterpret_cast<u32x2_t*>(sb + P::X_HI + off) = hi;
+            *reinterpret_cast<u32x2_t*>(sb + P::X_LO + off) = lo_of(st.x, hi[0], hi[1]);
+        }
+        if constexpr (W < 4) {
+            constexpr int half = (W == 1 || W == 3) ? 1 : 0, part = W >= 2 ? 1 : 0;
+            const u32x2_t hi = {pk2(st.z[0], st.z[1]), pk2(st.z[2], st.z[3])};
+            const int off = (half * 64 + L.lane) * 16 + part * 8;
+            *reinterpret_cast<u32x2_t*>(sb + P::Z_HI + off) = hi;
+            *reinterpret_cast<u32x2_t*>(sb + P::Z_LO + off) = lo_of(st.z, hi[0], hi[1]);
+        }
+    }
+}
+
+// The inter-chunk numerator over the pairs of one pass as hi*hi + lo*hi + hi*lo
+// (the lifted query is exact as hi + lo); pass 0 also takes tile 32 and returns
+// this lane's part of q^T Z q (summed over the lane groups by the caller).
+template <int PASS, int DV, int C>
+__device__ __forceinline__ float inter_pass(const char* sb, const QueryRow& Q,
+                                            f32x4_t (&num)[Cfg32<DV, C>::NTV + 1], const Lane& L) {
+    using F = Cfg32<DV, C>;
+    using P = Prec32<DV, C>;
+    static_for<0, 8>([&](auto pc) {
+        constexpr int pl = decltype(pc)::value;
+        float f[8];
+        query_pair_values<2 * (pl + 8 * PASS)>(Q, L, f);
+        u32x4_t fh, fl;
+        split8(f, fh, fl);
+#pragma unroll
+        for (int nt = 0; nt < F::NTV; ++nt) {
+            const char* a = sb + ((pl * F::NTV + nt) * 64 + L.lane) * 16;
+            const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(a);
+            const u32x4_t al = *reinterpret_cast<const u32x4_t*>(a + P::SPH);
+            num[nt] = mma32(ah, fh, num[nt]);
+            num[nt] = mma32(al, fh, num[nt]);
+            num[nt] = mma32(ah, fl, num[nt]);
+        }
+    });
+    float d = 0.0f;
+    if constexpr (PASS == 0) {
+        const bool lo = L.g < 2;
+        float f[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f[r] = query_entry<32>(Q, r, lo);
+        u32x2_t fh, fl;
+        split4(f, fh, fl);
+#pragma unroll
+        for (int nt = 0; nt < F::NTV; ++nt) {
+            const int off = (nt * 64 + L.lane) * 8;
+            const u32x2_t ah = *reinterpret_cast<const u32x2_t*>(sb + P::X_HI + off);
+            const u32x2_t al = *reinterpret_cast<const u32x2_t*>(sb + P::X_LO + off);
+            num[nt] = mma16_acc32(ah, fh, num[nt]);
+            num[nt] = mma16_acc32(al, fh, num[nt]);
+            num[nt] = mma16_acc32(ah, fl, num[nt]);
+        }
+        // Z q with Z as hi + lo (q is exact in bf16)
+        const u32x4_t zlh = *reinterpret_cast<const u32x4_t*>(sb + P::Z_HI + L.lane * 16);
+        const u32x4_t zuh = *reinterpret_cast<const u32x4_t*>(sb + P::Z_HI + (64 + L.lane) * 16);
+        const u32x4_t zll = *reinterpret_cast<const u32x4_t*>(sb + P::Z_LO + L.lane * 16);
+        const u32x4_t zul = *reinterpret_cast<const u32x4_t*>(sb + P::Z_LO + (64 + L.lane) * 16);
+        const f32x4_t zl = mma32(zll, Q.zf, mma32(zlh, Q.zf, zero4()));
+        const f32x4_t zu = mma32(zul, Q.zf, mma32(zuh, Q.zf, zero4()));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            d = __builtin_fmaf(Q.a[r], zl[r], d);
+            d = __builtin_fmaf(Q.b[r], zu[r], d);
+        }
+    }
+    return d;
+}
+
 // ---- per-wavefront bodies ----------------------------------------------------------
 
-template <int W, int DV, int C, bool DECAY>
+template <int W, int DV, int C, bool DECAY, bool PREC>
 __device__ __forceinline__ void seg_state_body32(const bf16_t* k, const bf16_t* v, const float* gdec,
                                                  float* rec, float* segdec, char* lds, int T,
                                                  int NC, int G, int NSEG, const Lane& L) {
@@ -423,14 +580,14 @@ __device__ __forceinline__ void seg_state_body32(const bf16_t* k, const bf16_t* 
             lsum += kd.last;
         }
 #pragma unroll
-        for (int m = 0; m < F::KS; ++m) state_step<W, DV, C, DECAY>(st, bk, bv, m, L, kd);
+        for (int m = 0; m < F::KS; ++m) state_step<W, DV, C, DECAY, PREC>(st, bk, bv, m, L, kd);
         compiler_fence();
     }
     record_store32<W, DV, C>(rec + (bh * NSEG + seg) * (size_t)F::REC, st, L);
     if (DECAY && W == 0 && L.lane == 0) segdec[bh * NSEG + seg] = exp2_neg(lsum);
 }
 
-template <int W, int DV, int C, bool CAUSAL, bool DECAY>
+template <int W, int DV, int C, bool CAUSAL, bool DECAY, bool PREC>
 __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                            const float* gdec, const float* prefix,
                                            float* final_rec, bf16_t* o, char* lds, int T, int NC,
@@ -441,8 +598,9 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
     Pipeline<DK, DV, C, F::NW, F::NW, DECAY> P{lds, seg * G, min(NC, seg * G + G), T, bh * T,
                                                true, gdec};
     char* sb = lds + 2 * F::IO::BUF;
-    char* otile = sb + F::SB + W * F::OTILE;
-    float* krow = reinterpret_cast<float*>(sb + F::SB + F::NW * F::OTILE + W * F::KROW);
+    constexpr int SBX = PREC ? Prec32<DV, C>::SB : F::SB;   // published state operands
+    char* otile = sb + SBX + W * F::OTILE;
+    float* krow = reinterpret_cast<float*>(sb + SBX + F::NW * F::OTILE + W * F::KROW);
 
     State32<DV, C> st;
     record_load32<W, DV, C>(prefix + (CAUSAL ? bh * NSEG + seg : bh) * (size_t)F::REC, st, L);
@@ -459,8 +617,9 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
         if constexpr (DECAY) kd = chunk_key_decays<C>(buf + 2 * F::IO::QB + F::IO::VB, krow, L);
 
         // the state before this chunk, as bf16 operands for every wavefront (the
-        // acquire barrier guarantees the previous chunk's readers are done)
-        if (CAUSAL || c == P.c0) {
+        // acquire barrier guarantees the previous chunk's readers are done);
+        // split operands are published in two passes inside the tile loop
+        if (!PREC && (CAUSAL || c == P.c0)) {
             publish_state<W, DV, C>(sb, st, L);
             lds_barrier();
         }
@@ -477,7 +636,21 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
 #pragma unroll
             for (int nt = 0; nt <= F::NTV; ++nt) num[nt] = zero4();
             float di;
-            {
+            if constexpr (PREC) {
+                static_assert(F::TW == 1, "one query tile per wavefront");
+                QueryRow Q;
+                load_query32(bq, tt, L, Q);
+                publish_pass<W, 0, DV, C>(sb, st, L);
+                lds_barrier();
+                float d = inter_pass<0, DV, C>(sb, Q, num, L);
+                lds_barrier();                            // pass 0 read by everyone
+                publish_pass<W, 1, DV, C>(sb, st, L);
+                lds_barrier();
+                inter_pass<1, DV, C>(sb, Q, num, L);
+                d += __shfl_xor(d, 16, 64);
+                d += __shfl_xor(d, 32, 64);
+                di = d;
+            } else {
                 QueryRow Q;
                 load_query32(bq, tt, L, Q);
                 static_for<0, 16>([&](auto pc) {
@@ -586,7 +759,7 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
         if (CAUSAL && (c + 1 < P.c1 || final_rec)) {
             if constexpr (DECAY) decay_state32<W, DV, C>(st, kd.last);
 #pragma unroll
-            for (int m = 0; m < F::KS; ++m) state_step<W, DV, C, DECAY>(st, bk, bv, m, L, kd);
+            for (int m = 0; m < F::KS; ++m) state_step<W, DV, C, DECAY, PREC>(st, bk, bv, m, L, kd);
         }
         compiler_fence();
     }
@@ -605,7 +778,7 @@ __device__ __forceinline__ void by_wave(int w, F&& f) {
 
 // ---- kernels -------------------------------------------------------------------
 
-template <int DV, int C, bool DECAY>
+template <int DV, int C, bool DECAY, bool PREC>
 __global__ __launch_bounds__(kThreads32<C>, kWavesPerSimd32<C>)
 void kata_seg_state32(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                       const float* __restrict__ gdec, float* __restrict__ rec,
@@ -614,22 +787,23 @@ void kata_seg_state32(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v
     __shared__ __attribute__((aligned(16))) char lds[F::LDS_SEG];
     const Lane L;
     by_wave<DV, C>(L.w, [&](auto wc) {
-        seg_state_body32<decltype(wc)::value, DV, C, DECAY>(k, v, gdec, rec, segdec, lds, T, NC,
+        seg_state_body32<decltype(wc)::value, DV, C, DECAY, PREC>(k, v, gdec, rec, segdec, lds, T, NC,
                                                             G, NSEG, as_wave<decltype(wc)::value>(L));
     });
 }
 
-template <int DV, int C, bool CAUSAL, bool DECAY>
+template <int DV, int C, bool CAUSAL, bool DECAY, bool PREC>
 __global__ __launch_bounds__(kThreads32<C>, kWavesPerSimd32<C>)
 void kata_fwd32(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bf16_t* __restrict__ v, const float* __restrict__ gdec,
                 const float* __restrict__ prefix, float* __restrict__ final_rec,
                 bf16_t* __restrict__ o, int T, int NC, int G, int NSEG) {
-    using F = Cfg32<DV, C, DECAY>;
-    __shared__ __attribute__((aligned(16))) char lds[F::LDS_FWD];
+    constexpr int kLds = lds_fwd32<DV, C, PREC, DECAY>();
+    static_assert(kLds <= 160 * 1024, "fits the LDS of a compute unit");
+    __shared__ __attribute__((aligned(16))) char lds[kLds];
     const Lane L;
     by_wave<DV, C>(L.w, [&](auto wc) {
-        fwd_body32<decltype(wc)::value, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o,
+        fwd_body32<decltype(wc)::value, DV, C, CAUSAL, DECAY, PREC>(q, k, v, gdec, prefix, final_rec, o,
                                                               lds, T, NC, G, NSEG,
                                                               as_wave<decltype(wc)::value>(L));
     });
@@ -648,6 +822,7 @@ struct Args32 {
     void* o;
     int causal, G, NSEG;
     bool state_only;
+    bool prec;             // split operands (the gated kernels always take them)
 };
 
 template <int DV, int C>
@@ -659,20 +834,31 @@ hipError_t launch_dv_c32(const Shape& s, const Args32& a, hipStream_t st) {
     if (a.gdec && !a.causal) return hipErrorInvalidValue;
     if (a.state_only) {
         if (a.gdec)
-            kata_seg_state32<DV, C, true><<<grid, threads, 0, st>>>(k, v, a.gdec, a.rec, a.segdec,
-                                                                     s.T, s.NC, a.G, a.NSEG);
+            kata_seg_state32<DV, C, true, true><<<grid, threads, 0, st>>>(k, v, a.gdec, a.rec, a.segdec,
+                                                                           s.T, s.NC, a.G, a.NSEG);
+        else if (a.prec)
+            kata_seg_state32<DV, C, false, true><<<grid, threads, 0, st>>>(k, v, nullptr, a.rec, nullptr,
+                                                                            s.T, s.NC, a.G, a.NSEG);
         else
-            kata_seg_state32<DV, C, false><<<grid, threads, 0, st>>>(k, v, nullptr, a.rec, nullptr,
-                                                                      s.T, s.NC, a.G, a.NSEG);
+            kata_seg_state32<DV, C, false, false><<<grid, threads, 0, st>>>(k, v, nullptr, a.rec, nullptr,
+                                                                             s.T, s.NC, a.G, a.NSEG);
     } else if (a.gdec) {
-        kata_fwd32<DV, C, true, true><<<grid, threads, 0, st>>>(q, k, v, a.gdec, a.prefix, a.rec, o,
-                                                                 s.T, s.NC, a.G, a.NSEG);
+        kata_fwd32<DV, C, true, true, true><<<grid, threads, 0, st>>>(q, k, v, a.gdec, a.prefix, a.rec, o,
+                                                                       s.T, s.NC, a.G, a.NSEG);
     } else if (a.causal) {
-        kata_fwd32<DV, C, true, false><<<grid, threads, 0, st>>>(q, k, v, nullptr, a.prefix, a.rec,
-                                                                  o, s.T, s.NC, a.G, a.NSEG);
+        if (a.prec)
+            kata_fwd32<DV, C, true, false, true><<<grid, threads, 0, st>>>(q, k, v, nullptr, a.prefix,
+                                                                            a.rec, o, s.T, s.NC, a.G, a.NSEG);
+        else
+            kata_fwd32<DV, C, true, false, false><<<grid, threads, 0, st>>>(q, k, v, nullptr, a.prefix,
+                                                                             a.rec, o, s.T, s.NC, a.G, a.NSEG);
     } else {
-        kata_fwd32<DV, C, false, false><<<grid, threads, 0, st>>>(q, k, v, nullptr, a.prefix, a.rec,
-                                                                   o, s.T, s.NC, a.G, a.NSEG);
+        if (a.prec)
+            kata_fwd32<DV, C, false, false, true><<<grid, threads, 0, st>>>(q, k, v, nullptr, a.prefix,
+                                                                             a.rec, o, s.T, s.NC, a.G, a.NSEG);
+        else
+            kata_fwd32<DV, C, false, false, false><<<grid, threads, 0, st>>>(q, k, v, nullptr, a.prefix,
+                                                                              a.rec, o, s.T, s.NC, a.G, a.NSEG);
     }
     return hipGetLastError();
 }
@@ -736,28 +922,28 @@ bool mfma32_supported(const Shape& s) {
 int mfma32_record_floats(int dv) { return NFT * (dv / 16) * 256 + NZ * 256; }
 
 hipError_t launch_seg_state32(const Shape& s, const void* k, const void* v, float* rec, int G,
-                              int NSEG, hipStream_t st) {
-    return dispatch32(s, Args32{nullptr, k, v, nullptr, rec, nullptr, nullptr, nullptr, 1, G, NSEG, true},
-                      st);
+                              int NSEG, bool prec, hipStream_t st) {
+    return dispatch32(s, Args32{nullptr, k, v, nullptr, rec, nullptr, nullptr, nullptr, 1, G, NSEG, true,
+                                prec}, st);
 }
 
 hipError_t launch_fwd32(const Shape& s, const void* q, const void* k, const void* v,
                         const float* prefix, float* final_rec, void* o, int causal, int G,
-                        int NSEG, hipStream_t st) {
-    return dispatch32(s, Args32{q, k, v, nullptr, final_rec, nullptr, prefix, o, causal, G, NSEG, false},
-                      st);
+                        int NSEG, bool prec, hipStream_t st) {
+    return dispatch32(s, Args32{q, k, v, nullptr, final_rec, nullptr, prefix, o, causal, G, NSEG, false,
+                                prec}, st);
 }
 
 hipError_t launch_seg_state32_decay(const Shape& s, const void* k, const void* v, const float* gdec,
                                     float* rec, float* segdec, int G, int NSEG, hipStream_t st) {
-    return dispatch32(s, Args32{nullptr, k, v, gdec, rec, segdec, nullptr, nullptr, 1, G, NSEG, true},
+    return dispatch32(s, Args32{nullptr, k, v, gdec, rec, segdec, nullptr, nullptr, 1, G, NSEG, true, true},
                       st);
 }
 
 hipError_t launch_fwd32_decay(const Shape& s, const void* q, const void* k, const void* v,
                               const float* gdec, const float* prefix, float* final_rec, void* o,
                               int G, int NSEG, hipStream_t st) {
-    return dispatch32(s, Args32{q, k, v, gdec, final_rec, nullptr, prefix, o, 1, G, NSEG, false}, st);
+    return dispatch32(s, Args32{q, k, v, gdec, final_rec, nullptr, prefix, o, 1, G, NSEG, false, true}, st);
 }
 
 hipError_t launch_record_from_packed32(float* rec, const float* S, const float* z, int dv,

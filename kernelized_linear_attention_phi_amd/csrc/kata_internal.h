@@ -71,17 +71,25 @@ hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream
 bool mfma16_supported(const Shape& s);
 // floats per state record (accumulator order, see kata_fwd16.hip)
 int mfma16_record_floats(int dv);
-// rec [BH, NSEG, REC]: total state of every segment
+// rec [BH, NSEG, REC]: total state of every segment. prec: split (hi + lo)
+// operands for the lifted keys (exact for bf16 keys), so the records are
+// fp32-accurate sums.
 hipError_t launch_seg_state16(const Shape& s, const void* k, const void* v, float* rec, int G,
-                              int NSEG, hipStream_t st);
+                              int NSEG, bool prec, hipStream_t st);
 // causal: prefix [BH, NSEG, REC] exclusive segment prefixes; else prefix [BH, REC] totals
 // final_rec (NULL or [BH, REC]): causal only, the running state after each
 // head's last segment (the final state when NSEG == 1)
+// prec: split (hi + lo) bf16 operands for the inter-chunk term phi(Q).S, the
+// Gram denominator and the state update (about three times their matrix work).
+// With G = 1 and a grid of one segment per head it recomputes only the first
+// chunk of every head from `prefix` (the initial-state record).
 hipError_t launch_fwd16(const Shape& s, const void* q, const void* k, const void* v,
                         const float* prefix, float* final_rec, void* o, int causal, int G,
-                        int NSEG, hipStream_t st);
+                        int NSEG, bool prec, hipStream_t st);
 // Decay-gated (causal only): gdec [BH, T] per-token log-decays (<= 0); the state
-// kernel also writes each segment's total decay to segdec [BH, NSEG].
+// kernel also writes each segment's total decay to segdec [BH, NSEG]. The gated
+// kernels always take split operands (a strong gate leaves a few keys in the
+// state, whose bf16 rounding would not average out).
 hipError_t launch_seg_state16_decay(const Shape& s, const void* k, const void* v,
                                     const float* gdec, float* rec, float* segdec, int G, int NSEG,
                                     hipStream_t st);
@@ -97,16 +105,18 @@ hipError_t launch_record_to_packed16(const float* rec, float* S, float* z, int d
 
 bool mfma32_supported(const Shape& s);
 int mfma32_record_floats(int dv);
+// prec as for d_k = 16
 hipError_t launch_seg_state32(const Shape& s, const void* k, const void* v, float* rec, int G,
-                              int NSEG, hipStream_t st);
+                              int NSEG, bool prec, hipStream_t st);
 // final_rec (NULL or [BH, REC]): causal only, the running state after each
-// head's last segment (the final state when NSEG == 1)
+// head's last segment (the final state when NSEG == 1). prec as for d_k = 16
+// (the split state is published in two passes of half the tiles each).
 hipError_t launch_fwd32(const Shape& s, const void* q, const void* k, const void* v,
                         const float* prefix, float* final_rec, void* o, int causal, int G,
-                        int NSEG, hipStream_t st);
-// Decay-gated (causal only, as for d_k = 16): gdec [BH, T] per-token log-decays
-// (<= 0); the state kernel also writes each segment's total decay to segdec
-// [BH, NSEG].
+                        int NSEG, bool prec, hipStream_t st);
+// Decay-gated (causal only, as for d_k = 16, split operands): gdec [BH, T]
+// per-token log-decays (<= 0); the state kernel also writes each segment's
+// total decay to segdec [BH, NSEG].
 hipError_t launch_seg_state32_decay(const Shape& s, const void* k, const void* v,
                                     const float* gdec, float* rec, float* segdec, int G, int NSEG,
                                     hipStream_t st);

@@ -36,6 +36,33 @@ __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w 
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
+// Split bf16 operands: a ~ hi + lo with hi = bf16(a) and lo = bf16(a - hi) (the
+// difference is exact in fp32), so hi + lo carries about 16 significant bits,
+// and exactly a when a is the product of two bf16 values (at most 16 significant
+// bits). A product of two split operands is taken as hi*hi + hi*lo + lo*hi on
+// the matrix cores (the lo*lo term is below 2^-16 of the product).
+__device__ __forceinline__ uint32_t pk2_lo(float a, float b, uint32_t hi) {
+    return pk2(a - lo_bf16(hi), b - hi_bf16(hi));
+}
+__device__ __forceinline__ void split8(const float (&f)[8], u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = pk2(f[2 * i], f[2 * i + 1]);
+        lo[i] = pk2_lo(f[2 * i], f[2 * i + 1], hi[i]);
+    }
+}
+__device__ __forceinline__ void split4(const float (&f)[4], u32x2_t& hi, u32x2_t& lo) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        hi[i] = pk2(f[2 * i], f[2 * i + 1]);
+        lo[i] = pk2_lo(f[2 * i], f[2 * i + 1], hi[i]);
+    }
+}
+// The bf16 remainder of an accumulator tile given its rounded pair words.
+__device__ __forceinline__ u32x2_t lo_of(const f32x4_t& x, uint32_t h0, uint32_t h1) {
+    return u32x2_t{pk2_lo(x[0], x[1], h0), pk2_lo(x[2], x[3], h1)};
+}
+
 // D = A(16x32) * B(32x16) + C with 8 bf16 per lane.
 __device__ __forceinline__ f32x4_t mma32(u32x4_t a, u32x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),

@@ -4,10 +4,12 @@
 
 Matrix-core paths (bf16; PSD lift at d_k = 16 with C in {32, 64} and at
 d_k = 32 with C in {64, 128}; first-order feature with C in {32, 64}; T a
-multiple of 4 across heads): fp32 accumulation of bf16 operands, outputs within
-2e-2 (row-normwise), final states within 2e-2 of the state norm (the lifted
-keys are rounded to bf16 before the matrix cores, as in the ungated parity
-tests). VALU path (every other shape): fp32 arithmetic
+multiple of 4 across heads): fp32 accumulation, outputs within 2e-2
+(row-normwise). The gated PSD kernels take split (hi + lo) bf16 operands for
+every lifted feature, state entry and Gram product, so their final states are
+fp32-accurate sums (within 1e-4 of the state norm) and strong gates, which
+leave only a few keys in the state, still meet 2e-2. The first-order kernels
+round scaled keys to bf16 (states within 2e-2). VALU path (every other shape): fp32 arithmetic
 throughout, outputs within 1e-4 for fp32 inputs and 2e-2 for bf16 (the bf16
 rounding of the output), states within 1e-4. The decode step is fp32
 arithmetic on the state (1e-5 for fp32 inputs)."""
@@ -21,7 +23,8 @@ from tests.gpu_util import dev, host, row_rel_err, sample_rows, say, state_rel_e
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
-STATE_TOL = 2e-2
+STATE_TOL = 2e-2          # first-order matrix-core kernels (bf16 keys after scaling)
+PSD_STATE_TOL = 1e-4      # gated PSD kernels: split operands, fp32-accurate sums
 
 
 @pytest.fixture(scope="module")
@@ -71,40 +74,42 @@ def test_decay_fwd(kata, prefix, dv, C, gmin):
     o, S, z = run(kata, q, k, v, g, C, prefix, state=True)
     assert row_rel_err(o, O.decay_brute_force(q, k, v, g)) <= TOL
     _, S_ref, z_ref = O.decay_recurrent(q, k, v, g)
-    assert state_rel_err(S, S_ref) <= STATE_TOL and state_rel_err(z, z_ref) <= STATE_TOL
+    assert state_rel_err(S, S_ref) <= PSD_STATE_TOL and state_rel_err(z, z_ref) <= PSD_STATE_TOL
 
 
 @pytest.mark.parametrize("prefix", ["scan", "sequential"])
-def test_decay_strong_gate(kata, prefix):
-    """Per-token decays down to exp(-0.5): the state holds a few recent keys.
-    The inter-chunk term evaluates (q.k)^2 through bf16-rounded lifted features
-    (absolute error about 2^-9 |q|^2 |k|^2 per key) while the intra-chunk term
-    gets q.k from fp32 accumulation; with so few keys the feature-rounding error
-    no longer averages out, so outputs just after a chunk start can exceed 2e-2
-    (2.3e-2 seen). The bar here: mean row error within 5e-3, max within 5e-2."""
+@pytest.mark.parametrize("C", [32, 64])
+@pytest.mark.parametrize("gmin", [-0.5, -1.0])
+def test_decay_strong_gate(kata, prefix, C, gmin):
+    """Per-token decays down to exp(-0.5) and exp(-1): the state holds a few
+    recent keys. The inter-chunk term evaluates (q.k)^2 through lifted features
+    (sum_p phi(q)_p phi(k)_p, terms of size up to |q|^2 |k|^2); with bf16
+    operands their rounding would not average out over so few keys (2.3e-2 was
+    seen), so the gated kernels split every operand into hi + lo. Every row
+    within 2e-2, states within 1e-4."""
     B, H, T = 2, 3, 1000
     q, k, v = gen.gaussian_qkv(B, H, T, 16, 64, seed=1296, dtype="bf16")
-    g = gen.log_decays(B, H, T, seed=1396, gmin=-0.5)
-    say(f"decay strong gate {prefix}")
-    o = run(kata, q, k, v, g, 32, prefix)
-    ref = O.decay_brute_force(q, k, v, g)
-    err = np.abs(o - ref).max(-1) / np.abs(ref).max(-1)
-    assert err.mean() <= 5e-3 and err.max() <= 5e-2
+    g = gen.log_decays(B, H, T, seed=1396, gmin=gmin)
+    say(f"decay strong gate {prefix} C={C} gmin={gmin}")
+    o, S, z = run(kata, q, k, v, g, C, prefix, state=True)
+    assert row_rel_err(o, O.decay_brute_force(q, k, v, g)) <= TOL
+    _, S_ref, z_ref = O.decay_recurrent(q, k, v, g)
+    assert state_rel_err(S, S_ref) <= PSD_STATE_TOL and state_rel_err(z, z_ref) <= PSD_STATE_TOL
 
 
 @pytest.mark.parametrize("prefix", ["scan", "sequential"])
 def test_decay_zero_gate_is_ungated(kata, prefix):
-    """g = 0 multiplies by exactly 1 everywhere: the gated kernels reproduce the
-    ungated forward bit for bit."""
-    import torch
+    """g = 0: the gated kernels (split operands) give the ungated result, within
+    2e-2 of the ungated oracle, and a final state within 1e-4 of the ungated
+    one (the bitwise comparison holds on the first-order and fp32 paths; here
+    the gated kernels are the more precise of the two)."""
     q, k, v = gen.gaussian_qkv(2, 2, 700, 16, 64, seed=1400, dtype="bf16")
     g = np.zeros((2, 2, 700), np.float32)
     say(f"decay zero gate {prefix}")
-    o = run(kata, q, k, v, g, 64, prefix)
-    ref = host(kata.chunked_fwd(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), chunk=64,
-                                prefix=prefix))
-    torch.cuda.synchronize()
-    assert np.array_equal(o, ref)
+    o, S, z = run(kata, q, k, v, g, 64, prefix, state=True)
+    assert row_rel_err(o, O.brute_force(q, k, v)) <= TOL
+    S_ref, z_ref = O.state_from_tokens(k, v)
+    assert state_rel_err(S, S_ref) <= PSD_STATE_TOL and state_rel_err(z, z_ref) <= PSD_STATE_TOL
 
 
 def test_decay_reset(kata):
@@ -134,7 +139,7 @@ def test_decay_resume(kata, prefix):
                   S0=S0.astype(np.float32), z0=z0.astype(np.float32), state=True)
     assert row_rel_err(o, O.decay_brute_force(q, k, v, g)[:, :, T1:]) <= TOL
     _, S_ref, z_ref = O.decay_recurrent(q, k, v, g)
-    assert state_rel_err(S, S_ref) <= STATE_TOL and state_rel_err(z, z_ref) <= STATE_TOL
+    assert state_rel_err(S, S_ref) <= PSD_STATE_TOL and state_rel_err(z, z_ref) <= PSD_STATE_TOL
 
 
 @pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 1001])
@@ -189,7 +194,7 @@ def test_decay_fwd32(kata, prefix, dv, C, gmin):
     o, S, z = run(kata, q, k, v, g, C, prefix, state=True)
     assert row_rel_err(o, O.decay_brute_force(q, k, v, g)) <= TOL
     _, S_ref, z_ref = O.decay_recurrent(q, k, v, g)
-    assert state_rel_err(S, S_ref) <= STATE_TOL and state_rel_err(z, z_ref) <= STATE_TOL
+    assert state_rel_err(S, S_ref) <= PSD_STATE_TOL and state_rel_err(z, z_ref) <= PSD_STATE_TOL
 
 
 @pytest.mark.parametrize("G", [2, 3])
@@ -205,36 +210,36 @@ def test_decay_fwd32_segments(kata, monkeypatch, G, C):
     o, S, z = run(kata, q, k, v, g, C, "scan", state=True)
     assert row_rel_err(o, O.decay_brute_force(q, k, v, g)) <= TOL
     _, S_ref, z_ref = O.decay_recurrent(q, k, v, g)
-    assert state_rel_err(S, S_ref) <= STATE_TOL and state_rel_err(z, z_ref) <= STATE_TOL
+    assert state_rel_err(S, S_ref) <= PSD_STATE_TOL and state_rel_err(z, z_ref) <= PSD_STATE_TOL
 
 
 @pytest.mark.parametrize("prefix", ["scan", "sequential"])
-def test_decay_fwd32_strong_gate(kata, prefix):
-    """Decays down to exp(-0.5) per token at d_k = 32, with the bar of the
-    d_k = 16 strong-gate test (few effective keys, so bf16 feature rounding
-    does not average out): mean row error within 5e-3, max within 5e-2."""
+@pytest.mark.parametrize("C", [64, 128])
+@pytest.mark.parametrize("gmin", [-0.5, -1.0])
+def test_decay_fwd32_strong_gate(kata, prefix, C, gmin):
+    """Decays down to exp(-0.5) and exp(-1) per token at d_k = 32 (few
+    effective keys; split operands as at d_k = 16): every row within 2e-2,
+    states within 1e-4."""
     q, k, v = gen.gaussian_qkv(2, 2, 1000, 32, 64, seed=1920, dtype="bf16")
-    g = gen.log_decays(2, 2, 1000, seed=1921, gmin=-0.5)
-    say(f"decay d32 strong gate {prefix}")
-    o = run(kata, q, k, v, g, 64, prefix)
-    ref = O.decay_brute_force(q, k, v, g)
-    err = np.abs(o - ref).max(-1) / np.abs(ref).max(-1)
-    assert err.mean() <= 5e-3 and err.max() <= 5e-2
+    g = gen.log_decays(2, 2, 1000, seed=1921, gmin=gmin)
+    say(f"decay d32 strong gate {prefix} C={C} gmin={gmin}")
+    o, S, z = run(kata, q, k, v, g, C, prefix, state=True)
+    assert row_rel_err(o, O.decay_brute_force(q, k, v, g)) <= TOL
+    _, S_ref, z_ref = O.decay_recurrent(q, k, v, g)
+    assert state_rel_err(S, S_ref) <= PSD_STATE_TOL and state_rel_err(z, z_ref) <= PSD_STATE_TOL
 
 
 @pytest.mark.parametrize("prefix", ["scan", "sequential"])
 @pytest.mark.parametrize("C", [64, 128])
 def test_decay_fwd32_zero_gate_is_ungated(kata, prefix, C):
-    """g = 0: the gated d_k = 32 kernels reproduce the ungated ones bit for bit."""
-    import torch
+    """g = 0 at d_k = 32: the ungated result (oracle, 2e-2) and state (1e-4)."""
     q, k, v = gen.gaussian_qkv(2, 2, 700, 32, 64, seed=1930, dtype="bf16")
     g = np.zeros((2, 2, 700), np.float32)
     say(f"decay d32 zero gate {prefix} C={C}")
-    o = run(kata, q, k, v, g, C, prefix)
-    ref = host(kata.chunked_fwd(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), chunk=C,
-                                prefix=prefix))
-    torch.cuda.synchronize()
-    assert np.array_equal(o, ref)
+    o, S, z = run(kata, q, k, v, g, C, prefix, state=True)
+    assert row_rel_err(o, O.brute_force(q, k, v)) <= TOL
+    S_ref, z_ref = O.state_from_tokens(k, v)
+    assert state_rel_err(S, S_ref) <= PSD_STATE_TOL and state_rel_err(z, z_ref) <= PSD_STATE_TOL
 
 
 def test_decay_fwd32_reset(kata):
@@ -265,7 +270,7 @@ def test_decay_fwd32_resume(kata, prefix):
                   S0=S0.astype(np.float32), z0=z0.astype(np.float32), state=True)
     assert row_rel_err(o, O.decay_brute_force(q, k, v, g)[:, :, T1:]) <= TOL
     _, S_ref, z_ref = O.decay_recurrent(q, k, v, g)
-    assert state_rel_err(S, S_ref) <= STATE_TOL and state_rel_err(z, z_ref) <= STATE_TOL
+    assert state_rel_err(S, S_ref) <= PSD_STATE_TOL and state_rel_err(z, z_ref) <= PSD_STATE_TOL
 
 
 def test_decay_fwd32_bitwise_causality(kata):

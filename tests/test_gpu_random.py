@@ -4,11 +4,14 @@ d_k, d_v, chunk, dtype, feature map, prefix method, causal or not, decay gate,
 initial state. Each runs through the C ABI and is compared with the float64
 oracles (oracle/kata_oracle.py, oracle/first_order_oracle.py,
 oracle/decay_oracle.py): outputs row-relative within 1e-4 (fp32 inputs) or
-2e-2 (bf16), final states within 1e-4 (fp32) or 2e-2 (bf16, where the matrix
-cores round lifted keys to bf16). Configurations are drawn only from the
-supported set: the sequential prefix needs a bf16 matrix-core shape, and the
-gated matrix-core shapes also T % 4 == 0 or a single head. Initial states
-stand for 32-300 earlier tokens, for causal and non-causal calls alike."""
+2e-2 (bf16), final states within 1e-4 where every lifted key enters the state
+exactly (fp32 inputs, the fp32 path, and the gated PSD matrix-core kernels,
+which take split operands) and 2e-2 elsewhere (the matrix cores round lifted
+keys to bf16). Configurations are drawn only from
+the supported set: the sequential prefix needs a bf16 matrix-core shape, and
+the gated matrix-core shapes also T % 4 == 0 or a single head. Initial states
+stand for 1-300 earlier tokens, for causal and non-causal calls alike, and
+per-token decays reach down to exp(-0.5)."""
 import numpy as np
 import pytest
 
@@ -39,15 +42,16 @@ def _draw(i):
         "feature": str(r.choice(["psd", "psd", "identity"])), "gated": bool(r.random() < 0.4),
     }
     cfg["causal"] = cfg["gated"] or bool(r.random() < 0.85)
-    # an initial state standing for 32-300 earlier tokens (states of a few
-    # tokens are their own regime: test_initial_state_of_few_keys)
+    # an initial state standing for 1-300 earlier tokens (half of them for at
+    # most 8: the few-key regime)
     cfg["S0"] = bool(r.random() < 0.5)
-    cfg["T0"] = int(r.integers(32, 300))
+    cfg["T0"] = int(r.choice([int(r.integers(1, 9)), int(r.integers(1, 300))]))
     mc = _matrix_core_shape(cfg["dtype"], cfg["feature"], cfg["dk"], cfg["C"], cfg["gated"])
     if cfg["gated"] and cfg["T"] % 4 and cfg["B"] * cfg["H"] > 1:
         mc = False                              # gated matrix cores stage T-aligned rows
+    cfg["mc"] = mc
     cfg["prefix"] = "sequential" if mc and r.random() < 0.4 else "scan"
-    cfg["gmin"] = float(r.choice([-0.02, -0.2]))
+    cfg["gmin"] = float(r.choice([-0.02, -0.2, -0.5]))
     return cfg
 
 
@@ -117,7 +121,10 @@ def test_random_config(kata, c):
     assert np.all(np.isfinite(o))
     assert row_rel_err(o, o_ref) <= tol
     if want_state:
-        assert state_rel_err(host(S), S_ref) <= tol and state_rel_err(host(z), z_ref) <= tol
+        # bf16-rounded key lifts: the matrix-core kernels without split operands
+        rounded = dtype == "bf16" and c["mc"] and (feature == "identity" or not c["gated"])
+        stol = 2e-2 if rounded else 1e-4
+        assert state_rel_err(host(S), S_ref) <= stol and state_rel_err(host(z), z_ref) <= stol
 
 
 def _draw_flash(i):
