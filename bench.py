@@ -340,16 +340,36 @@ def cpu_chunked(w, q, k, v, budget_s):
                       "tokens/s = token-heads/(H*s)"}
 
 
+def host_description():
+    """CPU model (from /proc/cpuinfo), cores available to this process, and the
+    BLAS library numpy uses with its thread count."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = None, None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in libs)
+            threads = sum(i.get("num_threads", 0) for i in libs)
+    except Exception:  # noqa: BLE001
+        pass
+    return {"cpu_model": model, "cores_available": len(os.sched_getaffinity(0)),
+            "blas": blas, "blas_threads": threads}
+
+
 def cpu_baseline(w, q, k, v, budget_s):
     """The float64 brute-force oracle on a bounded sample of query rows of the
     same workload (head 0, uniformly drawn positions), scaled to tokens/s."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas")
-    except Exception:  # noqa: BLE001
-        cores = None
-    cores = cores or len(os.sched_getaffinity(0))
+    hostd = host_description()
+    cores = hostd["blas_threads"] or hostd["cores_available"]
     rng = np.random.Generator(np.random.PCG64(99))
     qq, kk, vv = q[:1, :1], k[:1, :1], v[:1, :1]
     rows_done = 0
@@ -362,7 +382,9 @@ def cpu_baseline(w, q, k, v, budget_s):
     tok_s = rows_done / (w.H * el)     # each token needs H head-rows
     return {"value": tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"float64 brute force on {rows_done} uniformly drawn query rows of head "
-                      f"(0,0) of the {w.name} workload in {el:.1f} s; tokens/s = rows/(H*s)"}
+                      f"(0,0) of the {w.name} workload in {el:.1f} s; tokens/s = rows/(H*s)",
+            "cpu_model": hostd["cpu_model"], "blas": hostd["blas"],
+            "cores_available": hostd["cores_available"]}
 
 
 def main():

@@ -75,10 +75,8 @@ const char* kata_version(void);
 /* Bytes of workspace kata_chunked_fwd needs for this problem (0 if none).
  * Returns 0 for unsupported or invalid shapes too; kata_chunked_fwd then
  * reports the precise error. The matrix-core paths cut each (batch, head) into
- * segments of G chunks (about 1024 segments over the whole problem, 256 at
- * d_k = 32); the environment variable KATA_SEGMENT_CHUNKS = G (> 0) overrides
- * G, for tests and tuning. It changes the workspace size, so set it before
- * both calls. */
+ * segments of G chunks, about 1024 segments over the whole problem (256 at
+ * d_k = 32); kata_chunked_fwd_ex takes G explicitly. */
 size_t kata_chunked_fwd_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                   kata_dtype_t dtype, int causal);
 
@@ -96,10 +94,17 @@ size_t kata_chunked_fwd_workspace(int B, int H, int T, int d_k, int d_v, int chu
  *     bytes (may be NULL when that is 0).
  * Output dtype equals input dtype. The mask is inclusive (position t sees j <= t):
  * the explainers' output gate blends the previous readout with the current
- * value (section 2.1). With causal = 0, bf16 inputs, no initial state and T <=
- * chunk, o is evaluated in the quadratic form (as kata_flash_fwd), so that a
- * few keys do not meet the bf16 rounding of lifted features; the final state is
- * formed as otherwise. */
+ * value (section 2.1).
+ * Few keys. Where the inter-chunk prefix may hold only a few keys, its terms
+ * phi(q)_p S_p (each up to |q|^2 |k|^2) sum to weights (q.k)^2 that can be far
+ * smaller, so the bf16 matrix-core shapes (PSD lift; d_k = 16 with chunk 32 or
+ * 64, d_k = 32 with chunk 64 or 128) take those terms with split operands
+ * (hi + lo bf16, about 16 significant bits): with an initial state, the first
+ * chunk of every head (one extra launch of one chunk per head) and, for a
+ * non-causal call within one chunk, every query and the state build. With
+ * causal = 0, no initial state and T <= chunk on those shapes, o is evaluated
+ * in the quadratic form (as kata_flash_fwd), every (q.k)^2 in fp32; the final
+ * state is formed as otherwise. */
 kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, void* o,
                                int B, int H, int T, int d_k, int d_v, int chunk, int causal,
                                kata_dtype_t dtype,
@@ -147,14 +152,21 @@ typedef enum { KATA_PREFIX_SCAN = 0, KATA_PREFIX_SEQUENTIAL = 1 } kata_prefix_t;
  * KATA_FEATURE_IDENTITY; -1 for d < 0 or an unknown feature. */
 int kata_feature_dim(int d, kata_feature_t feature);
 
-/* Workspace of kata_chunked_fwd_ex (0 if none or if the arguments are invalid). */
+/* Workspace of kata_chunked_fwd_ex (0 if none or if the arguments are invalid);
+ * segment_chunks as there (it sets the number of segment records). */
 size_t kata_chunked_fwd_ex_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                      kata_dtype_t dtype, int causal, kata_feature_t feature,
-                                     kata_prefix_t prefix);
+                                     kata_prefix_t prefix, int segment_chunks);
 
 /* kata_chunked_fwd with a choice of feature map and prefix method; every other
  * argument as there, with the state dimension of `feature` in S0, z0, S_out,
- * z_out. KATA_FEATURE_PSD with KATA_PREFIX_SCAN is kata_chunked_fwd.
+ * z_out. KATA_FEATURE_PSD with KATA_PREFIX_SCAN and segment_chunks = 0 is
+ * kata_chunked_fwd.
+ * segment_chunks - G, the chunks per segment of the matrix-core scan paths
+ *   (each segment's state is built by one workgroup and the associative scan
+ *   runs over segment states); 0 = automatic (about one resident wave of
+ *   workgroups), negative = KATA_EINVAL. The same value must be given to the
+ *   workspace query. Ignored by the sequential prefix and the fp32 path.
  * KATA_PREFIX_SEQUENTIAL needs a shape of a bf16 matrix-core path (else
  * KATA_EUNSUPPORTED): for KATA_FEATURE_PSD d_k = 16 with chunk 32 or 64, d_k = 32
  * with chunk 64 or 128; for KATA_FEATURE_IDENTITY chunk 32, 64 or 128. Every
@@ -163,7 +175,7 @@ size_t kata_chunked_fwd_ex_workspace(int B, int H, int T, int d_k, int d_v, int 
 kata_status_t kata_chunked_fwd_ex(const void* q, const void* k, const void* v, void* o,
                                   int B, int H, int T, int d_k, int d_v, int chunk, int causal,
                                   kata_dtype_t dtype, kata_feature_t feature,
-                                  kata_prefix_t prefix,
+                                  kata_prefix_t prefix, int segment_chunks,
                                   const float* S0, const float* z0,
                                   float* S_out, float* z_out,
                                   void* workspace, size_t ws_bytes, void* stream);
@@ -199,19 +211,24 @@ kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v
                                      float* S_out, float* z_out,
                                      void* workspace, size_t ws_bytes, void* stream);
 
-/* kata_chunked_fwd_decay with a choice of feature map: KATA_FEATURE_PSD is
- * kata_chunked_fwd_decay; KATA_FEATURE_IDENTITY gates the first-order feature
- * phi1(x) = x (weights (q_t.k_j) exp(g_{j+1} + ... + g_t), state d_k x d_v in
- * S0, z0, S_out, z_out): on the matrix cores for dtype KATA_BF16 with chunk 32
- * or 64 (either prefix; T a multiple of 4 or B*H == 1), else on the fp32 path
- * with KATA_PREFIX_SCAN. Every other argument, error and layout as there. */
+/* kata_chunked_fwd_decay with a choice of feature map and segment length:
+ * KATA_FEATURE_PSD with segment_chunks = 0 is kata_chunked_fwd_decay;
+ * KATA_FEATURE_IDENTITY gates the first-order feature phi1(x) = x (weights
+ * (q_t.k_j) exp(g_{j+1} + ... + g_t), state d_k x d_v in S0, z0, S_out, z_out):
+ * on the matrix cores for dtype KATA_BF16 with chunk 32 or 64 (either prefix;
+ * T a multiple of 4 or B*H == 1), else on the fp32 path with KATA_PREFIX_SCAN.
+ * segment_chunks as for kata_chunked_fwd_ex. Every other argument, error and
+ * layout as kata_chunked_fwd_decay. The gated PSD matrix-core kernels take
+ * split (hi + lo bf16) operands for every lifted query, key, state entry and
+ * Gram product: strong gates leave only a few keys in the state. */
 size_t kata_chunked_fwd_decay_ex_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                            kata_dtype_t dtype, kata_feature_t feature,
-                                           kata_prefix_t prefix);
+                                           kata_prefix_t prefix, int segment_chunks);
 kata_status_t kata_chunked_fwd_decay_ex(const void* q, const void* k, const void* v,
                                         const float* log_decay, void* o, int B, int H, int T,
                                         int d_k, int d_v, int chunk, kata_dtype_t dtype,
                                         kata_feature_t feature, kata_prefix_t prefix,
+                                        int segment_chunks,
                                         const float* S0, const float* z0, float* S_out,
                                         float* z_out, void* workspace, size_t ws_bytes,
                                         void* stream);

@@ -55,9 +55,9 @@ def lib() -> ctypes.CDLL:
         L.kata_chunked_fwd_profiled.restype = i
         L.kata_feature_dim.argtypes = [i, i]
         L.kata_feature_dim.restype = i
-        L.kata_chunked_fwd_ex_workspace.argtypes = [i, i, i, i, i, i, i, i, i, i]
+        L.kata_chunked_fwd_ex_workspace.argtypes = [i, i, i, i, i, i, i, i, i, i, i]
         L.kata_chunked_fwd_ex_workspace.restype = sz
-        L.kata_chunked_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i,
+        L.kata_chunked_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i,
                                           vp, vp, vp, vp, vp, sz, vp]
         L.kata_chunked_fwd_ex.restype = i
         L.kata_chunked_fwd_decay_workspace.argtypes = [i, i, i, i, i, i, i, i]
@@ -65,9 +65,9 @@ def lib() -> ctypes.CDLL:
         L.kata_chunked_fwd_decay.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                              vp, vp, vp, vp, vp, sz, vp]
         L.kata_chunked_fwd_decay.restype = i
-        L.kata_chunked_fwd_decay_ex_workspace.argtypes = [i, i, i, i, i, i, i, i, i]
+        L.kata_chunked_fwd_decay_ex_workspace.argtypes = [i, i, i, i, i, i, i, i, i, i]
         L.kata_chunked_fwd_decay_ex_workspace.restype = sz
-        L.kata_chunked_fwd_decay_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i,
+        L.kata_chunked_fwd_decay_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i,
                                                 vp, vp, vp, vp, vp, sz, vp]
         L.kata_chunked_fwd_decay_ex.restype = i
         L.kata_decode_step_decay.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
@@ -110,6 +110,33 @@ def _check_dev(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _check_qkv(q, k, v, o=None):
+    """q, k [B,H,T,d_k] and v (and o) [B,H,T,d_v] of one dtype on the GPU."""
+    _check_dev(q, k, v, o)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("expected q, k [B,H,T,d_k] and v [B,H,T,d_v]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    _dtype_code(q)
+    if o is not None and (o.shape != v.shape or o.dtype != v.dtype):
+        raise ValueError("o must match v in shape and dtype")
+
+
+def _check_state(S, z, lead, D, dv, what):
+    """S [*lead, D, d_v] and z [*lead, D], float32 on the GPU (both or neither)."""
+    if (S is None) != (z is None):
+        raise ValueError(f"{what}: give both S and z, or neither")
+    if S is None:
+        return
+    _check_dev(S, z)
+    if S.dtype != torch.float32 or z.dtype != torch.float32:
+        raise TypeError(f"{what}: states are float32")
+    lead = tuple(lead)
+    if tuple(S.shape) != lead + (D, dv) or tuple(z.shape) != lead + (D,):
+        raise ValueError(f"{what}: expected S {lead + (D, dv)} and z {lead + (D,)}, "
+                         f"got {tuple(S.shape)} and {tuple(z.shape)}")
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -135,37 +162,43 @@ def feature_dim(d: int, feature: str = "psd") -> int:
 
 
 def chunked_fwd_workspace(B, H, T, dk, dv, chunk, dtype_code, causal=True, feature="psd",
-                          prefix="scan") -> int:
+                          prefix="scan", segment_chunks=0) -> int:
     f, pf = _modes(feature, prefix)
-    if (f, pf) == (0, 0):
+    if (f, pf) == (0, 0) and segment_chunks == 0:
         return lib().kata_chunked_fwd_workspace(B, H, T, dk, dv, chunk, dtype_code,
                                                 int(bool(causal)))
     return lib().kata_chunked_fwd_ex_workspace(B, H, T, dk, dv, chunk, dtype_code,
-                                               int(bool(causal)), f, pf)
+                                               int(bool(causal)), f, pf, int(segment_chunks))
 
 
 def chunked_fwd_into(q, k, v, o, chunk, causal, workspace, S0=None, z0=None, S_out=None,
-                     z_out=None, events=None, feature="psd", prefix="scan"):
+                     z_out=None, events=None, feature="psd", prefix="scan", segment_chunks=0):
     """Raw call: every buffer preallocated by the caller (used by the benchmark).
 
     events: optional sequence of 5 torch.cuda.Event recorded at the phase
     boundaries (chunk states | scan | output kernel | state export) through
     kata_chunked_fwd_profiled (PSD lift with the scan only).
     feature / prefix: "psd" or "identity" / "scan" or "sequential"; anything but
-    ("psd", "scan") goes through kata_chunked_fwd_ex.
+    ("psd", "scan") or a segment_chunks other than 0 (automatic) goes through
+    kata_chunked_fwd_ex.
     """
+    _check_qkv(q, k, v, o)
+    _check_dev(workspace)
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     f, pf = _modes(feature, prefix)
+    D = phi_dim(dk) if f == 0 else dk
+    _check_state(S0, z0, (B, H), D, dv, "initial state")
+    _check_state(S_out, z_out, (B, H), D, dv, "final state")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, T, dk, dv, chunk, int(bool(causal)),
             _dtype_code(q))
     tail = (_ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(workspace), ws_bytes, _stream())
     args = head + tail
-    if (f, pf) != (0, 0):
+    if (f, pf) != (0, 0) or segment_chunks != 0:
         if events is not None:
             raise ValueError("phase events are for the PSD lift with the scan")
-        st = lib().kata_chunked_fwd_ex(*head, f, pf, *tail)
+        st = lib().kata_chunked_fwd_ex(*head, f, pf, int(segment_chunks), *tail)
     elif events is None:
         st = lib().kata_chunked_fwd(*args)
     else:
@@ -178,7 +211,7 @@ def chunked_fwd_into(q, k, v, o, chunk, causal, workspace, S0=None, z0=None, S_o
 
 
 def chunked_fwd(q, k, v, chunk=64, causal=True, initial_state=None, return_state=False,
-                feature="psd", prefix="scan"):
+                feature="psd", prefix="scan", segment_chunks=0):
     """o = KATA forward of q, k [B,H,T,d_k], v [B,H,T,d_v] (fp32 or bf16).
 
     initial_state: optional (S0 [B,H,D,d_v], z0 [B,H,D]) fp32.
@@ -187,12 +220,10 @@ def chunked_fwd(q, k, v, chunk=64, causal=True, initial_state=None, return_state
       first-order feature, D = d).
     prefix: "scan" (segments + associative scan) or "sequential" (one
       workgroup per head walks every chunk; bf16 matrix-core shapes only).
+    segment_chunks: chunks per segment of the matrix-core scan paths (0 =
+      automatic).
     """
-    _check_dev(q, k, v)
-    if q.dim() != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
-        raise ValueError("expected q, k [B,H,T,d_k] and v [B,H,T,d_v]")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k, v must share a dtype")
+    _check_qkv(q, k, v)
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     _modes(feature, prefix)
@@ -200,19 +231,15 @@ def chunked_fwd(q, k, v, chunk=64, causal=True, initial_state=None, return_state
     S0 = z0 = S_out = z_out = None
     if initial_state is not None:
         S0, z0 = initial_state
-        _check_dev(S0, z0)
-        if S0.dtype != torch.float32 or z0.dtype != torch.float32:
-            raise TypeError("states are float32")
-        if tuple(S0.shape) != (B, H, D, dv) or tuple(z0.shape) != (B, H, D):
-            raise ValueError("initial state shape mismatch")
     if return_state:
         S_out = torch.empty((B, H, D, dv), dtype=torch.float32, device=q.device)
         z_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
     o = torch.empty_like(v)
-    nbytes = chunked_fwd_workspace(B, H, T, dk, dv, chunk, _dtype_code(q), causal, feature, prefix)
+    nbytes = chunked_fwd_workspace(B, H, T, dk, dv, chunk, _dtype_code(q), causal, feature, prefix,
+                                   segment_chunks)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if nbytes else None
     chunked_fwd_into(q, k, v, o, chunk, causal, ws, S0, z0, S_out, z_out, feature=feature,
-                     prefix=prefix)
+                     prefix=prefix, segment_chunks=segment_chunks)
     return (o, (S_out, z_out)) if return_state else o
 
 
@@ -221,7 +248,7 @@ def scan_states(k, v, chunk=64, initial_state=None):
 
     Returns (S_prefix [B,H,NC,D,d_v], z_prefix [B,H,NC,D], S_T, z_T), fp32.
     """
-    _check_dev(k, v)
+    _check_qkv(k, k, v)
     B, H, T, dk = k.shape
     dv = v.shape[-1]
     D = phi_dim(dk)
@@ -229,7 +256,7 @@ def scan_states(k, v, chunk=64, initial_state=None):
     S0 = z0 = None
     if initial_state is not None:
         S0, z0 = initial_state
-        _check_dev(S0, z0)
+    _check_state(S0, z0, (B, H), D, dv, "initial state")
     dev = k.device
     Sp = torch.empty((B, H, NC, D, dv), dtype=torch.float32, device=dev)
     zp = torch.empty((B, H, NC, D), dtype=torch.float32, device=dev)
@@ -246,9 +273,13 @@ def scan_states(k, v, chunk=64, initial_state=None):
 
 def scan_states_into(k, v, chunk, S_prefix, z_prefix, S_out=None, z_out=None, S0=None, z0=None):
     """Raw kata_scan_states into preallocated outputs (used by the benchmark)."""
-    _check_dev(k, v)
+    _check_qkv(k, k, v)
     B, H, T, dk = k.shape
     dv = v.shape[-1]
+    D, NC = phi_dim(dk), -(-T // chunk)
+    _check_state(S_prefix, z_prefix, (B, H, NC), D, dv, "prefix states")
+    _check_state(S0, z0, (B, H), D, dv, "initial state")
+    _check_state(S_out, z_out, (B, H), D, dv, "final state")
     st = lib().kata_scan_states(_ptr(k), _ptr(v), B, H, T, dk, dv, chunk, _dtype_code(k),
                                 _ptr(S0), _ptr(z0), _ptr(S_prefix), _ptr(z_prefix), _ptr(S_out),
                                 _ptr(z_out), None, 0, _stream())
@@ -258,9 +289,7 @@ def scan_states_into(k, v, chunk, S_prefix, z_prefix, S_out=None, z_out=None, S0
 def flash_fwd(q, k, v, causal=True, out=None):
     """Quadratic-form forward (bf16 q, k [B,H,T,d_k], v [B,H,T,d_v]): the same
     output as chunked_fwd without chunk states."""
-    _check_dev(q, k, v)
-    if q.dim() != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
-        raise ValueError("expected q, k [B,H,T,d_k] and v [B,H,T,d_v]")
+    _check_qkv(q, k, v, out)
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     o = torch.empty_like(v) if out is None else out
@@ -273,7 +302,7 @@ def flash_fwd(q, k, v, causal=True, out=None):
 def decode_step(q, k, v, S, z, out=None):
     """One decode step for rows [N, d]: updates S [N,D,d_v], z [N,D] in place,
     returns o [N, d_v]."""
-    _check_dev(q, k, v, S, z)
+    _check_rows(q, k, v, S, z, out)
     N, dk = q.shape
     dv = v.shape[-1]
     o = torch.empty_like(v) if out is None else out
@@ -283,50 +312,71 @@ def decode_step(q, k, v, S, z, out=None):
     return o
 
 
+def _check_rows(q, k, v, S, z, out=None, log_decay=None):
+    """Decode-step arguments: q, k [N,d_k], v [N,d_v] of one dtype, S [N,D,d_v]
+    and z [N,D] float32, out like v, log_decay [N] float32."""
+    _check_dev(q, k, v, S, z, out, log_decay)
+    if q.dim() != 2 or k.shape != q.shape or v.dim() != 2 or v.shape[0] != q.shape[0]:
+        raise ValueError("expected q, k [N,d_k] and v [N,d_v]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    _dtype_code(q)
+    N, dk = q.shape
+    _check_state(S, z, (N,), phi_dim(dk), v.shape[1], "decode state")
+    if out is not None and (out.shape != v.shape or out.dtype != v.dtype):
+        raise ValueError("out must match v in shape and dtype")
+    if log_decay is not None and (log_decay.dtype != torch.float32 or tuple(log_decay.shape) != (N,)):
+        raise ValueError("log_decay must be float32 [N]")
+
+
 # ---- decay gate ------------------------------------------------------------------
 
 def chunked_fwd_decay_workspace(B, H, T, dk, dv, chunk, dtype_code, prefix="scan",
-                                feature="psd") -> int:
+                                feature="psd", segment_chunks=0) -> int:
     f, pf = _modes(feature, prefix)
-    if f == 0:
+    if f == 0 and segment_chunks == 0:
         return lib().kata_chunked_fwd_decay_workspace(B, H, T, dk, dv, chunk, dtype_code, pf)
-    return lib().kata_chunked_fwd_decay_ex_workspace(B, H, T, dk, dv, chunk, dtype_code, f, pf)
+    return lib().kata_chunked_fwd_decay_ex_workspace(B, H, T, dk, dv, chunk, dtype_code, f, pf,
+                                                     int(segment_chunks))
 
 
 def chunked_fwd_decay_into(q, k, v, log_decay, o, chunk, workspace, S0=None, z0=None, S_out=None,
-                           z_out=None, prefix="scan", feature="psd"):
+                           z_out=None, prefix="scan", feature="psd", segment_chunks=0):
     """Raw decay-gated call (kata_chunked_fwd_decay, or kata_chunked_fwd_decay_ex
-    for the identity feature); every buffer preallocated."""
-    _check_dev(log_decay)
-    if log_decay.dtype != torch.float32:
-        raise TypeError("log_decay is float32 [B,H,T]")
+    for the identity feature or an explicit segment length); every buffer
+    preallocated."""
+    _check_qkv(q, k, v, o)
+    _check_dev(log_decay, workspace)
     B, H, T, dk = q.shape
     dv = v.shape[-1]
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if log_decay.dtype != torch.float32 or tuple(log_decay.shape) != (B, H, T):
+        raise ValueError("log_decay must be float32 [B,H,T]")
     f, pf = _modes(feature, prefix)
+    D = phi_dim(dk) if f == 0 else dk
+    _check_state(S0, z0, (B, H), D, dv, "initial state")
+    _check_state(S_out, z_out, (B, H), D, dv, "final state")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(o), B, H, T, dk, dv, chunk,
             _dtype_code(q))
     tail = (_ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(workspace), ws_bytes, _stream())
-    if f == 0:
+    if f == 0 and segment_chunks == 0:
         st = lib().kata_chunked_fwd_decay(*head, pf, *tail)
         _raise(st, "kata_chunked_fwd_decay")
     else:
-        st = lib().kata_chunked_fwd_decay_ex(*head, f, pf, *tail)
+        st = lib().kata_chunked_fwd_decay_ex(*head, f, pf, int(segment_chunks), *tail)
         _raise(st, "kata_chunked_fwd_decay_ex")
 
 
 def chunked_fwd_decay(q, k, v, log_decay, chunk=64, initial_state=None, return_state=False,
-                      prefix="scan", feature="psd"):
+                      prefix="scan", feature="psd", segment_chunks=0):
     """Decay-gated causal KATA forward: log_decay [B,H,T] fp32 (<= 0) is the
     per-token log forget gate (S_t = exp(g_t) S_{t-1} + phi(k_t) v_t^T, z
     likewise). Matrix cores (either prefix) for bf16 with d_k = 16 and chunk 32
     or 64, d_k = 32 and chunk 64 or 128, or feature="identity" (the gated
     first-order feature) and chunk 32 or 64, when T is a multiple of 4 or
     B*H == 1; the fp32 path for every other supported shape (scan prefix).
-    initial_state / return_state as chunked_fwd."""
-    _check_dev(q, k, v)
-    if q.dim() != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
-        raise ValueError("expected q, k [B,H,T,d_k] and v [B,H,T,d_v]")
+    initial_state / return_state / segment_chunks as chunked_fwd."""
+    _check_qkv(q, k, v)
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     if tuple(log_decay.shape) != (B, H, T):
@@ -339,16 +389,17 @@ def chunked_fwd_decay(q, k, v, log_decay, chunk=64, initial_state=None, return_s
         S_out = torch.empty((B, H, D, dv), dtype=torch.float32, device=q.device)
         z_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
     o = torch.empty_like(v)
-    nbytes = chunked_fwd_decay_workspace(B, H, T, dk, dv, chunk, _dtype_code(q), prefix, feature)
+    nbytes = chunked_fwd_decay_workspace(B, H, T, dk, dv, chunk, _dtype_code(q), prefix, feature,
+                                         segment_chunks)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if nbytes else None
     chunked_fwd_decay_into(q, k, v, log_decay.contiguous(), o, chunk, ws, S0, z0, S_out, z_out,
-                           prefix=prefix, feature=feature)
+                           prefix=prefix, feature=feature, segment_chunks=segment_chunks)
     return (o, (S_out, z_out)) if return_state else o
 
 
 def decode_step_decay(q, k, v, log_decay, S, z, out=None):
     """decode_step with a per-row log-decay [N] (fp32): S = exp(g) S + phi(k) v^T."""
-    _check_dev(q, k, v, log_decay, S, z)
+    _check_rows(q, k, v, S, z, out, log_decay)
     N, dk = q.shape
     dv = v.shape[-1]
     o = torch.empty_like(v) if out is None else out

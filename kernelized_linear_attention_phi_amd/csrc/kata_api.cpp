@@ -3,7 +3,6 @@
 // allocates device memory or synchronises.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include <algorithm>
 
@@ -53,19 +52,17 @@ struct FwdPlan {
     size_t S_off, z_off, init_off, total_off, bytes;
 };
 
-int segment_chunks(const Shape& s, int workgroups) {
-    if (const char* e = getenv("KATA_SEGMENT_CHUNKS")) {
-        const int g = atoi(e);
-        if (g > 0) return g;
-    }
-    // about `workgroups` segments in flight (one wave of resident workgroups
-    // over the 256 compute units), each on a run of chunks
+// G for a requested value (> 0) or automatically (0): about `workgroups`
+// segments in flight (one wave of resident workgroups over the 256 compute
+// units), each on a run of chunks.
+int segment_chunks(const Shape& s, int workgroups, int requested) {
+    if (requested > 0) return requested;
     const long long chunks = (long long)s.B * s.H * s.NC;
     return (int)std::max<long long>(1, chunks / workgroups);
 }
 
 FwdPlan plan_fwd(const Shape& s, int causal, kata_feature_t f = KATA_FEATURE_PSD,
-                 kata_prefix_t pf = KATA_PREFIX_SCAN) {
+                 kata_prefix_t pf = KATA_PREFIX_SCAN, int seg_req = 0) {
     FwdPlan p{};
     if (f == KATA_FEATURE_IDENTITY) {
         // matrix cores for the bf16 shapes, else the fp32 path (scan prefix)
@@ -81,7 +78,7 @@ FwdPlan plan_fwd(const Shape& s, int causal, kata_feature_t f = KATA_FEATURE_PSD
     if (p.mfma) {
         // d_k = 16 and the identity feature: four 2-wavefront workgroups per
         // compute unit; d_k = 32: one workgroup (its LDS fills the compute unit)
-        p.G = p.seq ? s.NC : std::min(segment_chunks(s, p.mfma == 32 ? 256 : 1024), s.NC);
+        p.G = p.seq ? s.NC : std::min(segment_chunks(s, p.mfma == 32 ? 256 : 1024, seg_req), s.NC);
         p.NSEG = (s.NC + p.G - 1) / p.G;
         p.REC = p.mfma == 16   ? kata::mfma16_record_floats(s.dv)
                 : p.mfma == 32 ? kata::mfma32_record_floats(s.dv)
@@ -119,7 +116,7 @@ const char* kata_status_string(kata_status_t st) {
     return "unknown status";
 }
 
-const char* kata_version(void) { return "0.1.0"; }
+const char* kata_version(void) { return "0.2.0"; }
 
 size_t kata_chunked_fwd_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                   kata_dtype_t dtype, int causal) {
@@ -142,21 +139,22 @@ static bool valid_modes(kata_feature_t f, kata_prefix_t pf) {
 
 size_t kata_chunked_fwd_ex_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                      kata_dtype_t dtype, int causal, kata_feature_t feature,
-                                     kata_prefix_t prefix) {
+                                     kata_prefix_t prefix, int segment_chunks) {
     Shape s;
-    if (!valid_modes(feature, prefix)) return 0;
+    if (!valid_modes(feature, prefix) || segment_chunks < 0) return 0;
     if (make_shape(B, H, T, d_k, d_v, chunk, dtype, &s, feature) != KATA_OK) return 0;
-    return plan_fwd(s, causal, feature, prefix).bytes;
+    return plan_fwd(s, causal, feature, prefix, segment_chunks).bytes;
 }
 
 static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* v, void* o,
                                       int B, int H, int T, int d_k, int d_v, int chunk,
                                       int causal, kata_dtype_t dtype, kata_feature_t feature,
-                                      kata_prefix_t prefix, const float* S0, const float* z0,
-                                      float* S_out, float* z_out, void* workspace,
-                                      size_t ws_bytes, void* stream, void* const* events) {
+                                      kata_prefix_t prefix, int seg_req, const float* S0,
+                                      const float* z0, float* S_out, float* z_out,
+                                      void* workspace, size_t ws_bytes, void* stream,
+                                      void* const* events) {
     Shape s;
-    if (!valid_modes(feature, prefix)) return KATA_EINVAL;
+    if (!valid_modes(feature, prefix) || seg_req < 0) return KATA_EINVAL;
     kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s, feature);
     if (st != KATA_OK) return st;
     if ((S0 == nullptr) != (z0 == nullptr)) return KATA_EINVAL;
@@ -168,7 +166,7 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
                           (const void*)S0, (const void*)z0, (const void*)S_out,
                           (const void*)z_out, (const void*)workspace})
         if (p && !aligned16(p)) return KATA_EINVAL;
-    const FwdPlan plan = plan_fwd(s, causal, feature, prefix);
+    const FwdPlan plan = plan_fwd(s, causal, feature, prefix, seg_req);
     if (!plan.ok) return KATA_EUNSUPPORTED;
     if (ws_bytes < plan.bytes || (plan.bytes && !workspace)) return KATA_EWORKSPACE;
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -315,18 +313,19 @@ kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, void
                                float* S_out, float* z_out, void* workspace, size_t ws_bytes,
                                void* stream) {
     return chunked_fwd_impl(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, KATA_FEATURE_PSD,
-                            KATA_PREFIX_SCAN, S0, z0, S_out, z_out, workspace, ws_bytes, stream,
+                            KATA_PREFIX_SCAN, 0, S0, z0, S_out, z_out, workspace, ws_bytes, stream,
                             nullptr);
 }
 
 kata_status_t kata_chunked_fwd_ex(const void* q, const void* k, const void* v, void* o, int B,
                                   int H, int T, int d_k, int d_v, int chunk, int causal,
                                   kata_dtype_t dtype, kata_feature_t feature,
-                                  kata_prefix_t prefix, const float* S0, const float* z0,
-                                  float* S_out, float* z_out, void* workspace, size_t ws_bytes,
-                                  void* stream) {
+                                  kata_prefix_t prefix, int segment_chunks, const float* S0,
+                                  const float* z0, float* S_out, float* z_out, void* workspace,
+                                  size_t ws_bytes, void* stream) {
     return chunked_fwd_impl(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, feature, prefix,
-                            S0, z0, S_out, z_out, workspace, ws_bytes, stream, nullptr);
+                            segment_chunks, S0, z0, S_out, z_out, workspace, ws_bytes, stream,
+                            nullptr);
 }
 
 kata_status_t kata_chunked_fwd_profiled(const void* q, const void* k, const void* v, void* o,
@@ -339,7 +338,7 @@ kata_status_t kata_chunked_fwd_profiled(const void* q, const void* k, const void
     for (int i = 0; i < 5; ++i)
         if (!events[i]) return KATA_EINVAL;
     return chunked_fwd_impl(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, KATA_FEATURE_PSD,
-                            KATA_PREFIX_SCAN, S0, z0, S_out, z_out, workspace, ws_bytes, stream,
+                            KATA_PREFIX_SCAN, 0, S0, z0, S_out, z_out, workspace, ws_bytes, stream,
                             events);
 }
 
@@ -410,13 +409,14 @@ struct DecayPlan {
     size_t z_off = 0, dec_off = 0, bytes = 0;
 };
 
-static bool decay_plan(const Shape& s, kata_feature_t f, kata_prefix_t prefix, DecayPlan* d) {
+static bool decay_plan(const Shape& s, kata_feature_t f, kata_prefix_t prefix, int seg_req,
+                       DecayPlan* d) {
     const size_t BH = (size_t)s.B * s.H;
     const bool aligned_rows = s.T % 4 == 0 || BH <= 1;
     if (aligned_rows &&
         ((f == KATA_FEATURE_PSD && (kata::mfma16_supported(s) || kata::mfma32_supported(s))) ||
          (f == KATA_FEATURE_IDENTITY && kata::first_decay_supported(s)))) {
-        d->fwd = plan_fwd(s, 1, f, prefix);
+        d->fwd = plan_fwd(s, 1, f, prefix, seg_req);
         if (!d->fwd.ok) return false;
         d->dec_off = d->fwd.bytes;
         d->bytes = d->fwd.bytes;
@@ -434,29 +434,29 @@ static bool decay_plan(const Shape& s, kata_feature_t f, kata_prefix_t prefix, D
 
 size_t kata_chunked_fwd_decay_ex_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                            kata_dtype_t dtype, kata_feature_t feature,
-                                           kata_prefix_t prefix) {
+                                           kata_prefix_t prefix, int segment_chunks) {
     Shape s;
     DecayPlan p;
-    if (!valid_modes(feature, prefix)) return 0;
+    if (!valid_modes(feature, prefix) || segment_chunks < 0) return 0;
     if (make_shape(B, H, T, d_k, d_v, chunk, dtype, &s, feature) != KATA_OK) return 0;
-    if (!decay_plan(s, feature, prefix, &p)) return 0;
+    if (!decay_plan(s, feature, prefix, segment_chunks, &p)) return 0;
     return p.bytes;
 }
 
 size_t kata_chunked_fwd_decay_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                         kata_dtype_t dtype, kata_prefix_t prefix) {
     return kata_chunked_fwd_decay_ex_workspace(B, H, T, d_k, d_v, chunk, dtype, KATA_FEATURE_PSD,
-                                               prefix);
+                                               prefix, 0);
 }
 
 kata_status_t kata_chunked_fwd_decay_ex(const void* q, const void* k, const void* v,
                                         const float* log_decay, void* o, int B, int H, int T,
                                         int d_k, int d_v, int chunk, kata_dtype_t dtype,
                                         kata_feature_t feature, kata_prefix_t prefix,
-                                        const float* S0, const float* z0, float* S_out,
-                                        float* z_out, void* workspace, size_t ws_bytes,
-                                        void* stream) {
-    if (!valid_modes(feature, prefix)) return KATA_EINVAL;
+                                        int segment_chunks, const float* S0, const float* z0,
+                                        float* S_out, float* z_out, void* workspace,
+                                        size_t ws_bytes, void* stream) {
+    if (!valid_modes(feature, prefix) || segment_chunks < 0) return KATA_EINVAL;
     Shape s;
     kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s, feature);
     if (st != KATA_OK) return st;
@@ -470,7 +470,7 @@ kata_status_t kata_chunked_fwd_decay_ex(const void* q, const void* k, const void
                           (const void*)S_out, (const void*)z_out, (const void*)workspace})
         if (p && !aligned16(p)) return KATA_EINVAL;
     DecayPlan plan;
-    if (!decay_plan(s, feature, prefix, &plan)) return KATA_EUNSUPPORTED;
+    if (!decay_plan(s, feature, prefix, segment_chunks, &plan)) return KATA_EUNSUPPORTED;
     if (ws_bytes < plan.bytes || (plan.bytes && !workspace)) return KATA_EWORKSPACE;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const size_t nS = (size_t)s.D * s.dv, nz = s.D;
@@ -548,7 +548,7 @@ kata_status_t kata_chunked_fwd_decay(const void* q, const void* k, const void* v
                                      float* S_out, float* z_out, void* workspace, size_t ws_bytes,
                                      void* stream) {
     return kata_chunked_fwd_decay_ex(q, k, v, log_decay, o, B, H, T, d_k, d_v, chunk, dtype,
-                                     KATA_FEATURE_PSD, prefix, S0, z0, S_out, z_out, workspace,
+                                     KATA_FEATURE_PSD, prefix, 0, S0, z0, S_out, z_out, workspace,
                                      ws_bytes, stream);
 }
 

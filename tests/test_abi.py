@@ -74,9 +74,9 @@ SCAN, SEQUENTIAL = 0, 1
 
 
 def fwd_ex(L, feature=IDENTITY, prefix=SCAN, B=1, H=1, T=64, dk=16, dv=64, C=64, causal=1,
-           dtype=BF16, q=FAKE, ws=FAKE, ws_bytes=1 << 40, o=FAKE, S0=None, z0=None):
+           dtype=BF16, q=FAKE, ws=FAKE, ws_bytes=1 << 40, o=FAKE, S0=None, z0=None, G=0):
     return L.kata_chunked_fwd_ex(q, FAKE, FAKE, o, B, H, T, dk, dv, C, causal, dtype, feature,
-                                 prefix, S0, z0, None, None, ws, ws_bytes, None)
+                                 prefix, G, S0, z0, None, None, ws, ws_bytes, None)
 
 
 def test_fwd_ex_rejects_before_launch(L):
@@ -94,6 +94,23 @@ def test_fwd_ex_rejects_before_launch(L):
     assert fwd_ex(L, S0=FAKE) == EINVAL
     assert fwd_ex(L, T=0, q=None, o=None, ws=None, ws_bytes=0) == OK           # empty: no launch
     assert fwd_ex(L, feature=PSD, prefix=SEQUENTIAL, B=0, q=None, o=None, ws=None, ws_bytes=0) == OK
+    assert fwd_ex(L, feature=PSD, G=-1) == EINVAL                                # segment length
+
+
+def test_segment_chunks_sets_the_plan(L):
+    """G chunks per segment is an explicit argument (0 = automatic): it sets
+    the number of segment records, so the workspace follows it."""
+    ws = L.kata_chunked_fwd_ex_workspace
+    rec16 = 9 * 4 * 256 + 256
+    auto = ws(1, 8, 131072, 16, 64, 64, BF16, 1, PSD, SCAN, 0)
+    assert auto == L.kata_chunked_fwd_workspace(1, 8, 131072, 16, 64, 64, BF16, 1)
+    assert auto == ws(1, 8, 131072, 16, 64, 64, BF16, 1, PSD, SCAN, 16)     # automatic G = 16
+    # G = 4: 512 segments per head, plus the initial and the final record
+    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, PSD, SCAN, 4) == (512 + 2) * 8 * rec16 * 4
+    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, PSD, SCAN, -1) == 0
+    wsx = L.kata_chunked_fwd_decay_ex_workspace
+    assert wsx(1, 8, 131072, 16, 64, 64, BF16, PSD, SCAN, 4) > wsx(1, 8, 131072, 16, 64, 64, BF16, PSD, SCAN, 0)
+    assert wsx(1, 8, 131072, 16, 64, 64, BF16, PSD, SCAN, -2) == 0
 
 
 def test_feature_dim_and_ex_workspace(L):
@@ -102,18 +119,18 @@ def test_feature_dim_and_ex_workspace(L):
     assert L.kata_feature_dim(16, 7) == -1 and L.kata_feature_dim(-1, PSD) == -1
     ws = L.kata_chunked_fwd_ex_workspace
     # PSD with the scan: the same plan as kata_chunked_fwd
-    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, PSD, SCAN) == \
+    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, PSD, SCAN, 0) == \
         L.kata_chunked_fwd_workspace(1, 8, 131072, 16, 64, 64, BF16, 1)
     # sequential: one record per head for the segment, the initial and the final state
     rec16 = 9 * 4 * 256 + 256            # d_k = 16, d_v = 64: nine feature tiles + Gram tile
-    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, PSD, SEQUENTIAL) == 3 * 8 * rec16 * 4
+    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, PSD, SEQUENTIAL, 0) == 3 * 8 * rec16 * 4
     rec1 = 1 * 5 * 256                   # identity, d_k = 16, d_v = 64: four value tiles + z
-    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, IDENTITY, SEQUENTIAL) == 3 * 8 * rec1 * 4
-    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, IDENTITY, SCAN) > 3 * 8 * rec1 * 4
+    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, IDENTITY, SEQUENTIAL, 0) == 3 * 8 * rec1 * 4
+    assert ws(1, 8, 131072, 16, 64, 64, BF16, 1, IDENTITY, SCAN, 0) > 3 * 8 * rec1 * 4
     # identity on the VALU path: one S record (d_k x d_v) and one z record per chunk
-    assert ws(1, 1, 64, 16, 64, 64, F32, 1, IDENTITY, SCAN) == 16 * 64 * 4 + 256
-    assert ws(1, 1, 64, 16, 64, 64, F32, 1, IDENTITY, SEQUENTIAL) == 0
-    assert ws(1, 1, 64, 16, 64, 64, BF16, 1, 9, SCAN) == 0
+    assert ws(1, 1, 64, 16, 64, 64, F32, 1, IDENTITY, SCAN, 0) == 16 * 64 * 4 + 256
+    assert ws(1, 1, 64, 16, 64, 64, F32, 1, IDENTITY, SEQUENTIAL, 0) == 0
+    assert ws(1, 1, 64, 16, 64, 64, BF16, 1, 9, SCAN, 0) == 0
 
 
 def fwd_decay(L, B=1, H=2, T=64, dk=16, dv=64, C=64, dtype=BF16, prefix=SCAN, g=FAKE, q=FAKE,
@@ -151,7 +168,7 @@ def test_decay_rejects_before_launch(L):
     assert ws(1, 8, 4096, 16, 64, 64, F32, SCAN) == 8 * 64 * (136 * 64 * 4 + 136 * 4 + 4)
     dex = L.kata_chunked_fwd_decay_ex
     dex_args = lambda f, pf, wsb, dt=BF16, T=64, C=64: (FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, T, 16, 64, C,
-                                                         dt, f, pf, None, None, None, None, FAKE, wsb,
+                                                         dt, f, pf, 0, None, None, None, None, FAKE, wsb,
                                                          None)
     # identity: matrix cores for bf16 with chunk 32 or 64, else VALU with the scan only
     assert dex(*dex_args(IDENTITY, SEQUENTIAL, 1 << 40, dt=F32)) == EUNSUPPORTED
@@ -161,11 +178,11 @@ def test_decay_rejects_before_launch(L):
     assert dex(*dex_args(IDENTITY, SCAN, 16, dt=F32)) == EWORKSPACE
     assert dex(*dex_args(5, SCAN, 1 << 40)) == EINVAL
     wsx = L.kata_chunked_fwd_decay_ex_workspace
-    assert wsx(1, 8, 131072, 16, 64, 64, BF16, PSD, SCAN) == ws(1, 8, 131072, 16, 64, 64, BF16, SCAN)
-    assert wsx(1, 2, 64, 16, 64, 64, F32, IDENTITY, SCAN) == 2 * 16 * 64 * 4 + 256 + 256
+    assert wsx(1, 8, 131072, 16, 64, 64, BF16, PSD, SCAN, 0) == ws(1, 8, 131072, 16, 64, 64, BF16, SCAN)
+    assert wsx(1, 2, 64, 16, 64, 64, F32, IDENTITY, SCAN, 0) == 2 * 16 * 64 * 4 + 256 + 256
     rec1 = 1 * 5 * 256                   # identity, d_k = 16, d_v = 64: four value tiles + z
-    assert wsx(1, 8, 131072, 16, 64, 64, BF16, IDENTITY, SEQUENTIAL) == 3 * 8 * rec1 * 4
-    assert wsx(1, 8, 131072, 16, 64, 64, BF16, IDENTITY, SCAN) > 3 * 8 * rec1 * 4
+    assert wsx(1, 8, 131072, 16, 64, 64, BF16, IDENTITY, SEQUENTIAL, 0) == 3 * 8 * rec1 * 4
+    assert wsx(1, 8, 131072, 16, 64, 64, BF16, IDENTITY, SCAN, 0) > 3 * 8 * rec1 * 4
     dec = L.kata_decode_step_decay
     assert dec(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 16, 64, BF16, None) == EINVAL
     assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 12, 64, BF16, None) == EUNSUPPORTED

@@ -37,7 +37,8 @@ def kata():
     return k
 
 
-def run(kata, q, k, v, g, C, prefix, S0=None, z0=None, state=False, dtype="bf16", feature="psd"):
+def run(kata, q, k, v, g, C, prefix, S0=None, z0=None, state=False, dtype="bf16", feature="psd",
+        G=0):
     """kata_chunked_fwd_decay with outputs and workspace pre-filled with NaN."""
     import torch
     qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
@@ -50,11 +51,12 @@ def run(kata, q, k, v, g, C, prefix, S0=None, z0=None, state=False, dtype="bf16"
     S_out = torch.full((B, H, D, dv), nan, device="cuda") if state else None
     z_out = torch.full((B, H, D), nan, device="cuda") if state else None
     nbytes = kata.chunked_fwd_decay_workspace(B, H, T, dk, dv, C, 1 if dtype == "bf16" else 0,
-                                              prefix, feature)
+                                              prefix, feature, segment_chunks=G)
     ws = torch.full((max(nbytes, 4) // 4,), nan, device="cuda")
     kata.chunked_fwd_decay_into(qd, kd, vd, gd, o, C, ws,
                                 S0=None if S0 is None else dev(S0), z0=None if z0 is None else dev(z0),
-                                S_out=S_out, z_out=z_out, prefix=prefix, feature=feature)
+                                S_out=S_out, z_out=z_out, prefix=prefix, feature=feature,
+                                segment_chunks=G)
     torch.cuda.synchronize()
     if state:
         return host(o), host(S_out), host(z_out)
@@ -199,15 +201,14 @@ def test_decay_fwd32(kata, prefix, dv, C, gmin):
 
 @pytest.mark.parametrize("G", [2, 3])
 @pytest.mark.parametrize("C", [64, 128])
-def test_decay_fwd32_segments(kata, monkeypatch, G, C):
+def test_decay_fwd32_segments(kata, G, C):
     """Segments of several chunks: the output kernel carries the decaying state
     across chunks and the scan combines segment totals with their decays."""
     B, H, T = 1, 3, 1100
     q, k, v = gen.gaussian_qkv(B, H, T, 32, 64, seed=1910 + G + C, dtype="bf16")
     g = gen.log_decays(B, H, T, seed=1911 + G, gmin=-0.05)
-    monkeypatch.setenv("KATA_SEGMENT_CHUNKS", str(G))
     say(f"decay d32 segments G={G} C={C}")
-    o, S, z = run(kata, q, k, v, g, C, "scan", state=True)
+    o, S, z = run(kata, q, k, v, g, C, "scan", state=True, G=G)
     assert row_rel_err(o, O.decay_brute_force(q, k, v, g)) <= TOL
     _, S_ref, z_ref = O.decay_recurrent(q, k, v, g)
     assert state_rel_err(S, S_ref) <= PSD_STATE_TOL and state_rel_err(z, z_ref) <= PSD_STATE_TOL

@@ -31,10 +31,11 @@ def kata():
     return k
 
 
-def run_fwd(kata, q, k, v, dtype, C, causal=True, S0=None, z0=None, state=False):
+def run_fwd(kata, q, k, v, dtype, C, causal=True, S0=None, z0=None, state=False, G=0):
     """Forward through the raw entry point with every output and the workspace
     pre-filled with NaN: an element the library fails to write, or scratch it
-    reads before writing, cannot pass for a correct value."""
+    reads before writing, cannot pass for a correct value. G: chunks per
+    segment (0 = automatic; else through kata_chunked_fwd_ex)."""
     import torch
     qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
     B, H, T, dk = qd.shape
@@ -45,11 +46,11 @@ def run_fwd(kata, q, k, v, dtype, C, causal=True, S0=None, z0=None, state=False)
     S_out = torch.full((B, H, D, dv), nan, device="cuda") if state else None
     z_out = torch.full((B, H, D), nan, device="cuda") if state else None
     code = 1 if dtype == "bf16" else 0
-    nbytes = kata.chunked_fwd_workspace(B, H, T, dk, dv, C, code, causal)
+    nbytes = kata.chunked_fwd_workspace(B, H, T, dk, dv, C, code, causal, segment_chunks=G)
     ws = torch.full((max(nbytes, 4) // 4,), nan, device="cuda")
     kata.chunked_fwd_into(qd, kd, vd, o, C, causal, ws,
                           S0=None if S0 is None else dev(S0), z0=None if z0 is None else dev(z0),
-                          S_out=S_out, z_out=z_out)
+                          S_out=S_out, z_out=z_out, segment_chunks=G)
     torch.cuda.synchronize()
     if state:
         return host(o), host(S_out), host(z_out)
@@ -74,19 +75,18 @@ def test_fwd_small_full(kata, dtype, dk, dv, C):
 
 @pytest.mark.parametrize("G", [1, 2, 3, 5, 16, 40])
 @pytest.mark.parametrize("dk,C,T", [(16, 64, 1000), (16, 32, 999), (32, 128, 1000), (32, 64, 999)])
-def test_segment_lengths(kata, monkeypatch, G, dk, C, T):
+def test_segment_lengths(kata, G, dk, C, T):
     """Chunks per segment (running state carried across chunks, ragged last
     segment, one segment per head) must not change the result beyond rounding."""
-    monkeypatch.setenv("KATA_SEGMENT_CHUNKS", str(G))
     q, k, v = gen.gaussian_qkv(2, 3, T, dk, 64, seed=500 + G + dk, dtype="bf16")
     say(f"segments G={G} dk={dk} C={C} T={T}")
-    o, S, z = run_fwd(kata, q, k, v, "bf16", C, state=True)
+    o, S, z = run_fwd(kata, q, k, v, "bf16", C, state=True, G=G)
     assert row_rel_err(o, O.brute_force(q, k, v)) <= TOL["bf16"]
     S_ref, z_ref = O.state_from_tokens(k, v)
     assert state_rel_err(S, S_ref) <= STATE_TOL["bf16"]
     assert state_rel_err(z, z_ref) <= STATE_TOL["bf16"]
     S0, z0 = (a.astype(np.float32) for a in O.state_from_tokens(k[:, :, :77], v[:, :, :77]))
-    o2 = run_fwd(kata, q, k, v, "bf16", C, S0=S0, z0=z0)
+    o2 = run_fwd(kata, q, k, v, "bf16", C, S0=S0, z0=z0, G=G)
     ref2 = O.brute_force(q, k, v, S0=S0.astype(np.float64), z0=z0.astype(np.float64))
     assert row_rel_err(o2, ref2) <= TOL["bf16"]
 
@@ -230,21 +230,19 @@ def test_noncausal_few_keys(kata, dk, C, T):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,C,G", [(16, 64, 0), (32, 128, 0), (16, 16, 0), (16, 64, 2), (16, 32, 3),
                                     (32, 64, 2), (32, 128, 3)])
-def test_bitwise_causality(kata, monkeypatch, dtype, dk, C, G):
+def test_bitwise_causality(kata, dtype, dk, C, G):
     """Perturbing token j leaves every output before j bit-identical."""
-    if G:
-        monkeypatch.setenv("KATA_SEGMENT_CHUNKS", str(G))
     T = 4 * C + 37
     q, k, v = gen.gaussian_qkv(1, 2, T, dk, 64, seed=300 + C, dtype=dtype)
-    say(f"causality dtype={dtype} dk={dk} C={C}")
-    base = run_fwd(kata, q, k, v, dtype, C)
+    say(f"causality dtype={dtype} dk={dk} C={C} G={G}")
+    base = run_fwd(kata, q, k, v, dtype, C, G=G)
     r = np.random.Generator(np.random.PCG64(5))
     for j in [C - 1, C, C + 1, 2 * C, 3 * C - 1, int(r.integers(1, T - 1))]:
         q2, k2, v2 = q.copy(), k.copy(), v.copy()
         q2[:, :, j] = gen.round_to(-q[:, :, j] + 0.25, dtype)
         k2[:, :, j] = gen.round_to(k[:, :, j][..., ::-1] + 0.5, dtype)
         v2[:, :, j] = gen.round_to(v[:, :, j] * 3.0 + 1.0, dtype)
-        got = run_fwd(kata, q2, k2, v2, dtype, C)
+        got = run_fwd(kata, q2, k2, v2, dtype, C, G=G)
         assert np.array_equal(got[:, :, :j], base[:, :, :j]), f"output before {j} changed"
         assert not np.array_equal(got[:, :, j], base[:, :, j])
 
@@ -366,3 +364,46 @@ def test_determinism(kata, dtype, dk, C):
 def _inputs(name):
     from tests.gpu_util import workload_inputs
     return workload_inputs(name)
+
+
+@pytest.mark.parametrize("dk,C,S0", [(16, 64, False), (32, 128, True), (16, 16, False)])
+def test_profiled_entry_point(kata, dk, C, S0):
+    """kata_chunked_fwd_profiled does the same work as kata_chunked_fwd and
+    records its five phase events: outputs and states bit-identical to the
+    plain call, within the bar of the oracle, and the events in order."""
+    import torch
+    B, H, T, dv = 1, 3, 900, 64
+    q, k, v = gen.gaussian_qkv(B, H, T, dk, dv, seed=9700 + dk + C, dtype="bf16")
+    D = dk * (dk + 1) // 2
+    init = None
+    if S0:
+        init = tuple(dev(a.astype(np.float32)) for a in
+                     O.state_from_tokens(*gen.gaussian_qkv(B, H, 5, dk, dv, seed=9701, dtype="bf16")[1:]))
+    qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    nbytes = kata.chunked_fwd_workspace(B, H, T, dk, dv, C, 1, True)
+    outs = []
+    for events in (None, [torch.cuda.Event(enable_timing=True) for _ in range(5)]):
+        o = torch.full_like(vd, float("nan"))
+        S_out = torch.full((B, H, D, dv), float("nan"), device="cuda")
+        z_out = torch.full((B, H, D), float("nan"), device="cuda")
+        ws = torch.full((max(nbytes, 4) // 4,), float("nan"), device="cuda")
+        say(f"profiled dk={dk} C={C} S0={S0} events={events is not None}")
+        kata.chunked_fwd_into(qd, kd, vd, o, C, True, ws, S0=None if init is None else init[0],
+                              z0=None if init is None else init[1], S_out=S_out, z_out=z_out,
+                              events=events)
+        torch.cuda.synchronize()
+        outs.append((host(o), host(S_out), host(z_out)))
+        if events is not None:
+            times = [events[0].elapsed_time(e) for e in events[1:]]
+            assert all(t >= 0 for t in times) and times == sorted(times)
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    o, S, z = outs[1]
+    S0h = z0h = None
+    if init is not None:
+        S0h, z0h = (host(t) for t in init)
+    assert row_rel_err(o, O.brute_force(q, k, v, S0=S0h, z0=z0h)) <= TOL["bf16"]
+    S_ref, z_ref = O.state_from_tokens(k, v)
+    if S0h is not None:
+        S_ref, z_ref = S_ref + S0h, z_ref + z0h
+    assert state_rel_err(S, S_ref) <= 2e-2 and state_rel_err(z, z_ref) <= 2e-2
