@@ -40,8 +40,9 @@
  *    [cC, min(cC+C, T))); B, H >= 0. Empty inputs launch nothing except the
  *    state export. Inputs must be finite.
  *  - Inputs and outputs must not overlap, except decode's S and z, which are
- *    updated in place. The library keeps no global state and is thread-safe;
- *    calls that share a workspace must be ordered on one stream.
+ *    updated in place. The library keeps no global state (apart from the static
+ *    scratch of kata_chunked_fwd_noalloc) and is thread-safe; calls that share a
+ *    workspace must be ordered on one stream.
  */
 #ifndef KATA_H
 #define KATA_H
@@ -57,7 +58,8 @@ typedef enum {
     KATA_EINVAL = 1,
     KATA_EUNSUPPORTED = 2,
     KATA_EWORKSPACE = 3,
-    KATA_EHIP = 4
+    KATA_EHIP = 4,
+    KATA_ESCRATCH = 5     /* the problem needs more than the static scratch (noalloc call) */
 } kata_status_t;
 
 typedef enum { KATA_F32 = 0, KATA_BF16 = 1 } kata_dtype_t;
@@ -283,6 +285,31 @@ kata_status_t kata_flash_fwd(const void* q, const void* k, const void* v, void* 
 kata_status_t kata_decode_step(const void* q, const void* k, const void* v,
                                float* S, float* z, void* o,
                                int N, int d_k, int d_v, kata_dtype_t dtype, void* stream);
+
+/* Bytes of the library's static device scratch (per GPU) used by
+ * kata_chunked_fwd_noalloc. */
+#define KATA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* kata_chunked_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as kata_chunked_fwd, without the
+ * workspace: the scratch (segment records, initial and final state records)
+ * lives in a static device array of KATA_NOALLOC_SCRATCH_BYTES that each GPU
+ * the library runs on holds until the process ends (its address is looked up
+ * once per device, on the first call made with that device current). The
+ * call allocates nothing and calls no allocating routine.
+ *   Problems whose kata_chunked_fwd_workspace exceeds
+ *   KATA_NOALLOC_SCRATCH_BYTES return KATA_ESCRATCH, with nothing launched
+ *   (e.g. B1 H8 T131072 d_k16 d_v64 C64 needs 39.4 MB and fits).
+ *   Every call on one GPU shares that GPU's array, which keeps the last call's
+ *   contents (nothing in it has to start at zero). Calls that overlap on one
+ *   GPU - on different streams, or from threads without ordering - race;
+ *   order them on one stream. A failed device-symbol lookup returns KATA_EHIP. */
+kata_status_t kata_chunked_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                                       int B, int H, int T, int d_k, int d_v, int chunk,
+                                       int causal, kata_dtype_t dtype,
+                                       const float* S0, const float* z0,
+                                       float* S_out, float* z_out, void* stream);
 
 #ifdef __cplusplus
 }

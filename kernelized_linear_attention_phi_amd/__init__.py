@@ -7,13 +7,15 @@
     o2 = kata.flash_fwd(q, k, v)                            # quadratic form (bf16)
     o3 = kata.chunked_fwd(q, k, v, prefix="sequential")     # chunk-by-chunk prefix
     o4 = kata.chunked_fwd(q, k, v, feature="identity")      # first-order feature
-    o5 = kata.chunked_fwd_decay(q, k, v, log_decay)         # decay-gated (bf16, d_k 16)
+    o5 = kata.chunked_fwd_decay(q, k, v, log_decay)         # decay-gated
+    kata.chunked_fwd_noalloc_into(q, k, v, o, 64, True)     # no workspace, allocates nothing
 
 The shared library is loaded on first use; calls raise if it is missing.
 """
 from ._binding import (KataError, chunked_fwd, chunked_fwd_into, chunked_fwd_workspace,  # noqa: F401
                        chunked_fwd_decay, chunked_fwd_decay_into, chunked_fwd_decay_workspace,
                        decode_step, decode_step_decay, feature_dim, flash_fwd, lib, phi_dim,
-                       scan_states, scan_states_into, LIB_PATH)
+                       scan_states, scan_states_into, chunked_fwd_noalloc_into,
+                       NOALLOC_SCRATCH_BYTES, LIB_PATH)
 
-__version__ = "0.1.0"
+__version__ = "0.2.0"

@@ -14,12 +14,14 @@ import torch
 __all__ = ["KataError", "lib", "chunked_fwd", "chunked_fwd_into", "chunked_fwd_workspace",
            "scan_states", "flash_fwd", "decode_step", "phi_dim", "feature_dim",
            "chunked_fwd_decay", "chunked_fwd_decay_into", "chunked_fwd_decay_workspace",
-           "decode_step_decay", "LIB_PATH"]
+           "decode_step_decay", "chunked_fwd_noalloc_into", "NOALLOC_SCRATCH_BYTES", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkata.so")
 
 F32, BF16 = 0, 1
-_STATUS = {0: "KATA_OK", 1: "KATA_EINVAL", 2: "KATA_EUNSUPPORTED", 3: "KATA_EWORKSPACE", 4: "KATA_EHIP"}
+_STATUS = {0: "KATA_OK", 1: "KATA_EINVAL", 2: "KATA_EUNSUPPORTED", 3: "KATA_EWORKSPACE", 4: "KATA_EHIP",
+           5: "KATA_ESCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20     # KATA_NOALLOC_SCRATCH_BYTES
 
 
 class KataError(RuntimeError):
@@ -80,6 +82,9 @@ def lib() -> ctypes.CDLL:
         L.kata_flash_fwd.restype = i
         L.kata_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
         L.kata_decode_step.restype = i
+        L.kata_chunked_fwd_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                               vp, vp, vp, vp, vp]
+        L.kata_chunked_fwd_noalloc.restype = i
         _lib = L
     return _lib
 
@@ -208,6 +213,22 @@ def chunked_fwd_into(q, k, v, o, chunk, causal, workspace, S0=None, z0=None, S_o
         arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
         st = lib().kata_chunked_fwd_profiled(*args, arr, len(events))
     _raise(st, "kata_chunked_fwd")
+
+
+def chunked_fwd_noalloc_into(q, k, v, o, chunk, causal, S0=None, z0=None, S_out=None, z_out=None):
+    """kata_chunked_fwd_noalloc: kata_chunked_fwd with the library's static
+    device scratch in place of a workspace (every buffer preallocated by the
+    caller; the call allocates nothing)."""
+    _check_qkv(q, k, v, o)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    D = phi_dim(dk)
+    _check_state(S0, z0, (B, H), D, dv, "initial state")
+    _check_state(S_out, z_out, (B, H), D, dv, "final state")
+    st = lib().kata_chunked_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, T, dk, dv, chunk,
+                                        int(bool(causal)), _dtype_code(q), _ptr(S0), _ptr(z0),
+                                        _ptr(S_out), _ptr(z_out), _stream())
+    _raise(st, "kata_chunked_fwd_noalloc")
 
 
 def chunked_fwd(q, k, v, chunk=64, causal=True, initial_state=None, return_state=False,

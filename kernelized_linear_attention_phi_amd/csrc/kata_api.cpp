@@ -5,6 +5,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "../../include/kata.h"
 #include "kata_internal.h"
@@ -112,6 +114,7 @@ const char* kata_status_string(kata_status_t st) {
         case KATA_EUNSUPPORTED: return "unsupported shape";
         case KATA_EWORKSPACE: return "workspace too small";
         case KATA_EHIP: return "HIP launch error";
+        case KATA_ESCRATCH: return "problem needs more than the static scratch";
     }
     return "unknown status";
 }
@@ -583,3 +586,56 @@ kata_status_t kata_decode_step(const void* q, const void* k, const void* v, floa
 }
 
 }  // extern "C"
+
+// ---- allocation-free forward ------------------------------------------------
+// A file-scope device array stands in for the workspace. In host code its name
+// is only a host-side handle: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, looked up once per device with that device current, and
+// only that address is ever passed to a kernel.
+
+namespace {
+
+static __device__ __align__(256) char scratch[KATA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's scratch, or nullptr on failure.
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void* addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+        g_scratch_ptr[dev].store(addr, std::memory_order_release);
+        p = addr;
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" kata_status_t kata_chunked_fwd_noalloc(const void* q, const void* k, const void* v,
+                                                  void* o, int B, int H, int T, int d_k, int d_v,
+                                                  int chunk, int causal, kata_dtype_t dtype,
+                                                  const float* S0, const float* z0,
+                                                  float* S_out, float* z_out, void* stream) {
+    Shape s;
+    kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s);
+    if (st != KATA_OK) return st;
+    const size_t need = plan_fwd(s, causal).bytes;
+    if (need > KATA_NOALLOC_SCRATCH_BYTES) return KATA_ESCRATCH;
+    void* ws = nullptr;
+    if (need > 0) {
+        ws = scratch_for_current_device();
+        if (!ws) return KATA_EHIP;
+    }
+    return chunked_fwd_impl(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, KATA_FEATURE_PSD,
+                            KATA_PREFIX_SCAN, 0, S0, z0, S_out, z_out, ws,
+                            KATA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+}
