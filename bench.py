@@ -54,37 +54,45 @@ def alg_bytes_per_token_head(dk, dv, elem=2):
     return elem * (2 * dk + 2 * dv)
 
 
-def time_forward(kata, torch, w, q, k, v, steps, warmup):
+def time_forward(kata, torch, w, q, k, v, steps, warmup, sets=None):
     """Times `steps` forwards (state export included) with events on the stream
     the library launches on. Returns (ms per step, wall ms per step, per-phase
     ms): the per-step time comes from `steps` back-to-back forwards bracketed
     by one event pair; the phases from a second pass of `steps` forwards with
     events recorded between the phases (those events are instrumentation, so
-    that pass is not the headline)."""
+    that pass is not the headline). sets: optional list of (q, k, v, o) input
+    and output sets that step i rotates through (set i % len(sets)) instead of
+    the one (q, k, v)."""
     B, H, T = w.B, w.H, w.T
     D = w.dk * (w.dk + 1) // 2
-    o = torch.empty_like(v)
+    if sets is None:
+        sets = [(q, k, v, torch.empty_like(v))]
     S_out = torch.empty((B, H, D, w.dv), dtype=torch.float32, device="cuda")
     z_out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
     nbytes = kata.chunked_fwd_workspace(B, H, T, w.dk, w.dv, w.chunk, 1, True)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
-    for _ in range(warmup):
-        kata.chunked_fwd_into(q, k, v, o, w.chunk, True, ws, S_out=S_out, z_out=z_out)
+
+    def fwd(i, events=None):
+        qi, ki, vi, oi = sets[i % len(sets)]
+        kata.chunked_fwd_into(qi, ki, vi, oi, w.chunk, True, ws, S_out=S_out, z_out=z_out,
+                              events=events)
+
+    for i in range(warmup):
+        fwd(i)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(steps):
-        kata.chunked_fwd_into(q, k, v, o, w.chunk, True, ws, S_out=S_out, z_out=z_out)
+    for i in range(steps):
+        fwd(i)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     total = e0.elapsed_time(e1) / steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     for i in range(steps):
-        kata.chunked_fwd_into(q, k, v, o, w.chunk, True, ws, S_out=S_out, z_out=z_out,
-                              events=evs[i])
+        fwd(i, evs[i])
     torch.cuda.synchronize()
     phases = {name: sum(evs[i][a].elapsed_time(evs[i][a + 1]) for i in range(steps)) / steps
               for a, name in enumerate(["states", "scan", "output", "export"])}
@@ -128,9 +136,11 @@ def quadratic_vs_chunked(kata, torch, gen, name, steps, warmup):
 
 
 def decode_bench(kata, torch, steps=1024, n_seq=512, heads=4, dk=16, dv=64, reps=3, gated=False):
-    """1024 decode steps on n_seq x heads rows with fp32 state, replayed from a
-    HIP graph; returns ms per step and algorithmic GB/s. gated: the decay-gated
-    step, with per-row log-decays in [-0.05, 0]."""
+    """`steps` decode steps on n_seq x heads rows with fp32 state, replayed from
+    a HIP graph; returns ms per step and algorithmic GB/s. gated: the
+    decay-gated step, with per-row log-decays in [-0.05, 0]. With 512 x 4 rows
+    the state (72.4 MB) fits the 256 MB memory-side cache; with 2048 x 4 rows
+    (290 MB) it does not, so every step streams it from DRAM."""
     from kernelized_linear_attention_phi_amd import inputs as gen
     N = n_seq * heads
     D = dk * (dk + 1) // 2
@@ -231,10 +241,12 @@ def decay_gate(kata, torch, gen, steps, warmup):
 
 
 def scan_vs_sequential(kata, torch, gen, names, steps, warmup):
-    """The inter-chunk prefix by the associative scan (segments in parallel) and
-    by the sequential walk (one workgroup per head, depth N_C), for the PSD lift
-    and for the first-order identity feature (orthant inputs), on the same
-    shapes: ms per forward, tokens/s and the scan's speedup."""
+    """The inter-chunk prefix by the associative scan (segments in parallel;
+    blocked, the default, and the log-depth tree) and by the sequential walk
+    (one workgroup per head, depth N_C), for the PSD lift and for the
+    first-order identity feature (orthant inputs), on the same shapes: ms per
+    forward, tokens/s, the prefix depth (dependent state combines) and the
+    scan's speedup."""
     out = {}
     speedups = []
     to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
@@ -244,17 +256,20 @@ def scan_vs_sequential(kata, torch, gen, names, steps, warmup):
             q, k, v = (to(a) for a in draw(w.B, w.H, w.T, w.dk, w.dv, w.seed, "bf16"))
             o = torch.empty_like(v)
             row = {}
-            for prefix in ("scan", "sequential"):
+            for prefix in ("scan", "tree", "sequential"):
                 nbytes = kata.chunked_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1, True,
                                                     feature, prefix)
                 ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
-                n = steps if prefix == "scan" else max(1, min(steps, 3))
+                n = steps if prefix != "sequential" else max(1, min(steps, 3))
                 ms = time_calls(torch, lambda: kata.chunked_fwd_into(
                     q, k, v, o, w.chunk, True, ws, feature=feature, prefix=prefix), n,
                     min(warmup, 1) if prefix == "sequential" else warmup)
-                row[prefix] = {"ms": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3)}
+                row[prefix] = {"ms": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+                               "depth": kata.prefix_depth(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1,
+                                                          feature, prefix)}
                 del ws
             row["scan_speedup"] = row["sequential"]["ms"] / row["scan"]["ms"]
+            row["tree_speedup"] = row["sequential"]["ms"] / row["tree"]["ms"]
             speedups.append(row["scan_speedup"])
             out[f"{name}/{feature}"] = row
             del q, k, v, o
@@ -263,11 +278,11 @@ def scan_vs_sequential(kata, torch, gen, names, steps, warmup):
 
 
 def scan_states_bench(kata, torch, gen, names, steps, warmup):
-    """kata_scan_states (per-chunk exclusive prefix states, fp32 chunk states
-    then an in-place scan over one record per chunk) on the fwd131k and fwd32k
-    shapes: ms per call and GB/s over its minimal traffic (k, v read once; every
-    prefix S, z and the final state written once). The scan alone at one record
-    per chunk moves 2 x 4 D (d_v + 1) bytes per chunk and head (read and write)."""
+    """kata_scan_states (per-chunk exclusive prefix states: segment states, the
+    scan over segment records, then a walk of each segment writing every
+    chunk's packed prefix) on the fwd131k and fwd32k shapes: ms per call and
+    GB/s over its minimal traffic (k, v read once; every prefix S, z and the
+    final state written once)."""
     out = {}
     to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
     for name in names:
@@ -280,14 +295,16 @@ def scan_states_bench(kata, torch, gen, names, steps, warmup):
         zp = torch.empty((w.B, w.H, NC, D), device="cuda")
         ST = torch.empty((w.B, w.H, D, w.dv), device="cuda")
         zT = torch.empty((w.B, w.H, D), device="cuda")
-        ms = time_calls(torch, lambda: kata.scan_states_into(k, v, w.chunk, Sp, zp, ST, zT),
-                        steps, warmup)
+        nws = kata.lib().kata_scan_states_workspace(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+        ms = time_calls(torch, lambda: kata.scan_states_into(k, v, w.chunk, Sp, zp, ST, zT,
+                                                             workspace=ws), steps, warmup)
         nbytes = BH * (w.T * 2 * (w.dk + w.dv) + (NC + 1) * 4 * D * (w.dv + 1))
         scan_bytes = BH * NC * 2 * 4 * D * (w.dv + 1)
         out[name] = {"ms": ms, "alg_bytes": nbytes, "alg_GBps": nbytes / (ms * 1e-3) / 1e9,
                      "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "scan_alone_bytes": scan_bytes}
-        del k, v, Sp, zp, ST, zT
+        del k, v, Sp, zp, ST, zT, ws
     return out
 
 
@@ -437,6 +454,25 @@ def main():
     abytes = alg_bytes_per_token_head(w.dk, w.dv) * th
     out_ms = phases["output"]
     achieved = abytes / (out_ms * 1e-3) / 1e9
+    cold = None
+    if not args.quick:
+        # three input/output sets (3 x 335 MB) rotated through the timed steps:
+        # each step's inputs were last touched two steps earlier, beyond the
+        # 256 MB memory-side cache
+        sets = [dev_in + (torch.empty_like(dev_in[2]),)]
+        for r in (1, 2):
+            qh, kh, vh = gen.gaussian_qkv(w.B, w.H, w.T, w.dk, w.dv, w.seed + 1000 * r, w.dtype)
+            to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+            sets.append((to(qh), to(kh), to(vh), torch.empty_like(dev_in[2])))
+            del qh, kh, vh
+        ms_c, _, ph_c = time_forward(kata, torch, w, None, None, None, args.steps, args.warmup,
+                                     sets=sets)
+        cold = {"value_cold": tok / (ms_c * 1e-3), "ms_per_step": ms_c, "phase_ms": ph_c,
+                "output_kernel_GBps": abytes / (ph_c["output"] * 1e-3) / 1e9,
+                "definition": "the same forward with 3 input/output sets (335 MB each) rotated "
+                              "through the timed steps, so no step's inputs are resident in "
+                              "the 256 MB memory-side cache"}
+        del sets
     traffic = None
     if w.name == "fwd131k" and os.path.exists(COUNTERS_FILE):
         c = json.load(open(COUNTERS_FILE))
@@ -453,11 +489,16 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "output phase (fused intra+inter forward)",
                      "alg_bytes_per_launch": abytes, "avg_launch_ms": out_ms},
+        "value_cold": None if cold is None else cold["value_cold"],
         "parts": {w.name: {"phase_ms": phases, "wall_ms_per_step": wall_ms,
                               "mfma_util_alg": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                               "alg_tflops": flops / (ms * 1e-3) / 1e12,
                               "hbm_frac_alg_whole_step": abytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}},
     }
+    if cold is not None:
+        result["parts"][w.name]["cold"] = cold
+        result["roofline"]["achieved_cold"] = cold["output_kernel_GBps"]
+        result["roofline"]["frac_cold"] = cold["output_kernel_GBps"] / PEAK_HBM_GBS
     if not args.quick:
         del dev_in
         w3, host3, dev3 = load("fwd32k")
@@ -483,10 +524,26 @@ def main():
         dms, dgbs, dbytes = decode_bench(kata, torch)
         result["parts"]["decode"] = {"ms_per_step": dms, "alg_GBps": dgbs,
                                      "hbm_frac": dgbs / PEAK_HBM_GBS, "bytes_per_step": dbytes,
-                                     "rows": 2048, "steps": 1024, "hip_graph": True}
+                                     "rows": 2048, "steps": 1024, "hip_graph": True,
+                                     "state_MB": 2048 * 4 * 136 * 65 / 1e6,
+                                     "note": "state fits the 256 MB memory-side cache: cache-assisted"}
+        cold = {}
+        for n_seq, steps in ((2048, 128), (8192, 48)):
+            dms, dgbs, dbytes = decode_bench(kata, torch, steps=steps, n_seq=n_seq, reps=2)
+            rows = 4 * n_seq
+            cold[f"rows{rows}"] = {
+                "ms_per_step": dms, "alg_GBps": dgbs, "hbm_frac": dgbs / PEAK_HBM_GBS,
+                "bytes_per_step": dbytes, "rows": rows, "steps": steps, "hip_graph": True,
+                "state_MB": rows * 4 * 136 * 65 / 1e6}
+        cold["note"] = ("states of 290 MB and 1.16 GB, beyond the 256 MB memory-side cache "
+                        "(the larger one four times over), swept once per step")
+        result["parts"]["decode_cold"] = cold
         peaks = box_peaks(torch)
         result["parts"]["box_peaks"] = peaks
         result["roofline"]["frac_vs_measured_copy"] = achieved / peaks["copy_GBps"]
+        for key, row in result["parts"]["decode_cold"].items():
+            if isinstance(row, dict):
+                row["frac_vs_measured_copy"] = row["alg_GBps"] / peaks["copy_GBps"]
         result["parts"]["fwd32k"]["mfma_util_vs_measured_gemm"] = (
             result["parts"]["fwd32k"]["alg_tflops"] / peaks["bf16_gemm_tflops"])
     if not args.no_cpu_baseline:

@@ -144,11 +144,28 @@ typedef enum { KATA_FEATURE_PSD = 0, KATA_FEATURE_IDENTITY = 1 } kata_feature_t;
 /* How the inter-chunk prefix is formed (explainer section 2.3: recurrence depth
  * O(N_C) sequentially, O(log N_C) with an associative scan).
  *  KATA_PREFIX_SCAN: chunk states of parallel segments, an associative scan over
- *    them, then every segment's output in parallel (kata_chunked_fwd).
+ *    them, then every segment's output in parallel (kata_chunked_fwd). The scan
+ *    over segment states is blocked (records summed in runs of 16, groups of 8
+ *    runs, tiles of 128 records chained), the fastest at the segment counts the
+ *    library plans (about 1024 segments); its depth grows with the number of
+ *    tiles.
  *  KATA_PREFIX_SEQUENTIAL: one workgroup per (batch, head) walks every chunk in
  *    order, carrying the state from chunk to chunk (depth N_C). Same results up
- *    to fp32 summation order. bf16 only. */
-typedef enum { KATA_PREFIX_SCAN = 0, KATA_PREFIX_SEQUENTIAL = 1 } kata_prefix_t;
+ *    to fp32 summation order. bf16 only.
+ *  KATA_PREFIX_TREE: as KATA_PREFIX_SCAN with a log-depth scan over segment (or,
+ *    on the fp32 path, chunk) states: a Kogge-Stone scan within tiles of 128
+ *    states, reduce-then-scan across tiles (ceil(log2 n) combine levels per tile
+ *    pass and one per level of tiles; kata_prefix_depth reports it). */
+typedef enum { KATA_PREFIX_SCAN = 0, KATA_PREFIX_SEQUENTIAL = 1, KATA_PREFIX_TREE = 2 } kata_prefix_t;
+
+/* Depth of the inter-chunk prefix of a kata_chunked_fwd_ex call with these
+ * arguments: the number of dependent state combines on its longest chain - the
+ * chunks a segment's workgroup carries in order plus the levels of the scan
+ * over segment states (matrix-core paths), the scan levels over chunk states
+ * (fp32 path), or every chunk (KATA_PREFIX_SEQUENTIAL). -1 for invalid or
+ * unsupported arguments. */
+int kata_prefix_depth(int B, int H, int T, int d_k, int d_v, int chunk, kata_dtype_t dtype,
+                      kata_feature_t feature, kata_prefix_t prefix, int segment_chunks);
 
 /* State dimension of a feature: d(d+1)/2 for KATA_FEATURE_PSD, d for
  * KATA_FEATURE_IDENTITY; -1 for d < 0 or an unknown feature. */
@@ -173,7 +190,8 @@ size_t kata_chunked_fwd_ex_workspace(int B, int H, int T, int d_k, int d_v, int 
  * KATA_EUNSUPPORTED): for KATA_FEATURE_PSD d_k = 16 with chunk 32 or 64, d_k = 32
  * with chunk 64 or 128; for KATA_FEATURE_IDENTITY chunk 32, 64 or 128. Every
  * other supported shape (fp32 inputs, or chunk 16 with the identity feature)
- * runs the fp32 path with KATA_PREFIX_SCAN. */
+ * runs the fp32 path with KATA_PREFIX_SCAN or KATA_PREFIX_TREE (over one state
+ * per chunk). */
 kata_status_t kata_chunked_fwd_ex(const void* q, const void* k, const void* v, void* o,
                                   int B, int H, int T, int d_k, int d_v, int chunk, int causal,
                                   kata_dtype_t dtype, kata_feature_t feature,
@@ -198,7 +216,8 @@ kata_status_t kata_chunked_fwd_ex(const void* q, const void* k, const void* v, v
  * Every other argument as for kata_chunked_fwd (S0, z0 stand for earlier tokens
  * and decay with the sequence; S_out, z_out are the decayed final state).
  * Paths: dtype KATA_BF16 with d_k = 16 and chunk in {32, 64}, or d_k = 32 and
- * chunk in {64, 128}, runs on the matrix cores with either prefix, provided T
+ * chunk in {64, 128}, runs on the matrix cores with any prefix method (the
+ * tree scan combines segment states under the same operator), provided T
  * is a multiple of 4 or B*H == 1 (the log-decays of a head are copied 16 bytes
  * at a time). Every other supported shape (d_k in {16, 32}, d_v in {16, 32, 64},
  * chunk in {16, 32, 64, 128}, fp32 or bf16 inputs, any T) runs the fp32 path
@@ -242,12 +261,18 @@ kata_status_t kata_decode_step_decay(const void* q, const void* k, const void* v
                                      const float* log_decay, float* S, float* z, void* o,
                                      int N, int d_k, int d_v, kata_dtype_t dtype, void* stream);
 
-/* Bytes of workspace kata_scan_states needs (currently always 0). */
+/* Bytes of workspace kata_scan_states needs (0 for the fp32 path). */
 size_t kata_scan_states_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
                                   kata_dtype_t dtype);
 
 /* Per-chunk states and their exclusive prefix (the associative scan over chunk
- * states, section 2.3; operator +, identity S0 or 0).
+ * states, section 2.3; operator +, identity S0 or 0). bf16 inputs on the
+ * matrix-core shapes (d_k = 16 with chunk 32 or 64, d_k = 32 with chunk 64 or
+ * 128) take segment states, an associative scan over them and a walk of each
+ * segment that writes every chunk's prefix, with split (hi + lo) operands for
+ * the lifted keys, so the prefixes are exact sums up to fp32 rounding; every
+ * other shape the fp32 path (per-chunk states, then the scan over them).
+ *   workspace, ws_bytes - at least kata_scan_states_workspace bytes.
  *   k [B,H,T,d_k], v [B,H,T,d_v] (dtype) - inputs.
  *   S_prefix [B,H,NC,D,d_v], z_prefix [B,H,NC,D] (fp32, NC = ceil(T/chunk)) -
  *     output: entry c holds S0 + sum over chunks c' < c of phi(K_c')^T V_c'

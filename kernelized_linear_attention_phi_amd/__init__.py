@@ -16,6 +16,6 @@ from ._binding import (KataError, chunked_fwd, chunked_fwd_into, chunked_fwd_wor
                        chunked_fwd_decay, chunked_fwd_decay_into, chunked_fwd_decay_workspace,
                        decode_step, decode_step_decay, feature_dim, flash_fwd, lib, phi_dim,
                        scan_states, scan_states_into, chunked_fwd_noalloc_into,
-                       NOALLOC_SCRATCH_BYTES, LIB_PATH)
+                       NOALLOC_SCRATCH_BYTES, prefix_depth, LIB_PATH)
 
 __version__ = "0.2.0"

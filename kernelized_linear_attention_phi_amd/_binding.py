@@ -14,7 +14,8 @@ import torch
 __all__ = ["KataError", "lib", "chunked_fwd", "chunked_fwd_into", "chunked_fwd_workspace",
            "scan_states", "flash_fwd", "decode_step", "phi_dim", "feature_dim",
            "chunked_fwd_decay", "chunked_fwd_decay_into", "chunked_fwd_decay_workspace",
-           "decode_step_decay", "chunked_fwd_noalloc_into", "NOALLOC_SCRATCH_BYTES", "LIB_PATH"]
+           "decode_step_decay", "chunked_fwd_noalloc_into", "NOALLOC_SCRATCH_BYTES", "prefix_depth",
+           "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkata.so")
 
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.kata_chunked_fwd_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                                vp, vp, vp, vp, vp]
         L.kata_chunked_fwd_noalloc.restype = i
+        L.kata_prefix_depth.argtypes = [i, i, i, i, i, i, i, i, i, i]
+        L.kata_prefix_depth.restype = i
         _lib = L
     return _lib
 
@@ -152,13 +155,21 @@ def _raise(st, what):
 
 
 FEATURES = {"psd": 0, "identity": 1}       # kata_feature_t
-PREFIXES = {"scan": 0, "sequential": 1}    # kata_prefix_t
+PREFIXES = {"scan": 0, "sequential": 1, "tree": 2}    # kata_prefix_t
 
 
 def _modes(feature, prefix):
     if feature not in FEATURES or prefix not in PREFIXES:
         raise ValueError(f"feature in {sorted(FEATURES)}, prefix in {sorted(PREFIXES)}")
     return FEATURES[feature], PREFIXES[prefix]
+
+
+def prefix_depth(B, H, T, dk, dv, chunk, dtype_code=BF16, feature="psd", prefix="scan",
+                 segment_chunks=0) -> int:
+    """Dependent state combines on the longest chain of the inter-chunk prefix
+    (kata_prefix_depth); -1 for unsupported arguments."""
+    f, pf = _modes(feature, prefix)
+    return lib().kata_prefix_depth(B, H, T, dk, dv, chunk, dtype_code, f, pf, int(segment_chunks))
 
 
 def feature_dim(d: int, feature: str = "psd") -> int:
@@ -292,8 +303,11 @@ def scan_states(k, v, chunk=64, initial_state=None):
     return Sp, zp, ST, zT
 
 
-def scan_states_into(k, v, chunk, S_prefix, z_prefix, S_out=None, z_out=None, S0=None, z0=None):
-    """Raw kata_scan_states into preallocated outputs (used by the benchmark)."""
+def scan_states_into(k, v, chunk, S_prefix, z_prefix, S_out=None, z_out=None, S0=None, z0=None,
+                     workspace=None):
+    """Raw kata_scan_states into preallocated outputs (used by the benchmark);
+    workspace: at least kata_scan_states_workspace bytes (allocated here when
+    None)."""
     _check_qkv(k, k, v)
     B, H, T, dk = k.shape
     dv = v.shape[-1]
@@ -301,9 +315,14 @@ def scan_states_into(k, v, chunk, S_prefix, z_prefix, S_out=None, z_out=None, S0
     _check_state(S_prefix, z_prefix, (B, H, NC), D, dv, "prefix states")
     _check_state(S0, z0, (B, H), D, dv, "initial state")
     _check_state(S_out, z_out, (B, H), D, dv, "final state")
+    if workspace is None:
+        nbytes = lib().kata_scan_states_workspace(B, H, T, dk, dv, chunk, _dtype_code(k))
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=k.device) if nbytes else None
+    _check_dev(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().kata_scan_states(_ptr(k), _ptr(v), B, H, T, dk, dv, chunk, _dtype_code(k),
                                 _ptr(S0), _ptr(z0), _ptr(S_prefix), _ptr(z_prefix), _ptr(S_out),
-                                _ptr(z_out), None, 0, _stream())
+                                _ptr(z_out), _ptr(workspace), ws_bytes, _stream())
     _raise(st, "kata_scan_states")
 
 

@@ -50,8 +50,9 @@ struct FwdPlan {
     bool ok;    // supported combination of shape, feature and prefix method
     int mfma;   // 0 (VALU path), 16 or 32 (PSD lift, d_k), 1 (identity feature)
     bool seq;   // sequential prefix
+    bool tree;  // log-depth scan
     int G, NSEG, REC;
-    size_t S_off, z_off, init_off, total_off, bytes;
+    size_t S_off, z_off, init_off, total_off, tree_off, bytes;
 };
 
 // G for a requested value (> 0) or automatically (0): about `workgroups`
@@ -69,12 +70,13 @@ FwdPlan plan_fwd(const Shape& s, int causal, kata_feature_t f = KATA_FEATURE_PSD
     if (f == KATA_FEATURE_IDENTITY) {
         // matrix cores for the bf16 shapes, else the fp32 path (scan prefix)
         p.mfma = kata::first_supported(s) ? 1 : 0;
-        p.ok = p.mfma != 0 || pf == KATA_PREFIX_SCAN;
+        p.ok = p.mfma != 0 || pf != KATA_PREFIX_SEQUENTIAL;
     } else {
         p.mfma = kata::mfma16_supported(s) ? 16 : kata::mfma32_supported(s) ? 32 : 0;
-        p.ok = p.mfma != 0 || pf == KATA_PREFIX_SCAN;
+        p.ok = p.mfma != 0 || pf != KATA_PREFIX_SEQUENTIAL;
     }
     p.seq = pf == KATA_PREFIX_SEQUENTIAL;
+    p.tree = pf == KATA_PREFIX_TREE;
     const size_t BH = (size_t)s.B * s.H;
     if (!p.ok || BH == 0 || s.NC == 0) return p;
     if (p.mfma) {
@@ -88,14 +90,19 @@ FwdPlan plan_fwd(const Shape& s, int causal, kata_feature_t f = KATA_FEATURE_PSD
         p.S_off = 0;
         p.init_off = align256(BH * p.NSEG * p.REC * sizeof(float));
         p.total_off = p.init_off + align256(BH * p.REC * sizeof(float));
-        p.bytes = p.total_off + align256(BH * p.REC * sizeof(float));
+        p.tree_off = p.total_off + align256(BH * p.REC * sizeof(float));
+        // the tree scan's tile sums (and, gated, tile and record decays)
+        const size_t tree = p.tree ? kata::scan_tree_scratch_floats((int)BH, p.NSEG, p.REC, true) : 0;
+        p.bytes = p.tree_off + align256(tree * sizeof(float));
         return p;
     }
     // non-causal also needs the per-chunk totals before reducing them
     const size_t nrec = BH * (size_t)s.NC + (causal ? 0 : BH);
     p.S_off = 0;
     p.z_off = align256(nrec * s.D * s.dv * sizeof(float));
-    p.bytes = p.z_off + align256(nrec * s.D * sizeof(float));
+    p.tree_off = p.z_off + align256(nrec * s.D * sizeof(float));
+    const size_t tree = p.tree ? kata::scan_tree_scratch_floats((int)BH, s.NC, s.D * s.dv, true) : 0;
+    p.bytes = p.tree_off + align256(tree * sizeof(float));
     return p;
 }
 
@@ -137,7 +144,34 @@ int kata_feature_dim(int d, kata_feature_t feature) {
 
 static bool valid_modes(kata_feature_t f, kata_prefix_t pf) {
     return (f == KATA_FEATURE_PSD || f == KATA_FEATURE_IDENTITY) &&
-           (pf == KATA_PREFIX_SCAN || pf == KATA_PREFIX_SEQUENTIAL);
+           (pf == KATA_PREFIX_SCAN || pf == KATA_PREFIX_SEQUENTIAL || pf == KATA_PREFIX_TREE);
+}
+
+// The scan over n records by the plan's method (blocked or tree); dec: the
+// per-record decays of the gated operator (NULL = plain addition).
+static hipError_t scan_by_plan(const FwdPlan& p, char* ws, float* rec, const float* dec, int nseq,
+                               int n, int E, const float* init, float* total_a, float* total_b,
+                               hipStream_t hs, const kata::RecordExport* ex = nullptr) {
+    if (p.tree)
+        return kata::launch_scan_records_tree(rec, dec, nseq, n, E, init, total_a, total_b,
+                                              reinterpret_cast<float*>(ws + p.tree_off), hs, ex);
+    return dec ? kata::launch_scan_records_decay(rec, dec, nseq, n, E, init, total_a, total_b, hs, ex)
+               : kata::launch_scan_records(rec, nseq, n, E, init, total_a, total_b, hs, ex);
+}
+
+int kata_prefix_depth(int B, int H, int T, int d_k, int d_v, int chunk, kata_dtype_t dtype,
+                      kata_feature_t feature, kata_prefix_t prefix, int segment_chunks) {
+    Shape s;
+    if (!valid_modes(feature, prefix) || segment_chunks < 0) return -1;
+    if (make_shape(B, H, T, d_k, d_v, chunk, dtype, &s, feature) != KATA_OK) return -1;
+    const FwdPlan p = plan_fwd(s, 1, feature, prefix, segment_chunks);
+    if (!p.ok) return -1;
+    if ((size_t)B * H == 0 || s.NC == 0) return 0;
+    const int method = p.tree ? 2 : 0;
+    if (!p.mfma) return kata::scan_levels(s.NC, method);
+    if (p.seq) return s.NC;
+    // a segment's chunks in order, after the scan over segment states
+    return p.G + kata::scan_levels(p.NSEG, method);
 }
 
 size_t kata_chunked_fwd_ex_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
@@ -265,9 +299,9 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
                                                                                 : kata::kRecIdent,
                                             s.dk, s.dv, S_out, z_out};
                 if (e == hipSuccess)
-                    e = kata::launch_scan_records(rec, (int)BH, plan.NSEG, plan.REC,
-                                                  S0 ? init : nullptr, causal ? nullptr : total,
-                                                  nullptr, hs, S_out ? &ex : nullptr);
+                    e = scan_by_plan(plan, ws, rec, nullptr, (int)BH, plan.NSEG, plan.REC,
+                                     S0 ? init : nullptr, causal ? nullptr : total, nullptr, hs,
+                                     S_out ? &ex : nullptr);
             } else if (e == hipSuccess) {
                 e = mark(1);
             }
@@ -289,9 +323,9 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
     if (causal) {
         // exclusive prefix over chunks in place; inclusive total -> final state
         if (e == hipSuccess)
-            e = kata::launch_scan_records(S_rec, (int)BH, s.NC, (int)nS, S0, S_out, nullptr, hs);
+            e = scan_by_plan(plan, ws, S_rec, nullptr, (int)BH, s.NC, (int)nS, S0, S_out, nullptr, hs);
         if (e == hipSuccess)
-            e = kata::launch_scan_records(z_rec, (int)BH, s.NC, (int)nz, z0, z_out, nullptr, hs);
+            e = scan_by_plan(plan, ws, z_rec, nullptr, (int)BH, s.NC, (int)nz, z0, z_out, nullptr, hs);
         if (e == hipSuccess) e = mark(2);
         if (e == hipSuccess) e = kata::launch_fwd_valu(s, q, k, v, nullptr, S_rec, z_rec, o, 1, ident, hs);
     } else {
@@ -299,9 +333,9 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
         float* S_tot = S_rec + BH * s.NC * nS;
         float* z_tot = z_rec + BH * s.NC * nz;
         if (e == hipSuccess)
-            e = kata::launch_scan_records(S_rec, (int)BH, s.NC, (int)nS, S0, S_tot, S_out, hs);
+            e = scan_by_plan(plan, ws, S_rec, nullptr, (int)BH, s.NC, (int)nS, S0, S_tot, S_out, hs);
         if (e == hipSuccess)
-            e = kata::launch_scan_records(z_rec, (int)BH, s.NC, (int)nz, z0, z_tot, z_out, hs);
+            e = scan_by_plan(plan, ws, z_rec, nullptr, (int)BH, s.NC, (int)nz, z0, z_tot, z_out, hs);
         if (e == hipSuccess) e = mark(2);
         if (e == hipSuccess) e = kata::launch_fwd_valu(s, q, k, v, nullptr, S_tot, z_tot, o, 0, ident, hs);
     }
@@ -345,14 +379,30 @@ kata_status_t kata_chunked_fwd_profiled(const void* q, const void* k, const void
                             events);
 }
 
-size_t kata_scan_states_workspace(int, int, int, int, int, int, kata_dtype_t) { return 0; }
+// kata_scan_states on the matrix cores (bf16, PSD shapes of the output
+// kernels): segment states with split key operands, the scan over segment
+// records (the initial state as its identity, the packed total as S_out), then
+// each segment's chunks walked from its prefix, every chunk's exclusive prefix
+// written in the packed layout. Workspace: the segment records and one
+// initial-state record per head.
+static FwdPlan scan_plan(const Shape& s) {
+    FwdPlan p = plan_fwd(s, 1);
+    if (!p.mfma) p.bytes = 0;                 // the fp32 path writes into S_prefix itself
+    else p.bytes = p.total_off;               // no final-state record
+    return p;
+}
+
+size_t kata_scan_states_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                  kata_dtype_t dtype) {
+    Shape s;
+    if (make_shape(B, H, T, d_k, d_v, chunk, dtype, &s) != KATA_OK) return 0;
+    return scan_plan(s).bytes;
+}
 
 kata_status_t kata_scan_states(const void* k, const void* v, int B, int H, int T, int d_k,
                                int d_v, int chunk, kata_dtype_t dtype, const float* S0,
                                const float* z0, float* S_prefix, float* z_prefix, float* S_out,
                                float* z_out, void* workspace, size_t ws_bytes, void* stream) {
-    (void)workspace;
-    (void)ws_bytes;
     Shape s;
     kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s);
     if (st != KATA_OK) return st;
@@ -363,8 +413,10 @@ kata_status_t kata_scan_states(const void* k, const void* v, int B, int H, int T
     if (!empty && (!k || !v || !S_prefix || !z_prefix)) return KATA_EINVAL;
     for (const void* p : {(const void*)k, (const void*)v, (const void*)S0, (const void*)z0,
                           (const void*)S_prefix, (const void*)z_prefix, (const void*)S_out,
-                          (const void*)z_out})
+                          (const void*)z_out, (const void*)workspace})
         if (p && !aligned16(p)) return KATA_EINVAL;
+    const FwdPlan plan = empty ? FwdPlan{} : scan_plan(s);
+    if (ws_bytes < plan.bytes || (plan.bytes && !workspace)) return KATA_EWORKSPACE;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const size_t nS = (size_t)s.D * s.dv, nz = s.D;
     if (empty) {
@@ -374,6 +426,27 @@ kata_status_t kata_scan_states(const void* k, const void* v, int B, int H, int T
             return hip_status(e);
         }
         return KATA_OK;
+    }
+    if (plan.mfma == 16 || plan.mfma == 32) {
+        char* ws = static_cast<char*>(workspace);
+        float* rec = reinterpret_cast<float*>(ws + plan.S_off);
+        float* init = reinterpret_cast<float*>(ws + plan.init_off);
+        const bool m16 = plan.mfma == 16;
+        hipError_t e = hipSuccess;
+        if (S0)
+            e = m16 ? kata::launch_record_from_packed16(init, S0, z0, s.dv, (int)BH, hs)
+                    : kata::launch_record_from_packed32(init, S0, z0, s.dv, (int)BH, hs);
+        if (e == hipSuccess)
+            e = m16 ? kata::launch_seg_state16(s, k, v, rec, plan.G, plan.NSEG, true, hs)
+                    : kata::launch_seg_state32(s, k, v, rec, plan.G, plan.NSEG, true, hs);
+        const kata::RecordExport ex{m16 ? kata::kRecPsd16 : kata::kRecPsd32, s.dk, s.dv, S_out, z_out};
+        if (e == hipSuccess)
+            e = kata::launch_scan_records(rec, (int)BH, plan.NSEG, plan.REC, S0 ? init : nullptr,
+                                          nullptr, nullptr, hs, S_out ? &ex : nullptr);
+        if (e == hipSuccess)
+            e = m16 ? kata::launch_prefix16(s, k, v, rec, S_prefix, z_prefix, plan.G, plan.NSEG, hs)
+                    : kata::launch_prefix32(s, k, v, rec, S_prefix, z_prefix, plan.G, plan.NSEG, hs);
+        return hip_status(e);
     }
     hipError_t e = kata::launch_chunk_states_valu(s, k, v, nullptr, S_prefix, z_prefix, nullptr, 0, hs);
     if (e == hipSuccess)
@@ -536,9 +609,8 @@ kata_status_t kata_chunked_fwd_decay_ex(const void* q, const void* k, const void
                 : m == 16 ? kata::launch_seg_state16_decay(s, k, v, log_decay, rec, segdec, fp.G, fp.NSEG, hs)
                           : kata::launch_seg_state32_decay(s, k, v, log_decay, rec, segdec, fp.G, fp.NSEG, hs);
         if (e == hipSuccess)
-            e = kata::launch_scan_records_decay(rec, segdec, nrec, fp.NSEG, fp.REC,
-                                                S0 ? init : nullptr, nullptr, nullptr, hs,
-                                                S_out ? &ex : nullptr);
+            e = scan_by_plan(fp, ws, rec, segdec, nrec, fp.NSEG, fp.REC, S0 ? init : nullptr,
+                             nullptr, nullptr, hs, S_out ? &ex : nullptr);
         if (e == hipSuccess) e = output(rec, nullptr);
     }
     return hip_status(e);

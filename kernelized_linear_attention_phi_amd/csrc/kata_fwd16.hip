@@ -821,6 +821,122 @@ hipError_t launch_fwd16_decay(const Shape& s, const void* q, const void* k, cons
     return dispatch(s, Args{q, k, v, gdec, final_rec, nullptr, prefix, o, 1, G, NSEG, false, true}, st);
 }
 
+// ---- per-chunk exclusive prefixes (kata_scan_states) ---------------------------
+// One workgroup per segment starts from the segment's exclusive prefix (a
+// scanned segment record) and walks its chunks: it writes the running state -
+// the exclusive prefix of chunk c - to the packed S_prefix[c], z_prefix[c],
+// then adds chunk c with split key operands (exact for bf16 keys), so every
+// prefix is an fp32-accurate sum. Wavefront 0 writes feature tiles 0..3 and its
+// value tiles of tile 8, wavefront 1 tiles 4..7, the rest of tile 8 and the
+// Gram matrix (as z). Lanes 16g .. 16g + 15 write 16 consecutive value
+// columns of one packed row.
+
+namespace {
+
+template <int W, int DV, int C>
+__device__ __forceinline__ void store_packed16(const State<DV, C>& st, float* Sp, float* zp,
+                                               const Lane& L) {
+    using F = Cfg<DV, C>;
+    constexpr int l8 = lo8<W, F::NTV>(), h8 = hi8<W, F::NTV>();
+    auto put = [&](int tile, int nt, const f32x4_t& x) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            int col;
+            float scale;
+            bool lower;
+            const int p = rec16_to_packed(((tile * F::NTV + nt) * 64 + L.lane) * 4 + r, F::NTV,
+                                          &col, &scale, &lower);
+            if (p >= 0) Sp[p * DV + col] = x[r] * scale;
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int nt = 0; nt < F::NTV; ++nt) put(4 * W + i, nt, st.s[i][nt]);
+#pragma unroll
+    for (int j = 0; j < h8 - l8; ++j) put(8, l8 + j, st.x[j]);
+    if constexpr (W == 1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            int col;
+            float scale;
+            bool lower;
+            const int p = rec16_to_packed(NMT * F::NTV * 256 + L.lane * 4 + r, F::NTV, &col, &scale,
+                                          &lower);
+            if (!lower) zp[p] = st.zm[r] * scale;
+        }
+    }
+}
+
+template <int W, int DV, int C>
+__device__ __forceinline__ void prefix_body(const bf16_t* k, const bf16_t* v, const float* prefix,
+                                            float* Sp, float* zp, char* lds, int T, int NC, int G,
+                                            int NSEG, const Lane& L) {
+    using F = Cfg<DV, C>;
+    constexpr int D = DK * (DK + 1) / 2;
+    const int seg = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int c0 = seg * G, c1 = min(NC, seg * G + G);
+    // only the chunks whose state is added are staged (the last chunk's
+    // prefix is written from the state before it)
+    LoadPipeline<DK, DV, C, NW, 3, false> P{lds, c0, c1 - 1, T, bh * T, nullptr};
+    State<DV, C> st;
+    record_load<W, DV, C>(prefix + (bh * NSEG + seg) * (size_t)F::REC, st, L);
+    P.prologue(k, v, L);
+    for (int c = c0; c < c1 - 1; ++c) {
+        store_packed16<W, DV, C>(st, Sp + (bh * NC + c) * (size_t)(D * DV), zp + (bh * NC + c) * (size_t)D, L);
+        P.acquire(k, v, c, L);
+        const char* buf = P.buffer(c);
+        const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::QB);
+        const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::QB);
+        f32x4_t KT[F::TT];
+        k_transposed<DV, C>(bk, KT, L);
+        u32x4_t vop[F::KS][F::NTV];
+#pragma unroll
+        for (int m = 0; m < F::KS; ++m) v_fragment_step<DV, C>(bv, vop[m], m, L);
+        state_update<W, W == 1, DV, C, false, true>(st, KT, vop, L);
+        compiler_fence();
+    }
+    store_packed16<W, DV, C>(st, Sp + (bh * NC + c1 - 1) * (size_t)(D * DV),
+                             zp + (bh * NC + c1 - 1) * (size_t)D, L);
+}
+
+template <int DV, int C>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void kata_prefix16(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                   const float* __restrict__ prefix, float* __restrict__ Sp,
+                   float* __restrict__ zp, int T, int NC, int G, int NSEG) {
+    __shared__ __attribute__((aligned(16))) char lds[3 * ChunkIO<DK, DV, C, NW, NW, false>::BUF];
+    const Lane L;
+    if (L.w == 0) prefix_body<0, DV, C>(k, v, prefix, Sp, zp, lds, T, NC, G, NSEG, as_wave<0>(L));
+    else prefix_body<1, DV, C>(k, v, prefix, Sp, zp, lds, T, NC, G, NSEG, as_wave<1>(L));
+}
+
+template <int C>
+hipError_t launch_prefix16_c(const Shape& s, const void* k, const void* v, const float* prefix,
+                             float* Sp, float* zp, int G, int NSEG, hipStream_t st) {
+    dim3 grid(NSEG, s.B * s.H);
+    const bf16_t *kk = (const bf16_t*)k, *vv = (const bf16_t*)v;
+    switch (s.dv) {
+        case 16: kata_prefix16<16, C><<<grid, 64 * NW, 0, st>>>(kk, vv, prefix, Sp, zp, s.T, s.NC, G, NSEG); break;
+        case 32: kata_prefix16<32, C><<<grid, 64 * NW, 0, st>>>(kk, vv, prefix, Sp, zp, s.T, s.NC, G, NSEG); break;
+        case 64: kata_prefix16<64, C><<<grid, 64 * NW, 0, st>>>(kk, vv, prefix, Sp, zp, s.T, s.NC, G, NSEG); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefix16(const Shape& s, const void* k, const void* v, const float* prefix,
+                           float* Sp, float* zp, int G, int NSEG, hipStream_t st) {
+    switch (s.C) {
+        case 32: return launch_prefix16_c<32>(s, k, v, prefix, Sp, zp, G, NSEG, st);
+        case 64: return launch_prefix16_c<64>(s, k, v, prefix, Sp, zp, G, NSEG, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 // ---- record <-> packed state conversion ------------------------------------
 
 namespace {

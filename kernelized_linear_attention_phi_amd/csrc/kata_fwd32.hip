@@ -881,6 +881,102 @@ hipError_t dispatch32(const Shape& s, const Args32& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+// ---- per-chunk exclusive prefixes (kata_scan_states) -------------------------------
+// As at d_k = 16: one workgroup per segment walks its chunks from the segment's
+// scanned prefix, writes each chunk's exclusive prefix to the packed
+// S_prefix[c], z_prefix[c], then adds the chunk with split key operands.
+// Wavefront w writes the tiles, the tile-32 value tile and the Gram tile it
+// owns (its lower-triangle entries skipped).
+
+template <int W, int DV, int C>
+__device__ __forceinline__ void store_packed32(const State32<DV, C>& st, float* Sp, float* zp,
+                                               const Lane& L) {
+    using F = Cfg32<DV, C>;
+    auto put = [&](int tile, int nt, const f32x4_t& x) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            int col;
+            float scale;
+            bool lower;
+            const int p = rec32_to_packed(((tile * F::NTV + nt) * 64 + L.lane) * 4 + r, F::NTV,
+                                          &col, &scale, &lower);
+            Sp[p * DV + col] = x[r] * scale;
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < F::TPW; ++i)
+#pragma unroll
+        for (int nt = 0; nt < F::NTV; ++nt) put(F::TPW * W + i, nt, st.s[i][nt]);
+    if constexpr (has_x<DV, C, W>()) put(32, xnt<DV, C, W>(), st.x);
+    if constexpr (W < 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            int col;
+            float scale;
+            bool lower;
+            const int p = rec32_to_packed(NFT * F::NTV * 256 + (W * 64 + L.lane) * 4 + r, F::NTV,
+                                          &col, &scale, &lower);
+            if (!lower) zp[p] = st.z[r] * scale;
+        }
+    }
+}
+
+template <int W, int DV, int C>
+__device__ __forceinline__ void prefix_body32(const bf16_t* k, const bf16_t* v, const float* prefix,
+                                              float* Sp, float* zp, char* lds, int T, int NC,
+                                              int G, int NSEG, const Lane& L) {
+    using F = Cfg32<DV, C>;
+    constexpr int D = DK * (DK + 1) / 2;
+    const int seg = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int c0 = seg * G, c1 = min(NC, seg * G + G);
+    LoadPipeline<DK, DV, C, F::NW, 4, false> P{lds, c0, c1 - 1, T, bh * T, nullptr};
+    State32<DV, C> st;
+    record_load32<W, DV, C>(prefix + (bh * NSEG + seg) * (size_t)F::REC, st, L);
+    P.prologue(k, v, L);
+    for (int c = c0; c < c1 - 1; ++c) {
+        store_packed32<W, DV, C>(st, Sp + (bh * NC + c) * (size_t)(D * DV), zp + (bh * NC + c) * (size_t)D, L);
+        P.acquire(k, v, c, L);
+        const char* buf = P.buffer(c);
+        const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::IO::QB);
+        const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::IO::QB);
+#pragma unroll
+        for (int m = 0; m < F::KS; ++m) state_step<W, DV, C, false, true>(st, bk, bv, m, L);
+        compiler_fence();
+    }
+    store_packed32<W, DV, C>(st, Sp + (bh * NC + c1 - 1) * (size_t)(D * DV),
+                             zp + (bh * NC + c1 - 1) * (size_t)D, L);
+}
+
+template <int DV, int C>
+__global__ __launch_bounds__(kThreads32<C>, kWavesPerSimd32<C>)
+void kata_prefix32(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                   const float* __restrict__ prefix, float* __restrict__ Sp,
+                   float* __restrict__ zp, int T, int NC, int G, int NSEG) {
+    using F = Cfg32<DV, C>;
+    __shared__ __attribute__((aligned(16))) char lds[F::LDS_SEG];
+    const Lane L;
+    by_wave<DV, C>(L.w, [&](auto wc) {
+        prefix_body32<decltype(wc)::value, DV, C>(k, v, prefix, Sp, zp, lds, T, NC, G, NSEG,
+                                                  as_wave<decltype(wc)::value>(L));
+    });
+}
+
+template <int C>
+hipError_t launch_prefix32_c(const Shape& s, const void* k, const void* v, const float* prefix,
+                             float* Sp, float* zp, int G, int NSEG, hipStream_t st) {
+    dim3 grid(NSEG, s.B * s.H);
+    constexpr int threads = kThreads32<C>;
+    const bf16_t *kk = (const bf16_t*)k, *vv = (const bf16_t*)v;
+    switch (s.dv) {
+        case 16: kata_prefix32<16, C><<<grid, threads, 0, st>>>(kk, vv, prefix, Sp, zp, s.T, s.NC, G, NSEG); break;
+        case 32: kata_prefix32<32, C><<<grid, threads, 0, st>>>(kk, vv, prefix, Sp, zp, s.T, s.NC, G, NSEG); break;
+        case 64: kata_prefix32<64, C><<<grid, threads, 0, st>>>(kk, vv, prefix, Sp, zp, s.T, s.NC, G, NSEG); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 __global__ void record_from_packed32(float* __restrict__ rec, const float* __restrict__ S,
                                      const float* __restrict__ z, int NTV, int REC, int nrec) {
     const int D = DK * (DK + 1) / 2, DV = 16 * NTV;
@@ -944,6 +1040,15 @@ hipError_t launch_fwd32_decay(const Shape& s, const void* q, const void* k, cons
                               const float* gdec, const float* prefix, float* final_rec, void* o,
                               int G, int NSEG, hipStream_t st) {
     return dispatch32(s, Args32{q, k, v, gdec, final_rec, nullptr, prefix, o, 1, G, NSEG, false, true}, st);
+}
+
+hipError_t launch_prefix32(const Shape& s, const void* k, const void* v, const float* prefix,
+                           float* Sp, float* zp, int G, int NSEG, hipStream_t st) {
+    switch (s.C) {
+        case 64: return launch_prefix32_c<64>(s, k, v, prefix, Sp, zp, G, NSEG, st);
+        case 128: return launch_prefix32_c<128>(s, k, v, prefix, Sp, zp, G, NSEG, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_record_from_packed32(float* rec, const float* S, const float* z, int dv,

@@ -53,6 +53,19 @@ hipError_t launch_scan_records_decay(float* rec, const float* dec, int nseq, int
                                      const float* init, float* total_a, float* total_b,
                                      hipStream_t st, const RecordExport* ex = nullptr);
 
+// Log-depth variant of both (dec NULL = plain addition): a Kogge-Stone scan
+// within tiles of 128 records, reduce-then-scan across tiles. scratch: at least
+// scan_tree_scratch_floats floats (none for NR <= 128). Its depth is checked
+// against ceil(log2 NR) plus two combines per level of tiles.
+hipError_t launch_scan_records_tree(float* rec, const float* dec, int nseq, int NR, int E,
+                                    const float* init, float* total_a, float* total_b,
+                                    float* scratch, hipStream_t st,
+                                    const RecordExport* ex = nullptr);
+size_t scan_tree_scratch_floats(int nseq, int NR, int E, bool decay);
+// Dependent combine levels over NR records: method 0 the blocked scan, 1 the
+// sequential walk, 2 the tree.
+int scan_levels(int NR, int method);
+
 // Record layouts of the matrix-core kernels (kata_records.h) and a packed
 // state to export a record to.
 constexpr int kRecNone = 0, kRecPsd16 = 1, kRecPsd32 = 2, kRecIdent = 3;
@@ -96,6 +109,11 @@ hipError_t launch_seg_state16_decay(const Shape& s, const void* k, const void* v
 hipError_t launch_fwd16_decay(const Shape& s, const void* q, const void* k, const void* v,
                               const float* gdec, const float* prefix, float* final_rec, void* o,
                               int G, int NSEG, hipStream_t st);
+// Per-chunk exclusive prefixes for kata_scan_states: prefix [BH, NSEG, REC]
+// scanned (exclusive) segment records; writes the packed prefix of every chunk
+// to Sp [BH, NC, D, dv], zp [BH, NC, D] (split key operands: fp32-accurate).
+hipError_t launch_prefix16(const Shape& s, const void* k, const void* v, const float* prefix,
+                           float* Sp, float* zp, int G, int NSEG, hipStream_t st);
 hipError_t launch_record_from_packed16(float* rec, const float* S, const float* z, int dv,
                                        int nrec, hipStream_t st);
 hipError_t launch_record_to_packed16(const float* rec, float* S, float* z, int dv, int nrec,
@@ -123,6 +141,8 @@ hipError_t launch_seg_state32_decay(const Shape& s, const void* k, const void* v
 hipError_t launch_fwd32_decay(const Shape& s, const void* q, const void* k, const void* v,
                               const float* gdec, const float* prefix, float* final_rec, void* o,
                               int G, int NSEG, hipStream_t st);
+hipError_t launch_prefix32(const Shape& s, const void* k, const void* v, const float* prefix,
+                           float* Sp, float* zp, int G, int NSEG, hipStream_t st);
 hipError_t launch_record_from_packed32(float* rec, const float* S, const float* z, int dv,
                                        int nrec, hipStream_t st);
 hipError_t launch_record_to_packed32(const float* rec, float* S, float* z, int dv, int nrec,

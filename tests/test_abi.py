@@ -242,3 +242,39 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(b, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         b.lib()
+
+
+def test_prefix_depth(L):
+    """kata_prefix_depth: the sequential walk takes one combine per chunk; the
+    blocked scan grows with the number of 128-record tiles; the tree takes
+    ceil(log2 n) levels per tile pass plus one per level of tiles, within
+    ceil(log2 n) + 2 ceil(log128 n) (no GPU is touched)."""
+    import math
+    TREE = 2
+    dep = L.kata_prefix_depth
+    # the fp32 path scans one state per chunk: depth = scan levels over NC
+    for nc in [1, 2, 3, 100, 128, 129, 300, 2048, 16385, 100000]:
+        d = dep(1, 1, nc * 16, 16, 16, 16, F32, PSD, TREE, 0)
+        lg = math.ceil(math.log2(nc)) if nc > 1 else 0
+        tl = 0
+        n = nc
+        while n > 1:
+            n = -(-n // 128)
+            tl += 1
+        assert d <= lg + 2 * max(tl, 1), (nc, d)
+        assert d >= lg                        # no scan beats log2 n levels
+        # blocked scan: a walk below 33 records, else runs of 16, 8 groups and
+        # the carry across 128-record tiles
+        want = nc if nc <= 32 else 16 + 8 + -(-nc // 128)
+        assert dep(1, 1, nc * 16, 16, 16, 16, F32, PSD, SCAN, 0) == want
+    assert dep(1, 1, 128 * 16, 16, 16, 16, F32, PSD, TREE, 0) == 7 + 1
+    assert dep(1, 1, 2048 * 16, 16, 16, 16, F32, PSD, TREE, 0) == 7 + (4 + 1) + 1
+    # matrix cores: a segment's chunks in order, then the scan over segments
+    assert dep(1, 8, 131072, 16, 64, 64, BF16, PSD, SEQUENTIAL, 0) == 2048
+    assert dep(1, 8, 131072, 16, 64, 64, BF16, PSD, TREE, 0) == 16 + 7 + 1      # G 16, 128 segments
+    assert dep(1, 8, 131072, 16, 64, 64, BF16, PSD, TREE, 1) == 1 + 7 + 5 + 1  # G 1, 2048 segments
+    assert dep(1, 8, 131072, 16, 64, 64, BF16, PSD, SCAN, 0) == 16 + 16 + 8 + 1
+    assert dep(1, 1, 64, 24, 64, 64, BF16, PSD, TREE, 0) == -1
+    assert dep(1, 1, 64, 16, 64, 64, F32, PSD, SEQUENTIAL, 0) == -1
+    assert dep(1, 1, 64, 16, 64, 64, BF16, PSD, 7, 0) == -1
+    assert dep(0, 1, 64, 16, 64, 64, BF16, PSD, TREE, 0) == 0

@@ -6,7 +6,7 @@ import pytest
 
 import oracle as O
 from kernelized_linear_attention_phi_amd import inputs as gen
-from tests.gpu_util import dev, host, row_rel_err, sample_rows, say, workload_inputs
+from tests.gpu_util import dev, host, row_rel_err, sample_rows, say, state_rel_err, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -88,3 +88,27 @@ def test_fullsize_decode(kata):
         ref = O.brute_force_rows(qq, kk, vv, steps)[0, 0]
         err = row_rel_err(o_all[:, row], ref)
         assert err <= w.tol, (row, err)
+
+
+@pytest.mark.parametrize("dk,C", [(16, 64), (32, 128)])
+def test_scan_states_long(kata, dk, C):
+    """kata_scan_states on a 131k-token sequence (several chunks per segment,
+    so the per-segment walk carries its state across chunks): sampled chunk
+    prefixes, including those at segment edges, and the final state against
+    the float64 sum of the tokens before them (1e-5 of the state norm)."""
+    import torch
+    B, H, T, dv = 1, 3, 131072 if dk == 16 else 32768, 64
+    q, k, v = gen.gaussian_qkv(B, H, T, dk, dv, seed=4400 + dk, dtype="bf16")
+    say(f"scan_states long dk={dk} C={C} T={T}")
+    Sp, zp, ST, zT = kata.scan_states(dev(k, "bf16"), dev(v, "bf16"), chunk=C)
+    torch.cuda.synchronize()
+    NC = T // C
+    r = np.random.Generator(np.random.PCG64(44))
+    chunks = sorted({0, 1, 2, 3, 5, 6, 7, 8, 11, 12, 13, NC // 2, NC - 2, NC - 1,
+                     *(int(x) for x in r.integers(0, NC, 6))})
+    for c in chunks:
+        P, Z = O.state_from_tokens(k[:, :, :c * C], v[:, :, :c * C])
+        assert state_rel_err(host(Sp[:, :, c]), P) <= 1e-5, c
+        assert state_rel_err(host(zp[:, :, c]), Z) <= 1e-5, c
+    S_ref, z_ref = O.state_from_tokens(k, v)
+    assert state_rel_err(host(ST), S_ref) <= 1e-5 and state_rel_err(host(zT), z_ref) <= 1e-5
