@@ -320,6 +320,28 @@ def recall_forward(kata, torch, gen, steps, warmup):
                 alg_bytes_per_token_head(w.dk, w.dv) * w.B * w.H * w.T / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
+def delta_forward(kata, torch, gen, steps, warmup):
+    """DeltaKATA (kata_delta_fwd) on the recall-shaped stream at full size (B=8,
+    H=4, T=16384, d_k=16, d_v=64, C=64) with write strength 1 (the overwrite
+    the delta rule is for): ms, tokens/s and its fp32 vector-ALU rate.
+    Flops per token-head and value tile of 16 columns + z (fp32 FMAs x 2): the
+    products K A, phi(Q) A and K^T P over D (3 x 2 D x 17), the chunk's key and
+    query Gram terms (2 x 2 C d_k), the masked phi(Q) K^T P (C x 17) and the
+    blocked triangular solve (about C x 17 + 16 x 16)."""
+    w = gen.WORKLOADS["recall16k"]
+    to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+    q, k, v = (to(a) for a in gen.recall_stream(w.B, w.H, w.T, w.dk, w.dv, w.seed, w.dtype))
+    beta = torch.ones((w.B, w.H, w.T), device="cuda")
+    o = torch.empty_like(v)
+    ms = time_calls(torch, lambda: kata.delta_fwd_into(q, k, v, beta, o, w.chunk), steps, warmup)
+    D, C, tiles = w.dk * (w.dk + 1) // 2, w.chunk, w.dv // 16
+    per_tile = 3 * 2 * D * 17 + 2 * 2 * C * w.dk + 2 * C * 17 + 2 * (C * 17 + 256)
+    flops = w.B * w.H * w.T * tiles * per_tile
+    return {"ms": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3), "alg_tflops": flops / (ms * 1e-3) / 1e12,
+            "vs_fp32_vector_peak": flops / (ms * 1e-3) / 1e12 / 157.3,
+            "workgroups": w.B * w.H * tiles, "beta": 1.0, "workload": "recall16k"}
+
+
 def box_peaks(torch):
     """Measured yardsticks on this GPU: a large bf16 GEMM through torch and a 1 GiB
     device-to-device copy (bytes read + written per second)."""
@@ -521,6 +543,7 @@ def main():
                                                    args.warmup)
         result["parts"]["recall16k"] = recall_forward(kata, torch, gen, min(args.steps, 10),
                                                       args.warmup)
+        result["parts"]["delta_recall16k"] = delta_forward(kata, torch, gen, 3, 1)
         dms, dgbs, dbytes = decode_bench(kata, torch)
         result["parts"]["decode"] = {"ms_per_step": dms, "alg_GBps": dgbs,
                                      "hbm_frac": dgbs / PEAK_HBM_GBS, "bytes_per_step": dbytes,

@@ -311,6 +311,39 @@ kata_status_t kata_decode_step(const void* q, const void* k, const void* v,
                                float* S, float* z, void* o,
                                int N, int d_k, int d_v, kata_dtype_t dtype, void* stream);
 
+/* DeltaKATA forward (causal): the delta-rule variant the explainers name for
+ * repeated-key overwrite (section 4; no formula is printed). Reading built:
+ * with the unit-norm lifted key kappa_t = phi(k_t) / |k_t|^2 (0 for k = 0) and
+ * a write strength beta_t, the numerator and denominator states form one
+ * augmented state A = [S | z] updated by the delta rule of DeltaNet with the
+ * value [v_t, 1]:
+ *     A_t = A_{t-1} + beta_t kappa_t ([v_t, 1] - kappa_t^T A_{t-1}),
+ *     o_t = phi(q_t).S_t / phi(q_t).z_t     (0 where the denominator is 0).
+ * beta = 1 makes the state return exactly v_t for the key k_t; mutually
+ * orthogonal unit keys with beta = 1 give kata_chunked_fwd's output. The
+ * erase can make weights negative, so outputs need not be convex combinations.
+ *   q, k [B,H,T,d_k]; v, o [B,H,T,d_v] (dtype) - as kata_chunked_fwd.
+ *   beta [B,H,T] (fp32, device) - write strengths, expected in [0, 1].
+ *   chunk - 16, 32 or 64: chunks are walked in order (the state transition is
+ *     matrix-affine); inside a chunk a unit lower-triangular system gives the
+ *     tokens' writes, solved in blocks of 16.
+ *   S0, z0 / S_out, z_out - optional initial / final state as kata_chunked_fwd
+ *     (the packed layout; both of a pair or neither).
+ * d_k in {16, 32}, d_v in {16, 32, 64}, fp32 or bf16 inputs, any T >= 0; fp32
+ * arithmetic throughout; no workspace. One workgroup per (batch, head, 16 value
+ * columns). Errors as kata_chunked_fwd (chunk 128: KATA_EUNSUPPORTED). */
+kata_status_t kata_delta_fwd(const void* q, const void* k, const void* v, const float* beta,
+                             void* o, int B, int H, int T, int d_k, int d_v, int chunk,
+                             kata_dtype_t dtype, const float* S0, const float* z0,
+                             float* S_out, float* z_out, void* stream);
+
+/* One DeltaKATA decode step for N rows: [S | z] += beta kappa ([v, 1] -
+ * kappa^T [S | z]) in place, then o = phi(q).S / phi(q).z. Shapes, dtypes and
+ * errors as kata_decode_step; beta [N] (fp32, device; NULL = KATA_EINVAL). */
+kata_status_t kata_decode_step_delta(const void* q, const void* k, const void* v,
+                                     const float* beta, float* S, float* z, void* o, int N,
+                                     int d_k, int d_v, kata_dtype_t dtype, void* stream);
+
 /* Bytes of the library's static device scratch (per GPU) used by
  * kata_chunked_fwd_noalloc. */
 #define KATA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

@@ -9,6 +9,7 @@
     o4 = kata.chunked_fwd(q, k, v, feature="identity")      # first-order feature
     o5 = kata.chunked_fwd_decay(q, k, v, log_decay)         # decay-gated
     kata.chunked_fwd_noalloc_into(q, k, v, o, 64, True)     # no workspace, allocates nothing
+    o6 = kata.delta_fwd(q, k, v, beta)                      # DeltaKATA (delta rule)
 
 The shared library is loaded on first use; calls raise if it is missing.
 """
@@ -16,6 +17,7 @@ from ._binding import (KataError, chunked_fwd, chunked_fwd_into, chunked_fwd_wor
                        chunked_fwd_decay, chunked_fwd_decay_into, chunked_fwd_decay_workspace,
                        decode_step, decode_step_decay, feature_dim, flash_fwd, lib, phi_dim,
                        scan_states, scan_states_into, chunked_fwd_noalloc_into,
-                       NOALLOC_SCRATCH_BYTES, prefix_depth, LIB_PATH)
+                       NOALLOC_SCRATCH_BYTES, prefix_depth, delta_fwd, delta_fwd_into,
+                       decode_step_delta, LIB_PATH)
 
 __version__ = "0.2.0"

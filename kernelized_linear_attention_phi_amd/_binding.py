@@ -15,7 +15,7 @@ __all__ = ["KataError", "lib", "chunked_fwd", "chunked_fwd_into", "chunked_fwd_w
            "scan_states", "flash_fwd", "decode_step", "phi_dim", "feature_dim",
            "chunked_fwd_decay", "chunked_fwd_decay_into", "chunked_fwd_decay_workspace",
            "decode_step_decay", "chunked_fwd_noalloc_into", "NOALLOC_SCRATCH_BYTES", "prefix_depth",
-           "LIB_PATH"]
+           "delta_fwd", "delta_fwd_into", "decode_step_delta", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkata.so")
 
@@ -88,6 +88,10 @@ def lib() -> ctypes.CDLL:
         L.kata_chunked_fwd_noalloc.restype = i
         L.kata_prefix_depth.argtypes = [i, i, i, i, i, i, i, i, i, i]
         L.kata_prefix_depth.restype = i
+        L.kata_delta_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, vp, vp]
+        L.kata_delta_fwd.restype = i
+        L.kata_decode_step_delta.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+        L.kata_decode_step_delta.restype = i
         _lib = L
     return _lib
 
@@ -447,3 +451,53 @@ def decode_step_decay(q, k, v, log_decay, S, z, out=None):
                                       _ptr(o), N, dk, dv, _dtype_code(q), _stream())
     _raise(st, "kata_decode_step_decay")
     return o
+
+
+# ---- DeltaKATA ---------------------------------------------------------------------
+
+def delta_fwd_into(q, k, v, beta, o, chunk, S0=None, z0=None, S_out=None, z_out=None):
+    """Raw kata_delta_fwd into preallocated outputs."""
+    _check_qkv(q, k, v, o)
+    _check_dev(beta)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if beta.dtype != torch.float32 or tuple(beta.shape) != (B, H, T):
+        raise ValueError("beta must be float32 [B,H,T]")
+    D = phi_dim(dk)
+    _check_state(S0, z0, (B, H), D, dv, "initial state")
+    _check_state(S_out, z_out, (B, H), D, dv, "final state")
+    st = lib().kata_delta_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(o), B, H, T, dk, dv,
+                              chunk, _dtype_code(q), _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out),
+                              _stream())
+    _raise(st, "kata_delta_fwd")
+
+
+def delta_fwd(q, k, v, beta, chunk=64, initial_state=None, return_state=False):
+    """DeltaKATA forward: the delta rule on [S | z] with unit-norm lifted keys and
+    write strengths beta [B,H,T] (fp32) - kata_delta_fwd."""
+    _check_qkv(q, k, v)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    D = phi_dim(dk)
+    S0, z0 = initial_state if initial_state is not None else (None, None)
+    S_out = z_out = None
+    if return_state:
+        S_out = torch.empty((B, H, D, dv), dtype=torch.float32, device=q.device)
+        z_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    o = torch.empty_like(v)
+    delta_fwd_into(q, k, v, beta.contiguous(), o, chunk, S0, z0, S_out, z_out)
+    return (o, (S_out, z_out)) if return_state else o
+
+
+def decode_step_delta(q, k, v, beta, S, z, out=None):
+    """One DeltaKATA decode step on rows [N, d]: beta [N] fp32; S, z updated in
+    place; returns o [N, d_v]."""
+    _check_rows(q, k, v, S, z, out, beta)
+    N, dk = q.shape
+    dv = v.shape[-1]
+    o = torch.empty_like(v) if out is None else out
+    st = lib().kata_decode_step_delta(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(z),
+                                      _ptr(o), N, dk, dv, _dtype_code(q), _stream())
+    _raise(st, "kata_decode_step_delta")
+    return o
+

@@ -657,6 +657,52 @@ kata_status_t kata_decode_step(const void* q, const void* k, const void* v, floa
                                           dtype == KATA_BF16, static_cast<hipStream_t>(stream)));
 }
 
+// ---- DeltaKATA ---------------------------------------------------------------
+
+kata_status_t kata_delta_fwd(const void* q, const void* k, const void* v, const float* beta,
+                             void* o, int B, int H, int T, int d_k, int d_v, int chunk,
+                             kata_dtype_t dtype, const float* S0, const float* z0, float* S_out,
+                             float* z_out, void* stream) {
+    Shape s;
+    kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s);
+    if (st != KATA_OK) return st;
+    if (!kata::delta_supported(s)) return KATA_EUNSUPPORTED;
+    if ((S0 == nullptr) != (z0 == nullptr)) return KATA_EINVAL;
+    if ((S_out == nullptr) != (z_out == nullptr)) return KATA_EINVAL;
+    const size_t BH = (size_t)B * H;
+    const bool empty = BH == 0 || T == 0;
+    if (!empty && (!q || !k || !v || !o || !beta)) return KATA_EINVAL;
+    for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)o,
+                          (const void*)beta, (const void*)S0, (const void*)z0, (const void*)S_out,
+                          (const void*)z_out})
+        if (p && !aligned16(p)) return KATA_EINVAL;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (empty) {
+        hipError_t e = hipSuccess;
+        if (S_out) {
+            e = kata::launch_copy_or_zero(S_out, S0, BH * s.D * s.dv, hs);
+            if (e == hipSuccess) e = kata::launch_copy_or_zero(z_out, z0, BH * s.D, hs);
+        }
+        return hip_status(e);
+    }
+    return hip_status(kata::launch_delta_fwd(s, q, k, v, beta, o, S0, z0, S_out, z_out, hs));
+}
+
+kata_status_t kata_decode_step_delta(const void* q, const void* k, const void* v,
+                                     const float* beta, float* S, float* z, void* o, int N,
+                                     int d_k, int d_v, kata_dtype_t dtype, void* stream) {
+    if (N < 0 || d_k < 0 || d_v < 0) return KATA_EINVAL;
+    if (dtype != KATA_F32 && dtype != KATA_BF16) return KATA_EINVAL;
+    if (!supported_dk(d_k) || !supported_dv(d_v)) return KATA_EUNSUPPORTED;
+    if (N == 0) return KATA_OK;
+    if (!q || !k || !v || !S || !z || !o || !beta) return KATA_EINVAL;
+    for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)S,
+                          (const void*)z, (const void*)o, (const void*)beta})
+        if (!aligned16(p)) return KATA_EINVAL;
+    return hip_status(kata::launch_delta_decode(q, k, v, beta, S, z, o, N, d_k, d_v,
+                                                dtype == KATA_BF16, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 // ---- allocation-free forward ------------------------------------------------

@@ -174,6 +174,16 @@ bool flash_supported(const Shape& s);
 hipError_t launch_flash_fwd(const Shape& s, const void* q, const void* k, const void* v, void* o,
                             int causal, hipStream_t st);
 
+// ---- DeltaKATA (delta rule on [S | z], fp32 arithmetic) ----
+bool delta_supported(const Shape& s);
+// beta [BH, T]; S0, z0 / S_out, z_out packed states or NULL; no workspace
+hipError_t launch_delta_fwd(const Shape& s, const void* q, const void* k, const void* v,
+                            const float* beta, void* o, const float* S0, const float* z0,
+                            float* S_out, float* z_out, hipStream_t st);
+hipError_t launch_delta_decode(const void* q, const void* k, const void* v, const float* beta,
+                               float* S, float* z, void* o, int N, int dk, int dv, bool bf16,
+                               hipStream_t st);
+
 // ---- decode ----
 // g: NULL, or [N] per-row log-decays (S = exp(g) S + phi(k) v^T, z likewise)
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g, float* S,

@@ -68,10 +68,11 @@ def _aug(S0, z0, B, H, D, dv):
     return A
 
 
-def delta_recurrent(q, k, v, beta, S0=None, z0=None):
+def delta_recurrent(q, k, v, beta, S0=None, z0=None, parts=False):
     """Token-by-token DeltaKATA. q, k [B,H,T,d], v [B,H,T,dv], beta [B,H,T].
     Returns (o [B,H,T,dv], S [B,H,D,dv], z [B,H,D]), the state after the last
-    token."""
+    token; with parts=True, (num [B,H,T,dv], den [B,H,T], S, z) instead, the
+    readout's numerator and denominator before the division."""
     q = np.asarray(q, np.float64)
     v = np.asarray(v, np.float64)
     beta = np.asarray(beta, np.float64)
@@ -82,6 +83,8 @@ def delta_recurrent(q, k, v, beta, S0=None, z0=None):
     kap = delta_kappa(k)
     fq = phi(q)
     o = np.zeros((B, H, T, dv))
+    num = np.zeros((B, H, T, dv))
+    den = np.zeros((B, H, T))
     for t in range(T):
         u = np.concatenate([v[:, :, t], np.ones((B, H, 1))], -1)          # [B,H,dv+1]
         kt = kap[:, :, t]                                                   # [B,H,D]
@@ -89,6 +92,10 @@ def delta_recurrent(q, k, v, beta, S0=None, z0=None):
         A = A + beta[:, :, t, None, None] * kt[..., None] * (u - erase)[:, :, None, :]
         r = np.einsum("bhp,bhpc->bhc", fq[:, :, t], A)
         o[:, :, t] = _safe_ratio(r[..., :dv], r[..., dv])
+        num[:, :, t] = r[..., :dv]
+        den[:, :, t] = r[..., dv]
+    if parts:
+        return num, den, A[..., :dv], A[..., dv]
     return o, A[..., :dv], A[..., dv]
 
 

@@ -278,3 +278,22 @@ def test_prefix_depth(L):
     assert dep(1, 1, 64, 16, 64, 64, F32, PSD, SEQUENTIAL, 0) == -1
     assert dep(1, 1, 64, 16, 64, 64, BF16, PSD, 7, 0) == -1
     assert dep(0, 1, 64, 16, 64, 64, BF16, PSD, TREE, 0) == 0
+
+
+def test_delta_rejects_before_launch(L):
+    dfw = L.kata_delta_fwd
+    args = lambda **kw: (kw.get("q", FAKE), FAKE, FAKE, kw.get("beta", FAKE), FAKE, 1, 2,
+                         kw.get("T", 64), kw.get("dk", 16), kw.get("dv", 64), kw.get("C", 64),
+                         kw.get("dtype", BF16), kw.get("S0", None), None, None, None, None)
+    assert dfw(*args(C=128)) == EUNSUPPORTED
+    assert dfw(*args(dk=24)) == EUNSUPPORTED
+    assert dfw(*args(dv=48)) == EUNSUPPORTED
+    assert dfw(*args(beta=None)) == EINVAL
+    assert dfw(*args(q=MISALIGNED)) == EINVAL
+    assert dfw(*args(S0=FAKE)) == EINVAL             # S0 without z0
+    assert dfw(*args(dtype=5)) == EINVAL
+    assert dfw(*args(T=0, q=None, beta=None)) == OK   # empty: nothing launched
+    dec = L.kata_decode_step_delta
+    assert dec(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 16, 64, BF16, None) == EINVAL
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 12, 64, BF16, None) == EUNSUPPORTED
+    assert dec(None, None, None, None, None, None, None, 0, 16, 64, BF16, None) == OK
