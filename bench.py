@@ -438,6 +438,8 @@ def main():
                     help="with --quick: the forward workload to time (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scales HBM counters)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode steps (2048 rows, then 32768 rows; for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -457,6 +459,17 @@ def main():
     import kernelized_linear_attention_phi_amd as kata
     from kernelized_linear_attention_phi_amd import inputs as gen
     kata.lib()
+    if args.decode_only:
+        out = {}
+        for n_seq, steps in ((512, 64), (8192, 16)):
+            dms, dgbs, dbytes = decode_bench(kata, torch, steps=steps, n_seq=n_seq, reps=1)
+            out[f"rows{4 * n_seq}"] = {"ms_per_step": dms, "alg_GBps": dgbs, "bytes_per_step": dbytes,
+                                       "steps": steps}
+        print(json.dumps(out), flush=True)
+        return
+
+    def progress(part):
+        print(f"bench: {part} done", file=sys.stderr, flush=True)
 
     def load(name):
         w = gen.WORKLOADS[name]
@@ -469,6 +482,7 @@ def main():
         sys.exit(2)
     w, host_in, dev_in = load(args.workload)
     ms, wall_ms, phases = time_forward(kata, torch, w, *dev_in, args.steps, args.warmup)
+    progress(w.name)
     tok = w.B * w.T
     value = tok / (ms * 1e-3)
     th = w.B * w.H * w.T
@@ -495,6 +509,7 @@ def main():
                               "through the timed steps, so no step's inputs are resident in "
                               "the 256 MB memory-side cache"}
         del sets
+        progress("cold inputs")
     traffic = None
     if w.name == "fwd131k" and os.path.exists(COUNTERS_FILE):
         c = json.load(open(COUNTERS_FILE))
@@ -533,17 +548,23 @@ def main():
             "mfma_util_alg": fl3 / (ms3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "mfma_util_alg_output_phase": fl3 / (ph3["output"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         del dev3
+        progress("fwd32k")
         result["parts"]["fwd4k"] = quadratic_vs_chunked(kata, torch, gen, "fwd4k", args.steps,
                                                         args.warmup)
+        progress("fwd4k")
         result["parts"]["scan_vs_sequential"] = scan_vs_sequential(
             kata, torch, gen, ("fwd4k", "fwd32k", "fwd131k"), min(args.steps, 10), args.warmup)
+        progress("scan_vs_sequential")
         result["parts"]["scan_states"] = scan_states_bench(kata, torch, gen, ["fwd131k", "fwd32k"],
                                                            min(args.steps, 10), min(args.warmup, 3))
+        progress("scan_states")
         result["parts"]["decay_gate"] = decay_gate(kata, torch, gen, min(args.steps, 10),
                                                    args.warmup)
+        progress("decay_gate")
         result["parts"]["recall16k"] = recall_forward(kata, torch, gen, min(args.steps, 10),
                                                       args.warmup)
         result["parts"]["delta_recall16k"] = delta_forward(kata, torch, gen, 3, 1)
+        progress("recall16k and delta")
         dms, dgbs, dbytes = decode_bench(kata, torch)
         result["parts"]["decode"] = {"ms_per_step": dms, "alg_GBps": dgbs,
                                      "hbm_frac": dgbs / PEAK_HBM_GBS, "bytes_per_step": dbytes,
@@ -561,6 +582,7 @@ def main():
         cold["note"] = ("states of 290 MB and 1.16 GB, beyond the 256 MB memory-side cache "
                         "(the larger one four times over), swept once per step")
         result["parts"]["decode_cold"] = cold
+        progress("decode")
         peaks = box_peaks(torch)
         result["parts"]["box_peaks"] = peaks
         result["roofline"]["frac_vs_measured_copy"] = achieved / peaks["copy_GBps"]
