@@ -7,3 +7,4 @@ from .kata_oracle import *  # noqa: F401,F403
 from .first_order_oracle import *  # noqa: F401,F403
 from .decay_oracle import *  # noqa: F401,F403
 from .delta_oracle import *  # noqa: F401,F403
+from .factored_oracle import *  # noqa: F401,F403
