@@ -344,6 +344,58 @@ kata_status_t kata_decode_step_delta(const void* q, const void* k, const void* v
                                      const float* beta, float* S, float* z, void* o, int N,
                                      int d_k, int d_v, kata_dtype_t dtype, void* stream);
 
+/* Factored PSD features, KATA-Mg and KATA-Sigma-g: the variants the
+ * explainers name (technical summary 2.3, "Variants": multiple PSD factors and
+ * summed PSD factors, trading state size against packing efficiency) without
+ * printing a construction. Reading built: q and k (width d_k) are cut into g
+ * contiguous factors x_a = x[a p, (a+1) p), p = d_k / g, each lifted to the
+ * rank-one PSD matrix x_a x_a^T of section 2.2.
+ *   KATA_FACTORS_MULTI (KATA-Mg): the factors stay apart, feature
+ *     diag(x_1 x_1^T, ..., x_g x_g^T), weight sum_a (q_a . k_a)^2; packed as the
+ *     g packed lifts of the factors one after the other (D = g p(p+1)/2).
+ *   KATA_FACTORS_SUMMED (KATA-Sigma-g): the factors summed into one p x p
+ *     matrix sum_a x_a x_a^T, weight sum_{a,b} (q_a . k_b)^2; packed like one
+ *     lift of width p (D = p(p+1)/2).
+ * Each factor's lift uses the packing above (row-major upper triangle, sqrt(2)
+ * off the diagonal). Both weights are sums of squares, and g = 1 is plain KATA
+ * for both. The output is the normalised form of kata_chunked_fwd with these
+ * weights. */
+typedef enum { KATA_FACTORS_MULTI = 0, KATA_FACTORS_SUMMED = 1 } kata_factors_t;
+
+/* Feature dimension D of a factored feature; -1 when d < 0, g < 1, g does not
+ * divide d, or the kind is unknown. */
+int kata_factored_dim(int d, int g, kata_factors_t kind);
+
+/* Bytes of workspace kata_factored_fwd needs (0 if none, or for an invalid or
+ * unsupported problem). */
+size_t kata_factored_fwd_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                   kata_dtype_t dtype, int causal, int g, kata_factors_t kind);
+
+/* Chunked forward (causal, or full with causal = 0) with a factored feature.
+ * Arguments, layouts and errors as kata_chunked_fwd; S0, z0, S_out, z_out are
+ * [B,H,D,d_v] / [B,H,D] in the factored packed layout (D = kata_factored_dim).
+ * g = 1 is kata_chunked_fwd itself (same workspace). For g > 1 the matrix-core
+ * path serves bf16 inputs, chunk 64, d_v 32 or 64, and (d_k, g) in {(16, 2),
+ * (16, 4), (32, 4)} for both kinds and (32, 2) summed (D <= 144); other shapes
+ * return KATA_EUNSUPPORTED, g not dividing d_k KATA_EINVAL. Intra-chunk
+ * weights are formed from the factors' inner products in fp32; the lifted
+ * features and the state enter the matrix cores as split bf16 operands
+ * (hi + lo), so few keys in the prefix cost no accuracy. */
+kata_status_t kata_factored_fwd(const void* q, const void* k, const void* v, void* o,
+                                int B, int H, int T, int d_k, int d_v, int chunk, int causal,
+                                kata_dtype_t dtype, int g, kata_factors_t kind,
+                                const float* S0, const float* z0, float* S_out, float* z_out,
+                                void* workspace, size_t ws_bytes, void* stream);
+
+/* One recurrent decode step with a factored feature, as kata_decode_step:
+ * S [N,D,d_v], z [N,D] updated in place (S += phi(k) v^T, z += phi(k)), then
+ * o = phi(q).S / phi(q).z. fp32 or bf16 inputs; d_v in {16, 32, 64}; (d_k, g)
+ * as kata_factored_fwd; g = 1 is kata_decode_step. */
+kata_status_t kata_decode_step_factored(const void* q, const void* k, const void* v,
+                                        float* S, float* z, void* o, int N, int d_k, int d_v,
+                                        int g, kata_factors_t kind, kata_dtype_t dtype,
+                                        void* stream);
+
 /* Bytes of the library's static device scratch (per GPU) used by
  * kata_chunked_fwd_noalloc. */
 #define KATA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

@@ -10,6 +10,7 @@
     o5 = kata.chunked_fwd_decay(q, k, v, log_decay)         # decay-gated
     kata.chunked_fwd_noalloc_into(q, k, v, o, 64, True)     # no workspace, allocates nothing
     o6 = kata.delta_fwd(q, k, v, beta)                      # DeltaKATA (delta rule)
+    o7 = kata.factored_fwd(q, k, v, 2, "multi")             # KATA-Mg / "summed": KATA-Sigma-g
 
 The shared library is loaded on first use; calls raise if it is missing.
 """
@@ -18,6 +19,7 @@ from ._binding import (KataError, chunked_fwd, chunked_fwd_into, chunked_fwd_wor
                        decode_step, decode_step_decay, feature_dim, flash_fwd, lib, phi_dim,
                        scan_states, scan_states_into, chunked_fwd_noalloc_into,
                        NOALLOC_SCRATCH_BYTES, prefix_depth, delta_fwd, delta_fwd_into,
-                       decode_step_delta, LIB_PATH)
+                       decode_step_delta, factored_dim, factored_fwd, factored_fwd_into,
+                       factored_fwd_workspace, decode_step_factored, LIB_PATH)
 
 __version__ = "0.2.0"

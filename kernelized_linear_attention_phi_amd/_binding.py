@@ -92,6 +92,15 @@ def lib() -> ctypes.CDLL:
         L.kata_delta_fwd.restype = i
         L.kata_decode_step_delta.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
         L.kata_decode_step_delta.restype = i
+        L.kata_factored_dim.argtypes = [i, i, i]
+        L.kata_factored_dim.restype = i
+        L.kata_factored_fwd_workspace.argtypes = [i, i, i, i, i, i, i, i, i, i]
+        L.kata_factored_fwd_workspace.restype = sz
+        L.kata_factored_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i,
+                                        vp, vp, vp, vp, vp, sz, vp]
+        L.kata_factored_fwd.restype = i
+        L.kata_decode_step_factored.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+        L.kata_decode_step_factored.restype = i
         _lib = L
     return _lib
 
@@ -356,9 +365,10 @@ def decode_step(q, k, v, S, z, out=None):
     return o
 
 
-def _check_rows(q, k, v, S, z, out=None, log_decay=None):
+def _check_rows(q, k, v, S, z, out=None, log_decay=None, D=None):
     """Decode-step arguments: q, k [N,d_k], v [N,d_v] of one dtype, S [N,D,d_v]
-    and z [N,D] float32, out like v, log_decay [N] float32."""
+    and z [N,D] float32 (D the PSD lift's unless given), out like v,
+    log_decay [N] float32."""
     _check_dev(q, k, v, S, z, out, log_decay)
     if q.dim() != 2 or k.shape != q.shape or v.dim() != 2 or v.shape[0] != q.shape[0]:
         raise ValueError("expected q, k [N,d_k] and v [N,d_v]")
@@ -366,7 +376,7 @@ def _check_rows(q, k, v, S, z, out=None, log_decay=None):
         raise TypeError("q, k, v must share a dtype")
     _dtype_code(q)
     N, dk = q.shape
-    _check_state(S, z, (N,), phi_dim(dk), v.shape[1], "decode state")
+    _check_state(S, z, (N,), phi_dim(dk) if D is None else D, v.shape[1], "decode state")
     if out is not None and (out.shape != v.shape or out.dtype != v.dtype):
         raise ValueError("out must match v in shape and dtype")
     if log_decay is not None and (log_decay.dtype != torch.float32 or tuple(log_decay.shape) != (N,)):
@@ -501,3 +511,89 @@ def decode_step_delta(q, k, v, beta, S, z, out=None):
     _raise(st, "kata_decode_step_delta")
     return o
 
+
+
+# ---- factored PSD features (KATA-Mg "multi", KATA-Sigma-g "summed") ---------------
+
+FACTORS = {"multi": 0, "summed": 1}      # kata_factors_t
+
+
+def _factors(g, kind):
+    if kind not in FACTORS:
+        raise ValueError(f"kind in {sorted(FACTORS)}, got {kind!r}")
+    if int(g) < 1:
+        raise ValueError(f"g must be >= 1, got {g}")
+    return int(g), FACTORS[kind]
+
+
+def factored_dim(d: int, g: int, kind: str) -> int:
+    """Feature dimension of a factored feature (-1 if g does not divide d)."""
+    g, kd = _factors(g, kind)
+    return lib().kata_factored_dim(d, g, kd)
+
+
+def factored_fwd_workspace(B, H, T, dk, dv, chunk, dtype_code, causal, g, kind) -> int:
+    g, kd = _factors(g, kind)
+    return lib().kata_factored_fwd_workspace(B, H, T, dk, dv, chunk, dtype_code, int(bool(causal)),
+                                             g, kd)
+
+
+def factored_fwd_into(q, k, v, o, g, kind, chunk, causal, workspace, S0=None, z0=None,
+                      S_out=None, z_out=None):
+    """Raw kata_factored_fwd call: every buffer preallocated by the caller."""
+    _check_qkv(q, k, v, o)
+    _check_dev(workspace)
+    gg, kd = _factors(g, kind)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    D = lib().kata_factored_dim(dk, gg, kd)
+    if D < 0:
+        raise ValueError(f"g = {g} must divide d_k = {dk}")
+    _check_state(S0, z0, (B, H), D, dv, "initial state")
+    _check_state(S_out, z_out, (B, H), D, dv, "final state")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().kata_factored_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, T, dk, dv, chunk,
+                                 int(bool(causal)), _dtype_code(q), gg, kd, _ptr(S0), _ptr(z0),
+                                 _ptr(S_out), _ptr(z_out), _ptr(workspace), ws_bytes, _stream())
+    _raise(st, "kata_factored_fwd")
+
+
+def factored_fwd(q, k, v, g, kind, chunk=64, causal=True, initial_state=None, return_state=False):
+    """KATA forward with a factored PSD feature: q, k cut into g contiguous
+    factors; kind "multi" (KATA-Mg, factors kept apart) or "summed"
+    (KATA-Sigma-g, factors summed). States [B,H,D,d_v] / [B,H,D] with
+    D = factored_dim(d_k, g, kind)."""
+    _check_qkv(q, k, v)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    D = factored_dim(dk, g, kind)
+    if D < 0:
+        raise ValueError(f"g = {g} must divide d_k = {dk}")
+    S0 = z0 = S_out = z_out = None
+    if initial_state is not None:
+        S0, z0 = initial_state
+    if return_state:
+        S_out = torch.empty((B, H, D, dv), dtype=torch.float32, device=q.device)
+        z_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    o = torch.empty_like(v)
+    nbytes = factored_fwd_workspace(B, H, T, dk, dv, chunk, _dtype_code(q), causal, g, kind)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+    factored_fwd_into(q, k, v, o, g, kind, chunk, causal, ws, S0, z0, S_out, z_out)
+    return (o, (S_out, z_out)) if return_state else o
+
+
+def decode_step_factored(q, k, v, S, z, g, kind, out=None):
+    """One decode step with a factored feature: rows [N, d]; S [N,D,d_v],
+    z [N,D] updated in place; returns o [N, d_v]."""
+    gg, kd = _factors(g, kind)
+    D = lib().kata_factored_dim(q.shape[-1], gg, kd)
+    if D < 0:
+        raise ValueError(f"g = {g} must divide d_k = {q.shape[-1]}")
+    _check_rows(q, k, v, S, z, out, D=D)
+    N, dk = q.shape
+    dv = v.shape[-1]
+    o = torch.empty_like(v) if out is None else out
+    st = lib().kata_decode_step_factored(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(o), N,
+                                         dk, dv, gg, kd, _dtype_code(q), _stream())
+    _raise(st, "kata_decode_step_factored")
+    return o

@@ -703,6 +703,135 @@ kata_status_t kata_decode_step_delta(const void* q, const void* k, const void* v
                                                 dtype == KATA_BF16, static_cast<hipStream_t>(stream)));
 }
 
+// ---- factored PSD features (KATA-Mg, KATA-Sigma-g) ----------------------------
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of kata_factored_fwd: segment records [BH, NSEG, REC], then the
+// initial-state record and the total record per head (records in the
+// first-order layout with the factored feature's rows).
+struct FactPlan {
+    bool ok;
+    int G, NSEG, REC, D;
+    size_t init_off, total_off, bytes;
+};
+
+FactPlan plan_fact(const Shape& s, int g, bool summed) {
+    FactPlan p{};
+    p.ok = kata::factored_supported(s, g, summed);
+    const size_t BH = (size_t)s.B * s.H;
+    if (!p.ok || BH == 0 || s.NC == 0) return p;
+    p.D = kata::factored_dim(s.dk, g, summed);
+    // four-wavefront workgroups, about two per compute unit
+    p.G = std::min(segment_chunks(s, 512, 0), s.NC);
+    p.NSEG = (s.NC + p.G - 1) / p.G;
+    p.REC = kata::factored_record_floats(s.dk, s.dv, g, summed);
+    p.init_off = align256(BH * p.NSEG * p.REC * sizeof(float));
+    p.total_off = p.init_off + align256(BH * p.REC * sizeof(float));
+    p.bytes = p.total_off + align256(BH * p.REC * sizeof(float));
+    return p;
+}
+
+bool valid_factors(int g, kata_factors_t kind) {
+    return g >= 1 && (kind == KATA_FACTORS_MULTI || kind == KATA_FACTORS_SUMMED);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kata_factored_dim(int d, int g, kata_factors_t kind) {
+    if (d < 0 || !valid_factors(g, kind) || d % g) return -1;
+    return kata::factored_dim(d, g, kind == KATA_FACTORS_SUMMED);
+}
+
+size_t kata_factored_fwd_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                   kata_dtype_t dtype, int causal, int g, kata_factors_t kind) {
+    if (!valid_factors(g, kind)) return 0;
+    if (g == 1) return kata_chunked_fwd_workspace(B, H, T, d_k, d_v, chunk, dtype, causal);
+    Shape s;
+    if (make_shape(B, H, T, d_k, d_v, chunk, dtype, &s) != KATA_OK || d_k % g) return 0;
+    return plan_fact(s, g, kind == KATA_FACTORS_SUMMED).bytes;
+}
+
+kata_status_t kata_factored_fwd(const void* q, const void* k, const void* v, void* o, int B,
+                                int H, int T, int d_k, int d_v, int chunk, int causal,
+                                kata_dtype_t dtype, int g, kata_factors_t kind, const float* S0,
+                                const float* z0, float* S_out, float* z_out, void* workspace,
+                                size_t ws_bytes, void* stream) {
+    if (!valid_factors(g, kind)) return KATA_EINVAL;
+    if (g == 1)
+        return kata_chunked_fwd(q, k, v, o, B, H, T, d_k, d_v, chunk, causal, dtype, S0, z0, S_out,
+                                z_out, workspace, ws_bytes, stream);
+    Shape s;
+    kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s);
+    if (st != KATA_OK) return st;
+    if (d_k % g) return KATA_EINVAL;
+    const bool summed = kind == KATA_FACTORS_SUMMED;
+    s.D = kata::factored_dim(d_k, g, summed);
+    if ((S0 == nullptr) != (z0 == nullptr)) return KATA_EINVAL;
+    if ((S_out == nullptr) != (z_out == nullptr)) return KATA_EINVAL;
+    const size_t BH = (size_t)B * H;
+    const bool empty = BH == 0 || T == 0;
+    if (!empty && (!q || !k || !v || !o)) return KATA_EINVAL;
+    for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)o,
+                          (const void*)S0, (const void*)z0, (const void*)S_out,
+                          (const void*)z_out, (const void*)workspace})
+        if (p && !aligned16(p)) return KATA_EINVAL;
+    const FactPlan plan = plan_fact(s, g, summed);
+    if (!plan.ok) return KATA_EUNSUPPORTED;
+    if (ws_bytes < plan.bytes || (plan.bytes && !workspace)) return KATA_EWORKSPACE;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const size_t nS = (size_t)s.D * s.dv, nz = s.D;
+    if (empty) {
+        hipError_t e = hipSuccess;
+        if (S_out) {
+            e = kata::launch_copy_or_zero(S_out, S0, BH * nS, hs);
+            if (e == hipSuccess) e = kata::launch_copy_or_zero(z_out, z0, BH * nz, hs);
+        }
+        return hip_status(e);
+    }
+    char* ws = static_cast<char*>(workspace);
+    float* rec = reinterpret_cast<float*>(ws);
+    float* init = reinterpret_cast<float*>(ws + plan.init_off);
+    float* total = reinterpret_cast<float*>(ws + plan.total_off);
+    hipError_t e = hipSuccess;
+    if (S0) e = kata::launch_fact_record_from_packed(init, S0, z0, s.D, s.dv, plan.REC, (int)BH, hs);
+    if (e == hipSuccess)
+        e = kata::launch_fact_seg_state(s, g, summed, k, v, rec, plan.G, plan.NSEG, hs);
+    // exclusive prefix over segments in place; the inclusive total goes to the
+    // packed final state (when asked for) and, for the non-causal output, to
+    // the total record
+    const kata::RecordExport ex{kata::kRecIdent, s.D, s.dv, S_out, z_out};
+    if (e == hipSuccess)
+        e = kata::launch_scan_records(rec, (int)BH, plan.NSEG, plan.REC, S0 ? init : nullptr,
+                                      causal ? nullptr : total, nullptr, hs, S_out ? &ex : nullptr);
+    if (e == hipSuccess)
+        e = kata::launch_fact_fwd(s, g, summed, q, k, v, causal ? rec : total, o, causal, plan.G,
+                                  plan.NSEG, hs);
+    return hip_status(e);
+}
+
+kata_status_t kata_decode_step_factored(const void* q, const void* k, const void* v, float* S,
+                                        float* z, void* o, int N, int d_k, int d_v, int g,
+                                        kata_factors_t kind, kata_dtype_t dtype, void* stream) {
+    if (N < 0 || d_k < 0 || d_v < 0 || !valid_factors(g, kind)) return KATA_EINVAL;
+    if (dtype != KATA_F32 && dtype != KATA_BF16) return KATA_EINVAL;
+    if (g == 1) return kata_decode_step(q, k, v, S, z, o, N, d_k, d_v, dtype, stream);
+    if (d_k % g) return KATA_EINVAL;
+    const bool summed = kind == KATA_FACTORS_SUMMED;
+    if (!kata::factored_decode_supported(d_k, d_v, g, summed)) return KATA_EUNSUPPORTED;
+    if (N == 0) return KATA_OK;
+    if (!q || !k || !v || !S || !z || !o) return KATA_EINVAL;
+    for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)S,
+                          (const void*)z, (const void*)o})
+        if (!aligned16(p)) return KATA_EINVAL;
+    return hip_status(kata::launch_fact_decode(q, k, v, S, z, o, N, d_k, d_v, g, summed,
+                                               dtype == KATA_BF16, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 // ---- allocation-free forward ------------------------------------------------

@@ -71,7 +71,7 @@ int scan_levels(int NR, int method);
 constexpr int kRecNone = 0, kRecPsd16 = 1, kRecPsd32 = 2, kRecIdent = 3;
 struct RecordExport {
     int layout;      // kRecPsd16, kRecPsd32 or kRecIdent
-    int dk, dv;
+    int dk, dv;      // kRecIdent: dk = the feature count (rows) of the record
     float* S;        // [nseq, D, dv]
     float* z;        // [nseq, D]
 };
@@ -183,6 +183,28 @@ hipError_t launch_delta_fwd(const Shape& s, const void* q, const void* k, const 
 hipError_t launch_delta_decode(const void* q, const void* k, const void* v, const float* beta,
                                float* S, float* z, void* o, int N, int dk, int dv, bool bf16,
                                hipStream_t st);
+
+// ---- factored PSD features (KATA-Mg: summed = false, KATA-Sigma-g: summed = true) ----
+// G factors of width d_k / G; bf16, chunk 64, d_v 32 or 64; feature dimension
+// at most 144 (d_k 16 with G 2 or 4, d_k 32 with G 4, d_k 32 with G 2 summed).
+int factored_dim(int dk, int G, bool summed);
+bool factored_supported(const Shape& s, int G, bool summed);
+bool factored_decode_supported(int dk, int dv, int G, bool summed);
+// floats per record: feature tiles x (value tiles + z tile) x 256, layout of
+// the first-order records (kRecIdent export with dk = the feature dimension)
+int factored_record_floats(int dk, int dv, int G, bool summed);
+hipError_t launch_fact_seg_state(const Shape& s, int G, bool summed, const void* k, const void* v,
+                                 float* rec, int Gs, int NSEG, hipStream_t st);
+hipError_t launch_fact_fwd(const Shape& s, int G, bool summed, const void* q, const void* k,
+                           const void* v, const float* prefix, void* o, int causal, int Gs,
+                           int NSEG, hipStream_t st);
+hipError_t launch_fact_record_from_packed(float* rec, const float* S, const float* z, int D,
+                                          int dv, int REC, int nrec, hipStream_t st);
+hipError_t launch_fact_record_to_packed(const float* rec, float* S, float* z, int D, int dv,
+                                        int REC, int nrec, hipStream_t st);
+hipError_t launch_fact_decode(const void* q, const void* k, const void* v, float* S, float* z,
+                              void* o, int N, int dk, int dv, int G, bool summed, bool bf16,
+                              hipStream_t st);
 
 // ---- decode ----
 // g: NULL, or [N] per-row log-decays (S = exp(g) S + phi(k) v^T, z likewise)

@@ -72,9 +72,10 @@ __device__ __forceinline__ int rec32_to_packed(int idx, int NTV, int* col, float
     return i * DK - i * (i - 1) / 2 + (j - i);
 }
 
-// First-order record (units (at, u) of 256 floats, u = NTV the z tile whose
-// column 0 holds z): element e -> feature a, value column, and whether it is in
-// the z tile.
+// First-order and factored-feature record (units (at, u) of 256 floats, u = NTV
+// the z tile whose column 0 holds z): element e -> feature a, value column, and
+// whether it is in the z tile. The last feature tile may run past the feature
+// count (its rows stay zero).
 __device__ __forceinline__ void rec1_coords(int e, int NTV, int* a, int* col, bool* zt) {
     const int unit = e / 256, lane = (e % 256) / 4, r = e % 4;
     const int at = unit / (NTV + 1), u = unit % (NTV + 1);
@@ -90,6 +91,7 @@ __device__ __forceinline__ void export_element(const RecordExport& x, size_t b, 
         int a, col;
         bool zt;
         rec1_coords(idx, NTV, &a, &col, &zt);
+        if (a >= x.dk) return;                     // rows past the feature count
         if (!zt) x.S[(b * x.dk + a) * x.dv + col] = val;
         else if (col == 0) x.z[b * x.dk + a] = val;
         return;

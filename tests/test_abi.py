@@ -297,3 +297,56 @@ def test_delta_rejects_before_launch(L):
     assert dec(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 16, 64, BF16, None) == EINVAL
     assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 12, 64, BF16, None) == EUNSUPPORTED
     assert dec(None, None, None, None, None, None, None, 0, 16, 64, BF16, None) == OK
+
+
+def test_factored_dim_and_workspace(L):
+    MULTI, SUMMED = 0, 1
+    assert L.kata_factored_dim(16, 2, MULTI) == 72 and L.kata_factored_dim(16, 2, SUMMED) == 36
+    assert L.kata_factored_dim(16, 4, MULTI) == 40 and L.kata_factored_dim(16, 4, SUMMED) == 10
+    assert L.kata_factored_dim(32, 4, MULTI) == 144 and L.kata_factored_dim(32, 2, SUMMED) == 136
+    assert L.kata_factored_dim(16, 1, MULTI) == 136 == L.kata_factored_dim(16, 1, SUMMED)
+    assert L.kata_factored_dim(16, 3, MULTI) == -1 and L.kata_factored_dim(16, 0, MULTI) == -1
+    assert L.kata_factored_dim(16, 2, 7) == -1 and L.kata_factored_dim(-1, 1, MULTI) == -1
+    ws = L.kata_factored_fwd_workspace
+    # g = 1 is the plain forward's workspace
+    assert ws(1, 8, 4096, 16, 64, 64, BF16, 1, 1, MULTI) == L.kata_chunked_fwd_workspace(
+        1, 8, 4096, 16, 64, 64, BF16, 1)
+    # segment records + initial + total record per head: 512 segments of
+    # 5 tiles x 5 units x 256 floats for d_k 16, g 2, multi (72 features)
+    B, H, T = 1, 8, 131072
+    rec = 5 * 5 * 256 * 4
+    assert ws(B, H, T, 16, 64, 64, BF16, 1, 2, MULTI) >= (512 + 2 * B * H) * rec
+    assert ws(B, H, T, 16, 64, 64, F32, 1, 2, MULTI) == 0          # bf16 only
+    assert ws(B, H, T, 16, 64, 32, BF16, 1, 2, MULTI) == 0         # chunk 64 only
+    assert ws(B, H, T, 32, 64, 64, BF16, 1, 2, MULTI) == 0         # 272 features: not built
+    assert ws(B, H, T, 16, 64, 64, BF16, 1, 3, MULTI) == 0         # 3 does not divide 16
+
+
+def test_factored_rejects_before_launch(L):
+    MULTI, SUMMED = 0, 1
+    fw = L.kata_factored_fwd
+    args = lambda **kw: (kw.get("q", FAKE), FAKE, FAKE, FAKE, 1, 2, kw.get("T", 256),
+                         kw.get("dk", 16), kw.get("dv", 64), kw.get("C", 64), 1,
+                         kw.get("dtype", BF16), kw.get("g", 2), kw.get("kind", MULTI),
+                         kw.get("S0", None), None, None, None, kw.get("ws", FAKE),
+                         kw.get("wsb", 1 << 30), None)
+    assert fw(*args(g=3)) == EINVAL
+    assert fw(*args(g=0)) == EINVAL
+    assert fw(*args(kind=5)) == EINVAL
+    assert fw(*args(dtype=F32)) == EUNSUPPORTED
+    assert fw(*args(C=32)) == EUNSUPPORTED
+    assert fw(*args(dv=16)) == EUNSUPPORTED
+    assert fw(*args(dk=32, g=2, kind=MULTI)) == EUNSUPPORTED
+    assert fw(*args(dk=24)) == EUNSUPPORTED
+    assert fw(*args(q=MISALIGNED)) == EINVAL
+    assert fw(*args(S0=FAKE)) == EINVAL                            # S0 without z0
+    assert fw(*args(wsb=16)) == EWORKSPACE
+    assert fw(*args(ws=None)) == EWORKSPACE
+    assert fw(*args(T=0, q=None, ws=None, wsb=0)) == OK              # empty: nothing launched
+    assert fw(*args(g=1, C=48)) == EUNSUPPORTED                     # g = 1: kata_chunked_fwd
+    dec = L.kata_decode_step_factored
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 64, 3, MULTI, BF16, None) == EINVAL
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 64, 2, MULTI, BF16, None) == EUNSUPPORTED
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 48, 2, SUMMED, BF16, None) == EUNSUPPORTED
+    assert dec(MISALIGNED, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 64, 2, SUMMED, F32, None) == EINVAL
+    assert dec(None, None, None, None, None, None, 0, 16, 64, 2, SUMMED, BF16, None) == OK
