@@ -342,6 +342,37 @@ def delta_forward(kata, torch, gen, steps, warmup):
             "workgroups": w.B * w.H * tiles, "beta": 1.0, "workload": "recall16k"}
 
 
+def factored_forward(kata, torch, gen, steps, warmup):
+    """KATA-Mg ("multi") and KATA-Sigma-g ("summed") through kata_factored_fwd
+    (state export included) on the fwd131k inputs (B=1, H=8, T=131072, d_k=16,
+    d_v=64, C=64) with 2 and 4 factors, and on the fwd32k inputs (B=1, H=16,
+    T=32768, d_k=32, d_v=64) at C=64: ms, tokens/s and the algorithmic HBM rate
+    of the step (q, k, v read once, o written once)."""
+    out = {}
+    for name, cases in (("fwd131k", ((2, "multi"), (2, "summed"), (4, "multi"), (4, "summed"))),
+                        ("fwd32k", ((4, "multi"), (4, "summed"), (2, "summed")))):
+        w = gen.WORKLOADS[name]
+        to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+        q, k, v = (to(a) for a in gen.gaussian_qkv(w.B, w.H, w.T, w.dk, w.dv, w.seed, w.dtype))
+        o = torch.empty_like(v)
+        nbytes = (2 * w.dk + 2 * w.dv) * 2 * w.B * w.H * w.T
+        for g, kind in cases:
+            D = kata.factored_dim(w.dk, g, kind)
+            S = torch.empty((w.B, w.H, D, w.dv), dtype=torch.float32, device="cuda")
+            z = torch.empty((w.B, w.H, D), dtype=torch.float32, device="cuda")
+            wsb = kata.factored_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, 64, 1, True, g, kind)
+            ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+            ms = time_calls(torch, lambda: kata.factored_fwd_into(q, k, v, o, g, kind, 64, True, ws,
+                                                                  S_out=S, z_out=z), steps, warmup)
+            out[f"{name}/{kind}{g}"] = {
+                "ms": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3), "features": D,
+                "alg_GBps": nbytes / (ms * 1e-3) / 1e9,
+                "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            del ws, S, z
+        del q, k, v, o
+    return out
+
+
 def box_peaks(torch):
     """Measured yardsticks on this GPU: a large bf16 GEMM through torch and a 1 GiB
     device-to-device copy (bytes read + written per second)."""
@@ -440,6 +471,8 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy (scales HBM counters)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode steps (2048 rows, then 32768 rows; for counter runs)")
+    ap.add_argument("--factored-only", action="store_true",
+                    help="only the KATA-Mg / KATA-Sigma-g forwards (parts.factored)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -459,6 +492,9 @@ def main():
     import kernelized_linear_attention_phi_amd as kata
     from kernelized_linear_attention_phi_amd import inputs as gen
     kata.lib()
+    if args.factored_only:
+        print(json.dumps(factored_forward(kata, torch, gen, args.steps, args.warmup)), flush=True)
+        return
     if args.decode_only:
         out = {}
         for n_seq, steps in ((512, 64), (8192, 16)):
@@ -564,6 +600,8 @@ def main():
         result["parts"]["recall16k"] = recall_forward(kata, torch, gen, min(args.steps, 10),
                                                       args.warmup)
         result["parts"]["delta_recall16k"] = delta_forward(kata, torch, gen, 3, 1)
+        result["parts"]["factored"] = factored_forward(kata, torch, gen, min(args.steps, 10),
+                                                       min(args.warmup, 3))
         progress("recall16k and delta")
         dms, dgbs, dbytes = decode_bench(kata, torch)
         result["parts"]["decode"] = {"ms_per_step": dms, "alg_GBps": dgbs,
