@@ -240,40 +240,57 @@ def decay_gate(kata, torch, gen, steps, warmup):
             "decode_gated_hbm_frac": dgbs / PEAK_HBM_GBS}
 
 
+# A batch-filled shape for the first-order comparison: 256 heads of 4096
+# tokens, so that even the sequential walk (one workgroup per head and value
+# tile) has 1024 workgroups, four per compute unit.
+BATCH4K = dict(name="batch4k", B=16, H=16, T=4096, dk=16, dv=64, chunk=64, seed=12)
+
+
 def scan_vs_sequential(kata, torch, gen, names, steps, warmup):
     """The inter-chunk prefix by the associative scan (segments in parallel;
     blocked, the default, and the log-depth tree) and by the sequential walk
-    (one workgroup per head, depth N_C), for the PSD lift and for the
-    first-order identity feature (orthant inputs), on the same shapes: ms per
-    forward, tokens/s, the prefix depth (dependent state combines) and the
-    scan's speedup."""
+    (depth N_C: for the PSD lift one workgroup per head, for the first-order
+    feature one per head and 16-column value tile), for the PSD lift and for
+    the first-order identity feature (orthant inputs), on the same shapes: ms
+    per forward, tokens/s, the prefix depth (dependent state combines), the
+    workgroups of the output launch and the scan's speedup. The first-order
+    feature also runs on a batch-filled shape (BATCH4K) where the sequential
+    walk occupies every compute unit, so that its speedup reflects depth
+    rather than idle compute units."""
+    import types
     out = {}
-    speedups = []
+    speedups, first_order = [], []
     to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
-    for name in names:
-        w = gen.WORKLOADS[name]
-        for feature, draw in (("psd", gen.gaussian_qkv), ("identity", gen.orthant_qkv)):
-            q, k, v = (to(a) for a in draw(w.B, w.H, w.T, w.dk, w.dv, w.seed, "bf16"))
-            o = torch.empty_like(v)
-            row = {}
-            for prefix in ("scan", "tree", "sequential"):
-                nbytes = kata.chunked_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1, True,
-                                                    feature, prefix)
-                ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
-                n = steps if prefix != "sequential" else max(1, min(steps, 3))
-                ms = time_calls(torch, lambda: kata.chunked_fwd_into(
-                    q, k, v, o, w.chunk, True, ws, feature=feature, prefix=prefix), n,
-                    min(warmup, 1) if prefix == "sequential" else warmup)
-                row[prefix] = {"ms": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
-                               "depth": kata.prefix_depth(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1,
-                                                          feature, prefix)}
-                del ws
-            row["scan_speedup"] = row["sequential"]["ms"] / row["scan"]["ms"]
-            row["tree_speedup"] = row["sequential"]["ms"] / row["tree"]["ms"]
-            speedups.append(row["scan_speedup"])
-            out[f"{name}/{feature}"] = row
-            del q, k, v, o
+    cases = [(gen.WORKLOADS[n], f) for n in names for f in ("psd", "identity")]
+    cases.append((types.SimpleNamespace(**BATCH4K), "identity"))
+    for w, feature in cases:
+        draw = gen.gaussian_qkv if feature == "psd" else gen.orthant_qkv
+        q, k, v = (to(a) for a in draw(w.B, w.H, w.T, w.dk, w.dv, w.seed, "bf16"))
+        o = torch.empty_like(v)
+        row = {}
+        for prefix in ("scan", "tree", "sequential"):
+            nbytes = kata.chunked_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1, True,
+                                                feature, prefix)
+            ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+            n = steps if prefix != "sequential" else max(1, min(steps, 3))
+            ms = time_calls(torch, lambda: kata.chunked_fwd_into(
+                q, k, v, o, w.chunk, True, ws, feature=feature, prefix=prefix), n,
+                min(warmup, 1) if prefix == "sequential" else warmup)
+            row[prefix] = {"ms": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+                           "depth": kata.prefix_depth(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1,
+                                                      feature, prefix)}
+            if prefix == "sequential":
+                row[prefix]["workgroups"] = w.B * w.H * (w.dv // 16 if feature == "identity" else 1)
+            del ws
+        row["scan_speedup"] = row["sequential"]["ms"] / row["scan"]["ms"]
+        row["tree_speedup"] = row["sequential"]["ms"] / row["tree"]["ms"]
+        speedups.append(row["scan_speedup"])
+        if feature == "identity":
+            first_order.append(row["scan_speedup"])
+        out[f"{w.name}/{feature}"] = row
+        del q, k, v, o
     out["geomean_scan_speedup"] = float(np.exp(np.mean(np.log(speedups))))
+    out["geomean_first_order_scan_speedup"] = float(np.exp(np.mean(np.log(first_order))))
     return out
 
 
@@ -471,8 +488,8 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy (scales HBM counters)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode steps (2048 rows, then 32768 rows; for counter runs)")
-    ap.add_argument("--factored-only", action="store_true",
-                    help="only the KATA-Mg / KATA-Sigma-g forwards (parts.factored)")
+    ap.add_argument("--only", choices=["factored", "scan_vs_sequential", "scan_states", "delta"],
+                    help="run one part of parts.* alone and print it (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -492,8 +509,14 @@ def main():
     import kernelized_linear_attention_phi_amd as kata
     from kernelized_linear_attention_phi_amd import inputs as gen
     kata.lib()
-    if args.factored_only:
-        print(json.dumps(factored_forward(kata, torch, gen, args.steps, args.warmup)), flush=True)
+    if args.only:
+        part = {"factored": lambda: factored_forward(kata, torch, gen, args.steps, args.warmup),
+                "scan_vs_sequential": lambda: scan_vs_sequential(
+                    kata, torch, gen, ("fwd4k", "fwd32k", "fwd131k"), args.steps, args.warmup),
+                "scan_states": lambda: scan_states_bench(kata, torch, gen, ["fwd131k", "fwd32k"],
+                                                         args.steps, args.warmup),
+                "delta": lambda: delta_forward(kata, torch, gen, 3, 1)}[args.only]
+        print(json.dumps(part()), flush=True)
         return
     if args.decode_only:
         out = {}

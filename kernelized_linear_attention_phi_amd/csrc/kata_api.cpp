@@ -259,7 +259,8 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
         auto output = [&](const float* pre, float* fin) {
             return m == 16   ? kata::launch_fwd16(s, q, k, v, pre, fin, o, causal, plan.G, plan.NSEG, prec_all, hs)
                    : m == 32 ? kata::launch_fwd32(s, q, k, v, pre, fin, o, causal, plan.G, plan.NSEG, prec_all, hs)
-                             : kata::launch_fwd1(s, q, k, v, pre, fin, o, causal, plan.G, plan.NSEG, hs);
+                             : kata::launch_fwd1(s, q, k, v, pre, fin, o, causal, plan.G, plan.NSEG, hs,
+                                                 plan.seq);
         };
         // the first chunk of every head again, from the initial-state record
         // (one segment of one chunk per head; the output launch above wrote it
@@ -272,7 +273,9 @@ static kata_status_t chunked_fwd_impl(const void* q, const void* k, const void* 
         if (S0 && e == hipSuccess) e = from_packed();
         if (plan.seq && causal) {
             // one segment per head walks every chunk from the initial state; its
-            // running state at the end is the final state
+            // running state at the end is the final state (the first-order
+            // feature splits the walk over 16-column value tiles, one
+            // workgroup each, so that it is not held to B*H workgroups)
             if (!S0 && e == hipSuccess)
                 e = kata::launch_copy_or_zero(init, nullptr, BH * plan.REC, hs);
             if (e == hipSuccess) e = mark(1);
@@ -585,7 +588,8 @@ kata_status_t kata_chunked_fwd_decay_ex(const void* q, const void* k, const void
     float* total = reinterpret_cast<float*>(ws + fp.total_off);
     const int nrec = (int)BH;
     auto output = [&](const float* pre, float* fin) {
-        return m == 1    ? kata::launch_fwd1_decay(s, q, k, v, log_decay, pre, fin, o, fp.G, fp.NSEG, hs)
+        return m == 1    ? kata::launch_fwd1_decay(s, q, k, v, log_decay, pre, fin, o, fp.G, fp.NSEG, hs,
+                                                   fp.seq)
                : m == 16 ? kata::launch_fwd16_decay(s, q, k, v, log_decay, pre, fin, o, fp.G, fp.NSEG, hs)
                          : kata::launch_fwd32_decay(s, q, k, v, log_decay, pre, fin, o, fp.G, fp.NSEG, hs);
     };

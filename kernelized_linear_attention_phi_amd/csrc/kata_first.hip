@@ -75,6 +75,12 @@ __host__ __device__ constexpr bool owns(int at, int u) {
     return W == ALL || (at * NU + u) % NW1 == W;
 }
 
+// Value-tile split (the sequential walk): a workgroup of value tile vt
+// evaluates only the columns of that tile and the z tile; vt < 0: every tile.
+__device__ __forceinline__ bool live_unit(int vt, int u, int NTV) {
+    return vt < 0 || u == vt || u == NTV;
+}
+
 // The 8 bf16 of an operand fragment, each times its own factor, rounded back.
 __device__ __forceinline__ u32x4_t scale_bf16x8(const u32x4_t& x, const float (&f)[8]) {
     u32x4_t y;
@@ -99,7 +105,7 @@ __device__ __forceinline__ void decay_state1(State1<DK, DV, C>& st, const ChunkD
 template <int W, int DK, int DV, int C, bool DECAY = false>
 __device__ __forceinline__ void state_update1(State1<DK, DV, C>& st, const bf16_t* bk,
                                               const bf16_t* bv, const Lane& L,
-                                              const KeyDecay& kd = KeyDecay{}) {
+                                              const KeyDecay& kd = KeyDecay{}, int vt = -1) {
     using F = Cfg1<DK, DV, C>;
     const u32x4_t ones = ones_op(L);
 #pragma unroll
@@ -117,6 +123,7 @@ __device__ __forceinline__ void state_update1(State1<DK, DV, C>& st, const bf16_
         }
 #pragma unroll
         for (int u = 0; u < F::NU; ++u) {
+            if (!live_unit(vt, u, F::NTV)) continue;
             bool any = false;
 #pragma unroll
             for (int at = 0; at < F::NAT; ++at) any = any || owns<W, F::NU>(at, u);
@@ -129,27 +136,31 @@ __device__ __forceinline__ void state_update1(State1<DK, DV, C>& st, const bf16_
     }
 }
 
+// Units of a split workgroup: its value tile, and the z tile from value tile 0
+// only (every split workgroup of a head holds the same z).
 template <int W, int DK, int DV, int C>
 __device__ __forceinline__ void record_store1(float* rec, const State1<DK, DV, C>& st,
-                                              const Lane& L) {
+                                              const Lane& L, int vt = -1) {
     using F = Cfg1<DK, DV, C>;
     f32x4_t* r4 = reinterpret_cast<f32x4_t*>(rec);
 #pragma unroll
     for (int at = 0; at < F::NAT; ++at)
 #pragma unroll
         for (int u = 0; u < F::NU; ++u)
-            if (owns<W, F::NU>(at, u)) r4[(at * F::NU + u) * 64 + L.lane] = st.s[at][u];
+            if (owns<W, F::NU>(at, u) && live_unit(vt, u, F::NTV) && (u < F::NTV || vt <= 0))
+                r4[(at * F::NU + u) * 64 + L.lane] = st.s[at][u];
 }
 
 template <int DK, int DV, int C>
 __device__ __forceinline__ void record_load1(const float* rec, State1<DK, DV, C>& st,
-                                             const Lane& L) {
+                                             const Lane& L, int vt = -1) {
     using F = Cfg1<DK, DV, C>;
     const f32x4_t* r4 = reinterpret_cast<const f32x4_t*>(rec);
 #pragma unroll
     for (int at = 0; at < F::NAT; ++at)
 #pragma unroll
-        for (int u = 0; u < F::NU; ++u) st.s[at][u] = r4[(at * F::NU + u) * 64 + L.lane];
+        for (int u = 0; u < F::NU; ++u)
+            st.s[at][u] = live_unit(vt, u, F::NTV) ? r4[(at * F::NU + u) * 64 + L.lane] : zero4();
 }
 
 // ---- segment states ----------------------------------------------------------
@@ -212,16 +223,18 @@ __global__ __launch_bounds__(64 * NW1) void kata_seg_state1(const bf16_t* __rest
 // Rows staged by wavefront w (its query tiles NW1*u + w, row stride OROW): staged
 // row r goes to oc[16*NW1*(r/16) + r%16] when that is below n (the caller offsets
 // oc and n by the wavefront's 16 w rows). Wavefront 1 only.
-template <int DK, int DV, int C>
-__device__ __forceinline__ void store_rows1(const char* ost, bf16_t* oc, int n, const Lane& L) {
+// SPLIT: only the two 16-byte units of value tile vt of each row.
+template <int DK, int DV, int C, bool SPLIT = false>
+__device__ __forceinline__ void store_rows1(const char* ost, bf16_t* oc, int n, const Lane& L,
+                                            int vt = 0) {
     using F = Cfg1<DK, DV, C>;
-    constexpr int UPR = DV * 2 / 16;              // 16-byte units per row
+    constexpr int UPR = SPLIT ? 2 : DV * 2 / 16;  // 16-byte units stored per row
     constexpr int NUN = F::TW * 16 * UPR;
 #pragma unroll
     for (int i = 0; i < (NUN + 63) / 64; ++i) {
         const int unit = L.lane + 64 * i;
         if (unit < NUN) {
-            const int rl = unit / UPR, col = unit % UPR;
+            const int rl = unit / UPR, col = (SPLIT ? 2 * vt : 0) + unit % UPR;
             const int row = 16 * NW1 * (rl / 16) + rl % 16;
             const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ost + rl * F::OROW + 16 * col);
             if (row < n) *reinterpret_cast<u32x4_t*>(oc + (size_t)row * DV + 8 * col) = val;
@@ -250,7 +263,7 @@ __device__ __forceinline__ f32x4_t scores1(const bf16_t* bk, const bf16_t* bq, i
     }
 }
 
-template <int W, int DK, int DV, int C, bool CAUSAL, bool DECAY>
+template <int W, int DK, int DV, int C, bool CAUSAL, bool DECAY, bool SPLIT>
 __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                           const float* gdec, const float* prefix,
                                           float* final_rec, bf16_t* o, char* lds, int T, int NC,
@@ -259,13 +272,14 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
     using FG = Cfg1<DK, DV, C, DECAY>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
+    const int vt = SPLIT ? (int)blockIdx.z : -1;   // value tile of a split workgroup
     Pipeline<DK, DV, C, NW1, 1, DECAY> P{lds, seg * G, min(NC, seg * G + G), T, bh * T, true, gdec};
     // staged rows: wavefront 0 in buffer (c - c0) % 2, wavefront 1 in buffer 2
     char* ostage = lds + 2 * FG::IO::BUF;
     float* krow = reinterpret_cast<float*>(lds + 2 * FG::IO::BUF + 3 * F::OST + W * kKeyDecayRowBytes);
 
     State1<DK, DV, C> st;
-    record_load1<DK, DV, C>(prefix + (CAUSAL ? bh * NSEG + seg : bh) * (size_t)F::REC, st, L);
+    record_load1<DK, DV, C>(prefix + (CAUSAL ? bh * NSEG + seg : bh) * (size_t)F::REC, st, L, vt);
     const u32x4_t ones = ones_op(L);
 
     P.stage(q, k, v, P.c0, L);
@@ -287,7 +301,8 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
 
         // wavefront 0's rows of the previous chunk (always a full chunk)
         if (W == 1 && c > P.c0)
-            store_rows1<DK, DV, C>(ostage + ((c - 1 - P.c0) & 1) * F::OST, oc - (size_t)C * DV, C, L);
+            store_rows1<DK, DV, C, SPLIT>(ostage + ((c - 1 - P.c0) & 1) * F::OST,
+                                          oc - (size_t)C * DV, C, L, vt);
         compiler_fence();
         char* own = ostage + (W == 0 ? ((c - P.c0) & 1) : 2) * F::OST;
 
@@ -314,7 +329,8 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
             for (int at = 0; at < F::NAT; ++at) {
                 const u32x2_t qa = query16<DK>(bq, qrow, at, L);
 #pragma unroll
-                for (int u = 0; u < F::NU; ++u) num[u] = mma16_acc32(sop[at][u], qa, num[u]);
+                for (int u = 0; u < F::NU; ++u)
+                    if (live_unit(vt, u, F::NTV)) num[u] = mma16_acc32(sop[at][u], qa, num[u]);
             }
             float bt = 0.0f;                          // b of this lane's query
             if constexpr (DECAY) {                    // the prefix state decays to query t
@@ -343,7 +359,7 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
                     const u32x4_t a = {pk2(w[0], w[1]), pk2(w[2], w[3]), pk2(w[4], w[5]), pk2(w[6], w[7])};
 #pragma unroll
                     for (int nt = 0; nt < F::NTV; ++nt)
-                        num[nt] = mma32(v_fragment_tr<DV>(bv, m, nt, L), a, num[nt]);
+                        if (live_unit(vt, nt, F::NTV)) num[nt] = mma32(v_fragment_tr<DV>(bv, m, nt, L), a, num[nt]);
                     num[F::NTV] = mma32(ones, a, num[F::NTV]);
                 }
             }
@@ -351,19 +367,20 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
             const float y = inv_den(__shfl(num[F::NTV][0], L.c16, 64));   // 0 -> o = 0
 #pragma unroll
             for (int nt = 0; nt < F::NTV; ++nt)
-                *reinterpret_cast<u32x2_t*>(own + (16 * ui + L.c16) * F::OROW +
-                                            2 * (16 * nt + 4 * L.g)) =
-                    u32x2_t{pk2(num[nt][0] * y, num[nt][1] * y), pk2(num[nt][2] * y, num[nt][3] * y)};
+                if (live_unit(vt, nt, F::NTV))
+                    *reinterpret_cast<u32x2_t*>(own + (16 * ui + L.c16) * F::OROW +
+                                                2 * (16 * nt + 4 * L.g)) =
+                        u32x2_t{pk2(num[nt][0] * y, num[nt][1] * y), pk2(num[nt][2] * y, num[nt][3] * y)};
         }
         // wavefront 1's own rows leave in this chunk, as whole rows
         compiler_fence();
-        if (W == 1) store_rows1<DK, DV, C>(own, oc + 16 * DV, n - 16, L);
+        if (W == 1) store_rows1<DK, DV, C, SPLIT>(own, oc + 16 * DV, n - 16, L, vt);
 
         // ---- running state: S += K_c^T V_c, z += K_c^T 1 (both wavefronts; not
         // needed after the segment's last chunk unless the final state is asked for)
         if (CAUSAL && (c + 1 < P.c1 || final_rec)) {
             if constexpr (DECAY) decay_state1<DK, DV, C>(st, cd);
-            state_update1<ALL, DK, DV, C, DECAY>(st, bk, bv, L, kd);
+            state_update1<ALL, DK, DV, C, DECAY>(st, bk, bv, L, kd, vt);
         }
         compiler_fence();
     }
@@ -371,15 +388,15 @@ __device__ __forceinline__ void fwd_body1(const bf16_t* q, const bf16_t* k, cons
     lds_barrier();
     if (W == 1) {
         const int cl = P.c1 - 1;
-        store_rows1<DK, DV, C>(ostage + ((cl - P.c0) & 1) * F::OST, o + (bh * T + (size_t)cl * C) * DV,
-                               min(C, T - cl * C), L);
+        store_rows1<DK, DV, C, SPLIT>(ostage + ((cl - P.c0) & 1) * F::OST,
+                                      o + (bh * T + (size_t)cl * C) * DV, min(C, T - cl * C), L, vt);
     }
     // running state after the segment (the final state when one segment covers
     // the sequence); the two wavefronts hold the same state and split the units
-    if (CAUSAL && final_rec) record_store1<W, DK, DV, C>(final_rec + bh * (size_t)F::REC, st, L);
+    if (CAUSAL && final_rec) record_store1<W, DK, DV, C>(final_rec + bh * (size_t)F::REC, st, L, vt);
 }
 
-template <int DK, int DV, int C, bool CAUSAL, bool DECAY>
+template <int DK, int DV, int C, bool CAUSAL, bool DECAY, bool SPLIT = false>
 __global__ __launch_bounds__(64 * NW1) void kata_fwd1(const bf16_t* __restrict__ q,
                                                       const bf16_t* __restrict__ k,
                                                       const bf16_t* __restrict__ v,
@@ -391,11 +408,11 @@ __global__ __launch_bounds__(64 * NW1) void kata_fwd1(const bf16_t* __restrict__
     __shared__ __attribute__((aligned(16))) char lds[Cfg1<DK, DV, C, DECAY>::LDS_FWD];
     const Lane L;
     if (L.w == 0)
-        fwd_body1<0, DK, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G,
-                                               NSEG, as_wave<0>(L));
+        fwd_body1<0, DK, DV, C, CAUSAL, DECAY, SPLIT>(q, k, v, gdec, prefix, final_rec, o, lds, T,
+                                                      NC, G, NSEG, as_wave<0>(L));
     else
-        fwd_body1<1, DK, DV, C, CAUSAL, DECAY>(q, k, v, gdec, prefix, final_rec, o, lds, T, NC, G,
-                                               NSEG, as_wave<1>(L));
+        fwd_body1<1, DK, DV, C, CAUSAL, DECAY, SPLIT>(q, k, v, gdec, prefix, final_rec, o, lds, T,
+                                                      NC, G, NSEG, as_wave<1>(L));
 }
 
 // ---- record <-> packed (S [d_k, d_v] row-major, z [d_k]) ---------------------
@@ -439,6 +456,7 @@ struct Args1 {
     void* o;
     int causal, G, NSEG;
     bool state_only;
+    bool split = false;    // causal output: one workgroup per 16-column value tile
 };
 
 template <int DK, int DV, int C>
@@ -458,6 +476,17 @@ hipError_t launch_dk_dv_c1(const Shape& s, const Args1& a, hipStream_t st) {
         }
         kata_seg_state1<DK, DV, C, false><<<grid, 64 * NW1, 0, st>>>(k, v, nullptr, a.rec, nullptr,
                                                                     s.T, s.NC, a.G, a.NSEG);
+    } else if (a.causal && a.split) {
+        const dim3 sgrid(a.NSEG, s.B * s.H, DV / 16);
+        if constexpr (kGate) {
+            if (a.gdec) {
+                kata_fwd1<DK, DV, C, true, true, true><<<sgrid, 64 * NW1, 0, st>>>(
+                    q, k, v, a.gdec, a.prefix, a.rec, o, s.T, s.NC, a.G, a.NSEG);
+                return hipGetLastError();
+            }
+        }
+        kata_fwd1<DK, DV, C, true, false, true><<<sgrid, 64 * NW1, 0, st>>>(
+            q, k, v, nullptr, a.prefix, a.rec, o, s.T, s.NC, a.G, a.NSEG);
     } else if (a.causal) {
         if constexpr (kGate) {
             if (a.gdec) {
@@ -518,8 +547,9 @@ hipError_t launch_seg_state1(const Shape& s, const void* k, const void* v, float
 
 hipError_t launch_fwd1(const Shape& s, const void* q, const void* k, const void* v,
                        const float* prefix, float* final_rec, void* o, int causal, int G,
-                       int NSEG, hipStream_t st) {
-    return dispatch1(s, Args1{q, k, v, nullptr, final_rec, nullptr, prefix, o, causal, G, NSEG, false}, st);
+                       int NSEG, hipStream_t st, bool split) {
+    return dispatch1(s, Args1{q, k, v, nullptr, final_rec, nullptr, prefix, o, causal, G, NSEG, false,
+                              split && causal}, st);
 }
 
 bool first_decay_supported(const Shape& s) { return first_supported(s) && (s.C == 32 || s.C == 64); }
@@ -531,8 +561,8 @@ hipError_t launch_seg_state1_decay(const Shape& s, const void* k, const void* v,
 
 hipError_t launch_fwd1_decay(const Shape& s, const void* q, const void* k, const void* v,
                              const float* gdec, const float* prefix, float* final_rec, void* o,
-                             int G, int NSEG, hipStream_t st) {
-    return dispatch1(s, Args1{q, k, v, gdec, final_rec, nullptr, prefix, o, 1, G, NSEG, false}, st);
+                             int G, int NSEG, hipStream_t st, bool split) {
+    return dispatch1(s, Args1{q, k, v, gdec, final_rec, nullptr, prefix, o, 1, G, NSEG, false, split}, st);
 }
 
 hipError_t launch_record_from_packed1(float* rec, const float* S, const float* z, int dk, int dv,

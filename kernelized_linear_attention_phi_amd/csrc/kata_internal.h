@@ -153,9 +153,12 @@ bool first_supported(const Shape& s);
 int first_record_floats(int dk, int dv);
 hipError_t launch_seg_state1(const Shape& s, const void* k, const void* v, float* rec, int G,
                              int NSEG, hipStream_t st);
+// split (causal only): one workgroup per (segment, head, 16-column value tile),
+// each evaluating its tile's columns (and the denominator); used by the
+// sequential walk, whose one segment per head leaves compute units idle.
 hipError_t launch_fwd1(const Shape& s, const void* q, const void* k, const void* v,
                        const float* prefix, float* final_rec, void* o, int causal, int G,
-                       int NSEG, hipStream_t st);
+                       int NSEG, hipStream_t st, bool split = false);
 // Decay-gated variants (causal, chunk 32 or 64): gdec [BH, T] log-decays;
 // the state kernel also writes each segment's decay factor to segdec [BH, NSEG].
 bool first_decay_supported(const Shape& s);
@@ -163,7 +166,7 @@ hipError_t launch_seg_state1_decay(const Shape& s, const void* k, const void* v,
                                    float* rec, float* segdec, int G, int NSEG, hipStream_t st);
 hipError_t launch_fwd1_decay(const Shape& s, const void* q, const void* k, const void* v,
                              const float* gdec, const float* prefix, float* final_rec, void* o,
-                             int G, int NSEG, hipStream_t st);
+                             int G, int NSEG, hipStream_t st, bool split = false);
 hipError_t launch_record_from_packed1(float* rec, const float* S, const float* z, int dk, int dv,
                                       int nrec, hipStream_t st);
 hipError_t launch_record_to_packed1(const float* rec, float* S, float* z, int dk, int dv, int nrec,
