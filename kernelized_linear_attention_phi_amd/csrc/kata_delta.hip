@@ -19,18 +19,23 @@
 // thread per column), then block rows in order, each a product with the
 // earlier blocks' P and with its block inverse.
 //
-// One workgroup per (batch, head, 16-column value tile) keeps its 16 columns of
-// S and the z column in LDS (the z column is recomputed by every value tile of
-// a head). Lifted keys and queries are formed on the fly from the staged
-// coordinates through a pair table. Everything is fp32.
+// One workgroup of 16 wavefronts per (batch, head, 16-column value tile) keeps
+// its 16 columns of S and the z column in LDS (the z column is recomputed by
+// every value tile of a head); the products R, O and K^T P are spread one
+// (token, column) or (feature, column) per thread. At d_k = 16 the chunk's
+// lifted keys and queries are formed once per chunk in LDS; at d_k = 32 (528
+// features, too many to hold beside the state) on the fly through a pair
+// table. Everything is fp32.
 #include "kata_device.h"
 #include "kata_internal.h"
+#include "kata_mfma.h"
 
 namespace kata {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;          // decode
+constexpr int kFwdThreads = 1024;      // forward: 16 wavefronts per (head, value tile)
 constexpr int kCols = 17;              // 16 value columns + z
 constexpr int kSub = 16;               // rows per block of the triangular solve
 
@@ -38,8 +43,6 @@ template <int DK, int C>
 struct DeltaCfg {
     static constexpr int D = DK * (DK + 1) / 2;
     static constexpr int NB = C / kSub;
-    static constexpr int TPT = kThreads / C;          // threads per token (R, O)
-    static constexpr int NCT = kSub / TPT;            // value columns per such thread
     // LDS layout, in floats
     static constexpr int S_OFF = 0;                           // state [D][17]
     static constexpr int K_OFF = S_OFF + D * kCols;           // keys [C][DK]
@@ -53,19 +56,32 @@ struct DeltaCfg {
     static constexpr int P_OFF = R_OFF + C * kCols;           // P [C][17]
     static constexpr int TI_OFF = P_OFF + C * kCols;          // block inverses [NB][16][16]
     static constexpr int O_OFF = TI_OFF + NB * kSub * kSub;   // outputs [C][17]
-    static constexpr int FLOATS = O_OFF + C * kCols;
-    static_assert(C % kSub == 0 && kThreads % C == 0 && kSub % TPT == 0, "chunk of 16, 32 or 64");
+    static constexpr int BASE = O_OFF + C * kCols;
+    // the chunk's lifted keys kappa [C][D] and queries phi(q) [C][D], formed
+    // once per chunk where they fit next to the rest (d_k = 16)
+    static constexpr bool PRE = (BASE + 2 * C * D) * 4 + D * 4 <= 150 * 1024;
+    static constexpr int KAP_OFF = BASE;
+    static constexpr int FQ_OFF = KAP_OFF + C * D;
+    static constexpr int FLOATS = PRE ? FQ_OFF + C * D : BASE;
+    static_assert(C % kSub == 0 && NB * kSub <= kFwdThreads && kSub * kCols <= kFwdThreads,
+                  "chunk of 16, 32 or 64");
     static_assert(FLOATS * 4 + D * 4 <= 160 * 1024, "fits the LDS of a compute unit");
 };
 
+// D = A(16x4) * B(4x16) + C in fp32 (v_mfma_f32_16x16x4_f32): fp32 operands,
+// fp32 accumulation.
+__device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <typename TIn, int DK, int C>
-__global__ __launch_bounds__(kThreads) void delta_fwd_kernel(
+__global__ __launch_bounds__(kFwdThreads) void delta_fwd_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ beta, TIn* __restrict__ o, const float* __restrict__ S0,
     const float* __restrict__ z0, float* __restrict__ S_out, float* __restrict__ z_out, int T,
     int DV) {
     using F = DeltaCfg<DK, C>;
-    constexpr int D = F::D;
+    constexpr int D = F::D, NT = kFwdThreads;
     __shared__ float sm[F::FLOATS];
     __shared__ uint32_t pairs[D];
     float* St = sm + F::S_OFF;
@@ -80,13 +96,15 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(
     float* P = sm + F::P_OFF;
     float* TI = sm + F::TI_OFF;
     float* Os = sm + F::O_OFF;
+    float* Kap = sm + F::KAP_OFF;              // PRE only
+    float* Fq = sm + F::FQ_OFF;                // PRE only
 
     const int vt = blockIdx.x;                 // value tile: columns 16 vt .. 16 vt + 15
     const size_t bh = blockIdx.y;
     const int tid = threadIdx.x;
 
-    for (int p = tid; p < D; p += kThreads) pairs[p] = pack_pair(p, DK);
-    for (int e = tid; e < D * kCols; e += kThreads) {
+    for (int p = tid; p < D; p += NT) pairs[p] = pack_pair(p, DK);
+    for (int e = tid; e < D * kCols; e += NT) {
         const int p = e / kCols, c = e % kCols;
         float x = 0.0f;
         if (S0) x = c < kSub ? S0[(bh * D + p) * DV + kSub * vt + c] : z0[bh * D + p];
@@ -94,29 +112,53 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(
     }
     __syncthreads();
 
-    // thread (token tt, column group cg) of the R and O products: columns
-    // cg + TPT i, and z for cg == 0
-    const int tt = tid / F::TPT, cg = tid % F::TPT;
+    // lifted key (kappa, scaled by 1 / |k_t|^2) and query of token t, feature p
+    auto kappa = [&](int t, int p) -> float {
+        if constexpr (F::PRE) {
+            return Kap[t * D + p];
+        } else {
+            const uint32_t pr = pairs[p];
+            const int a = pr & 0xff, b = pr >> 8;
+            return Ks[t * DK + a] * Ks[t * DK + b] * ((a == b ? 1.0f : kSqrt2) * Inv[t]);
+        }
+    };
+    auto phiq = [&](int t, int p) -> float {
+        if constexpr (F::PRE) {
+            return Fq[t * D + p];
+        } else {
+            const uint32_t pr = pairs[p];
+            const int a = pr & 0xff, b = pr >> 8;
+            return Qs[t * DK + a] * Qs[t * DK + b] * (a == b ? 1.0f : kSqrt2);
+        }
+    };
+
+    // matrix-core tiles: wavefront w takes tiles w, w + 16, ...; lane (c16, g)
+    // of a 16x16x4 fp32 product holds A[row c16][k g], B[k g][column c16] and
+    // accumulator rows 4g + r of column c16
+    const int wave = tid >> 6, lane = tid & 63, c16 = lane & 15, g4 = lane >> 4;
+    constexpr int NWV = NT / 64;
+    constexpr int MT = C / 16;                      // token tiles
+    constexpr int FT = (D + 15) / 16;               // feature tiles
 
     for (int c0 = 0; c0 < T; c0 += C) {
         const int n = min(C, T - c0);
         const size_t tok0 = bh * (size_t)T + c0;
         // ---- stage the chunk (rows past a ragged end are zero: no key, no
         // write, beta 0)
-        for (int e = tid; e < C * DK; e += kThreads) {
+        for (int e = tid; e < C * DK; e += NT) {
             const int t = e / DK;
             Ks[e] = t < n ? io<TIn>::ld(k, tok0 * DK + e) : 0.0f;
             Qs[e] = t < n ? io<TIn>::ld(q, tok0 * DK + e) : 0.0f;
         }
-        for (int e = tid; e < C * kCols; e += kThreads) {
+        for (int e = tid; e < C * kCols; e += NT) {
             const int t = e / kCols, c = e % kCols;
             float x = 0.0f;
             if (t < n) x = c < kSub ? io<TIn>::ld(v, (tok0 + t) * DV + kSub * vt + c) : 1.0f;
             Us[e] = x;
         }
-        for (int t = tid; t < C; t += kThreads) Bs[t] = t < n ? beta[tok0 + t] : 0.0f;
+        for (int t = tid; t < C; t += NT) Bs[t] = t < n ? beta[tok0 + t] : 0.0f;
         __syncthreads();
-        for (int t = tid; t < C; t += kThreads) {
+        for (int t = tid; t < C; t += NT) {
             float s = 0.0f;
 #pragma unroll
             for (int a = 0; a < DK; ++a) s = __builtin_fmaf(Ks[t * DK + a], Ks[t * DK + a], s);
@@ -125,46 +167,63 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(
         __syncthreads();
 
         // ---- G = beta_t kappa_t.kappa_j (j < t) and Aq = phi(q_t).kappa_j (j <= t),
-        // from raw dot products: kappa_t.kappa_j = (k_t.k_j)^2 / (|k_t|^2 |k_j|^2)
-        for (int e = tid; e < C * C; e += kThreads) {
-            const int t = e / C, j = e % C;
-            float dk = 0.0f, dq = 0.0f;
+        // from raw dot products on the matrix cores: kappa_t.kappa_j =
+        // (k_t.k_j)^2 / (|k_t|^2 |k_j|^2); the lifted keys and queries of the chunk
+        for (int tile = wave; tile < MT * MT; tile += NWV) {
+            const int mt = tile / MT, jt = tile % MT;
+            f32x4_t dk = zero4(), dq = zero4();
 #pragma unroll
-            for (int a = 0; a < DK; ++a) {
-                dk = __builtin_fmaf(Ks[t * DK + a], Ks[j * DK + a], dk);
-                dq = __builtin_fmaf(Qs[t * DK + a], Ks[j * DK + a], dq);
+            for (int s4 = 0; s4 < DK / 4; ++s4) {
+                const int a = 4 * s4 + g4;
+                const float kb = Ks[(16 * jt + c16) * DK + a];
+                dk = mfma4(Ks[(16 * mt + c16) * DK + a], kb, dk);
+                dq = mfma4(Qs[(16 * mt + c16) * DK + a], kb, dq);
             }
-            G[e] = j < t ? Bs[t] * (dk * dk) * (Inv[t] * Inv[j]) : 0.0f;
-            Aq[e] = j <= t ? (dq * dq) * Inv[j] : 0.0f;
-        }
-        // ---- R = U - K A (kappa formed on the fly)
-        {
-            float acc[F::NCT + 1];
+            const int jj = 16 * jt + c16;
 #pragma unroll
-            for (int i = 0; i <= F::NCT; ++i) acc[i] = 0.0f;
-            const float inv = Inv[tt];
-            for (int p = 0; p < D; ++p) {
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * mt + 4 * g4 + r;
+                G[t * C + jj] = jj < t ? Bs[t] * (dk[r] * dk[r]) * (Inv[t] * Inv[jj]) : 0.0f;
+                Aq[t * C + jj] = jj <= t ? (dq[r] * dq[r]) * Inv[jj] : 0.0f;
+            }
+        }
+        if constexpr (F::PRE) {
+            for (int e = tid; e < C * D; e += NT) {
+                const int t = e / D, p = e % D;
                 const uint32_t pr = pairs[p];
                 const int a = pr & 0xff, b = pr >> 8;
-                const float kap = Ks[tt * DK + a] * Ks[tt * DK + b] * (a == b ? inv : kSqrt2 * inv);
-#pragma unroll
-                for (int i = 0; i < F::NCT; ++i)
-                    acc[i] = __builtin_fmaf(kap, St[p * kCols + cg + F::TPT * i], acc[i]);
-                if (cg == 0) acc[F::NCT] = __builtin_fmaf(kap, St[p * kCols + kSub], acc[F::NCT]);
+                const float sc = a == b ? 1.0f : kSqrt2;
+                Kap[e] = Ks[t * DK + a] * Ks[t * DK + b] * (sc * Inv[t]);
+                Fq[e] = Qs[t * DK + a] * Qs[t * DK + b] * sc;
             }
-#pragma unroll
-            for (int i = 0; i < F::NCT; ++i) {
-                const int c = cg + F::TPT * i;
-                R[tt * kCols + c] = Us[tt * kCols + c] - acc[i];
-            }
-            if (cg == 0) R[tt * kCols + kSub] = Us[tt * kCols + kSub] - acc[F::NCT];
         }
         __syncthreads();
 
+        // ---- R = U - K A (tiles of 16 tokens x 16 columns; the second column
+        // tile holds only z)
+        for (int tile = wave; tile < MT * 2; tile += NWV) {
+            const int mt = tile >> 1, col = 16 * (tile & 1) + c16;
+            const bool colok = col < kCols;
+            f32x4_t acc = zero4();
+#pragma unroll 2
+            for (int s4 = 0; s4 < D / 4; ++s4) {
+                const int p = 4 * s4 + g4;
+                acc = mfma4(kappa(16 * mt + c16, p), colok ? St[p * kCols + col] : 0.0f, acc);
+            }
+            if (colok) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * mt + 4 * g4 + r;
+                    R[t * kCols + col] = Us[t * kCols + col] - acc[r];
+                }
+            }
+        }
         // ---- inverses of the diagonal blocks I + N_b (N_b strictly lower, the
         // block's part of G): column j of each inverse by forward substitution
-        if (tid < F::NB * kSub) {
-            const int b = tid / kSub, j = tid % kSub, r0 = kSub * b;
+        // (G is complete after the barrier above)
+        if (tid >= NT - F::NB * kSub) {
+            const int id = tid - (NT - F::NB * kSub);
+            const int b = id / kSub, j = id % kSub, r0 = kSub * b;
             float x[kSub];
 #pragma unroll
             for (int r = 0; r < kSub; ++r) {
@@ -179,19 +238,21 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(
         __syncthreads();
 
         // ---- P block by block: rhs = beta R - G_{b,<b} P_{<b}, P_b = inv_b rhs
+#pragma unroll 1
         for (int b = 0; b < F::NB; ++b) {
             const int r0 = kSub * b;
-            for (int e = tid; e < kSub * kCols; e += kThreads) {
+            for (int e = tid; e < kSub * kCols; e += NT) {
                 const int t = r0 + e / kCols, c = e % kCols;
                 float s = Bs[t] * R[t * kCols + c];
+#pragma unroll 4
                 for (int j = 0; j < r0; ++j) s = __builtin_fmaf(-G[t * C + j], P[j * kCols + c], s);
                 R[t * kCols + c] = s;
             }
             __syncthreads();
-            for (int e = tid; e < kSub * kCols; e += kThreads) {
+            for (int e = tid; e < kSub * kCols; e += NT) {
                 const int r = e / kCols, c = e % kCols;
                 float s = 0.0f;
-#pragma unroll
+#pragma unroll 4
                 for (int j = 0; j < kSub; ++j)
                     s = __builtin_fmaf(TI[(b * kSub + r) * kSub + j], R[(r0 + j) * kCols + c], s);
                 P[(r0 + r) * kCols + c] = s;
@@ -199,59 +260,60 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(
             __syncthreads();
         }
 
-        // ---- O = phi(Q) A + mask(phi(Q) K^T) P
-        {
-            float acc[F::NCT + 1];
-#pragma unroll
-            for (int i = 0; i <= F::NCT; ++i) acc[i] = 0.0f;
-            for (int p = 0; p < D; ++p) {
-                const uint32_t pr = pairs[p];
-                const int a = pr & 0xff, b = pr >> 8;
-                const float fq = Qs[tt * DK + a] * Qs[tt * DK + b] * (a == b ? 1.0f : kSqrt2);
-#pragma unroll
-                for (int i = 0; i < F::NCT; ++i)
-                    acc[i] = __builtin_fmaf(fq, St[p * kCols + cg + F::TPT * i], acc[i]);
-                if (cg == 0) acc[F::NCT] = __builtin_fmaf(fq, St[p * kCols + kSub], acc[F::NCT]);
+        // ---- O = phi(Q) A + mask(phi(Q) K^T) P (Aq holds the masked weights)
+        for (int tile = wave; tile < MT * 2; tile += NWV) {
+            const int mt = tile >> 1, col = 16 * (tile & 1) + c16;
+            const bool colok = col < kCols;
+            f32x4_t acc = zero4();
+#pragma unroll 2
+            for (int s4 = 0; s4 < D / 4; ++s4) {
+                const int p = 4 * s4 + g4;
+                acc = mfma4(phiq(16 * mt + c16, p), colok ? St[p * kCols + col] : 0.0f, acc);
             }
-            for (int j = 0; j <= tt; ++j) {
-                const float w = Aq[tt * C + j];
-#pragma unroll
-                for (int i = 0; i < F::NCT; ++i)
-                    acc[i] = __builtin_fmaf(w, P[j * kCols + cg + F::TPT * i], acc[i]);
-                if (cg == 0) acc[F::NCT] = __builtin_fmaf(w, P[j * kCols + kSub], acc[F::NCT]);
+#pragma unroll 2
+            for (int s4 = 0; s4 < C / 4; ++s4) {
+                const int jj = 4 * s4 + g4;
+                acc = mfma4(Aq[(16 * mt + c16) * C + jj], colok ? P[jj * kCols + col] : 0.0f, acc);
             }
+            if (colok) {
 #pragma unroll
-            for (int i = 0; i < F::NCT; ++i) Os[tt * kCols + cg + F::TPT * i] = acc[i];
-            if (cg == 0) Os[tt * kCols + kSub] = acc[F::NCT];
+                for (int r = 0; r < 4; ++r) Os[(16 * mt + 4 * g4 + r) * kCols + col] = acc[r];
+            }
         }
         __syncthreads();
 
-        // ---- normalise and store; the state gains K^T P (reads P, K; the
-        // outputs above were the last reads of the old state)
-        for (int e = tid; e < n * kSub; e += kThreads) {
+        // ---- normalise and store; the state gains K^T P (tiles of 16 features
+        // x 16 columns; the outputs above were the last reads of the old state)
+        for (int e = tid; e < n * kSub; e += NT) {
             const int t = e / kSub, c = e % kSub;
             io<TIn>::st(o, (tok0 + t) * DV + kSub * vt + c, safe_div(Os[t * kCols + c], Os[t * kCols + kSub]));
         }
-        for (int p = tid; p < D; p += kThreads) {
-            const uint32_t pr = pairs[p];
-            const int a = pr & 0xff, b = pr >> 8;
-            const float sc = a == b ? 1.0f : kSqrt2;
-            float s[kCols];
+        for (int tile = wave; tile < FT * 2; tile += NWV) {
+            const int ft = tile >> 1, col = 16 * (tile & 1) + c16;
+            const bool colok = col < kCols;
+            const int pa = 16 * ft + c16;            // this lane's A row (feature)
+            f32x4_t acc;
 #pragma unroll
-            for (int c = 0; c < kCols; ++c) s[c] = 0.0f;
-            for (int t = 0; t < n; ++t) {
-                const float kap = Ks[t * DK + a] * Ks[t * DK + b] * (sc * Inv[t]);
-#pragma unroll
-                for (int c = 0; c < kCols; ++c) s[c] = __builtin_fmaf(kap, P[t * kCols + c], s[c]);
+            for (int r = 0; r < 4; ++r) {
+                const int p = 16 * ft + 4 * g4 + r;
+                acc[r] = (p < D && colok) ? St[p * kCols + col] : 0.0f;
+            }
+#pragma unroll 2
+            for (int s4 = 0; s4 < C / 4; ++s4) {
+                const int t = 4 * s4 + g4;
+                acc = mfma4(pa < D ? kappa(t, pa) : 0.0f, colok ? P[t * kCols + col] : 0.0f, acc);
             }
 #pragma unroll
-            for (int c = 0; c < kCols; ++c) St[p * kCols + c] += s[c];
+            for (int r = 0; r < 4; ++r) {
+                const int p = 16 * ft + 4 * g4 + r;
+                if (p < D && colok) St[p * kCols + col] = acc[r];
+            }
         }
         __syncthreads();
     }
 
     if (S_out) {
-        for (int e = tid; e < D * kCols; e += kThreads) {
+        for (int e = tid; e < D * kCols; e += NT) {
             const int p = e / kCols, c = e % kCols;
             if (c < kSub) S_out[(bh * D + p) * DV + kSub * vt + c] = St[e];
             else if (vt == 0) z_out[bh * D + p] = St[e];
@@ -390,7 +452,7 @@ hipError_t launch_fwd_t(const Shape& s, const void* q, const void* k, const void
                         const float* beta, void* o, const float* S0, const float* z0, float* S_out,
                         float* z_out, hipStream_t st) {
     dim3 grid(s.dv / kSub, s.B * s.H);
-    delta_fwd_kernel<TIn, DK, C><<<grid, kThreads, 0, st>>>(
+    delta_fwd_kernel<TIn, DK, C><<<grid, kFwdThreads, 0, st>>>(
         (const TIn*)q, (const TIn*)k, (const TIn*)v, beta, (TIn*)o, S0, z0, S_out, z_out, s.T, s.dv);
     return hipGetLastError();
 }
