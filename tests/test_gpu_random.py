@@ -1,4 +1,5 @@
-"""Seeded random configurations across every option of the chunked forwards:
+"""Seeded random configurations across every option of the chunked forwards (and
+of the factored-feature and DeltaKATA forwards, below):
 batch, heads, any length T (ragged tails, T not a multiple of 4 across heads),
 d_k, d_v, chunk, dtype, feature map, prefix method, causal or not, decay gate,
 initial state. Each runs through the C ABI and is compared with the float64
@@ -193,3 +194,105 @@ def test_random_decode(kata, c):
         assert row_rel_err(host(o), o_ref) <= (1e-5 if dtype == "f32" else 2e-2)
     assert state_rel_err(host(S), S_ref, lead=1) <= 1e-5
     assert state_rel_err(host(z), z_ref, lead=1) <= 1e-5
+
+
+# ---- factored PSD features (KATA-Mg / KATA-Sigma-g) -------------------------------
+
+FACTORED_SHAPES = [(16, 2, "multi"), (16, 2, "summed"), (16, 4, "multi"), (16, 4, "summed"),
+                   (32, 4, "multi"), (32, 4, "summed"), (32, 2, "summed")]
+
+
+def _draw_factored(i):
+    r = np.random.Generator(np.random.PCG64(7900 + i))
+    dk, g, kind = FACTORED_SHAPES[int(r.integers(0, len(FACTORED_SHAPES)))]
+    return {"B": int(r.integers(1, 3)), "H": int(r.integers(1, 4)),
+            "T": int(r.choice([int(r.integers(1, 9)), int(r.integers(9, 260)),
+                               int(r.integers(260, 700)), int(r.integers(2000, 9000))])),
+            "dk": dk, "g": g, "kind": kind, "dv": int(r.choice([32, 64])),
+            "causal": bool(r.random() < 0.85), "S0": bool(r.random() < 0.5),
+            "T0": int(r.choice([int(r.integers(1, 9)), int(r.integers(1, 300))]))}
+
+
+FACTORED_CASES = [_draw_factored(i) for i in range(32)]
+
+
+def _fid(c):
+    return (f"B{c['B']}H{c['H']}T{c['T']}d{c['dk']}v{c['dv']}-{c['kind']}{c['g']}"
+            f"{'' if c['causal'] else '-full'}{'-S0' if c['S0'] else ''}")
+
+
+@pytest.mark.parametrize("c", FACTORED_CASES, ids=[_fid(c) for c in FACTORED_CASES])
+def test_random_factored(kata, c):
+    """kata_factored_fwd on random shapes, lengths (up to 9000 tokens: many
+    segments), causality and initial states of 1-300 tokens, against the
+    factored oracle: outputs within 2e-2, final states within 1e-4 (split
+    operands)."""
+    import torch
+    B, H, T, dk, dv, g, kind = c["B"], c["H"], c["T"], c["dk"], c["dv"], c["g"], c["kind"]
+    T0 = c["T0"] if c["S0"] else 0
+    seed = 8000 + FACTORED_CASES.index(c)
+    q, k, v = gen.gaussian_qkv(B, H, T0 + T, dk, dv, seed=seed, dtype="bf16")
+    S0 = z0 = None
+    if c["S0"]:
+        S0, z0 = O.factored_state_from_tokens(k[:, :, :T0], v[:, :, :T0], g, kind)
+    qs, ks, vs = q[:, :, T0:], k[:, :, T0:], v[:, :, T0:]
+    say(f"random factored {_fid(c)}")
+    init = None if S0 is None else (dev(S0), dev(z0))
+    o, (S, z) = kata.factored_fwd(dev(qs, "bf16"), dev(ks, "bf16"), dev(vs, "bf16"), g, kind,
+                                  causal=c["causal"], initial_state=init, return_state=True)
+    torch.cuda.synchronize()
+    o = host(o)
+    assert np.all(np.isfinite(o))
+    if T <= 1000:
+        ref = O.factored_brute_force(qs, ks, vs, g, kind, c["causal"], S0, z0)
+        assert row_rel_err(o, ref) <= 2e-2
+    else:
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, T - 1], np.arange(0, T, 997)]))
+        ref = O.factored_brute_force_rows(qs, ks, vs, rows, g, kind, c["causal"], S0, z0)
+        assert row_rel_err(o[:, :, rows], ref) <= 2e-2
+    S_ref, z_ref = O.factored_state_from_tokens(k, v, g, kind)
+    assert state_rel_err(host(S), S_ref) <= 1e-4 and state_rel_err(host(z), z_ref) <= 1e-4
+
+
+# ---- DeltaKATA ---------------------------------------------------------------------
+
+def _draw_delta(i):
+    r = np.random.Generator(np.random.PCG64(8100 + i))
+    return {"B": int(r.integers(1, 3)), "H": int(r.integers(1, 3)),
+            "T": int(r.choice([int(r.integers(1, 17)), int(r.integers(17, 300)), int(r.integers(300, 900))])),
+            "dk": int(r.choice([16, 32])), "dv": int(r.choice([16, 32, 64])),
+            "C": int(r.choice([16, 32, 64])), "dtype": str(r.choice(["bf16", "f32"])),
+            "S0": bool(r.random() < 0.5), "blo": float(r.choice([0.0, 0.5, 1.0]))}
+
+
+DELTA_CASES = [_draw_delta(i) for i in range(24)]
+
+
+def _did(c):
+    return (f"B{c['B']}H{c['H']}T{c['T']}d{c['dk']}v{c['dv']}C{c['C']}{c['dtype']}"
+            f"-beta{c['blo']}{'-S0' if c['S0'] else ''}")
+
+
+@pytest.mark.parametrize("c", DELTA_CASES, ids=[_did(c) for c in DELTA_CASES])
+def test_random_delta(kata, c):
+    """kata_delta_fwd on random shapes, lengths, chunk sizes and dtypes, write
+    strengths drawn from [beta_lo, 1], with and without an initial state,
+    against the delta oracle under the bars of tests/test_gpu_delta.py."""
+    import torch
+    from tests.test_gpu_delta import _check_rows
+    B, H, T, dk, dv, C, dtype = c["B"], c["H"], c["T"], c["dk"], c["dv"], c["C"], c["dtype"]
+    seed = 8200 + DELTA_CASES.index(c)
+    q, k, v = gen.gaussian_qkv(B, H, T, dk, dv, seed=seed, dtype=dtype)
+    rb = np.random.Generator(np.random.PCG64(seed + 1))
+    beta = rb.uniform(c["blo"], 1.0, (B, H, T)).astype(np.float32).astype(np.float64)
+    S0 = z0 = None
+    if c["S0"]:
+        S0, z0 = O.state_from_tokens(*gen.gaussian_qkv(B, H, 5, dk, dv, seed=seed + 2, dtype="f32")[1:])
+    say(f"random delta {_did(c)}")
+    init = None if S0 is None else (dev(S0.astype(np.float32)), dev(z0.astype(np.float32)))
+    o, (S, z) = kata.delta_fwd(dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(beta), chunk=C,
+                               initial_state=init, return_state=True)
+    torch.cuda.synchronize()
+    num, den, S_ref, z_ref = O.delta_recurrent(q, k, v, beta, S0, z0, parts=True)
+    _check_rows(host(o), num, den, dtype)
+    assert state_rel_err(host(S), S_ref) <= 1e-4 and state_rel_err(host(z), z_ref) <= 1e-4
