@@ -39,6 +39,7 @@
 // state, intra-chunk term, normalisation, store).
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "kata_chunk.h"
 #include "kata_internal.h"
@@ -49,8 +50,6 @@ namespace kata {
 namespace {
 
 constexpr int NWF = 4;                 // wavefronts per workgroup
-constexpr uint32_t kValid = 1u << 16;  // feature-table flags
-constexpr uint32_t kOffDiag = 1u << 17;
 
 template <int DK_, int G_, bool SUMMED_>
 struct Fact {
@@ -67,9 +66,9 @@ struct Fact {
 };
 
 // Factor (multi: its index; summed: 0) and element pair (i <= j, within the
-// factor) of feature f < D in the packed order.
+// factor) of feature f < D in the packed order (compile-time for the lifts).
 template <class F>
-__host__ __device__ inline void feature_pair(int f, int* a, int* i, int* j) {
+__host__ __device__ constexpr void feature_pair(int f, int* a, int* i, int* j) {
     *a = F::SUMMED ? 0 : f / F::NF;
     int r = f % F::NF, row = 0;
     while (r >= F::P - row) {                      // row `row` holds P - row entries
@@ -80,46 +79,136 @@ __host__ __device__ inline void feature_pair(int f, int* a, int* i, int* j) {
     *j = row + r;
 }
 
-// LDS feature table: entry f = element indices (in the row) of the pair,
-// validity and the off-diagonal flag; summed features name factor 0's pair.
-template <class F>
-__device__ __forceinline__ void fill_table(uint32_t* tab, int tid, int nthr) {
-    for (int f = tid; f < 32 * F::NPAIR; f += nthr) {
-        uint32_t e = 0;
-        if (f < F::D) {
-            int a, i, j;
-            feature_pair<F>(f, &a, &i, &j);
-            e = (uint32_t)(a * F::P + i) | ((uint32_t)(a * F::P + j) << 8) | kValid |
-                (i != j ? kOffDiag : 0u);
-        }
-        tab[f] = e;
+// Lifted rows of the chunk in LDS: per feature tile, [C][16] bf16 rows (32
+// bytes, swizzled as staged rows) of the hi and the lo parts, keys then
+// queries. Key tiles are read as transposed A fragments of the state update,
+// query tiles as B fragments of the inter-chunk term.
+template <int C, int NP>
+struct Lifted {
+    static constexpr int TILE = C * 32;            // bytes of one [C][16] bf16 tile
+    // part: 0 key hi, 1 key lo, 2 query hi, 3 query lo (NP = 2: keys only)
+    __device__ static const bf16_t* tile(const char* base, int at, int part) {
+        return reinterpret_cast<const bf16_t*>(base + (NP * at + part) * TILE);
     }
-}
+    __device__ static char* tile_w(char* base, int at, int part) { return base + (NP * at + part) * TILE; }
+};
 
-// bf16 element e of staged row r (rows of DK bf16, swizzled), as fp32.
+// The staged row r (DK bf16, swizzled) as fp32.
 template <int DK>
-__device__ __forceinline__ float elem(const bf16_t* rows, int r, int e) {
-    const uint16_t h = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(rows) +
-                                                          Swz<2 * DK>::off(r, 2 * e));
-    return __uint_as_float((uint32_t)h << 16);
+__device__ __forceinline__ void load_row(const bf16_t* rows, int r, float (&x)[DK]) {
+#pragma unroll
+    for (int u = 0; u < DK / 8; ++u) {
+        const u32x4_t w = lds_row<2 * DK, u32x4_t>(rows, r, 16 * u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[8 * u + 2 * e] = lo_bf16(w[e]);
+            x[8 * u + 2 * e + 1] = hi_bf16(w[e]);
+        }
+    }
 }
 
-// Feature (table entry e) of staged row r, in fp32: products of bf16 values
-// are exact, a summed feature adds the G factors' products.
-template <class F>
-__device__ __forceinline__ float lift(const bf16_t* rows, int r, uint32_t e) {
-    if (!(e & kValid)) return 0.0f;
-    const int i = e & 0xff, j = (e >> 8) & 0xff;
-    float acc;
-    if constexpr (F::SUMMED) {
-        acc = 0.0f;
-#pragma unroll
-        for (int a = 0; a < F::G; ++a)
-            acc += elem<F::DK>(rows, r, a * F::P + i) * elem<F::DK>(rows, r, a * F::P + j);
+// Feature f of a row x (fp32; products of bf16 values are exact, a summed
+// feature adds the G factors' products), f compile-time.
+template <class F, int f>
+__device__ __forceinline__ float lift_value(const float (&x)[F::DK]) {
+    if constexpr (f >= F::D) {
+        return 0.0f;
     } else {
-        acc = elem<F::DK>(rows, r, i) * elem<F::DK>(rows, r, j);
+        constexpr int a = [] { int a_ = 0, i_ = 0, j_ = 0; feature_pair<F>(f, &a_, &i_, &j_); return a_; }();
+        constexpr int i = [] { int a_ = 0, i_ = 0, j_ = 0; feature_pair<F>(f, &a_, &i_, &j_); return i_; }();
+        constexpr int j = [] { int a_ = 0, i_ = 0, j_ = 0; feature_pair<F>(f, &a_, &i_, &j_); return j_; }();
+        float acc;
+        if constexpr (F::SUMMED) {
+            acc = 0.0f;
+#pragma unroll
+            for (int b = 0; b < F::G; ++b) acc += x[b * F::P + i] * x[b * F::P + j];
+        } else {
+            acc = x[a * F::P + i] * x[a * F::P + j];
+        }
+        return i != j ? acc * kSqrt2 : acc;
     }
-    return (e & kOffDiag) ? acc * kSqrt2 : acc;
+}
+
+// Tile AT (features 16 AT .. 16 AT + 15) of row r: split into hi and lo and
+// written as two 32-byte rows.
+template <class F, int AT, int... c>
+__device__ __forceinline__ void lift16(const float (&x)[F::DK], float (&f)[16],
+                                       std::integer_sequence<int, c...>) {
+    ((f[c] = lift_value<F, 16 * AT + c>(x)), ...);
+}
+
+template <class F, int C, int NP, int AT>
+__device__ __forceinline__ void lift_tile(const float (&x)[F::DK], char* lifted, int r, int part0) {
+    float f[16];
+    lift16<F, AT>(x, f, std::make_integer_sequence<int, 16>{});
+    u32x4_t hi[2], lo[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float g8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) g8[e] = f[8 * h + e];
+        split8(g8, hi[h], lo[h]);
+    }
+    char* th = Lifted<C, NP>::tile_w(lifted, AT, part0);
+    char* tl = Lifted<C, NP>::tile_w(lifted, AT, part0 + 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        *reinterpret_cast<u32x4_t*>(th + Swz<32>::off(r, 16 * h)) = hi[h];
+        *reinterpret_cast<u32x4_t*>(tl + Swz<32>::off(r, 16 * h)) = lo[h];
+    }
+}
+
+// Tiles R, R + 4, ... of row r.
+template <class F, int C, int NP, int R>
+__device__ __forceinline__ void lift_tiles(const float (&x)[F::DK], char* lifted, int r, int part0) {
+    if constexpr (R < F::NAT) {
+        lift_tile<F, C, NP, R>(x, lifted, r, part0);
+        lift_tiles<F, C, NP, R + 4>(x, lifted, r, part0);
+    }
+}
+
+// The lifted key (WITH_K) and query (WITH_Q) tiles of the staged chunk:
+// thread t takes row t / 4 and the tiles congruent to t % 4 modulo 4.
+template <class F, int C, int NP, bool WITH_K, bool WITH_Q>
+__device__ __forceinline__ void lift_chunk(const bf16_t* bq, const bf16_t* bk, char* lifted, int tid) {
+    static_assert(C * 4 == 64 * NWF, "four threads per row");
+    const int r = tid >> 2, q4 = tid & 3;
+    float x[F::DK];
+    if constexpr (WITH_K) {
+        load_row<F::DK>(bk, r, x);
+        switch (q4) {
+            case 0: lift_tiles<F, C, NP, 0>(x, lifted, r, 0); break;
+            case 1: lift_tiles<F, C, NP, 1>(x, lifted, r, 0); break;
+            case 2: lift_tiles<F, C, NP, 2>(x, lifted, r, 0); break;
+            default: lift_tiles<F, C, NP, 3>(x, lifted, r, 0); break;
+        }
+    }
+    if constexpr (WITH_Q) {
+        load_row<F::DK>(bq, r, x);
+        switch (q4) {
+            case 0: lift_tiles<F, C, NP, 0>(x, lifted, r, 2); break;
+            case 1: lift_tiles<F, C, NP, 1>(x, lifted, r, 2); break;
+            case 2: lift_tiles<F, C, NP, 2>(x, lifted, r, 2); break;
+            default: lift_tiles<F, C, NP, 3>(x, lifted, r, 2); break;
+        }
+    }
+}
+
+// The B operand slots of tile pair P2 for lane group G4 of a query row x:
+// slot s is feature 16 (2 P2 + s / 4) + 4 G4 + s % 4 (compile-time pairs).
+template <class F, int P2, int G4, int... s>
+__device__ __forceinline__ void query_slots(const float (&x)[F::DK], float (&f)[8],
+                                            std::integer_sequence<int, s...>) {
+    ((f[s] = lift_value<F, 16 * (2 * P2 + s / 4) + 4 * G4 + s % 4>(x)), ...);
+}
+template <class F, int P2>
+__device__ __forceinline__ void query_feats(const float (&x)[F::DK], int g, float (&f)[8]) {
+    switch (g) {
+        case 0: query_slots<F, P2, 0>(x, f, std::make_integer_sequence<int, 8>{}); break;
+        case 1: query_slots<F, P2, 1>(x, f, std::make_integer_sequence<int, 8>{}); break;
+        case 2: query_slots<F, P2, 2>(x, f, std::make_integer_sequence<int, 8>{}); break;
+        default: query_slots<F, P2, 3>(x, f, std::make_integer_sequence<int, 8>{}); break;
+    }
 }
 
 // Running state of one wavefront: units (tile W + 4 o, u), u = DV/16 the z
@@ -144,16 +233,14 @@ __device__ __forceinline__ void state_zero(FState<F, DV>& st) {
 }
 
 // S += phi(K_c)^T [V_c | 1] for the wavefront's tiles: A = lifted keys (lane
-// c16 = feature, slots = tokens 32m + 16(s/4) + 4g + s%4) as split operands,
-// B = V^T fragments (exact bf16) or the ones operand.
-template <int W, class F, int DV, int C>
-__device__ __forceinline__ void state_update(FState<F, DV>& st, const uint32_t* tab,
-                                             const bf16_t* bk, const bf16_t* bv, const Lane& L) {
+// c16 = feature, slots = tokens 32m + 16(s/4) + 4g + s%4), read transposed from
+// the lifted hi and lo tiles, against exact bf16 V^T fragments or the ones
+// operand.
+template <int W, class F, int DV, int C, int NP>
+__device__ __forceinline__ void state_update(FState<F, DV>& st, const char* lifted,
+                                             const bf16_t* bv, const Lane& L) {
     constexpr int NTV = DV / 16, NU = NTV + 1;
     const u32x4_t ones = ones_op(L);
-    uint32_t ent[F::NOWN];
-#pragma unroll
-    for (int o = 0; o < F::NOWN; ++o) ent[o] = owned<W, F>(o) ? tab[16 * (W + NWF * o) + L.c16] : 0u;
 #pragma unroll
     for (int m = 0; m < C / 32; ++m) {
         u32x4_t b[NU];
@@ -162,12 +249,9 @@ __device__ __forceinline__ void state_update(FState<F, DV>& st, const uint32_t* 
 #pragma unroll
         for (int o = 0; o < F::NOWN; ++o) {
             if (!owned<W, F>(o)) continue;
-            float f[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-                f[s] = lift<F>(bk, 32 * m + 16 * (s / 4) + 4 * L.g + s % 4, ent[o]);
-            u32x4_t hi, lo;
-            split8(f, hi, lo);
+            const int at = W + NWF * o;
+            const u32x4_t hi = v_fragment_tr<16>(Lifted<C, NP>::tile(lifted, at, 0), m, 0, L);
+            const u32x4_t lo = v_fragment_tr<16>(Lifted<C, NP>::tile(lifted, at, 1), m, 0, L);
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 st.s[o][u] = mma32(hi, b[u], st.s[o][u]);
@@ -229,6 +313,32 @@ __device__ __forceinline__ void publish(const FState<F, DV>& st, char* pub, cons
     }
 }
 
+// num[u] += S^T (published, split) . phi(q) (split) over tile pair P2.
+template <class F, int DV, int P2>
+__device__ __forceinline__ void inter_pair(const float (&x)[F::DK], const char* pub,
+                                           f32x4_t (&num)[DV / 16 + 1], const Lane& L) {
+    using PB = Pub<F, DV>;
+    float f[8];
+    query_feats<F, P2>(x, L.g, f);
+    u32x4_t qh, ql;
+    split8(f, qh, ql);
+#pragma unroll
+    for (int u = 0; u < PB::NU; ++u) {
+        const int off = PB::off(P2, u, L.lane);
+        const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(pub + off);
+        const u32x4_t al = *reinterpret_cast<const u32x4_t*>(pub + PB::BYTES + off);
+        num[u] = mma32(ah, qh, num[u]);
+        num[u] = mma32(ah, ql, num[u]);
+        num[u] = mma32(al, qh, num[u]);
+    }
+}
+template <class F, int DV, int... P2>
+__device__ __forceinline__ void inter_pairs(const float (&x)[F::DK], const char* pub,
+                                            f32x4_t (&num)[DV / 16 + 1], const Lane& L,
+                                            std::integer_sequence<int, P2...>) {
+    (inter_pair<F, DV, P2>(x, pub, num, L), ...);
+}
+
 // Scores of 16 keys (staged rows krow .. +15: lane c16 = key) against this
 // lane's query: D[key 4g + r][query c16] = the weight of that pair, sum over
 // factor pairs of their squared inner products.
@@ -268,16 +378,17 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
     Pipeline<F::DK, DV, C, NWF> P{lds, seg * Gs, min(NC, seg * Gs + Gs), T, bh * T, false};
-    uint32_t* tab = reinterpret_cast<uint32_t*>(lds + 2 * IO::BUF);
-    fill_table<F>(tab, threadIdx.x, 64 * NWF);
+    char* lifted = lds + 2 * IO::BUF;              // lifted key tiles of the chunk
     FState<F, DV> st;
     state_zero<W, F, DV>(st);
     P.stage(nullptr, k, v, P.c0, L);
     for (int c = P.c0; c < P.c1; ++c) {
-        P.acquire(nullptr, k, v, c, L);
+        P.acquire(nullptr, k, v, c, L);            // also: every wavefront is done with chunk c - 1's lifts
         const char* buf = P.buffer(c);
-        state_update<W, F, DV, C>(st, tab, reinterpret_cast<const bf16_t*>(buf + IO::QB),
-                                  reinterpret_cast<const bf16_t*>(buf + 2 * IO::QB), L);
+        lift_chunk<F, C, 2, true, false>(nullptr, reinterpret_cast<const bf16_t*>(buf + IO::QB), lifted,
+                                         threadIdx.x);
+        lds_barrier();
+        state_update<W, F, DV, C, 2>(st, lifted, reinterpret_cast<const bf16_t*>(buf + 2 * IO::QB), L);
         compiler_fence();
     }
     constexpr int REC = F::NAT * (DV / 16 + 1) * 256;
@@ -286,7 +397,7 @@ __device__ __forceinline__ void seg_state_body(const bf16_t* k, const bf16_t* v,
 
 template <class F, int DV, int C>
 constexpr int lds_seg() {
-    return 2 * ChunkIO<F::DK, DV, C, NWF>::BUF + 32 * F::NPAIR * 4;
+    return 2 * ChunkIO<F::DK, DV, C, NWF>::BUF + 2 * F::NAT * Lifted<C, 2>::TILE;
 }
 
 template <class F, int DV, int C>
@@ -308,7 +419,7 @@ __global__ __launch_bounds__(64 * NWF) void kata_fact_seg_state(const bf16_t* __
 
 template <class F, int DV, int C>
 constexpr int lds_fwd() {
-    return 2 * ChunkIO<F::DK, DV, C, NWF>::BUF + 32 * F::NPAIR * 4 + 2 * Pub<F, DV>::BYTES;
+    return 2 * ChunkIO<F::DK, DV, C, NWF>::BUF + 2 * F::NAT * Lifted<C, 2>::TILE + 2 * Pub<F, DV>::BYTES;
 }
 
 template <int W, class F, int DV, int C, bool CAUSAL>
@@ -324,9 +435,8 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
     Pipeline<F::DK, DV, C, NWF> P{lds, seg * Gs, min(NC, seg * Gs + Gs), T, bh * T, true};
-    uint32_t* tab = reinterpret_cast<uint32_t*>(lds + 2 * IO::BUF);
-    char* pub = lds + 2 * IO::BUF + 32 * F::NPAIR * 4;
-    fill_table<F>(tab, threadIdx.x, 64 * NWF);
+    char* lifted = lds + 2 * IO::BUF;              // lifted key tiles of the chunk
+    char* pub = lifted + 2 * F::NAT * Lifted<C, 2>::TILE;
     // the second half of an odd last tile pair is never published: zero it all
     for (int i = threadIdx.x; i < 2 * PB::BYTES / 16; i += 64 * NWF)
         reinterpret_cast<u32x4_t*>(pub)[i] = u32x4_t{0u, 0u, 0u, 0u};
@@ -345,7 +455,9 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         const bf16_t* bq = reinterpret_cast<const bf16_t*>(buf);
         const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + IO::QB);
         const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * IO::QB);
-        // the state before this chunk (the whole sequence's when not causal)
+        // the chunk's lifted queries (and keys, for the state update), and the
+        // state before this chunk (the whole sequence's when not causal)
+        if constexpr (CAUSAL) lift_chunk<F, C, 2, true, false>(nullptr, bk, lifted, threadIdx.x);
         if (CAUSAL || c == P.c0) {
             publish<W, F, DV>(st, pub, L);
             lds_barrier();
@@ -354,28 +466,12 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
         f32x4_t num[NU];
 #pragma unroll
         for (int u = 0; u < NU; ++u) num[u] = zero4();
-        // ---- inter-chunk term phi(q).S and phi(q).z, split operands
-#pragma unroll
-        for (int p = 0; p < F::NPAIR; ++p) {
-            const u32x4_t e0 = *reinterpret_cast<const u32x4_t*>(tab + 32 * p + 4 * L.g);
-            const u32x4_t e1 = *reinterpret_cast<const u32x4_t*>(tab + 32 * p + 16 + 4 * L.g);
-            float f[8];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                f[s] = lift<F>(bq, qrow, e0[s]);
-                f[4 + s] = lift<F>(bq, qrow, e1[s]);
-            }
-            u32x4_t qh, ql;
-            split8(f, qh, ql);
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                const int off = PB::off(p, u, L.lane);
-                const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(pub + off);
-                const u32x4_t al = *reinterpret_cast<const u32x4_t*>(pub + PB::BYTES + off);
-                num[u] = mma32(ah, qh, num[u]);
-                num[u] = mma32(ah, ql, num[u]);
-                num[u] = mma32(al, qh, num[u]);
-            }
+        // ---- inter-chunk term phi(q).S and phi(q).z, split operands; this
+        // lane's query features lifted from its row in registers
+        {
+            float x[F::DK];
+            load_row<F::DK>(bq, qrow, x);
+            inter_pairs<F, DV>(x, pub, num, L, std::make_integer_sequence<int, F::NPAIR>{});
         }
         // ---- intra-chunk term: weights of keys j <= t of this chunk times [V | 1]
         if constexpr (CAUSAL) {
@@ -415,7 +511,7 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
                     u32x2_t{pk2(num[nt][0] * y, num[nt][1] * y), pk2(num[nt][2] * y, num[nt][3] * y)};
         }
         // ---- running state (not needed after the segment's last chunk)
-        if (CAUSAL && c + 1 < P.c1) state_update<W, F, DV, C>(st, tab, bk, bv, L);
+        if (CAUSAL && c + 1 < P.c1) state_update<W, F, DV, C, 2>(st, lifted, bv, L);
         compiler_fence();
     }
 }
