@@ -338,27 +338,31 @@ def recall_forward(kata, torch, gen, steps, warmup):
 
 
 def delta_forward(kata, torch, gen, steps, warmup):
-    """DeltaKATA (kata_delta_fwd) on the recall-shaped stream at full size (B=8,
-    H=4, T=16384, d_k=16, d_v=64, C=64) with write strength 1 (the overwrite
-    the delta rule is for): ms, tokens/s and its fp32 rate against the fp32
-    peak (157.3 TFLOP/s, the same for the vector ALUs and the fp32 matrix
-    cores the kernel's products run on).
-    Flops per token-head and value tile of 16 columns + z (fp32 FMAs x 2): the
-    products K A, phi(Q) A and K^T P over D (3 x 2 D x 17), the chunk's key and
-    query Gram terms (2 x 2 C d_k), the masked phi(Q) K^T P (C x 17) and the
-    blocked triangular solve (about C x 17 + 16 x 16)."""
+    """DeltaKATA (kata_delta_fwd: the per-chunk inverse kernel, then the chunk
+    walk) on the recall-shaped stream at full size (B=8, H=4, T=16384, d_k=16,
+    d_v=64, C=64) with write strength 1 (the overwrite the delta rule is for):
+    ms, tokens/s and its fp32 rate against the fp32 peak (157.3 TFLOP/s, the
+    same for the vector ALUs and the fp32 matrix cores the products run on).
+    Algorithmic flops per token-head (fp32 FMAs x 2, the whole state of d_v + 1
+    columns once): the products K A, phi(Q) A and K^T P over D (3 x 2 D (d_v+1)),
+    the lower-triangular T R and masked-weight products (2 x 2 (C/2) (d_v+1)),
+    the chunk's key and query Gram terms (2 x 2 C d_k) and the triangular
+    inverse (2 C^2 / 3)."""
     w = gen.WORKLOADS["recall16k"]
     to = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
     q, k, v = (to(a) for a in gen.recall_stream(w.B, w.H, w.T, w.dk, w.dv, w.seed, w.dtype))
     beta = torch.ones((w.B, w.H, w.T), device="cuda")
     o = torch.empty_like(v)
-    ms = time_calls(torch, lambda: kata.delta_fwd_into(q, k, v, beta, o, w.chunk), steps, warmup)
-    D, C, tiles = w.dk * (w.dk + 1) // 2, w.chunk, w.dv // 16
-    per_tile = 3 * 2 * D * 17 + 2 * 2 * C * w.dk + 2 * C * 17 + 2 * (C * 17 + 256)
-    flops = w.B * w.H * w.T * tiles * per_tile
+    nws = kata.delta_fwd_workspace(w.B, w.H, w.T, w.dk, w.dv, w.chunk, 1)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ms = time_calls(torch, lambda: kata.delta_fwd_into(q, k, v, beta, o, w.chunk, workspace=ws),
+                    steps, warmup)
+    D, C, cols = w.dk * (w.dk + 1) // 2, w.chunk, w.dv + 1
+    per_token = 3 * 2 * D * cols + 2 * 2 * (C // 2) * cols + 2 * 2 * C * w.dk + 2 * C * C / 3
+    flops = w.B * w.H * w.T * per_token
     return {"ms": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3), "alg_tflops": flops / (ms * 1e-3) / 1e12,
             "vs_fp32_peak": flops / (ms * 1e-3) / 1e12 / 157.3,
-            "workgroups": w.B * w.H * tiles, "beta": 1.0, "workload": "recall16k"}
+            "workgroups": w.B * w.H * -(-w.dv // 15), "beta": 1.0, "workload": "recall16k"}
 
 
 def factored_forward(kata, torch, gen, steps, warmup):

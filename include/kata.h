@@ -326,16 +326,29 @@ kata_status_t kata_decode_step(const void* q, const void* k, const void* v,
  *   beta [B,H,T] (fp32, device) - write strengths, expected in [0, 1].
  *   chunk - 16, 32 or 64: chunks are walked in order (the state transition is
  *     matrix-affine); inside a chunk a unit lower-triangular system gives the
- *     tokens' writes, solved in blocks of 16.
+ *     tokens' writes. Its inverse depends only on the chunk's keys and write
+ *     strengths, so a first kernel forms it for every chunk at once (blocks of
+ *     16, by forward substitution); the walk then does four matrix products
+ *     per chunk.
  *   S0, z0 / S_out, z_out - optional initial / final state as kata_chunked_fwd
  *     (the packed layout; both of a pair or neither).
+ *   workspace - device memory of kata_delta_fwd_workspace() bytes, 16-byte
+ *     aligned, owned by the caller (NULL only when B*H*T == 0); it holds each
+ *     chunk's inverse and masked weights between the two kernels.
  * d_k in {16, 32}, d_v in {16, 32, 64}, fp32 or bf16 inputs, any T >= 0; fp32
- * arithmetic throughout; no workspace. One workgroup per (batch, head, 16 value
- * columns). Errors as kata_chunked_fwd (chunk 128: KATA_EUNSUPPORTED). */
+ * arithmetic throughout. The walk runs one workgroup per (batch, head, 15 value
+ * columns plus the denominator column). Errors as kata_chunked_fwd (chunk 128:
+ * KATA_EUNSUPPORTED; a short workspace: KATA_EWORKSPACE). */
 kata_status_t kata_delta_fwd(const void* q, const void* k, const void* v, const float* beta,
                              void* o, int B, int H, int T, int d_k, int d_v, int chunk,
                              kata_dtype_t dtype, const float* S0, const float* z0,
-                             float* S_out, float* z_out, void* stream);
+                             float* S_out, float* z_out, void* workspace, size_t ws_bytes,
+                             void* stream);
+
+/* Bytes of workspace kata_delta_fwd needs for this shape: 8 C^2 per (batch,
+ * head, chunk); 0 for an unsupported shape. */
+size_t kata_delta_fwd_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                kata_dtype_t dtype);
 
 /* One DeltaKATA decode step for N rows: [S | z] += beta kappa ([v, 1] -
  * kappa^T [S | z]) in place, then o = phi(q).S / phi(q).z. Shapes, dtypes and

@@ -19,7 +19,7 @@ from ._binding import (KataError, chunked_fwd, chunked_fwd_into, chunked_fwd_wor
                        decode_step, decode_step_decay, feature_dim, flash_fwd, lib, phi_dim,
                        scan_states, scan_states_into, chunked_fwd_noalloc_into,
                        NOALLOC_SCRATCH_BYTES, prefix_depth, delta_fwd, delta_fwd_into,
-                       decode_step_delta, factored_dim, factored_fwd, factored_fwd_into,
+                       decode_step_delta, delta_fwd_workspace, factored_dim, factored_fwd, factored_fwd_into,
                        factored_fwd_workspace, decode_step_factored, LIB_PATH)
 
 __version__ = "0.2.0"

@@ -15,7 +15,7 @@ __all__ = ["KataError", "lib", "chunked_fwd", "chunked_fwd_into", "chunked_fwd_w
            "scan_states", "flash_fwd", "decode_step", "phi_dim", "feature_dim",
            "chunked_fwd_decay", "chunked_fwd_decay_into", "chunked_fwd_decay_workspace",
            "decode_step_decay", "chunked_fwd_noalloc_into", "NOALLOC_SCRATCH_BYTES", "prefix_depth",
-           "delta_fwd", "delta_fwd_into", "decode_step_delta", "LIB_PATH"]
+           "delta_fwd", "delta_fwd_into", "delta_fwd_workspace", "decode_step_delta", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkata.so")
 
@@ -88,8 +88,11 @@ def lib() -> ctypes.CDLL:
         L.kata_chunked_fwd_noalloc.restype = i
         L.kata_prefix_depth.argtypes = [i, i, i, i, i, i, i, i, i, i]
         L.kata_prefix_depth.restype = i
-        L.kata_delta_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, vp, vp]
+        L.kata_delta_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, vp,
+                                     vp, sz, vp]
         L.kata_delta_fwd.restype = i
+        L.kata_delta_fwd_workspace.argtypes = [i, i, i, i, i, i, i]
+        L.kata_delta_fwd_workspace.restype = sz
         L.kata_decode_step_delta.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
         L.kata_decode_step_delta.restype = i
         L.kata_factored_dim.argtypes = [i, i, i]
@@ -465,8 +468,14 @@ def decode_step_decay(q, k, v, log_decay, S, z, out=None):
 
 # ---- DeltaKATA ---------------------------------------------------------------------
 
-def delta_fwd_into(q, k, v, beta, o, chunk, S0=None, z0=None, S_out=None, z_out=None):
-    """Raw kata_delta_fwd into preallocated outputs."""
+def delta_fwd_workspace(B, H, T, dk, dv, chunk, dtype_code) -> int:
+    return lib().kata_delta_fwd_workspace(B, H, T, dk, dv, chunk, dtype_code)
+
+
+def delta_fwd_into(q, k, v, beta, o, chunk, S0=None, z0=None, S_out=None, z_out=None,
+                   workspace=None):
+    """Raw kata_delta_fwd into preallocated outputs (the workspace is allocated
+    here when not given)."""
     _check_qkv(q, k, v, o)
     _check_dev(beta)
     B, H, T, dk = q.shape
@@ -476,9 +485,15 @@ def delta_fwd_into(q, k, v, beta, o, chunk, S0=None, z0=None, S_out=None, z_out=
     D = phi_dim(dk)
     _check_state(S0, z0, (B, H), D, dv, "initial state")
     _check_state(S_out, z_out, (B, H), D, dv, "final state")
+    if workspace is None:
+        nbytes = delta_fwd_workspace(B, H, T, dk, dv, chunk, _dtype_code(q))
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+    else:
+        _check_dev(workspace)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().kata_delta_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(o), B, H, T, dk, dv,
                               chunk, _dtype_code(q), _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out),
-                              _stream())
+                              _ptr(workspace), nbytes, _stream())
     _raise(st, "kata_delta_fwd")
 
 

@@ -663,10 +663,18 @@ kata_status_t kata_decode_step(const void* q, const void* k, const void* v, floa
 
 // ---- DeltaKATA ---------------------------------------------------------------
 
+size_t kata_delta_fwd_workspace(int B, int H, int T, int d_k, int d_v, int chunk,
+                                kata_dtype_t dtype) {
+    Shape s;
+    if (make_shape(B, H, T, d_k, d_v, chunk, dtype, &s) != KATA_OK || !kata::delta_supported(s))
+        return 0;
+    return kata::delta_workspace_bytes(s);
+}
+
 kata_status_t kata_delta_fwd(const void* q, const void* k, const void* v, const float* beta,
                              void* o, int B, int H, int T, int d_k, int d_v, int chunk,
                              kata_dtype_t dtype, const float* S0, const float* z0, float* S_out,
-                             float* z_out, void* stream) {
+                             float* z_out, void* workspace, size_t ws_bytes, void* stream) {
     Shape s;
     kata_status_t st = make_shape(B, H, T, d_k, d_v, chunk, dtype, &s);
     if (st != KATA_OK) return st;
@@ -678,7 +686,7 @@ kata_status_t kata_delta_fwd(const void* q, const void* k, const void* v, const 
     if (!empty && (!q || !k || !v || !o || !beta)) return KATA_EINVAL;
     for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)o,
                           (const void*)beta, (const void*)S0, (const void*)z0, (const void*)S_out,
-                          (const void*)z_out})
+                          (const void*)z_out, (const void*)workspace})
         if (p && !aligned16(p)) return KATA_EINVAL;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (empty) {
@@ -689,7 +697,9 @@ kata_status_t kata_delta_fwd(const void* q, const void* k, const void* v, const 
         }
         return hip_status(e);
     }
-    return hip_status(kata::launch_delta_fwd(s, q, k, v, beta, o, S0, z0, S_out, z_out, hs));
+    if (!workspace || ws_bytes < kata::delta_workspace_bytes(s)) return KATA_EWORKSPACE;
+    return hip_status(kata::launch_delta_fwd(s, q, k, v, beta, o, S0, z0, S_out, z_out,
+                                             static_cast<float*>(workspace), hs));
 }
 
 kata_status_t kata_decode_step_delta(const void* q, const void* k, const void* v,

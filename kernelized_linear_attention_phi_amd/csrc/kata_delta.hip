@@ -11,120 +11,327 @@
 // explainers' chunked-state form, summary 2.3, with the delta rule's chunk
 // recursion): inside chunk c with the state A before it,
 //     R = U - K A                      (K rows kappa_t),
-//     (I + diag(beta) L) P = diag(beta) R,   L the strictly lower part of K K^T,
+//     P = T R,   T = (I + diag(beta) L)^-1 diag(beta),   L the strictly lower
+//                                      part of K K^T,
 //     O = phi(Q) A + mask(phi(Q) K^T) P      (inclusive causal mask),
 //     A <- A + K^T P.
-// The triangular system is solved in blocks of 16 rows: the inverse of each
-// unit lower-triangular 16 x 16 diagonal block by forward substitution (one
-// thread per column), then block rows in order, each a product with the
-// earlier blocks' P and with its block inverse.
-//
-// One workgroup of 16 wavefronts per (batch, head, 16-column value tile) keeps
-// its 16 columns of S and the z column in LDS (the z column is recomputed by
-// every value tile of a head); the products R, O and K^T P are spread one
-// (token, column) or (feature, column) per thread. At d_k = 16 the chunk's
-// lifted keys and queries are formed once per chunk in LDS; at d_k = 32 (528
-// features, too many to hold beside the state) on the fly through a pair
-// table. Everything is fp32.
+// T and the masked weights depend on the chunk's keys, queries and write
+// strengths only, so they are formed for every chunk at once by a first kernel
+// (delta_prep_kernel, one workgroup per chunk: the inverse of each unit
+// lower-triangular 16 x 16 diagonal block by forward substitution, then block
+// rows in order). The second kernel (delta_chain_kernel) walks the chunks of one
+// (batch, head, value tile) in order and does only the four products above on
+// the fp32 matrix cores. A value tile is 15 value columns plus the z column,
+// so one 16-column product tile carries both numerator and denominator.
+// Scalings: with Inv_t = 1 / |k_t|^2 the first kernel stores diag(Inv) T and
+// the mask of (q_t.k_j)^2, so the chain works with the plain lifts phi(k),
+// phi(q):  R = U - diag(Inv) phi(K) A,  P' = diag(Inv) T R,
+// O = phi(Q) A + mask((Q K^T)^2) P',  A <- A + phi(K)^T P'.
 #include "kata_device.h"
 #include "kata_internal.h"
 #include "kata_mfma.h"
+
+#include <utility>
 
 namespace kata {
 
 namespace {
 
 constexpr int kThreads = 256;          // decode
-constexpr int kFwdThreads = 1024;      // forward: 16 wavefronts per (head, value tile)
-constexpr int kCols = 17;              // 16 value columns + z
+constexpr int kPrepThreads = 256;      // per-chunk triangular inverses
+constexpr int kChainThreads = 512;     // chunk walk: 8 wavefronts per (head, value tile)
 constexpr int kSub = 16;               // rows per block of the triangular solve
-
-template <int DK, int C>
-struct DeltaCfg {
-    static constexpr int D = DK * (DK + 1) / 2;
-    static constexpr int NB = C / kSub;
-    // LDS layout, in floats
-    static constexpr int S_OFF = 0;                           // state [D][17]
-    static constexpr int K_OFF = S_OFF + D * kCols;           // keys [C][DK]
-    static constexpr int Q_OFF = K_OFF + C * DK;              // queries [C][DK]
-    static constexpr int U_OFF = Q_OFF + C * DK;              // [v | 1] [C][17]
-    static constexpr int INV_OFF = U_OFF + C * kCols;         // 1 / |k_t|^2 [C]
-    static constexpr int B_OFF = INV_OFF + C;                 // beta [C]
-    static constexpr int G_OFF = B_OFF + C;                   // beta_t kappa_t.kappa_j, j < t [C][C]
-    static constexpr int A_OFF = G_OFF + C * C;               // phi(q_t).kappa_j, j <= t [C][C]
-    static constexpr int R_OFF = A_OFF + C * C;               // R, then the block right-hand sides [C][17]
-    static constexpr int P_OFF = R_OFF + C * kCols;           // P [C][17]
-    static constexpr int TI_OFF = P_OFF + C * kCols;          // block inverses [NB][16][16]
-    static constexpr int O_OFF = TI_OFF + NB * kSub * kSub;   // outputs [C][17]
-    static constexpr int BASE = O_OFF + C * kCols;
-    // the chunk's lifted keys kappa [C][D] and queries phi(q) [C][D], formed
-    // once per chunk where they fit next to the rest (d_k = 16)
-    static constexpr bool PRE = (BASE + 2 * C * D) * 4 + D * 4 <= 150 * 1024;
-    static constexpr int KAP_OFF = BASE;
-    static constexpr int FQ_OFF = KAP_OFF + C * D;
-    static constexpr int FLOATS = PRE ? FQ_OFF + C * D : BASE;
-    static_assert(C % kSub == 0 && NB * kSub <= kFwdThreads && kSub * kCols <= kFwdThreads,
-                  "chunk of 16, 32 or 64");
-    static_assert(FLOATS * 4 + D * 4 <= 160 * 1024, "fits the LDS of a compute unit");
-};
+constexpr int kTileCols = 16;          // state columns per workgroup: 15 values + z
+constexpr int kVals = 15;
 
 // D = A(16x4) * B(4x16) + C in fp32 (v_mfma_f32_16x16x4_f32): fp32 operands,
-// fp32 accumulation.
+// fp32 accumulation. Lane (c16, g) supplies A[c16][g] and B[g][c16] and holds
+// rows 4g + r of column c16 of the result.
 __device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Per-chunk matrices are stored in the layout the chain kernel reads them in as
+// matrix-core A operands: element (mt 64 + lane) C/4 + s of a chunk's C x C
+// matrix X holds X[16 mt + lane % 16][4 s + lane / 16], so each lane's C/4
+// values of one token tile mt are contiguous.
+
+template <int DK, int C>
+struct PrepCfg {
+    static constexpr int NB = C / kSub;
+    static constexpr int MT = C / 16;
+    // LDS, in floats
+    static constexpr int K_OFF = 0;                     // keys [C][DK]
+    static constexpr int Q_OFF = K_OFF + C * DK;        // queries [C][DK]
+    static constexpr int INV_OFF = Q_OFF + C * DK;      // 1 / |k_t|^2 [C]
+    static constexpr int B_OFF = INV_OFF + C;           // beta [C]
+    static constexpr int G_OFF = B_OFF + C;             // beta_t kappa_t.kappa_j, j < t [C][C]
+    static constexpr int T_OFF = G_OFF + C * C;         // T [C][C]
+    static constexpr int X_OFF = T_OFF + C * C;         // block right-hand sides [16][C]
+    static constexpr int TI_OFF = X_OFF + kSub * C;     // diagonal block inverses [NB][16][16]
+    static constexpr int FLOATS = TI_OFF + NB * kSub * kSub;
+    static_assert(C % kSub == 0 && NB * kSub <= kPrepThreads && MT <= kPrepThreads / 64,
+                  "chunk of 16, 32 or 64");
+};
+
+// One workgroup of four wavefronts per (chunk, batch*head): writes diag(Inv) T
+// and the mask of
+// (q_t.k_j)^2 (j <= t) for the chunk, 2 C^2 floats at
+// ws + ((bh * NC + chunk) * 2) C^2, in that layout.
 template <typename TIn, int DK, int C>
-__global__ __launch_bounds__(kFwdThreads) void delta_fwd_kernel(
-    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const float* __restrict__ beta, TIn* __restrict__ o, const float* __restrict__ S0,
-    const float* __restrict__ z0, float* __restrict__ S_out, float* __restrict__ z_out, int T,
-    int DV) {
-    using F = DeltaCfg<DK, C>;
-    constexpr int D = F::D, NT = kFwdThreads;
+__global__ __launch_bounds__(kPrepThreads) void delta_prep_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ beta,
+    float* __restrict__ ws, int T, int NC) {
+    using F = PrepCfg<DK, C>;
+    constexpr int NT = kPrepThreads;
     __shared__ float sm[F::FLOATS];
-    __shared__ uint32_t pairs[D];
-    float* St = sm + F::S_OFF;
     float* Ks = sm + F::K_OFF;
     float* Qs = sm + F::Q_OFF;
-    float* Us = sm + F::U_OFF;
     float* Inv = sm + F::INV_OFF;
     float* Bs = sm + F::B_OFF;
     float* G = sm + F::G_OFF;
-    float* Aq = sm + F::A_OFF;
-    float* R = sm + F::R_OFF;
-    float* P = sm + F::P_OFF;
+    float* Tm = sm + F::T_OFF;
+    float* X = sm + F::X_OFF;
     float* TI = sm + F::TI_OFF;
-    float* Os = sm + F::O_OFF;
-    float* Kap = sm + F::KAP_OFF;              // PRE only
-    float* Fq = sm + F::FQ_OFF;                // PRE only
+    float* Ms = G;                              // the masked weights, once G is done
 
-    const int vt = blockIdx.x;                 // value tile: columns 16 vt .. 16 vt + 15
+    const int chunk = blockIdx.x;
     const size_t bh = blockIdx.y;
     const int tid = threadIdx.x;
+    const int c0 = chunk * C;
+    const int n = min(C, T - c0);
+    const size_t tok0 = bh * (size_t)T + c0;
+    float* out = ws + (bh * NC + chunk) * (size_t)(2 * C * C);
 
-    for (int p = tid; p < D; p += NT) pairs[p] = pack_pair(p, DK);
-    for (int e = tid; e < D * kCols; e += NT) {
-        const int p = e / kCols, c = e % kCols;
-        float x = 0.0f;
-        if (S0) x = c < kSub ? S0[(bh * D + p) * DV + kSub * vt + c] : z0[bh * D + p];
-        St[e] = x;
+    // rows past a ragged end are zero: no key, no write, beta 0
+    for (int e = tid; e < C * DK; e += NT) {
+        const bool ok = e / DK < n;
+        Ks[e] = ok ? io<TIn>::ld(k, tok0 * DK + e) : 0.0f;
+        Qs[e] = ok ? io<TIn>::ld(q, tok0 * DK + e) : 0.0f;
+    }
+    for (int t = tid; t < C; t += NT) Bs[t] = t < n ? beta[tok0 + t] : 0.0f;
+    __syncthreads();
+    for (int t = tid; t < C; t += NT) {
+        float s = 0.0f;
+#pragma unroll
+        for (int a = 0; a < DK; ++a) s = __builtin_fmaf(Ks[t * DK + a], Ks[t * DK + a], s);
+        Inv[t] = s > 0.0f ? 1.0f / s : 0.0f;
     }
     __syncthreads();
 
-    // lifted key (kappa, scaled by 1 / |k_t|^2) and query of token t, feature p
-    auto kappa = [&](int t, int p) -> float {
+    // G = beta_t kappa_t.kappa_j (j < t), with kappa_t.kappa_j =
+    // (k_t.k_j)^2 Inv_t Inv_j; (with X = Q, after the solve) the masked
+    // weights (q_t.k_j)^2 (j <= t)
+    const int wave = tid >> 6, lane = tid & 63, c16 = lane & 15, g4 = lane >> 4;
+    auto gram = [&](const float* X, bool keys) {
+        for (int tile = wave; tile < F::MT * F::MT; tile += NT / 64) {
+            const int mt = tile / F::MT, jt = tile % F::MT;
+            f32x4_t d = zero4();
+#pragma unroll
+            for (int s4 = 0; s4 < DK / 4; ++s4) {
+                const int a = 4 * s4 + g4;
+                d = mfma4(X[(16 * mt + c16) * DK + a], Ks[(16 * jt + c16) * DK + a], d);
+            }
+            const int jj = 16 * jt + c16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * mt + 4 * g4 + r;
+                if (keys) G[t * C + jj] = jj < t ? Bs[t] * (d[r] * d[r]) * (Inv[t] * Inv[jj]) : 0.0f;
+                else Ms[t * C + jj] = jj <= t ? d[r] * d[r] : 0.0f;
+            }
+        }
+    };
+    gram(Ks, true);
+    __syncthreads();
+
+    // inverses of the diagonal blocks I + G_bb: column j of each by forward
+    // substitution
+    if (tid < F::NB * kSub) {
+        const int b = tid / kSub, j = tid % kSub, r0 = kSub * b;
+        float x[kSub];
+#pragma unroll
+        for (int r = 0; r < kSub; ++r) {
+            float s = r == j ? 1.0f : 0.0f;
+#pragma unroll
+            for (int s2 = 0; s2 < r; ++s2) s = __builtin_fmaf(-G[(r0 + r) * C + r0 + s2], x[s2], s);
+            x[r] = s;
+        }
+#pragma unroll
+        for (int r = 0; r < kSub; ++r) TI[(b * kSub + r) * kSub + j] = x[r];
+    }
+    __syncthreads();
+
+    // block rows of (I + G) T = diag(beta) in order,
+    // T_b = inv_b (diag(beta)_b - G_{b,<b} T_{<b}), both products on the matrix
+    // cores: wavefront w forms column tile w of the block row (T is lower
+    // triangular, so tiles right of the diagonal block are zero)
+#pragma unroll 1
+    for (int b = 0; b < F::NB; ++b) {
+        const int r0 = kSub * b;
+        const int ct = wave, j = 16 * ct + c16;
+        if (ct < F::MT) {
+            f32x4_t acc = zero4();
+            if (ct < b)
+                for (int s4 = 0; s4 < r0 / 4; ++s4)
+                    acc = mfma4(G[(r0 + c16) * C + 4 * s4 + g4], Tm[(4 * s4 + g4) * C + j], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = r0 + 4 * g4 + r;
+                X[(4 * g4 + r) * C + j] = (t == j ? Bs[t] : 0.0f) - acc[r];
+            }
+        }
+        __syncthreads();
+        if (ct < F::MT) {
+            f32x4_t acc = zero4();
+            if (ct <= b) {
+#pragma unroll
+                for (int s4 = 0; s4 < kSub / 4; ++s4)
+                    acc = mfma4(TI[(b * kSub + c16) * kSub + 4 * s4 + g4], X[(4 * s4 + g4) * C + j], acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Tm[(r0 + 4 * g4 + r) * C + j] = acc[r];
+        }
+        __syncthreads();
+    }
+    gram(Qs, false);
+    __syncthreads();
+    // diag(Inv) T and the masked weights, written in the chain kernel's order
+    for (int f = tid; f < C * C; f += NT) {
+        constexpr int S4 = C / 4;
+        const int ln = (f / S4) % 64;
+        const int t = 16 * (f / (64 * S4)) + (ln & 15), j = 4 * (f % S4) + (ln >> 4);
+        out[f] = Inv[t] * Tm[t * C + j];
+        out[C * C + f] = Ms[t * C + j];
+    }
+}
+
+template <int DK, int C>
+struct ChainCfg {
+    static constexpr int D = DK * (DK + 1) / 2;
+    static constexpr int MT = C / 16;                   // token tiles
+    static constexpr int FT = (D + 15) / 16;            // feature tiles
+    static constexpr int S4 = C / 4;                    // 4-token steps of a chunk
+    // the chunk's lifts phi(k), phi(q) are formed once per chunk in LDS where
+    // they fit (d_k = 16). A row stride of 17 (mod 64) words puts the 64 rows
+    // of a lift write on distinct banks and keeps the matrix-core operand reads
+    // (16 rows x 4 features, or 4 rows x 16 features) at most 2-way conflicted.
+    static constexpr bool PRE = DK == 16;
+    static constexpr int DP = D + ((17 - D % 64) % 64 + 64) % 64;
+    // LDS, in floats
+    static constexpr int A_OFF = 0;                     // state [D][16] (column 15 = z)
+    static constexpr int K_OFF = A_OFF + D * kTileCols; // keys [C][DK]
+    static constexpr int Q_OFF = K_OFF + C * DK;        // queries [C][DK]
+    static constexpr int U_OFF = Q_OFF + C * DK;        // [v | 1] [C][16]
+    static constexpr int R_OFF = U_OFF + C * kTileCols; // R [C][16]
+    static constexpr int P_OFF = R_OFF + C * kTileCols; // P' [C][16]
+    static constexpr int INV_OFF = P_OFF + C * kTileCols;   // 1 / |k_t|^2 [C]
+    static constexpr int KAP_OFF = INV_OFF + C;         // phi(k) [C][DP] (PRE)
+    static constexpr int FQ_OFF = KAP_OFF + (PRE ? C * DP : 0);   // phi(q) [C][DP] (PRE)
+    static constexpr int FLOATS = FQ_OFF + (PRE ? C * DP : 0);
+    static_assert(D % 8 == 0 && MT <= 4, "pairs of 4-feature steps, at most 4 token tiles");
+    static_assert(FLOATS * 4 + D * 4 <= 160 * 1024, "fits the LDS of a compute unit");
+};
+
+// Workgroups of one head run on one XCD (so the per-chunk matrices they all
+// read stay in that XCD's L2): linear block L -> head 8 (L / (8 NVT)) + L % 8,
+// value tile (L / 8) % NVT.
+__device__ __forceinline__ void chain_coords(int NVT, int& vt, int& bh) {
+    const int L = blockIdx.x;
+    bh = 8 * (L / (8 * NVT)) + L % 8;
+    vt = (L / 8) % NVT;
+}
+
+// Packed feature p of the row-major upper triangle of x x^T (width d):
+// first and second index.
+__host__ __device__ constexpr int pair_first(int p, int d) {
+    int i = 0;
+    while (p >= d - i) {
+        p -= d - i;
+        ++i;
+    }
+    return i;
+}
+__host__ __device__ constexpr int pair_second(int p, int d) {
+    int i = 0;
+    while (p >= d - i) {
+        p -= d - i;
+        ++i;
+    }
+    return i + p;
+}
+
+// phi(x)[P] (d_k = 16) with the feature's pair fixed at compile time.
+template <int P>
+__device__ __forceinline__ float lift_one(const float (&x)[16]) {
+    constexpr int a = pair_first(P, 16), b = pair_second(P, 16);
+    return x[a] * x[b] * (a == b ? 1.0f : kSqrt2);
+}
+
+// dst[i] = phi(x)[P0 + i] for the features of one run.
+template <int P0, int... I>
+__device__ __forceinline__ void lift_run(const float (&x)[16], float* dst,
+                                         std::integer_sequence<int, I...>) {
+    ((dst[I] = lift_one<P0 + I>(x)), ...);
+}
+
+// One workgroup of 8 wavefronts per (batch*head, value tile of 15 columns + z).
+// Wavefronts 0..MT-1 form R and P' of token tile w, wavefronts 4..3+MT the
+// outputs of token tile w - 4; feature tiles of the state update are dealt
+// round-robin over all eight.
+template <typename TIn, int DK, int C>
+__global__ __launch_bounds__(kChainThreads) void delta_chain_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const float* __restrict__ ws, TIn* __restrict__ o, const float* __restrict__ S0,
+    const float* __restrict__ z0, float* __restrict__ S_out, float* __restrict__ z_out, int T,
+    int DV, int BH, int NVT) {
+    using F = ChainCfg<DK, C>;
+    constexpr int D = F::D, NT = kChainThreads, S4 = F::S4;
+    __shared__ float sm[F::FLOATS];
+    __shared__ uint32_t pairs[D];
+    float* St = sm + F::A_OFF;
+    float* Ks = sm + F::K_OFF;
+    float* Qs = sm + F::Q_OFF;
+    float* Us = sm + F::U_OFF;
+    float* R = sm + F::R_OFF;
+    float* P = sm + F::P_OFF;
+    float* Inv = sm + F::INV_OFF;
+    float* Kap = sm + F::KAP_OFF;              // PRE only
+    float* Fq = sm + F::FQ_OFF;                // PRE only
+
+    int vt, bhi;
+    chain_coords(NVT, vt, bhi);
+    if (bhi >= BH) return;                     // padding of the head count to 8
+    const size_t bh = bhi;
+    const int tid = threadIdx.x;
+    const int NC = (T + C - 1) / C;
+    const int col0 = kVals * vt;
+    // state column c of this workgroup: value column col0 + c (c < 15, if it
+    // exists) or z (c = 15)
+    auto vcol = [&](int c) { return c < kVals && col0 + c < DV; };
+
+    for (int p = tid; p < D; p += NT) pairs[p] = pack_pair(p, DK);
+    for (int e = tid; e < D * kTileCols; e += NT) {
+        const int p = e / kTileCols, c = e % kTileCols;
+        float x = 0.0f;
+        if (S0) {
+            if (c == kVals) x = z0[bh * D + p];
+            else if (vcol(c)) x = S0[(bh * D + p) * DV + col0 + c];
+        }
+        St[e] = x;
+    }
+
+    auto phik = [&](int t, int p) -> float {
         if constexpr (F::PRE) {
-            return Kap[t * D + p];
+            return Kap[t * F::DP + p];
         } else {
             const uint32_t pr = pairs[p];
             const int a = pr & 0xff, b = pr >> 8;
-            return Ks[t * DK + a] * Ks[t * DK + b] * ((a == b ? 1.0f : kSqrt2) * Inv[t]);
+            return Ks[t * DK + a] * Ks[t * DK + b] * (a == b ? 1.0f : kSqrt2);
         }
     };
     auto phiq = [&](int t, int p) -> float {
         if constexpr (F::PRE) {
-            return Fq[t * D + p];
+            return Fq[t * F::DP + p];
         } else {
             const uint32_t pr = pairs[p];
             const int a = pr & 0xff, b = pr >> 8;
@@ -132,191 +339,204 @@ __global__ __launch_bounds__(kFwdThreads) void delta_fwd_kernel(
         }
     };
 
-    // matrix-core tiles: wavefront w takes tiles w, w + 16, ...; lane (c16, g)
-    // of a 16x16x4 fp32 product holds A[row c16][k g], B[k g][column c16] and
-    // accumulator rows 4g + r of column c16
     const int wave = tid >> 6, lane = tid & 63, c16 = lane & 15, g4 = lane >> 4;
-    constexpr int NWV = NT / 64;
-    constexpr int MT = C / 16;                      // token tiles
-    constexpr int FT = (D + 15) / 16;               // feature tiles
+    const bool rwave = wave < F::MT;                       // forms R, P' of tile wave
+    const bool owave = wave >= 4 && wave < 4 + F::MT;      // outputs of tile wave - 4
+    const int mt = rwave ? wave : wave - 4;
 
-    for (int c0 = 0; c0 < T; c0 += C) {
+    // a chunk's inputs are loaded into registers one chunk ahead (rows past a
+    // ragged end are zero) and staged into LDS once the chunk before is done
+    constexpr int EK = (C * DK + NT - 1) / NT, EU = (C * kTileCols + NT - 1) / NT;
+    float nk[EK], nq[EK], nu[EU];
+    auto fetch = [&](int c0) {
         const int n = min(C, T - c0);
         const size_t tok0 = bh * (size_t)T + c0;
-        // ---- stage the chunk (rows past a ragged end are zero: no key, no
-        // write, beta 0)
-        for (int e = tid; e < C * DK; e += NT) {
-            const int t = e / DK;
-            Ks[e] = t < n ? io<TIn>::ld(k, tok0 * DK + e) : 0.0f;
-            Qs[e] = t < n ? io<TIn>::ld(q, tok0 * DK + e) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < EK; ++i) {
+            const int e = tid + i * NT;
+            const bool ok = e < C * DK && e / DK < n;
+            nk[i] = ok ? io<TIn>::ld(k, tok0 * DK + e) : 0.0f;
+            nq[i] = ok ? io<TIn>::ld(q, tok0 * DK + e) : 0.0f;
         }
-        for (int e = tid; e < C * kCols; e += NT) {
-            const int t = e / kCols, c = e % kCols;
+#pragma unroll
+        for (int i = 0; i < EU; ++i) {
+            const int e = tid + i * NT;
+            const int t = e / kTileCols, c = e % kTileCols;
             float x = 0.0f;
-            if (t < n) x = c < kSub ? io<TIn>::ld(v, (tok0 + t) * DV + kSub * vt + c) : 1.0f;
-            Us[e] = x;
+            if (e < C * kTileCols && t < n)
+                x = c == kVals ? 1.0f : vcol(c) ? io<TIn>::ld(v, (tok0 + t) * DV + col0 + c) : 0.0f;
+            nu[i] = x;
         }
-        for (int t = tid; t < C; t += NT) Bs[t] = t < n ? beta[tok0 + t] : 0.0f;
-        __syncthreads();
-        for (int t = tid; t < C; t += NT) {
-            float s = 0.0f;
-#pragma unroll
-            for (int a = 0; a < DK; ++a) s = __builtin_fmaf(Ks[t * DK + a], Ks[t * DK + a], s);
-            Inv[t] = s > 0.0f ? 1.0f / s : 0.0f;
-        }
-        __syncthreads();
+    };
+    fetch(0);
+    __syncthreads();
 
-        // ---- G = beta_t kappa_t.kappa_j (j < t) and Aq = phi(q_t).kappa_j (j <= t),
-        // from raw dot products on the matrix cores: kappa_t.kappa_j =
-        // (k_t.k_j)^2 / (|k_t|^2 |k_j|^2); the lifted keys and queries of the chunk
-        for (int tile = wave; tile < MT * MT; tile += NWV) {
-            const int mt = tile / MT, jt = tile % MT;
-            f32x4_t dk = zero4(), dq = zero4();
+    for (int c = 0; c < NC; ++c) {
+        const int c0 = c * C;
+        const int n = min(C, T - c0);
+        const size_t tok0 = bh * (size_t)T + c0;
+        // ---- stage the chunk, start loading the next one and this chunk's
+        // matrices (T' for the R wavefronts, the masked weights for the output
+        // ones; first used two phases later)
 #pragma unroll
-            for (int s4 = 0; s4 < DK / 4; ++s4) {
-                const int a = 4 * s4 + g4;
-                const float kb = Ks[(16 * jt + c16) * DK + a];
-                dk = mfma4(Ks[(16 * mt + c16) * DK + a], kb, dk);
-                dq = mfma4(Qs[(16 * mt + c16) * DK + a], kb, dq);
-            }
-            const int jj = 16 * jt + c16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * mt + 4 * g4 + r;
-                G[t * C + jj] = jj < t ? Bs[t] * (dk[r] * dk[r]) * (Inv[t] * Inv[jj]) : 0.0f;
-                Aq[t * C + jj] = jj <= t ? (dq[r] * dq[r]) * Inv[jj] : 0.0f;
+        for (int i = 0; i < EK; ++i) {
+            const int e = tid + i * NT;
+            if (e < C * DK) {
+                Ks[e] = nk[i];
+                Qs[e] = nq[i];
             }
         }
+#pragma unroll
+        for (int i = 0; i < EU; ++i) {
+            const int e = tid + i * NT;
+            if (e < C * kTileCols) Us[e] = nu[i];
+        }
+        __syncthreads();
+        if (c + 1 < NC) fetch(c0 + C);
+        float mf[S4];
+        if (rwave || owave) {
+            const float* src = ws + ((bh * NC + c) * 2 + (owave ? 1 : 0)) * (size_t)(C * C) +
+                               (size_t)(mt * 64 + lane) * S4;
+#pragma unroll
+            for (int s = 0; s < S4; s += 4) {
+                const float4 x = *reinterpret_cast<const float4*>(src + s);
+                mf[s] = x.x;
+                mf[s + 1] = x.y;
+                mf[s + 2] = x.z;
+                mf[s + 3] = x.w;
+            }
+        }
+
+        // ---- 1 / |k_t|^2 and the chunk's lifts: at d_k = 16 lane t of
+        // wavefront w lifts token t's key (w < 4) or query (w >= 4), features
+        // 34 (w % 4) .. 34 (w % 4) + 33
         if constexpr (F::PRE) {
-            for (int e = tid; e < C * D; e += NT) {
-                const int t = e / D, p = e % D;
-                const uint32_t pr = pairs[p];
-                const int a = pr & 0xff, b = pr >> 8;
-                const float sc = a == b ? 1.0f : kSqrt2;
-                Kap[e] = Ks[t * DK + a] * Ks[t * DK + b] * (sc * Inv[t]);
-                Fq[e] = Qs[t * DK + a] * Qs[t * DK + b] * sc;
-            }
-        }
-        __syncthreads();
-
-        // ---- R = U - K A (tiles of 16 tokens x 16 columns; the second column
-        // tile holds only z)
-        for (int tile = wave; tile < MT * 2; tile += NWV) {
-            const int mt = tile >> 1, col = 16 * (tile & 1) + c16;
-            const bool colok = col < kCols;
-            f32x4_t acc = zero4();
-#pragma unroll 2
-            for (int s4 = 0; s4 < D / 4; ++s4) {
-                const int p = 4 * s4 + g4;
-                acc = mfma4(kappa(16 * mt + c16, p), colok ? St[p * kCols + col] : 0.0f, acc);
-            }
-            if (colok) {
+            if (lane < C) {
+                const float* src = (wave < 4 ? Ks : Qs) + lane * DK;
+                float x[16];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * mt + 4 * g4 + r;
-                    R[t * kCols + col] = Us[t * kCols + col] - acc[r];
+                for (int a = 0; a < 16; a += 4) {
+                    const float4 y = *reinterpret_cast<const float4*>(src + a);
+                    x[a] = y.x;
+                    x[a + 1] = y.y;
+                    x[a + 2] = y.z;
+                    x[a + 3] = y.w;
+                }
+                if (wave == 0) {
+                    float s = 0.0f;
+#pragma unroll
+                    for (int a = 0; a < 16; ++a) s = __builtin_fmaf(x[a], x[a], s);
+                    Inv[lane] = s > 0.0f ? 1.0f / s : 0.0f;
+                }
+                float* dst = (wave < 4 ? Kap : Fq) + lane * F::DP;
+                using Run = std::make_integer_sequence<int, D / 4>;
+                switch (wave & 3) {
+                    case 0: lift_run<0>(x, dst, Run{}); break;
+                    case 1: lift_run<D / 4>(x, dst + D / 4, Run{}); break;
+                    case 2: lift_run<2 * (D / 4)>(x, dst + 2 * (D / 4), Run{}); break;
+                    default: lift_run<3 * (D / 4)>(x, dst + 3 * (D / 4), Run{}); break;
                 }
             }
-        }
-        // ---- inverses of the diagonal blocks I + N_b (N_b strictly lower, the
-        // block's part of G): column j of each inverse by forward substitution
-        // (G is complete after the barrier above)
-        if (tid >= NT - F::NB * kSub) {
-            const int id = tid - (NT - F::NB * kSub);
-            const int b = id / kSub, j = id % kSub, r0 = kSub * b;
-            float x[kSub];
-#pragma unroll
-            for (int r = 0; r < kSub; ++r) {
-                float s = r == j ? 1.0f : 0.0f;
-#pragma unroll
-                for (int s2 = 0; s2 < r; ++s2) s = __builtin_fmaf(-G[(r0 + r) * C + r0 + s2], x[s2], s);
-                x[r] = s;
-            }
-#pragma unroll
-            for (int r = 0; r < kSub; ++r) TI[(b * kSub + r) * kSub + j] = x[r];
-        }
-        __syncthreads();
-
-        // ---- P block by block: rhs = beta R - G_{b,<b} P_{<b}, P_b = inv_b rhs
-#pragma unroll 1
-        for (int b = 0; b < F::NB; ++b) {
-            const int r0 = kSub * b;
-            for (int e = tid; e < kSub * kCols; e += NT) {
-                const int t = r0 + e / kCols, c = e % kCols;
-                float s = Bs[t] * R[t * kCols + c];
-#pragma unroll 4
-                for (int j = 0; j < r0; ++j) s = __builtin_fmaf(-G[t * C + j], P[j * kCols + c], s);
-                R[t * kCols + c] = s;
-            }
-            __syncthreads();
-            for (int e = tid; e < kSub * kCols; e += NT) {
-                const int r = e / kCols, c = e % kCols;
+        } else {
+            for (int t = tid; t < C; t += NT) {
                 float s = 0.0f;
-#pragma unroll 4
-                for (int j = 0; j < kSub; ++j)
-                    s = __builtin_fmaf(TI[(b * kSub + r) * kSub + j], R[(r0 + j) * kCols + c], s);
-                P[(r0 + r) * kCols + c] = s;
-            }
-            __syncthreads();
-        }
-
-        // ---- O = phi(Q) A + mask(phi(Q) K^T) P (Aq holds the masked weights)
-        for (int tile = wave; tile < MT * 2; tile += NWV) {
-            const int mt = tile >> 1, col = 16 * (tile & 1) + c16;
-            const bool colok = col < kCols;
-            f32x4_t acc = zero4();
-#pragma unroll 2
-            for (int s4 = 0; s4 < D / 4; ++s4) {
-                const int p = 4 * s4 + g4;
-                acc = mfma4(phiq(16 * mt + c16, p), colok ? St[p * kCols + col] : 0.0f, acc);
-            }
-#pragma unroll 2
-            for (int s4 = 0; s4 < C / 4; ++s4) {
-                const int jj = 4 * s4 + g4;
-                acc = mfma4(Aq[(16 * mt + c16) * C + jj], colok ? P[jj * kCols + col] : 0.0f, acc);
-            }
-            if (colok) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Os[(16 * mt + 4 * g4 + r) * kCols + col] = acc[r];
+                for (int a = 0; a < DK; ++a) s = __builtin_fmaf(Ks[t * DK + a], Ks[t * DK + a], s);
+                Inv[t] = s > 0.0f ? 1.0f / s : 0.0f;
             }
         }
         __syncthreads();
 
-        // ---- normalise and store; the state gains K^T P (tiles of 16 features
-        // x 16 columns; the outputs above were the last reads of the old state)
-        for (int e = tid; e < n * kSub; e += NT) {
-            const int t = e / kSub, c = e % kSub;
-            io<TIn>::st(o, (tok0 + t) * DV + kSub * vt + c, safe_div(Os[t * kCols + c], Os[t * kCols + kSub]));
-        }
-        for (int tile = wave; tile < FT * 2; tile += NWV) {
-            const int ft = tile >> 1, col = 16 * (tile & 1) + c16;
-            const bool colok = col < kCols;
-            const int pa = 16 * ft + c16;            // this lane's A row (feature)
-            f32x4_t acc;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int p = 16 * ft + 4 * g4 + r;
-                acc[r] = (p < D && colok) ? St[p * kCols + col] : 0.0f;
-            }
+        // ---- phase 1: R = U - diag(Inv) phi(K) A (R wavefronts) and the
+        // inter-chunk part phi(Q) A of the outputs (output wavefronts); both
+        // read the state before the chunk
+        f32x4_t oacc = zero4();
+        if (rwave || owave) {
+            // two accumulators so that consecutive products do not wait on
+            // each other
+            f32x4_t acc = zero4(), acc2 = zero4();
+            const int t = 16 * mt + c16;
 #pragma unroll 2
-            for (int s4 = 0; s4 < C / 4; ++s4) {
+            for (int s4 = 0; s4 < D / 4; s4 += 2) {
+                const int p = 4 * s4 + g4;
+                const float a = rwave ? phik(t, p) : phiq(t, p);
+                const float a2 = rwave ? phik(t, p + 4) : phiq(t, p + 4);
+                acc = mfma4(a, St[p * kTileCols + c16], acc);
+                acc2 = mfma4(a2, St[(p + 4) * kTileCols + c16], acc2);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] += acc2[r];
+            if (rwave) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tr = 16 * mt + 4 * g4 + r;
+                    R[tr * kTileCols + c16] = Us[tr * kTileCols + c16] - Inv[tr] * acc[r];
+                }
+            } else {
+                oacc = acc;
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 2: P' = diag(Inv) T R (T lower triangular: token tile mt
+        // needs the first 16 (mt + 1) tokens)
+        if (rwave) {
+            f32x4_t acc = zero4();
+#pragma unroll
+            for (int s = 0; s < S4; ++s)
+                if (s < 4 * (mt + 1)) acc = mfma4(mf[s], R[(4 * s + g4) * kTileCols + c16], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) P[(16 * mt + 4 * g4 + r) * kTileCols + c16] = acc[r];
+        }
+        __syncthreads();
+
+        // ---- phase 3: the intra-chunk part mask((Q K^T)^2) P' of the outputs,
+        // normalise and store (output wavefronts); the state gains phi(K)^T P'
+        // (feature tiles round-robin; the last reads of the old state were in
+        // phase 1)
+        if (owave) {
+#pragma unroll
+            for (int s = 0; s < S4; ++s)
+                if (s < 4 * (mt + 1)) oacc = mfma4(mf[s], P[(4 * s + g4) * kTileCols + c16], oacc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float den = __shfl(oacc[r], 16 * g4 + kVals, 64);
+                const int t = 16 * mt + 4 * g4 + r;
+                if (t < n && vcol(c16))
+                    io<TIn>::st(o, (tok0 + t) * DV + col0 + c16, safe_div(oacc[r], den));
+            }
+        }
+        for (int ft = wave; ft < F::FT; ft += NT / 64) {
+            const int pa = 16 * ft + c16;            // this lane's A row (feature)
+            f32x4_t acc, acc2 = zero4();
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int p = 16 * ft + 4 * g4 + r;
+                acc[r] = p < D ? St[p * kTileCols + c16] : 0.0f;
+            }
+#pragma unroll 4
+            for (int s4 = 0; s4 < S4; s4 += 2) {
                 const int t = 4 * s4 + g4;
-                acc = mfma4(pa < D ? kappa(t, pa) : 0.0f, colok ? P[t * kCols + col] : 0.0f, acc);
+                acc = mfma4(pa < D ? phik(t, pa) : 0.0f, P[t * kTileCols + c16], acc);
+                acc2 = mfma4(pa < D ? phik(t + 4, pa) : 0.0f, P[(t + 4) * kTileCols + c16], acc2);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int p = 16 * ft + 4 * g4 + r;
-                if (p < D && colok) St[p * kCols + col] = acc[r];
+                if (p < D) St[p * kTileCols + c16] = acc[r] + acc2[r];
             }
         }
         __syncthreads();
     }
 
     if (S_out) {
-        for (int e = tid; e < D * kCols; e += NT) {
-            const int p = e / kCols, c = e % kCols;
-            if (c < kSub) S_out[(bh * D + p) * DV + kSub * vt + c] = St[e];
-            else if (vt == 0) z_out[bh * D + p] = St[e];
+        for (int e = tid; e < D * kTileCols; e += NT) {
+            const int p = e / kTileCols, c = e % kTileCols;
+            if (c == kVals) {
+                if (vt == 0) z_out[bh * D + p] = St[e];
+            } else if (vcol(c)) {
+                S_out[(bh * D + p) * DV + col0 + c] = St[e];
+            }
         }
     }
 }
@@ -450,21 +670,29 @@ __global__ __launch_bounds__(kThreads) void delta_decode_kernel(
 template <typename TIn, int DK, int C>
 hipError_t launch_fwd_t(const Shape& s, const void* q, const void* k, const void* v,
                         const float* beta, void* o, const float* S0, const float* z0, float* S_out,
-                        float* z_out, hipStream_t st) {
-    dim3 grid(s.dv / kSub, s.B * s.H);
-    delta_fwd_kernel<TIn, DK, C><<<grid, kFwdThreads, 0, st>>>(
-        (const TIn*)q, (const TIn*)k, (const TIn*)v, beta, (TIn*)o, S0, z0, S_out, z_out, s.T, s.dv);
+                        float* z_out, float* ws, hipStream_t st) {
+    const int BH = s.B * s.H;
+    const int NC = (s.T + C - 1) / C;
+    delta_prep_kernel<TIn, DK, C><<<dim3(NC, BH), kPrepThreads, 0, st>>>(
+        (const TIn*)q, (const TIn*)k, beta, ws, s.T, NC);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int NVT = (s.dv + kVals - 1) / kVals;
+    const int blocks = NVT * 8 * ((BH + 7) / 8);
+    delta_chain_kernel<TIn, DK, C><<<blocks, kChainThreads, 0, st>>>(
+        (const TIn*)q, (const TIn*)k, (const TIn*)v, ws, (TIn*)o, S0, z0, S_out, z_out, s.T, s.dv,
+        BH, NVT);
     return hipGetLastError();
 }
 
 template <typename TIn, int DK>
 hipError_t launch_fwd_dk(const Shape& s, const void* q, const void* k, const void* v,
                          const float* beta, void* o, const float* S0, const float* z0,
-                         float* S_out, float* z_out, hipStream_t st) {
+                         float* S_out, float* z_out, float* ws, hipStream_t st) {
     switch (s.C) {
-        case 16: return launch_fwd_t<TIn, DK, 16>(s, q, k, v, beta, o, S0, z0, S_out, z_out, st);
-        case 32: return launch_fwd_t<TIn, DK, 32>(s, q, k, v, beta, o, S0, z0, S_out, z_out, st);
-        case 64: return launch_fwd_t<TIn, DK, 64>(s, q, k, v, beta, o, S0, z0, S_out, z_out, st);
+        case 16: return launch_fwd_t<TIn, DK, 16>(s, q, k, v, beta, o, S0, z0, S_out, z_out, ws, st);
+        case 32: return launch_fwd_t<TIn, DK, 32>(s, q, k, v, beta, o, S0, z0, S_out, z_out, ws, st);
+        case 64: return launch_fwd_t<TIn, DK, 64>(s, q, k, v, beta, o, S0, z0, S_out, z_out, ws, st);
     }
     return hipErrorInvalidValue;
 }
@@ -495,14 +723,19 @@ bool delta_supported(const Shape& s) {
            (s.C == 16 || s.C == 32 || s.C == 64);
 }
 
+size_t delta_workspace_bytes(const Shape& s) {
+    const size_t NC = (size_t)(s.T + s.C - 1) / s.C;
+    return (size_t)s.B * s.H * NC * 2 * s.C * s.C * sizeof(float);
+}
+
 hipError_t launch_delta_fwd(const Shape& s, const void* q, const void* k, const void* v,
                             const float* beta, void* o, const float* S0, const float* z0,
-                            float* S_out, float* z_out, hipStream_t st) {
+                            float* S_out, float* z_out, float* ws, hipStream_t st) {
     if (s.bf16)
-        return s.dk == 16 ? launch_fwd_dk<bf16_t, 16>(s, q, k, v, beta, o, S0, z0, S_out, z_out, st)
-                          : launch_fwd_dk<bf16_t, 32>(s, q, k, v, beta, o, S0, z0, S_out, z_out, st);
-    return s.dk == 16 ? launch_fwd_dk<float, 16>(s, q, k, v, beta, o, S0, z0, S_out, z_out, st)
-                      : launch_fwd_dk<float, 32>(s, q, k, v, beta, o, S0, z0, S_out, z_out, st);
+        return s.dk == 16 ? launch_fwd_dk<bf16_t, 16>(s, q, k, v, beta, o, S0, z0, S_out, z_out, ws, st)
+                          : launch_fwd_dk<bf16_t, 32>(s, q, k, v, beta, o, S0, z0, S_out, z_out, ws, st);
+    return s.dk == 16 ? launch_fwd_dk<float, 16>(s, q, k, v, beta, o, S0, z0, S_out, z_out, ws, st)
+                      : launch_fwd_dk<float, 32>(s, q, k, v, beta, o, S0, z0, S_out, z_out, ws, st);
 }
 
 hipError_t launch_delta_decode(const void* q, const void* k, const void* v, const float* beta,

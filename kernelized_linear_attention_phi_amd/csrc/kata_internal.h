@@ -179,10 +179,14 @@ hipError_t launch_flash_fwd(const Shape& s, const void* q, const void* k, const 
 
 // ---- DeltaKATA (delta rule on [S | z], fp32 arithmetic) ----
 bool delta_supported(const Shape& s);
-// beta [BH, T]; S0, z0 / S_out, z_out packed states or NULL; no workspace
+// Workspace of the forward: each chunk's diag(Inv) T and masked weights,
+// 2 C^2 floats per (batch*head, chunk).
+size_t delta_workspace_bytes(const Shape& s);
+// beta [BH, T]; S0, z0 / S_out, z_out packed states or NULL; ws of
+// delta_workspace_bytes(s), 16-byte aligned
 hipError_t launch_delta_fwd(const Shape& s, const void* q, const void* k, const void* v,
                             const float* beta, void* o, const float* S0, const float* z0,
-                            float* S_out, float* z_out, hipStream_t st);
+                            float* S_out, float* z_out, float* ws, hipStream_t st);
 hipError_t launch_delta_decode(const void* q, const void* k, const void* v, const float* beta,
                                float* S, float* z, void* o, int N, int dk, int dv, bool bf16,
                                hipStream_t st);

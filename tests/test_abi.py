@@ -284,7 +284,8 @@ def test_delta_rejects_before_launch(L):
     dfw = L.kata_delta_fwd
     args = lambda **kw: (kw.get("q", FAKE), FAKE, FAKE, kw.get("beta", FAKE), FAKE, 1, 2,
                          kw.get("T", 64), kw.get("dk", 16), kw.get("dv", 64), kw.get("C", 64),
-                         kw.get("dtype", BF16), kw.get("S0", None), None, None, None, None)
+                         kw.get("dtype", BF16), kw.get("S0", None), None, None, None,
+                         kw.get("ws", FAKE), kw.get("nws", 1 << 40), None)
     assert dfw(*args(C=128)) == EUNSUPPORTED
     assert dfw(*args(dk=24)) == EUNSUPPORTED
     assert dfw(*args(dv=48)) == EUNSUPPORTED
@@ -292,7 +293,14 @@ def test_delta_rejects_before_launch(L):
     assert dfw(*args(q=MISALIGNED)) == EINVAL
     assert dfw(*args(S0=FAKE)) == EINVAL             # S0 without z0
     assert dfw(*args(dtype=5)) == EINVAL
-    assert dfw(*args(T=0, q=None, beta=None)) == OK   # empty: nothing launched
+    assert dfw(*args(T=0, q=None, beta=None, ws=None, nws=0)) == OK   # empty: nothing launched
+    need = L.kata_delta_fwd_workspace(1, 2, 64, 16, 64, 64, BF16)
+    assert need == 2 * 1 * 2 * 64 * 64 * 4                      # 2 C^2 floats per head and chunk
+    assert L.kata_delta_fwd_workspace(1, 2, 65, 16, 64, 64, BF16) == 2 * need   # ragged: 2 chunks
+    assert L.kata_delta_fwd_workspace(1, 2, 64, 16, 64, 128, BF16) == 0          # unsupported
+    assert dfw(*args(nws=need - 1)) == EWORKSPACE
+    assert dfw(*args(ws=None)) == EWORKSPACE
+    assert dfw(*args(ws=MISALIGNED)) == EINVAL
     dec = L.kata_decode_step_delta
     assert dec(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 16, 64, BF16, None) == EINVAL
     assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 12, 64, BF16, None) == EUNSUPPORTED
