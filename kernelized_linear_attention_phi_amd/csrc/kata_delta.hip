@@ -27,6 +27,7 @@
 // the mask of (q_t.k_j)^2, so the chain works with the plain lifts phi(k),
 // phi(q):  R = U - diag(Inv) phi(K) A,  P' = diag(Inv) T R,
 // O = phi(Q) A + mask((Q K^T)^2) P',  A <- A + phi(K)^T P'.
+#include "kata_chunk.h"
 #include "kata_device.h"
 #include "kata_internal.h"
 #include "kata_mfma.h"
@@ -211,12 +212,13 @@ struct ChainCfg {
     static constexpr int MT = C / 16;                   // token tiles
     static constexpr int FT = (D + 15) / 16;            // feature tiles
     static constexpr int S4 = C / 4;                    // 4-token steps of a chunk
-    // the chunk's lifts phi(k), phi(q) are formed once per chunk in LDS where
-    // they fit (d_k = 16). A row stride of 17 (mod 64) words puts the 64 rows
-    // of a lift write on distinct banks and keeps the matrix-core operand reads
-    // (16 rows x 4 features, or 4 rows x 16 features) at most 2-way conflicted.
-    static constexpr bool PRE = DK == 16;
-    static constexpr int DP = D + ((17 - D % 64) % 64 + 64) % 64;
+    // Feature order of the state rows. d_k = 16: circulant, row 16 delta + rho
+    // holds the pair (rho, (rho + delta) mod 16) for delta = 0..7 and, for
+    // delta = 8, rho = 0..7 (136 rows, every unordered pair once); a lane then
+    // lifts its own token's features from one rotated copy of the token in
+    // registers with compile-time indices. d_k = 32: the packed row-major
+    // order, lifted through a pair table.
+    static constexpr bool CIRC = DK == 16;
     // LDS, in floats
     static constexpr int A_OFF = 0;                     // state [D][16] (column 15 = z)
     static constexpr int K_OFF = A_OFF + D * kTileCols; // keys [C][DK]
@@ -224,13 +226,13 @@ struct ChainCfg {
     static constexpr int U_OFF = Q_OFF + C * DK;        // [v | 1] [C][16]
     static constexpr int R_OFF = U_OFF + C * kTileCols; // R [C][16]
     static constexpr int P_OFF = R_OFF + C * kTileCols; // P' [C][16]
-    static constexpr int INV_OFF = P_OFF + C * kTileCols;   // 1 / |k_t|^2 [C]
-    static constexpr int KAP_OFF = INV_OFF + C;         // phi(k) [C][DP] (PRE)
-    static constexpr int FQ_OFF = KAP_OFF + (PRE ? C * DP : 0);   // phi(q) [C][DP] (PRE)
-    static constexpr int FLOATS = FQ_OFF + (PRE ? C * DP : 0);
+    static constexpr int FLOATS = P_OFF + C * kTileCols;
     static_assert(D % 8 == 0 && MT <= 4, "pairs of 4-feature steps, at most 4 token tiles");
     static_assert(FLOATS * 4 + D * 4 <= 160 * 1024, "fits the LDS of a compute unit");
 };
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x); }
 
 // Workgroups of one head run on one XCD (so the per-chunk matrices they all
 // read stay in that XCD's L2): linear block L -> head 8 (L / (8 NVT)) + L % 8,
@@ -241,43 +243,45 @@ __device__ __forceinline__ void chain_coords(int NVT, int& vt, int& bh) {
     vt = (L / 8) % NVT;
 }
 
-// Packed feature p of the row-major upper triangle of x x^T (width d):
-// first and second index.
-__host__ __device__ constexpr int pair_first(int p, int d) {
-    int i = 0;
-    while (p >= d - i) {
-        p -= d - i;
-        ++i;
-    }
-    return i;
-}
-__host__ __device__ constexpr int pair_second(int p, int d) {
-    int i = 0;
-    while (p >= d - i) {
-        p -= d - i;
-        ++i;
-    }
-    return i + p;
+// Index of the pair (i, j), i <= j, in the packed row-major upper triangle of
+// width d.
+__device__ __forceinline__ int packed_index(int i, int j, int d) {
+    return i * d - i * (i - 1) / 2 + (j - i);
 }
 
-// phi(x)[P] (d_k = 16) with the feature's pair fixed at compile time.
-template <int P>
-__device__ __forceinline__ float lift_one(const float (&x)[16]) {
-    constexpr int a = pair_first(P, 16), b = pair_second(P, 16);
-    return x[a] * x[b] * (a == b ? 1.0f : kSqrt2);
+// Circulant state row f (d_k = 16) -> its packed feature index.
+__device__ __forceinline__ int circ_to_packed(int f) {
+    const int delta = f >> 4, rho = f & 15, r2 = (rho + delta) & 15;
+    return packed_index(min(rho, r2), max(rho, r2), 16);
 }
 
-// dst[i] = phi(x)[P0 + i] for the features of one run.
-template <int P0, int... I>
-__device__ __forceinline__ void lift_run(const float (&x)[16], float* dst,
-                                         std::integer_sequence<int, I...>) {
-    ((dst[I] = lift_one<P0 + I>(x)), ...);
+// Circulant feature 4 S + g of a token whose coordinates a lane of group g holds
+// rotated by g (y[m] = x[(m + g) mod 16]): x_rho x_{rho + delta}, scaled by
+// sqrt 2 off the diagonal, with delta = S / 4 and rho = 4 (S mod 4) + g.
+template <int S>
+__device__ __forceinline__ float circ_feature(const float (&y)[16]) {
+    constexpr int delta = S / 4, j = S % 4;
+    if constexpr (delta == 0) return y[4 * j] * y[4 * j];
+    else return y[4 * j] * (kSqrt2 * y[(4 * j + delta) % 16]);
+}
+
+// acc (+ acc2 for odd steps) += phi(x) rows of the lane's token against the
+// state rows 4 S + g, S = 0 .. D/4 - 1 (d_k = 16).
+template <int... S>
+__device__ __forceinline__ void circ_products(const float (&y)[16], const float* St, int c16,
+                                              int g4, f32x4_t& acc, f32x4_t& acc2,
+                                              std::integer_sequence<int, S...>) {
+    ((S % 2 == 0 ? (acc = mfma4(circ_feature<S>(y), St[(4 * S + g4) * kTileCols + c16], acc))
+                 : (acc2 = mfma4(circ_feature<S>(y), St[(4 * S + g4) * kTileCols + c16], acc2))),
+     ...);
 }
 
 // One workgroup of 8 wavefronts per (batch*head, value tile of 15 columns + z).
 // Wavefronts 0..MT-1 form R and P' of token tile w, wavefronts 4..3+MT the
 // outputs of token tile w - 4; feature tiles of the state update are dealt
-// round-robin over all eight.
+// round-robin over all eight. The barriers of the chunk loop wait for LDS
+// operations only, so the next chunk's loads and this chunk's output stores
+// stay in flight across them.
 template <typename TIn, int DK, int C>
 __global__ __launch_bounds__(kChainThreads) void delta_chain_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
@@ -294,9 +298,6 @@ __global__ __launch_bounds__(kChainThreads) void delta_chain_kernel(
     float* Us = sm + F::U_OFF;
     float* R = sm + F::R_OFF;
     float* P = sm + F::P_OFF;
-    float* Inv = sm + F::INV_OFF;
-    float* Kap = sm + F::KAP_OFF;              // PRE only
-    float* Fq = sm + F::FQ_OFF;                // PRE only
 
     int vt, bhi;
     chain_coords(NVT, vt, bhi);
@@ -308,175 +309,148 @@ __global__ __launch_bounds__(kChainThreads) void delta_chain_kernel(
     // state column c of this workgroup: value column col0 + c (c < 15, if it
     // exists) or z (c = 15)
     auto vcol = [&](int c) { return c < kVals && col0 + c < DV; };
+    // state row f -> packed feature index
+    auto packed = [&](int f) { return F::CIRC ? circ_to_packed(f) : f; };
 
-    for (int p = tid; p < D; p += NT) pairs[p] = pack_pair(p, DK);
+    if constexpr (!F::CIRC)
+        for (int p = tid; p < D; p += NT) pairs[p] = pack_pair(p, DK);
     for (int e = tid; e < D * kTileCols; e += NT) {
-        const int p = e / kTileCols, c = e % kTileCols;
+        const int f = e / kTileCols, c = e % kTileCols;
         float x = 0.0f;
         if (S0) {
+            const int p = packed(f);
             if (c == kVals) x = z0[bh * D + p];
             else if (vcol(c)) x = S0[(bh * D + p) * DV + col0 + c];
         }
         St[e] = x;
     }
 
-    auto phik = [&](int t, int p) -> float {
-        if constexpr (F::PRE) {
-            return Kap[t * F::DP + p];
-        } else {
-            const uint32_t pr = pairs[p];
-            const int a = pr & 0xff, b = pr >> 8;
-            return Ks[t * DK + a] * Ks[t * DK + b] * (a == b ? 1.0f : kSqrt2);
-        }
-    };
-    auto phiq = [&](int t, int p) -> float {
-        if constexpr (F::PRE) {
-            return Fq[t * F::DP + p];
-        } else {
-            const uint32_t pr = pairs[p];
-            const int a = pr & 0xff, b = pr >> 8;
-            return Qs[t * DK + a] * Qs[t * DK + b] * (a == b ? 1.0f : kSqrt2);
-        }
-    };
-
     const int wave = tid >> 6, lane = tid & 63, c16 = lane & 15, g4 = lane >> 4;
     const bool rwave = wave < F::MT;                       // forms R, P' of tile wave
     const bool owave = wave >= 4 && wave < 4 + F::MT;      // outputs of tile wave - 4
     const int mt = rwave ? wave : wave - 4;
 
-    // a chunk's inputs are loaded into registers one chunk ahead (rows past a
-    // ragged end are zero) and staged into LDS once the chunk before is done
+    // a chunk's inputs are loaded into registers one chunk ahead and staged
+    // into LDS once the chunk before is done. The loads are unconditional (their
+    // addresses clamped into the chunk's valid rows and the head's columns), so
+    // that no branch join makes the wavefront wait for them; rows past a ragged
+    // end and columns past d_v are zeroed when staged.
+    // The raw input words are kept until then: a conversion right after the
+    // load would wait for it.
     constexpr int EK = (C * DK + NT - 1) / NT, EU = (C * kTileCols + NT - 1) / NT;
-    float nk[EK], nq[EK], nu[EU];
+    TIn nk[EK], nq[EK], nu[EU];
     auto fetch = [&](int c0) {
         const int n = min(C, T - c0);
         const size_t tok0 = bh * (size_t)T + c0;
 #pragma unroll
         for (int i = 0; i < EK; ++i) {
-            const int e = tid + i * NT;
-            const bool ok = e < C * DK && e / DK < n;
-            nk[i] = ok ? io<TIn>::ld(k, tok0 * DK + e) : 0.0f;
-            nq[i] = ok ? io<TIn>::ld(q, tok0 * DK + e) : 0.0f;
+            const int e = (tid + i * NT) % (C * DK);
+            const int ec = min(e / DK, n - 1) * DK + e % DK;
+            nk[i] = k[tok0 * DK + ec];
+            nq[i] = q[tok0 * DK + ec];
         }
 #pragma unroll
         for (int i = 0; i < EU; ++i) {
-            const int e = tid + i * NT;
-            const int t = e / kTileCols, c = e % kTileCols;
-            float x = 0.0f;
-            if (e < C * kTileCols && t < n)
-                x = c == kVals ? 1.0f : vcol(c) ? io<TIn>::ld(v, (tok0 + t) * DV + col0 + c) : 0.0f;
-            nu[i] = x;
+            const int e = (tid + i * NT) % (C * kTileCols);
+            const int t = min(e / kTileCols, n - 1), col = min(col0 + e % kTileCols, DV - 1);
+            nu[i] = v[(tok0 + t) * DV + col];
         }
     };
-    fetch(0);
-    __syncthreads();
-
-    for (int c = 0; c < NC; ++c) {
-        const int c0 = c * C;
-        const int n = min(C, T - c0);
-        const size_t tok0 = bh * (size_t)T + c0;
-        // ---- stage the chunk, start loading the next one and this chunk's
-        // matrices (T' for the R wavefronts, the masked weights for the output
-        // ones; first used two phases later)
-#pragma unroll
-        for (int i = 0; i < EK; ++i) {
-            const int e = tid + i * NT;
-            if (e < C * DK) {
-                Ks[e] = nk[i];
-                Qs[e] = nq[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < EU; ++i) {
-            const int e = tid + i * NT;
-            if (e < C * kTileCols) Us[e] = nu[i];
-        }
-        __syncthreads();
-        if (c + 1 < NC) fetch(c0 + C);
-        float mf[S4];
+    // this chunk's T' (R wavefronts) or masked weights (output wavefronts),
+    // also loaded one chunk ahead
+    float mf[S4], mfn[S4];
+    auto fetch_mats = [&](int c, float (&dst)[S4]) {
         if (rwave || owave) {
             const float* src = ws + ((bh * NC + c) * 2 + (owave ? 1 : 0)) * (size_t)(C * C) +
                                (size_t)(mt * 64 + lane) * S4;
 #pragma unroll
             for (int s = 0; s < S4; s += 4) {
                 const float4 x = *reinterpret_cast<const float4*>(src + s);
-                mf[s] = x.x;
-                mf[s + 1] = x.y;
-                mf[s + 2] = x.z;
-                mf[s + 3] = x.w;
+                dst[s] = x.x;
+                dst[s + 1] = x.y;
+                dst[s + 2] = x.z;
+                dst[s + 3] = x.w;
             }
         }
+    };
+    fetch(0);
+    fetch_mats(0, mf);
+    __syncthreads();
 
-        // ---- 1 / |k_t|^2 and the chunk's lifts: at d_k = 16 lane t of
-        // wavefront w lifts token t's key (w < 4) or query (w >= 4), features
-        // 34 (w % 4) .. 34 (w % 4) + 33
-        if constexpr (F::PRE) {
-            if (lane < C) {
-                const float* src = (wave < 4 ? Ks : Qs) + lane * DK;
-                float x[16];
+    for (int c = 0; c < NC; ++c) {
+        const int c0 = c * C;
+        const int n = min(C, T - c0);
+        const size_t tok0 = bh * (size_t)T + c0;
+        // ---- stage the chunk, start loading the next one (inputs and
+        // matrices)
 #pragma unroll
-                for (int a = 0; a < 16; a += 4) {
-                    const float4 y = *reinterpret_cast<const float4*>(src + a);
-                    x[a] = y.x;
-                    x[a + 1] = y.y;
-                    x[a + 2] = y.z;
-                    x[a + 3] = y.w;
-                }
-                if (wave == 0) {
-                    float s = 0.0f;
-#pragma unroll
-                    for (int a = 0; a < 16; ++a) s = __builtin_fmaf(x[a], x[a], s);
-                    Inv[lane] = s > 0.0f ? 1.0f / s : 0.0f;
-                }
-                float* dst = (wave < 4 ? Kap : Fq) + lane * F::DP;
-                using Run = std::make_integer_sequence<int, D / 4>;
-                switch (wave & 3) {
-                    case 0: lift_run<0>(x, dst, Run{}); break;
-                    case 1: lift_run<D / 4>(x, dst + D / 4, Run{}); break;
-                    case 2: lift_run<2 * (D / 4)>(x, dst + 2 * (D / 4), Run{}); break;
-                    default: lift_run<3 * (D / 4)>(x, dst + 3 * (D / 4), Run{}); break;
-                }
-            }
-        } else {
-            for (int t = tid; t < C; t += NT) {
-                float s = 0.0f;
-#pragma unroll
-                for (int a = 0; a < DK; ++a) s = __builtin_fmaf(Ks[t * DK + a], Ks[t * DK + a], s);
-                Inv[t] = s > 0.0f ? 1.0f / s : 0.0f;
+        for (int i = 0; i < EK; ++i) {
+            const int e = tid + i * NT;
+            if (e < C * DK) {
+                const bool ok = e / DK < n;
+                Ks[e] = ok ? to_f32(nk[i]) : 0.0f;
+                Qs[e] = ok ? to_f32(nq[i]) : 0.0f;
             }
         }
-        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < EU; ++i) {
+            const int e = tid + i * NT;
+            const int t = e / kTileCols, cc = e % kTileCols;
+            if (e < C * kTileCols)
+                Us[e] = t >= n ? 0.0f : cc == kVals ? 1.0f : vcol(cc) ? to_f32(nu[i]) : 0.0f;
+        }
+        lds_barrier();
+        if (c + 1 < NC) {
+            fetch(c0 + C);
+            fetch_mats(c + 1, mfn);
+        }
 
         // ---- phase 1: R = U - diag(Inv) phi(K) A (R wavefronts) and the
         // inter-chunk part phi(Q) A of the outputs (output wavefronts); both
-        // read the state before the chunk
+        // read the state before the chunk. Lane (c16, g) lifts token
+        // 16 mt + c16 itself.
         f32x4_t oacc = zero4();
         if (rwave || owave) {
+            const float* xr = (rwave ? Ks : Qs) + (16 * mt + c16) * DK;
             // two accumulators so that consecutive products do not wait on
             // each other
             f32x4_t acc = zero4(), acc2 = zero4();
-            const int t = 16 * mt + c16;
+            float nrm = 0.0f;
+            if constexpr (F::CIRC) {
+                float y[16];
+#pragma unroll
+                for (int m = 0; m < 16; ++m) y[m] = xr[(m + g4) & 15];
+#pragma unroll
+                for (int m = 0; m < 16; ++m) nrm = __builtin_fmaf(y[m], y[m], nrm);
+                circ_products(y, St, c16, g4, acc, acc2, std::make_integer_sequence<int, D / 4>{});
+            } else {
+#pragma unroll
+                for (int a = 0; a < DK; ++a) nrm = __builtin_fmaf(xr[a], xr[a], nrm);
 #pragma unroll 2
-            for (int s4 = 0; s4 < D / 4; s4 += 2) {
-                const int p = 4 * s4 + g4;
-                const float a = rwave ? phik(t, p) : phiq(t, p);
-                const float a2 = rwave ? phik(t, p + 4) : phiq(t, p + 4);
-                acc = mfma4(a, St[p * kTileCols + c16], acc);
-                acc2 = mfma4(a2, St[(p + 4) * kTileCols + c16], acc2);
+                for (int s4 = 0; s4 < D / 4; s4 += 2) {
+                    const int p = 4 * s4 + g4;
+                    const uint32_t pr = pairs[p], pr2 = pairs[p + 4];
+                    const float a = xr[pr & 0xff] * xr[pr >> 8] * ((pr & 0xff) == (pr >> 8) ? 1.0f : kSqrt2);
+                    const float a2 = xr[pr2 & 0xff] * xr[pr2 >> 8] * ((pr2 & 0xff) == (pr2 >> 8) ? 1.0f : kSqrt2);
+                    acc = mfma4(a, St[p * kTileCols + c16], acc);
+                    acc2 = mfma4(a2, St[(p + 4) * kTileCols + c16], acc2);
+                }
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] += acc2[r];
             if (rwave) {
+                const float inv = nrm > 0.0f ? 1.0f / nrm : 0.0f;      // of token 16 mt + c16
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int tr = 16 * mt + 4 * g4 + r;
-                    R[tr * kTileCols + c16] = Us[tr * kTileCols + c16] - Inv[tr] * acc[r];
+                    const float inv_r = __shfl(inv, 4 * g4 + r, 64);
+                    R[tr * kTileCols + c16] = Us[tr * kTileCols + c16] - inv_r * acc[r];
                 }
             } else {
                 oacc = acc;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- phase 2: P' = diag(Inv) T R (T lower triangular: token tile mt
         // needs the first 16 (mt + 1) tokens)
@@ -488,7 +462,7 @@ __global__ __launch_bounds__(kChainThreads) void delta_chain_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) P[(16 * mt + 4 * g4 + r) * kTileCols + c16] = acc[r];
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- phase 3: the intra-chunk part mask((Q K^T)^2) P' of the outputs,
         // normalise and store (output wavefronts); the state gains phi(K)^T P'
@@ -507,7 +481,22 @@ __global__ __launch_bounds__(kChainThreads) void delta_chain_kernel(
             }
         }
         for (int ft = wave; ft < F::FT; ft += NT / 64) {
-            const int pa = 16 * ft + c16;            // this lane's A row (feature)
+            // this lane's A row: state row (feature) 16 ft + c16 = pair (a, b)
+            const int f = 16 * ft + c16;
+            int a = 0, b = 0;
+            float sc = 0.0f;
+            if (f < D) {
+                if constexpr (F::CIRC) {
+                    a = c16;
+                    b = (c16 + ft) & 15;
+                    sc = ft == 0 ? 1.0f : kSqrt2;
+                } else {
+                    const uint32_t pr = pairs[f];
+                    a = pr & 0xff;
+                    b = pr >> 8;
+                    sc = a == b ? 1.0f : kSqrt2;
+                }
+            }
             f32x4_t acc, acc2 = zero4();
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -517,8 +506,9 @@ __global__ __launch_bounds__(kChainThreads) void delta_chain_kernel(
 #pragma unroll 4
             for (int s4 = 0; s4 < S4; s4 += 2) {
                 const int t = 4 * s4 + g4;
-                acc = mfma4(pa < D ? phik(t, pa) : 0.0f, P[t * kTileCols + c16], acc);
-                acc2 = mfma4(pa < D ? phik(t + 4, pa) : 0.0f, P[(t + 4) * kTileCols + c16], acc2);
+                acc = mfma4(Ks[t * DK + a] * Ks[t * DK + b] * sc, P[t * kTileCols + c16], acc);
+                acc2 = mfma4(Ks[(t + 4) * DK + a] * Ks[(t + 4) * DK + b] * sc,
+                             P[(t + 4) * kTileCols + c16], acc2);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -526,12 +516,15 @@ __global__ __launch_bounds__(kChainThreads) void delta_chain_kernel(
                 if (p < D) St[p * kTileCols + c16] = acc[r] + acc2[r];
             }
         }
-        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < S4; ++s) mf[s] = mfn[s];
+        lds_barrier();
     }
 
     if (S_out) {
         for (int e = tid; e < D * kTileCols; e += NT) {
-            const int p = e / kTileCols, c = e % kTileCols;
+            const int f = e / kTileCols, c = e % kTileCols;
+            const int p = packed(f);
             if (c == kVals) {
                 if (vt == 0) z_out[bh * D + p] = St[e];
             } else if (vcol(c)) {
