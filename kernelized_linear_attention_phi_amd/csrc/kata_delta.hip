@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kChainThreads) void delta_chain_kernel(
     using F = ChainCfg<DK, C>;
     constexpr int D = F::D, NT = kChainThreads, S4 = F::S4;
     __shared__ float sm[F::FLOATS];
-    __shared__ uint32_t pairs[D];
+    __shared__ uint32_t pairs[F::CIRC ? 1 : D];          // packed order: feature -> pair
     float* St = sm + F::A_OFF;
     float* Ks = sm + F::K_OFF;
     float* Qs = sm + F::Q_OFF;
