@@ -178,3 +178,39 @@ def test_delta_fullsize_recall16k(kata):
     num, den, S_ref, z_ref = O.delta_recurrent(q, k, v, beta, parts=True)
     _check_rows(o, num, den, "bf16")
     assert state_rel_err(S, S_ref) <= 1e-4 and state_rel_err(z, z_ref) <= 1e-4
+
+
+@pytest.mark.parametrize("dk,C", [(16, 64), (32, 16)])
+@pytest.mark.parametrize("T", [1, 5, 17, 64, 65])
+def test_delta_short_sequences(kata, dk, C, T):
+    """Sequences of one token, shorter than a chunk, exactly one chunk and one
+    past it, over 15 heads (not a multiple of 8, so some workgroups of the chunk
+    walk fall past the last head): outputs and final state."""
+    B, H, dv = 3, 5, 32
+    q, k, v = gen.gaussian_qkv(B, H, T, dk, dv, seed=6700 + T + dk, dtype="bf16")
+    beta = _betas(B, H, T, 6701 + T)
+    say(f"delta short dk={dk} C={C} T={T}")
+    o, S, z = _run(kata, q, k, v, beta, C, "bf16")
+    num, den, S_ref, z_ref = O.delta_recurrent(q, k, v, beta, parts=True)
+    _check_rows(o, num, den, "bf16")
+    assert state_rel_err(S, S_ref) <= 1e-4 and state_rel_err(z, z_ref) <= 1e-4
+
+
+def test_delta_caller_workspace_reused(kata):
+    """A caller-owned workspace sized for a long call serves a shorter call
+    next; both equal the calls that allocate their own (bit for bit)."""
+    import torch
+    B, H, dk, dv, C = 1, 3, 16, 64, 64
+    nws = kata.delta_fwd_workspace(B, H, 700, dk, dv, C, 1)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    for T, seed in ((700, 6800), (130, 6801)):
+        q, k, v = (dev(x, "bf16") for x in gen.gaussian_qkv(B, H, T, dk, dv, seed=seed, dtype="bf16"))
+        beta = dev(_betas(B, H, T, seed + 1))
+        say(f"delta workspace reuse T={T}")
+        o1 = torch.empty_like(v)
+        kata.delta_fwd_into(q, k, v, beta, o1, C, workspace=ws)
+        o2 = kata.delta_fwd(q, k, v, beta, chunk=C)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+    with pytest.raises(kata.KataError):
+        kata.delta_fwd_into(q, k, v, beta, o1, C, workspace=ws[:16])
