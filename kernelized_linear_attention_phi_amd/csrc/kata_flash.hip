@@ -11,11 +11,16 @@
 //
 // One workgroup of four wavefronts owns 16 * FQT * 4 consecutive queries of one
 // (batch, head); wavefront w owns FQT consecutive query tiles of 16. Key blocks
-// of 64 are staged to LDS (k | v, FNBUF buffers, direct-to-LDS copies). Per key block and
-// 32-key step: S = K Q^T on MFMA (keys as rows, the query tile as columns),
-// A = S^2 in fp32, masked to j <= t only on blocks that cross the diagonal,
-// cast to bf16, then num += V^T A and den += 1^T A on MFMA, with V^T fragments
-// read transposed from LDS once per step for all of the wavefront's query tiles.
+// (64 or 128 keys, CfgF) are staged to LDS (k | v, FNBUF buffers, direct-to-LDS
+// copies). Per 32-key step: S = K Q^T on MFMA (keys as rows, the query tile as
+// columns), A = S^2 in fp32, cast to bf16, then num += V^T A and den += 1^T A on
+// MFMA, with V^T fragments read transposed from LDS once per step for all of
+// the wavefront's query tiles. A block whose keys all precede the wavefront's
+// first query runs as straight-line code with every score product of the block
+// issued before the first square, so matrix-core latency is covered by other
+// tiles' work; only blocks that reach the diagonal take the per-step path with
+// skips and the j <= t mask. The wavefront index is made scalar, so these
+// choices are scalar branches rather than lane-masked ones.
 //
 // Launch order: heaviest query blocks first (causal work grows with the query
 // index); when B*H is a multiple of 8, all query blocks of a head go to one of
@@ -34,14 +39,21 @@ namespace {
 #ifndef KATA_FLASH_NBUF
 #define KATA_FLASH_NBUF 2
 #endif
+#ifndef KATA_FLASH_NW
+#define KATA_FLASH_NW 4
+#endif
+
 constexpr int FQT = KATA_FLASH_QT;      // query tiles of 16 per wavefront
-constexpr int FNW = 4;                  // wavefronts per workgroup
+constexpr int FNW = KATA_FLASH_NW;      // wavefronts per workgroup
 constexpr int FQB = 16 * FQT * FNW;     // queries per workgroup
-constexpr int FKB = 64;                 // keys per staged block
 constexpr int FNBUF = KATA_FLASH_NBUF;  // staging depth
 
+// Keys per staged block: 128 halves the barriers per key, and is faster where a
+// block's work per wavefront is small (d_k = 32 scores on 16x16x32 products,
+// d_v < 64); at d_k = 16, d_v = 64 blocks of 64 measured as fast or faster.
 template <int DK, int DV>
 struct CfgF {
+    static constexpr int FKB = DK == 16 && DV == 64 ? 64 : 128;
     static constexpr int NTV = DV / 16;
     using IO = ChunkIO<DK, DV, FKB, FNW>;
     static constexpr int LDS = FNBUF * IO::BUF;
@@ -84,25 +96,32 @@ __device__ __forceinline__ f32x4_t key_scores(const bf16_t* bk, int row, const Q
     }
 }
 
-template <int DK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(64 * FNW) void kata_flash_fwd_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    bf16_t* __restrict__ o, int T, int NQB, int BH) {
-    using F = CfgF<DK, DV>;
-    __shared__ __attribute__((aligned(16))) char lds[F::LDS];
-    const Lane L;
+// Weights of one 32-key step for a query tile: A = S^2 (fp32) as a bf16 B
+// operand (slot 4h + r = key 16h + 4g + r of the step), entries with key j > t
+// zeroed when MASK.
+template <bool MASK>
+__device__ __forceinline__ u32x4_t step_weights(const f32x4_t (&sc)[2], int key0, int t,
+                                                const Lane& L) {
+    float w[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = sc[h][r] * sc[h][r];
+            w[4 * h + r] = (!MASK || key0 + 16 * h + 4 * L.g + r <= t) ? x : 0.0f;
+        }
+    return u32x4_t{pk2(w[0], w[1]), pk2(w[2], w[3]), pk2(w[4], w[5]), pk2(w[6], w[7])};
+}
 
-    // block -> (head, query block), heaviest first, head-to-XCD affinity
-    const int lin = blockIdx.x;
-    int bh, qb;
-    if (BH % 8 == 0) {
-        const int xcd = lin % 8, slot = lin / 8, hpx = BH / 8;
-        qb = NQB - 1 - slot / hpx;
-        bh = (slot % hpx) * 8 + xcd;
-    } else {
-        qb = NQB - 1 - lin / BH;
-        bh = lin % BH;
-    }
+// One query block (FQB queries from qb * FQB) of head bh: stream the key blocks
+// it needs through LDS, then normalise and store.
+template <int DK, int DV, bool CAUSAL>
+__device__ __forceinline__ void flash_query_block(const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                                                  bf16_t* o, int T, int bh, int qb, char* lds,
+                                                  const Lane& L) {
+    using F = CfgF<DK, DV>;
+    constexpr int FKB = F::FKB;
+    constexpr int KS = FKB / 32;                  // 32-key steps per staged block
     const size_t head = (size_t)bh * T;
     const int q0 = qb * FQB + 16 * FQT * L.w;    // first query of this wavefront
 
@@ -127,34 +146,55 @@ __global__ __launch_bounds__(64 * FNW) void kata_flash_fwd_kernel(
         const char* buf = P.buffer(kb);
         const bf16_t* bk = reinterpret_cast<const bf16_t*>(buf + F::IO::QB);
         const bf16_t* bv = reinterpret_cast<const bf16_t*>(buf + 2 * F::IO::QB);
+        if (!CAUSAL || kb * FKB + FKB - 1 <= q0) {
+            // every key of the block precedes every query of this wavefront:
+            // straight-line code, all score products issued before the squares
+            f32x4_t sc[KS][FQT][2];
 #pragma unroll
-        for (int m = 0; m < FKB / 32; ++m) {
-            const int key0 = kb * FKB + 32 * m;
-            if (CAUSAL && key0 > q0 + 16 * FQT - 1) continue;   // after every own query
-            u32x4_t vop[F::NTV];
+            for (int m = 0; m < KS; ++m)
 #pragma unroll
-            for (int nt = 0; nt < F::NTV; ++nt) vop[nt] = v_fragment_tr<DV>(bv, m, nt, L);
+                for (int u = 0; u < FQT; ++u)
 #pragma unroll
-            for (int u = 0; u < FQT; ++u) {
-                const int t0 = q0 + 16 * u;
-                if (CAUSAL && key0 > t0 + 15) continue;
-                const bool diag = CAUSAL && key0 + 31 > t0;
-                const int t = t0 + L.c16;
-                float w[8];
+                    for (int h = 0; h < 2; ++h)
+                        sc[m][u][h] = key_scores<DK>(bk, 32 * m + 16 * h + L.c16, qf[u], L);
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const f32x4_t sc = key_scores<DK>(bk, 32 * m + 16 * h + L.c16, qf[u], L);
+            for (int m = 0; m < KS; ++m) {
+                u32x4_t vop[F::NTV];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = key0 + 16 * h + 4 * L.g + r;
-                        const float x = sc[r] * sc[r];
-                        w[4 * h + r] = (!diag || j <= t) ? x : 0.0f;
-                    }
+                for (int nt = 0; nt < F::NTV; ++nt) vop[nt] = v_fragment_tr<DV>(bv, m, nt, L);
+#pragma unroll
+                for (int u = 0; u < FQT; ++u) {
+                    const u32x4_t at = step_weights<false>(sc[m][u], 0, 0, L);
+#pragma unroll
+                    for (int nt = 0; nt < F::NTV; ++nt) num[u][nt] = mma32(vop[nt], at, num[u][nt]);
+                    num[u][F::NTV] = mma32(ones, at, num[u][F::NTV]);
                 }
-                const u32x4_t at = {pk2(w[0], w[1]), pk2(w[2], w[3]), pk2(w[4], w[5]), pk2(w[6], w[7])};
+            }
+        } else {
+            // the block reaches past the first query of this wavefront: steps
+            // after every own query are skipped, tiles whose queries all precede
+            // the step too, and steps crossing a tile's diagonal are masked
 #pragma unroll
-                for (int nt = 0; nt < F::NTV; ++nt) num[u][nt] = mma32(vop[nt], at, num[u][nt]);
-                num[u][F::NTV] = mma32(ones, at, num[u][F::NTV]);
+            for (int m = 0; m < KS; ++m) {
+                const int key0 = kb * FKB + 32 * m;
+                if (key0 > q0 + 16 * FQT - 1) continue;
+                u32x4_t vop[F::NTV];
+#pragma unroll
+                for (int nt = 0; nt < F::NTV; ++nt) vop[nt] = v_fragment_tr<DV>(bv, m, nt, L);
+#pragma unroll
+                for (int u = 0; u < FQT; ++u) {
+                    const int t0 = q0 + 16 * u;
+                    if (key0 > t0 + 15) continue;
+                    f32x4_t sc[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        sc[h] = key_scores<DK>(bk, 32 * m + 16 * h + L.c16, qf[u], L);
+                    const u32x4_t at = key0 + 31 > t0 ? step_weights<true>(sc, key0, t0 + L.c16, L)
+                                                      : step_weights<false>(sc, key0, 0, L);
+#pragma unroll
+                    for (int nt = 0; nt < F::NTV; ++nt) num[u][nt] = mma32(vop[nt], at, num[u][nt]);
+                    num[u][F::NTV] = mma32(ones, at, num[u][F::NTV]);
+                }
             }
         }
         compiler_fence();
@@ -178,6 +218,29 @@ __global__ __launch_bounds__(64 * FNW) void kata_flash_fwd_kernel(
                     u32x2_t{pk2(ov[0], ov[1]), pk2(ov[2], ov[3])};
         }
     }
+}
+
+template <int DK, int DV, bool CAUSAL>
+__global__ __launch_bounds__(64 * FNW) void kata_flash_fwd_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    bf16_t* __restrict__ o, int T, int NQB, int BH) {
+    __shared__ __attribute__((aligned(16))) char lds[CfgF<DK, DV>::LDS];
+    Lane L;
+    // the wavefront index is uniform: as a scalar, every per-wavefront condition
+    // (causal skips, the masked diagonal path) is a scalar branch
+    L.w = __builtin_amdgcn_readfirstlane(L.w);
+    // block -> (head, query block), heaviest first, head-to-XCD affinity
+    const int lin = blockIdx.x;
+    int bh, qb;
+    if (BH % 8 == 0) {
+        const int xcd = lin % 8, slot = lin / 8, hpx = BH / 8;
+        qb = NQB - 1 - slot / hpx;
+        bh = (slot % hpx) * 8 + xcd;
+    } else {
+        qb = NQB - 1 - lin / BH;
+        bh = lin % BH;
+    }
+    flash_query_block<DK, DV, CAUSAL>(q, k, v, o, T, bh, qb, lds, L);
 }
 
 template <int DK, int DV>
