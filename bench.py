@@ -494,7 +494,8 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy (scales HBM counters)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode steps (2048 rows, then 32768 rows; for counter runs)")
-    ap.add_argument("--only", choices=["factored", "scan_vs_sequential", "scan_states", "delta"],
+    ap.add_argument("--only", choices=["factored", "scan_vs_sequential", "scan_states", "delta",
+                                       "quadratic"],
                     help="run one part of parts.* alone and print it (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -521,7 +522,9 @@ def main():
                     kata, torch, gen, ("fwd4k", "fwd32k", "fwd131k"), args.steps, args.warmup),
                 "scan_states": lambda: scan_states_bench(kata, torch, gen, ["fwd131k", "fwd32k"],
                                                          args.steps, args.warmup),
-                "delta": lambda: delta_forward(kata, torch, gen, 3, 1)}[args.only]
+                "delta": lambda: delta_forward(kata, torch, gen, 3, 1),
+                "quadratic": lambda: quadratic_vs_chunked(kata, torch, gen, "fwd4k", args.steps,
+                                                          args.warmup)}[args.only]
         print(json.dumps(part()), flush=True)
         return
     if args.decode_only:
