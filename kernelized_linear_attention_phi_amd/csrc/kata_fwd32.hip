@@ -73,7 +73,8 @@ struct Cfg32 {
     static constexpr int TW = TT / NW;            // query tiles per wavefront
     static constexpr int KS = C / 32;             // 32-token K-steps per chunk
     using IO = ChunkIO<DK, DV, C, NW, NW, GATE>;
-    // LDS: two chunk buffers | bf16 state operands | one output tile per wavefront
+    // LDS (output kernel): bf16 state operands | two chunk buffers | one output
+    // tile per wavefront
     static constexpr int SPAIR = 16 * NTV * 1024;   // S^T operands of tile pairs 0..15
     static constexpr int S32 = NTV * 512;           // S^T operands of tile 32
     static constexpr int ZOP = 2 * 1024;            // Gram operands (rows L, rows U)
@@ -595,12 +596,16 @@ __device__ __forceinline__ void fwd_body32(const bf16_t* q, const bf16_t* k, con
     using F = Cfg32<DV, C, DECAY>;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    Pipeline<DK, DV, C, F::NW, F::NW, DECAY> P{lds, seg * G, min(NC, seg * G + G), T, bh * T,
-                                               true, gdec};
-    char* sb = lds + 2 * F::IO::BUF;
+    // LDS: published state operands | two chunk buffers | output tiles | key
+    // decays. The state operands come first: the workgroup's LDS starts at
+    // address 0, so every state operand read of the first 64 KB is the lane's
+    // base plus an immediate offset, with no address register per read.
     constexpr int SBX = PREC ? Prec32<DV, C>::SB : F::SB;   // published state operands
-    char* otile = sb + SBX + W * F::OTILE;
-    float* krow = reinterpret_cast<float*>(sb + SBX + F::NW * F::OTILE + W * F::KROW);
+    char* sb = lds;
+    Pipeline<DK, DV, C, F::NW, F::NW, DECAY> P{lds + SBX, seg * G, min(NC, seg * G + G), T, bh * T,
+                                               true, gdec};
+    char* otile = lds + SBX + 2 * F::IO::BUF + W * F::OTILE;
+    float* krow = reinterpret_cast<float*>(lds + SBX + 2 * F::IO::BUF + F::NW * F::OTILE + W * F::KROW);
 
     State32<DV, C> st;
     record_load32<W, DV, C>(prefix + (CAUSAL ? bh * NSEG + seg : bh) * (size_t)F::REC, st, L);
