@@ -434,9 +434,14 @@ __device__ __forceinline__ void fwd_body(const bf16_t* q, const bf16_t* k, const
     constexpr int REC = F::NAT * NU * 256;
     const int seg = blockIdx.x;
     const size_t bh = blockIdx.y;
-    Pipeline<F::DK, DV, C, NWF> P{lds, seg * Gs, min(NC, seg * Gs + Gs), T, bh * T, true};
-    char* lifted = lds + 2 * IO::BUF;              // lifted key tiles of the chunk
-    char* pub = lifted + 2 * F::NAT * Lifted<C, 2>::TILE;
+    // LDS: published state (hi | lo) | lifted key tiles | two chunk buffers. The
+    // published operands come first: the workgroup's LDS starts at address 0,
+    // so each operand read is the lane's base plus an immediate offset (an
+    // immediate reaches 64 KB), with no address register per read.
+    char* pub = lds;
+    char* lifted = lds + 2 * PB::BYTES;            // lifted key tiles of the chunk
+    Pipeline<F::DK, DV, C, NWF> P{lifted + 2 * F::NAT * Lifted<C, 2>::TILE, seg * Gs,
+                                  min(NC, seg * Gs + Gs), T, bh * T, true};
     // the second half of an odd last tile pair is never published: zero it all
     for (int i = threadIdx.x; i < 2 * PB::BYTES / 16; i += 64 * NWF)
         reinterpret_cast<u32x4_t*>(pub)[i] = u32x4_t{0u, 0u, 0u, 0u};
